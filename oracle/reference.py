@@ -1,0 +1,430 @@
+"""Plain float64 CPU oracle: forward and hand-written backward of the decoder
+stack, the fused next-token cross-entropy and the embedding.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never called by the
+product path.  Slow on purpose: no blocking, fusion or reordering beyond each
+definition, so every function can be checked against the pages by eye.
+
+Sources (page title, then section):
+  [FR] "Comment Entraîner Votre Propre ChatGPT Pour 50€ ?", section
+       "1. Le modèle GPT (nanochat/gpt.py)": RoPE without learned positions,
+       QK normalisation, untied token embedding and output projection, ReLU²
+       MLP, grouped-query attention, sliding-window attention; the value-
+       embedding snippet and the three "astuces d'efficacité" snippets
+       (per-layer residual scaling, smear, backout); section "3. Gestion de la
+       précision": bias-free Linear computing F.linear(x, W) with W stored
+       [out, in]; section "5. Unification de Flash Attention": the attention
+       call takes (B, T, H, D) tensors with causal=True and a window_size.
+  [JA] the same article on dev.to (Japanese), section "1. GPTモデル".
+  [ZH] "nanochat：仅需73美元，3小时训练GPT-2级别大语言模型", section "排行榜"
+       (the d24 run: batch 16 per device, sequence 2048).
+
+Readings taken where the pages are silent (each listed in the design doc):
+  * pre-norm blocks x += Attn(rms(x)); x += MLP(rms(x)); final rms before the
+    head; no biases; RMSNorm has no affine and eps = 1e-6 everywhere;
+  * QK norm is an RMSNorm over head_dim per (token, head), applied before
+    RoPE (the two commute: RoPE is a rotation and the norm has no affine);
+  * RoPE pairs dimension j with j + D/2, angle t * base^(-2j/D), positions
+    restart at 0 on every row;
+  * softmax scale 1/sqrt(D); window W >= 0 makes key j visible from query i
+    iff 0 <= i - j <= W; W < 0 is plain causal attention;
+  * query head h reads K/V head h // (H / Hkv);
+  * the loss is the mean over all B*T positions, no ignore index;
+  * fp8 operands (d26 MLP) are OCP e4m3fn with a per-tensor scale
+    amax/448, round-to-nearest-even, saturating; gradients pass straight
+    through the quantiser.
+
+Pins (tests/test_oracle_*.py): finite differences of every gradient on tiny
+shapes; RoPE preserves norms, is the identity at t = 0 and depends only on
+relative position; softmax rows sum to one and vanish off the mask; W = 0 gives
+o = v and zero dq, dk; W >= T - 1 equals full causal; Hkv = H equals MHA and
+GQA equals MHA on repeated K/V; causality under perturbation; the whole
+forward/backward against torch float64 autograd on library primitives
+(F.rms_norm, F.linear, F.scaled_dot_product_attention, F.cross_entropy);
+cross-entropy closed form at W_lm = 0; the e4m3 quantiser against torch's
+float8_e4m3fn cast.  Parity with nanochat's own numerics is unpinned: the
+pages print no forward or backward value.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+__all__ = [
+    "rms_norm", "rms_norm_backward", "rope_tables", "rope", "rope_backward",
+    "visible_mask", "attention", "attention_backward", "e4m3_round",
+    "fp8_quant_dequant", "block_forward", "block_backward", "lm_head_ce",
+    "embed_forward", "embed_backward", "smear_forward", "smear_backward",
+    "stack_forward_backward", "FP8_E4M3_MAX",
+]
+
+FP8_E4M3_MAX = 448.0
+
+
+# ----------------------------------------------------------------- RMSNorm
+def rms_norm(x: np.ndarray, eps: float) -> Tuple[np.ndarray, np.ndarray]:
+    """y = x / sqrt(mean(x^2) + eps) over the last axis (no affine).
+    Returns y and r = 1/sqrt(mean(x^2) + eps) (shape x.shape[:-1])."""
+    ms = np.mean(x * x, axis=-1)
+    r = 1.0 / np.sqrt(ms + eps)
+    return x * r[..., None], r
+
+
+def rms_norm_backward(dy: np.ndarray, y: np.ndarray, r: np.ndarray) -> np.ndarray:
+    """Chain rule through y = x*r, r = (mean(x^2)+eps)^(-1/2):
+    dx = r * (dy - y * mean(dy * y))."""
+    return r[..., None] * (dy - y * np.mean(dy * y, axis=-1, keepdims=True))
+
+
+# -------------------------------------------------------------------- RoPE
+def rope_tables(T: int, D: int, base: float) -> Tuple[np.ndarray, np.ndarray]:
+    """cos and sin of theta[t, j] = t * base^(-2j/D), t < T, j < D/2 (float64)."""
+    j = np.arange(D // 2, dtype=np.float64)
+    inv_freq = base ** (-2.0 * j / D)
+    theta = np.arange(T, dtype=np.float64)[:, None] * inv_freq[None, :]
+    return np.cos(theta), np.sin(theta)
+
+
+def rope(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Rotate each pair (x[j], x[j + D/2]) of x [B, T, H, D] by theta[t, j]:
+    (a, b) -> (a cos - b sin, a sin + b cos)."""
+    D = x.shape[-1]
+    a, b = x[..., : D // 2], x[..., D // 2:]
+    c, s = cos[None, :, None, :], sin[None, :, None, :]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def rope_backward(dy: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Transpose of the rotation (= rotation by -theta)."""
+    D = dy.shape[-1]
+    da, db = dy[..., : D // 2], dy[..., D // 2:]
+    c, s = cos[None, :, None, :], sin[None, :, None, :]
+    return np.concatenate([da * c + db * s, -da * s + db * c], axis=-1)
+
+
+# --------------------------------------------------------------- attention
+def visible_mask(T: int, window: int) -> np.ndarray:
+    """[T, T] bool: query i sees key j iff j <= i and (window < 0 or i - j <= window)."""
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    m = j <= i
+    if window >= 0:
+        m &= (i - j) <= window
+    return m
+
+
+def _kv_head(h: int, H: int, Hkv: int) -> int:
+    return h // (H // Hkv)
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, window: int
+              ) -> Tuple[np.ndarray, np.ndarray]:
+    """Softmax attention on q [B,T,H,D], k/v [B,T,Hkv,D]; scale 1/sqrt(D).
+    Returns o [B,T,H,D] and the probabilities P [B,H,T,T] (zero off-mask)."""
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    mask = visible_mask(T, window)
+    scale = 1.0 / math.sqrt(D)
+    o = np.zeros_like(q)
+    P = np.zeros((B, H, T, T))
+    for b in range(B):
+        for h in range(H):
+            g = _kv_head(h, H, Hkv)
+            s = (q[b, :, h, :] @ k[b, :, g, :].T) * scale
+            s = np.where(mask, s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            e = np.exp(s)
+            p = e / e.sum(axis=1, keepdims=True)
+            P[b, h] = p
+            o[b, :, h, :] = p @ v[b, :, g, :]
+    return o, P
+
+
+def attention_backward(do: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                       P: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Backward of `attention`: dP = dO V^T, dS = P*(dP - rowsum(dP*P)),
+    dQ = dS K * scale, dK = dS^T Q * scale, dV = P^T dO; K/V gradients are summed
+    over the query heads that share a K/V head."""
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    scale = 1.0 / math.sqrt(D)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            g = _kv_head(h, H, Hkv)
+            p = P[b, h]
+            dv[b, :, g, :] += p.T @ do[b, :, h, :]
+            dp = do[b, :, h, :] @ v[b, :, g, :].T
+            ds = p * (dp - np.sum(dp * p, axis=1, keepdims=True))
+            dq[b, :, h, :] = (ds @ k[b, :, g, :]) * scale
+            dk[b, :, g, :] += (ds.T @ q[b, :, h, :]) * scale
+    return dq, dk, dv
+
+
+# --------------------------------------------------------------------- fp8
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest OCP e4m3fn value (ties to even), saturating at
+    +-448.  e4m3fn: 3 mantissa bits, exponent bias 7, smallest normal 2^-6,
+    subnormal spacing 2^-9, no infinities."""
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.abs(x)
+    _, e = np.frexp(ax)                       # ax = m * 2^e, m in [0.5, 1)
+    quantum = np.ldexp(1.0, np.maximum(e - 4, -9))  # 2^(floor(log2 ax) - 3), >= 2^-9
+    q = np.round(ax / quantum) * quantum      # np.round: half to even
+    q = np.minimum(q, FP8_E4M3_MAX)
+    return np.where(x < 0, -q, q)
+
+
+def fp8_quant_dequant(x: np.ndarray) -> np.ndarray:
+    """Per-tensor dynamic scaling s = amax|x| / 448, then x ~ e4m3(x / s) * s."""
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    if amax == 0.0:
+        return np.zeros_like(x)
+    s = amax / FP8_E4M3_MAX
+    return e4m3_round(x / s) * s
+
+
+def _mm_nt(a, b, fp8):
+    """a @ b^T, operands optionally through the fp8 quantiser."""
+    if fp8:
+        a, b = fp8_quant_dequant(a), fp8_quant_dequant(b)
+    return a @ b.T
+
+
+# ------------------------------------------------------------------- block
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def block_forward(x: np.ndarray, p: Dict[str, np.ndarray], cfg, l: int,
+                  cos: np.ndarray, sin: np.ndarray,
+                  x0: Optional[np.ndarray] = None,
+                  ids: Optional[np.ndarray] = None) -> Tuple[np.ndarray, dict]:
+    """One pre-norm decoder block on x [B, T, C] (all float64).
+
+    [d26 extras: x <- resid_lambda*x + x0_lambda*x0 first; on odd layers
+    v += 3*sigmoid(xn1[..., :32] @ W_g^T) * VE[ids] per K/V head.]
+    xn1 = rms(x); q,k,v = xn1 W_qkv^T; qh = rope(rms_D(q)), kh = rope(rms_D(k));
+    o = attn(qh, kh, v); x_mid = x + o W_o^T; xn2 = rms(x_mid);
+    u = xn2 W_fc^T; h = relu(u)^2; out = x_mid + h W_proj^T.
+    """
+    B, T, C = x.shape
+    H, Hkv, D = cfg.n_head, cfg.n_kv_head, cfg.head_dim
+    Q, KV = H * D, Hkv * D
+    eps, window = cfg.eps, cfg.windows[l]
+    fp8 = bool(getattr(cfg, "mlp_fp8", False))
+    c = {}
+    if cfg.extras:
+        c["x_premix"], c["x0"] = x, x0
+        x = p["resid_lambda"] * x + p["x0_lambda"] * x0
+    c["x_in"] = x
+    xn1, r1 = rms_norm(x, eps)
+    qkv = xn1 @ p["w_qkv"].T
+    q = qkv[..., :Q].reshape(B, T, H, D)
+    k = qkv[..., Q:Q + KV].reshape(B, T, Hkv, D)
+    v = qkv[..., Q + KV:].reshape(B, T, Hkv, D)
+    if cfg.extras and "ve" in p:
+        nch = cfg.ve_gate_channels
+        s = xn1[..., :nch] @ p["ve_gate"].T                 # [B, T, Hkv]
+        gate = 3.0 * _sigmoid(s)
+        ve = p["ve"][ids].reshape(B, T, Hkv, D)
+        c.update(ve_s=s, ve_gate=gate, ve_rows=ve)
+        v = v + gate[..., None] * ve
+    qn, rq = rms_norm(q, eps)
+    kn, rk = rms_norm(k, eps)
+    qh, kh = rope(qn, cos, sin), rope(kn, cos, sin)
+    o, P = attention(qh, kh, v, window)
+    o2 = o.reshape(B, T, Q)
+    x_mid = x + o2 @ p["w_o"].T
+    xn2, r2 = rms_norm(x_mid, eps)
+    u = _mm_nt(xn2, p["w_fc"], fp8)
+    h = np.maximum(u, 0.0) ** 2
+    out = x_mid + _mm_nt(h, p["w_proj"], fp8)
+    c.update(xn1=xn1, r1=r1, qn=qn, rq=rq, kn=kn, rk=rk, qh=qh, kh=kh, v=v, o=o2,
+             P=P, x_mid=x_mid, xn2=xn2, r2=r2, u=u, h=h)
+    return out, c
+
+
+def block_backward(dout: np.ndarray, c: dict, p: Dict[str, np.ndarray], cfg, l: int,
+                   cos: np.ndarray, sin: np.ndarray,
+                   ids: Optional[np.ndarray] = None) -> Tuple[np.ndarray, dict]:
+    """Reverse of `block_forward`.  Returns dx (w.r.t. the block input; with
+    the extras, w.r.t. the pre-mix stream) and a dict of float64 gradients
+    (w_qkv, w_o, w_fc, w_proj[, resid_lambda, x0_lambda, x0, ve, ve_gate])."""
+    B, T, C = dout.shape
+    H, Hkv, D = cfg.n_head, cfg.n_kv_head, cfg.head_dim
+    Q, KV = H * D, Hkv * D
+    fp8 = bool(getattr(cfg, "mlp_fp8", False))
+    g = {}
+    q8 = fp8_quant_dequant if fp8 else (lambda a: a)
+    # MLP: out = x_mid + h W_proj^T, h = relu(u)^2, u = xn2 W_fc^T
+    dh = q8(dout) @ q8(p["w_proj"])
+    g["w_proj"] = np.einsum("btc,btf->cf", q8(dout), q8(c["h"]))
+    du = dh * 2.0 * np.maximum(c["u"], 0.0)
+    dxn2 = q8(du) @ q8(p["w_fc"])
+    g["w_fc"] = np.einsum("btf,btc->fc", q8(du), q8(c["xn2"]))
+    dx_mid = dout + rms_norm_backward(dxn2, c["xn2"], c["r2"])
+    # attention output projection
+    do2 = dx_mid @ p["w_o"]
+    g["w_o"] = np.einsum("btc,btq->cq", dx_mid, c["o"])
+    dqh, dkh, dv = attention_backward(do2.reshape(B, T, H, D), c["qh"], c["kh"], c["v"], c["P"])
+    dq = rms_norm_backward(rope_backward(dqh, cos, sin), c["qn"], c["rq"])
+    dk = rms_norm_backward(rope_backward(dkh, cos, sin), c["kn"], c["rk"])
+    dxn1_extra = 0.0
+    if cfg.extras and "ve" in p:
+        # v' = v + gate * ve
+        dgate = np.sum(dv * c["ve_rows"], axis=-1)                   # [B,T,Hkv]
+        dve_rows = dv * c["ve_gate"][..., None]
+        sg = _sigmoid(c["ve_s"])
+        ds = dgate * 3.0 * sg * (1.0 - sg)
+        nch = cfg.ve_gate_channels
+        g["ve_gate"] = np.einsum("bth,btc->hc", ds, c["xn1"][..., :nch])
+        dxe = np.zeros_like(c["xn1"])
+        dxe[..., :nch] = ds @ p["ve_gate"]
+        dxn1_extra = dxe
+        dve = np.zeros_like(p["ve"])
+        np.add.at(dve, ids.reshape(-1), dve_rows.reshape(B * T, KV))
+        g["ve"] = dve
+    dqkv = np.concatenate([dq.reshape(B, T, Q), dk.reshape(B, T, KV), dv.reshape(B, T, KV)], -1)
+    dxn1 = dqkv @ p["w_qkv"] + dxn1_extra
+    g["w_qkv"] = np.einsum("btk,btc->kc", dqkv, c["xn1"])
+    dx = dx_mid + rms_norm_backward(dxn1, c["xn1"], c["r1"])
+    if cfg.extras:
+        g["resid_lambda"] = np.sum(dx * c["x_premix"])
+        g["x0_lambda"] = np.sum(dx * c["x0"])
+        g["x0"] = p["x0_lambda"] * dx
+        dx = p["resid_lambda"] * dx
+    return dx, g
+
+
+# ------------------------------------------------------- head + loss, embed
+def lm_head_ce(x: np.ndarray, w_lm: np.ndarray, targets: np.ndarray, eps: float
+               ) -> Tuple[float, np.ndarray, np.ndarray, dict]:
+    """xf = rms(x); z = xf W_lm^T; loss = mean_n(logsumexp(z_n) - z_n[y_n]).
+    Returns loss, dx (w.r.t. the pre-norm x), dW_lm and a cache
+    (z, lse, dz = (softmax(z) - onehot(y)) / N)."""
+    shp = x.shape
+    x2 = x.reshape(-1, shp[-1])
+    y = targets.reshape(-1)
+    N = x2.shape[0]
+    xf, rf = rms_norm(x2, eps)
+    z = xf @ w_lm.T
+    m = z.max(axis=1)
+    lse = m + np.log(np.sum(np.exp(z - m[:, None]), axis=1))
+    loss = float(np.mean(lse - z[np.arange(N), y]))
+    dz = np.exp(z - lse[:, None])
+    dz[np.arange(N), y] -= 1.0
+    dz /= N
+    dxf = dz @ w_lm
+    dw = dz.T @ xf
+    dx = rms_norm_backward(dxf, xf, rf).reshape(shp)
+    return loss, dx, dw, {"z": z, "lse": lse, "dz": dz, "xf": xf, "rf": rf}
+
+
+def embed_forward(wte: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    return wte[ids]
+
+
+def embed_backward(dx: np.ndarray, ids: np.ndarray, V: int) -> np.ndarray:
+    """dWte[v] = sum of dx rows whose id is v."""
+    C = dx.shape[-1]
+    dw = np.zeros((V, C))
+    np.add.at(dw, ids.reshape(-1), dx.reshape(-1, C))
+    return dw
+
+
+def smear_forward(e: np.ndarray, w_s: np.ndarray, lam: float) -> Tuple[np.ndarray, dict]:
+    """x_t = e_t + lam * sigmoid(w_s . e_t[:n]) * e_{t-1} for t >= 1; x_0 = e_0.
+    e [B, T, C]; the gate reads the current token, the mixed vector is the
+    previous token's embedding."""
+    n = w_s.shape[0]
+    s = e[..., :n] @ w_s                     # [B, T]
+    sg = _sigmoid(s)
+    prev = np.zeros_like(e)
+    prev[:, 1:] = e[:, :-1]
+    gate = lam * sg
+    gate[:, 0] = 0.0
+    return e + gate[..., None] * prev, {"s": s, "sg": sg, "prev": prev, "gate": gate}
+
+
+def smear_backward(dx: np.ndarray, e: np.ndarray, w_s: np.ndarray, lam: float, c: dict
+                   ) -> Tuple[np.ndarray, np.ndarray, float]:
+    n = w_s.shape[0]
+    de = dx.copy()
+    de[:, :-1] += c["gate"][:, 1:, None] * dx[:, 1:]
+    dgate = np.sum(dx * c["prev"], axis=-1)           # [B, T]
+    dgate[:, 0] = 0.0
+    dlam = float(np.sum(dgate * c["sg"]))
+    ds = dgate * lam * c["sg"] * (1.0 - c["sg"])
+    dws = np.einsum("bt,btc->c", ds, e[..., :n])
+    de[..., :n] += ds[..., None] * w_s
+    return de, dws, dlam
+
+
+# ------------------------------------------------------------------- stack
+def stack_forward_backward(cfg, ids: np.ndarray, glob: Dict[str, np.ndarray],
+                           layers: List[Dict[str, np.ndarray]], keep: bool = False):
+    """Full step on ids [B, T+1]: embedding [-> smear], L blocks [with residual
+    mixing, value embeddings, backout], final rms, lm_head, mean next-token
+    cross-entropy; then the backward of all of it.  Returns (loss, grads,
+    acts) where grads has 'wte', 'w_lm', 'layers' (list of dicts) [and the
+    extras' scalars], and acts (if keep) holds each block's input stream."""
+    B, T1 = ids.shape
+    T = T1 - 1
+    inp, tgt = ids[:, :T], ids[:, 1:]
+    L = cfg.n_layer
+    cos, sin = rope_tables(T, cfg.head_dim, cfg.rope_base)
+    f64 = lambda a: np.asarray(a, dtype=np.float64)
+    glob = {k: f64(v) for k, v in glob.items()}
+    layers = [{k: f64(v) for k, v in p.items()} for p in layers]
+    e = embed_forward(glob["wte"], inp)
+    x0 = None
+    if cfg.extras:
+        x, sc = smear_forward(e, glob["smear_gate"], float(glob["smear_lambda"]))
+        x0 = x
+    else:
+        x = e
+    caches, acts = [], []
+    i_bo = L // 2 - 1
+    x_bo = None
+    for l in range(L):
+        acts.append(x)
+        x, c = block_forward(x, layers[l], cfg, l, cos, sin, x0=x0, ids=inp)
+        caches.append(c)
+        if cfg.extras and l == i_bo:
+            x_bo = x
+    acts.append(x)
+    if cfg.extras:
+        x_final = x - glob["backout_lambda"] * x_bo
+    else:
+        x_final = x
+    loss, dx, dw_lm, hc = lm_head_ce(x_final, glob["w_lm"], tgt, cfg.eps)
+    grads = {"w_lm": dw_lm, "layers": [None] * L}
+    if cfg.extras:
+        grads["backout_lambda"] = -float(np.sum(dx * x_bo))
+        dx_bo = -glob["backout_lambda"] * dx
+        dx0 = np.zeros_like(dx)
+    for l in reversed(range(L)):
+        if cfg.extras and l == i_bo:
+            dx = dx + dx_bo
+        dx, g = block_backward(dx, caches[l], layers[l], cfg, l, cos, sin, ids=inp)
+        if cfg.extras:
+            dx0 += g.pop("x0")
+        grads["layers"][l] = g
+    if cfg.extras:
+        dx = dx + dx0
+        de, dws, dlam = smear_backward(dx, e, glob["smear_gate"], float(glob["smear_lambda"]), sc)
+        grads["smear_gate"] = dws
+        grads["smear_lambda"] = dlam
+    else:
+        de = dx
+    grads["wte"] = embed_backward(de, inp, glob["wte"].shape[0])
+    out = {"head": hc, "x_final": x_final}
+    if keep:
+        out["acts"] = acts
+        out["caches"] = caches
+    return loss, grads, out

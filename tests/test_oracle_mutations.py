@@ -1,0 +1,74 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch each one: a dropped term, a wrong sign, an off-by-one, a transposed
+operand.  Every mutant must fail the torch-autograd cross-check or the
+finite-difference check."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle.reference as R
+from test_oracle_pins import _params, tiny_cfg
+from test_oracle_vs_torch import _compare
+
+
+def _mut_rms_bwd(dy, y, r):          # dropped projection term
+    return r[..., None] * dy
+
+
+def _mut_rope(x, cos, sin):          # wrong rotation sign in the forward only
+    D = x.shape[-1]
+    a, b = x[..., : D // 2], x[..., D // 2:]
+    c, s = cos[None, :, None, :], sin[None, :, None, :]
+    return np.concatenate([a * c + b * s, -a * s + b * c], axis=-1)
+
+
+def _mut_mask(T, window):            # window off by one (i - j < W)
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    m = j <= i
+    if window >= 0:
+        m &= (i - j) < window
+    return m
+
+
+_orig_attn_bwd = R.attention_backward
+
+
+def _mut_attn_bwd(do, q, k, v, P):  # transposed P in dV
+    dq, dk, dv = _orig_attn_bwd(do, q, k, v, P)
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            dv[b, :, h // (H // Hkv)] += P[b, h] @ do[b, :, h]
+    return dq, dk, dv
+
+
+def _mut_kv_head(h, H, Hkv):         # interleaved instead of contiguous head groups
+    return h % Hkv
+
+
+_orig_ce = R.lm_head_ce
+
+
+def _mut_ce(x, w, t, eps):           # loss not divided by N in the gradient
+    loss, dx, dw, c = _orig_ce(x, w, t, eps)
+    n = x.reshape(-1, x.shape[-1]).shape[0]
+    return loss, dx * n, dw * n, c
+
+
+MUTANTS = [("rms_norm_backward", _mut_rms_bwd), ("rope", _mut_rope),
+           ("visible_mask", _mut_mask), ("attention_backward", _mut_attn_bwd),
+           ("_kv_head", _mut_kv_head), ("lm_head_ce", _mut_ce)]
+
+
+@pytest.mark.parametrize("name,fn", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(monkeypatch, name, fn):
+    cfg = tiny_cfg(n_head=4, n_kv_head=2, head_dim=4, windows=(3, -1), T=9)
+    ids, glob, layers = _params(cfg, np.random.default_rng(13))
+    _compare(cfg, ids, glob, layers)            # unmutated: passes
+    monkeypatch.setattr(R, name, fn)
+    with pytest.raises(AssertionError):
+        _compare(cfg, ids, glob, layers)

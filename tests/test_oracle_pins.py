@@ -1,0 +1,360 @@
+"""Pins of the CPU oracle to facts outside itself: closed forms, invariants,
+special cases and finite differences (all float64, CPU only)."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from seeded_inputs import Workload
+
+RNG = np.random.default_rng(20260101)
+
+
+def tiny_cfg(**kw):
+    base = dict(name="pin", n_layer=2, B=2, T=6, C=16, n_head=2, n_kv_head=1, head_dim=8,
+                mlp_hidden=64, vocab=11, windows=(-1, 2), dtype="f32", seed=7)
+    base.update(kw)
+    return Workload(**base)
+
+
+# ------------------------------------------------------------------ RMSNorm
+def test_rmsnorm_closed_form():
+    x = RNG.standard_normal((5, 37)) * 3.0
+    eps = 1e-6
+    y, r = O.rms_norm(x, eps)
+    ms = np.mean(x ** 2, axis=1)
+    # output RMS is sqrt(ms / (ms + eps)); r is exactly the inverse RMS
+    np.testing.assert_allclose(np.sqrt(np.mean(y ** 2, axis=1)), np.sqrt(ms / (ms + eps)), rtol=1e-14)
+    np.testing.assert_allclose(r, 1.0 / np.sqrt(ms + eps), rtol=1e-14)
+    # scale invariance (eps -> 0)
+    y1, _ = O.rms_norm(x, 0.0)
+    y2, _ = O.rms_norm(7.5 * x, 0.0)
+    np.testing.assert_allclose(y1, y2, rtol=1e-13)
+
+
+def test_rmsnorm_backward_orthogonal_at_eps0():
+    # with eps = 0 the norm is scale invariant, so <dx, x> = 0 for any dy
+    x = RNG.standard_normal((4, 24))
+    dy = RNG.standard_normal((4, 24))
+    y, r = O.rms_norm(x, 0.0)
+    dx = O.rms_norm_backward(dy, y, r)
+    assert np.max(np.abs(np.sum(dx * x, axis=1))) < 1e-12
+
+
+def fd_check(f, x, dx_analytic, h=1e-6, n_dirs=3, rtol=1e-6):
+    for _ in range(n_dirs):
+        d = RNG.standard_normal(x.shape)
+        num = (f(x + h * d) - f(x - h * d)) / (2 * h)
+        ana = float(np.sum(dx_analytic * d))
+        assert abs(num - ana) <= rtol * max(1.0, abs(ana)), (num, ana)
+
+
+def test_rmsnorm_backward_fd():
+    x = RNG.standard_normal((3, 10))
+    w = RNG.standard_normal((3, 10))
+    f = lambda z: float(np.sum(O.rms_norm(z, 1e-6)[0] * w))
+    y, r = O.rms_norm(x, 1e-6)
+    fd_check(f, x, O.rms_norm_backward(w, y, r))
+
+
+# --------------------------------------------------------------------- RoPE
+def test_rope_preserves_norm_and_identity_at_t0():
+    T, H, D = 9, 3, 16
+    cos, sin = O.rope_tables(T, D, 10000.0)
+    x = RNG.standard_normal((2, T, H, D))
+    y = O.rope(x, cos, sin)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    np.testing.assert_allclose(y[:, 0], x[:, 0], rtol=0, atol=0)
+
+
+def test_rope_relative_position():
+    # <R_m q, R_n k> depends only on m - n
+    T, D = 40, 16
+    cos, sin = O.rope_tables(T, D, 10000.0)
+    q = RNG.standard_normal(D)
+    k = RNG.standard_normal(D)
+    X = np.zeros((1, T, 2, D))
+    X[0, :, 0] = q
+    X[0, :, 1] = k
+    Y = O.rope(X, cos, sin)
+    for m, n, s in [(5, 2, 11), (9, 9, 20), (3, 7, 30)]:
+        a = Y[0, m, 0] @ Y[0, n, 1]
+        b = Y[0, m + s, 0] @ Y[0, n + s, 1]
+        assert abs(a - b) < 1e-12
+
+
+def test_rope_closed_form_basis_vector():
+    # rotating e_j at position t gives cos(theta) e_j + sin(theta) e_{j+D/2}
+    T, D, base = 7, 8, 10000.0
+    cos, sin = O.rope_tables(T, D, base)
+    for j in range(D // 2):
+        x = np.zeros((1, T, 1, D))
+        x[..., j] = 1.0
+        y = O.rope(x, cos, sin)
+        for t in range(T):
+            th = t * base ** (-2.0 * j / D)
+            expect = np.zeros(D)
+            expect[j] = math.cos(th)
+            expect[j + D // 2] = math.sin(th)
+            np.testing.assert_allclose(y[0, t, 0], expect, atol=1e-15)
+
+
+def test_rope_backward_is_inverse():
+    T, H, D = 5, 2, 8
+    cos, sin = O.rope_tables(T, D, 10000.0)
+    x = RNG.standard_normal((1, T, H, D))
+    np.testing.assert_allclose(O.rope_backward(O.rope(x, cos, sin), cos, sin), x, atol=1e-14)
+
+
+def test_rms_and_rope_commute():
+    T, H, D = 6, 2, 8
+    cos, sin = O.rope_tables(T, D, 10000.0)
+    x = RNG.standard_normal((1, T, H, D))
+    a = O.rope(O.rms_norm(x, 1e-6)[0], cos, sin)
+    b = O.rms_norm(O.rope(x, cos, sin), 1e-6)[0]
+    np.testing.assert_allclose(a, b, atol=1e-14)
+
+
+# ---------------------------------------------------------------- attention
+def _qkv(B=2, T=12, H=4, Hkv=2, D=8):
+    return (RNG.standard_normal((B, T, H, D)), RNG.standard_normal((B, T, Hkv, D)),
+            RNG.standard_normal((B, T, Hkv, D)))
+
+
+@pytest.mark.parametrize("window", [-1, 0, 1, 3, 11, 40])
+def test_softmax_rows_sum_to_one_and_mask(window):
+    q, k, v = _qkv()
+    T = q.shape[1]
+    _, P = O.attention(q, k, v, window)
+    np.testing.assert_allclose(P.sum(-1), 1.0, atol=1e-14)
+    m = O.visible_mask(T, window)
+    assert np.all(P[..., ~m] == 0.0)
+    assert np.all(P[..., m] > 0.0)
+    # the visible set is exactly the keys with 0 <= i - j <= W
+    i, j = np.nonzero(m)
+    assert np.all(i - j >= 0)
+    if window >= 0:
+        assert np.all(i - j <= window)
+        assert m.sum() == sum(min(t, window) + 1 for t in range(T))
+
+
+def test_window_zero_gives_v_and_no_qk_grad():
+    q, k, v = _qkv()
+    o, P = O.attention(q, k, v, 0)
+    G = q.shape[2] // k.shape[2]
+    np.testing.assert_allclose(o, np.repeat(v, G, axis=2), atol=1e-15)
+    do = RNG.standard_normal(o.shape)
+    dq, dk, dv = O.attention_backward(do, q, k, v, P)
+    assert np.max(np.abs(dq)) < 1e-15 and np.max(np.abs(dk)) < 1e-15
+
+
+def test_window_ge_T_minus_1_is_full_causal():
+    q, k, v = _qkv(T=10)
+    o_full, _ = O.attention(q, k, v, -1)
+    o_w, _ = O.attention(q, k, v, 9)
+    o_w2, _ = O.attention(q, k, v, 500)
+    np.testing.assert_array_equal(o_full, o_w)
+    np.testing.assert_array_equal(o_full, o_w2)
+    o_w8, _ = O.attention(q, k, v, 8)
+    assert np.max(np.abs(o_w8 - o_full)) > 1e-6  # one key fewer on the last row
+
+
+def test_gqa_equals_mha_on_repeated_kv():
+    q, k, v = _qkv(H=6, Hkv=2)
+    G = 3
+    kr, vr = np.repeat(k, G, axis=2), np.repeat(v, G, axis=2)
+    o_g, P_g = O.attention(q, k, v, 3)
+    o_m, P_m = O.attention(q, kr, vr, 3)
+    np.testing.assert_allclose(o_g, o_m, atol=1e-15)
+    do = RNG.standard_normal(o_g.shape)
+    dq_g, dk_g, dv_g = O.attention_backward(do, q, k, v, P_g)
+    dq_m, dk_m, dv_m = O.attention_backward(do, q, kr, vr, P_m)
+    np.testing.assert_allclose(dq_g, dq_m, atol=1e-14)
+    B, T = q.shape[:2]
+    np.testing.assert_allclose(dk_g, dk_m.reshape(B, T, 2, G, -1).sum(3), atol=1e-13)
+    np.testing.assert_allclose(dv_g, dv_m.reshape(B, T, 2, G, -1).sum(3), atol=1e-13)
+
+
+def test_mha_head_independence():
+    # n_kv_head = n_head: head h of the output depends only on head h inputs
+    q, k, v = _qkv(H=3, Hkv=3)
+    o, _ = O.attention(q, k, v, -1)
+    for h in range(3):
+        oh, _ = O.attention(q[:, :, h:h + 1], k[:, :, h:h + 1], v[:, :, h:h + 1], -1)
+        np.testing.assert_allclose(o[:, :, h:h + 1], oh, atol=1e-15)
+
+
+@pytest.mark.parametrize("window", [-1, 2])
+def test_causality_under_perturbation(window):
+    q, k, v = _qkv(T=14)
+    o, _ = O.attention(q, k, v, window)
+    j = 6
+    k2, v2 = k.copy(), v.copy()
+    k2[:, j] += 1.0
+    v2[:, j] -= 2.0
+    o2, _ = O.attention(q, k2, v2, window)
+    np.testing.assert_array_equal(o[:, :j], o2[:, :j])
+    if window >= 0:
+        np.testing.assert_array_equal(o[:, j + window + 1:], o2[:, j + window + 1:])
+    assert np.max(np.abs(o[:, j] - o2[:, j])) > 1e-3
+
+
+@pytest.mark.parametrize("window", [-1, 0, 3])
+def test_attention_backward_fd(window):
+    q, k, v = _qkv(B=1, T=7, H=4, Hkv=2, D=4)
+    w = RNG.standard_normal(q.shape)
+    o, P = O.attention(q, k, v, window)
+    dq, dk, dv = O.attention_backward(w, q, k, v, P)
+    fd_check(lambda z: float(np.sum(O.attention(z, k, v, window)[0] * w)), q, dq)
+    fd_check(lambda z: float(np.sum(O.attention(q, z, v, window)[0] * w)), k, dk)
+    fd_check(lambda z: float(np.sum(O.attention(q, k, z, window)[0] * w)), v, dv)
+
+
+# ------------------------------------------------------------ cross-entropy
+def test_ce_zero_head_closed_form():
+    N, C, V = 9, 12, 17
+    x = RNG.standard_normal((N, C))
+    y = RNG.integers(0, V, size=N)
+    loss, dx, dw, c = O.lm_head_ce(x, np.zeros((V, C)), y, 1e-6)
+    assert loss == pytest.approx(math.log(V), rel=1e-15)
+    onehot = np.zeros((N, V))
+    onehot[np.arange(N), y] = 1.0
+    np.testing.assert_allclose(c["dz"], (1.0 / V - onehot) / N, atol=1e-16)
+    assert np.all(dx == 0.0)
+
+
+def test_ce_rows_of_dz_sum_to_zero_and_fd():
+    N, C, V = 6, 10, 13
+    x = RNG.standard_normal((N, C))
+    W = RNG.standard_normal((V, C)) * 0.3
+    y = RNG.integers(0, V, size=N)
+    loss, dx, dw, c = O.lm_head_ce(x, W, y, 1e-6)
+    np.testing.assert_allclose(c["dz"].sum(1), 0.0, atol=1e-16)
+    fd_check(lambda z: O.lm_head_ce(z, W, y, 1e-6)[0], x, dx, rtol=1e-7)
+    fd_check(lambda z: O.lm_head_ce(x, z, y, 1e-6)[0], W, dw, rtol=1e-7)
+
+
+def test_ce_init_statistics():
+    # at init the normalised stream has unit RMS so logits are ~N(0, 0.02^2 C);
+    # E[loss] ~= ln V + 0.0002 C
+    N, C, V = 256, 128, 512
+    x = RNG.standard_normal((N, C))
+    W = RNG.standard_normal((V, C)) * 0.02
+    y = RNG.integers(0, V, size=N)
+    loss = O.lm_head_ce(x, W, y, 1e-6)[0]
+    assert abs(loss - (math.log(V) + 0.0002 * C)) < 0.05
+
+
+# --------------------------------------------------------------------- fp8
+def test_e4m3_grid_special_values():
+    vals = np.array([0.0, 1.0, 1.0625, 1.125, 1.1875, 448.0, 464.0, 470.0, 1e9, 2 ** -9,
+                     2 ** -10, 3 * 2 ** -11, -1.0625, 2 ** -6, 0.0009765625])
+    exp = np.array([0.0, 1.0, 1.0, 1.125, 1.25, 448.0, 448.0, 448.0, 448.0, 2 ** -9,
+                    0.0, 2 ** -9, -1.0, 2 ** -6, 0.0])
+    np.testing.assert_array_equal(O.e4m3_round(vals), exp)
+
+
+def test_e4m3_matches_torch_cast_on_all_bf16_in_range():
+    torch = pytest.importorskip("torch")
+    bits = np.arange(0, 1 << 16, dtype=np.uint32)
+    f = (bits << 16).view(np.float32).astype(np.float64)
+    ok = np.isfinite(f) & (np.abs(f) <= 464.0)   # torch's cast overflows to NaN above 464
+    f = f[ok]
+    ref = torch.from_numpy(f).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.e4m3_round(f), ref)
+
+
+def test_fp8_quant_dequant_error_bound():
+    x = RNG.standard_normal((64, 64)) * 5.0
+    y = O.fp8_quant_dequant(x)
+    s = np.max(np.abs(x)) / 448.0
+    # relative half-ulp 2^-4 on normals, absolute half-ulp 2^-10 * s on subnormals
+    assert np.all(np.abs(y - x) <= np.maximum(np.abs(x) * 2.0 ** -4, s * 2.0 ** -10) + 1e-15)
+    assert np.max(np.abs(y)) == pytest.approx(np.max(np.abs(x)), rel=1e-15)
+
+
+# ------------------------------------------------------ whole-step FD pins
+def _params(cfg, rng):
+    Q, KV = cfg.n_head * cfg.head_dim, cfg.n_kv_head * cfg.head_dim
+    C, F, V = cfg.C, cfg.mlp_hidden, cfg.vocab
+    s = 0.3
+    glob = {"wte": rng.standard_normal((V, C)), "w_lm": rng.standard_normal((V, C)) * s}
+    layers = []
+    for l in range(cfg.n_layer):
+        p = {"w_qkv": rng.standard_normal((Q + 2 * KV, C)) * s, "w_o": rng.standard_normal((C, Q)) * s,
+             "w_fc": rng.standard_normal((F, C)) * s, "w_proj": rng.standard_normal((C, F)) * s}
+        if cfg.extras:
+            p["resid_lambda"] = rng.uniform(0.5, 1.5)
+            p["x0_lambda"] = rng.uniform(0.5, 1.5)
+            if l % 2 == 1:
+                p["ve"] = rng.standard_normal((V, KV))
+                p["ve_gate"] = rng.standard_normal((cfg.n_kv_head, cfg.ve_gate_channels)) * s
+        layers.append(p)
+    if cfg.extras:
+        glob["smear_lambda"] = rng.uniform(0.5, 1.5)
+        glob["backout_lambda"] = rng.uniform(0.5, 1.5)
+        glob["smear_gate"] = rng.standard_normal(cfg.smear_channels) * s
+    ids = rng.integers(0, V, size=(cfg.B, cfg.T + 1))
+    return ids, glob, layers
+
+
+def _loss(cfg, ids, glob, layers):
+    return O.stack_forward_backward(cfg, ids, glob, layers)[0]
+
+
+def _fd_all(cfg, seed, h=1e-6, rtol=2e-6):
+    rng = np.random.default_rng(seed)
+    ids, glob, layers = _params(cfg, rng)
+    loss, grads, _ = O.stack_forward_backward(cfg, ids, glob, layers)
+    checked = 0
+
+    def check(get, setv, g):
+        nonlocal checked
+        base = np.array(get(), dtype=np.float64)
+        d = rng.standard_normal(base.shape)
+        setv(base + h * d)
+        lp = _loss(cfg, ids, glob, layers)
+        setv(base - h * d)
+        lm = _loss(cfg, ids, glob, layers)
+        setv(base)
+        num = (lp - lm) / (2 * h)
+        ana = float(np.sum(np.asarray(g) * d))
+        assert abs(num - ana) <= rtol * max(abs(ana), 1e-3), (num, ana)
+        checked += 1
+
+    for key in list(glob.keys()):
+        g = grads[key]
+        check(lambda k=key: glob[k], lambda v, k=key: glob.__setitem__(k, v), g)
+    for l, p in enumerate(layers):
+        for key in list(p.keys()):
+            g = grads["layers"][l][key]
+            check(lambda k=key, p=p: p[k], lambda v, k=key, p=p: p.__setitem__(k, v), g)
+    return checked
+
+
+def test_fd_whole_step_gqa_window():
+    assert _fd_all(tiny_cfg(), 1) == 2 + 2 * 4
+
+
+def test_fd_whole_step_mha_full():
+    assert _fd_all(tiny_cfg(n_kv_head=2, windows=(-1, -1), T=5), 2) == 10
+
+
+def test_fd_whole_step_window0_and_T1():
+    _fd_all(tiny_cfg(windows=(0, 1), T=4), 3)
+    _fd_all(tiny_cfg(T=1, B=3), 4)
+
+
+def test_fd_whole_step_extras():
+    cfg = tiny_cfg(C=48, n_head=3, n_kv_head=1, head_dim=16, mlp_hidden=96, vocab=13, T=5,
+                   n_layer=2, windows=(-1, 2), extras=True)
+    n = _fd_all(cfg, 5)
+    assert n == 5 + (4 + 2) + (4 + 2 + 2)
+
+
+def test_fd_whole_step_extras_four_layers():
+    # backout taken after block L/2 - 1 = 1, value embeddings on layers 1 and 3
+    cfg = tiny_cfg(C=48, n_head=3, n_kv_head=3, head_dim=16, mlp_hidden=96, vocab=9, T=4, B=1,
+                   n_layer=4, windows=(-1, 1, -1, 2), extras=True)
+    _fd_all(cfg, 6)

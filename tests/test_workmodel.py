@@ -1,0 +1,53 @@
+"""The FLOP/byte model against the run summary printed on the pages."""
+import os
+
+import pytest
+
+from gpt_decoder_block_amd.workmodel import (attn_pairs, flops_per_token, flops_per_token_pages,
+                                             matrix_params, step_flops)
+from seeded_inputs import workload
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "d24_run_summary.txt")
+
+
+def _summary():
+    out = {}
+    for line in open(GOLDEN):
+        if line.startswith("#") or not line.strip():
+            continue
+        k, v = line.split()
+        out[k] = v
+    return out
+
+
+def test_pages_flop_total_reproduced_exactly():
+    s = _summary()
+    steps = int(s["step"])
+    tokens = steps * 2 ** 19                      # 2 micro-steps of 8 GPUs x 16 x 2048
+    L, C, H, D, V, T = 24, 1536, 12, 128, 32768, 2048
+    # the data:param ratio of 12 fixes the token count from the matrix parameters
+    assert tokens == 12 * matrix_params(L, C, H, H, D, 4 * C, V)
+    # SSSL windows (short = T/2, long = T on every fourth layer), value-embedding
+    # gates (32 -> n_kv_head) on alternating layers
+    windows = [1024 if (l % 4) != 3 else -1 for l in range(L)]
+    ve_gate_params = (L // 2) * 32 * H
+    per_tok = flops_per_token_pages(L, C, H, H, D, 4 * C, V, T, windows, ve_gate_params)
+    assert repr(float(tokens * per_tok)) == repr(float(s["total_training_flops"]))
+    # one unit more per token changes the printed float
+    assert float(tokens * (per_tok + 1)) != float(s["total_training_flops"])
+
+
+def test_attn_pairs_brute_force():
+    for T in (1, 2, 7, 33):
+        for W in (-1, 0, 1, 5, T - 2, T - 1, T + 4):
+            brute = sum(1 for i in range(T) for j in range(T) if j <= i and (W < 0 or i - j <= W))
+            assert attn_pairs(T, W) == brute
+
+
+def test_d24_algorithmic_flops():
+    w = workload("d24")
+    per_tok = flops_per_token(w.n_layer, w.C, w.n_head, w.n_kv_head, w.head_dim,
+                              w.mlp_hidden, w.vocab, w.T, w.windows)
+    assert per_tok == 4775491584
+    sf = step_flops(w)
+    assert sf["total"] == pytest.approx(per_tok * w.B * w.T, rel=1e-15)
