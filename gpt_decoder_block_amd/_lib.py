@@ -1,0 +1,106 @@
+"""ctypes binding of libgdb.so (the C ABI declared in include/gdb.h).
+
+Argument marshalling only: torch tensors are turned into device pointers and
+the current HIP stream; every step of the computation runs in the library's
+HIP kernels.  Loading fails loudly if the library has not been built; there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdb.so")
+
+GDB_OK, GDB_EINVAL, GDB_EUNSUPPORTED, GDB_EHIP, GDB_EWORKSPACE = 0, -1, -2, -3, -4
+GDB_F32, GDB_BF16 = 0, 1
+
+c_void_p, c_int32, c_float, c_size_t = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+
+
+class BlockCfg(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("T", c_int32), ("C", c_int32),
+                ("n_head", c_int32), ("n_kv_head", c_int32), ("head_dim", c_int32),
+                ("mlp_hidden", c_int32), ("window", c_int32), ("dtype", c_int32),
+                ("mlp_fp8", c_int32), ("accumulate_wgrad", c_int32), ("eps", c_float)]
+
+
+class BlockWeights(ctypes.Structure):
+    _fields_ = [("w_qkv", c_void_p), ("w_o", c_void_p), ("w_fc", c_void_p), ("w_proj", c_void_p)]
+
+
+class BlockWgrads(ctypes.Structure):
+    _fields_ = [("dw_qkv", c_void_p), ("dw_o", c_void_p), ("dw_fc", c_void_p), ("dw_proj", c_void_p)]
+
+
+class GdbError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+        self.msg = msg
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+# name -> (restype, argtypes), in the order of include/gdb.h
+SIGNATURES = {
+    "gdb_abi_version": (c_int32, []),
+    "gdb_last_error": (ctypes.c_char_p, []),
+    "gdb_block_sizes": (c_int32, [ctypes.POINTER(BlockCfg), ctypes.POINTER(c_size_t),
+                                  ctypes.POINTER(c_size_t), ctypes.POINTER(c_size_t)]),
+    "gdb_rope_table_host": (c_int32, [c_int32, c_int32, ctypes.c_double, c_void_p]),
+    "gdb_embed_fwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "gdb_embed_bwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int32,
+                                c_void_p]),
+    "gdb_block_fwd": (c_int32, [ctypes.POINTER(BlockCfg), ctypes.POINTER(BlockWeights), c_void_p, c_void_p,
+                                c_void_p, c_void_p, c_void_p, c_void_p]),
+    "gdb_block_bwd": (c_int32, [ctypes.POINTER(BlockCfg), ctypes.POINTER(BlockWeights), c_void_p, c_void_p,
+                                c_void_p, c_void_p, ctypes.POINTER(BlockWgrads), c_void_p, c_void_p]),
+    "gdb_lm_head_ce_sizes": (c_int32, [c_int32, c_int32, c_int32, c_int32, ctypes.POINTER(c_size_t)]),
+    "gdb_lm_head_ce_fwd_bwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p,
+                                         c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
+    "gdb_rmsnorm_fwd": (c_int32, [c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "gdb_rmsnorm_bwd": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_void_p]),
+    "gdb_gemm_ws_bytes": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, ctypes.POINTER(c_size_t)]),
+    "gdb_gemm": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_int32,
+                           c_int32, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
+                           c_void_p]),
+    "gdb_qk_norm_rope_fwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_float, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, c_void_p]),
+    "gdb_qk_norm_rope_bwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_void_p]),
+    "gdb_attention_fwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                    c_int32, c_void_p, c_int32, c_void_p, c_void_p]),
+    "gdb_attention_bwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                    c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_int32,
+                                    c_void_p, c_void_p]),
+    "gdb_cross_entropy": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    c_void_p]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m gpt_decoder_block_amd.build` "
+                               "(the HIP library is required; there is no CPU fallback)")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def check(fn: str, status: int) -> None:
+    if status != GDB_OK:
+        raise GdbError(fn, status, lib().gdb_last_error().decode())
+
+
+def call(fn: str, *args) -> None:
+    check(fn, getattr(lib(), fn)(*args))

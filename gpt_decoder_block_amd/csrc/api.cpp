@@ -1,0 +1,501 @@
+// C ABI of the decoder-block hot path: argument validation, layout of the
+// caller-provided saved/workspace buffers, and the composition of the kernels
+// into block forward, block backward and the fused lm_head + cross-entropy.
+// Validation happens before any HIP call, so every argument error is
+// reported without touching a device.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+#include <string>
+
+#include "../../include/gdb.h"
+#include "kernels.h"
+
+using namespace gdb;
+
+namespace {
+
+thread_local std::string g_err;
+
+gdb_status fail(gdb_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIPCHK(expr)                                                                    \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess) return fail(GDB_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+#define CHECK_PTR(p)                                                                       \
+  do {                                                                                     \
+    if ((p) == nullptr) return fail(GDB_EINVAL, "%s is NULL", #p);                         \
+    if (((uintptr_t)(p)) & 15) return fail(GDB_EINVAL, "%s is not 16-byte aligned", #p);  \
+  } while (0)
+
+// Sequential carving of a caller buffer into 256-byte aligned pieces; with a
+// NULL base it only measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <typename T>
+  T* take(size_t bytes) {
+    off = (off + 255) & ~(size_t)255;
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+struct BlockDims {
+  int B, T, N, C, H, Hkv, D, Q, KV, W3, F, window, dt, s;
+  float eps;
+};
+
+gdb_status check_cfg(const gdb_block_cfg* c, BlockDims* d) {
+  if (!c) return fail(GDB_EINVAL, "cfg is NULL");
+  if (c->B <= 0 || c->T <= 0 || c->C <= 0) return fail(GDB_EINVAL, "B, T, C must be positive (got %d, %d, %d)", c->B, c->T, c->C);
+  if (c->dtype != GDB_F32 && c->dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", c->dtype);
+  if (c->n_head <= 0 || c->n_kv_head <= 0) return fail(GDB_EINVAL, "n_head and n_kv_head must be positive");
+  if (c->n_head % c->n_kv_head != 0) return fail(GDB_EINVAL, "n_head (%d) must be a multiple of n_kv_head (%d)", c->n_head, c->n_kv_head);
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(GDB_EUNSUPPORTED, "head_dim %d not supported (64 or 128)", c->head_dim);
+  if (c->dtype == GDB_BF16 && c->head_dim != 128) return fail(GDB_EUNSUPPORTED, "bf16 attention needs head_dim 128 (got %d)", c->head_dim);
+  if (c->n_head * c->head_dim != c->C) return fail(GDB_EUNSUPPORTED, "n_head*head_dim (%d) must equal C (%d)", c->n_head * c->head_dim, c->C);
+  if (c->C % 8 || c->mlp_hidden <= 0 || c->mlp_hidden % 8) return fail(GDB_EINVAL, "C and mlp_hidden must be positive multiples of 8");
+  if (c->window < -1) return fail(GDB_EINVAL, "window must be >= -1 (got %d)", c->window);
+  if (c->mlp_fp8) return fail(GDB_EUNSUPPORTED, "mlp_fp8 is not available in this build");
+  if (!(c->eps > 0.f) || !std::isfinite(c->eps)) return fail(GDB_EINVAL, "eps must be positive and finite");
+  if ((long long)c->B * c->T > (1LL << 30)) return fail(GDB_EINVAL, "B*T too large");
+  d->B = c->B; d->T = c->T; d->N = c->B * c->T; d->C = c->C;
+  d->H = c->n_head; d->Hkv = c->n_kv_head; d->D = c->head_dim;
+  d->Q = d->H * d->D; d->KV = d->Hkv * d->D; d->W3 = d->Q + 2 * d->KV;
+  d->F = c->mlp_hidden; d->window = c->window >= c->T - 1 ? -1 : c->window;
+  d->dt = c->dtype; d->s = dt_size(c->dtype); d->eps = c->eps;
+  return GDB_OK;
+}
+
+struct Saved {
+  void *xn1, *qkvh, *o, *xn2, *u, *h;
+  float *r1, *rqk, *lse, *r2;
+};
+struct WsFwd {
+  void *qkv, *x_mid;
+};
+struct WsBwd {
+  void *du, *dxn, *dx_mid, *dout, *dqkv;
+  float *delta, *partial;
+};
+
+void carve_saved(const BlockDims& d, Carver& c, Saved& s) {
+  const size_t N = d.N;
+  s.xn1 = c.take<char>(N * d.C * d.s);
+  s.r1 = c.take<float>(N * 4);
+  s.qkvh = c.take<char>(N * d.W3 * d.s);
+  s.rqk = c.take<float>(N * (d.H + d.Hkv) * 4);
+  s.o = c.take<char>(N * d.Q * d.s);
+  s.lse = c.take<float>(N * d.H * 4);
+  s.xn2 = c.take<char>(N * d.C * d.s);
+  s.r2 = c.take<float>(N * 4);
+  s.u = c.take<char>(N * d.F * d.s);
+  s.h = c.take<char>(N * d.F * d.s);
+}
+void carve_fwd(const BlockDims& d, Carver& c, WsFwd& w) {
+  w.qkv = c.take<char>((size_t)d.N * d.W3 * d.s);
+  w.x_mid = c.take<char>((size_t)d.N * d.C * d.s);
+}
+size_t wgrad_partial_floats(const BlockDims& d) {
+  size_t m = 0;
+  const int shapes[4][2] = {{d.C, d.F}, {d.F, d.C}, {d.C, d.Q}, {d.W3, d.C}};
+  for (auto& sh : shapes) {
+    const int sp = gemm_splits(d.dt, sh[0], sh[1], d.N, EPI_F32);
+    if (sp > 1) m = std::max(m, (size_t)sp * sh[0] * sh[1]);
+  }
+  return m;
+}
+void carve_bwd(const BlockDims& d, Carver& c, WsBwd& w) {
+  const size_t N = d.N;
+  w.du = c.take<char>(N * d.F * d.s);
+  w.dxn = c.take<char>(N * d.C * d.s);
+  w.dx_mid = c.take<char>(N * d.C * d.s);
+  w.dout = c.take<char>(N * d.Q * d.s);
+  w.dqkv = c.take<char>(N * d.W3 * d.s);
+  w.delta = c.take<float>(N * d.H * 4);
+  w.partial = c.take<float>(wgrad_partial_floats(d) * 4);
+}
+
+GemmArgs gemm_args(const void* A, bool ak, int lda, const void* B, bool bk, int ldb, int M, int N, int K,
+                   int epi, void* C, int ldc) {
+  GemmArgs g{};
+  g.A = A; g.B = B; g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb;
+  g.a_kmajor = ak; g.b_kmajor = bk; g.epi = epi; g.C = C; g.ldc = ldc;
+  g.splits = 1;
+  return g;
+}
+
+// fp32 weight gradient C[M, N] (+)= sum_k A[k, m] B[k, n] (A, B token-major)
+hipError_t wgrad(int dt, const void* A, int lda, const void* B, int ldb, int M, int N, int K, float* C,
+                 int accumulate, float* partial, hipStream_t s) {
+  GemmArgs g = gemm_args(A, false, lda, B, false, ldb, M, N, K, EPI_F32, C, N);
+  g.accumulate = accumulate;
+  g.splits = gemm_splits(dt, M, N, K, EPI_F32);
+  g.partial = partial;
+  hipError_t e = gemm(dt, g, s);
+  if (e != hipSuccess || g.splits == 1) return e;
+  return splitk_reduce(partial, C, g.splits, (size_t)M * N, accumulate, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gdb_abi_version(void) { return GDB_ABI_VERSION; }
+
+const char* gdb_last_error(void) { return g_err.c_str(); }
+
+gdb_status gdb_block_sizes(const gdb_block_cfg* cfg, size_t* saved_bytes, size_t* ws_fwd_bytes,
+                           size_t* ws_bwd_bytes) {
+  BlockDims d;
+  gdb_status st = check_cfg(cfg, &d);
+  if (st != GDB_OK) return st;
+  Saved sv;
+  WsFwd wf;
+  WsBwd wb;
+  Carver c1(nullptr), c2(nullptr), c3(nullptr);
+  carve_saved(d, c1, sv);
+  carve_fwd(d, c2, wf);
+  carve_bwd(d, c3, wb);
+  if (saved_bytes) *saved_bytes = c1.off;
+  if (ws_fwd_bytes) *ws_fwd_bytes = c2.off;
+  if (ws_bwd_bytes) *ws_bwd_bytes = c3.off;
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_rope_table_host(int32_t T, int32_t head_dim, double base, float* out_host) {
+  if (T <= 0 || head_dim <= 0 || head_dim % 2) return fail(GDB_EINVAL, "T and head_dim must be positive, head_dim even");
+  if (!(base > 1.0)) return fail(GDB_EINVAL, "rope base must be > 1");
+  if (!out_host) return fail(GDB_EINVAL, "out_host is NULL");
+  const int hd = head_dim / 2;
+  for (int t = 0; t < T; ++t)
+    for (int j = 0; j < hd; ++j) {
+      const double th = (double)t * std::pow(base, -2.0 * j / head_dim);
+      out_host[((size_t)t * hd + j) * 2] = (float)std::cos(th);
+      out_host[((size_t)t * hd + j) * 2 + 1] = (float)std::sin(th);
+    }
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_embed_fwd(int32_t N, int32_t C, int32_t V, int32_t dtype, const int32_t* ids, const void* wte,
+                         void* x0, void* stream) {
+  if (N < 0 || C <= 0 || V <= 0 || C % 8) return fail(GDB_EINVAL, "bad sizes N=%d C=%d V=%d (C multiple of 8)", N, C, V);
+  if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
+  if (N == 0) { g_err.clear(); return GDB_OK; }
+  CHECK_PTR(ids); CHECK_PTR(wte); CHECK_PTR(x0);
+  HIPCHK(embed_fwd(dtype, ids, wte, x0, N, C, V, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_embed_bwd(int32_t N, int32_t C, int32_t V, int32_t dtype, const int32_t* ids, const void* dx0,
+                         float* dwte, int32_t accumulate, void* stream) {
+  if (N < 0 || C <= 0 || V <= 0 || C % 8) return fail(GDB_EINVAL, "bad sizes N=%d C=%d V=%d (C multiple of 8)", N, C, V);
+  if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
+  CHECK_PTR(dwte);
+  if (N > 0) { CHECK_PTR(ids); CHECK_PTR(dx0); }
+  HIPCHK(embed_bwd(dtype, ids, dx0, dwte, N, C, V, accumulate, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, const float* rope_tab,
+                         const void* x_in, void* x_out, void* saved, void* ws, void* stream) {
+  BlockDims d;
+  gdb_status st = check_cfg(cfg, &d);
+  if (st != GDB_OK) return st;
+  if (!w) return fail(GDB_EINVAL, "weights is NULL");
+  CHECK_PTR(w->w_qkv); CHECK_PTR(w->w_o); CHECK_PTR(w->w_fc); CHECK_PTR(w->w_proj);
+  CHECK_PTR(rope_tab); CHECK_PTR(x_in); CHECK_PTR(x_out); CHECK_PTR(saved); CHECK_PTR(ws);
+  if (x_in == x_out) return fail(GDB_EINVAL, "x_out must not alias x_in");
+  hipStream_t s = (hipStream_t)stream;
+  Saved sv;
+  WsFwd wf;
+  Carver c1(saved), c2(ws);
+  carve_saved(d, c1, sv);
+  carve_fwd(d, c2, wf);
+  const int dt = d.dt, N = d.N;
+
+  HIPCHK(rmsnorm_fwd(dt, x_in, sv.xn1, sv.r1, N, d.C, d.eps, s));
+  HIPCHK(gemm(dt, gemm_args(sv.xn1, true, d.C, w->w_qkv, true, d.C, N, d.W3, d.C, EPI_STORE, wf.qkv, d.W3), s));
+  HIPCHK(qk_norm_rope_fwd(dt, wf.qkv, sv.qkvh, sv.rqk, rope_tab, d.B, d.T, d.H, d.Hkv, d.D, d.eps, s));
+  AttnArgs at{};
+  at.B = d.B; at.T = d.T; at.H = d.H; at.Hkv = d.Hkv; at.D = d.D; at.window = d.window;
+  at.qkv = sv.qkvh; at.ld = d.W3; at.o = sv.o; at.ldo = d.Q; at.lse = sv.lse;
+  HIPCHK(attn_fwd(dt, at, s));
+  GemmArgs g = gemm_args(sv.o, true, d.Q, w->w_o, true, d.Q, N, d.C, d.Q, EPI_RESID, wf.x_mid, d.C);
+  g.R = x_in; g.ldr = d.C;
+  HIPCHK(gemm(dt, g, s));
+  HIPCHK(rmsnorm_fwd(dt, wf.x_mid, sv.xn2, sv.r2, N, d.C, d.eps, s));
+  g = gemm_args(sv.xn2, true, d.C, w->w_fc, true, d.C, N, d.F, d.C, EPI_RELU2, sv.u, d.F);
+  g.C2 = sv.h;
+  HIPCHK(gemm(dt, g, s));
+  g = gemm_args(sv.h, true, d.F, w->w_proj, true, d.F, N, d.C, d.F, EPI_RESID, x_out, d.C);
+  g.R = wf.x_mid; g.ldr = d.C;
+  HIPCHK(gemm(dt, g, s));
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_block_bwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, const float* rope_tab,
+                         const void* saved, const void* dx_out, void* dx_in, const gdb_block_wgrads* dw, void* ws,
+                         void* stream) {
+  BlockDims d;
+  gdb_status st = check_cfg(cfg, &d);
+  if (st != GDB_OK) return st;
+  if (!w || !dw) return fail(GDB_EINVAL, "weights or wgrads is NULL");
+  CHECK_PTR(w->w_qkv); CHECK_PTR(w->w_o); CHECK_PTR(w->w_fc); CHECK_PTR(w->w_proj);
+  CHECK_PTR(dw->dw_qkv); CHECK_PTR(dw->dw_o); CHECK_PTR(dw->dw_fc); CHECK_PTR(dw->dw_proj);
+  CHECK_PTR(rope_tab); CHECK_PTR(saved); CHECK_PTR(dx_out); CHECK_PTR(dx_in); CHECK_PTR(ws);
+  hipStream_t s = (hipStream_t)stream;
+  Saved sv;
+  WsBwd wb;
+  Carver c1((void*)saved), c2(ws);
+  carve_saved(d, c1, sv);
+  carve_bwd(d, c2, wb);
+  const int dt = d.dt, N = d.N, acc = cfg->accumulate_wgrad ? 1 : 0;
+
+  // MLP
+  GemmArgs g = gemm_args(dx_out, true, d.C, w->w_proj, false, d.F, N, d.F, d.C, EPI_DRELU2, wb.du, d.F);
+  g.R = sv.u; g.ldr = d.F;
+  HIPCHK(gemm(dt, g, s));
+  HIPCHK(wgrad(dt, dx_out, d.C, sv.h, d.F, d.C, d.F, N, dw->dw_proj, acc, wb.partial, s));
+  HIPCHK(gemm(dt, gemm_args(wb.du, true, d.F, w->w_fc, false, d.C, N, d.C, d.F, EPI_STORE, wb.dxn, d.C), s));
+  HIPCHK(wgrad(dt, wb.du, d.F, sv.xn2, d.C, d.F, d.C, N, dw->dw_fc, acc, wb.partial, s));
+  HIPCHK(rmsnorm_bwd(dt, wb.dxn, sv.xn2, sv.r2, dx_out, wb.dx_mid, N, d.C, s));
+  // attention output projection
+  HIPCHK(gemm(dt, gemm_args(wb.dx_mid, true, d.C, w->w_o, false, d.Q, N, d.Q, d.C, EPI_STORE, wb.dout, d.Q), s));
+  HIPCHK(wgrad(dt, wb.dx_mid, d.C, sv.o, d.Q, d.C, d.Q, N, dw->dw_o, acc, wb.partial, s));
+  // attention
+  AttnArgs at{};
+  at.B = d.B; at.T = d.T; at.H = d.H; at.Hkv = d.Hkv; at.D = d.D; at.window = d.window;
+  at.qkv = sv.qkvh; at.ld = d.W3; at.o = sv.o; at.ldo = d.Q; at.lse = sv.lse;
+  at.dout = wb.dout; at.lddo = d.Q; at.dqkv = wb.dqkv; at.lddq = d.W3; at.delta = wb.delta;
+  HIPCHK(attn_bwd(dt, at, s));
+  HIPCHK(qk_norm_rope_bwd(dt, wb.dqkv, sv.qkvh, sv.rqk, rope_tab, d.B, d.T, d.H, d.Hkv, d.D, s));
+  // QKV projection
+  HIPCHK(gemm(dt, gemm_args(wb.dqkv, true, d.W3, w->w_qkv, false, d.C, N, d.C, d.W3, EPI_STORE, wb.dxn, d.C), s));
+  HIPCHK(wgrad(dt, wb.dqkv, d.W3, sv.xn1, d.C, d.W3, d.C, N, dw->dw_qkv, acc, wb.partial, s));
+  HIPCHK(rmsnorm_bwd(dt, wb.dxn, sv.xn1, sv.r1, wb.dx_mid, dx_in, N, d.C, s));
+  g_err.clear();
+  return GDB_OK;
+}
+
+namespace {
+struct HeadWs {
+  void *xf, *z, *dxf;
+  float *rf, *row_loss, *partial;
+};
+gdb_status check_head(int N, int C, int V, int dtype) {
+  if (N <= 0 || C <= 0 || V <= 0) return fail(GDB_EINVAL, "N, C, V must be positive (got %d, %d, %d)", N, C, V);
+  if (C % 8 || V % 8) return fail(GDB_EINVAL, "C and V must be multiples of 8");
+  if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
+  return GDB_OK;
+}
+void carve_head(int N, int C, int V, int dt, Carver& c, HeadWs& h) {
+  const int s = dt_size(dt);
+  h.xf = c.take<char>((size_t)N * C * s);
+  h.rf = c.take<float>((size_t)N * 4);
+  h.z = c.take<char>((size_t)N * V * s);
+  h.row_loss = c.take<float>((size_t)N * 4);
+  h.dxf = c.take<char>((size_t)N * C * s);
+  const int sp = gemm_splits(dt, V, C, N, EPI_F32);
+  h.partial = c.take<float>(sp > 1 ? (size_t)sp * V * C * 4 : 0);
+}
+}  // namespace
+
+gdb_status gdb_lm_head_ce_sizes(int32_t N, int32_t C, int32_t V, int32_t dtype, size_t* ws_bytes) {
+  gdb_status st = check_head(N, C, V, dtype);
+  if (st != GDB_OK) return st;
+  HeadWs h;
+  Carver c(nullptr);
+  carve_head(N, C, V, dtype, c, h);
+  if (ws_bytes) *ws_bytes = c.off;
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_lm_head_ce_fwd_bwd(int32_t N, int32_t C, int32_t V, int32_t dtype, float eps, const void* x,
+                                  const void* w_lm, const int32_t* targets, float* loss, void* dx, float* dw_lm,
+                                  int32_t accumulate, void* ws, void* stream) {
+  gdb_status st = check_head(N, C, V, dtype);
+  if (st != GDB_OK) return st;
+  if (!(eps > 0.f) || !std::isfinite(eps)) return fail(GDB_EINVAL, "eps must be positive and finite");
+  CHECK_PTR(x); CHECK_PTR(w_lm); CHECK_PTR(targets); CHECK_PTR(loss); CHECK_PTR(dx); CHECK_PTR(dw_lm); CHECK_PTR(ws);
+  hipStream_t s = (hipStream_t)stream;
+  HeadWs h;
+  Carver c(ws);
+  carve_head(N, C, V, dtype, c, h);
+  HIPCHK(rmsnorm_fwd(dtype, x, h.xf, h.rf, N, C, eps, s));
+  HIPCHK(gemm(dtype, gemm_args(h.xf, true, C, w_lm, true, C, N, V, C, EPI_STORE, h.z, V), s));
+  HIPCHK(ce_fwd_bwd(dtype, h.z, targets, h.row_loss, N, V, s));
+  HIPCHK(loss_reduce(h.row_loss, loss, N, s));
+  HIPCHK(gemm(dtype, gemm_args(h.z, true, V, w_lm, false, C, N, C, V, EPI_STORE, h.dxf, C), s));
+  HIPCHK(wgrad(dtype, h.z, V, h.xf, C, V, C, N, dw_lm, accumulate ? 1 : 0, h.partial, s));
+  HIPCHK(rmsnorm_bwd(dtype, h.dxf, h.xf, h.rf, nullptr, dx, N, C, s));
+  g_err.clear();
+  return GDB_OK;
+}
+
+// ----------------------------------------------------------- building blocks
+gdb_status gdb_rmsnorm_fwd(int32_t N, int32_t C, int32_t dtype, float eps, const void* x, void* xn, float* r,
+                           void* stream) {
+  if (N < 0 || C <= 0 || C % 8) return fail(GDB_EINVAL, "bad sizes N=%d C=%d (C multiple of 8)", N, C);
+  if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
+  if (!(eps > 0.f) || !std::isfinite(eps)) return fail(GDB_EINVAL, "eps must be positive and finite");
+  CHECK_PTR(x); CHECK_PTR(xn); CHECK_PTR(r);
+  HIPCHK(rmsnorm_fwd(dtype, x, xn, r, N, C, eps, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_rmsnorm_bwd(int32_t N, int32_t C, int32_t dtype, const void* dxn, const void* xn, const float* r,
+                           const void* dres, void* dx, void* stream) {
+  if (N < 0 || C <= 0 || C % 8) return fail(GDB_EINVAL, "bad sizes N=%d C=%d (C multiple of 8)", N, C);
+  if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
+  CHECK_PTR(dxn); CHECK_PTR(xn); CHECK_PTR(r); CHECK_PTR(dx);
+  if (dres && (((uintptr_t)dres) & 15)) return fail(GDB_EINVAL, "dres is not 16-byte aligned");
+  HIPCHK(rmsnorm_bwd(dtype, dxn, xn, r, dres, dx, N, C, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_gemm_ws_bytes(int32_t dtype, int32_t M, int32_t N, int32_t K, int32_t epi, size_t* ws_bytes) {
+  if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
+  if (M < 0 || N < 0 || K < 0) return fail(GDB_EINVAL, "negative size");
+  if (epi < 0 || epi > EPI_F32) return fail(GDB_EINVAL, "unknown epilogue %d", epi);
+  const int sp = gemm_splits(dtype, M, N, K, epi);
+  if (ws_bytes) *ws_bytes = sp > 1 ? (size_t)sp * M * N * 4 : 0;
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A, int32_t a_kmajor, int32_t lda,
+                    const void* B, int32_t b_kmajor, int32_t ldb, int32_t epi, void* C, int32_t ldc, const void* R,
+                    int32_t ldr, void* C2, int32_t accumulate, void* ws, void* stream) {
+  if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
+  if (M < 0 || N < 0 || K < 0) return fail(GDB_EINVAL, "negative size");
+  if (epi < 0 || epi > EPI_F32) return fail(GDB_EINVAL, "unknown epilogue %d", epi);
+  if (N % 8 || ldc % 8 || lda % 8 || ldb % 8) return fail(GDB_EINVAL, "N, lda, ldb, ldc must be multiples of 8");
+  if (a_kmajor ? (K % 8 != 0) : (M % 8 != 0)) return fail(GDB_EINVAL, "the contiguous dimension of A must be a multiple of 8");
+  if (b_kmajor && K % 8) return fail(GDB_EINVAL, "K must be a multiple of 8 when B is K-major");
+  if (lda < (a_kmajor ? K : M) || ldb < (b_kmajor ? K : N) || ldc < N) return fail(GDB_EINVAL, "leading dimension too small");
+  if (M == 0 || N == 0) { g_err.clear(); return GDB_OK; }
+  CHECK_PTR(A); CHECK_PTR(B); CHECK_PTR(C);
+  if (epi == EPI_RESID || epi == EPI_DRELU2) {
+    CHECK_PTR(R);
+    if (ldr % 8 || ldr < N) return fail(GDB_EINVAL, "ldr must be a multiple of 8 and >= N");
+  }
+  if (epi == EPI_RELU2) CHECK_PTR(C2);
+  if (epi == EPI_F32 && ldc != N) return fail(GDB_EINVAL, "fp32 output needs ldc == N");
+  GemmArgs g = gemm_args(A, a_kmajor != 0, lda, B, b_kmajor != 0, ldb, M, N, K, epi, C, ldc);
+  g.R = R; g.ldr = ldr; g.C2 = C2; g.accumulate = accumulate ? 1 : 0;
+  if (epi == EPI_F32) {
+    g.splits = gemm_splits(dtype, M, N, K, epi);
+    if (g.splits > 1) CHECK_PTR(ws);
+    g.partial = (float*)ws;
+    HIPCHK(gemm(dtype, g, (hipStream_t)stream));
+    if (g.splits > 1) HIPCHK(splitk_reduce(g.partial, (float*)C, g.splits, (size_t)M * N, g.accumulate, (hipStream_t)stream));
+  } else {
+    HIPCHK(gemm(dtype, g, (hipStream_t)stream));
+  }
+  g_err.clear();
+  return GDB_OK;
+}
+
+namespace {
+gdb_status check_attn(int B, int T, int H, int Hkv, int D, int window, int dtype) {
+  if (B <= 0 || T <= 0 || H <= 0 || Hkv <= 0) return fail(GDB_EINVAL, "B, T, H, Hkv must be positive");
+  if (H % Hkv) return fail(GDB_EINVAL, "H (%d) must be a multiple of Hkv (%d)", H, Hkv);
+  if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
+  if (D != 64 && D != 128) return fail(GDB_EUNSUPPORTED, "head_dim %d not supported", D);
+  if (dtype == GDB_BF16 && D != 128) return fail(GDB_EUNSUPPORTED, "bf16 attention needs head_dim 128");
+  if (window < -1) return fail(GDB_EINVAL, "window must be >= -1");
+  return GDB_OK;
+}
+}  // namespace
+
+gdb_status gdb_qk_norm_rope_fwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t D, int32_t dtype, float eps,
+                                const void* qkv, void* out, float* rinv, const float* rope_tab, void* stream) {
+  gdb_status st = check_attn(B, T, H, Hkv, D, -1, dtype);
+  if (st != GDB_OK) return st;
+  if (!(eps > 0.f) || !std::isfinite(eps)) return fail(GDB_EINVAL, "eps must be positive and finite");
+  CHECK_PTR(qkv); CHECK_PTR(out); CHECK_PTR(rinv); CHECK_PTR(rope_tab);
+  if (qkv == out) return fail(GDB_EINVAL, "out must not alias qkv");
+  HIPCHK(qk_norm_rope_fwd(dtype, qkv, out, rinv, rope_tab, B, T, H, Hkv, D, eps, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_qk_norm_rope_bwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t D, int32_t dtype, void* d,
+                                const void* qkvh, const float* rinv, const float* rope_tab, void* stream) {
+  gdb_status st = check_attn(B, T, H, Hkv, D, -1, dtype);
+  if (st != GDB_OK) return st;
+  CHECK_PTR(d); CHECK_PTR(qkvh); CHECK_PTR(rinv); CHECK_PTR(rope_tab);
+  HIPCHK(qk_norm_rope_bwd(dtype, d, qkvh, rinv, rope_tab, B, T, H, Hkv, D, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_attention_fwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t D, int32_t window, int32_t dtype,
+                             const void* qkv, int32_t ld, void* o, int32_t ldo, float* lse, void* stream) {
+  gdb_status st = check_attn(B, T, H, Hkv, D, window, dtype);
+  if (st != GDB_OK) return st;
+  if (ld < (H + 2 * Hkv) * D || ld % 8 || ldo < H * D || ldo % 8) return fail(GDB_EINVAL, "bad leading dimension");
+  CHECK_PTR(qkv); CHECK_PTR(o); CHECK_PTR(lse);
+  AttnArgs at{};
+  at.B = B; at.T = T; at.H = H; at.Hkv = Hkv; at.D = D; at.window = window >= T - 1 ? -1 : window;
+  at.qkv = qkv; at.ld = ld; at.o = o; at.ldo = ldo; at.lse = lse;
+  HIPCHK(attn_fwd(dtype, at, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_attention_bwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t D, int32_t window, int32_t dtype,
+                             const void* qkv, int32_t ld, const void* o, int32_t ldo, const float* lse,
+                             const void* dout, int32_t lddo, void* dqkv, int32_t lddq, float* delta, void* stream) {
+  gdb_status st = check_attn(B, T, H, Hkv, D, window, dtype);
+  if (st != GDB_OK) return st;
+  if (ld < (H + 2 * Hkv) * D || ld % 8 || ldo < H * D || ldo % 8 || lddo < H * D || lddo % 8 ||
+      lddq < (H + 2 * Hkv) * D || lddq % 8)
+    return fail(GDB_EINVAL, "bad leading dimension");
+  CHECK_PTR(qkv); CHECK_PTR(o); CHECK_PTR(lse); CHECK_PTR(dout); CHECK_PTR(dqkv); CHECK_PTR(delta);
+  AttnArgs at{};
+  at.B = B; at.T = T; at.H = H; at.Hkv = Hkv; at.D = D; at.window = window >= T - 1 ? -1 : window;
+  at.qkv = qkv; at.ld = ld; at.o = (void*)o; at.ldo = ldo; at.lse = (float*)lse;
+  at.dout = dout; at.lddo = lddo; at.dqkv = dqkv; at.lddq = lddq; at.delta = delta;
+  HIPCHK(attn_bwd(dtype, at, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_cross_entropy(int32_t N, int32_t V, int32_t dtype, void* z, const int32_t* targets, float* row_loss,
+                             float* loss, void* stream) {
+  if (N <= 0 || V <= 0 || V % 8) return fail(GDB_EINVAL, "N must be positive, V a positive multiple of 8");
+  if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
+  CHECK_PTR(z); CHECK_PTR(targets); CHECK_PTR(row_loss); CHECK_PTR(loss);
+  HIPCHK(ce_fwd_bwd(dtype, z, targets, row_loss, N, V, (hipStream_t)stream));
+  HIPCHK(loss_reduce(row_loss, loss, N, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
+}  // extern "C"

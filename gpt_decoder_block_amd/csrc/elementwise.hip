@@ -1,0 +1,477 @@
+// Bandwidth-bound kernels: RMSNorm forward/backward, embedding gather/scatter,
+// QK RMS-norm + rotary embedding forward/backward, fused softmax cross-entropy,
+// deterministic loss and split-K reductions.
+//
+// Each kernel reads and writes every element once with 16-byte vector
+// accesses (rows are multiples of 8 elements); per-row statistics are
+// wavefront or workgroup reductions in fp32.
+#include "common.h"
+#include "kernels.h"
+
+namespace gdb {
+
+// ------------------------------------------------------------------- fill
+__global__ __launch_bounds__(256) void fill_f32_k(float* p, size_t n, float v) {
+  size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  size_t stride = (size_t)gridDim.x * 256 * 4;
+  for (; i + 3 < n; i += stride) {
+    f32x4 q = {v, v, v, v};
+    *(f32x4*)(p + i) = q;
+  }
+  if (i < n)
+    for (size_t j = i; j < n; ++j) p[j] = v;
+}
+
+hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 1023) / 1024;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(fill_f32_k, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- RMSNorm
+// One wavefront per row; up to MAXV 16-byte vectors per lane stay in registers
+// (C <= 64*MAXV*VN), longer rows are streamed twice.
+constexpr int RMS_MAXV = 4;
+
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_k(const T* __restrict__ x, T* __restrict__ xn,
+                                                      float* __restrict__ r, int N, int C, float eps) {
+  constexpr int VN = V16<T>::n;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (row >= N) return;
+  const T* xr = x + (size_t)row * C;
+  T* yr = xn + (size_t)row * C;
+  const int nv = C / VN;
+  float ss = 0.f;
+  if (nv <= 64 * RMS_MAXV) {
+    float v[RMS_MAXV][VN];
+#pragma unroll
+    for (int i = 0; i < RMS_MAXV; ++i) {
+      const int vi = l + 64 * i;
+      if (vi < nv) {
+        ld16(xr + vi * VN, v[i]);
+#pragma unroll
+        for (int e = 0; e < VN; ++e) ss += v[i][e] * v[i][e];
+      }
+    }
+    const float ri = rsqrtf(wave_sum(ss) / (float)C + eps);
+#pragma unroll
+    for (int i = 0; i < RMS_MAXV; ++i) {
+      const int vi = l + 64 * i;
+      if (vi < nv) {
+#pragma unroll
+        for (int e = 0; e < VN; ++e) v[i][e] *= ri;
+        st16(yr + vi * VN, v[i]);
+      }
+    }
+    if (l == 0) r[row] = ri;
+  } else {
+    for (int vi = l; vi < nv; vi += 64) {
+      float v[VN];
+      ld16(xr + vi * VN, v);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) ss += v[e] * v[e];
+    }
+    const float ri = rsqrtf(wave_sum(ss) / (float)C + eps);
+    for (int vi = l; vi < nv; vi += 64) {
+      float v[VN];
+      ld16(xr + vi * VN, v);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) v[e] *= ri;
+      st16(yr + vi * VN, v);
+    }
+    if (l == 0) r[row] = ri;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_k(const T* __restrict__ dy, const T* __restrict__ y,
+                                                      const float* __restrict__ r, const T* dres, T* dx,
+                                                      int N, int C) {
+  constexpr int VN = V16<T>::n;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (row >= N) return;
+  const size_t off = (size_t)row * C;
+  const int nv = C / VN;
+  const float ri = r[row];
+  float dot = 0.f;
+  if (nv <= 64 * RMS_MAXV) {
+    float g[RMS_MAXV][VN], h[RMS_MAXV][VN];
+#pragma unroll
+    for (int i = 0; i < RMS_MAXV; ++i) {
+      const int vi = l + 64 * i;
+      if (vi < nv) {
+        ld16(dy + off + vi * VN, g[i]);
+        ld16(y + off + vi * VN, h[i]);
+#pragma unroll
+        for (int e = 0; e < VN; ++e) dot += g[i][e] * h[i][e];
+      }
+    }
+    const float m = wave_sum(dot) / (float)C;
+#pragma unroll
+    for (int i = 0; i < RMS_MAXV; ++i) {
+      const int vi = l + 64 * i;
+      if (vi < nv) {
+        float o[VN], rs[VN];
+        if (dres) ld16(dres + off + vi * VN, rs);
+#pragma unroll
+        for (int e = 0; e < VN; ++e) o[e] = ri * (g[i][e] - h[i][e] * m) + (dres ? rs[e] : 0.f);
+        st16(dx + off + vi * VN, o);
+      }
+    }
+  } else {
+    for (int vi = l; vi < nv; vi += 64) {
+      float g[VN], h[VN];
+      ld16(dy + off + vi * VN, g);
+      ld16(y + off + vi * VN, h);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) dot += g[e] * h[e];
+    }
+    const float m = wave_sum(dot) / (float)C;
+    for (int vi = l; vi < nv; vi += 64) {
+      float g[VN], h[VN], o[VN], rs[VN];
+      ld16(dy + off + vi * VN, g);
+      ld16(y + off + vi * VN, h);
+      if (dres) ld16(dres + off + vi * VN, rs);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) o[e] = ri * (g[e] - h[e] * m) + (dres ? rs[e] : 0.f);
+      st16(dx + off + vi * VN, o);
+    }
+  }
+}
+
+hipError_t rmsnorm_fwd(int dt, const void* x, void* xn, float* r, int N, int C, float eps, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  dim3 g((N + 3) / 4), b(256);
+  if (dt == BF16)
+    hipLaunchKernelGGL(rmsnorm_fwd_k<bf16>, g, b, 0, s, (const bf16*)x, (bf16*)xn, r, N, C, eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_fwd_k<float>, g, b, 0, s, (const float*)x, (float*)xn, r, N, C, eps);
+  return hipGetLastError();
+}
+
+hipError_t rmsnorm_bwd(int dt, const void* dxn, const void* xn, const float* r, const void* dres, void* dx,
+                       int N, int C, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  dim3 g((N + 3) / 4), b(256);
+  if (dt == BF16)
+    hipLaunchKernelGGL(rmsnorm_bwd_k<bf16>, g, b, 0, s, (const bf16*)dxn, (const bf16*)xn, r,
+                       (const bf16*)dres, (bf16*)dx, N, C);
+  else
+    hipLaunchKernelGGL(rmsnorm_bwd_k<float>, g, b, 0, s, (const float*)dxn, (const float*)xn, r,
+                       (const float*)dres, (float*)dx, N, C);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------- embedding
+template <typename T>
+__global__ __launch_bounds__(256) void embed_fwd_k(const int32_t* __restrict__ ids, const T* __restrict__ wte,
+                                                    T* __restrict__ x, int N, int C, int V) {
+  constexpr int VN = V16<T>::n;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (row >= N) return;
+  int id = ids[row];
+  id = id < 0 ? 0 : (id >= V ? V - 1 : id);
+  const T* src = wte + (size_t)id * C;
+  T* dst = x + (size_t)row * C;
+  for (int vi = l; vi < C / VN; vi += 64) *(uint4*)(dst + vi * VN) = *(const uint4*)(src + vi * VN);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void embed_bwd_k(const int32_t* __restrict__ ids, const T* __restrict__ dx,
+                                                    float* __restrict__ dwte, int N, int C, int V) {
+  constexpr int VN = V16<T>::n;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (row >= N) return;
+  int id = ids[row];
+  id = id < 0 ? 0 : (id >= V ? V - 1 : id);
+  float* dst = dwte + (size_t)id * C;
+  const T* src = dx + (size_t)row * C;
+  for (int vi = l; vi < C / VN; vi += 64) {
+    float v[VN];
+    ld16(src + vi * VN, v);
+#pragma unroll
+    for (int e = 0; e < VN; ++e) unsafeAtomicAdd(dst + vi * VN + e, v[e]);
+  }
+}
+
+hipError_t embed_fwd(int dt, const int32_t* ids, const void* wte, void* x, int N, int C, int V, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  dim3 g((N + 3) / 4), b(256);
+  if (dt == BF16)
+    hipLaunchKernelGGL(embed_fwd_k<bf16>, g, b, 0, s, ids, (const bf16*)wte, (bf16*)x, N, C, V);
+  else
+    hipLaunchKernelGGL(embed_fwd_k<float>, g, b, 0, s, ids, (const float*)wte, (float*)x, N, C, V);
+  return hipGetLastError();
+}
+
+hipError_t embed_bwd(int dt, const int32_t* ids, const void* dx, float* dwte, int N, int C, int V,
+                     int accumulate, hipStream_t s) {
+  if (!accumulate) {
+    hipError_t e = fill_f32(dwte, (size_t)V * C, 0.f, s);
+    if (e != hipSuccess) return e;
+  }
+  if (N == 0) return hipSuccess;
+  dim3 g((N + 3) / 4), b(256);
+  if (dt == BF16)
+    hipLaunchKernelGGL(embed_bwd_k<bf16>, g, b, 0, s, ids, (const bf16*)dx, dwte, N, C, V);
+  else
+    hipLaunchKernelGGL(embed_bwd_k<float>, g, b, 0, s, ids, (const float*)dx, dwte, N, C, V);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------ QK norm + RoPE
+// One workgroup per token row.  A head of D elements is handled by D/2
+// threads, thread j holding the rotary pair (j, j + D/2); the head's mean
+// square is a reduction over those D/2 lanes.  Then v is copied with 16-byte
+// vectors.
+template <typename T>
+__global__ __launch_bounds__(256) void qk_norm_rope_fwd_k(const T* __restrict__ qkv, T* __restrict__ out,
+                                                           float* __restrict__ rinv, const float* __restrict__ rope,
+                                                           int T_, int H, int Hkv, int D, float eps) {
+  const int row = blockIdx.x;
+  const int t = row % T_;
+  const int HD = D / 2;
+  const int nqk = H + Hkv;
+  const int ld = (H + 2 * Hkv) * D;
+  const T* src = qkv + (size_t)row * ld;
+  T* dst = out + (size_t)row * ld;
+  const int heads_per_pass = 256 / HD;
+  const int hh = threadIdx.x / HD, j = threadIdx.x % HD;
+  const float c = rope[((size_t)t * HD + j) * 2], sn = rope[((size_t)t * HD + j) * 2 + 1];
+  for (int h0 = 0; h0 < nqk; h0 += heads_per_pass) {
+    const int h = h0 + hh;
+    const bool act = h < nqk;
+    float a = 0.f, b = 0.f;
+    if (act) {
+      a = to_f(src[h * D + j]);
+      b = to_f(src[h * D + j + HD]);
+    }
+    float ss = a * a + b * b;
+    for (int o = HD / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float r = rsqrtf(ss / (float)D + eps);
+    if (act) {
+      a *= r;
+      b *= r;
+      dst[h * D + j] = from_f<T>(a * c - b * sn);
+      dst[h * D + j + HD] = from_f<T>(a * sn + b * c);
+      if (j == 0) rinv[(size_t)row * nqk + h] = r;
+    }
+  }
+  constexpr int VN = V16<T>::n;
+  const int voff = nqk * D, nv = Hkv * D / VN;
+  for (int vi = threadIdx.x; vi < nv; vi += 256)
+    *(uint4*)(dst + voff + vi * VN) = *(const uint4*)(src + voff + vi * VN);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void qk_norm_rope_bwd_k(T* d, const T* __restrict__ qkvh,
+                                                           const float* __restrict__ rinv,
+                                                           const float* __restrict__ rope, int T_, int H,
+                                                           int Hkv, int D) {
+  const int row = blockIdx.x;
+  const int t = row % T_;
+  const int HD = D / 2;
+  const int nqk = H + Hkv;
+  const int ld = (H + 2 * Hkv) * D;
+  T* g = d + (size_t)row * ld;
+  const T* y = qkvh + (size_t)row * ld;
+  const int heads_per_pass = 256 / HD;
+  const int hh = threadIdx.x / HD, j = threadIdx.x % HD;
+  const float c = rope[((size_t)t * HD + j) * 2], sn = rope[((size_t)t * HD + j) * 2 + 1];
+  for (int h0 = 0; h0 < nqk; h0 += heads_per_pass) {
+    const int h = h0 + hh;
+    const bool act = h < nqk;
+    float ga = 0.f, gb = 0.f, ya = 0.f, yb = 0.f;
+    if (act) {
+      ga = to_f(g[h * D + j]);
+      gb = to_f(g[h * D + j + HD]);
+      ya = to_f(y[h * D + j]);
+      yb = to_f(y[h * D + j + HD]);
+    }
+    float dot = ga * ya + gb * yb;
+    for (int o = HD / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
+    const float m = dot / (float)D;
+    if (act) {
+      const float r = rinv[(size_t)row * nqk + h];
+      const float ua = ga - ya * m, ub = gb - yb * m;
+      // inverse rotation
+      g[h * D + j] = from_f<T>(r * (ua * c + ub * sn));
+      g[h * D + j + HD] = from_f<T>(r * (-ua * sn + ub * c));
+    }
+  }
+}
+
+hipError_t qk_norm_rope_fwd(int dt, const void* qkv, void* qkvh, float* rinv, const float* rope, int B, int T,
+                            int H, int Hkv, int D, float eps, hipStream_t s) {
+  const int N = B * T;
+  if (N == 0) return hipSuccess;
+  if (dt == BF16)
+    hipLaunchKernelGGL(qk_norm_rope_fwd_k<bf16>, dim3(N), dim3(256), 0, s, (const bf16*)qkv, (bf16*)qkvh, rinv,
+                       rope, T, H, Hkv, D, eps);
+  else
+    hipLaunchKernelGGL(qk_norm_rope_fwd_k<float>, dim3(N), dim3(256), 0, s, (const float*)qkv, (float*)qkvh,
+                       rinv, rope, T, H, Hkv, D, eps);
+  return hipGetLastError();
+}
+
+hipError_t qk_norm_rope_bwd(int dt, void* d, const void* qkvh, const float* rinv, const float* rope, int B,
+                            int T, int H, int Hkv, int D, hipStream_t s) {
+  const int N = B * T;
+  if (N == 0) return hipSuccess;
+  if (dt == BF16)
+    hipLaunchKernelGGL(qk_norm_rope_bwd_k<bf16>, dim3(N), dim3(256), 0, s, (bf16*)d, (const bf16*)qkvh, rinv,
+                       rope, T, H, Hkv, D);
+  else
+    hipLaunchKernelGGL(qk_norm_rope_bwd_k<float>, dim3(N), dim3(256), 0, s, (float*)d, (const float*)qkvh, rinv,
+                       rope, T, H, Hkv, D);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- cross-entropy
+// One workgroup of 256 threads per row of logits.  The row (up to
+// 256*CE_MAXV vectors) is read once into registers: max, sum of exp,
+// log-sum-exp, then (softmax - onehot)/N is written over the logits.
+constexpr int CE_MAXV = 16;
+
+template <typename T>
+__global__ __launch_bounds__(256) void ce_k(T* z, const int32_t* __restrict__ tgt, float* __restrict__ row_loss,
+                                             int N, int V) {
+  constexpr int VN = V16<T>::n;
+  __shared__ float red[4];
+  const int n = blockIdx.x;
+  T* zr = z + (size_t)n * V;
+  const int nv = V / VN;
+  int y = tgt[n];
+  y = y < 0 ? 0 : (y >= V ? V - 1 : y);
+  const float zy = to_f(zr[y]);
+  float v[CE_MAXV][VN];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < CE_MAXV; ++i) {
+    const int vi = threadIdx.x + 256 * i;
+    if (vi < nv) {
+      ld16(zr + vi * VN, v[i]);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) mx = fmaxf(mx, v[i][e]);
+    }
+  }
+  mx = block_max<256>(mx, red);
+  float se = 0.f;
+#pragma unroll
+  for (int i = 0; i < CE_MAXV; ++i) {
+    const int vi = threadIdx.x + 256 * i;
+    if (vi < nv) {
+#pragma unroll
+      for (int e = 0; e < VN; ++e) se += fast_exp(v[i][e] - mx);
+    }
+  }
+  se = block_sum<256>(se, red);
+  const float lse = mx + logf(se);
+  const float invN = 1.0f / (float)N;
+#pragma unroll
+  for (int i = 0; i < CE_MAXV; ++i) {
+    const int vi = threadIdx.x + 256 * i;
+    if (vi < nv) {
+      float o[VN];
+#pragma unroll
+      for (int e = 0; e < VN; ++e) {
+        float p = fast_exp(v[i][e] - lse);
+        if (vi * VN + e == y) p -= 1.0f;
+        o[e] = p * invN;
+      }
+      st16(zr + vi * VN, o);
+    }
+  }
+  if (threadIdx.x == 0) row_loss[n] = lse - zy;
+}
+
+// Rows longer than the register-resident capacity: three streamed passes.
+template <typename T>
+__global__ __launch_bounds__(256) void ce_long_k(T* z, const int32_t* __restrict__ tgt, float* __restrict__ row_loss,
+                                                  int N, int V) {
+  constexpr int VN = V16<T>::n;
+  __shared__ float red[4];
+  const int n = blockIdx.x;
+  T* zr = z + (size_t)n * V;
+  const int nv = V / VN;
+  int y = tgt[n];
+  y = y < 0 ? 0 : (y >= V ? V - 1 : y);
+  const float zy = to_f(zr[y]);
+  float mx = -INFINITY;
+  for (int vi = threadIdx.x; vi < nv; vi += 256) {
+    float v[VN];
+    ld16(zr + vi * VN, v);
+    for (int e = 0; e < VN; ++e) mx = fmaxf(mx, v[e]);
+  }
+  mx = block_max<256>(mx, red);
+  float se = 0.f;
+  for (int vi = threadIdx.x; vi < nv; vi += 256) {
+    float v[VN];
+    ld16(zr + vi * VN, v);
+    for (int e = 0; e < VN; ++e) se += fast_exp(v[e] - mx);
+  }
+  se = block_sum<256>(se, red);
+  const float lse = mx + logf(se);
+  const float invN = 1.0f / (float)N;
+  for (int vi = threadIdx.x; vi < nv; vi += 256) {
+    float v[VN];
+    ld16(zr + vi * VN, v);
+    for (int e = 0; e < VN; ++e) {
+      float p = fast_exp(v[e] - lse);
+      if (vi * VN + e == y) p -= 1.0f;
+      v[e] = p * invN;
+    }
+    st16(zr + vi * VN, v);
+  }
+  if (threadIdx.x == 0) row_loss[n] = lse - zy;
+}
+
+hipError_t ce_fwd_bwd(int dt, void* z, const int32_t* tgt, float* row_loss, int N, int V, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  const int vn = dt == BF16 ? 8 : 4;
+  const bool fits = V / vn <= 256 * CE_MAXV;
+  if (dt == BF16) {
+    if (fits) hipLaunchKernelGGL(ce_k<bf16>, dim3(N), dim3(256), 0, s, (bf16*)z, tgt, row_loss, N, V);
+    else hipLaunchKernelGGL(ce_long_k<bf16>, dim3(N), dim3(256), 0, s, (bf16*)z, tgt, row_loss, N, V);
+  } else {
+    if (fits) hipLaunchKernelGGL(ce_k<float>, dim3(N), dim3(256), 0, s, (float*)z, tgt, row_loss, N, V);
+    else hipLaunchKernelGGL(ce_long_k<float>, dim3(N), dim3(256), 0, s, (float*)z, tgt, row_loss, N, V);
+  }
+  return hipGetLastError();
+}
+
+// Deterministic: fixed per-thread strides, fixed reduction tree.
+__global__ __launch_bounds__(1024) void loss_reduce_k(const float* __restrict__ row_loss, float* loss, int N) {
+  __shared__ float red[16];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < N; i += 1024) s += row_loss[i];
+  s = block_sum<1024>(s, red);
+  if (threadIdx.x == 0) loss[0] = N > 0 ? s / (float)N : 0.f;
+}
+
+hipError_t loss_reduce(const float* row_loss, float* loss, int N, hipStream_t s) {
+  hipLaunchKernelGGL(loss_reduce_k, dim3(1), dim3(1024), 0, s, row_loss, loss, N);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------ split-K reduce
+__global__ __launch_bounds__(256) void splitk_reduce_k(const float* __restrict__ part, float* __restrict__ C,
+                                                        int splits, size_t MN, int accumulate) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= MN) return;  // MN is a multiple of 4 (feature sizes are multiples of 8)
+  f32x4 acc = accumulate ? *(const f32x4*)(C + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int z = 0; z < splits; ++z) acc += *(const f32x4*)(part + (size_t)z * MN + i);
+  *(f32x4*)(C + i) = acc;
+}
+
+hipError_t splitk_reduce(const float* partial, float* C, int splits, size_t MN, int accumulate, hipStream_t s) {
+  if (MN == 0) return hipSuccess;
+  size_t blocks = (MN / 4 + 255) / 256;
+  hipLaunchKernelGGL(splitk_reduce_k, dim3((unsigned)blocks), dim3(256), 0, s, partial, C, splits, MN, accumulate);
+  return hipGetLastError();
+}
+
+}  // namespace gdb

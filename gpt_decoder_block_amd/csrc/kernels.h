@@ -1,0 +1,82 @@
+// Internal launchers of the gfx950 kernels (not part of the public ABI).
+// Every launcher enqueues on `s` and returns the launch status; shapes have
+// been validated by the caller (api.cpp).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdb {
+
+// storage dtype of activations/weights
+enum Dt { F32 = 0, BF16 = 1 };
+
+inline int dt_size(int dt) { return dt == BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------- elementwise
+hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s);
+// xn = x * r, r = 1/sqrt(mean(x^2)+eps) per row of [N, C]
+hipError_t rmsnorm_fwd(int dt, const void* x, void* xn, float* r, int N, int C, float eps, hipStream_t s);
+// dx = r*(dxn - xn*mean(dxn*xn)) (+ dres if non-null); dx may alias dres
+hipError_t rmsnorm_bwd(int dt, const void* dxn, const void* xn, const float* r, const void* dres,
+                       void* dx, int N, int C, hipStream_t s);
+hipError_t embed_fwd(int dt, const int32_t* ids, const void* wte, void* x, int N, int C, int V, hipStream_t s);
+hipError_t embed_bwd(int dt, const int32_t* ids, const void* dx, float* dwte, int N, int C, int V,
+                     int accumulate, hipStream_t s);
+// QK RMS-norm + RoPE on [N, Q+2KV] rows: q, k heads normalised over D and
+// rotated, v copied.  rinv [N, H+Hkv] fp32 (inverse RMS of each q/k head).
+hipError_t qk_norm_rope_fwd(int dt, const void* qkv, void* qkvh, float* rinv, const float* rope,
+                            int B, int T, int H, int Hkv, int D, float eps, hipStream_t s);
+// In place on d (= dqkvh [N, Q+2KV]): dq = r * R^-1 (dqh - qh*mean(dqh*qh)), same for k.
+hipError_t qk_norm_rope_bwd(int dt, void* d, const void* qkvh, const float* rinv, const float* rope,
+                            int B, int T, int H, int Hkv, int D, hipStream_t s);
+// Cross-entropy on logits z [N, V] (in place: z <- (softmax - onehot)/N), per-row loss.
+hipError_t ce_fwd_bwd(int dt, void* z, const int32_t* tgt, float* row_loss, int N, int V, hipStream_t s);
+// loss = sum(row_loss)/N (one deterministic workgroup)
+hipError_t loss_reduce(const float* row_loss, float* loss, int N, hipStream_t s);
+// C (+)= sum_z partial[z] over `splits` fp32 [M, N] slices
+hipError_t splitk_reduce(const float* partial, float* C, int splits, size_t MN, int accumulate, hipStream_t s);
+
+// ----------------------------------------------------------------------- GEMM
+// C[m, n] = sum_k A(m, k) * B(n, k)
+//   A(m,k) = a_kmajor ? A[m*lda + k] : A[k*lda + m]
+//   B(n,k) = b_kmajor ? B[n*ldb + k] : B[k*ldb + n]
+enum Epi {
+  EPI_STORE = 0,   // C = acc                       (dtype out)
+  EPI_RESID = 1,   // C = R + acc                   (dtype out, R may alias C)
+  EPI_RELU2 = 2,   // C = acc (u), C2 = relu(acc)^2  (dtype out)
+  EPI_DRELU2 = 3,  // C = acc * 2*max(R, 0)          (dtype out, R = saved u)
+  EPI_F32 = 4      // fp32 C (+)= acc (split-K through `partial`)
+};
+struct GemmArgs {
+  const void* A; const void* B;
+  int M, N, K, lda, ldb;
+  bool a_kmajor, b_kmajor;
+  int epi;
+  void* C; int ldc;
+  const void* R; int ldr;
+  void* C2;
+  int accumulate;      // EPI_F32
+  float* partial;      // EPI_F32 split-K scratch [splits, M, N] or null
+  int splits;          // >= 1
+};
+hipError_t gemm(int dt, const GemmArgs& a, hipStream_t s);
+// split-K factor and partial-buffer size (floats) the GEMM will use for this shape
+int gemm_splits(int dt, int M, int N, int K, int epi);
+
+// ------------------------------------------------------------------ attention
+// q, k, v: rows of qkvh [N, ld] at column offsets 0, H*D, (H+Hkv)*D.
+struct AttnArgs {
+  int B, T, H, Hkv, D, window;
+  const void* qkv; int ld;        // q^, k^, v (row stride ld)
+  void* o; int ldo;               // [N, H*D]
+  float* lse;                     // [B, H, T]
+  // backward
+  const void* dout; int lddo;     // dO [N, H*D]
+  void* dqkv; int lddq;           // dq^, dk^, dv written at the same offsets
+  float* delta;                   // [B, H, T] scratch: rowsum(dO * O)
+  float* dq_acc;                  // fp32 scratch [N, H*D] (fp32 path)
+};
+hipError_t attn_fwd(int dt, const AttnArgs& a, hipStream_t s);
+hipError_t attn_bwd(int dt, const AttnArgs& a, hipStream_t s);
+
+}  // namespace gdb

@@ -1,0 +1,164 @@
+"""Python names of the C-ABI entry points (include/gdb.h), taking torch tensors.
+
+Marshalling only: each function checks that tensors are contiguous device
+tensors of the expected dtype, passes raw pointers and the current HIP stream,
+and raises GdbError with the library's message on a non-zero status.  PyTorch
+provides device memory and streams; it computes nothing here.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Sequence, Tuple
+
+import torch
+
+from . import _lib as L
+
+_DT = {torch.float32: L.GDB_F32, torch.bfloat16: L.GDB_BF16}
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    return _DT[dt]
+
+
+def _p(t: torch.Tensor) -> ctypes.c_void_p:
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    if t.device.type != "cuda":
+        raise ValueError("tensors must live on the GPU (device 'cuda')")
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def make_cfg(B: int, T: int, C: int, n_head: int, n_kv_head: int, head_dim: int, mlp_hidden: int,
+             window: int, dtype: torch.dtype, eps: float = 1e-6, accumulate_wgrad: bool = False) -> L.BlockCfg:
+    return L.BlockCfg(B, T, C, n_head, n_kv_head, head_dim, mlp_hidden, window, dtype_code(dtype), 0,
+                      int(accumulate_wgrad), eps)
+
+
+def block_sizes(cfg: L.BlockCfg) -> Tuple[int, int, int]:
+    s, f, b = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    L.call("gdb_block_sizes", ctypes.byref(cfg), ctypes.byref(s), ctypes.byref(f), ctypes.byref(b))
+    return s.value, f.value, b.value
+
+
+def rope_table(T: int, head_dim: int, base: float, device) -> torch.Tensor:
+    """[T, head_dim/2, 2] fp32 (cos, sin), filled on the host by the library."""
+    host = torch.empty((T, head_dim // 2, 2), dtype=torch.float32)
+    L.call("gdb_rope_table_host", T, head_dim, base, ctypes.c_void_p(host.data_ptr()))
+    return host.to(device)
+
+
+def embed_fwd(ids: torch.Tensor, wte: torch.Tensor, x0: torch.Tensor) -> None:
+    V, C = wte.shape
+    L.call("gdb_embed_fwd", ids.numel(), C, V, dtype_code(wte.dtype), _p(ids), _p(wte), _p(x0), _stream(wte))
+
+
+def embed_bwd(ids: torch.Tensor, dx0: torch.Tensor, dwte: torch.Tensor, accumulate: bool = False) -> None:
+    V, C = dwte.shape
+    L.call("gdb_embed_bwd", ids.numel(), C, V, dtype_code(dx0.dtype), _p(ids), _p(dx0), _p(dwte),
+           int(accumulate), _stream(dwte))
+
+
+def _weights(w: Sequence[torch.Tensor]) -> L.BlockWeights:
+    return L.BlockWeights(*[t.data_ptr() for t in w])
+
+
+def block_fwd(cfg: L.BlockCfg, w: Sequence[torch.Tensor], rope: torch.Tensor, x_in: torch.Tensor,
+              x_out: torch.Tensor, saved: torch.Tensor, ws: torch.Tensor) -> None:
+    for t in w:
+        _p(t)
+    L.call("gdb_block_fwd", ctypes.byref(cfg), ctypes.byref(_weights(w)), _p(rope), _p(x_in), _p(x_out),
+           _p(saved), _p(ws), _stream(x_in))
+
+
+def block_bwd(cfg: L.BlockCfg, w: Sequence[torch.Tensor], rope: torch.Tensor, saved: torch.Tensor,
+              dx_out: torch.Tensor, dx_in: torch.Tensor, dw: Sequence[torch.Tensor], ws: torch.Tensor) -> None:
+    for t in list(w) + list(dw):
+        _p(t)
+    wg = L.BlockWgrads(*[t.data_ptr() for t in dw])
+    L.call("gdb_block_bwd", ctypes.byref(cfg), ctypes.byref(_weights(w)), _p(rope), _p(saved), _p(dx_out),
+           _p(dx_in), ctypes.byref(wg), _p(ws), _stream(dx_out))
+
+
+def lm_head_ce_sizes(N: int, C: int, V: int, dtype: torch.dtype) -> int:
+    s = ctypes.c_size_t()
+    L.call("gdb_lm_head_ce_sizes", N, C, V, dtype_code(dtype), ctypes.byref(s))
+    return s.value
+
+
+def lm_head_ce_fwd_bwd(x: torch.Tensor, w_lm: torch.Tensor, targets: torch.Tensor, loss: torch.Tensor,
+                       dx: torch.Tensor, dw_lm: torch.Tensor, ws: torch.Tensor, eps: float = 1e-6,
+                       accumulate: bool = False) -> None:
+    N, C = x.shape[-2] if x.dim() == 2 else x.numel() // x.shape[-1], x.shape[-1]
+    V = w_lm.shape[0]
+    L.call("gdb_lm_head_ce_fwd_bwd", N, C, V, dtype_code(x.dtype), eps, _p(x), _p(w_lm), _p(targets), _p(loss),
+           _p(dx), _p(dw_lm), int(accumulate), _p(ws), _stream(x))
+
+
+# ------------------------------------------------------------ building blocks
+def _opt(t):
+    return None if t is None else _p(t)
+
+
+def rmsnorm_fwd(x: torch.Tensor, xn: torch.Tensor, r: torch.Tensor, eps: float = 1e-6) -> None:
+    C = x.shape[-1]
+    L.call("gdb_rmsnorm_fwd", x.numel() // C, C, dtype_code(x.dtype), eps, _p(x), _p(xn), _p(r), _stream(x))
+
+
+def rmsnorm_bwd(dxn: torch.Tensor, xn: torch.Tensor, r: torch.Tensor, dres, dx: torch.Tensor) -> None:
+    C = dxn.shape[-1]
+    L.call("gdb_rmsnorm_bwd", dxn.numel() // C, C, dtype_code(dxn.dtype), _p(dxn), _p(xn), _p(r), _opt(dres),
+           _p(dx), _stream(dxn))
+
+
+EPI_STORE, EPI_RESID, EPI_RELU2, EPI_DRELU2, EPI_F32 = 0, 1, 2, 3, 4
+
+
+def gemm_ws_bytes(dtype: torch.dtype, M: int, N: int, K: int, epi: int) -> int:
+    s = ctypes.c_size_t()
+    L.call("gdb_gemm_ws_bytes", dtype_code(dtype), M, N, K, epi, ctypes.byref(s))
+    return s.value
+
+
+def gemm(M: int, N: int, K: int, A: torch.Tensor, a_kmajor: bool, lda: int, B: torch.Tensor, b_kmajor: bool,
+         ldb: int, epi: int, C: torch.Tensor, ldc: int, R=None, ldr: int = 0, C2=None, accumulate: bool = False,
+         ws=None) -> None:
+    L.call("gdb_gemm", dtype_code(A.dtype), M, N, K, _p(A), int(a_kmajor), lda, _p(B), int(b_kmajor), ldb, epi,
+           _p(C), ldc, _opt(R), ldr, _opt(C2), int(accumulate), _opt(ws), _stream(A))
+
+
+def qk_norm_rope_fwd(B: int, T: int, H: int, Hkv: int, D: int, qkv: torch.Tensor, out: torch.Tensor,
+                     rinv: torch.Tensor, rope: torch.Tensor, eps: float = 1e-6) -> None:
+    L.call("gdb_qk_norm_rope_fwd", B, T, H, Hkv, D, dtype_code(qkv.dtype), eps, _p(qkv), _p(out), _p(rinv),
+           _p(rope), _stream(qkv))
+
+
+def qk_norm_rope_bwd(B: int, T: int, H: int, Hkv: int, D: int, d: torch.Tensor, qkvh: torch.Tensor,
+                     rinv: torch.Tensor, rope: torch.Tensor) -> None:
+    L.call("gdb_qk_norm_rope_bwd", B, T, H, Hkv, D, dtype_code(d.dtype), _p(d), _p(qkvh), _p(rinv), _p(rope),
+           _stream(d))
+
+
+def attention_fwd(B: int, T: int, H: int, Hkv: int, D: int, window: int, qkv: torch.Tensor, ld: int,
+                  o: torch.Tensor, ldo: int, lse: torch.Tensor) -> None:
+    L.call("gdb_attention_fwd", B, T, H, Hkv, D, window, dtype_code(qkv.dtype), _p(qkv), ld, _p(o), ldo, _p(lse),
+           _stream(qkv))
+
+
+def attention_bwd(B: int, T: int, H: int, Hkv: int, D: int, window: int, qkv: torch.Tensor, ld: int,
+                  o: torch.Tensor, ldo: int, lse: torch.Tensor, dout: torch.Tensor, lddo: int,
+                  dqkv: torch.Tensor, lddq: int, delta: torch.Tensor) -> None:
+    L.call("gdb_attention_bwd", B, T, H, Hkv, D, window, dtype_code(qkv.dtype), _p(qkv), ld, _p(o), ldo, _p(lse),
+           _p(dout), lddo, _p(dqkv), lddq, _p(delta), _stream(qkv))
+
+
+def cross_entropy(z: torch.Tensor, targets: torch.Tensor, row_loss: torch.Tensor, loss: torch.Tensor) -> None:
+    N, V = z.shape
+    L.call("gdb_cross_entropy", N, V, dtype_code(z.dtype), _p(z), _p(targets), _p(row_loss), _p(loss),
+           _stream(z))

@@ -1,0 +1,229 @@
+/*
+ * gdb.h — C ABI of the MI355X (gfx950) decoder-block training hot path.
+ *
+ * One training step of a nanochat-style GPT as the pages describe it
+ * ("Comment Entraîner Votre Propre ChatGPT Pour 50€ ?", section "1. Le modèle
+ * GPT": rotary embeddings, QK normalisation, untied token embedding and output
+ * projection, ReLU² MLP, grouped-query attention, sliding-window attention;
+ * section "3. Gestion de la précision": bias-free Linear layers F.linear(x, W)
+ * with W stored [out, in] and explicit compute dtypes):
+ *
+ *   gdb_embed_fwd -> L x gdb_block_fwd -> gdb_lm_head_ce_fwd_bwd
+ *                 -> L x gdb_block_bwd (reverse order) -> gdb_embed_bwd
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named in a signature are DEVICE pointers unless the comment
+ *     says "host".  The caller allocates every buffer (inputs, outputs, saved
+ *     activations, workspace); the library never allocates or frees device
+ *     memory, never synchronises, and enqueues all work on `stream`
+ *     (a hipStream_t passed as void*, NULL = the default stream).
+ *   - Activations are row-major [N, C] with N = B*T tokens (row n = b*T + t);
+ *     attention views the same memory as [B, T, heads, head_dim].
+ *   - dtype GDB_F32: every tensor float32, fp32 arithmetic throughout.
+ *     dtype GDB_BF16: weights, activations and activation gradients bfloat16
+ *     (round to nearest even); GEMM accumulation, norm statistics, softmax,
+ *     log-sum-exp and the loss in float32.  Weight gradients are always
+ *     float32 (the masters are fp32).
+ *   - Weight gradients are overwritten, or added to when `accumulate` /
+ *     cfg->accumulate_wgrad is non-zero (gradient accumulation).
+ *   - Every function validates its arguments before enqueuing anything and
+ *     returns a gdb_status; on failure gdb_last_error() describes the problem.
+ *     No function aborts or throws across the boundary.  Errors from the HIP
+ *     runtime (a failed launch) return GDB_EHIP.
+ *   - Device pointers must be non-NULL and 16-byte aligned; feature sizes
+ *     (C, head_dim, mlp_hidden, V) must be multiples of 8.
+ */
+#ifndef GDB_H
+#define GDB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDB_ABI_VERSION 1
+
+typedef enum {
+  GDB_OK = 0,
+  GDB_EINVAL = -1,        /* bad argument (shape, pointer, alignment, dtype) */
+  GDB_EUNSUPPORTED = -2,  /* valid but not implemented (e.g. head_dim 96)     */
+  GDB_EHIP = -3,          /* the HIP runtime reported an error                */
+  GDB_EWORKSPACE = -4     /* a size query's answer was not respected          */
+} gdb_status;
+
+typedef enum { GDB_F32 = 0, GDB_BF16 = 1 } gdb_dtype;
+
+/* Shape and options of one decoder block.
+ *   Q = n_head*head_dim must equal C; KV = n_kv_head*head_dim;
+ *   n_head % n_kv_head == 0 (query head h reads K/V head h / (n_head/n_kv_head));
+ *   head_dim in {64, 128} (bf16: 128 only); window: < 0 full causal, else key j
+ *   is visible from query i iff 0 <= i - j <= window ("window_size" argument of
+ *   the attention call, section "5. Unification de Flash Attention").
+ *   eps: RMSNorm epsilon (1e-6), used for the block norms and the QK norm.   */
+typedef struct {
+  int32_t B, T, C;
+  int32_t n_head, n_kv_head, head_dim;
+  int32_t mlp_hidden;         /* F, the ReLU² MLP width (4*C in every workload) */
+  int32_t window;
+  int32_t dtype;              /* gdb_dtype */
+  int32_t mlp_fp8;            /* reserved: must be 0 */
+  int32_t accumulate_wgrad;   /* 0: dW = ..., 1: dW += ... */
+  float eps;
+} gdb_block_cfg;
+
+/* Block weights, all [out, in] row-major in cfg->dtype:
+ *   w_qkv  [Q + 2*KV, C]  rows: the Q query rows (head-major), then KV key rows, then KV value rows
+ *   w_o    [C, Q]
+ *   w_fc   [F, C]
+ *   w_proj [C, F]                                                              */
+typedef struct {
+  const void *w_qkv, *w_o, *w_fc, *w_proj;
+} gdb_block_weights;
+
+/* fp32 weight gradients, same shapes as gdb_block_weights. */
+typedef struct {
+  float *dw_qkv, *dw_o, *dw_fc, *dw_proj;
+} gdb_block_wgrads;
+
+/* ABI version (GDB_ABI_VERSION of the built library). */
+int32_t gdb_abi_version(void);
+
+/* Text of the last error on the calling thread ("" if none). Valid until the
+ * next gdb_* call on this thread. */
+const char* gdb_last_error(void);
+
+/* Sizes in bytes of the opaque `saved` buffer that gdb_block_fwd fills and
+ * gdb_block_bwd reads, and of the scratch workspaces of each direction.
+ * Any argument pointer may be NULL to skip that answer. */
+gdb_status gdb_block_sizes(const gdb_block_cfg* cfg, size_t* saved_bytes,
+                           size_t* ws_fwd_bytes, size_t* ws_bwd_bytes);
+
+/* HOST function: fill out_host[T][head_dim/2][2] with (cos, sin) of the rotary
+ * angle t * base^(-2j/head_dim), j < head_dim/2, computed in double precision
+ * and rounded to float.  Dimension j is paired with j + head_dim/2; positions
+ * restart at 0 on every sequence ("Embeddings rotatifs (RoPE)", section
+ * "1. Le modèle GPT").  The table is copied to the device by the caller. */
+gdb_status gdb_rope_table_host(int32_t T, int32_t head_dim, double base, float* out_host);
+
+/* Token embedding lookup (untied embedding, section "1. Le modèle GPT"):
+ * x0[n, :] = wte[ids[n], :].  ids int32 [N] with values in [0, V) (out-of-range
+ * ids are a caller error; they are clamped, never read out of bounds);
+ * wte [V, C] and x0 [N, C] in `dtype`. */
+gdb_status gdb_embed_fwd(int32_t N, int32_t C, int32_t V, int32_t dtype,
+                         const int32_t* ids, const void* wte, void* x0, void* stream);
+
+/* Embedding gradient: dwte[v, :] (+)= sum of dx0[n, :] over n with ids[n] == v.
+ * dx0 [N, C] in `dtype`; dwte [V, C] float32, zeroed first unless
+ * `accumulate`. Summation order is not fixed (float32 atomics). */
+gdb_status gdb_embed_bwd(int32_t N, int32_t C, int32_t V, int32_t dtype,
+                         const int32_t* ids, const void* dx0, float* dwte,
+                         int32_t accumulate, void* stream);
+
+/* Forward of one pre-norm decoder block on x_in [N, C]:
+ *   xn1 = rms(x_in); [q k v] = xn1 W_qkv^T;  q^ = rope(rms_D(q)), k^ = rope(rms_D(k));
+ *   o = softmax(q^ k^T / sqrt(head_dim), causal/window mask) v  (GQA head sharing);
+ *   x_mid = x_in + o W_o^T;  xn2 = rms(x_mid);  h = relu(xn2 W_fc^T)^2;
+ *   x_out = x_mid + h W_proj^T.
+ * rope_tab: device copy of gdb_rope_table_host(T, head_dim, base).
+ * saved: gdb_block_sizes' saved_bytes, kept intact until gdb_block_bwd.
+ * ws: ws_fwd_bytes of scratch.  x_out must not alias x_in. */
+gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w,
+                         const float* rope_tab, const void* x_in, void* x_out,
+                         void* saved, void* ws, void* stream);
+
+/* Backward of gdb_block_fwd: given dx_out [N, C] (gradient w.r.t. x_out) and
+ * the `saved` buffer of the matching forward, writes dx_in [N, C] (may alias
+ * dx_out) and the fp32 weight gradients.  ws: ws_bwd_bytes of scratch. */
+gdb_status gdb_block_bwd(const gdb_block_cfg* cfg, const gdb_block_weights* w,
+                         const float* rope_tab, const void* saved, const void* dx_out,
+                         void* dx_in, const gdb_block_wgrads* dw, void* ws, void* stream);
+
+/* Workspace of gdb_lm_head_ce_fwd_bwd (holds the normalised stream, its
+ * inverse RMS, the [N, V] logits/gradients, per-row losses). */
+gdb_status gdb_lm_head_ce_sizes(int32_t N, int32_t C, int32_t V, int32_t dtype,
+                                size_t* ws_bytes);
+
+/* Final RMSNorm, lm_head and mean next-token cross-entropy, forward and
+ * backward in one call:
+ *   xf = rms(x); z = xf W_lm^T; loss = (1/N) sum_n (logsumexp(z_n) - z_n[targets[n]]);
+ *   dz = (softmax(z) - onehot(targets)) / N;  dxf = dz W_lm;  dW_lm (+)= dz^T xf;
+ *   dx = rms backward of dxf.
+ * x [N, C], w_lm [V, C], dx [N, C] in `dtype`; targets int32 [N] in [0, V);
+ * loss: device float32 scalar (written); dw_lm [V, C] float32. */
+gdb_status gdb_lm_head_ce_fwd_bwd(int32_t N, int32_t C, int32_t V, int32_t dtype, float eps,
+                                  const void* x, const void* w_lm, const int32_t* targets,
+                                  float* loss, void* dx, float* dw_lm, int32_t accumulate,
+                                  void* ws, void* stream);
+
+
+/* ------------------------------------------------------------------------
+ * Building blocks.  The calls above are compositions of these; they are
+ * exported so each stage can be run and checked on its own.  Same
+ * conventions (device pointers, caller-owned memory, async on `stream`).
+ * ---------------------------------------------------------------------- */
+
+/* RMSNorm without affine over rows of x [N, C]: xn = x * r, r[n] = 1/sqrt(mean(x[n]^2) + eps)
+ * (r float32 [N]).  RMSNorm with eps = 1e-6 is the norm before attention, before
+ * the MLP, on q and k per head, and before the lm_head. */
+gdb_status gdb_rmsnorm_fwd(int32_t N, int32_t C, int32_t dtype, float eps, const void* x, void* xn,
+                           float* r, void* stream);
+/* dx = r * (dxn - xn * mean(dxn * xn)) + dres   (dres may be NULL or alias dx). */
+gdb_status gdb_rmsnorm_bwd(int32_t N, int32_t C, int32_t dtype, const void* dxn, const void* xn,
+                           const float* r, const void* dres, void* dx, void* stream);
+
+/* GEMM C[m, n] = sum_k A(m, k) B(n, k) with fp32 accumulation (bf16 dtype: MFMA).
+ *   A(m, k) = a_kmajor ? A[m*lda + k] : A[k*lda + m];  B(n, k) likewise with ldb.
+ *   epi 0: C = acc;  1: C = R + acc;  2: C = acc and C2 = relu(acc)^2;
+ *   3: C = acc * 2*max(R, 0);  (C, C2, R in dtype, leading dims ldc, ldr)
+ *   4: C float32 [M, N] with ldc == N, C = acc or C += acc (accumulate); needs
+ *      gdb_gemm_ws_bytes of workspace for the split-K partial sums.
+ * The bias-free Linear y = x W^T of section "3. Gestion de la précision" is
+ * A = x (K-major), B = W [out, in] (K-major). M, N, K, lda, ldb, ldc, ldr must be
+ * multiples of 8 except M (tokens) when A is K-major and K when A is M-major. */
+gdb_status gdb_gemm_ws_bytes(int32_t dtype, int32_t M, int32_t N, int32_t K, int32_t epi, size_t* ws_bytes);
+gdb_status gdb_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A, int32_t a_kmajor,
+                    int32_t lda, const void* B, int32_t b_kmajor, int32_t ldb, int32_t epi, void* C,
+                    int32_t ldc, const void* R, int32_t ldr, void* C2, int32_t accumulate, void* ws,
+                    void* stream);
+
+/* QK RMS-norm + RoPE on rows of qkv [B*T, (H + 2*Hkv)*D] (q heads, k heads, v heads):
+ * out rows hold rope(rms_D(q_h)), rope(rms_D(k_g)) and v copied; rinv float32
+ * [B*T, H + Hkv] receives the inverse RMS of each q and k head.  out != qkv. */
+gdb_status gdb_qk_norm_rope_fwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t D, int32_t dtype,
+                                float eps, const void* qkv, void* out, float* rinv, const float* rope_tab,
+                                void* stream);
+/* Backward, in place on d [B*T, (H + 2*Hkv)*D]: the q/k parts of d (gradients
+ * w.r.t. the rotated, normalised heads) become gradients w.r.t. the raw q/k;
+ * the v part is left as is.  qkvh: the forward's output, rinv its factors. */
+gdb_status gdb_qk_norm_rope_bwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t D, int32_t dtype,
+                                void* d, const void* qkvh, const float* rinv, const float* rope_tab,
+                                void* stream);
+
+/* Attention forward on rows of qkv [B*T, ld] holding q heads at column h*D,
+ * k heads at (H + g)*D and v heads at (H + Hkv + g)*D:
+ *   o[n, h*D + d] = sum_j P_ij v_j[d],  P = softmax over visible j of q.k / sqrt(D);
+ *   lse float32 [B, H, T] = log-sum-exp of each row of scaled scores.
+ * window as in gdb_block_cfg.  bf16: D = 128 only. */
+gdb_status gdb_attention_fwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t D, int32_t window,
+                             int32_t dtype, const void* qkv, int32_t ld, void* o, int32_t ldo, float* lse,
+                             void* stream);
+/* Attention backward: from dO [B*T, lddo] writes dq, dk, dv into dqkv [B*T, lddq]
+ * at the same column offsets as qkv (dk, dv summed over the query heads that
+ * share a K/V head). delta: float32 scratch [B, H, T]. */
+gdb_status gdb_attention_bwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t D, int32_t window,
+                             int32_t dtype, const void* qkv, int32_t ld, const void* o, int32_t ldo,
+                             const float* lse, const void* dout, int32_t lddo, void* dqkv, int32_t lddq,
+                             float* delta, void* stream);
+
+/* Fused softmax cross-entropy on logits z [N, V] (overwritten by
+ * dz = (softmax(z) - onehot(targets)) / N), row_loss float32 [N] =
+ * logsumexp(z_n) - z_n[targets[n]], loss = mean(row_loss) (device scalar). */
+gdb_status gdb_cross_entropy(int32_t N, int32_t V, int32_t dtype, void* z, const int32_t* targets,
+                             float* row_loss, float* loss, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDB_H */

@@ -54,7 +54,7 @@ import numpy as np
 
 __all__ = [
     "rms_norm", "rms_norm_backward", "rope_tables", "rope", "rope_backward",
-    "visible_mask", "attention", "attention_backward", "e4m3_round",
+    "visible_mask", "attention", "attention_logsumexp", "attention_backward", "cross_entropy", "e4m3_round",
     "fp8_quant_dequant", "block_forward", "block_backward", "lm_head_ce",
     "embed_forward", "embed_backward", "smear_forward", "smear_backward",
     "stack_forward_backward", "FP8_E4M3_MAX",
@@ -140,6 +140,22 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, window: int
             P[b, h] = p
             o[b, :, h, :] = p @ v[b, :, g, :]
     return o, P
+
+
+def attention_logsumexp(q: np.ndarray, k: np.ndarray, window: int) -> np.ndarray:
+    """log of the softmax denominator of each query row, [B, H, T]:
+    lse[b, h, i] = log sum over visible j of exp(q_i . k_j / sqrt(D))."""
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    mask = visible_mask(T, window)
+    out = np.zeros((B, H, T))
+    for b in range(B):
+        for h in range(H):
+            s = (q[b, :, h, :] @ k[b, :, _kv_head(h, H, Hkv), :].T) / math.sqrt(D)
+            s = np.where(mask, s, -np.inf)
+            m = s.max(axis=1)
+            out[b, h] = m + np.log(np.sum(np.exp(s - m[:, None]), axis=1))
+    return out
 
 
 def attention_backward(do: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray,
@@ -302,6 +318,20 @@ def block_backward(dout: np.ndarray, c: dict, p: Dict[str, np.ndarray], cfg, l: 
 
 
 # ------------------------------------------------------- head + loss, embed
+def cross_entropy(z: np.ndarray, y: np.ndarray) -> Tuple[float, np.ndarray, np.ndarray, np.ndarray]:
+    """Mean next-token cross-entropy on logits z [N, V] with targets y [N]:
+    row_loss = logsumexp(z_n) - z_n[y_n]; loss = mean(row_loss);
+    dz = (softmax(z) - onehot(y)) / N.  Returns loss, row_loss, dz, lse."""
+    N = z.shape[0]
+    m = z.max(axis=1)
+    lse = m + np.log(np.sum(np.exp(z - m[:, None]), axis=1))
+    row_loss = lse - z[np.arange(N), y]
+    dz = np.exp(z - lse[:, None])
+    dz[np.arange(N), y] -= 1.0
+    dz /= N
+    return float(np.mean(row_loss)), row_loss, dz, lse
+
+
 def lm_head_ce(x: np.ndarray, w_lm: np.ndarray, targets: np.ndarray, eps: float
                ) -> Tuple[float, np.ndarray, np.ndarray, dict]:
     """xf = rms(x); z = xf W_lm^T; loss = mean_n(logsumexp(z_n) - z_n[y_n]).
@@ -313,12 +343,7 @@ def lm_head_ce(x: np.ndarray, w_lm: np.ndarray, targets: np.ndarray, eps: float
     N = x2.shape[0]
     xf, rf = rms_norm(x2, eps)
     z = xf @ w_lm.T
-    m = z.max(axis=1)
-    lse = m + np.log(np.sum(np.exp(z - m[:, None]), axis=1))
-    loss = float(np.mean(lse - z[np.arange(N), y]))
-    dz = np.exp(z - lse[:, None])
-    dz[np.arange(N), y] -= 1.0
-    dz /= N
+    loss, row_loss, dz, lse = cross_entropy(z, y)
     dxf = dz @ w_lm
     dw = dz.T @ xf
     dx = rms_norm_backward(dxf, xf, rf).reshape(shp)

@@ -1,0 +1,222 @@
+"""Parity of each HIP building block (through the C ABI) with the CPU oracle,
+element by element, at sizes that span several tiles and a ragged tail."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpt_decoder_block_amd import ops
+from gpu_util import DEV, TDT, TOL, assert_close, dev, empty, host, rounded
+
+pytestmark = pytest.mark.gpu
+RNG = np.random.default_rng(777)
+
+
+# ------------------------------------------------------------------ RMSNorm
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,C", [(37, 1536), (5, 128), (64, 4096), (1, 1664)])
+def test_rmsnorm(dt, N, C):
+    print(f"rmsnorm dt={dt} N={N} C={C}", flush=True)
+    x = rounded(RNG.standard_normal((N, C)) * 3.0, dt)
+    dy = rounded(RNG.standard_normal((N, C)), dt)
+    dres = rounded(RNG.standard_normal((N, C)), dt)
+    xg, dyg, dresg = dev(x, dt), dev(dy, dt), dev(dres, dt)
+    xn, r = empty((N, C), dt), empty((N,), torch.float32)
+    ops.rmsnorm_fwd(xg, xn, r, 1e-6)
+    y_ref, r_ref = O.rms_norm(x.astype(np.float64), 1e-6)
+    assert_close(xn, y_ref, dt, "xn")
+    assert_close(r, r_ref, "f32", "r", tol=1e-5)
+    dx = empty((N, C), dt)
+    ops.rmsnorm_bwd(dyg, xn, r, dresg, dx)
+    ref = O.rms_norm_backward(dy.astype(np.float64), y_ref, r_ref) + dres
+    assert_close(dx, ref, dt, "dx")
+    ops.rmsnorm_bwd(dyg, xn, r, None, dx)
+    assert_close(dx, O.rms_norm_backward(dy.astype(np.float64), y_ref, r_ref), dt, "dx (no residual)")
+
+
+# --------------------------------------------------------------------- GEMM
+def _store(Mat, kmajor):
+    """Mat [rows, K] stored K-major ([rows, K]) or rows-major ([K, rows])."""
+    return np.ascontiguousarray(Mat if kmajor else Mat.T)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("ak,bk", [(True, True), (True, False), (False, False), (False, True)])
+@pytest.mark.parametrize("epi", [0, 1, 2, 3, 4])
+def test_gemm(dt, ak, bk, epi):
+    M, N, K = 296, 264, 200
+    print(f"gemm dt={dt} ak={ak} bk={bk} epi={epi} M={M} N={N} K={K}", flush=True)
+    A = rounded(RNG.standard_normal((M, K)), dt)
+    B = rounded(RNG.standard_normal((N, K)), dt)
+    R = rounded(RNG.standard_normal((M, N)), dt)
+    acc = A.astype(np.float64) @ B.astype(np.float64).T
+    Ag, Bg = dev(_store(A, ak), dt), dev(_store(B, bk), dt)
+    lda, ldb = (K if ak else M), (K if bk else N)
+    if epi == 4:
+        for accumulate in (False, True):
+            C0 = RNG.standard_normal((M, N)).astype(np.float32)
+            C = torch.from_numpy(C0).to(DEV)
+            ws = empty((max(1, ops.gemm_ws_bytes(TDT[dt], M, N, K, 4) // 4),), torch.float32)
+            ops.gemm(M, N, K, Ag, ak, lda, Bg, bk, ldb, 4, C, N, accumulate=accumulate, ws=ws)
+            assert_close(C, acc + (C0 if accumulate else 0.0), "f32", f"fp32 out acc={accumulate}",
+                         tol=1e-5 if dt == "f32" else 1e-5)
+        return
+    C = empty((M, N), dt)
+    C2 = empty((M, N), dt)
+    Rg = dev(R, dt)
+    ops.gemm(M, N, K, Ag, ak, lda, Bg, bk, ldb, epi, C, N, R=Rg if epi in (1, 3) else None, ldr=N,
+             C2=C2 if epi == 2 else None)
+    if epi == 0:
+        assert_close(C, acc, dt, "store")
+    elif epi == 1:
+        assert_close(C, R + acc, dt, "residual")
+    elif epi == 2:
+        assert_close(C, acc, dt, "u")
+        assert_close(C2, np.maximum(acc, 0) ** 2, dt, "relu2")
+    elif epi == 3:
+        assert_close(C, acc * 2.0 * np.maximum(R, 0), dt, "relu2 backward")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_gemm_splitk_large_k(dt):
+    # weight-gradient shape: small output, long token contraction -> split-K
+    M, N, K = 296, 264, 8192
+    A = rounded(RNG.standard_normal((K, M)), dt)   # token-major operands
+    B = rounded(RNG.standard_normal((K, N)), dt)
+    ws_b = ops.gemm_ws_bytes(TDT[dt], M, N, K, 4)
+    if dt == "bf16":
+        assert ws_b > 0, "expected split-K for this shape"
+    ws = empty((max(1, ws_b // 4),), torch.float32)
+    C = empty((M, N), torch.float32)
+    ops.gemm(M, N, K, dev(A, dt), False, M, dev(B, dt), False, N, 4, C, N, ws=ws)
+    assert_close(C, A.astype(np.float64).T @ B.astype(np.float64), "f32", "split-K", tol=1e-5)
+
+
+def test_gemm_bf16_multi_tile_exact_shapes():
+    # full 256x256 tiles plus XCD remap over many tiles
+    M, N, K = 1024, 2048, 768
+    A = rounded(RNG.standard_normal((M, K)), "bf16")
+    B = rounded(RNG.standard_normal((N, K)), "bf16")
+    C = empty((M, N), "bf16")
+    ops.gemm(M, N, K, dev(A, "bf16"), True, K, dev(B, "bf16"), True, K, 0, C, N)
+    assert_close(C, A.astype(np.float64) @ B.astype(np.float64).T, "bf16", "store")
+
+
+# ---------------------------------------------------------------- attention
+def _attn_case(dt, B, T, H, Hkv, D, window):
+    W3 = (H + 2 * Hkv) * D
+    qkv = rounded(RNG.standard_normal((B * T, W3)), dt)
+    q = qkv[:, :H * D].reshape(B, T, H, D).astype(np.float64)
+    k = qkv[:, H * D:(H + Hkv) * D].reshape(B, T, Hkv, D).astype(np.float64)
+    v = qkv[:, (H + Hkv) * D:].reshape(B, T, Hkv, D).astype(np.float64)
+    qkvg = dev(qkv, dt)
+    o = empty((B * T, H * D), dt)
+    lse = empty((B, H, T), torch.float32)
+    ops.attention_fwd(B, T, H, Hkv, D, window, qkvg, W3, o, H * D, lse)
+    o_ref, P = O.attention(q, k, v, window)
+    assert_close(o, o_ref.reshape(B * T, H * D), dt, "o")
+    assert_close(lse, O.attention_logsumexp(q, k, window), "f32", "lse", tol=1e-4 if dt == "bf16" else 1e-5)
+    do = rounded(RNG.standard_normal((B * T, H * D)), dt)
+    dqkv = empty((B * T, W3), dt, fill=0.0)
+    delta = empty((B, H, T), torch.float32)
+    ops.attention_bwd(B, T, H, Hkv, D, window, qkvg, W3, o, H * D, lse, dev(do, dt), H * D, dqkv, W3, delta)
+    dq, dk, dv = O.attention_backward(do.reshape(B, T, H, D).astype(np.float64), q, k, v, P)
+    g = host(dqkv)
+    dq_g = g[:, :H * D]
+    dk_g = g[:, H * D:(H + Hkv) * D]
+    dv_g = g[:, (H + Hkv) * D:]
+    assert_close(dq_g, dq.reshape(B * T, -1), dt, "dq")
+    assert_close(dk_g, dk.reshape(B * T, -1), dt, "dk")
+    assert_close(dv_g, dv.reshape(B * T, -1), dt, "dv")
+
+
+@pytest.mark.parametrize("window", [-1, 0, 1, 63, 64, 70, 199, 1000])
+def test_attention_bf16_gqa_windows(window):
+    print(f"attention bf16 B=2 T=200 H=6 Hkv=2 window={window}", flush=True)
+    _attn_case("bf16", 2, 200, 6, 2, 128, window)
+
+
+@pytest.mark.parametrize("B,T,H,Hkv", [(1, 1, 2, 2), (1, 64, 2, 1), (1, 130, 2, 2), (1, 384, 3, 1)])
+def test_attention_bf16_shapes(B, T, H, Hkv):
+    print(f"attention bf16 B={B} T={T} H={H} Hkv={Hkv}", flush=True)
+    _attn_case("bf16", B, T, H, Hkv, 128, -1)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("window", [-1, 0, 5])
+def test_attention_f32(D, window):
+    print(f"attention f32 D={D} window={window}", flush=True)
+    _attn_case("f32", 2, 50, 4, 2, D, window)
+
+
+# ------------------------------------------------------------ QK norm + RoPE
+@pytest.mark.parametrize("dt,D", [("f32", 64), ("f32", 128), ("bf16", 128)])
+def test_qk_norm_rope(dt, D):
+    B, T, H, Hkv = 2, 70, 6, 2
+    print(f"qk_norm_rope dt={dt} D={D}", flush=True)
+    W3 = (H + 2 * Hkv) * D
+    qkv = rounded(RNG.standard_normal((B * T, W3)) * RNG.uniform(0.1, 3.0, size=(1, W3)), dt)
+    rope = ops.rope_table(T, D, 10000.0, DEV)
+    out = empty((B * T, W3), dt)
+    rinv = empty((B * T, H + Hkv), torch.float32)
+    ops.qk_norm_rope_fwd(B, T, H, Hkv, D, dev(qkv, dt), out, rinv, rope, 1e-6)
+    cos, sin = O.rope_tables(T, D, 10000.0)
+    x = qkv.astype(np.float64)
+    q = x[:, :H * D].reshape(B, T, H, D)
+    k = x[:, H * D:(H + Hkv) * D].reshape(B, T, Hkv, D)
+    qn, rq = O.rms_norm(q, 1e-6)
+    kn, rk = O.rms_norm(k, 1e-6)
+    qh, kh = O.rope(qn, cos, sin), O.rope(kn, cos, sin)
+    g = host(out)
+    assert_close(g[:, :H * D], qh.reshape(B * T, -1), dt, "q^")
+    assert_close(g[:, H * D:(H + Hkv) * D], kh.reshape(B * T, -1), dt, "k^")
+    np.testing.assert_array_equal(g[:, (H + Hkv) * D:], x[:, (H + Hkv) * D:])
+    r_ref = np.concatenate([rq.reshape(B * T, H), rk.reshape(B * T, Hkv)], 1)
+    assert_close(rinv, r_ref, "f32", "rinv", tol=1e-5)
+    d = rounded(RNG.standard_normal((B * T, W3)), dt)
+    dg = dev(d, dt)
+    ops.qk_norm_rope_bwd(B, T, H, Hkv, D, dg, out, rinv, rope)
+    dd = d.astype(np.float64)
+    dq = O.rms_norm_backward(O.rope_backward(dd[:, :H * D].reshape(B, T, H, D), cos, sin), qn, rq)
+    dk = O.rms_norm_backward(O.rope_backward(dd[:, H * D:(H + Hkv) * D].reshape(B, T, Hkv, D), cos, sin), kn, rk)
+    g = host(dg)
+    assert_close(g[:, :H * D], dq.reshape(B * T, -1), dt, "dq")
+    assert_close(g[:, H * D:(H + Hkv) * D], dk.reshape(B * T, -1), dt, "dk")
+    np.testing.assert_array_equal(g[:, (H + Hkv) * D:], dd[:, (H + Hkv) * D:])
+
+
+# ------------------------------------------------------------ cross-entropy
+@pytest.mark.parametrize("dt,N,V", [("bf16", 37, 32768), ("f32", 64, 512), ("bf16", 5, 40000), ("f32", 3, 32768)])
+def test_cross_entropy(dt, N, V):
+    print(f"cross_entropy dt={dt} N={N} V={V}", flush=True)
+    z = rounded(RNG.standard_normal((N, V)) * 2.0, dt)
+    y = RNG.integers(0, V, size=N)
+    zg = dev(z, dt)
+    tg = torch.from_numpy(y.astype(np.int32)).to(DEV)
+    row = empty((N,), torch.float32)
+    loss = empty((1,), torch.float32)
+    ops.cross_entropy(zg, tg, row, loss)
+    l_ref, row_ref, dz_ref, _ = O.cross_entropy(z.astype(np.float64), y)
+    assert_close(row, row_ref, "f32", "row loss", tol=1e-5)
+    assert abs(float(loss.item()) - l_ref) <= 1e-5 * abs(l_ref)
+    assert_close(zg, dz_ref, dt, "dz")
+
+
+# ---------------------------------------------------------------- embedding
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_embedding(dt):
+    N, C, V = 300, 136, 50   # many duplicate ids
+    ids = RNG.integers(0, V, size=N)
+    wte = rounded(RNG.standard_normal((V, C)), dt)
+    idg = torch.from_numpy(ids.astype(np.int32)).to(DEV)
+    x = empty((N, C), dt)
+    ops.embed_fwd(idg, dev(wte, dt), x)
+    np.testing.assert_array_equal(host(x), O.embed_forward(wte.astype(np.float64), ids))
+    dx = rounded(RNG.standard_normal((N, C)), dt)
+    dw = empty((V, C), torch.float32, fill=float("nan"))
+    ops.embed_bwd(idg, dev(dx, dt), dw)
+    assert_close(dw, O.embed_backward(dx.astype(np.float64), ids, V), "f32", "dwte", tol=1e-6)
+    ops.embed_bwd(idg, dev(dx, dt), dw, accumulate=True)
+    assert_close(dw, 2 * O.embed_backward(dx.astype(np.float64), ids, V), "f32", "dwte accumulate", tol=1e-6)

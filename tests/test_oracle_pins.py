@@ -358,3 +358,30 @@ def test_fd_whole_step_extras_four_layers():
     cfg = tiny_cfg(C=48, n_head=3, n_kv_head=3, head_dim=16, mlp_hidden=96, vocab=9, T=4, B=1,
                    n_layer=4, windows=(-1, 1, -1, 2), extras=True)
     _fd_all(cfg, 6)
+
+
+def test_attention_logsumexp_matches_softmax_denominator():
+    q, k, v = _qkv(T=9)
+    for window in (-1, 0, 2):
+        lse = O.attention_logsumexp(q, k, window)
+        _, P = O.attention(q, k, v, window)
+        # P_ij = exp(s_ij - lse_i) on visible pairs
+        B, T, H, D = q.shape
+        for b in range(B):
+            for h in range(H):
+                s = q[b, :, h] @ k[b, :, h // (H // k.shape[2])].T / math.sqrt(D)
+                m = O.visible_mask(T, window)
+                np.testing.assert_allclose(P[b, h][m], np.exp(s - lse[b, h][:, None])[m], rtol=1e-12)
+
+
+def test_cross_entropy_against_torch():
+    torch = pytest.importorskip("torch")
+    z = RNG.standard_normal((7, 23)) * 2.0
+    y = RNG.integers(0, 23, size=7)
+    zt = torch.tensor(z, requires_grad=True)
+    lt = torch.nn.functional.cross_entropy(zt, torch.tensor(y))
+    lt.backward()
+    loss, row_loss, dz, lse = O.cross_entropy(z, y)
+    assert abs(loss - float(lt)) < 1e-13
+    np.testing.assert_allclose(dz, zt.grad.numpy(), atol=1e-15)
+    np.testing.assert_allclose(lse, torch.logsumexp(torch.tensor(z), 1).numpy(), rtol=1e-14)
