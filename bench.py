@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Training-step throughput of the decoder stack on one MI355X.
+
+One step = embed_fwd -> L x block_fwd -> lm_head_ce_fwd_bwd -> L x block_bwd
+-> embed_bwd on seeded synthetic inputs already resident in HBM (the optimizer
+step is not part of the path).  Prints ONE JSON line with tokens/s, TFLOP/s
+and the fraction of the bf16 MFMA peak, a roofline entry for the dominant
+kernel (timed on its own with HIP events on the stream it is launched on),
+per-kernel figures, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload d24] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "train tokens/s on 1 MI355X, d24 stack fwd+bwd; % of bf16 MFMA peak"
+PEAK_BF16 = 2.5e15       # dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12        # HBM3E, bytes/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="d24")
+    ap.add_argument("--batch", type=int, default=None, help="override B (default: the workload's)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    return ap.parse_args()
+
+
+def ev_time(fn, reps, torch):
+    """Average duration (s) of fn() over reps launches, HIP events on the current stream."""
+    s = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    a.record(s)
+    for _ in range(reps):
+        fn()
+    b.record(s)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / 1e3 / reps
+
+
+def kernel_figures(w, st, reps, torch, ops):
+    """Each hot kernel class timed alone at the workload's shapes."""
+    dev, dt = st.device, st.dt
+    N, C, F, V = st.N, w.C, w.mlp_hidden, w.vocab
+    H, Hkv, D = w.n_head, w.n_kv_head, w.head_dim
+    W3 = (H + 2 * Hkv) * D
+    g = torch.Generator(device=dev).manual_seed(1)
+    rnd = lambda *shape: torch.randn(*shape, generator=g, device=dev, dtype=torch.float32).to(dt)
+    out = {}
+    # MLP up-projection with fused ReLU^2 (the largest block GEMM)
+    A, B = rnd(N, C), rnd(F, C) * 0.02
+    U, Hh = torch.empty(N, F, dtype=dt, device=dev), torch.empty(N, F, dtype=dt, device=dev)
+    t = ev_time(lambda: ops.gemm(N, F, C, A, True, C, B, True, C, ops.EPI_RELU2, U, F, C2=Hh), reps, torch)
+    fl = 2.0 * N * F * C
+    out["gemm_mlp_up_relu2"] = {"shape": [N, F, C], "ms": t * 1e3, "tflops": fl / t / 1e12,
+                                "frac_bf16_peak": fl / t / PEAK_BF16, "flops": fl}
+    # weight gradient of the MLP down projection (token contraction, fp32 out)
+    dW = torch.empty(C, F, dtype=torch.float32, device=dev)
+    wsz = ops.gemm_ws_bytes(dt, C, F, N, ops.EPI_F32)
+    ws = torch.empty(max(wsz, 16), dtype=torch.uint8, device=dev)
+    t = ev_time(lambda: ops.gemm(C, F, N, A, False, C, Hh, False, F, ops.EPI_F32, dW, F, ws=ws), reps, torch)
+    out["gemm_wgrad_mlp_down"] = {"shape": [C, F, N], "ms": t * 1e3, "tflops": fl / t / 1e12,
+                                  "frac_bf16_peak": fl / t / PEAK_BF16}
+    del U, Hh, dW, ws
+    # attention forward / backward, full causal and windowed
+    from gpt_decoder_block_amd.workmodel import attn_pairs
+    qkv = rnd(N, W3)
+    o = torch.empty(N, H * D, dtype=dt, device=dev)
+    lse = torch.empty(w.B, H, w.T, dtype=torch.float32, device=dev)
+    do = rnd(N, H * D)
+    dqkv = torch.empty(N, W3, dtype=dt, device=dev)
+    delta = torch.empty(w.B, H, w.T, dtype=torch.float32, device=dev)
+    for win in sorted(set(w.windows)):
+        pairs = attn_pairs(w.T, win) * w.B * H
+        f_fwd, f_bwd = 4.0 * D * pairs, 8.0 * D * pairs
+        tf = ev_time(lambda: ops.attention_fwd(w.B, w.T, H, Hkv, D, win, qkv, W3, o, H * D, lse), reps, torch)
+        tb = ev_time(lambda: ops.attention_bwd(w.B, w.T, H, Hkv, D, win, qkv, W3, o, H * D, lse, do, H * D,
+                                               dqkv, W3, delta), reps, torch)
+        key = "full" if win < 0 else f"window{win}"
+        out[f"attn_fwd_{key}"] = {"ms": tf * 1e3, "tflops": f_fwd / tf / 1e12, "frac_bf16_peak": f_fwd / tf / PEAK_BF16}
+        out[f"attn_bwd_{key}"] = {"ms": tb * 1e3, "tflops": f_bwd / tb / 1e12, "frac_bf16_peak": f_bwd / tb / PEAK_BF16}
+    del qkv, o, do, dqkv
+    # RMSNorm forward (bandwidth): read x, write xn, write r
+    x, xn, r = rnd(N, C), torch.empty(N, C, dtype=dt, device=dev), torch.empty(N, dtype=torch.float32, device=dev)
+    s = 2 if dt == torch.bfloat16 else 4
+    t = ev_time(lambda: ops.rmsnorm_fwd(x, xn, r, w.eps), reps, torch)
+    by = 2.0 * N * C * s + 4 * N
+    out["rmsnorm_fwd"] = {"ms": t * 1e3, "GBps": by / t / 1e9, "frac_hbm_peak": by / t / PEAK_HBM}
+    dres = rnd(N, C)
+    dx = torch.empty(N, C, dtype=dt, device=dev)
+    t = ev_time(lambda: ops.rmsnorm_bwd(x, xn, r, dres, dx), reps, torch)
+    by = 4.0 * N * C * s + 4 * N
+    out["rmsnorm_bwd"] = {"ms": t * 1e3, "GBps": by / t / 1e9, "frac_hbm_peak": by / t / PEAK_HBM}
+    del x, xn, dres, dx
+    # cross-entropy over the vocabulary (bandwidth): one read + one write of the logits
+    z0 = rnd(N, V)
+    z = torch.empty_like(z0)
+    tg = torch.randint(0, V, (N,), device=dev, dtype=torch.int32)
+    rl, ls = torch.empty(N, dtype=torch.float32, device=dev), torch.empty(1, dtype=torch.float32, device=dev)
+    # restore the logits before each launch outside the timed launches: time copy+ce, subtract copy
+    tc = ev_time(lambda: z.copy_(z0), reps, torch)
+    tce = ev_time(lambda: (z.copy_(z0), ops.cross_entropy(z, tg, rl, ls)), reps, torch) - tc
+    by = N * V * 2.0 * s + 8 * N
+    out["cross_entropy"] = {"ms": tce * 1e3, "GBps": by / tce / 1e9, "frac_hbm_peak": by / tce / PEAK_HBM}
+    del z0, z
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(w, budget_s=40.0):
+    """The fp64 oracle on the host cores: one block forward+backward per layer
+    kind at B=1, T=w.T, plus the head at N=T tokens; scaled to the whole stack."""
+    import oracle as O
+    from seeded_inputs import draw_globals, draw_layer, draw_upstream, to_dtype
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    T = w.T
+    cos, sin = O.rope_tables(T, w.head_dim, w.rope_base)
+    times = {}
+    t_start = time.perf_counter()
+    for l, win in enumerate(w.windows):
+        if win in times:
+            continue
+        p = {k: to_dtype(v, w.dtype).astype(np.float64) for k, v in draw_layer(w, l).items()}
+        x = draw_upstream(w, 100, (1, T, w.C), 1.0).astype(np.float64)
+        dy = draw_upstream(w, 200, (1, T, w.C), 1.0).astype(np.float64)
+        t0 = time.perf_counter()
+        out, c = O.block_forward(x, p, w, l, cos, sin)
+        O.block_backward(dy, c, p, w, l, cos, sin)
+        times[win] = time.perf_counter() - t0
+    g = draw_globals(w)
+    x = draw_upstream(w, 300, (T, w.C), 1.0).astype(np.float64)
+    y = np.random.default_rng(0).integers(0, w.vocab, size=T)
+    t0 = time.perf_counter()
+    O.lm_head_ce(x, to_dtype(g["w_lm"], w.dtype).astype(np.float64), y, w.eps)
+    O.embed_backward(x, y, w.vocab)
+    t_head = time.perf_counter() - t0
+    total = sum(times[win] for win in w.windows) + t_head
+    return {"value": T / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one block fwd+bwd per layer kind ({len(times)} kinds) at B=1, T={T} and the "
+                      f"head+embedding at {T} tokens, fp64 numpy; per-step time = sum over the {w.n_layer} "
+                      f"layers of their kind's time + head; measured {time.perf_counter() - t_start:.1f} s",
+            "host_cpu_count": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+                                   "(the multi-GPU data-parallel design is described, not built)"}))
+        sys.exit(2)
+    import torch
+    from gpt_decoder_block_amd import ops
+    from gpt_decoder_block_amd.stack import DecoderStack
+    from gpt_decoder_block_amd.workmodel import flops_per_token, flops_per_token_pages, step_flops
+    from seeded_inputs import draw_globals, draw_ids, draw_layer, to_dtype, workload
+
+    w = workload(args.workload)
+    if args.batch:
+        w = w.with_(B=args.batch)
+    if w.extras or w.mlp_fp8:
+        w = w.with_(extras=False, mlp_fp8=False)
+    dev = "cuda:0"
+    st = DecoderStack(n_layer=w.n_layer, B=w.B, T=w.T, C=w.C, n_head=w.n_head, n_kv_head=w.n_kv_head,
+                      head_dim=w.head_dim, mlp_hidden=w.mlp_hidden, vocab=w.vocab, windows=w.windows,
+                      dtype=w.dtype, eps=w.eps, rope_base=w.rope_base, device=dev)
+    print(f"[bench] {w.name}: L={w.n_layer} B={w.B} T={w.T} C={w.C} H={w.n_head}/{w.n_kv_head} "
+          f"dtype={w.dtype}; drawing weights", file=sys.stderr, flush=True)
+    g = draw_globals(w)
+    st._put(st.wte, to_dtype(g["wte"], w.dtype))
+    st._put(st.w_lm, to_dtype(g["w_lm"], w.dtype))
+    for l in range(w.n_layer):
+        p = draw_layer(w, l)
+        for t, k in zip(st.layers[l], st.shapes):
+            st._put(t, to_dtype(p[k], w.dtype))
+    st.set_ids(draw_ids(w))
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        st.step()
+    torch.cuda.synchronize()
+    loss0 = float(st.loss.item())
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record(s)
+    for _ in range(args.steps):
+        st.step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] {args.steps} steps: {ms:.2f} ms/step (wall {wall / args.steps * 1e3:.2f}), loss {loss0:.4f}",
+          file=sys.stderr, flush=True)
+    tokens = w.B * w.T
+    fpt = flops_per_token(w.n_layer, w.C, w.n_head, w.n_kv_head, w.head_dim, w.mlp_hidden, w.vocab, w.T, w.windows)
+    fpt_pages = flops_per_token_pages(w.n_layer, w.C, w.n_head, w.n_kv_head, w.head_dim, w.mlp_hidden, w.vocab,
+                                      w.T, w.windows)
+    tps = tokens / (ms / 1e3)
+    tflops = fpt * tps / 1e12
+    kern = kernel_figures(w, st, args.kernel_reps, torch, ops)
+    dom = kern["gemm_mlp_up_relu2"]
+    roof = {"kernel": "gemm_bf16_k<K-major, K-major, ReLU2 epilogue> (MLP up-projection)",
+            "bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+            "frac": dom["tflops"] / (PEAK_BF16 / 1e12), "traffic": None,
+            "algorithmic_per_launch": f"2*M*N*K = {dom['flops']:.4g} FLOP (M={dom['shape'][0]} tokens, "
+                                      f"N={dom['shape'][1]}, K={dom['shape'][2]})",
+            "avg_launch_ms": dom["ms"]}
+    res = {"metric": METRIC, "value": tps, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+           "config": {"workload": f"{w.name}: {w.n_layer} blocks, C={w.C}, heads {w.n_head}/{w.n_kv_head}x"
+                                  f"{w.head_dim}, MLP {w.mlp_hidden}, vocab {w.vocab}",
+                      "global_batch": w.B, "seq_len": w.T, "windows": sorted(set(w.windows)),
+                      "parallelism": "single GPU"},
+           "tflops": tflops, "pct_bf16_peak": 100.0 * tflops * 1e12 / PEAK_BF16,
+           "flops_per_token": fpt, "flops_per_token_pages_convention": fpt_pages,
+           "tflops_pages_convention": fpt_pages * tps / 1e12,
+           "loss_after_warmup": loss0,
+           "roofline": roof, "kernels": kern}
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()
