@@ -35,32 +35,66 @@ constexpr int TILE_ELEMS = BM * BK;  // elements of one operand tile
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// Global -> registers: 8 vectors of 8 bf16 per thread and operand.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over [base, base + bytes): loads at offsets >= bytes return
+// zero, which implements the ragged-edge predication without branches.
+constexpr unsigned OOB = 0xFFFFFFF0u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+  const unsigned n = bytes > 0xFFFFFF00ull ? 0xFFFFFF00u : (unsigned)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ bf16x8 bload(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// Global -> registers: 8 vectors of 8 bf16 per thread and operand, then
+// registers -> LDS (K-contiguous, swizzled).  The resource is rebased at the
+// tile's first row (K-major) or at (kbeg, first row) (M-major), so offsets
+// stay far below 4 GiB; rows past the operand's end and k past the split's
+// end read as zero.
 template <bool KMAJ>
 struct Loader {
   bf16x8 r[8];
-  // rows [r0, r0+256) of the operand (m for A, n for B), k in [k0, k0+64)
-  __device__ __forceinline__ void load(const bf16* __restrict__ P, int ld, int rows, int K, int r0, int k0, int kend) {
+  __amdgpu_buffer_rsrc_t rs;
+  unsigned off0;      // byte offset of this thread's first vector at k step 0
+  unsigned step;      // bytes to advance per K step
+  unsigned rowstep;   // bytes between the thread's consecutive vectors
+  int kcol, kend_rel; // K-major: this thread's k within a step; split end (relative)
+  __device__ __forceinline__ void init(const bf16* P, int ld, int rows, int r0, int kbeg, int kend) {
     const int t = threadIdx.x;
     if (KMAJ) {
       const int c = t & 7, rr = t >> 3;
-      const int k = k0 + c * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = r0 + rr + 32 * i;
-        if (row < rows && k < kend) r[i] = *(const bf16x8*)(P + (size_t)row * ld + k);
-        else r[i] = bf16x8{};
-      }
+      const bf16* base = P + (size_t)r0 * ld + kbeg;
+      const size_t bytes = rows > r0 ? ((size_t)(rows - r0) * ld - kbeg) * 2 : 0;
+      rs = make_rsrc(base, bytes);
+      off0 = (unsigned)((rr * ld + c * 8) * 2);
+      step = BK * 2;
+      rowstep = (unsigned)(32 * ld * 2);
+      kcol = c * 8;
+      kend_rel = kend - kbeg;
     } else {
       const int mc = t & 31, kb = t >> 5;
-      const int row = r0 + mc * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = k0 + kb * 8 + i;
-        if (row < rows && k < kend) r[i] = *(const bf16x8*)(P + (size_t)k * ld + row);
-        else r[i] = bf16x8{};
-      }
+      const bf16* base = P + (size_t)kbeg * ld + r0;
+      const size_t bytes = (size_t)(kend - kbeg) * ld * 2;
+      rs = make_rsrc(base, bytes);
+      const bool mvalid = r0 + mc * 8 < rows;
+      off0 = mvalid ? (unsigned)(((kb * 8) * ld + mc * 8) * 2) : OOB;
+      step = (unsigned)(BK * ld * 2);
+      rowstep = (unsigned)(ld * 2);
+      kcol = 0;
+      kend_rel = kend - kbeg;
     }
+  }
+  __device__ __forceinline__ void load(int kt) {
+    // invalid vectors get an offset >= 0xFFFFFFF0 (past any resource size):
+    // an OR with an all-ones mask, so the compiler cannot turn it into a branch
+    unsigned bad;
+    if (KMAJ) bad = 0u - (unsigned)(kt * BK + kcol >= kend_rel);
+    else bad = 0u - (unsigned)(off0 == OOB);
+    const unsigned o = (off0 + kt * step) | (bad & OOB);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = bload(rs, (o + i * rowstep) | (bad & OOB));
   }
   __device__ __forceinline__ void store(bf16* __restrict__ S) {
     const int t = threadIdx.x;
@@ -100,6 +134,22 @@ __device__ __forceinline__ void tile_coords(int bid, int nbm, int nbn, int& tm, 
   tn = in / gsize;
 }
 
+// MFMA fragments of one 16-wide k sub-step: 4 row blocks of A, 4 of B.
+__device__ __forceinline__ void load_frags(const bf16* As, const bf16* Bs, int kk, int wm, int wn, int lr,
+                                           int lh, bf16x8* af, bf16x8* bfr) {
+  const int ch = kk * 2 + lh;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = wm * 128 + i * 32 + lr;
+    af[i] = *(const bf16x8*)(As + row * BK + ((ch ^ swz(row)) * 8));
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = wn * 128 + j * 32 + lr;
+    bfr[j] = *(const bf16x8*)(Bs + row * BK + ((ch ^ swz(row)) * 8));
+  }
+}
+
 template <bool AK, bool BK_, int EPI>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) bf16 smem[2][2][TILE_ELEMS];  // [stage][A|B]
@@ -109,14 +159,14 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
   const int m0 = tm * BM, n0 = tn * BN;
   // split-K range
   const int ksplit = ((p.K + p.splits * BK - 1) / (p.splits * BK)) * BK;
-  const int kbeg = blockIdx.y * ksplit;
+  const int kbeg = min(p.K, (int)blockIdx.y * ksplit);
   const int kend = min(p.K, kbeg + ksplit);
-  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  const int nk = (kend - kbeg + BK - 1) / BK;
 
-  const bf16* A = (const bf16*)p.A;
-  const bf16* B = (const bf16*)p.B;
   Loader<AK> la;
   Loader<BK_> lb;
+  la.init((const bf16*)p.A, p.lda, p.M, m0, kbeg, kend);
+  lb.init((const bf16*)p.B, p.ldb, p.N, n0, kbeg, kend);
 
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -128,63 +178,90 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  if (nk > 0) {
-    la.load(A, p.lda, p.M, p.K, m0, kbeg, kend);
-    lb.load(B, p.ldb, p.N, p.K, n0, kbeg, kend);
-    la.store(smem[0][0]);
-    lb.store(smem[0][1]);
-  }
+  la.load(0);
+  lb.load(0);
+  la.store(smem[0][0]);
+  lb.store(smem[0][1]);
   __syncthreads();
+  bf16x8 af[2][4], bfr[2][4];
+  load_frags(smem[0][0], smem[0][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
 
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.load(A, p.lda, p.M, p.K, m0, kbeg + (kt + 1) * BK, kend);
-      lb.load(B, p.ldb, p.N, p.K, n0, kbeg + (kt + 1) * BK, kend);
-    }
+    // next tile (zeros past the end: harmless, the stage it lands in is not read)
+    la.load(kt + 1);
+    lb.load(kt + 1);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch at the top of the step
     const bf16* As = smem[st][0];
     const bf16* Bs = smem[st][1];
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[4], bfr[4];
-      const int ch = kk * 2 + lh;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 128 + i * 32 + lr;
-        af[i] = *(const bf16x8*)(As + row * BK + ((ch ^ swz(row)) * 8));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = wn * 128 + j * 32 + lr;
-        bfr[j] = *(const bf16x8*)(Bs + row * BK + ((ch ^ swz(row)) * 8));
-      }
+      const int cb = kk & 1;
+      if (kk + 1 < BK / 16) load_frags(As, Bs, kk + 1, wm, wn, lr, lh, af[cb ^ 1], bfr[cb ^ 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
+      if (kk + 1 < BK / 16) {
+        // interleave the next sub-step's 8 LDS reads among the 16 MFMAs
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
     }
-    if (more) {
-      la.store(smem[st ^ 1][0]);
-      lb.store(smem[st ^ 1][1]);
-    }
+    la.store(smem[st ^ 1][0]);
+    lb.store(smem[st ^ 1][1]);
     __syncthreads();
+    load_frags(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
   }
 
-  // epilogue: lane holds rows m = m0 + wm*128 + i*32 + lr, columns
-  // n = n0 + wn*128 + j*32 + 8g + 4lh + {0..3} in acc[i][j][4g..4g+3]
+  // Epilogue through LDS, in two passes of 128 rows (the 128 KiB of operand
+  // stages hold a [128][256] fp32 half tile).  Pass q: the waves with wm == q
+  // write their accumulators (lane: 4 consecutive n of row m, 16-byte chunk
+  // XOR-swizzled by the row), then every wave writes whole rows to memory:
+  // 64 lanes x 4 columns = one 256-column row per instruction.
+  float* stage = (float*)&smem[0][0][0];
+  const int ncols = min(BN, p.N - n0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm * 128 + i * 32 + lr;
-    if (m >= p.M) continue;
+  for (int q = 0; q < 2; ++q) {
+    if (wm == q) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+      for (int i = 0; i < 4; ++i) {
+        const int r = i * 32 + lr;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 128 + j * 32 + 8 * g + 4 * lh;
-        if (n >= p.N) continue;
-        float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = (wn * 128 + j * 32 + 8 * g + 4 * lh) >> 2;  // 16-byte chunk (4 floats)
+            *(f32x4*)(stage + r * 256 + ((c ^ (r & 15)) << 2)) =
+                f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          }
+      }
+    }
+    __syncthreads();
+    const int c = lane;            // this lane's 4-column chunk of the row
+    const int n = n0 + c * 4;
+    const bool cok = c * 4 < ncols;
+    constexpr int RPW = 128 / (NTHR / 64);  // rows per wave per pass
+    // residual / saved-u operand for all of this wave's rows, loaded up front
+    bf16x4 rv[RPW];
+    if (EPI == EPI_RESID || EPI == EPI_DRELU2) {
+#pragma unroll
+      for (int k = 0; k < RPW; ++k) {
+        const int m = m0 + q * 128 + w + k * (NTHR / 64);
+        rv[k] = (cok && m < p.M) ? *(const bf16x4*)((const bf16*)p.R + (size_t)m * p.ldr + n) : bf16x4{};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+      const int r = w + k * (NTHR / 64);
+      const int m = m0 + q * 128 + r;
+      if (cok && m < p.M) {
+        const f32x4 v4 = *(const f32x4*)(stage + r * 256 + ((c ^ (r & 15)) << 2));
+        float v[4] = {v4[0], v4[1], v4[2], v4[3]};
         if (EPI == EPI_F32) {
           float* C = (float*)p.C;
           size_t off = (size_t)m * p.ldc + n;
@@ -192,7 +269,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
             C = p.partial + (size_t)blockIdx.y * p.M * p.N;
             off = (size_t)m * p.N + n;
           } else if (p.accumulate) {
-            f32x4 o = *(const f32x4*)(C + off);
+            const f32x4 o = *(const f32x4*)(C + off);
             v[0] += o[0]; v[1] += o[1]; v[2] += o[2]; v[3] += o[3];
           }
           *(f32x4*)(C + off) = f32x4{v[0], v[1], v[2], v[3]};
@@ -201,13 +278,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
           const size_t off = (size_t)m * p.ldc + n;
           bf16x4 o;
           if (EPI == EPI_RESID) {
-            const bf16x4 r = *(const bf16x4*)((const bf16*)p.R + (size_t)m * p.ldr + n);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = (bf16)(v[e] + (float)r[e]);
+            for (int e = 0; e < 4; ++e) o[e] = (bf16)(v[e] + (float)rv[k][e]);
           } else if (EPI == EPI_DRELU2) {
-            const bf16x4 u = *(const bf16x4*)((const bf16*)p.R + (size_t)m * p.ldr + n);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = (bf16)(v[e] * 2.0f * fmaxf((float)u[e], 0.f));
+            for (int e = 0; e < 4; ++e) o[e] = (bf16)(v[e] * 2.0f * fmaxf((float)rv[k][e], 0.f));
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
@@ -217,14 +292,15 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
             bf16x4 h;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float r = fmaxf(v[e], 0.f);
-              h[e] = (bf16)(r * r);
+              const float rl = fmaxf(v[e], 0.f);
+              h[e] = (bf16)(rl * rl);
             }
             *(bf16x4*)((bf16*)p.C2 + off) = h;
           }
         }
       }
     }
+    if (q == 0) __syncthreads();
   }
 }
 
