@@ -81,6 +81,9 @@ def kernel_figures(w, st, reps, torch, ops):
     # attention forward / backward, full causal and windowed
     from gpt_decoder_block_amd.workmodel import attn_pairs
     qkv = rnd(N, W3)
+    qk = qkv[:, :(H + Hkv) * D].float().view(N, H + Hkv, D)   # unit-RMS q, k heads (QK-norm output)
+    qkv[:, :(H + Hkv) * D] = (qk * torch.rsqrt(qk.pow(2).mean(-1, keepdim=True))).view(N, -1).to(dt)
+    del qk
     o = torch.empty(N, H * D, dtype=dt, device=dev)
     lse = torch.empty(w.B, H, w.T, dtype=torch.float32, device=dev)
     do = rnd(N, H * D)
@@ -89,7 +92,8 @@ def kernel_figures(w, st, reps, torch, ops):
     for win in sorted(set(w.windows)):
         pairs = attn_pairs(w.T, win) * w.B * H
         f_fwd, f_bwd = 4.0 * D * pairs, 8.0 * D * pairs
-        tf = ev_time(lambda: ops.attention_fwd(w.B, w.T, H, Hkv, D, win, qkv, W3, o, H * D, lse), reps, torch)
+        tf = ev_time(lambda: ops.attention_fwd(w.B, w.T, H, Hkv, D, win, qkv, W3, o, H * D, lse, qk_normed=True),
+                     reps, torch)
         tb = ev_time(lambda: ops.attention_bwd(w.B, w.T, H, Hkv, D, win, qkv, W3, o, H * D, lse, do, H * D,
                                                dqkv, W3, delta), reps, torch)
         key = "full" if win < 0 else f"window{win}"

@@ -72,8 +72,8 @@ SIGNATURES = {
                                        c_void_p, c_void_p, c_void_p, c_void_p]),
     "gdb_qk_norm_rope_bwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
                                        c_void_p, c_void_p, c_void_p]),
-    "gdb_attention_fwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
-                                    c_int32, c_void_p, c_int32, c_void_p, c_void_p]),
+    "gdb_attention_fwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                    c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p]),
     "gdb_attention_bwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                     c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_int32,
                                     c_void_p, c_void_p]),

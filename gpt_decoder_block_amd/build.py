@@ -18,6 +18,9 @@ OUT = os.path.join(HERE, "libgdb.so")
 BUILD = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 SOURCES = ["elementwise.hip", "gemm.hip", "attention.hip", "api.cpp"]
+# per-file code-generation options: the attention kernels run their softmax on
+# the MFMA results, so those stay in VGPRs (no AGPR round trips)
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -35,7 +38,7 @@ def _flags():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + _flags() + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + _flags() + EXTRA.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stderr}")

@@ -239,6 +239,7 @@ gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
   HIPCHK(qk_norm_rope_fwd(dt, wf.qkv, sv.qkvh, sv.rqk, rope_tab, d.B, d.T, d.H, d.Hkv, d.D, d.eps, s));
   AttnArgs at{};
   at.B = d.B; at.T = d.T; at.H = d.H; at.Hkv = d.Hkv; at.D = d.D; at.window = d.window;
+  at.qk_normed = 1;  // q^, k^ come out of the QK RMS-norm
   at.qkv = sv.qkvh; at.ld = d.W3; at.o = sv.o; at.ldo = d.Q; at.lse = sv.lse;
   HIPCHK(attn_fwd(dt, at, s));
   GemmArgs g = gemm_args(sv.o, true, d.Q, w->w_o, true, d.Q, N, d.C, d.Q, EPI_RESID, wf.x_mid, d.C);
@@ -455,14 +456,16 @@ gdb_status gdb_qk_norm_rope_bwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, in
   return GDB_OK;
 }
 
-gdb_status gdb_attention_fwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t D, int32_t window, int32_t dtype,
-                             const void* qkv, int32_t ld, void* o, int32_t ldo, float* lse, void* stream) {
+gdb_status gdb_attention_fwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t D, int32_t window,
+                             int32_t qk_normed, int32_t dtype, const void* qkv, int32_t ld, void* o, int32_t ldo,
+                             float* lse, void* stream) {
   gdb_status st = check_attn(B, T, H, Hkv, D, window, dtype);
   if (st != GDB_OK) return st;
   if (ld < (H + 2 * Hkv) * D || ld % 8 || ldo < H * D || ldo % 8) return fail(GDB_EINVAL, "bad leading dimension");
   CHECK_PTR(qkv); CHECK_PTR(o); CHECK_PTR(lse);
   AttnArgs at{};
   at.B = B; at.T = T; at.H = H; at.Hkv = Hkv; at.D = D; at.window = window >= T - 1 ? -1 : window;
+  at.qk_normed = qk_normed ? 1 : 0;
   at.qkv = qkv; at.ld = ld; at.o = o; at.ldo = ldo; at.lse = lse;
   HIPCHK(attn_fwd(dtype, at, (hipStream_t)stream));
   g_err.clear();

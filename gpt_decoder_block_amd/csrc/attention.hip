@@ -37,175 +37,261 @@ namespace gdb {
 namespace {
 
 constexpr int HD = 128;  // head_dim of the MFMA path
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// Row-major tile [rows][128] bf16: 16 chunks of 8 per row, XOR-swizzled.
+// Tiles are [64 rows][128] bf16 in LDS, row-major (256 B per row), with the
+// 16-byte chunk index XOR-swizzled by (row & 15).  They are filled by direct
+// global->LDS loads (no staging registers): in each wave instruction, lane L
+// writes the 16 bytes at LDS base + 16L, so lane L fetches the logical chunk
+// that belongs at physical chunk L%16 of row L/16.
 __device__ __forceinline__ int kswz(int row, int chunk) { return chunk ^ (row & 15); }
-// Transposed tile [128 d][64 j] bf16: 16 units of 4 per row, XOR-swizzled.
-__device__ __forceinline__ int tswz(int d, int unit) { return unit ^ ((d ^ (d >> 3)) & 15); }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// read the A-operand of a 32x32x16 MFMA from a transposed tile: row `d`,
-// contraction slots e -> key 16ks + 8(e/4) + 4lh + e%4
-__device__ __forceinline__ bf16x8 ld_t_frag(const bf16* S, int d, int ks, int lh) {
-  const bf16x4 lo = *(const bf16x4*)(S + d * 64 + tswz(d, 4 * ks + lh) * 4);
-  const bf16x4 hi = *(const bf16x4*)(S + d * 64 + tswz(d, 4 * ks + 2 + lh) * 4);
+// Issue the 4 direct loads (per wave) of a 64-row tile; rows past nrows are
+// clamped to the last row (finite values that every use masks out).
+__device__ __forceinline__ void tile_async(const bf16* base, size_t ld, int row0, int nrows, bf16* S) {
+  const int t = threadIdx.x, w = t >> 6, L = t & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = w * 16 + i * 4 + (L >> 4);
+    const int c = kswz(r, L & 15);
+    int row = row0 + r;
+    row = row < nrows ? row : nrows - 1;
+    __builtin_amdgcn_global_load_lds((const void*)(base + (size_t)row * ld + c * 8), (lds_ptr)(S + (w * 16 + i * 4) * HD),
+                                     16, 0, 0);
+  }
+}
+
+// 64 floats (one per lane) straight into LDS; index clamped to n - 1.
+__device__ __forceinline__ void vec64_async(const float* src, int i0, int n, float* S) {
+  const int L = threadIdx.x & 63;
+  int i = i0 + L;
+  i = i < n ? i : n - 1;
+  __builtin_amdgcn_global_load_lds((const void*)(src + i), (lds_ptr)S, 4, 0, 0);
+}
+
+// MFMA operand with rows = tile rows (A of S = K Q^T etc.): lane (row lr of
+// block rb, half lh) reads columns kk*16 + 8lh .. +7.
+__device__ __forceinline__ bf16x8 row_frag(const bf16* S, int rb, int kk, int lr, int lh) {
+  const int row = rb * 32 + lr;
+  return *(const bf16x8*)(S + row * HD + kswz(row, 2 * kk + lh) * 8);
+}
+
+__device__ __forceinline__ bf16x4 tr_read(const bf16* p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p));
+}
+
+// Transposed operand read with the gfx950 LDS transpose load: the MFMA A
+// operand with rows = tile columns d (block db) and contraction over tile
+// rows: lane (d = 32db + lane%32, lh) gets rows 16ks + 8(e/4) + 4lh + e%4,
+// e = 0..7.  In each 16-lane group the hardware returns to lane i element i%4
+// of the 8 bytes addressed by lane 4j + i/4 (j = 0..3), so source lane s
+// addresses row k0 + s/4, columns dbase + 4(s%4) .. +3.
+__device__ __forceinline__ bf16x8 tr_frag(const bf16* S, int db, int ks, int lane) {
+  const int G = lane >> 4, sl = lane & 15;
+  const int lh = G >> 1;
+  const int col = 32 * db + 16 * (G & 1) + 4 * (sl & 3);
+  const int r0 = 16 * ks + 4 * lh + (sl >> 2);
+  const int r1 = r0 + 8;
+  const bf16x4 lo = tr_read(S + r0 * HD + (kswz(r0, col >> 3) << 3) + (col & 7));
+  const bf16x4 hi = tr_read(S + r1 * HD + (kswz(r1, col >> 3) << 3) + (col & 7));
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
-
-// pack the accumulator values of keys (or queries) 16ks..16ks+15 held by this
-// lane into the matching contraction slots (same relabelling as ld_t_frag)
-__device__ __forceinline__ bf16x8 pack_p(const f32x16* s, int ks) {
-  const f32x16& x = s[ks >> 1];
-  const int b = 8 * (ks & 1);
-  return bf16x8{(bf16)x[b + 0], (bf16)x[b + 1], (bf16)x[b + 2], (bf16)x[b + 3],
-                (bf16)x[b + 4], (bf16)x[b + 5], (bf16)x[b + 6], (bf16)x[b + 7]};
-}
-
-// Global -> registers for a 64-row x 128-d tile: each thread loads 4
-// consecutive rows of one 16-byte chunk (row (t>>4)*4 + i, chunk t & 15).
-struct TileRegs {
-  bf16x8 r[4];
-  __device__ __forceinline__ void load(const bf16* base, size_t ld, int row0, int nrows) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = row0 + (t >> 4) * 4 + i;
-      r[i] = row < nrows ? *(const bf16x8*)(base + (size_t)row * ld + (t & 15) * 8) : bf16x8{};
-    }
-  }
-  __device__ __forceinline__ void store_rows(bf16* S) const {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (t >> 4) * 4 + i;
-      *(bf16x8*)(S + row * HD + kswz(row, t & 15) * 8) = r[i];
-    }
-  }
-  __device__ __forceinline__ void store_trans(bf16* S) const {
-    const int t = threadIdx.x;
-    const int unit = t >> 4;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int d = (t & 15) * 8 + jj;
-      *(bf16x4*)(S + d * 64 + tswz(d, unit) * 4) = bf16x4{r[0][jj], r[1][jj], r[2][jj], r[3][jj]};
-    }
-  }
-};
 
 __device__ __forceinline__ bool visible(int i, int j, int T, int W) {
   return j < T && j <= i && (W < 0 || i - j <= W);
 }
 
+// wait until at most N vector-memory operations of this wave are in flight
+#define WAIT_VM(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
+
 // ----------------------------------------------------------------- forward
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_k(AttnArgs a, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][64 * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[2][HD * 64];
-  const int T = a.T, H = a.H, Hkv = a.Hkv, W = a.window;
-  const int nqb = (T + 127) / 128;
-  const int qb = nqb - 1 - (int)blockIdx.x;  // heaviest query blocks first
-  const int b = blockIdx.y / H, h = blockIdx.y % H, g = h / (H / Hkv);
-  const int q0 = qb * 128;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 31, lh = lane >> 5;
-  const int qi = q0 + w * 32 + lr;
-  const bf16* base = (const bf16*)a.qkv + (size_t)b * T * a.ld;
-  const bf16* kbase = base + (H + g) * HD;
-  const bf16* vbase = base + (H + Hkv + g) * HD;
+// Workgroup: IB*128 query rows of one (b, h); wave w owns IB blocks of 32
+// rows (the K and V fragments read from LDS serve every block of the wave).
+// Lane (lr, lh) of block ib holds query q0 + 32*IB*w + 32ib + lr.  K and V
+// tiles of 64 keys stream through 3 LDS stages, two tiles ahead.
+//
+// BOUNDED: q^ and k^ come out of the QK RMS-norm (no affine), so each has
+// norm <= sqrt(D) and every score q^.k^/sqrt(D) lies in [-sqrt(D), sqrt(D)].
+// Softmax is invariant to a shift, so the fixed offset M = sqrt(D) (with 1%
+// margin for bf16 rounding of q^, k^) replaces the running row max: no max
+// reduction, no rescaling of O, and exp never overflows.  Otherwise the usual
+// online max with rescaling.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-  bf16x8 qf[8];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    qf[kk] = qi < T ? *(const bf16x8*)(base + (size_t)qi * a.ld + h * HD + kk * 16 + lh * 8) : bf16x8{};
-
-  int kv_lo = W >= 0 ? max(0, q0 - W) : 0;
-  kv_lo &= ~63;
-  const int kv_hi = min(T, q0 + 128);
-  const int ntile = (kv_hi - kv_lo + 63) / 64;
-
-  TileRegs kr, vr;
-  kr.load(kbase, a.ld, kv_lo, T);
-  vr.load(vbase, a.ld, kv_lo, T);
-  kr.store_rows(Ks[0]);
-  vr.store_trans(Vt[0]);
-  __syncthreads();
-
-  f32x16 o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float m = -INFINITY, l = 0.f;
-
-  for (int it = 0; it < ntile; ++it) {
-    const int st = it & 1;
-    const int kv0 = kv_lo + it * 64;
-    const bool more = it + 1 < ntile;
-    if (more) {
-      kr.load(kbase, a.ld, kv0 + 64, T);
-      vr.load(vbase, a.ld, kv0 + 64, T);
-    }
-    f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        const int row = jb * 32 + lr;
-        const bf16x8 kf = *(const bf16x8*)(Ks[st] + row * HD + kswz(row, 2 * kk + lh) * 8);
-        s[jb] = mfma32(kf, qf[kk], s[jb]);
-      }
-    }
+// Probabilities of one 32-query x 64-key tile for this lane's query, written
+// straight into the bf16 operand registers of the P V^T MFMA (pk[ks] = keys
+// 16ks..16ks+15 in contraction-slot order).  The row sum l accumulates the
+// bf16-rounded weights (v_dot2 with ones), so O is an exact convex
+// combination of V rows whatever the rounding of P.
+template <bool MASK, bool BOUNDED>
+__device__ __forceinline__ void softmax_pack(const f32x16 (&s)[2], bf16x8 (&pk)[4], int qi, int kv0, int lh, int T,
+                                             int W, float scale_log2, float& m, float& l, float& alpha) {
+  float msafe;
+  if (BOUNDED) {
+    msafe = m;
+    alpha = 1.0f;
+  } else {
     float mx = -INFINITY;
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int j = kv0 + jb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-        const float x = visible(qi, j, T, W) ? s[jb][v] * scale_log2 : -INFINITY;
-        s[jb][v] = x;
-        mx = fmaxf(mx, x);
+        mx = fmaxf(mx, (!MASK || visible(qi, j, T, W)) ? s[jb][v] : -INFINITY);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(m, mx);
-    const float msafe = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(m - msafe);
+    // running max in the log2 domain (scores scaled by scale*log2(e))
+    const float mnew = fmaxf(m, mx * scale_log2);
+    msafe = mnew == -INFINITY ? 0.f : mnew;
+    alpha = __builtin_amdgcn_exp2f(m - msafe);  // exactly 1 when the max did not move
     l *= alpha;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] *= alpha;
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(s[jb][v] - msafe);
-        s[jb][v] = p;
-        l += p;
-      }
     m = mnew;
+  }
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 pf = pack_p(s, ks);
+  for (int ks = 0; ks < 4; ++ks) {
+    bf16x8 out;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] = mfma32(ld_t_frag(Vt[st], db * 32 + lr, ks, lh), pf, o[db]);
+    for (int e = 0; e < 8; ++e) {
+      const int jb = ks >> 1, v = 8 * (ks & 1) + e;
+      float p = __builtin_amdgcn_exp2f(fmaf(s[jb][v], scale_log2, -msafe));
+      if (MASK) {
+        const int j = kv0 + jb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+        if (!visible(qi, j, T, W)) p = 0.f;
+      }
+      out[e] = (bf16)p;
     }
-    if (more) {
-      kr.store_rows(Ks[st ^ 1]);
-      vr.store_trans(Vt[st ^ 1]);
+    pk[ks] = out;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{out[2 * q], out[2 * q + 1]}, ones, l, false);
+  }
+}
+
+template <int IB, bool BOUNDED>
+__global__ __launch_bounds__(256, 1) void attn_fwd_bf16_k(AttnArgs a, float scale_log2) {
+  constexpr int FQ = 128 * IB;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[3][64 * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[3][64 * HD];
+  const int T = a.T, H = a.H, Hkv = a.Hkv, W = a.window;
+  // grid (B*H, query blocks): every head's heaviest query block is dispatched first
+  const int nqb = (T + FQ - 1) / FQ;
+  const int qb = nqb - 1 - (int)blockIdx.y;
+  const int b = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / Hkv);
+  const int q0 = qb * FQ;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 31, lh = lane >> 5;
+  const int qw0 = q0 + w * 32 * IB;          // first query of this wave
+  const bf16* base = (const bf16*)a.qkv + (size_t)b * T * a.ld;
+  const bf16* kbase = base + (H + g) * HD;
+  const bf16* vbase = base + (H + Hkv + g) * HD;
+
+  int kv_lo = W >= 0 ? max(0, q0 - W) : 0;
+  kv_lo &= ~63;
+  const int kv_hi = min(T, q0 + FQ);
+  const int ntile = (kv_hi - kv_lo + 63) / 64;
+  // this wave's visible key range
+  const int wq_hi = min(qw0 + 32 * IB - 1, T - 1);
+  const int wk_lo = W >= 0 ? max(0, qw0 - W) : 0;
+
+  tile_async(kbase, a.ld, kv_lo, T, Ks[0]);
+  tile_async(vbase, a.ld, kv_lo, T, Vs[0]);
+  if (ntile > 1) {
+    tile_async(kbase, a.ld, kv_lo + 64, T, Ks[1]);
+    tile_async(vbase, a.ld, kv_lo + 64, T, Vs[1]);
+  }
+
+  bf16x8 qf[IB][8];
+#pragma unroll
+  for (int ib = 0; ib < IB; ++ib) {
+    const int qi = min(qw0 + ib * 32 + lr, T - 1);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qf[ib][kk] = *(const bf16x8*)(base + (size_t)qi * a.ld + h * HD + kk * 16 + lh * 8);
+  }
+  f32x16 o[IB][4];
+  float m[IB], l[IB];
+#pragma unroll
+  for (int ib = 0; ib < IB; ++ib) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[ib][i] = f32x16{};
+    m[ib] = BOUNDED ? 1.01f * sqrtf((float)HD) * scale_log2 : -INFINITY;
+    l[ib] = 0.f;
+  }
+  WAIT_VM(0);
+  __syncthreads();
+
+  for (int it = 0; it < ntile; ++it) {
+    const int st = it % 3;
+    const int kv0 = kv_lo + it * 64;
+    const bool ahead = it + 2 < ntile;
+    if (ahead) {
+      const int sn = (it + 2) % 3;
+      tile_async(kbase, a.ld, kv0 + 128, T, Ks[sn]);
+      tile_async(vbase, a.ld, kv0 + 128, T, Vs[sn]);
     }
+    // wave-uniform: does the tile touch this wave's rows, and is it fully visible?
+    const bool any = qw0 < T && kv0 <= wq_hi && kv0 + 63 >= wk_lo;
+    if (any) {
+      const bool full = kv0 + 63 <= qw0 && kv0 + 63 < T && (W < 0 || wq_hi - kv0 <= W);
+      f32x16 s[IB][2];
+#pragma unroll
+      for (int ib = 0; ib < IB; ++ib) s[ib][0] = s[ib][1] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          const bf16x8 kf = row_frag(Ks[st], jb, kk, lr, lh);
+#pragma unroll
+          for (int ib = 0; ib < IB; ++ib) s[ib][jb] = mfma32(kf, qf[ib][kk], s[ib][jb]);
+        }
+      }
+      bf16x8 pk[IB][4];
+#pragma unroll
+      for (int ib = 0; ib < IB; ++ib) {
+        const int qi = qw0 + ib * 32 + lr;
+        float alpha;
+        if (full) softmax_pack<false, BOUNDED>(s[ib], pk[ib], qi, kv0, lh, T, W, scale_log2, m[ib], l[ib], alpha);
+        else softmax_pack<true, BOUNDED>(s[ib], pk[ib], qi, kv0, lh, T, W, scale_log2, m[ib], l[ib], alpha);
+        if (!BOUNDED && __any(alpha != 1.0f)) {
+#pragma unroll
+          for (int db = 0; db < 4; ++db) o[ib][db] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16x8 vf = tr_frag(Vs[st], db, ks, lane);
+#pragma unroll
+          for (int ib = 0; ib < IB; ++ib) o[ib][db] = mfma32(vf, pk[ib][ks], o[ib][db]);
+        }
+      }
+    }
+    if (ahead) WAIT_VM(8);  // tile it+1 landed; tile it+2 may still be in flight
+    else WAIT_VM(0);
     __syncthreads();
   }
 
-  const float lt = l + __shfl_xor(l, 32, 64);
-  if (qi < T) {
-    const float inv = 1.0f / lt;
-    bf16* orow = (bf16*)a.o + ((size_t)b * T + qi) * a.ldo + h * HD;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int ib = 0; ib < IB; ++ib) {
+    const int qi = qw0 + ib * 32 + lr;
+    const float lt = l[ib] + __shfl_xor(l[ib], 32, 64);
+    if (qi < T) {
+      const float inv = 1.0f / lt;
+      bf16* orow = (bf16*)a.o + ((size_t)b * T + qi) * a.ldo + h * HD;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d = db * 32 + 8 * gq + 4 * lh;
-        *(bf16x4*)(orow + d) = bf16x4{(bf16)(o[db][4 * gq] * inv), (bf16)(o[db][4 * gq + 1] * inv),
-                                      (bf16)(o[db][4 * gq + 2] * inv), (bf16)(o[db][4 * gq + 3] * inv)};
-      }
-    if (lh == 0) a.lse[((size_t)b * H + h) * T + qi] = (m + __log2f(lt)) * 0.69314718055994531f;
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d = db * 32 + 8 * gq + 4 * lh;
+          *(bf16x4*)(orow + d) = bf16x4{(bf16)(o[ib][db][4 * gq] * inv), (bf16)(o[ib][db][4 * gq + 1] * inv),
+                                        (bf16)(o[ib][db][4 * gq + 2] * inv), (bf16)(o[ib][db][4 * gq + 3] * inv)};
+        }
+      if (lh == 0) a.lse[((size_t)b * H + h) * T + qi] = (m[ib] + __log2f(lt)) * 0.69314718055994531f;
+    }
   }
 }
 
@@ -227,109 +313,109 @@ __global__ __launch_bounds__(256) void attn_delta_k(AttnArgs a) {
 }
 
 // ------------------------------------------------------ backward: dK, dV
+// Workgroup: 128 keys of one (b, kv head), 32 per wave (lane = key).  Loops
+// over the query heads of the group and the visible 64-row query tiles; Q,
+// dO (row-major) and the tile's log-sum-exp and delta stream through 3 LDS
+// stages.  dV^T += dO^T P and dK^T += Q^T dS accumulate in registers, with
+// the transposed operands read by the LDS transpose load.
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_bf16_k(AttnArgs a, float scale_log2, float scale) {
-  __shared__ __attribute__((aligned(16))) bf16 Qs[2][64 * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Qt[2][HD * 64];
-  __shared__ __attribute__((aligned(16))) bf16 Ds[2][64 * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Dt[2][HD * 64];
-  __shared__ __attribute__((aligned(16))) float Ls[2][64];
-  __shared__ __attribute__((aligned(16))) float Dl[2][64];
+  __shared__ __attribute__((aligned(16))) bf16 Qs[3][64 * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Ds[3][64 * HD];
+  __shared__ __attribute__((aligned(16))) float Ls[3][4][64];  // [stage][lse, delta, spare, spare][row]
   const int T = a.T, H = a.H, Hkv = a.Hkv, W = a.window, G = H / Hkv;
-  const int b = blockIdx.y / Hkv, g = blockIdx.y % Hkv;
-  const int kv0 = blockIdx.x * 128;
+  const int b = blockIdx.x / Hkv, g = blockIdx.x % Hkv;   // grid (B*Hkv, key blocks), heaviest first
+  const int kv0 = blockIdx.y * 128;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 31, lh = lane >> 5;
   const int kj = kv0 + w * 32 + lr;  // this lane's key
   const bf16* base = (const bf16*)a.qkv + (size_t)b * T * a.ld;
   const bf16* dbase = (const bf16*)a.dout + (size_t)b * T * a.lddo;
 
-  bf16x8 kf[8], vf[8];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    const size_t roff = (size_t)kj * a.ld + kk * 16 + lh * 8;
-    kf[kk] = kj < T ? *(const bf16x8*)(base + roff + (H + g) * HD) : bf16x8{};
-    vf[kk] = kj < T ? *(const bf16x8*)(base + roff + (H + Hkv + g) * HD) : bf16x8{};
-  }
-  f32x16 dk[4], dv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
-
   const int q_lo = kv0;  // multiple of 64
   const int q_hi = W >= 0 ? min(T, kv0 + 128 + W) : T;
   const int nqt = q_hi > q_lo ? (q_hi - q_lo + 63) / 64 : 0;
   const int total = nqt * G;
+  // wave's keys
+  const int wk0 = kv0 + w * 32, wk_hi = min(wk0 + 31, T - 1);
 
-  TileRegs qr, dr;
-  float lsev = 0.f, delv = 0.f;
-  auto gload = [&](int it) {
+  auto issue = [&](int it, int stg) {
     const int hh = g * G + it / nqt;
     const int i0 = q_lo + (it % nqt) * 64;
-    qr.load(base + hh * HD, a.ld, i0, T);
-    dr.load(dbase + hh * HD, a.lddo, i0, T);
-    if (t < 64) {
-      const int i = i0 + t;
-      const size_t li = ((size_t)b * H + hh) * T + i;
-      lsev = i < T ? a.lse[li] * 1.4426950408889634f : 0.f;
-      delv = i < T ? a.delta[li] : 0.f;
+    tile_async(base + hh * HD, a.ld, i0, T, Qs[stg]);
+    tile_async(dbase + hh * HD, a.lddo, i0, T, Ds[stg]);
+    const size_t lo = ((size_t)b * H + hh) * T;
+    vec64_async((w & 1) ? a.delta + lo : a.lse + lo, i0, T, Ls[stg][w]);
+  };
+  if (total > 0) issue(0, 0);
+  if (total > 1) issue(1, 1);
+
+  bf16x8 kf[8], vf[8];
+  {
+    const int kc = min(kj, T - 1);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const size_t roff = (size_t)kc * a.ld + kk * 16 + lh * 8;
+      kf[kk] = *(const bf16x8*)(base + roff + (H + g) * HD);
+      vf[kk] = *(const bf16x8*)(base + roff + (H + Hkv + g) * HD);
     }
-  };
-  auto sstore = [&](int st) {
-    qr.store_rows(Qs[st]);
-    qr.store_trans(Qt[st]);
-    dr.store_rows(Ds[st]);
-    dr.store_trans(Dt[st]);
-    if (t < 64) { Ls[st][t] = lsev; Dl[st][t] = delv; }
-  };
-  if (total > 0) {
-    gload(0);
-    sstore(0);
   }
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
+  WAIT_VM(0);
   __syncthreads();
 
   for (int it = 0; it < total; ++it) {
-    const int st = it & 1;
+    const int st = it % 3;
     const int i0 = q_lo + (it % nqt) * 64;
-    const bool more = it + 1 < total;
-    if (more) gload(it + 1);
-    // S[i][j] and dP[i][j]: lane = key j, registers = queries
-    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    const bool ahead = it + 2 < total;
+    if (ahead) issue(it + 2, (it + 2) % 3);
+    // wave-uniform visibility of this query tile for the wave's 32 keys
+    const int iq_hi = min(i0 + 63, T - 1);
+    const bool any = wk0 < T && i0 + 63 >= wk0 && (W < 0 || i0 - wk_hi <= W);
+    if (any) {
+      const bool full = i0 >= wk_hi && iq_hi < T && (W < 0 || iq_hi - wk0 <= W) && i0 + 63 < T;
+      // S[i][j] and dP[i][j]: lane = key j, registers = queries
+      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+      for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
-        const int row = ib * 32 + lr;
-        const bf16x8 qa = *(const bf16x8*)(Qs[st] + row * HD + kswz(row, 2 * kk + lh) * 8);
-        const bf16x8 da = *(const bf16x8*)(Ds[st] + row * HD + kswz(row, 2 * kk + lh) * 8);
-        s[ib] = mfma32(qa, kf[kk], s[ib]);
-        dp[ib] = mfma32(da, vf[kk], dp[ib]);
+        for (int ib = 0; ib < 2; ++ib) {
+          s[ib] = mfma32(row_frag(Qs[st], ib, kk, lr, lh), kf[kk], s[ib]);
+          dp[ib] = mfma32(row_frag(Ds[st], ib, kk, lr, lh), vf[kk], dp[ib]);
+        }
       }
-    }
+      // P and dS straight into bf16 operand registers (slot order of tr_frag)
+      bf16x8 pf[4], sf[4];
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
+      for (int ks = 0; ks < 4; ++ks) {
+        const int ib = ks >> 1;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int il = ib * 32 + 8 * gq + 4 * lh;
-        const f32x4 L4 = *(const f32x4*)(&Ls[st][il]);
-        const f32x4 D4 = *(const f32x4*)(&Dl[st][il]);
+        for (int hq = 0; hq < 2; ++hq) {
+          const int gq = 2 * (ks & 1) + hq;
+          const int il = ib * 32 + 8 * gq + 4 * lh;
+          const f32x4 L4 = *(const f32x4*)(&Ls[st][0][il]);
+          const f32x4 D4 = *(const f32x4*)(&Ls[st][1][il]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int v = 4 * gq + r;
-          const int i = i0 + il + r;
-          const float p = visible(i, kj, T, W) && i < T ? __builtin_amdgcn_exp2f(s[ib][v] * scale_log2 - L4[r]) : 0.f;
-          s[ib][v] = p;
-          dp[ib][v] = p * (dp[ib][v] - D4[r]);
+          for (int r = 0; r < 4; ++r) {
+            const int v = 4 * gq + r;
+            float p = __builtin_amdgcn_exp2f(fmaf(s[ib][v], scale_log2, -L4[r] * 1.4426950408889634f));
+            if (!full && !(visible(i0 + il + r, kj, T, W) && i0 + il + r < T)) p = 0.f;
+            pf[ks][4 * hq + r] = (bf16)p;
+            sf[ks][4 * hq + r] = (bf16)(p * (dp[ib][v] - D4[r]));
+          }
         }
       }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 pf = pack_p(s, ks);
-      const bf16x8 sf = pack_p(dp, ks);
+      for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        dv[db] = mfma32(ld_t_frag(Dt[st], db * 32 + lr, ks, lh), pf, dv[db]);
-        dk[db] = mfma32(ld_t_frag(Qt[st], db * 32 + lr, ks, lh), sf, dk[db]);
+        for (int db = 0; db < 4; ++db) {
+          dv[db] = mfma32(tr_frag(Ds[st], db, ks, lane), pf[ks], dv[db]);
+          dk[db] = mfma32(tr_frag(Qs[st], db, ks, lane), sf[ks], dk[db]);
+        }
       }
     }
-    if (more) sstore(st ^ 1);
+    if (ahead) WAIT_VM(9);
+    else WAIT_VM(0);
     __syncthreads();
   }
 
@@ -350,87 +436,97 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_bf16_k(AttnArgs a, float 
 }
 
 // ------------------------------------------------------------ backward: dQ
+// Workgroup: 128 query rows of one (b, h), 32 per wave (lane = query).  K and
+// V tiles of 64 keys stream through 3 LDS stages; dQ^T += K^T dS^T with K^T
+// read by the LDS transpose load.
 __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_k(AttnArgs a, float scale_log2, float scale) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][64 * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Kt[2][HD * 64];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][64 * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[3][64 * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[3][64 * HD];
   const int T = a.T, H = a.H, Hkv = a.Hkv, W = a.window;
   const int nqb = (T + 127) / 128;
-  const int qb = nqb - 1 - (int)blockIdx.x;
-  const int b = blockIdx.y / H, h = blockIdx.y % H, g = h / (H / Hkv);
+  const int qb = nqb - 1 - (int)blockIdx.y;   // grid (B*H, query blocks), heaviest first
+  const int b = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / Hkv);
   const int q0 = qb * 128;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 31, lh = lane >> 5;
   const int qi = q0 + w * 32 + lr;
+  const int qw0 = q0 + w * 32, wq_hi = min(qw0 + 31, T - 1);
+  const int wk_lo = W >= 0 ? max(0, qw0 - W) : 0;
   const bf16* base = (const bf16*)a.qkv + (size_t)b * T * a.ld;
   const bf16* kbase = base + (H + g) * HD;
   const bf16* vbase = base + (H + Hkv + g) * HD;
-
-  bf16x8 qf[8], df[8];
-  const bf16* drow = (const bf16*)a.dout + ((size_t)b * T + qi) * a.lddo + h * HD;
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    qf[kk] = qi < T ? *(const bf16x8*)(base + (size_t)qi * a.ld + h * HD + kk * 16 + lh * 8) : bf16x8{};
-    df[kk] = qi < T ? *(const bf16x8*)(drow + kk * 16 + lh * 8) : bf16x8{};
-  }
-  const size_t li = ((size_t)b * H + h) * T + qi;
-  const float lse2 = qi < T ? a.lse[li] * 1.4426950408889634f : 0.f;
-  const float dlt = qi < T ? a.delta[li] : 0.f;
 
   int kv_lo = W >= 0 ? max(0, q0 - W) : 0;
   kv_lo &= ~63;
   const int kv_hi = min(T, q0 + 128);
   const int ntile = (kv_hi - kv_lo + 63) / 64;
 
-  TileRegs kr, vr;
-  kr.load(kbase, a.ld, kv_lo, T);
-  vr.load(vbase, a.ld, kv_lo, T);
-  kr.store_rows(Ks[0]);
-  kr.store_trans(Kt[0]);
-  vr.store_rows(Vs[0]);
-  __syncthreads();
-
+  tile_async(kbase, a.ld, kv_lo, T, Ks[0]);
+  tile_async(vbase, a.ld, kv_lo, T, Vs[0]);
+  if (ntile > 1) {
+    tile_async(kbase, a.ld, kv_lo + 64, T, Ks[1]);
+    tile_async(vbase, a.ld, kv_lo + 64, T, Vs[1]);
+  }
+  bf16x8 qf[8], df[8];
+  const int qc = min(qi, T - 1);
+  const bf16* drow = (const bf16*)a.dout + ((size_t)b * T + qc) * a.lddo + h * HD;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    qf[kk] = *(const bf16x8*)(base + (size_t)qc * a.ld + h * HD + kk * 16 + lh * 8);
+    df[kk] = *(const bf16x8*)(drow + kk * 16 + lh * 8);
+  }
+  const size_t li = ((size_t)b * H + h) * T + qc;
+  const float lse2 = a.lse[li] * 1.4426950408889634f;
+  const float dlt = a.delta[li];
   f32x16 dq[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) dq[i] = f32x16{};
+  WAIT_VM(0);
+  __syncthreads();
 
   for (int it = 0; it < ntile; ++it) {
-    const int st = it & 1;
+    const int st = it % 3;
     const int kv0 = kv_lo + it * 64;
-    const bool more = it + 1 < ntile;
-    if (more) {
-      kr.load(kbase, a.ld, kv0 + 64, T);
-      vr.load(vbase, a.ld, kv0 + 64, T);
+    const bool ahead = it + 2 < ntile;
+    if (ahead) {
+      const int sn = (it + 2) % 3;
+      tile_async(kbase, a.ld, kv0 + 128, T, Ks[sn]);
+      tile_async(vbase, a.ld, kv0 + 128, T, Vs[sn]);
     }
-    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    const bool any = qw0 < T && kv0 <= wq_hi && kv0 + 63 >= wk_lo;
+    if (any) {
+      const bool full = kv0 + 63 <= qw0 && kv0 + 63 < T && (W < 0 || wq_hi - kv0 <= W);
+      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+      for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        const int row = jb * 32 + lr;
-        const int off = row * HD + kswz(row, 2 * kk + lh) * 8;
-        s[jb] = mfma32(*(const bf16x8*)(Ks[st] + off), qf[kk], s[jb]);
-        dp[jb] = mfma32(*(const bf16x8*)(Vs[st] + off), df[kk], dp[jb]);
+        for (int jb = 0; jb < 2; ++jb) {
+          s[jb] = mfma32(row_frag(Ks[st], jb, kk, lr, lh), qf[kk], s[jb]);
+          dp[jb] = mfma32(row_frag(Vs[st], jb, kk, lr, lh), df[kk], dp[jb]);
+        }
+      }
+      bf16x8 sf[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int jb = ks >> 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int v = 8 * (ks & 1) + e;
+          float p = __builtin_amdgcn_exp2f(fmaf(s[jb][v], scale_log2, -lse2));
+          if (!full) {
+            const int j = kv0 + jb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+            if (!visible(qi, j, T, W)) p = 0.f;
+          }
+          sf[ks][e] = (bf16)(p * (dp[jb][v] - dlt));
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) dq[db] = mfma32(tr_frag(Ks[st], db, ks, lane), sf[ks], dq[db]);
       }
     }
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int j = kv0 + jb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-        const float p = visible(qi, j, T, W) ? __builtin_amdgcn_exp2f(s[jb][v] * scale_log2 - lse2) : 0.f;
-        dp[jb][v] = p * (dp[jb][v] - dlt);
-      }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 sf = pack_p(dp, ks);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) dq[db] = mfma32(ld_t_frag(Kt[st], db * 32 + lr, ks, lh), sf, dq[db]);
-    }
-    if (more) {
-      kr.store_rows(Ks[st ^ 1]);
-      kr.store_trans(Kt[st ^ 1]);
-      vr.store_rows(Vs[st ^ 1]);
-    }
+    if (ahead) WAIT_VM(8);
+    else WAIT_VM(0);
     __syncthreads();
   }
   if (qi < T) {
@@ -543,8 +639,13 @@ hipError_t attn_fwd(int dt, const AttnArgs& a, hipStream_t s) {
   if (a.B * a.T == 0) return hipSuccess;
   const float scale = 1.0f / sqrtf((float)a.D);
   if (dt == BF16) {
-    dim3 g((a.T + 127) / 128, a.B * a.H);
-    hipLaunchKernelGGL(attn_fwd_bf16_k, g, dim3(256), 0, s, a, scale * 1.4426950408889634f);
+    if (a.qk_normed) {
+      dim3 g(a.B * a.H, (a.T + 255) / 256);
+      hipLaunchKernelGGL((attn_fwd_bf16_k<2, true>), g, dim3(256), 0, s, a, scale * 1.4426950408889634f);
+    } else {
+      dim3 g(a.B * a.H, (a.T + 127) / 128);
+      hipLaunchKernelGGL((attn_fwd_bf16_k<1, false>), g, dim3(256), 0, s, a, scale * 1.4426950408889634f);
+    }
   } else {
     dim3 g((a.B * a.H * a.T + 63) / 64);
     if (a.D == 64) hipLaunchKernelGGL(attn_fwd_f32_k<64>, g, dim3(64), 0, s, a, scale);
@@ -562,11 +663,11 @@ hipError_t attn_bwd(int dt, const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (dt == BF16) {
-    hipLaunchKernelGGL(attn_bwd_dkv_bf16_k, dim3((a.T + 127) / 128, a.B * a.Hkv), dim3(256), 0, s, a,
+    hipLaunchKernelGGL(attn_bwd_dkv_bf16_k, dim3(a.B * a.Hkv, (a.T + 127) / 128), dim3(256), 0, s, a,
                        scale * 1.4426950408889634f, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_bwd_dq_bf16_k, dim3((a.T + 127) / 128, a.B * a.H), dim3(256), 0, s, a,
+    hipLaunchKernelGGL(attn_bwd_dq_bf16_k, dim3(a.B * a.H, (a.T + 127) / 128), dim3(256), 0, s, a,
                        scale * 1.4426950408889634f, scale);
   } else {
     dim3 gq((a.B * a.H * a.T + 63) / 64), gk((a.B * a.Hkv * a.T + 63) / 64);

@@ -67,6 +67,7 @@ int gemm_splits(int dt, int M, int N, int K, int epi);
 // q, k, v: rows of qkvh [N, ld] at column offsets 0, H*D, (H+Hkv)*D.
 struct AttnArgs {
   int B, T, H, Hkv, D, window;
+  int qk_normed;                  // q^, k^ rows have RMS <= 1 (QK RMS-norm output)
   const void* qkv; int ld;        // q^, k^, v (row stride ld)
   void* o; int ldo;               // [N, H*D]
   float* lse;                     // [B, H, T]

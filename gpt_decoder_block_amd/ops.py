@@ -146,9 +146,9 @@ def qk_norm_rope_bwd(B: int, T: int, H: int, Hkv: int, D: int, d: torch.Tensor, 
 
 
 def attention_fwd(B: int, T: int, H: int, Hkv: int, D: int, window: int, qkv: torch.Tensor, ld: int,
-                  o: torch.Tensor, ldo: int, lse: torch.Tensor) -> None:
-    L.call("gdb_attention_fwd", B, T, H, Hkv, D, window, dtype_code(qkv.dtype), _p(qkv), ld, _p(o), ldo, _p(lse),
-           _stream(qkv))
+                  o: torch.Tensor, ldo: int, lse: torch.Tensor, qk_normed: bool = False) -> None:
+    L.call("gdb_attention_fwd", B, T, H, Hkv, D, window, int(qk_normed), dtype_code(qkv.dtype), _p(qkv), ld, _p(o),
+           ldo, _p(lse), _stream(qkv))
 
 
 def attention_bwd(B: int, T: int, H: int, Hkv: int, D: int, window: int, qkv: torch.Tensor, ld: int,

@@ -205,10 +205,14 @@ gdb_status gdb_qk_norm_rope_bwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, in
  * k heads at (H + g)*D and v heads at (H + Hkv + g)*D:
  *   o[n, h*D + d] = sum_j P_ij v_j[d],  P = softmax over visible j of q.k / sqrt(D);
  *   lse float32 [B, H, T] = log-sum-exp of each row of scaled scores.
- * window as in gdb_block_cfg.  bf16: D = 128 only. */
+ * window as in gdb_block_cfg.  bf16: D = 128 only.
+ * qk_normed != 0 promises that every q and k head vector has RMS <= 1 (the
+ * output of the QK RMS-norm, as in gdb_block_fwd); then |score| <= sqrt(D)
+ * and the kernel uses that fixed softmax offset instead of a running max.
+ * With larger vectors and qk_normed != 0 the result is undefined. */
 gdb_status gdb_attention_fwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t D, int32_t window,
-                             int32_t dtype, const void* qkv, int32_t ld, void* o, int32_t ldo, float* lse,
-                             void* stream);
+                             int32_t qk_normed, int32_t dtype, const void* qkv, int32_t ld, void* o,
+                             int32_t ldo, float* lse, void* stream);
 /* Attention backward: from dO [B*T, lddo] writes dq, dk, dv into dqkv [B*T, lddq]
  * at the same column offsets as qkv (dk, dv summed over the query heads that
  * share a K/V head). delta: float32 scratch [B, H, T]. */
