@@ -37,7 +37,32 @@ def parse():
     ap.add_argument("--batch", type=int, default=None, help="override B (default: the workload's)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--counter-run", action="store_true",
+                    help="only launch the roofline kernel (MLP up-projection GEMM at the workload's shape) 3 times "
+                         "and a 1 GiB device copy 3 times, for hardware-counter collection")
     return ap.parse_args()
+
+
+def counter_run(w):
+    """Launch sequence for rocprofv3 --pmc passes: the roofline kernel, then a
+    plain copy of known size (its FETCH_SIZE / WRITE_SIZE readings calibrate
+    the counters to bytes)."""
+    import torch
+    from gpt_decoder_block_amd import ops
+    dev, dt = "cuda:0", torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    N, C, F = w.B * w.T, w.C, w.mlp_hidden
+    g = torch.Generator(device=dev).manual_seed(1)
+    A = torch.randn(N, C, generator=g, device=dev).to(dt)
+    B = (torch.randn(F, C, generator=g, device=dev) * 0.02).to(dt)
+    U, Hh = torch.empty(N, F, dtype=dt, device=dev), torch.empty(N, F, dtype=dt, device=dev)
+    for _ in range(3):
+        ops.gemm(N, F, C, A, True, C, B, True, C, ops.EPI_RELU2, U, F, C2=Hh)
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)   # 1 GiB
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"counter_run": True, "gemm_shape": [N, F, C], "copy_bytes": src.numel() * 4}))
 
 
 def ev_time(fn, reps, torch):
@@ -63,8 +88,12 @@ def kernel_figures(w, st, reps, torch, ops):
     g = torch.Generator(device=dev).manual_seed(1)
     rnd = lambda *shape: torch.randn(*shape, generator=g, device=dev, dtype=torch.float32).to(dt)
     out = {}
-    # MLP up-projection with fused ReLU^2 (the largest block GEMM)
-    A, B = rnd(N, C), rnd(F, C) * 0.02
+    # MLP up-projection with fused ReLU^2 (the largest block GEMM), on a real
+    # normalised residual stream (middle layer) and that layer's W_fc
+    lm = w.n_layer // 2
+    A = torch.empty(N, C, dtype=dt, device=dev)
+    ops.rmsnorm_fwd(st.xs[lm], A, torch.empty(N, dtype=torch.float32, device=dev), w.eps)
+    B = st.layers[lm][2]
     U, Hh = torch.empty(N, F, dtype=dt, device=dev), torch.empty(N, F, dtype=dt, device=dev)
     t = ev_time(lambda: ops.gemm(N, F, C, A, True, C, B, True, C, ops.EPI_RELU2, U, F, C2=Hh), reps, torch)
     fl = 2.0 * N * F * C
@@ -127,6 +156,32 @@ def kernel_figures(w, st, reps, torch, ops):
     return out
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mlp_up_d24_hbm_traffic.txt")
+GEMM_SOURCES = [os.path.join(ROOT, "gpt_decoder_block_amd", "csrc", f) for f in ("gemm.hip", "common.h", "kernels.h")]
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the roofline kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, each calibrated on a copy of known
+    size), or None when the GEMM sources changed since it was taken."""
+    try:
+        kv = dict(l.split(":", 1) for l in open(TRAFFIC_FILE) if ":" in l and not l.startswith("#"))
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        if kv.get("source_sha256_16") != gemm_source_hash():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, budget_s=40.0):
     """The fp64 oracle on the host cores: one block forward+backward per layer
     kind at B=1, T=w.T, plus the head at N=T tokens; scaled to the whole stack."""
@@ -183,6 +238,9 @@ def main():
         w = w.with_(B=args.batch)
     if w.extras or w.mlp_fp8:
         w = w.with_(extras=False, mlp_fp8=False)
+    if args.counter_run:
+        counter_run(w)
+        return
     dev = "cuda:0"
     st = DecoderStack(n_layer=w.n_layer, B=w.B, T=w.T, C=w.C, n_head=w.n_head, n_kv_head=w.n_kv_head,
                       head_dim=w.head_dim, mlp_hidden=w.mlp_hidden, vocab=w.vocab, windows=w.windows,
@@ -203,6 +261,10 @@ def main():
         st.step()
     torch.cuda.synchronize()
     loss0 = float(st.loss.item())
+    print("[bench] kernel figures", file=sys.stderr, flush=True)
+    kern = kernel_figures(w, st, args.kernel_reps, torch, ops)
+    for _ in range(2):   # back to the step's steady state
+        st.step()
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -222,11 +284,10 @@ def main():
                                       w.T, w.windows)
     tps = tokens / (ms / 1e3)
     tflops = fpt * tps / 1e12
-    kern = kernel_figures(w, st, args.kernel_reps, torch, ops)
     dom = kern["gemm_mlp_up_relu2"]
     roof = {"kernel": "gemm_bf16_k<K-major, K-major, ReLU2 epilogue> (MLP up-projection)",
             "bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-            "frac": dom["tflops"] / (PEAK_BF16 / 1e12), "traffic": None,
+            "frac": dom["tflops"] / (PEAK_BF16 / 1e12), "traffic": measured_traffic(),
             "algorithmic_per_launch": f"2*M*N*K = {dom['flops']:.4g} FLOP (M={dom['shape'][0]} tokens, "
                                       f"N={dom['shape'][1]}, K={dom['shape'][2]})",
             "avg_launch_ms": dom["ms"]}

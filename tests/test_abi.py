@@ -1,0 +1,149 @@
+"""The C-ABI library on a CPU-only host: it loads, exports every function that
+include/gdb.h declares, and rejects bad arguments with a message before any
+device work (no compute call is made here)."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdb.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from gpt_decoder_block_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from gpt_decoder_block_amd import build
+        build.build()
+    return _lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdb_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("gdb_block_fwd", "gdb_block_bwd", "gdb_lm_head_ce_fwd_bwd", "gdb_embed_fwd", "gdb_embed_bwd"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    lib = L.lib()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the Python binding covers exactly the declared functions
+    assert sorted(L.SIGNATURES) == declared_functions()
+
+
+def test_abi_version(L):
+    assert L.lib().gdb_abi_version() == 1
+
+
+def _cfg(L, **kw):
+    base = dict(B=2, T=64, C=256, n_head=2, n_kv_head=1, head_dim=128, mlp_hidden=1024, window=-1, dtype=1,
+                mlp_fp8=0, accumulate_wgrad=0, eps=1e-6)
+    base.update(kw)
+    return L.BlockCfg(**base)
+
+
+def _sizes(L, cfg):
+    s, f, b = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    st = L.lib().gdb_block_sizes(ctypes.byref(cfg), ctypes.byref(s), ctypes.byref(f), ctypes.byref(b))
+    return st, s.value, f.value, b.value
+
+
+def test_block_sizes_valid_and_monotone(L):
+    st, s1, f1, b1 = _sizes(L, _cfg(L))
+    assert st == L.GDB_OK and s1 > 0 and f1 > 0 and b1 > 0
+    st, s2, f2, b2 = _sizes(L, _cfg(L, B=4))
+    assert st == L.GDB_OK and s2 > s1 and f2 > f1 and b2 > b1
+    # saved activations: xn1, q^k^v, o, xn2, u, h in bf16 plus fp32 statistics
+    N, C, W3, F = 128, 256, 4 * 128, 1024
+    assert s1 >= N * (C + W3 + C + C + 2 * F) * 2
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(n_kv_head=3), -1, "multiple of n_kv_head"),
+    (dict(head_dim=96, C=192), -2, "head_dim"),
+    (dict(head_dim=64, C=128), -2, "bf16 attention needs head_dim 128"),
+    (dict(C=384), -2, "must equal C"),
+    (dict(B=0), -1, "positive"),
+    (dict(window=-2), -1, "window"),
+    (dict(dtype=7), -1, "dtype"),
+    (dict(mlp_fp8=1), -2, "mlp_fp8"),
+    (dict(mlp_hidden=1020), -1, "multiples of 8"),
+    (dict(eps=0.0), -1, "eps"),
+])
+def test_block_cfg_validation(L, kw, code, msg):
+    st, *_ = _sizes(L, _cfg(L, **kw))
+    assert st == code
+    assert msg in L.lib().gdb_last_error().decode()
+
+
+def test_block_fwd_rejects_null_and_misaligned_pointers(L):
+    lib = L.lib()
+    cfg = _cfg(L)
+    buf = ctypes.create_string_buffer(4096)
+    base = ctypes.addressof(buf)
+    al = (base + 255) & ~255
+    w = L.BlockWeights(al, al, al, al)
+    st = lib.gdb_block_fwd(ctypes.byref(cfg), ctypes.byref(w), None, al, al + 512, al, al, None)
+    assert st == L.GDB_EINVAL and "rope_tab is NULL" in lib.gdb_last_error().decode()
+    st = lib.gdb_block_fwd(ctypes.byref(cfg), ctypes.byref(w), al, al + 2, al + 512, al, al, None)
+    assert st == L.GDB_EINVAL and "x_in is not 16-byte aligned" in lib.gdb_last_error().decode()
+    st = lib.gdb_block_fwd(ctypes.byref(cfg), ctypes.byref(w), al, al, al, al, al, None)
+    assert st == L.GDB_EINVAL and "alias" in lib.gdb_last_error().decode()
+    st = lib.gdb_block_fwd(ctypes.byref(cfg), None, al, al, al + 512, al, al, None)
+    assert st == L.GDB_EINVAL
+    dw = L.BlockWgrads(al, 0, al, al)
+    st = lib.gdb_block_bwd(ctypes.byref(cfg), ctypes.byref(w), al, al, al, al, ctypes.byref(dw), al, None)
+    assert st == L.GDB_EINVAL and "dw_o is NULL" in lib.gdb_last_error().decode()
+
+
+def test_gemm_and_attention_validation(L):
+    lib = L.lib()
+    al = 1 << 20   # never dereferenced: validation fails first
+    st = lib.gdb_gemm(1, 64, 60, 64, al, 1, 64, al, 1, 64, 0, al, 60, None, 0, None, 0, None, None)
+    assert st == L.GDB_EINVAL and "multiples of 8" in lib.gdb_last_error().decode()
+    st = lib.gdb_gemm(1, 64, 64, 64, al, 1, 32, al, 1, 64, 0, al, 64, None, 0, None, 0, None, None)
+    assert st == L.GDB_EINVAL and "leading dimension" in lib.gdb_last_error().decode()
+    st = lib.gdb_gemm(1, 64, 64, 64, al, 1, 64, al, 1, 64, 9, al, 64, None, 0, None, 0, None, None)
+    assert st == L.GDB_EINVAL and "epilogue" in lib.gdb_last_error().decode()
+    st = lib.gdb_gemm(1, 64, 64, 64, al, 1, 64, al, 1, 64, 1, al, 64, None, 64, None, 0, None, None)
+    assert st == L.GDB_EINVAL and "R is NULL" in lib.gdb_last_error().decode()
+    st = lib.gdb_attention_fwd(1, 64, 3, 2, 128, -1, 0, 1, al, 896, al, 384, al, None)
+    assert st == L.GDB_EINVAL and "multiple of Hkv" in lib.gdb_last_error().decode()
+    st = lib.gdb_attention_fwd(1, 64, 2, 1, 64, -1, 0, 1, al, 256, al, 128, al, None)
+    assert st == L.GDB_EUNSUPPORTED
+    st = lib.gdb_lm_head_ce_fwd_bwd(8, 128, 100, 1, 1e-6, al, al, al, al, al, al, 0, al, None)
+    assert st == L.GDB_EINVAL and "multiples of 8" in lib.gdb_last_error().decode()
+    st = lib.gdb_embed_fwd(8, 12, 100, 1, al, al, al, None)
+    assert st == L.GDB_EINVAL
+
+
+def test_rope_table_host(L):
+    T, D, base = 37, 64, 10000.0
+    out = np.zeros((T, D // 2, 2), dtype=np.float32)
+    st = L.lib().gdb_rope_table_host(T, D, base, out.ctypes.data_as(ctypes.c_void_p))
+    assert st == L.GDB_OK
+    t = np.arange(T)[:, None]
+    j = np.arange(D // 2)[None, :]
+    th = t * base ** (-2.0 * j / D)
+    np.testing.assert_array_equal(out[..., 0], np.cos(th).astype(np.float32))
+    np.testing.assert_array_equal(out[..., 1], np.sin(th).astype(np.float32))
+    assert L.lib().gdb_rope_table_host(T, 63, base, out.ctypes.data_as(ctypes.c_void_p)) == L.GDB_EINVAL
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from gpt_decoder_block_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        _lib.lib()
