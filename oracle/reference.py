@@ -55,7 +55,7 @@ import numpy as np
 __all__ = [
     "rms_norm", "rms_norm_backward", "rope_tables", "rope", "rope_backward",
     "visible_mask", "attention", "attention_logsumexp", "attention_backward", "cross_entropy", "e4m3_round",
-    "fp8_quant_dequant", "block_forward", "block_backward", "lm_head_ce",
+    "fp8_quantize", "fp8_quant_dequant", "block_forward", "block_backward", "lm_head_ce",
     "embed_forward", "embed_backward", "smear_forward", "smear_backward",
     "stack_forward_backward", "FP8_E4M3_MAX",
 ]
@@ -195,13 +195,26 @@ def e4m3_round(x: np.ndarray) -> np.ndarray:
     return np.where(x < 0, -q, q)
 
 
-def fp8_quant_dequant(x: np.ndarray) -> np.ndarray:
-    """Per-tensor dynamic scaling s = amax|x| / 448, then x ~ e4m3(x / s) * s."""
-    amax = float(np.max(np.abs(x))) if x.size else 0.0
+def fp8_quantize(x: np.ndarray) -> Tuple[np.ndarray, float]:
+    """Per-tensor dynamic scaling: s = amax|x| / 448 and codes e4m3(x / s).
+    The pages fix no precision for the scale and the division; both are taken
+    in float32 (amax rounded to float32, s = amax / 448 and x / s each one
+    correctly rounded float32 operation), so an input that is exactly
+    representable in float32 gets the same code whatever computes it.
+    Returns (the e4m3 values as float64, s as a float)."""
+    x = np.asarray(x, dtype=np.float64)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
     if amax == 0.0:
-        return np.zeros_like(x)
-    s = amax / FP8_E4M3_MAX
-    return e4m3_round(x / s) * s
+        return np.zeros_like(x), 0.0
+    s = np.float32(amax / np.float32(FP8_E4M3_MAX))
+    q = x.astype(np.float32) / s
+    return e4m3_round(q.astype(np.float64)), float(s)
+
+
+def fp8_quant_dequant(x: np.ndarray) -> np.ndarray:
+    """x ~ e4m3(x / s) * s with the per-tensor scale of `fp8_quantize`."""
+    q, s = fp8_quantize(x)
+    return q * s
 
 
 def _mm_nt(a, b, fp8):
@@ -312,6 +325,10 @@ def block_backward(dout: np.ndarray, c: dict, p: Dict[str, np.ndarray], cfg, l: 
     if cfg.extras:
         g["resid_lambda"] = np.sum(dx * c["x_premix"])
         g["x0_lambda"] = np.sum(dx * c["x0"])
+        # sum of the magnitudes of the summed terms: the scale of the forward
+        # error bound of each of these two sums
+        g["sum_abs"] = {"resid_lambda": np.sum(np.abs(dx * c["x_premix"])),
+                        "x0_lambda": np.sum(np.abs(dx * c["x0"]))}
         g["x0"] = p["x0_lambda"] * dx
         dx = p["resid_lambda"] * dx
     return dx, g
@@ -431,6 +448,7 @@ def stack_forward_backward(cfg, ids: np.ndarray, glob: Dict[str, np.ndarray],
     grads = {"w_lm": dw_lm, "layers": [None] * L}
     if cfg.extras:
         grads["backout_lambda"] = -float(np.sum(dx * x_bo))
+        sum_abs = {"backout_lambda": float(np.sum(np.abs(dx * x_bo)))}
         dx_bo = -glob["backout_lambda"] * dx
         dx0 = np.zeros_like(dx)
     for l in reversed(range(L)):
@@ -445,10 +463,13 @@ def stack_forward_backward(cfg, ids: np.ndarray, glob: Dict[str, np.ndarray],
         de, dws, dlam = smear_backward(dx, e, glob["smear_gate"], float(glob["smear_lambda"]), sc)
         grads["smear_gate"] = dws
         grads["smear_lambda"] = dlam
+        sum_abs["smear_lambda"] = float(np.sum(np.abs(np.sum(dx * sc["prev"], axis=-1) * sc["sg"])))
     else:
         de = dx
     grads["wte"] = embed_backward(de, inp, glob["wte"].shape[0])
     out = {"head": hc, "x_final": x_final}
+    if cfg.extras:
+        out["sum_abs"] = sum_abs
     if keep:
         out["acts"] = acts
         out["caches"] = caches

@@ -271,7 +271,25 @@ def test_fp8_quant_dequant_error_bound():
     s = np.max(np.abs(x)) / 448.0
     # relative half-ulp 2^-4 on normals, absolute half-ulp 2^-10 * s on subnormals
     assert np.all(np.abs(y - x) <= np.maximum(np.abs(x) * 2.0 ** -4, s * 2.0 ** -10) + 1e-15)
-    assert np.max(np.abs(y)) == pytest.approx(np.max(np.abs(x)), rel=1e-15)
+    # amax lands on the top code 448: back to amax up to the float32 scale
+    assert np.max(np.abs(y)) == pytest.approx(np.max(np.abs(x)), rel=2 ** -22)
+
+
+def test_fp8_quantize_codes_are_float32_decisions():
+    # an input exactly halfway between two e4m3 steps after a float32 division
+    # rounds to even; codes depend only on float32 arithmetic
+    x = np.array([448.0, -224.0, 1.0, 0.0, 3.5, 7.0, 15.0])
+    q, s = O.fp8_quantize(x)
+    assert s == float(np.float32(448.0) / np.float32(448.0)) == 1.0
+    np.testing.assert_array_equal(q, [448.0, -224.0, 1.0, 0.0, 3.5, 7.0, 15.0])
+    q, s = O.fp8_quantize(x * 3.0)          # s = 3: 3.5*3/3 = 3.5 exactly, etc.
+    assert s == 3.0
+    np.testing.assert_array_equal(q, [448.0, -224.0, 1.0, 0.0, 3.5, 7.0, 15.0])
+    q, s = O.fp8_quantize(np.zeros(5))
+    assert s == 0.0 and not np.any(q)
+    # 17 = 16 * 1.0625 is a tie between 16 and 18 (3 mantissa bits): even -> 16
+    q, _ = O.fp8_quantize(np.array([448.0, 17.0, 19.0]))
+    np.testing.assert_array_equal(q, [448.0, 16.0, 20.0])
 
 
 # ------------------------------------------------------ whole-step FD pins
