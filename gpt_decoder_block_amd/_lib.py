@@ -35,6 +35,19 @@ class BlockWgrads(ctypes.Structure):
     _fields_ = [("dw_qkv", c_void_p), ("dw_o", c_void_p), ("dw_fc", c_void_p), ("dw_proj", c_void_p)]
 
 
+class BlockExtras(ctypes.Structure):
+    _fields_ = [("lambdas", c_void_p), ("x0", c_void_p), ("x_in", c_void_p), ("ids", c_void_p),
+                ("ve", c_void_p), ("ve_gate", c_void_p), ("ve_vocab", c_int32), ("ve_gate_channels", c_int32)]
+
+
+class BlockExtrasGrads(ctypes.Structure):
+    _fields_ = [("dlambdas", c_void_p), ("dx0", c_void_p), ("dve", c_void_p), ("dve_gate", c_void_p),
+                ("accumulate_dx0", c_int32)]
+
+
+GDB_EXTRAS_WS_BYTES = 1 << 20
+
+
 class GdbError(RuntimeError):
     def __init__(self, fn: str, status: int, msg: str):
         super().__init__(f"{fn} failed with status {status}: {msg}")
@@ -54,13 +67,24 @@ SIGNATURES = {
     "gdb_embed_fwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "gdb_embed_bwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int32,
                                 c_void_p]),
-    "gdb_block_fwd": (c_int32, [ctypes.POINTER(BlockCfg), ctypes.POINTER(BlockWeights), c_void_p, c_void_p,
-                                c_void_p, c_void_p, c_void_p, c_void_p]),
-    "gdb_block_bwd": (c_int32, [ctypes.POINTER(BlockCfg), ctypes.POINTER(BlockWeights), c_void_p, c_void_p,
-                                c_void_p, c_void_p, ctypes.POINTER(BlockWgrads), c_void_p, c_void_p]),
+    "gdb_block_fwd": (c_int32, [ctypes.POINTER(BlockCfg), ctypes.POINTER(BlockWeights),
+                                ctypes.POINTER(BlockExtras), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                c_void_p]),
+    "gdb_block_bwd": (c_int32, [ctypes.POINTER(BlockCfg), ctypes.POINTER(BlockWeights),
+                                ctypes.POINTER(BlockExtras), c_void_p, c_void_p, c_void_p, c_void_p,
+                                ctypes.POINTER(BlockWgrads), ctypes.POINTER(BlockExtrasGrads), c_void_p,
+                                c_void_p]),
     "gdb_lm_head_ce_sizes": (c_int32, [c_int32, c_int32, c_int32, c_int32, ctypes.POINTER(c_size_t)]),
     "gdb_lm_head_ce_fwd_bwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
+    "gdb_smear_fwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_void_p, c_void_p]),
+    "gdb_smear_bwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                                c_void_p]),
+    "gdb_backout_fwd": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "gdb_backout_bwd": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_int32, c_void_p, c_void_p]),
     "gdb_rmsnorm_fwd": (c_int32, [c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p, c_void_p, c_void_p]),
     "gdb_rmsnorm_bwd": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p]),

@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 #include <string>
 
@@ -61,6 +62,9 @@ struct BlockDims {
   float eps;
 };
 
+// Largest value-embedding gate width (one lane per channel).
+constexpr int MAX_VE_GATE = 64;
+
 gdb_status check_cfg(const gdb_block_cfg* c, BlockDims* d) {
   if (!c) return fail(GDB_EINVAL, "cfg is NULL");
   if (c->B <= 0 || c->T <= 0 || c->C <= 0) return fail(GDB_EINVAL, "B, T, C must be positive (got %d, %d, %d)", c->B, c->T, c->C);
@@ -86,13 +90,17 @@ gdb_status check_cfg(const gdb_block_cfg* c, BlockDims* d) {
 struct Saved {
   void *xn1, *qkvh, *o, *xn2, *u, *h;
   float *r1, *rqk, *lse, *r2;
+  float* ve_s;          // value-embedding gate logits [N, Hkv]
 };
 struct WsFwd {
   void *qkv, *x_mid;
+  void* x_mix;          // residual-mixed block input [N, C]
 };
 struct WsBwd {
   void *du, *dxn, *dx_mid, *dout, *dqkv;
   float *delta, *partial;
+  float* ds;            // value-embedding gate logit gradients [N, Hkv]
+  float* xpart;         // partial sums of the extras' parameter gradients
 };
 
 void carve_saved(const BlockDims& d, Carver& c, Saved& s) {
@@ -107,10 +115,12 @@ void carve_saved(const BlockDims& d, Carver& c, Saved& s) {
   s.r2 = c.take<float>(N * 4);
   s.u = c.take<char>(N * d.F * d.s);
   s.h = c.take<char>(N * d.F * d.s);
+  s.ve_s = c.take<float>(N * d.Hkv * 4);
 }
 void carve_fwd(const BlockDims& d, Carver& c, WsFwd& w) {
   w.qkv = c.take<char>((size_t)d.N * d.W3 * d.s);
   w.x_mid = c.take<char>((size_t)d.N * d.C * d.s);
+  w.x_mix = c.take<char>((size_t)d.N * d.C * d.s);
 }
 size_t wgrad_partial_floats(const BlockDims& d) {
   size_t m = 0;
@@ -130,6 +140,36 @@ void carve_bwd(const BlockDims& d, Carver& c, WsBwd& w) {
   w.dqkv = c.take<char>(N * d.W3 * d.s);
   w.delta = c.take<float>(N * d.H * 4);
   w.partial = c.take<float>(wgrad_partial_floats(d) * 4);
+  w.ds = c.take<float>(N * d.Hkv * 4);
+  const size_t xp = std::max((size_t)mix_partials(d.N) * 2, (size_t)ve_gate_partials(d.N) * d.Hkv * MAX_VE_GATE);
+  w.xpart = c.take<float>(xp * 4);
+}
+
+// Which extras a call uses; validates their pointers and sizes.
+struct Extras {
+  bool mix = false, ve = false;
+};
+gdb_status check_extras(const BlockDims& d, const gdb_block_extras* ex, bool bwd, Extras* e) {
+  *e = Extras{};
+  if (!ex) return GDB_OK;
+  if (ex->lambdas) {
+    e->mix = true;
+    if (((uintptr_t)ex->lambdas) & 3) return fail(GDB_EINVAL, "ex->lambdas is not 4-byte aligned");
+    CHECK_PTR(ex->x0);
+    if (bwd) CHECK_PTR(ex->x_in);
+  }
+  if (ex->ve) {
+    e->ve = true;
+    CHECK_PTR(ex->ve);
+    CHECK_PTR(ex->ve_gate);
+    if (!ex->ids || (((uintptr_t)ex->ids) & 3)) return fail(GDB_EINVAL, "ex->ids is NULL or not 4-byte aligned");
+    if (ex->ve_vocab <= 0) return fail(GDB_EINVAL, "ex->ve_vocab must be positive (got %d)", ex->ve_vocab);
+    if (ex->ve_gate_channels < 1 || ex->ve_gate_channels > MAX_VE_GATE || ex->ve_gate_channels > d.C)
+      return fail(GDB_EINVAL, "ex->ve_gate_channels must be in [1, min(%d, C)] (got %d)", MAX_VE_GATE,
+                  ex->ve_gate_channels);
+    if (d.Hkv > 64) return fail(GDB_EUNSUPPORTED, "value embeddings need n_kv_head <= 64 (got %d)", d.Hkv);
+  }
+  return GDB_OK;
 }
 
 GemmArgs gemm_args(const void* A, bool ak, int lda, const void* B, bool bk, int ldb, int M, int N, int K,
@@ -217,8 +257,8 @@ gdb_status gdb_embed_bwd(int32_t N, int32_t C, int32_t V, int32_t dtype, const i
   return GDB_OK;
 }
 
-gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, const float* rope_tab,
-                         const void* x_in, void* x_out, void* saved, void* ws, void* stream) {
+gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, const gdb_block_extras* ex,
+                         const float* rope_tab, const void* x_in, void* x_out, void* saved, void* ws, void* stream) {
   BlockDims d;
   gdb_status st = check_cfg(cfg, &d);
   if (st != GDB_OK) return st;
@@ -226,6 +266,8 @@ gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
   CHECK_PTR(w->w_qkv); CHECK_PTR(w->w_o); CHECK_PTR(w->w_fc); CHECK_PTR(w->w_proj);
   CHECK_PTR(rope_tab); CHECK_PTR(x_in); CHECK_PTR(x_out); CHECK_PTR(saved); CHECK_PTR(ws);
   if (x_in == x_out) return fail(GDB_EINVAL, "x_out must not alias x_in");
+  Extras xe;
+  if ((st = check_extras(d, ex, false, &xe)) != GDB_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   Saved sv;
   WsFwd wf;
@@ -234,8 +276,16 @@ gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
   carve_fwd(d, c2, wf);
   const int dt = d.dt, N = d.N;
 
-  HIPCHK(rmsnorm_fwd(dt, x_in, sv.xn1, sv.r1, N, d.C, d.eps, s));
+  const void* x = x_in;
+  if (xe.mix) {
+    HIPCHK(mix_fwd(dt, x_in, ex->x0, ex->lambdas, wf.x_mix, (size_t)N * d.C, s));
+    x = wf.x_mix;
+  }
+  HIPCHK(rmsnorm_fwd(dt, x, sv.xn1, sv.r1, N, d.C, d.eps, s));
   HIPCHK(gemm(dt, gemm_args(sv.xn1, true, d.C, w->w_qkv, true, d.C, N, d.W3, d.C, EPI_STORE, wf.qkv, d.W3), s));
+  if (xe.ve)
+    HIPCHK(ve_fwd(dt, wf.qkv, d.W3, d.Q + d.KV, sv.xn1, d.C, ex->ids, ex->ve, ex->ve_gate, ex->ve_gate_channels,
+                  d.Hkv, d.D, ex->ve_vocab, sv.ve_s, N, s));
   HIPCHK(qk_norm_rope_fwd(dt, wf.qkv, sv.qkvh, sv.rqk, rope_tab, d.B, d.T, d.H, d.Hkv, d.D, d.eps, s));
   AttnArgs at{};
   at.B = d.B; at.T = d.T; at.H = d.H; at.Hkv = d.Hkv; at.D = d.D; at.window = d.window;
@@ -243,7 +293,7 @@ gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
   at.qkv = sv.qkvh; at.ld = d.W3; at.o = sv.o; at.ldo = d.Q; at.lse = sv.lse;
   HIPCHK(attn_fwd(dt, at, s));
   GemmArgs g = gemm_args(sv.o, true, d.Q, w->w_o, true, d.Q, N, d.C, d.Q, EPI_RESID, wf.x_mid, d.C);
-  g.R = x_in; g.ldr = d.C;
+  g.R = x; g.ldr = d.C;
   HIPCHK(gemm(dt, g, s));
   HIPCHK(rmsnorm_fwd(dt, wf.x_mid, sv.xn2, sv.r2, N, d.C, d.eps, s));
   g = gemm_args(sv.xn2, true, d.C, w->w_fc, true, d.C, N, d.F, d.C, EPI_RELU2, sv.u, d.F);
@@ -256,9 +306,9 @@ gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
   return GDB_OK;
 }
 
-gdb_status gdb_block_bwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, const float* rope_tab,
-                         const void* saved, const void* dx_out, void* dx_in, const gdb_block_wgrads* dw, void* ws,
-                         void* stream) {
+gdb_status gdb_block_bwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, const gdb_block_extras* ex,
+                         const float* rope_tab, const void* saved, const void* dx_out, void* dx_in,
+                         const gdb_block_wgrads* dw, const gdb_block_extras_grads* dex, void* ws, void* stream) {
   BlockDims d;
   gdb_status st = check_cfg(cfg, &d);
   if (st != GDB_OK) return st;
@@ -266,6 +316,16 @@ gdb_status gdb_block_bwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
   CHECK_PTR(w->w_qkv); CHECK_PTR(w->w_o); CHECK_PTR(w->w_fc); CHECK_PTR(w->w_proj);
   CHECK_PTR(dw->dw_qkv); CHECK_PTR(dw->dw_o); CHECK_PTR(dw->dw_fc); CHECK_PTR(dw->dw_proj);
   CHECK_PTR(rope_tab); CHECK_PTR(saved); CHECK_PTR(dx_out); CHECK_PTR(dx_in); CHECK_PTR(ws);
+  Extras xe;
+  if ((st = check_extras(d, ex, true, &xe)) != GDB_OK) return st;
+  if (xe.mix || xe.ve) {
+    if (!dex) return fail(GDB_EINVAL, "extras given without extras gradients");
+    if (xe.mix) {
+      if (!dex->dlambdas || (((uintptr_t)dex->dlambdas) & 3)) return fail(GDB_EINVAL, "dex->dlambdas is NULL or misaligned");
+      CHECK_PTR(dex->dx0);
+    }
+    if (xe.ve) { CHECK_PTR(dex->dve); CHECK_PTR(dex->dve_gate); }
+  }
   hipStream_t s = (hipStream_t)stream;
   Saved sv;
   WsBwd wb;
@@ -292,10 +352,25 @@ gdb_status gdb_block_bwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
   at.dout = wb.dout; at.lddo = d.Q; at.dqkv = wb.dqkv; at.lddq = d.W3; at.delta = wb.delta;
   HIPCHK(attn_bwd(dt, at, s));
   HIPCHK(qk_norm_rope_bwd(dt, wb.dqkv, sv.qkvh, sv.rqk, rope_tab, d.B, d.T, d.H, d.Hkv, d.D, s));
+  // value embeddings: gate-logit gradients and the table's rows (dv passes through unchanged)
+  if (xe.ve) {
+    if (!acc) HIPCHK(fill_f32(dex->dve, (size_t)ex->ve_vocab * d.KV, 0.f, s));
+    HIPCHK(ve_bwd(dt, wb.dqkv, d.W3, d.Q + d.KV, ex->ids, ex->ve, sv.ve_s, d.Hkv, d.D, ex->ve_vocab, wb.ds, dex->dve,
+                  N, s));
+  }
   // QKV projection
   HIPCHK(gemm(dt, gemm_args(wb.dqkv, true, d.W3, w->w_qkv, false, d.C, N, d.C, d.W3, EPI_STORE, wb.dxn, d.C), s));
   HIPCHK(wgrad(dt, wb.dqkv, d.W3, sv.xn1, d.C, d.W3, d.C, N, dw->dw_qkv, acc, wb.partial, s));
-  HIPCHK(rmsnorm_bwd(dt, wb.dxn, sv.xn1, sv.r1, wb.dx_mid, dx_in, N, d.C, s));
+  if (xe.ve)
+    HIPCHK(ve_gate_bwd(dt, wb.ds, sv.xn1, wb.dxn, d.C, ex->ve_gate, ex->ve_gate_channels, d.Hkv, wb.xpart,
+                       dex->dve_gate, acc, N, s));
+  if (xe.mix) {
+    HIPCHK(rmsnorm_bwd(dt, wb.dxn, sv.xn1, sv.r1, wb.dx_mid, wb.dx_mid, N, d.C, s));
+    HIPCHK(mix_bwd(dt, wb.dx_mid, ex->x_in, ex->x0, ex->lambdas, dx_in, dex->dx0, dex->accumulate_dx0 ? 1 : 0,
+                   wb.xpart, dex->dlambdas, acc, N, d.C, s));
+  } else {
+    HIPCHK(rmsnorm_bwd(dt, wb.dxn, sv.xn1, sv.r1, wb.dx_mid, dx_in, N, d.C, s));
+  }
   g_err.clear();
   return GDB_OK;
 }
@@ -497,6 +572,85 @@ gdb_status gdb_cross_entropy(int32_t N, int32_t V, int32_t dtype, void* z, const
   CHECK_PTR(z); CHECK_PTR(targets); CHECK_PTR(row_loss); CHECK_PTR(loss);
   HIPCHK(ce_fwd_bwd(dtype, z, targets, row_loss, N, V, (hipStream_t)stream));
   HIPCHK(loss_reduce(row_loss, loss, N, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
+// ---------------------------------------------------------- smear, backout
+namespace {
+gdb_status check_rows(int32_t N, int32_t C, int32_t dtype) {
+  if (N < 0 || C <= 0 || C % 8) return fail(GDB_EINVAL, "bad sizes N=%d C=%d (C a positive multiple of 8)", N, C);
+  if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
+  return GDB_OK;
+}
+gdb_status check_scalar(const float* p, const char* name) {
+  if (!p || (((uintptr_t)p) & 3)) return fail(GDB_EINVAL, "%s is NULL or not 4-byte aligned", name);
+  return GDB_OK;
+}
+constexpr int MAX_SMEAR = 63;
+}  // namespace
+
+gdb_status gdb_smear_fwd(int32_t B, int32_t T, int32_t C, int32_t ng, int32_t dtype, const void* e, const void* w,
+                         const float* lam, void* x, float* s_save, void* stream) {
+  gdb_status st;
+  if (B < 0 || T <= 0) return fail(GDB_EINVAL, "B must be >= 0 and T positive (got %d, %d)", B, T);
+  if ((long long)B * T > (1LL << 30)) return fail(GDB_EINVAL, "B*T too large");
+  if ((st = check_rows(B * T, C, dtype)) != GDB_OK) return st;
+  if (ng < 1 || ng > MAX_SMEAR || ng > C) return fail(GDB_EINVAL, "ng must be in [1, min(%d, C)] (got %d)", MAX_SMEAR, ng);
+  if (B == 0) { g_err.clear(); return GDB_OK; }
+  CHECK_PTR(e); CHECK_PTR(w); CHECK_PTR(x); CHECK_PTR(s_save);
+  if ((st = check_scalar(lam, "lam")) != GDB_OK) return st;
+  if (x == e) return fail(GDB_EINVAL, "x must not alias e");
+  HIPCHK(smear_fwd(dtype, e, w, ng, lam, x, s_save, B * T, T, C, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_smear_bwd(int32_t B, int32_t T, int32_t C, int32_t ng, int32_t dtype, const void* e, const void* w,
+                         const float* lam, const float* s_save, const void* dx, const float* dxa, void* de,
+                         float* dlam, float* dw, int32_t accumulate, void* ws, void* stream) {
+  gdb_status st;
+  if (B <= 0 || T <= 0) return fail(GDB_EINVAL, "B and T must be positive (got %d, %d)", B, T);
+  if ((long long)B * T > (1LL << 30)) return fail(GDB_EINVAL, "B*T too large");
+  if ((st = check_rows(B * T, C, dtype)) != GDB_OK) return st;
+  if (ng < 1 || ng > MAX_SMEAR || ng > C) return fail(GDB_EINVAL, "ng must be in [1, min(%d, C)] (got %d)", MAX_SMEAR, ng);
+  CHECK_PTR(e); CHECK_PTR(w); CHECK_PTR(s_save); CHECK_PTR(dx); CHECK_PTR(de); CHECK_PTR(ws);
+  if (dxa) CHECK_PTR(dxa);
+  if ((st = check_scalar(lam, "lam")) != GDB_OK) return st;
+  if ((st = check_scalar(dlam, "dlam")) != GDB_OK) return st;
+  if ((st = check_scalar(dw, "dw")) != GDB_OK) return st;
+  if (de == dx || de == (const void*)dxa) return fail(GDB_EINVAL, "de must not alias dx or dxa");
+  const int nb = smear_partials(B * T);
+  if ((size_t)nb * (ng + 1) * 4 > GDB_EXTRAS_WS_BYTES) return fail(GDB_EWORKSPACE, "extras workspace too small");
+  HIPCHK(smear_bwd(dtype, e, w, ng, lam, s_save, dx, dxa, de, (float*)ws, dlam, dw, accumulate ? 1 : 0, B * T, T, C,
+                   (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_backout_fwd(int32_t N, int32_t C, int32_t dtype, const void* x, const void* x_bo, const float* lam,
+                           void* y, void* stream) {
+  gdb_status st;
+  if ((st = check_rows(N, C, dtype)) != GDB_OK) return st;
+  if (N == 0) { g_err.clear(); return GDB_OK; }
+  CHECK_PTR(x); CHECK_PTR(x_bo); CHECK_PTR(y);
+  if ((st = check_scalar(lam, "lam")) != GDB_OK) return st;
+  if (y == x_bo && x != x_bo) return fail(GDB_EINVAL, "y must not alias x_bo");
+  HIPCHK(backout_fwd(dtype, x, x_bo, lam, y, (size_t)N * C, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_backout_bwd(int32_t N, int32_t C, int32_t dtype, const void* dy, const void* x_bo, const float* lam,
+                           void* dx_bo, float* dlam, int32_t accumulate, void* ws, void* stream) {
+  gdb_status st;
+  if ((st = check_rows(N, C, dtype)) != GDB_OK) return st;
+  if (N == 0) return fail(GDB_EINVAL, "N must be positive");
+  CHECK_PTR(dy); CHECK_PTR(x_bo); CHECK_PTR(dx_bo); CHECK_PTR(ws);
+  if ((st = check_scalar(lam, "lam")) != GDB_OK) return st;
+  if ((st = check_scalar(dlam, "dlam")) != GDB_OK) return st;
+  if (dx_bo == dy || dx_bo == x_bo) return fail(GDB_EINVAL, "dx_bo must not alias dy or x_bo");
+  HIPCHK(backout_bwd(dtype, dy, x_bo, lam, dx_bo, (float*)ws, dlam, accumulate ? 1 : 0, N, C, (hipStream_t)stream));
   g_err.clear();
   return GDB_OK;
 }

@@ -80,4 +80,40 @@ struct AttnArgs {
 hipError_t attn_fwd(int dt, const AttnArgs& a, hipStream_t s);
 hipError_t attn_bwd(int dt, const AttnArgs& a, hipStream_t s);
 
+// --------------------------------------------------------------------- extras
+// Kernels that reduce scalar gradients write one fp32 partial row per
+// workgroup; *_partials(N) gives the number of rows (at most EXTRA_PBLK for the
+// grid-stride ones), then one workgroup adds them in a fixed order.
+constexpr int EXTRA_PBLK = 1024;
+int mix_partials(int N);        // rows of 2 floats
+int ve_gate_partials(int N);    // rows of Hkv*nc floats
+int smear_partials(int N);      // rows of ng+1 floats
+int backout_partials(int N);    // rows of 1 float
+// y = lam[0]*x + lam[1]*x0 (n elements)
+hipError_t mix_fwd(int dt, const void* x, const void* x0, const float* lam, void* y, size_t n, hipStream_t s);
+// dx = lam[0]*dy (may alias dy); dx0 (+)= lam[1]*dy (fp32); dlam (+)= (sum dy*x, sum dy*x0)
+hipError_t mix_bwd(int dt, const void* dy, const void* x, const void* x0, const float* lam, void* dx, float* dx0,
+                   int acc_dx0, float* part, float* dlam, int accumulate, int N, int C, hipStream_t s);
+// v columns (offset voff) of qkv [N, ldq] += 3*sigmoid(xn[:, :nc] Wg^T) * VE[ids]; s_save [N, Hkv]
+hipError_t ve_fwd(int dt, void* qkv, int ldq, int voff, const void* xn, int C, const int32_t* ids, const void* ve,
+                  const void* wg, int nc, int Hkv, int D, int V, float* s_save, int N, hipStream_t s);
+// ds [N, Hkv] (gradient of the gate logits) and dve (fp32 atomics) from the v columns of dqkv
+hipError_t ve_bwd(int dt, const void* dqkv, int ldq, int voff, const int32_t* ids, const void* ve,
+                  const float* s_save, int Hkv, int D, int V, float* ds, float* dve, int N, hipStream_t s);
+// dxn[:, :nc] += ds Wg; dwg (+)= ds^T xn[:, :nc]
+hipError_t ve_gate_bwd(int dt, const float* ds, const void* xn, void* dxn, int C, const void* wg, int nc, int Hkv,
+                       float* part, float* dwg, int accumulate, int N, hipStream_t s);
+// x[t] = e[t] + lam*sigmoid(e[t, :ng] . w)*e[t-1] (t >= 1 within each row of T tokens); s_save [N]
+hipError_t smear_fwd(int dt, const void* e, const void* w, int ng, const float* lam, void* x, float* s_save, int N,
+                     int T, int C, hipStream_t s);
+// de from dx (+ optional fp32 dxa); dlam, dw (+)=
+hipError_t smear_bwd(int dt, const void* e, const void* w, int ng, const float* lam, const float* s_save,
+                     const void* dx, const float* dxa, void* de, float* part, float* dlam, float* dw, int accumulate,
+                     int N, int T, int C, hipStream_t s);
+// y = x - lam*xb
+hipError_t backout_fwd(int dt, const void* x, const void* xb, const float* lam, void* y, size_t n, hipStream_t s);
+// dxb += -lam*dy (in place); dlam (+)= -sum(dy*xb)
+hipError_t backout_bwd(int dt, const void* dy, const void* xb, const float* lam, void* dxb, float* part, float* dlam,
+                       int accumulate, int N, int C, hipStream_t s);
+
 }  // namespace gdb

@@ -69,21 +69,81 @@ def _weights(w: Sequence[torch.Tensor]) -> L.BlockWeights:
     return L.BlockWeights(*[t.data_ptr() for t in w])
 
 
+def block_extras(lambdas: torch.Tensor = None, x0: torch.Tensor = None, x_in: torch.Tensor = None,
+                 ids: torch.Tensor = None, ve: torch.Tensor = None, ve_gate: torch.Tensor = None) -> L.BlockExtras:
+    """Extras of one block (residual mixing when `lambdas` is given, value
+    embedding when `ve` is given).  The tensors must outlive the calls."""
+    ex = L.BlockExtras()
+    if lambdas is not None:
+        if lambdas.dtype != torch.float32 or lambdas.numel() != 2:
+            raise ValueError("lambdas must be a float32 tensor of 2 elements")
+        ex.lambdas, ex.x0 = _p(lambdas).value, _p(x0).value
+        if x_in is not None:
+            ex.x_in = _p(x_in).value
+    if ve is not None:
+        if ids.dtype != torch.int32:
+            raise ValueError("ids must be int32")
+        ex.ids, ex.ve, ex.ve_gate = _p(ids).value, _p(ve).value, _p(ve_gate).value
+        ex.ve_vocab, ex.ve_gate_channels = ve.shape[0], ve_gate.shape[1]
+    return ex
+
+
+def block_extras_grads(dlambdas: torch.Tensor = None, dx0: torch.Tensor = None, dve: torch.Tensor = None,
+                       dve_gate: torch.Tensor = None, accumulate_dx0: bool = False) -> L.BlockExtrasGrads:
+    g = L.BlockExtrasGrads()
+    for name, t in (("dlambdas", dlambdas), ("dx0", dx0), ("dve", dve), ("dve_gate", dve_gate)):
+        if t is not None:
+            if t.dtype != torch.float32:
+                raise ValueError(f"{name} must be float32")
+            setattr(g, name, _p(t).value)
+    g.accumulate_dx0 = int(accumulate_dx0)
+    return g
+
+
 def block_fwd(cfg: L.BlockCfg, w: Sequence[torch.Tensor], rope: torch.Tensor, x_in: torch.Tensor,
-              x_out: torch.Tensor, saved: torch.Tensor, ws: torch.Tensor) -> None:
+              x_out: torch.Tensor, saved: torch.Tensor, ws: torch.Tensor, ex: L.BlockExtras = None) -> None:
     for t in w:
         _p(t)
-    L.call("gdb_block_fwd", ctypes.byref(cfg), ctypes.byref(_weights(w)), _p(rope), _p(x_in), _p(x_out),
-           _p(saved), _p(ws), _stream(x_in))
+    L.call("gdb_block_fwd", ctypes.byref(cfg), ctypes.byref(_weights(w)), None if ex is None else ctypes.byref(ex),
+           _p(rope), _p(x_in), _p(x_out), _p(saved), _p(ws), _stream(x_in))
 
 
 def block_bwd(cfg: L.BlockCfg, w: Sequence[torch.Tensor], rope: torch.Tensor, saved: torch.Tensor,
-              dx_out: torch.Tensor, dx_in: torch.Tensor, dw: Sequence[torch.Tensor], ws: torch.Tensor) -> None:
+              dx_out: torch.Tensor, dx_in: torch.Tensor, dw: Sequence[torch.Tensor], ws: torch.Tensor,
+              ex: L.BlockExtras = None, dex: L.BlockExtrasGrads = None) -> None:
     for t in list(w) + list(dw):
         _p(t)
     wg = L.BlockWgrads(*[t.data_ptr() for t in dw])
-    L.call("gdb_block_bwd", ctypes.byref(cfg), ctypes.byref(_weights(w)), _p(rope), _p(saved), _p(dx_out),
-           _p(dx_in), ctypes.byref(wg), _p(ws), _stream(dx_out))
+    L.call("gdb_block_bwd", ctypes.byref(cfg), ctypes.byref(_weights(w)), None if ex is None else ctypes.byref(ex),
+           _p(rope), _p(saved), _p(dx_out), _p(dx_in), ctypes.byref(wg), None if dex is None else ctypes.byref(dex),
+           _p(ws), _stream(dx_out))
+
+
+def smear_fwd(B: int, T: int, e: torch.Tensor, w: torch.Tensor, lam: torch.Tensor, x: torch.Tensor,
+              s_save: torch.Tensor) -> None:
+    C = e.shape[-1]
+    L.call("gdb_smear_fwd", B, T, C, w.numel(), dtype_code(e.dtype), _p(e), _p(w), _p(lam), _p(x), _p(s_save),
+           _stream(e))
+
+
+def smear_bwd(B: int, T: int, e: torch.Tensor, w: torch.Tensor, lam: torch.Tensor, s_save: torch.Tensor,
+              dx: torch.Tensor, dxa, de: torch.Tensor, dlam: torch.Tensor, dw: torch.Tensor, ws: torch.Tensor,
+              accumulate: bool = False) -> None:
+    C = e.shape[-1]
+    L.call("gdb_smear_bwd", B, T, C, w.numel(), dtype_code(e.dtype), _p(e), _p(w), _p(lam), _p(s_save), _p(dx),
+           None if dxa is None else _p(dxa), _p(de), _p(dlam), _p(dw), int(accumulate), _p(ws), _stream(e))
+
+
+def backout_fwd(x: torch.Tensor, x_bo: torch.Tensor, lam: torch.Tensor, y: torch.Tensor) -> None:
+    C = x.shape[-1]
+    L.call("gdb_backout_fwd", x.numel() // C, C, dtype_code(x.dtype), _p(x), _p(x_bo), _p(lam), _p(y), _stream(x))
+
+
+def backout_bwd(dy: torch.Tensor, x_bo: torch.Tensor, lam: torch.Tensor, dx_bo: torch.Tensor, dlam: torch.Tensor,
+                ws: torch.Tensor, accumulate: bool = False) -> None:
+    C = dy.shape[-1]
+    L.call("gdb_backout_bwd", dy.numel() // C, C, dtype_code(dy.dtype), _p(dy), _p(x_bo), _p(lam), _p(dx_bo),
+           _p(dlam), int(accumulate), _p(ws), _stream(dy))
 
 
 def lm_head_ce_sizes(N: int, C: int, V: int, dtype: torch.dtype) -> int:

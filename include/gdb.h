@@ -11,6 +11,14 @@
  *   gdb_embed_fwd -> L x gdb_block_fwd -> gdb_lm_head_ce_fwd_bwd
  *                 -> L x gdb_block_bwd (reverse order) -> gdb_embed_bwd
  *
+ * The largest model adds (same section: the value-embedding snippet and the
+ * snippets on per-layer residual scaling, smear and backout):
+ *
+ *   gdb_embed_fwd -> gdb_smear_fwd -> L x gdb_block_fwd(extras) -> gdb_backout_fwd
+ *     -> gdb_lm_head_ce_fwd_bwd -> gdb_backout_bwd (when the backward reaches
+ *     the block whose output was subtracted) ... L x gdb_block_bwd(extras)
+ *     -> gdb_smear_bwd -> gdb_embed_bwd
+ *
  * Conventions shared by every entry point
  *   - Pointers named in a signature are DEVICE pointers unless the comment
  *     says "host".  The caller allocates every buffer (inputs, outputs, saved
@@ -43,7 +51,10 @@
 extern "C" {
 #endif
 
-#define GDB_ABI_VERSION 1
+#define GDB_ABI_VERSION 2
+
+/* Scratch bytes that gdb_smear_bwd and gdb_backout_bwd need in `ws`. */
+#define GDB_EXTRAS_WS_BYTES ((size_t)1 << 20)
 
 typedef enum {
   GDB_OK = 0,
@@ -87,6 +98,42 @@ typedef struct {
   float *dw_qkv, *dw_o, *dw_fc, *dw_proj;
 } gdb_block_wgrads;
 
+/* Per-block extras of the largest model (section "1. Le modèle GPT": the
+ * value-embedding snippet and the per-layer residual scaling snippet).
+ * Pass NULL to gdb_block_fwd / gdb_block_bwd for a plain block.
+ *
+ * Residual mixing, active when lambdas != NULL: the block first forms
+ *   x = lambdas[0]*x_in + lambdas[1]*x0
+ * and runs on x (both residual additions go onto x).
+ * Value embedding, active when ve != NULL: right after the QKV projection,
+ *   v[n, g, :] += 3*sigmoid(xn1[n, :nc] . ve_gate[g, :]) * ve[ids[n], g*D : (g+1)*D]
+ * for every K/V head g (nc = ve_gate_channels, xn1 = the normalised x), before
+ * the QK norm and attention. */
+typedef struct {
+  const float* lambdas;      /* fp32 [2] device: (residual scale, x0 scale); NULL: no mixing        */
+  const void* x0;            /* [N, C] dtype: the stream after embedding and smear                   */
+  const void* x_in;          /* gdb_block_bwd only: the x_in given to gdb_block_fwd (before mixing)  */
+  const int32_t* ids;        /* int32 [N] input token ids (clamped into [0, ve_vocab))               */
+  const void* ve;            /* [ve_vocab, n_kv_head*head_dim] dtype; NULL: no value embedding       */
+  const void* ve_gate;       /* [n_kv_head, ve_gate_channels] dtype                                  */
+  int32_t ve_vocab;
+  int32_t ve_gate_channels;  /* 1 .. min(64, C); 32 in the pages' model                              */
+} gdb_block_extras;
+
+/* fp32 gradients of the extras.  dlambdas [2], dve and dve_gate are
+ * overwritten, or added to when cfg->accumulate_wgrad != 0 (dve is zeroed
+ * first otherwise; its rows are summed with atomics, in no fixed order).
+ * dx0 [N, C] receives lambdas[1]*dx (the x0 share of the mixed stream's
+ * gradient): overwritten, or added to when accumulate_dx0 != 0, so the
+ * blocks of one backward pass can sum their shares in place. */
+typedef struct {
+  float* dlambdas;           /* [2] */
+  float* dx0;                /* [N, C] */
+  float* dve;                /* [ve_vocab, n_kv_head*head_dim] */
+  float* dve_gate;           /* [n_kv_head, ve_gate_channels] */
+  int32_t accumulate_dx0;
+} gdb_block_extras_grads;
+
 /* ABI version (GDB_ABI_VERSION of the built library). */
 int32_t gdb_abi_version(void);
 
@@ -126,19 +173,24 @@ gdb_status gdb_embed_bwd(int32_t N, int32_t C, int32_t V, int32_t dtype,
  *   o = softmax(q^ k^T / sqrt(head_dim), causal/window mask) v  (GQA head sharing);
  *   x_mid = x_in + o W_o^T;  xn2 = rms(x_mid);  h = relu(xn2 W_fc^T)^2;
  *   x_out = x_mid + h W_proj^T.
+ * ex: NULL, or the extras above (x_in is then the stream before mixing).
  * rope_tab: device copy of gdb_rope_table_host(T, head_dim, base).
  * saved: gdb_block_sizes' saved_bytes, kept intact until gdb_block_bwd.
  * ws: ws_fwd_bytes of scratch.  x_out must not alias x_in. */
 gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w,
-                         const float* rope_tab, const void* x_in, void* x_out,
-                         void* saved, void* ws, void* stream);
+                         const gdb_block_extras* ex, const float* rope_tab,
+                         const void* x_in, void* x_out, void* saved, void* ws, void* stream);
 
 /* Backward of gdb_block_fwd: given dx_out [N, C] (gradient w.r.t. x_out) and
  * the `saved` buffer of the matching forward, writes dx_in [N, C] (may alias
- * dx_out) and the fp32 weight gradients.  ws: ws_bwd_bytes of scratch. */
+ * dx_out) and the fp32 weight gradients.  ex: the forward's extras (with x_in
+ * set when mixing) or NULL; dex: their gradients (required when ex uses any
+ * extra).  ws: ws_bwd_bytes of scratch. */
 gdb_status gdb_block_bwd(const gdb_block_cfg* cfg, const gdb_block_weights* w,
-                         const float* rope_tab, const void* saved, const void* dx_out,
-                         void* dx_in, const gdb_block_wgrads* dw, void* ws, void* stream);
+                         const gdb_block_extras* ex, const float* rope_tab,
+                         const void* saved, const void* dx_out, void* dx_in,
+                         const gdb_block_wgrads* dw, const gdb_block_extras_grads* dex,
+                         void* ws, void* stream);
 
 /* Workspace of gdb_lm_head_ce_fwd_bwd (holds the normalised stream, its
  * inverse RMS, the [N, V] logits/gradients, per-row losses). */
@@ -157,6 +209,38 @@ gdb_status gdb_lm_head_ce_fwd_bwd(int32_t N, int32_t C, int32_t V, int32_t dtype
                                   float* loss, void* dx, float* dw_lm, int32_t accumulate,
                                   void* ws, void* stream);
 
+/* Smear, once after the embedding (section "1. Le modèle GPT", the smear
+ * snippet): with s[n] = e[n, :ng] . w,
+ *   x[b, t] = e[b, t] + lam[0]*sigmoid(s[b, t])*e[b, t-1]  for t >= 1,  x[b, 0] = e[b, 0].
+ * The gate reads the current token; the mixed-in vector is the previous
+ * token's embedding.  e, x [B*T, C] and w [ng] in dtype, 1 <= ng <= min(63, C);
+ * lam: fp32 [1] device; s_save fp32 [B*T] is written for the backward.
+ * x must not alias e. */
+gdb_status gdb_smear_fwd(int32_t B, int32_t T, int32_t C, int32_t ng, int32_t dtype,
+                         const void* e, const void* w, const float* lam, void* x,
+                         float* s_save, void* stream);
+/* Backward of gdb_smear_fwd.  The gradient w.r.t. x is dx [B*T, C] (dtype)
+ * plus, if dxa != NULL, the fp32 addend dxa [B*T, C] (the summed dx0 shares
+ * of the blocks).  Writes de [B*T, C] (dtype; must not alias dx or dxa) and
+ * the fp32 gradients dlam [1] and dw [ng], overwritten or added to
+ * (`accumulate`).  ws: GDB_EXTRAS_WS_BYTES of scratch. */
+gdb_status gdb_smear_bwd(int32_t B, int32_t T, int32_t C, int32_t ng, int32_t dtype,
+                         const void* e, const void* w, const float* lam, const float* s_save,
+                         const void* dx, const float* dxa, void* de, float* dlam, float* dw,
+                         int32_t accumulate, void* ws, void* stream);
+
+/* Backout, once before the final norm (section "1. Le modèle GPT", the backout
+ * snippet): y = x - lam[0]*x_bo, where x_bo is the output of block L/2 - 1.
+ * [N, C] in dtype; y may alias x but not x_bo; lam fp32 [1] device. */
+gdb_status gdb_backout_fwd(int32_t N, int32_t C, int32_t dtype, const void* x, const void* x_bo,
+                           const float* lam, void* y, void* stream);
+/* Backward: dy is the gradient w.r.t. y.  dx_bo += -lam[0]*dy in place (call
+ * it once dx_bo holds the gradient w.r.t. the output of block L/2 - 1 from the
+ * blocks above); dlam (fp32 [1]) = or += -sum(dy * x_bo).  dy's gradient
+ * w.r.t. x is dy itself.  ws: GDB_EXTRAS_WS_BYTES of scratch. */
+gdb_status gdb_backout_bwd(int32_t N, int32_t C, int32_t dtype, const void* dy, const void* x_bo,
+                           const float* lam, void* dx_bo, float* dlam, int32_t accumulate,
+                           void* ws, void* stream);
 
 /* ------------------------------------------------------------------------
  * Building blocks.  The calls above are compositions of these; they are

@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for must in ("gdb_block_fwd", "gdb_block_bwd", "gdb_lm_head_ce_fwd_bwd", "gdb_embed_fwd", "gdb_embed_bwd"):
+    for must in ("gdb_block_fwd", "gdb_block_bwd", "gdb_lm_head_ce_fwd_bwd", "gdb_embed_fwd", "gdb_embed_bwd",
+                 "gdb_smear_fwd", "gdb_smear_bwd", "gdb_backout_fwd", "gdb_backout_bwd"):
         assert must in names
 
 
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.lib().gdb_abi_version() == 1
+    assert L.lib().gdb_abi_version() == 2
 
 
 def _cfg(L, **kw):
@@ -94,17 +95,72 @@ def test_block_fwd_rejects_null_and_misaligned_pointers(L):
     base = ctypes.addressof(buf)
     al = (base + 255) & ~255
     w = L.BlockWeights(al, al, al, al)
-    st = lib.gdb_block_fwd(ctypes.byref(cfg), ctypes.byref(w), None, al, al + 512, al, al, None)
+    st = lib.gdb_block_fwd(ctypes.byref(cfg), ctypes.byref(w), None, None, al, al + 512, al, al, None)
     assert st == L.GDB_EINVAL and "rope_tab is NULL" in lib.gdb_last_error().decode()
-    st = lib.gdb_block_fwd(ctypes.byref(cfg), ctypes.byref(w), al, al + 2, al + 512, al, al, None)
+    st = lib.gdb_block_fwd(ctypes.byref(cfg), ctypes.byref(w), None, al, al + 2, al + 512, al, al, None)
     assert st == L.GDB_EINVAL and "x_in is not 16-byte aligned" in lib.gdb_last_error().decode()
-    st = lib.gdb_block_fwd(ctypes.byref(cfg), ctypes.byref(w), al, al, al, al, al, None)
+    st = lib.gdb_block_fwd(ctypes.byref(cfg), ctypes.byref(w), None, al, al, al, al, al, None)
     assert st == L.GDB_EINVAL and "alias" in lib.gdb_last_error().decode()
-    st = lib.gdb_block_fwd(ctypes.byref(cfg), None, al, al, al + 512, al, al, None)
+    st = lib.gdb_block_fwd(ctypes.byref(cfg), None, None, al, al, al + 512, al, al, None)
     assert st == L.GDB_EINVAL
     dw = L.BlockWgrads(al, 0, al, al)
-    st = lib.gdb_block_bwd(ctypes.byref(cfg), ctypes.byref(w), al, al, al, al, ctypes.byref(dw), al, None)
+    st = lib.gdb_block_bwd(ctypes.byref(cfg), ctypes.byref(w), None, al, al, al, al, ctypes.byref(dw), None, al,
+                           None)
     assert st == L.GDB_EINVAL and "dw_o is NULL" in lib.gdb_last_error().decode()
+
+
+def test_block_extras_validation(L):
+    lib = L.lib()
+    cfg = _cfg(L)
+    buf = ctypes.create_string_buffer(4096)
+    al = (ctypes.addressof(buf) + 255) & ~255
+    w = L.BlockWeights(al, al, al, al)
+    dw = L.BlockWgrads(al, al, al, al)
+
+    def fwd(ex):
+        return lib.gdb_block_fwd(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ex), al, al, al + 512, al, al,
+                                 None)
+
+    assert fwd(L.BlockExtras(lambdas=al)) == L.GDB_EINVAL
+    assert "ex->x0 is NULL" in lib.gdb_last_error().decode()
+    assert fwd(L.BlockExtras(lambdas=al + 2, x0=al)) == L.GDB_EINVAL
+    assert fwd(L.BlockExtras(ve=al, ve_gate=al, ids=al, ve_vocab=100, ve_gate_channels=65)) == L.GDB_EINVAL
+    assert "ve_gate_channels" in lib.gdb_last_error().decode()
+    assert fwd(L.BlockExtras(ve=al, ve_gate=al, ids=None, ve_vocab=100, ve_gate_channels=32)) == L.GDB_EINVAL
+    assert fwd(L.BlockExtras(ve=al, ve_gate=al, ids=al, ve_vocab=0, ve_gate_channels=32)) == L.GDB_EINVAL
+    # backward: mixing needs x_in and the gradients
+    ex = L.BlockExtras(lambdas=al, x0=al)
+    st = lib.gdb_block_bwd(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ex), al, al, al, al, ctypes.byref(dw),
+                           None, al, None)
+    assert st == L.GDB_EINVAL and "ex->x_in is NULL" in lib.gdb_last_error().decode()
+    ex = L.BlockExtras(lambdas=al, x0=al, x_in=al)
+    st = lib.gdb_block_bwd(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ex), al, al, al, al, ctypes.byref(dw),
+                           None, al, None)
+    assert st == L.GDB_EINVAL and "without extras gradients" in lib.gdb_last_error().decode()
+    dex = L.BlockExtrasGrads(dlambdas=al, dx0=None)
+    st = lib.gdb_block_bwd(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ex), al, al, al, al, ctypes.byref(dw),
+                           ctypes.byref(dex), al, None)
+    assert st == L.GDB_EINVAL and "dx0 is NULL" in lib.gdb_last_error().decode()
+
+
+def test_smear_backout_validation(L):
+    lib = L.lib()
+    al = 1 << 20   # never dereferenced: validation fails first
+    assert lib.gdb_smear_fwd(2, 16, 128, 64, 1, al, al, al, al + 4096, al, None) == L.GDB_EINVAL
+    assert "ng must be" in lib.gdb_last_error().decode()
+    assert lib.gdb_smear_fwd(2, 16, 128, 24, 1, al, al, al, al, al, None) == L.GDB_EINVAL
+    assert "alias" in lib.gdb_last_error().decode()
+    assert lib.gdb_smear_fwd(2, 16, 12, 8, 1, al, al, al, al + 4096, al, None) == L.GDB_EINVAL
+    assert lib.gdb_smear_fwd(0, 16, 128, 24, 1, None, None, None, None, None, None) == L.GDB_OK
+    assert lib.gdb_smear_bwd(2, 16, 128, 24, 1, al, al, al, al, al, None, al, al, al, 0, None, None) == L.GDB_EINVAL
+    assert "ws is NULL" in lib.gdb_last_error().decode()
+    assert lib.gdb_smear_bwd(2, 16, 128, 24, 1, al, al, al, al, al, None, al, al, al, 0, al, None) == L.GDB_EINVAL
+    assert "de must not alias" in lib.gdb_last_error().decode()
+    assert lib.gdb_backout_fwd(8, 128, 1, al, al + 4096, al, al + 4096, None) == L.GDB_EINVAL
+    assert lib.gdb_backout_fwd(0, 128, 1, None, None, None, None, None) == L.GDB_OK
+    assert lib.gdb_backout_bwd(8, 128, 1, al, al + 4096, None, al + 8192, al, 0, al, None) == L.GDB_EINVAL
+    assert "lam is NULL" in lib.gdb_last_error().decode()
+    assert lib.gdb_backout_bwd(8, 128, 1, al, al + 4096, al, al, al, 0, al, None) == L.GDB_EINVAL
 
 
 def test_gemm_and_attention_validation(L):

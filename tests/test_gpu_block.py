@@ -9,8 +9,8 @@ import torch
 import oracle as O
 from gpt_decoder_block_amd import ops
 from gpt_decoder_block_amd.stack import DecoderStack
-from gpu_util import DEV, TDT, assert_close, dev, empty, host, rounded
-from seeded_inputs import draw_all, draw_layer, draw_upstream, workload
+from gpu_util import DEV, TDT, TOL, assert_close, dev, empty, host, rounded
+from seeded_inputs import draw_all, draw_ids, draw_layer, draw_upstream, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -104,12 +104,13 @@ def _stack_case(w):
     layers = [{k: rounded(v, w.dtype) for k, v in p.items()} for p in d["layers"]]
     st = DecoderStack(n_layer=w.n_layer, B=w.B, T=w.T, C=w.C, n_head=w.n_head, n_kv_head=w.n_kv_head,
                       head_dim=w.head_dim, mlp_hidden=w.mlp_hidden, vocab=w.vocab, windows=w.windows,
-                      dtype=w.dtype, eps=w.eps, rope_base=w.rope_base, device=DEV)
+                      dtype=w.dtype, eps=w.eps, rope_base=w.rope_base, device=DEV, extras=w.extras,
+                      ve_gate_channels=w.ve_gate_channels, smear_channels=w.smear_channels)
     st.load(glob, layers)
     st.set_ids(d["ids"])
     loss = st.step()
     torch.cuda.synchronize()
-    l_ref, g, _ = O.stack_forward_backward(w, d["ids"], glob, layers)
+    l_ref, g, o_out = O.stack_forward_backward(w, d["ids"], glob, layers)
     dt = w.dtype
     tol = 1e-4 if dt == "f32" else 2e-2
     errs = {"loss": abs(loss.item() - l_ref) / abs(l_ref)}
@@ -119,7 +120,41 @@ def _stack_case(w):
     for l in range(w.n_layer):
         for t, k in zip(st.dlayers[l], ("w_qkv", "w_o", "w_fc", "w_proj")):
             errs[f"{l}.{k}"] = assert_close(t, g["layers"][l][k], dt, f"layer {l} d{k}")
-    print(f"stack {w.name} L={w.n_layer} B={w.B} T={w.T} errs={errs}", flush=True)
+        if w.extras:
+            gl = g["layers"][l]
+            if st.ve_layers[l]:
+                errs[f"{l}.ve"] = assert_close(st.dve[l], gl["ve"], dt, f"layer {l} dve")
+                errs[f"{l}.ve_gate"] = assert_close(st.dve_gate[l], gl["ve_gate"], dt, f"layer {l} dve_gate")
+    if w.extras:
+        # The residual, smear and backout scalars' gradients are sums over all
+        # B*T*C activations with heavy cancellation (the sum of the terms'
+        # magnitudes is 10^2..10^3 times the sum at these shapes), so a
+        # per-element error e of the bf16 activations moves them by up to
+        # e * sum|terms|, not e * |sum|.  The bar is the tensor bar applied to
+        # that forward error bound: |gpu - oracle| <= TOL * sum|terms|.  In fp32
+        # mode the plain relative bar holds as well.
+        sa = o_out["sum_abs"]
+        dl = np.stack([host(t) for t in st.dlambdas])
+
+        def scalar_close(gpu, ref, bound, what):
+            err = abs(float(gpu) - float(ref))
+            rel = err / max(abs(float(ref)), 1e-300)
+            ok = err <= TOL[dt] * bound if dt == "bf16" else rel <= TOL[dt]
+            assert ok, f"{what}: |d| {err:.3e} (rel {rel:.3e}, sum|terms| {bound:.3e})"
+            return err / bound
+
+        for l in range(w.n_layer):
+            gl = g["layers"][l]
+            errs[f"{l}.resid_lambda"] = scalar_close(dl[l, 0], gl["resid_lambda"], gl["sum_abs"]["resid_lambda"],
+                                                     f"layer {l} d resid_lambda")
+            errs[f"{l}.x0_lambda"] = scalar_close(dl[l, 1], gl["x0_lambda"], gl["sum_abs"]["x0_lambda"],
+                                                  f"layer {l} d x0_lambda")
+        errs["smear_lambda"] = scalar_close(host(st.d_smear_lambda)[0], g["smear_lambda"], sa["smear_lambda"],
+                                            "d smear_lambda")
+        errs["backout_lambda"] = scalar_close(host(st.d_backout_lambda)[0], g["backout_lambda"],
+                                              sa["backout_lambda"], "d backout_lambda")
+        errs["smear_gate"] = assert_close(st.d_smear_gate, g["smear_gate"], dt, "d smear_gate")
+    print(f"stack {w.name} L={w.n_layer} B={w.B} T={w.T} extras={w.extras} errs={errs}", flush=True)
 
 
 def test_stack_tiny_exact_workload():
@@ -133,3 +168,80 @@ def test_stack_d12_gqa_window_two_layers():
 
 def test_stack_d24_two_layers():
     _stack_case(workload("d24").with_(n_layer=2, B=1, T=256, windows=(-1, 128)))
+
+
+# ------------------------------------------------------------ extras (d26)
+def _block_extras_case(w, l, B, T):
+    """One block with residual mixing (and, on odd l, the value embedding);
+    dx0 is pre-filled to check that the x0 share is added to it."""
+    w = w.with_(B=B, T=T)
+    dt = w.dtype
+    N, C, KV = B * T, w.C, w.n_kv_head * w.head_dim
+    p = {k: (rounded(v, dt) if np.ndim(v) else np.float32(v)) for k, v in draw_layer(w, l).items()}
+    x = rounded(draw_upstream(w, 100 + l, (N, C), 1.0), dt)
+    x0 = rounded(draw_upstream(w, 150 + l, (N, C), 1.0), dt)
+    dy = rounded(draw_upstream(w, 200 + l, (N, C), 1.0), dt)
+    dx0_prev = draw_upstream(w, 250 + l, (N, C), 0.1).astype(np.float32)
+    ids = draw_ids(w)[:, :T]
+    cfg = ops.make_cfg(B, T, C, w.n_head, w.n_kv_head, w.head_dim, w.mlp_hidden, w.windows[l], TDT[dt], w.eps)
+    sv, wf, wb = ops.block_sizes(cfg)
+    saved = torch.empty(sv, dtype=torch.uint8, device=DEV)
+    wsf = torch.empty(wf, dtype=torch.uint8, device=DEV)
+    wsb = torch.empty(wb, dtype=torch.uint8, device=DEV)
+    W = [dev(p[k], dt) for k in ("w_qkv", "w_o", "w_fc", "w_proj")]
+    dW = [empty(t.shape, torch.float32) for t in W]
+    rope = ops.rope_table(T, w.head_dim, w.rope_base, DEV)
+    xg, x0g, out = dev(x, dt), dev(x0, dt), empty((N, C), dt)
+    lam = torch.tensor([p["resid_lambda"], p["x0_lambda"]], dtype=torch.float32, device=DEV)
+    idsg = torch.from_numpy(ids.reshape(-1).astype(np.int32)).to(DEV)
+    has_ve = "ve" in p
+    ve = dev(p["ve"], dt) if has_ve else None
+    vg = dev(p["ve_gate"], dt) if has_ve else None
+    dlam = empty((2,), torch.float32)
+    dx0 = torch.from_numpy(dx0_prev).to(DEV)
+    dve = empty((w.vocab, KV), torch.float32, fill=7.0) if has_ve else None   # overwritten (no accumulate)
+    dvg = empty((w.n_kv_head, w.ve_gate_channels), torch.float32) if has_ve else None
+    ex = ops.block_extras(lam, x0g, xg, idsg, ve, vg)
+    dex = ops.block_extras_grads(dlam, dx0, dve, dvg, accumulate_dx0=True)
+    ops.block_fwd(cfg, W, rope, xg, out, saved, wsf, ex)
+    dx = dev(dy, dt)
+    ops.block_bwd(cfg, W, rope, saved, dx, dx, dW, wsb, ex, dex)
+    torch.cuda.synchronize()
+    cos, sin = O.rope_tables(T, w.head_dim, w.rope_base)
+    pp = {k: np.asarray(v, dtype=np.float64) for k, v in p.items()}
+    o_out, c = O.block_forward(x.astype(np.float64).reshape(B, T, C), pp, w, l, cos, sin,
+                               x0=x0.astype(np.float64).reshape(B, T, C), ids=ids)
+    o_dx, g = O.block_backward(dy.astype(np.float64).reshape(B, T, C), c, pp, w, l, cos, sin, ids=ids)
+    errs = {"x_out": assert_close(out, o_out.reshape(N, C), dt, "x_out"),
+            "dx_in": assert_close(dx, o_dx.reshape(N, C), dt, "dx_in"),
+            "dx0": assert_close(dx0, dx0_prev + g["x0"].reshape(N, C), dt, "dx0"),
+            "dlambdas": assert_close(dlam, [g["resid_lambda"], g["x0_lambda"]], dt, "dlambdas")}
+    for name, t in zip(("w_qkv", "w_o", "w_fc", "w_proj"), dW):
+        errs[name] = assert_close(t, g[name], dt, "d" + name)
+    if has_ve:
+        errs["ve"] = assert_close(dve, g["ve"], dt, "dve")
+        errs["ve_gate"] = assert_close(dvg, g["ve_gate"], dt, "dve_gate")
+    print(f"block+extras {w.name} l={l} B={B} T={T} ve={has_ve} errs={errs}", flush=True)
+
+
+@pytest.mark.parametrize("l", [0, 1])
+def test_block_extras_d26_widths(l):
+    # d26 widths (C=1664, 13 heads), vocabulary cut to 512 so the oracle's
+    # value-embedding table stays small; l=1 carries a value embedding
+    w = workload("d26").with_(n_layer=2, windows=(-1, -1), vocab=512, mlp_fp8=False)
+    _block_extras_case(w, l, 1, 130)
+
+
+@pytest.mark.parametrize("l", [0, 1])
+def test_block_extras_tiny_fp32(l):
+    w = workload("tiny").with_(n_layer=2, windows=(-1, -1), extras=True)
+    _block_extras_case(w, l, 2, 37)
+
+
+def test_stack_extras_tiny_fp32():
+    _stack_case(workload("tiny").with_(n_layer=4, windows=(-1,) * 4, extras=True))
+
+
+def test_stack_extras_d26_four_layers():
+    # smear, residual mixing, value embeddings on layers 1 and 3, backout of block 1
+    _stack_case(workload("d26").with_(n_layer=4, B=1, T=128, vocab=512, windows=(-1,) * 4, mlp_fp8=False))
