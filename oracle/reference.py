@@ -32,7 +32,9 @@ Readings taken where the pages are silent (each listed in the design doc):
   * the loss is the mean over all B*T positions, no ignore index;
   * fp8 operands (d26 MLP) are OCP e4m3fn with a per-tensor scale
     amax/448, round-to-nearest-even, saturating; gradients pass straight
-    through the quantiser.
+    through the quantiser; all six MLP products (forward, data and weight
+    gradients) take fp8 operands; scale and division in float32, and in
+    bf16 mode the quantised tensors are bf16 values.
 
 Pins (tests/test_oracle_*.py): finite differences of every gradient on tiny
 shapes; RoPE preserves norms, is the identity at t = 0 and depends only on
@@ -55,7 +57,7 @@ import numpy as np
 __all__ = [
     "rms_norm", "rms_norm_backward", "rope_tables", "rope", "rope_backward",
     "visible_mask", "attention", "attention_logsumexp", "attention_backward", "cross_entropy", "e4m3_round",
-    "fp8_quantize", "fp8_quant_dequant", "block_forward", "block_backward", "lm_head_ce",
+    "bf16_round", "fp8_quantize", "fp8_quant_dequant", "block_forward", "block_backward", "lm_head_ce",
     "embed_forward", "embed_backward", "smear_forward", "smear_backward",
     "stack_forward_backward", "FP8_E4M3_MAX",
 ]
@@ -195,14 +197,27 @@ def e4m3_round(x: np.ndarray) -> np.ndarray:
     return np.where(x < 0, -q, q)
 
 
-def fp8_quantize(x: np.ndarray) -> Tuple[np.ndarray, float]:
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest bfloat16 (ties to even, via float32), as float64."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    b = f.view(np.uint32)
+    b = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return b.view(np.float32).astype(np.float64)
+
+
+def fp8_quantize(x: np.ndarray, storage: Optional[str] = None) -> Tuple[np.ndarray, float]:
     """Per-tensor dynamic scaling: s = amax|x| / 448 and codes e4m3(x / s).
     The pages fix no precision for the scale and the division; both are taken
     in float32 (amax rounded to float32, s = amax / 448 and x / s each one
     correctly rounded float32 operation), so an input that is exactly
     representable in float32 gets the same code whatever computes it.
+    storage="bf16": the quantised tensor is a bfloat16 activation (explicit
+    dtypes, section "3. Gestion de la précision"), so its values are rounded
+    to bfloat16 before the codes are chosen.
     Returns (the e4m3 values as float64, s as a float)."""
     x = np.asarray(x, dtype=np.float64)
+    if storage == "bf16":
+        x = bf16_round(x)
     amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
     if amax == 0.0:
         return np.zeros_like(x), 0.0
@@ -211,16 +226,16 @@ def fp8_quantize(x: np.ndarray) -> Tuple[np.ndarray, float]:
     return e4m3_round(q.astype(np.float64)), float(s)
 
 
-def fp8_quant_dequant(x: np.ndarray) -> np.ndarray:
+def fp8_quant_dequant(x: np.ndarray, storage: Optional[str] = None) -> np.ndarray:
     """x ~ e4m3(x / s) * s with the per-tensor scale of `fp8_quantize`."""
-    q, s = fp8_quantize(x)
+    q, s = fp8_quantize(x, storage)
     return q * s
 
 
-def _mm_nt(a, b, fp8):
+def _mm_nt(a, b, fp8, storage=None):
     """a @ b^T, operands optionally through the fp8 quantiser."""
     if fp8:
-        a, b = fp8_quant_dequant(a), fp8_quant_dequant(b)
+        a, b = fp8_quant_dequant(a, storage), fp8_quant_dequant(b, storage)
     return a @ b.T
 
 
@@ -270,9 +285,10 @@ def block_forward(x: np.ndarray, p: Dict[str, np.ndarray], cfg, l: int,
     o2 = o.reshape(B, T, Q)
     x_mid = x + o2 @ p["w_o"].T
     xn2, r2 = rms_norm(x_mid, eps)
-    u = _mm_nt(xn2, p["w_fc"], fp8)
+    st = getattr(cfg, "dtype", None)
+    u = _mm_nt(xn2, p["w_fc"], fp8, st)
     h = np.maximum(u, 0.0) ** 2
-    out = x_mid + _mm_nt(h, p["w_proj"], fp8)
+    out = x_mid + _mm_nt(h, p["w_proj"], fp8, st)
     c.update(xn1=xn1, r1=r1, qn=qn, rq=rq, kn=kn, rk=rk, qh=qh, kh=kh, v=v, o=o2,
              P=P, x_mid=x_mid, xn2=xn2, r2=r2, u=u, h=h)
     return out, c
@@ -289,7 +305,8 @@ def block_backward(dout: np.ndarray, c: dict, p: Dict[str, np.ndarray], cfg, l: 
     Q, KV = H * D, Hkv * D
     fp8 = bool(getattr(cfg, "mlp_fp8", False))
     g = {}
-    q8 = fp8_quant_dequant if fp8 else (lambda a: a)
+    st = getattr(cfg, "dtype", None)
+    q8 = (lambda a: fp8_quant_dequant(a, st)) if fp8 else (lambda a: a)
     # MLP: out = x_mid + h W_proj^T, h = relu(u)^2, u = xn2 W_fc^T
     dh = q8(dout) @ q8(p["w_proj"])
     g["w_proj"] = np.einsum("btc,btf->cf", q8(dout), q8(c["h"]))

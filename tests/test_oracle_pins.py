@@ -265,6 +265,16 @@ def test_e4m3_matches_torch_cast_on_all_bf16_in_range():
     np.testing.assert_array_equal(O.e4m3_round(f), ref)
 
 
+def test_bf16_round_matches_torch_cast():
+    torch = pytest.importorskip("torch")
+    x = np.concatenate([RNG.standard_normal(4096) * 10.0 ** RNG.integers(-8, 8, 4096),
+                        # exact ties between two bfloat16 values: 1 + 2^-8 -> 1, 1 + 3*2^-8 -> 1 + 2^-6
+                        [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 0.0, 65504.0]])
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.bf16_round(x), ref)
+    assert O.bf16_round(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
+
+
 def test_fp8_quant_dequant_error_bound():
     x = RNG.standard_normal((64, 64)) * 5.0
     y = O.fp8_quant_dequant(x)

@@ -6,7 +6,13 @@ F.embedding and F.cross_entropy, and takes every gradient from autograd.  It
 shares nothing with the oracle's hand-written backward, so it pins the
 oracle's forward to the library routines and its backward to autograd.  Only
 RoPE and the d26 extras are written out here (RoPE is pinned separately by
-its invariants in test_oracle_pins.py)."""
+its invariants in test_oracle_pins.py).
+
+The fp8 MLP is checked the same way: torch's own float8_e4m3fn cast makes the
+codes, a straight-through wrapper passes gradients through the quantiser, and
+an identity whose backward quantises the incoming gradient puts the output
+gradient of each MLP product on fp8 as well, so autograd yields the six fp8
+products without any hand-written backward."""
 import math
 
 import numpy as np
@@ -27,6 +33,36 @@ def _rope_t(x, T, D, base):
     c, s = torch.cos(th)[None, :, None, :], torch.sin(th)[None, :, None, :]
     a, b = x[..., : D // 2], x[..., D // 2:]
     return torch.cat([a * c - b * s, a * s + b * c], dim=-1)
+
+
+def _q8_t(x, storage):
+    """Per-tensor e4m3 quantise-dequantise with torch's cast (float32 scale and division)."""
+    if storage == "bf16":
+        x = x.to(torch.bfloat16).to(torch.float64)
+    amax = x.abs().max().to(torch.float32)
+    if float(amax) == 0.0:
+        return torch.zeros_like(x)
+    s = amax / torch.tensor(448.0, dtype=torch.float32)
+    q = (x.to(torch.float32) / s).to(torch.float8_e4m3fn).to(torch.float64)
+    return q * s.to(torch.float64)
+
+
+class _GradQ(torch.autograd.Function):
+    """Identity whose backward quantises the incoming gradient."""
+
+    @staticmethod
+    def forward(ctx, x, storage):
+        ctx.storage = storage
+        return x.view_as(x)
+
+    @staticmethod
+    def backward(ctx, g):
+        return _q8_t(g, ctx.storage), None
+
+
+def _fp8_linear(x, w, storage):
+    st = lambda a: a + (_q8_t(a.detach(), storage) - a).detach()   # value q8(a), gradient 1
+    return _GradQ.apply(F.linear(st(x), st(w)), storage)
 
 
 def torch_step(cfg, ids, glob, layers):
@@ -69,8 +105,12 @@ def torch_step(cfg, ids, glob, layers):
                                            attn_mask=mask, enable_gqa=True)
         o = o.transpose(1, 2).reshape(B, T, Q)
         x = x + F.linear(o, p["w_o"])
-        h = F.relu(F.linear(F.rms_norm(x, (C,), eps=eps), p["w_fc"])) ** 2
-        x = x + F.linear(h, p["w_proj"])
+        if getattr(cfg, "mlp_fp8", False):
+            h = F.relu(_fp8_linear(F.rms_norm(x, (C,), eps=eps), p["w_fc"], cfg.dtype)) ** 2
+            x = x + _fp8_linear(h, p["w_proj"], cfg.dtype)
+        else:
+            h = F.relu(F.linear(F.rms_norm(x, (C,), eps=eps), p["w_fc"])) ** 2
+            x = x + F.linear(h, p["w_proj"])
         if cfg.extras and l == cfg.n_layer // 2 - 1:
             x_bo = x
     if cfg.extras:
@@ -122,3 +162,16 @@ def test_oracle_matches_torch_on_tiny_workload():
     w = workload("tiny")
     d = draw_all(w)
     _compare(w, d["ids"], d["globals"], d["layers"], tol=1e-10)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_oracle_matches_torch_autograd_fp8_mlp(dtype):
+    # fp8 MLP with and without the other extras; "bf16" also rounds every
+    # quantised tensor to bfloat16 first (on both sides, by different code)
+    cfg = tiny_cfg(C=48, n_head=3, n_kv_head=1, head_dim=16, mlp_hidden=96, vocab=13, T=7,
+                   n_layer=4, windows=(-1, 2, -1, 3), extras=True, mlp_fp8=True, dtype=dtype)
+    ids, glob, layers = _params(cfg, np.random.default_rng(13))
+    _compare(cfg, ids, glob, layers)
+    cfg = tiny_cfg(mlp_fp8=True, dtype=dtype)
+    ids, glob, layers = _params(cfg, np.random.default_rng(14))
+    _compare(cfg, ids, glob, layers)
