@@ -92,6 +92,12 @@ SIGNATURES = {
     "gdb_gemm": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_int32,
                            c_int32, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
                            c_void_p]),
+    "gdb_fp8_quantize": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                   c_void_p]),
+    "gdb_gemm_fp8_ws_bytes": (c_int32, [c_int32, c_int32, c_int32, c_int32, ctypes.POINTER(c_size_t)]),
+    "gdb_gemm_fp8": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
+                               c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
+                               c_void_p]),
     "gdb_qk_norm_rope_fwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_float, c_void_p,
                                        c_void_p, c_void_p, c_void_p, c_void_p]),
     "gdb_qk_norm_rope_bwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,

@@ -60,6 +60,8 @@ struct Carver {
 struct BlockDims {
   int B, T, N, C, H, Hkv, D, Q, KV, W3, F, window, dt, s;
   float eps;
+  bool fp8;   // MLP GEMMs on e4m3 codes
+  int Np;     // N rounded up to 16: K of the fp8 weight-gradient GEMMs
 };
 
 // Largest value-embedding gate width (one lane per channel).
@@ -76,7 +78,7 @@ gdb_status check_cfg(const gdb_block_cfg* c, BlockDims* d) {
   if (c->n_head * c->head_dim != c->C) return fail(GDB_EUNSUPPORTED, "n_head*head_dim (%d) must equal C (%d)", c->n_head * c->head_dim, c->C);
   if (c->C % 8 || c->mlp_hidden <= 0 || c->mlp_hidden % 8) return fail(GDB_EINVAL, "C and mlp_hidden must be positive multiples of 8");
   if (c->window < -1) return fail(GDB_EINVAL, "window must be >= -1 (got %d)", c->window);
-  if (c->mlp_fp8) return fail(GDB_EUNSUPPORTED, "mlp_fp8 is not available in this build");
+  if (c->mlp_fp8 && (c->C % 16 || c->mlp_hidden % 16)) return fail(GDB_EINVAL, "mlp_fp8 needs C and mlp_hidden multiples of 16");
   if (!(c->eps > 0.f) || !std::isfinite(c->eps)) return fail(GDB_EINVAL, "eps must be positive and finite");
   if ((long long)c->B * c->T > (1LL << 30)) return fail(GDB_EINVAL, "B*T too large");
   d->B = c->B; d->T = c->T; d->N = c->B * c->T; d->C = c->C;
@@ -84,6 +86,8 @@ gdb_status check_cfg(const gdb_block_cfg* c, BlockDims* d) {
   d->Q = d->H * d->D; d->KV = d->Hkv * d->D; d->W3 = d->Q + 2 * d->KV;
   d->F = c->mlp_hidden; d->window = c->window >= c->T - 1 ? -1 : c->window;
   d->dt = c->dtype; d->s = dt_size(c->dtype); d->eps = c->eps;
+  d->fp8 = c->mlp_fp8 != 0;
+  d->Np = (d->N + 15) / 16 * 16;
   return GDB_OK;
 }
 
@@ -91,16 +95,22 @@ struct Saved {
   void *xn1, *qkvh, *o, *xn2, *u, *h;
   float *r1, *rqk, *lse, *r2;
   float* ve_s;          // value-embedding gate logits [N, Hkv]
+  // fp8 MLP: transposed codes for the backward and the four amax values
+  uint8_t *xn2T, *hT, *wfcT, *wprojT;   // [C, Np], [F, Np], [C, F], [F, C]
+  float* amax;                          // xn2, w_fc, h, w_proj
 };
 struct WsFwd {
   void *qkv, *x_mid;
   void* x_mix;          // residual-mixed block input [N, C]
+  uint8_t *xn2q, *wfcq, *hq, *wprojq;  // fp8 MLP codes, row-major
 };
 struct WsBwd {
   void *du, *dxn, *dx_mid, *dout, *dqkv;
   float *delta, *partial;
   float* ds;            // value-embedding gate logit gradients [N, Hkv]
   float* xpart;         // partial sums of the extras' parameter gradients
+  uint8_t *doutq, *doutT, *duq, *duT;  // fp8 MLP backward codes: [N, C], [C, Np], [N, F], [F, Np]
+  float* amax8;                        // dout, du
 };
 
 void carve_saved(const BlockDims& d, Carver& c, Saved& s) {
@@ -116,11 +126,22 @@ void carve_saved(const BlockDims& d, Carver& c, Saved& s) {
   s.u = c.take<char>(N * d.F * d.s);
   s.h = c.take<char>(N * d.F * d.s);
   s.ve_s = c.take<float>(N * d.Hkv * 4);
+  const size_t f8 = d.fp8 ? 1 : 0, Np = d.Np;
+  s.xn2T = c.take<uint8_t>(f8 * d.C * Np);
+  s.hT = c.take<uint8_t>(f8 * d.F * Np);
+  s.wfcT = c.take<uint8_t>(f8 * d.C * d.F);
+  s.wprojT = c.take<uint8_t>(f8 * d.F * d.C);
+  s.amax = c.take<float>(f8 * 4 * 4);
 }
 void carve_fwd(const BlockDims& d, Carver& c, WsFwd& w) {
   w.qkv = c.take<char>((size_t)d.N * d.W3 * d.s);
   w.x_mid = c.take<char>((size_t)d.N * d.C * d.s);
   w.x_mix = c.take<char>((size_t)d.N * d.C * d.s);
+  const size_t f8 = d.fp8 ? 1 : 0, N = d.N;
+  w.xn2q = c.take<uint8_t>(f8 * N * d.C);
+  w.wfcq = c.take<uint8_t>(f8 * d.F * d.C);
+  w.hq = c.take<uint8_t>(f8 * N * d.F);
+  w.wprojq = c.take<uint8_t>(f8 * d.C * d.F);
 }
 size_t wgrad_partial_floats(const BlockDims& d) {
   size_t m = 0;
@@ -128,6 +149,10 @@ size_t wgrad_partial_floats(const BlockDims& d) {
   for (auto& sh : shapes) {
     const int sp = gemm_splits(d.dt, sh[0], sh[1], d.N, EPI_F32);
     if (sp > 1) m = std::max(m, (size_t)sp * sh[0] * sh[1]);
+    if (d.fp8) {
+      const int s8 = gemm_splits(FP8, sh[0], sh[1], d.Np, EPI_F32);
+      if (s8 > 1) m = std::max(m, (size_t)s8 * sh[0] * sh[1]);
+    }
   }
   return m;
 }
@@ -143,6 +168,12 @@ void carve_bwd(const BlockDims& d, Carver& c, WsBwd& w) {
   w.ds = c.take<float>(N * d.Hkv * 4);
   const size_t xp = std::max((size_t)mix_partials(d.N) * 2, (size_t)ve_gate_partials(d.N) * d.Hkv * MAX_VE_GATE);
   w.xpart = c.take<float>(xp * 4);
+  const size_t f8 = d.fp8 ? 1 : 0, Np = d.Np;
+  w.doutq = c.take<uint8_t>(f8 * N * d.C);
+  w.doutT = c.take<uint8_t>(f8 * d.C * Np);
+  w.duq = c.take<uint8_t>(f8 * N * d.F);
+  w.duT = c.take<uint8_t>(f8 * d.F * Np);
+  w.amax8 = c.take<float>(f8 * 2 * 4);
 }
 
 // Which extras a call uses; validates their pointers and sizes.
@@ -189,6 +220,20 @@ hipError_t wgrad(int dt, const void* A, int lda, const void* B, int ldb, int M, 
   g.splits = gemm_splits(dt, M, N, K, EPI_F32);
   g.partial = partial;
   hipError_t e = gemm(dt, g, s);
+  if (e != hipSuccess || g.splits == 1) return e;
+  return splitk_reduce(partial, C, g.splits, (size_t)M * N, accumulate, s);
+}
+
+// fp32 weight gradient from fp8 codes: C[M, N] (+)= s_a s_b sum_k A[m, k] B[n, k]
+// (A [M, K], B [N, K] row-major codes, K the padded token count)
+hipError_t wgrad_fp8(const uint8_t* A, const float* amax_a, const uint8_t* B, const float* amax_b, int M, int N,
+                     int K, float* C, int accumulate, float* partial, hipStream_t s) {
+  GemmArgs g = gemm_args(A, true, K, B, true, K, M, N, K, EPI_F32, C, N);
+  g.accumulate = accumulate;
+  g.splits = gemm_splits(FP8, M, N, K, EPI_F32);
+  g.partial = partial;
+  g.amax_a = amax_a; g.amax_b = amax_b;
+  hipError_t e = gemm_fp8(BF16, g, s);  // fp32 output: the element type of C is fixed
   if (e != hipSuccess || g.splits == 1) return e;
   return splitk_reduce(partial, C, g.splits, (size_t)M * N, accumulate, s);
 }
@@ -296,6 +341,26 @@ gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
   g.R = x; g.ldr = d.C;
   HIPCHK(gemm(dt, g, s));
   HIPCHK(rmsnorm_fwd(dt, wf.x_mid, sv.xn2, sv.r2, N, d.C, d.eps, s));
+  if (d.fp8) {
+    // e4m3 codes of both operands of each MLP product (row-major for the
+    // forward, transposed copies kept for the backward), per-tensor scales
+    HIPCHK(fp8_amax(dt, sv.xn2, (size_t)N * d.C, sv.amax + 0, s));
+    HIPCHK(fp8_quant(dt, sv.xn2, N, d.C, sv.amax + 0, wf.xn2q, sv.xn2T, d.Np, s));
+    HIPCHK(fp8_amax(dt, w->w_fc, (size_t)d.F * d.C, sv.amax + 1, s));
+    HIPCHK(fp8_quant(dt, w->w_fc, d.F, d.C, sv.amax + 1, wf.wfcq, sv.wfcT, d.F, s));
+    g = gemm_args(wf.xn2q, true, d.C, wf.wfcq, true, d.C, N, d.F, d.C, EPI_RELU2, sv.u, d.F);
+    g.C2 = sv.h; g.amax_a = sv.amax + 0; g.amax_b = sv.amax + 1;
+    HIPCHK(gemm_fp8(dt, g, s));
+    HIPCHK(fp8_amax(dt, sv.h, (size_t)N * d.F, sv.amax + 2, s));
+    HIPCHK(fp8_quant(dt, sv.h, N, d.F, sv.amax + 2, wf.hq, sv.hT, d.Np, s));
+    HIPCHK(fp8_amax(dt, w->w_proj, (size_t)d.C * d.F, sv.amax + 3, s));
+    HIPCHK(fp8_quant(dt, w->w_proj, d.C, d.F, sv.amax + 3, wf.wprojq, sv.wprojT, d.C, s));
+    g = gemm_args(wf.hq, true, d.F, wf.wprojq, true, d.F, N, d.C, d.F, EPI_RESID, x_out, d.C);
+    g.R = wf.x_mid; g.ldr = d.C; g.amax_a = sv.amax + 2; g.amax_b = sv.amax + 3;
+    HIPCHK(gemm_fp8(dt, g, s));
+    g_err.clear();
+    return GDB_OK;
+  }
   g = gemm_args(sv.xn2, true, d.C, w->w_fc, true, d.C, N, d.F, d.C, EPI_RELU2, sv.u, d.F);
   g.C2 = sv.h;
   HIPCHK(gemm(dt, g, s));
@@ -335,12 +400,29 @@ gdb_status gdb_block_bwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
   const int dt = d.dt, N = d.N, acc = cfg->accumulate_wgrad ? 1 : 0;
 
   // MLP
-  GemmArgs g = gemm_args(dx_out, true, d.C, w->w_proj, false, d.F, N, d.F, d.C, EPI_DRELU2, wb.du, d.F);
-  g.R = sv.u; g.ldr = d.F;
-  HIPCHK(gemm(dt, g, s));
-  HIPCHK(wgrad(dt, dx_out, d.C, sv.h, d.F, d.C, d.F, N, dw->dw_proj, acc, wb.partial, s));
-  HIPCHK(gemm(dt, gemm_args(wb.du, true, d.F, w->w_fc, false, d.C, N, d.C, d.F, EPI_STORE, wb.dxn, d.C), s));
-  HIPCHK(wgrad(dt, wb.du, d.F, sv.xn2, d.C, d.F, d.C, N, dw->dw_fc, acc, wb.partial, s));
+  if (d.fp8) {
+    // straight-through fp8: the same codes and scales as the forward for the
+    // weights and saved activations, fresh ones for dout and du
+    HIPCHK(fp8_amax(dt, dx_out, (size_t)N * d.C, wb.amax8 + 0, s));
+    HIPCHK(fp8_quant(dt, dx_out, N, d.C, wb.amax8 + 0, wb.doutq, wb.doutT, d.Np, s));
+    GemmArgs g = gemm_args(wb.doutq, true, d.C, sv.wprojT, true, d.C, N, d.F, d.C, EPI_DRELU2, wb.du, d.F);
+    g.R = sv.u; g.ldr = d.F; g.amax_a = wb.amax8 + 0; g.amax_b = sv.amax + 3;
+    HIPCHK(gemm_fp8(dt, g, s));
+    HIPCHK(wgrad_fp8(wb.doutT, wb.amax8 + 0, sv.hT, sv.amax + 2, d.C, d.F, d.Np, dw->dw_proj, acc, wb.partial, s));
+    HIPCHK(fp8_amax(dt, wb.du, (size_t)N * d.F, wb.amax8 + 1, s));
+    HIPCHK(fp8_quant(dt, wb.du, N, d.F, wb.amax8 + 1, wb.duq, wb.duT, d.Np, s));
+    g = gemm_args(wb.duq, true, d.F, sv.wfcT, true, d.F, N, d.C, d.F, EPI_STORE, wb.dxn, d.C);
+    g.amax_a = wb.amax8 + 1; g.amax_b = sv.amax + 1;
+    HIPCHK(gemm_fp8(dt, g, s));
+    HIPCHK(wgrad_fp8(wb.duT, wb.amax8 + 1, sv.xn2T, sv.amax + 0, d.F, d.C, d.Np, dw->dw_fc, acc, wb.partial, s));
+  } else {
+    GemmArgs g = gemm_args(dx_out, true, d.C, w->w_proj, false, d.F, N, d.F, d.C, EPI_DRELU2, wb.du, d.F);
+    g.R = sv.u; g.ldr = d.F;
+    HIPCHK(gemm(dt, g, s));
+    HIPCHK(wgrad(dt, dx_out, d.C, sv.h, d.F, d.C, d.F, N, dw->dw_proj, acc, wb.partial, s));
+    HIPCHK(gemm(dt, gemm_args(wb.du, true, d.F, w->w_fc, false, d.C, N, d.C, d.F, EPI_STORE, wb.dxn, d.C), s));
+    HIPCHK(wgrad(dt, wb.du, d.F, sv.xn2, d.C, d.F, d.C, N, dw->dw_fc, acc, wb.partial, s));
+  }
   HIPCHK(rmsnorm_bwd(dt, wb.dxn, sv.xn2, sv.r2, dx_out, wb.dx_mid, N, d.C, s));
   // attention output projection
   HIPCHK(gemm(dt, gemm_args(wb.dx_mid, true, d.C, w->w_o, false, d.Q, N, d.Q, d.C, EPI_STORE, wb.dout, d.Q), s));
@@ -493,6 +575,68 @@ gdb_status gdb_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* 
   } else {
     HIPCHK(gemm(dtype, g, (hipStream_t)stream));
   }
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_fp8_quantize(int32_t R, int32_t Cc, int32_t dtype, const void* x, float* amax, uint8_t* xq,
+                            uint8_t* xqt, int32_t Rp, void* stream) {
+  if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
+  if (R < 0 || Cc < 0 || Cc % 16) return fail(GDB_EINVAL, "R must be >= 0 and Cc a multiple of 16 (got %d, %d)", R, Cc);
+  if ((long long)R * Cc > (1LL << 40)) return fail(GDB_EINVAL, "tensor too large");
+  if (xqt && (Rp < R || Rp % 16)) return fail(GDB_EINVAL, "Rp must be a multiple of 16 and >= R (got %d)", Rp);
+  if (!amax || (((uintptr_t)amax) & 3)) return fail(GDB_EINVAL, "amax is NULL or not 4-byte aligned");
+  if (!xq && !xqt) return fail(GDB_EINVAL, "xq and xqt are both NULL");
+  if (R > 0 && Cc > 0) CHECK_PTR(x);
+  if (xq) CHECK_PTR(xq);
+  if (xqt) CHECK_PTR(xqt);
+  hipStream_t s = (hipStream_t)stream;
+  HIPCHK(fp8_amax(dtype, x, (size_t)R * Cc, amax, s));
+  HIPCHK(fp8_quant(dtype, x, R, Cc, amax, xq, xqt, xqt ? Rp : R, s));
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_gemm_fp8_ws_bytes(int32_t M, int32_t N, int32_t K, int32_t epi, size_t* ws_bytes) {
+  if (M < 0 || N < 0 || K < 0) return fail(GDB_EINVAL, "negative size");
+  if (epi < 0 || epi > EPI_F32) return fail(GDB_EINVAL, "unknown epilogue %d", epi);
+  const int sp = gemm_splits(FP8, M, N, K, epi);
+  if (ws_bytes) *ws_bytes = sp > 1 ? (size_t)sp * M * N * 4 : 0;
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_gemm_fp8(int32_t dtype, int32_t M, int32_t N, int32_t K, const uint8_t* A, int32_t lda,
+                        const float* amax_a, const uint8_t* B, int32_t ldb, const float* amax_b, int32_t epi, void* C,
+                        int32_t ldc, const void* R, int32_t ldr, void* C2, int32_t accumulate, void* ws,
+                        void* stream) {
+  if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
+  if (M < 0 || N < 0 || K < 0) return fail(GDB_EINVAL, "negative size");
+  if (epi < 0 || epi > EPI_F32) return fail(GDB_EINVAL, "unknown epilogue %d", epi);
+  if (K % 16 || lda % 16 || ldb % 16) return fail(GDB_EINVAL, "K, lda, ldb must be multiples of 16");
+  if (N % 8 || ldc % 8) return fail(GDB_EINVAL, "N and ldc must be multiples of 8");
+  if (lda < K || ldb < K || ldc < N) return fail(GDB_EINVAL, "leading dimension too small");
+  if (M == 0 || N == 0) { g_err.clear(); return GDB_OK; }
+  CHECK_PTR(A); CHECK_PTR(B); CHECK_PTR(C);
+  if (!amax_a || !amax_b || (((uintptr_t)amax_a) & 3) || (((uintptr_t)amax_b) & 3))
+    return fail(GDB_EINVAL, "amax_a or amax_b is NULL or not 4-byte aligned");
+  if (epi == EPI_RESID || epi == EPI_DRELU2) {
+    CHECK_PTR(R);
+    if (ldr % 8 || ldr < N) return fail(GDB_EINVAL, "ldr must be a multiple of 8 and >= N");
+  }
+  if (epi == EPI_RELU2) CHECK_PTR(C2);
+  if (epi == EPI_F32 && ldc != N) return fail(GDB_EINVAL, "fp32 output needs ldc == N");
+  hipStream_t s = (hipStream_t)stream;
+  GemmArgs g = gemm_args(A, true, lda, B, true, ldb, M, N, K, epi, C, ldc);
+  g.R = R; g.ldr = ldr; g.C2 = C2; g.accumulate = accumulate ? 1 : 0;
+  g.amax_a = amax_a; g.amax_b = amax_b;
+  if (epi == EPI_F32) {
+    g.splits = gemm_splits(FP8, M, N, K, epi);
+    if (g.splits > 1) CHECK_PTR(ws);
+    g.partial = (float*)ws;
+  }
+  HIPCHK(gemm_fp8(dtype, g, s));
+  if (epi == EPI_F32 && g.splits > 1) HIPCHK(splitk_reduce(g.partial, (float*)C, g.splits, (size_t)M * N, g.accumulate, s));
   g_err.clear();
   return GDB_OK;
 }

@@ -22,7 +22,14 @@
 //   * tile ids are remapped so that each XCD (blocks are dealt round-robin to
 //     the 8 XCDs) works on a contiguous, grouped range of tiles and reuses
 //     A rows / B columns in its own L2.
+// fp8 path (v_mfma_f32_32x32x64_f8f6f4 on OCP e4m3 codes, both operands
+// K-contiguous): the same tiles, LDS layout and loaders with a K step of 128
+// codes (the same 128-byte LDS rows); each lane's fragment is 32 bytes (two
+// swizzled chunks) and the per-tensor scales amax/448 of both operands
+// multiply the fp32 accumulators in the epilogue.
 // fp32 path: plain LDS-tiled FMA GEMM (64x64 tile, 4x4 per thread).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -31,7 +38,8 @@ namespace gdb {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64, NTHR = 256;
-constexpr int TILE_ELEMS = BM * BK;  // elements of one operand tile
+constexpr int TILE_ELEMS = BM * BK;  // bf16 elements of one operand tile (128-byte rows)
+constexpr int BK8 = 128;             // fp8 codes per K step (the same 128-byte rows)
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -48,34 +56,38 @@ __device__ __forceinline__ bf16x8 bload(__amdgpu_buffer_rsrc_t r, unsigned off) 
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
-// Global -> registers: 8 vectors of 8 bf16 per thread and operand, then
-// registers -> LDS (K-contiguous, swizzled).  The resource is rebased at the
-// tile's first row (K-major) or at (kbeg, first row) (M-major), so offsets
+// Global -> registers: 8 vectors of 16 bytes per thread and operand, then
+// registers -> LDS (K-contiguous, swizzled).  ES is the element size (2: bf16,
+// 1: fp8 codes; fp8 operands are always K-major).  The resource is rebased at
+// the tile's first row (K-major) or at (kbeg, first row) (M-major), so offsets
 // stay far below 4 GiB; rows past the operand's end and k past the split's
 // end read as zero.
-template <bool KMAJ>
+template <bool KMAJ, int ES = 2>
 struct Loader {
-  bf16x8 r[8];
+  static_assert(ES == 2 || KMAJ, "fp8 operands are K-major");
+  static constexpr int VEC = 16 / ES;   // elements per 16-byte vector
+  static constexpr int BKE = 128 / ES;  // elements per K step
+  bf16x8 r[8];        // 16-byte containers
   __amdgpu_buffer_rsrc_t rs;
   unsigned off0;      // byte offset of this thread's first vector at k step 0
   unsigned step;      // bytes to advance per K step
   unsigned rowstep;   // bytes between the thread's consecutive vectors
   int kcol, kend_rel; // K-major: this thread's k within a step; split end (relative)
-  __device__ __forceinline__ void init(const bf16* P, int ld, int rows, int r0, int kbeg, int kend) {
+  __device__ __forceinline__ void init(const void* P, int ld, int rows, int r0, int kbeg, int kend) {
     const int t = threadIdx.x;
     if (KMAJ) {
       const int c = t & 7, rr = t >> 3;
-      const bf16* base = P + (size_t)r0 * ld + kbeg;
-      const size_t bytes = rows > r0 ? ((size_t)(rows - r0) * ld - kbeg) * 2 : 0;
+      const char* base = (const char*)P + ((size_t)r0 * ld + kbeg) * ES;
+      const size_t bytes = rows > r0 ? ((size_t)(rows - r0) * ld - kbeg) * ES : 0;
       rs = make_rsrc(base, bytes);
-      off0 = (unsigned)((rr * ld + c * 8) * 2);
-      step = BK * 2;
-      rowstep = (unsigned)(32 * ld * 2);
-      kcol = c * 8;
+      off0 = (unsigned)((rr * ld + c * VEC) * ES);
+      step = 128;
+      rowstep = (unsigned)(32 * ld * ES);
+      kcol = c * VEC;
       kend_rel = kend - kbeg;
     } else {
       const int mc = t & 31, kb = t >> 5;
-      const bf16* base = P + (size_t)kbeg * ld + r0;
+      const bf16* base = (const bf16*)P + (size_t)kbeg * ld + r0;
       const size_t bytes = (size_t)(kend - kbeg) * ld * 2;
       rs = make_rsrc(base, bytes);
       const bool mvalid = r0 + mc * 8 < rows;
@@ -90,7 +102,7 @@ struct Loader {
     // invalid vectors get an offset >= 0xFFFFFFF0 (past any resource size):
     // an OR with an all-ones mask, so the compiler cannot turn it into a branch
     unsigned bad;
-    if (KMAJ) bad = 0u - (unsigned)(kt * BK + kcol >= kend_rel);
+    if (KMAJ) bad = 0u - (unsigned)(kt * BKE + kcol >= kend_rel);
     else bad = 0u - (unsigned)(off0 == OOB);
     const unsigned o = (off0 + kt * step) | (bad & OOB);
 #pragma unroll
@@ -150,23 +162,50 @@ __device__ __forceinline__ void load_frags(const bf16* As, const bf16* Bs, int k
   }
 }
 
-template <bool AK, bool BK_, int EPI>
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// fp8 fragments of one 64-code k sub-step (kk = 0, 1): lane half lh holds
+// codes 32*lh .. 32*lh+31 of its row, i.e. the two chunks 4kk+2lh, 4kk+2lh+1.
+__device__ __forceinline__ i32x8 frag8(const bf16* S, int row, int ch) {
+  const u32x4 lo = *(const u32x4*)(S + row * BK + ((ch ^ swz(row)) * 8));
+  const u32x4 hi = *(const u32x4*)(S + row * BK + (((ch + 1) ^ swz(row)) * 8));
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+__device__ __forceinline__ void load_frags8(const bf16* As, const bf16* Bs, int kk, int wm, int wn, int lr,
+                                            int lh, i32x8* af, i32x8* bfr) {
+  const int ch = kk * 4 + lh * 2;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) af[i] = frag8(As, wm * 128 + i * 32 + lr, ch);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bfr[j] = frag8(Bs, wn * 128 + j * 32 + lr, ch);
+}
+
+template <typename T> struct V4;
+template <> struct V4<bf16> { typedef bf16x4 t; };
+template <> struct V4<float> { typedef f32x4 t; };
+
+// OT: element type of C, C2 and R in the epilogues other than EPI_F32 (bf16;
+// float for the fp8 products of an fp32 model)
+template <bool AK, bool BK_, int EPI, bool F8 = false, typename OT = bf16>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
+  typedef typename V4<OT>::t OV;
+  constexpr int ES = F8 ? 1 : 2;
+  constexpr int KSTEP = F8 ? BK8 : BK;  // elements per K step
   __shared__ __attribute__((aligned(16))) bf16 smem[2][2][TILE_ELEMS];  // [stage][A|B]
   const int nbm = (p.M + BM - 1) / BM, nbn = (p.N + BN - 1) / BN;
   int tm, tn;
   tile_coords(blockIdx.x, nbm, nbn, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   // split-K range
-  const int ksplit = ((p.K + p.splits * BK - 1) / (p.splits * BK)) * BK;
+  const int ksplit = ((p.K + p.splits * KSTEP - 1) / (p.splits * KSTEP)) * KSTEP;
   const int kbeg = min(p.K, (int)blockIdx.y * ksplit);
   const int kend = min(p.K, kbeg + ksplit);
-  const int nk = (kend - kbeg + BK - 1) / BK;
+  const int nk = (kend - kbeg + KSTEP - 1) / KSTEP;
 
-  Loader<AK> la;
-  Loader<BK_> lb;
-  la.init((const bf16*)p.A, p.lda, p.M, m0, kbeg, kend);
-  lb.init((const bf16*)p.B, p.ldb, p.N, n0, kbeg, kend);
+  Loader<AK, ES> la;
+  Loader<BK_, ES> lb;
+  la.init(p.A, p.lda, p.M, m0, kbeg, kend);
+  lb.init(p.B, p.ldb, p.N, n0, kbeg, kend);
 
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -183,6 +222,40 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
   la.store(smem[0][0]);
   lb.store(smem[0][1]);
   __syncthreads();
+  if constexpr (F8) {
+    i32x8 af[2][4], bfr[2][4];
+    load_frags8(smem[0][0], smem[0][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st = kt & 1;
+      la.load(kt + 1);
+      lb.load(kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16* As = smem[st][0];
+      const bf16* Bs = smem[st][1];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        if (kk == 0) load_frags8(As, Bs, 1, wm, wn, lr, lh, af[1], bfr[1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[kk][j], af[kk][i], acc[i][j], 0, 0, 0, 0,
+                                                                       0, 0);
+        if (kk == 0) {
+          // interleave the second sub-step's 16 LDS reads among the 16 MFMAs
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        }
+      }
+      la.store(smem[st ^ 1][0]);
+      lb.store(smem[st ^ 1][1]);
+      __syncthreads();
+      load_frags8(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
+    }
+  } else {
   bf16x8 af[2][4], bfr[2][4];
   load_frags(smem[0][0], smem[0][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
 
@@ -217,6 +290,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
     __syncthreads();
     load_frags(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
   }
+  }
+  // fp8: both per-tensor scales (amax / 448, the quantiser's float32 values)
+  float oscale = 1.0f;
+  if constexpr (F8) oscale = (p.amax_a[0] / 448.0f) * (p.amax_b[0] / 448.0f);
 
   // Epilogue through LDS, in two passes of 128 rows (the 128 KiB of operand
   // stages hold a [128][256] fp32 half tile).  Pass q: the waves with wm == q
@@ -247,12 +324,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
     const bool cok = c * 4 < ncols;
     constexpr int RPW = 128 / (NTHR / 64);  // rows per wave per pass
     // residual / saved-u operand for all of this wave's rows, loaded up front
-    bf16x4 rv[RPW];
+    OV rv[RPW];
     if (EPI == EPI_RESID || EPI == EPI_DRELU2) {
 #pragma unroll
       for (int k = 0; k < RPW; ++k) {
         const int m = m0 + q * 128 + w + k * (NTHR / 64);
-        rv[k] = (cok && m < p.M) ? *(const bf16x4*)((const bf16*)p.R + (size_t)m * p.ldr + n) : bf16x4{};
+        rv[k] = (cok && m < p.M) ? *(const OV*)((const OT*)p.R + (size_t)m * p.ldr + n) : OV{};
       }
     }
 #pragma unroll
@@ -262,6 +339,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
       if (cok && m < p.M) {
         const f32x4 v4 = *(const f32x4*)(stage + r * 256 + ((c ^ (r & 15)) << 2));
         float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+        if constexpr (F8) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] *= oscale;
+        }
         if (EPI == EPI_F32) {
           float* C = (float*)p.C;
           size_t off = (size_t)m * p.ldc + n;
@@ -274,28 +355,28 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
           }
           *(f32x4*)(C + off) = f32x4{v[0], v[1], v[2], v[3]};
         } else {
-          bf16* C = (bf16*)p.C;
+          OT* C = (OT*)p.C;
           const size_t off = (size_t)m * p.ldc + n;
-          bf16x4 o;
+          OV o;
           if (EPI == EPI_RESID) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = (bf16)(v[e] + (float)rv[k][e]);
+            for (int e = 0; e < 4; ++e) o[e] = (OT)(v[e] + (float)rv[k][e]);
           } else if (EPI == EPI_DRELU2) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = (bf16)(v[e] * 2.0f * fmaxf((float)rv[k][e], 0.f));
+            for (int e = 0; e < 4; ++e) o[e] = (OT)(v[e] * 2.0f * fmaxf((float)rv[k][e], 0.f));
           } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+            for (int e = 0; e < 4; ++e) o[e] = (OT)v[e];
           }
-          *(bf16x4*)(C + off) = o;
+          *(OV*)(C + off) = o;
           if (EPI == EPI_RELU2) {
-            bf16x4 h;
+            OV h;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float rl = fmaxf(v[e], 0.f);
-              h[e] = (bf16)(rl * rl);
+              h[e] = (OT)(rl * rl);
             }
-            *(bf16x4*)((bf16*)p.C2 + off) = h;
+            *(OV*)((OT*)p.C2 + off) = h;
           }
         }
       }
@@ -372,14 +453,19 @@ __global__ __launch_bounds__(256) void gemm_f32_k(GemmArgs p) {
   }
 }
 
-template <bool AK, bool BKM>
+template <bool AK, bool BKM, bool F8 = false, typename OT = bf16>
 hipError_t launch_bf16(const GemmArgs& a, dim3 g, hipStream_t s) {
   switch (a.epi) {
-    case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_STORE>), g, dim3(NTHR), 0, s, a); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_RESID>), g, dim3(NTHR), 0, s, a); break;
-    case EPI_RELU2: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_RELU2>), g, dim3(NTHR), 0, s, a); break;
-    case EPI_DRELU2: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_DRELU2>), g, dim3(NTHR), 0, s, a); break;
-    case EPI_F32: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_F32>), g, dim3(NTHR), 0, s, a); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_STORE, F8, OT>), g, dim3(NTHR), 0, s, a); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_RESID, F8, OT>), g, dim3(NTHR), 0, s, a); break;
+    case EPI_RELU2: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_RELU2, F8, OT>), g, dim3(NTHR), 0, s, a); break;
+    case EPI_DRELU2: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_DRELU2, F8, OT>), g, dim3(NTHR), 0, s, a); break;
+    case EPI_F32:
+      if constexpr (std::is_same<OT, bf16>::value) {
+        hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_F32, F8, OT>), g, dim3(NTHR), 0, s, a);
+        break;
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -389,13 +475,22 @@ hipError_t launch_bf16(const GemmArgs& a, dim3 g, hipStream_t s) {
 
 int gemm_splits(int dt, int M, int N, int K, int epi) {
   if (epi != EPI_F32) return 1;
-  const int tile = dt == BF16 ? BM : FT;
+  const int tile = dt == F32 ? FT : BM;
   const int tiles = ((M + tile - 1) / tile) * ((N + tile - 1) / tile);
-  const int kstep = dt == BF16 ? BK : FK;
+  const int kstep = dt == F32 ? FK : (dt == FP8 ? BK8 : BK);
   int s = 1;
   // aim for >= 2 workgroups per CU on the 256-CU chip, keep >= 8 K steps per split
   while (tiles * s < 512 && (K / (kstep * (s * 2))) >= 8 && s < 32) s *= 2;
   return s;
+}
+
+hipError_t gemm_fp8(int out_dt, const GemmArgs& a, hipStream_t s) {
+  if (a.M == 0 || a.N == 0) return hipSuccess;
+  if (!a.a_kmajor || !a.b_kmajor || !a.amax_a || !a.amax_b) return hipErrorInvalidValue;
+  const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
+  const dim3 g(nbm * nbn, a.splits);
+  if (out_dt == F32 && a.epi != EPI_F32) return launch_bf16<true, true, true, float>(a, g, s);
+  return launch_bf16<true, true, true>(a, g, s);
 }
 
 hipError_t gemm(int dt, const GemmArgs& a, hipStream_t s) {

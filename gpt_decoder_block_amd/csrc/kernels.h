@@ -7,8 +7,9 @@
 
 namespace gdb {
 
-// storage dtype of activations/weights
-enum Dt { F32 = 0, BF16 = 1 };
+// storage dtype of activations/weights; FP8 (OCP e4m3 codes) only names the
+// operand type of the fp8 GEMM
+enum Dt { F32 = 0, BF16 = 1, FP8 = 2 };
 
 inline int dt_size(int dt) { return dt == BF16 ? 2 : 4; }
 
@@ -58,10 +59,27 @@ struct GemmArgs {
   int accumulate;      // EPI_F32
   float* partial;      // EPI_F32 split-K scratch [splits, M, N] or null
   int splits;          // >= 1
+  const float* amax_a; // fp8: per-tensor amax of A and B (scales amax/448)
+  const float* amax_b;
 };
 hipError_t gemm(int dt, const GemmArgs& a, hipStream_t s);
-// split-K factor and partial-buffer size (floats) the GEMM will use for this shape
+// fp8 e4m3 codes, both operands K-major (lda, ldb in codes, multiples of 16);
+// K a multiple of 16.  Epilogues as the bf16 GEMM; C, C2 and R of the
+// epilogues other than EPI_F32 have dtype out_dt (BF16 or F32).
+hipError_t gemm_fp8(int out_dt, const GemmArgs& a, hipStream_t s);
+// split-K factor the GEMM will use for this shape (dt FP8 for gemm_fp8)
 int gemm_splits(int dt, int M, int N, int K, int epi);
+
+// ------------------------------------------------------------ fp8 quantiser
+// amax[0] = max |x| over n elements (x dtype dt; n a multiple of 8); amax is
+// zeroed first (stream-ordered), so one call gives one tensor's amax.
+hipError_t fp8_amax(int dt, const void* x, size_t n, float* amax, hipStream_t s);
+// codes e4m3(x / s), s = amax / 448 (float32 division, round to nearest
+// even, saturating at 448): x [R, Cc] (dt), Cc a multiple of 16; xq [R, Cc]
+// row-major (or null); xqt [Cc, Rp] the transpose with rows R..Rp-1 zero (or
+// null), Rp a multiple of 16 and >= R.
+hipError_t fp8_quant(int dt, const void* x, int R, int Cc, const float* amax, uint8_t* xq, uint8_t* xqt, int Rp,
+                     hipStream_t s);
 
 // ------------------------------------------------------------------ attention
 // q, k, v: rows of qkvh [N, ld] at column offsets 0, H*D, (H+Hkv)*D.

@@ -36,8 +36,9 @@ def _stream(t: torch.Tensor) -> ctypes.c_void_p:
 
 
 def make_cfg(B: int, T: int, C: int, n_head: int, n_kv_head: int, head_dim: int, mlp_hidden: int,
-             window: int, dtype: torch.dtype, eps: float = 1e-6, accumulate_wgrad: bool = False) -> L.BlockCfg:
-    return L.BlockCfg(B, T, C, n_head, n_kv_head, head_dim, mlp_hidden, window, dtype_code(dtype), 0,
+             window: int, dtype: torch.dtype, eps: float = 1e-6, accumulate_wgrad: bool = False,
+             mlp_fp8: bool = False) -> L.BlockCfg:
+    return L.BlockCfg(B, T, C, n_head, n_kv_head, head_dim, mlp_hidden, window, dtype_code(dtype), int(mlp_fp8),
                       int(accumulate_wgrad), eps)
 
 
@@ -191,6 +192,26 @@ def gemm(M: int, N: int, K: int, A: torch.Tensor, a_kmajor: bool, lda: int, B: t
          ws=None) -> None:
     L.call("gdb_gemm", dtype_code(A.dtype), M, N, K, _p(A), int(a_kmajor), lda, _p(B), int(b_kmajor), ldb, epi,
            _p(C), ldc, _opt(R), ldr, _opt(C2), int(accumulate), _opt(ws), _stream(A))
+
+
+def fp8_quantize(x: torch.Tensor, amax: torch.Tensor, xq=None, xqt=None, Rp: int = 0) -> None:
+    """x [R, Cc] -> e4m3 codes (uint8) row-major in xq and/or transposed [Cc, Rp] in xqt; amax fp32 [1]."""
+    R, Cc = x.shape
+    L.call("gdb_fp8_quantize", R, Cc, dtype_code(x.dtype), _p(x), _p(amax), _opt(xq), _opt(xqt), Rp, _stream(x))
+
+
+def gemm_fp8_ws_bytes(M: int, N: int, K: int, epi: int) -> int:
+    s = ctypes.c_size_t()
+    L.call("gdb_gemm_fp8_ws_bytes", M, N, K, epi, ctypes.byref(s))
+    return s.value
+
+
+def gemm_fp8(M: int, N: int, K: int, A: torch.Tensor, lda: int, amax_a: torch.Tensor, B: torch.Tensor, ldb: int,
+             amax_b: torch.Tensor, epi: int, C: torch.Tensor, ldc: int, R=None, ldr: int = 0, C2=None,
+             accumulate: bool = False, ws=None) -> None:
+    out_dt = L.GDB_BF16 if epi == EPI_F32 else dtype_code(C.dtype)
+    L.call("gdb_gemm_fp8", out_dt, M, N, K, _p(A), lda, _p(amax_a), _p(B), ldb, _p(amax_b), epi, _p(C), ldc,
+           _opt(R), ldr, _opt(C2), int(accumulate), _opt(ws), _stream(A))
 
 
 def qk_norm_rope_fwd(B: int, T: int, H: int, Hkv: int, D: int, qkv: torch.Tensor, out: torch.Tensor,

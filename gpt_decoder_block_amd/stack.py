@@ -30,7 +30,7 @@ class DecoderStack:
     def __init__(self, *, n_layer: int, B: int, T: int, C: int, n_head: int, n_kv_head: int, head_dim: int,
                  mlp_hidden: int, vocab: int, windows: Sequence[int], dtype: str, eps: float = 1e-6,
                  rope_base: float = 10000.0, device: str = "cuda:0", extras: bool = False,
-                 ve_gate_channels: int = 32, smear_channels: int = 24):
+                 ve_gate_channels: int = 32, smear_channels: int = 24, mlp_fp8: bool = False):
         if len(windows) != n_layer:
             raise ValueError("one window per layer")
         if extras and n_layer < 2:
@@ -41,8 +41,8 @@ class DecoderStack:
         self.eps = eps
         self.extras = extras
         self.device = torch.device(device)
-        self.cfgs = [ops.make_cfg(B, T, C, n_head, n_kv_head, head_dim, mlp_hidden, w, self.dt, eps)
-                     for w in windows]
+        self.cfgs = [ops.make_cfg(B, T, C, n_head, n_kv_head, head_dim, mlp_hidden, w, self.dt, eps,
+                                  mlp_fp8=mlp_fp8) for w in windows]
         Q, KV = n_head * head_dim, n_kv_head * head_dim
         self.shapes = {"w_qkv": (Q + 2 * KV, C), "w_o": (C, Q), "w_fc": (mlp_hidden, C), "w_proj": (C, mlp_hidden)}
         dev, dt = self.device, self.dt

@@ -79,7 +79,7 @@ typedef struct {
   int32_t mlp_hidden;         /* F, the ReLU² MLP width (4*C in every workload) */
   int32_t window;
   int32_t dtype;              /* gdb_dtype */
-  int32_t mlp_fp8;            /* reserved: must be 0 */
+  int32_t mlp_fp8;            /* the MLP's six products on OCP e4m3 codes (gdb_fp8_quantize) */
   int32_t accumulate_wgrad;   /* 0: dW = ..., 1: dW += ... */
   float eps;
 } gdb_block_cfg;
@@ -271,6 +271,30 @@ gdb_status gdb_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* 
                     int32_t lda, const void* B, int32_t b_kmajor, int32_t ldb, int32_t epi, void* C,
                     int32_t ldc, const void* R, int32_t ldr, void* C2, int32_t accumulate, void* ws,
                     void* stream);
+
+/* fp8 operands ("Comment Entraîner Votre Propre ChatGPT Pour 50€ ?",
+ * section "1. Le modèle GPT": the largest model runs most matrix products in
+ * fp8).  Per-tensor dynamic scaling of x [R, Cc] (dtype):
+ *   amax = max |x| (float32, written to the device scalar *amax),
+ *   s = amax / 448 and code = e4m3(x / s), both float32 operations, round to
+ *   nearest even, saturating at 448 (OCP e4m3fn; amax = 0 gives all-zero codes).
+ * xq [R, Cc] receives the codes row-major, xqt [Cc, Rp] their transpose with
+ * columns R..Rp-1 zero (Rp a multiple of 16, >= R); either may be NULL.
+ * Cc must be a multiple of 16.  With mlp_fp8 the block quantises xn2, h,
+ * w_fc, w_proj and the gradients dx_out and du this way. */
+gdb_status gdb_fp8_quantize(int32_t R, int32_t Cc, int32_t dtype, const void* x, float* amax,
+                            uint8_t* xq, uint8_t* xqt, int32_t Rp, void* stream);
+
+/* GEMM on e4m3 codes, both operands K-contiguous:
+ *   C[m, n] = s_a s_b sum_k A[m*lda + k] B[n*ldb + k],  s = amax / 448 of each operand,
+ * with fp32 accumulation (v_mfma_f32_32x32x64_f8f6f4) and the epilogues of
+ * gdb_gemm: epi 0-3 with C, C2 and R in `dtype`; epi 4 fp32 C (needs
+ * gdb_gemm_fp8_ws_bytes of workspace).  K, lda, ldb multiples of 16. */
+gdb_status gdb_gemm_fp8_ws_bytes(int32_t M, int32_t N, int32_t K, int32_t epi, size_t* ws_bytes);
+gdb_status gdb_gemm_fp8(int32_t dtype, int32_t M, int32_t N, int32_t K, const uint8_t* A, int32_t lda,
+                        const float* amax_a, const uint8_t* B, int32_t ldb, const float* amax_b, int32_t epi,
+                        void* C, int32_t ldc, const void* R, int32_t ldr, void* C2, int32_t accumulate,
+                        void* ws, void* stream);
 
 /* QK RMS-norm + RoPE on rows of qkv [B*T, (H + 2*Hkv)*D] (q heads, k heads, v heads):
  * out rows hold rope(rms_D(q_h)), rope(rms_D(k_g)) and v copied; rinv float32

@@ -1,4 +1,6 @@
 """Helpers of the GPU parity tests (imported by test_gpu_*.py only)."""
+import contextlib
+
 import numpy as np
 import torch
 
@@ -44,3 +46,53 @@ def empty(shape, dt, fill=None):
     if fill is not None:
         t.fill_(fill)
     return t
+
+
+def fp8_bars(pairs: dict, dt: str) -> dict:
+    """Bars for outputs computed through fp8 products.  A code is a discrete
+    decision, so two correct implementations whose quantiser inputs differ by
+    one rounding differ by far more than that rounding: each tensor's bar is
+    twice the oracle's own spread under such a difference (never below the
+    dtype's plain bar).  pairs: name -> (oracle output, list of the oracle's
+    outputs with its quantiser inputs changed as `fp8_alternative` describes);
+    the spread is the largest over that list."""
+    bars = {}
+    for k, (ref, alts) in pairs.items():
+        ref = np.asarray(ref, dtype=np.float64)
+        den = float(np.max(np.abs(ref))) or 1.0
+        spread = max(float(np.max(np.abs(np.asarray(a) - ref))) for a in alts) / den
+        bars[k] = max(TOL[dt], 2.0 * spread)
+    return bars
+
+
+def fp8_alternatives(dt: str):
+    """The changes of the oracle's quantiser inputs that `fp8_bars` samples:
+    one for bf16 (a different rounding), three random ones for f32."""
+    return [0] if dt == "bf16" else [0, 1, 2]
+
+
+@contextlib.contextmanager
+def fp8_alternative(dt: str, seed: int = 0):
+    """The oracle with its quantiser inputs moved by about the rounding error
+    the GPU pipeline carries into them.  bf16: the quantised tensors are not
+    rounded to bfloat16 (float32 inputs instead).  f32: each input is scaled
+    by 1 +- 4e-6 (random signs), the size of the float32 pipeline's own
+    deviation from the oracle (an fp32 GEMM accumulating K ~ 10^3 terms is off
+    by ~sqrt(K) * 2^-24 of its terms' magnitude, several 1e-6 of a small
+    output).  Yields the dtype to give the oracle's cfg."""
+    if dt == "bf16":
+        yield "f32"
+        return
+    from oracle import reference as R
+    orig = R.fp8_quant_dequant
+    rng = np.random.default_rng(seed)
+
+    def moved(x, storage=None):
+        x = np.asarray(x, dtype=np.float64)
+        return orig(x * (1.0 + 4e-6 * rng.choice([-1.0, 1.0], size=x.shape)), storage)
+
+    R.fp8_quant_dequant = moved
+    try:
+        yield dt
+    finally:
+        R.fp8_quant_dequant = orig

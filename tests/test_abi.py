@@ -78,7 +78,7 @@ def test_block_sizes_valid_and_monotone(L):
     (dict(B=0), -1, "positive"),
     (dict(window=-2), -1, "window"),
     (dict(dtype=7), -1, "dtype"),
-    (dict(mlp_fp8=1), -2, "mlp_fp8"),
+    (dict(mlp_fp8=1, mlp_hidden=1032), -1, "multiples of 16"),
     (dict(mlp_hidden=1020), -1, "multiples of 8"),
     (dict(eps=0.0), -1, "eps"),
 ])
@@ -203,3 +203,33 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         _lib.lib()
+
+
+def test_fp8_sizes_and_validation(L):
+    lib = L.lib()
+    st, s0, f0, b0 = _sizes(L, _cfg(L))
+    st8, s1, f1, b1 = _sizes(L, _cfg(L, mlp_fp8=1))
+    assert st == st8 == L.GDB_OK
+    # the fp8 path keeps transposed codes of xn2, h and both weights for the backward
+    N, C, F = 128, 256, 1024
+    assert s1 - s0 >= N * (C + F) + 2 * C * F and f1 > f0 and b1 > b0
+    al = 1 << 20   # never dereferenced: validation fails first
+    assert lib.gdb_fp8_quantize(64, 24, 1, al, al, al, None, 0, None) == L.GDB_EINVAL
+    assert "multiple of 16" in lib.gdb_last_error().decode()
+    assert lib.gdb_fp8_quantize(64, 32, 1, al, al, None, al, 60, None) == L.GDB_EINVAL
+    assert "Rp" in lib.gdb_last_error().decode()
+    assert lib.gdb_fp8_quantize(64, 32, 1, al, al, None, None, 64, None) == L.GDB_EINVAL
+    assert lib.gdb_fp8_quantize(64, 32, 1, al, None, al, None, 0, None) == L.GDB_EINVAL
+    assert lib.gdb_gemm_fp8(1, 64, 64, 40, al, 40, al, al, 40, al, 0, al, 64, None, 0, None, 0, None,
+                            None) == L.GDB_EINVAL
+    assert "multiples of 16" in lib.gdb_last_error().decode()
+    assert lib.gdb_gemm_fp8(1, 64, 64, 64, al, 64, None, al, 64, al, 0, al, 64, None, 0, None, 0, None,
+                            None) == L.GDB_EINVAL
+    assert "amax" in lib.gdb_last_error().decode()
+    assert lib.gdb_gemm_fp8(1, 64, 64, 64, al, 64, al, al, 64, al, 3, al, 64, None, 64, None, 0, None,
+                            None) == L.GDB_EINVAL
+    assert "R is NULL" in lib.gdb_last_error().decode()
+    assert lib.gdb_gemm_fp8(5, 64, 64, 64, al, 64, al, al, 64, al, 0, al, 64, None, 0, None, 0, None,
+                            None) == L.GDB_EINVAL
+    ws = ctypes.c_size_t()
+    assert lib.gdb_gemm_fp8_ws_bytes(1536, 6144, 32768, 4, ctypes.byref(ws)) == L.GDB_OK

@@ -231,3 +231,79 @@ def test_embedding(dt):
     assert_close(dw, O.embed_backward(dx.astype(np.float64), ids, V), "f32", "dwte", tol=1e-6)
     ops.embed_bwd(idg, dev(dx, dt), dw, accumulate=True)
     assert_close(dw, 2 * O.embed_backward(dx.astype(np.float64), ids, V), "f32", "dwte accumulate", tol=1e-6)
+
+
+# ---------------------------------------------------------------------- fp8
+def _e4m3_values(codes: torch.Tensor) -> np.ndarray:
+    """uint8 e4m3fn codes -> float64 values (torch's own e4m3fn decode, on the host)."""
+    return codes.cpu().view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("R,Cc,Rp,scale", [(130, 96, 144, 1.0), (64, 64, 64, 1e-3), (1, 16, 16, 300.0),
+                                            (300, 1664, 304, 1.0)])
+def test_fp8_quantize_codes_exact(R, Cc, Rp, scale):
+    # the codes are integer work: bit-exact against the oracle's float32 decisions
+    print(f"fp8 quantize R={R} Cc={Cc} Rp={Rp}", flush=True)
+    x = rounded(RNG.standard_normal((R, Cc)) * scale, "bf16")
+    x[0, :3] = [0.0, -0.0, x[0, 3]]      # zeros and a repeated value
+    xg = dev(x, "bf16")
+    amax = empty((1,), torch.float32, fill=-5.0)
+    xq = torch.full((R, Cc), 0xAA, dtype=torch.uint8, device=DEV)
+    xqt = torch.full((Cc, Rp), 0xAA, dtype=torch.uint8, device=DEV)
+    ops.fp8_quantize(xg, amax, xq, xqt, Rp)
+    torch.cuda.synchronize()
+    q_ref, s_ref = O.fp8_quantize(x.astype(np.float64))
+    assert float(host(amax)[0]) == float(np.max(np.abs(x)))
+    assert float(host(amax)[0]) / 448.0 == pytest.approx(s_ref, rel=1e-7)
+    np.testing.assert_array_equal(_e4m3_values(xq), q_ref)
+    qt = _e4m3_values(xqt)
+    np.testing.assert_array_equal(qt[:, :R], q_ref.T)
+    assert not np.any(qt[:, R:])
+
+
+def test_fp8_quantize_zero_tensor():
+    x = torch.zeros((32, 32), dtype=torch.bfloat16, device=DEV)
+    amax = empty((1,), torch.float32, fill=3.0)
+    xq = torch.full((32, 32), 7, dtype=torch.uint8, device=DEV)
+    ops.fp8_quantize(x, amax, xq)
+    torch.cuda.synchronize()
+    assert host(amax)[0] == 0.0 and not torch.any(xq).item()
+
+
+@pytest.mark.parametrize("epi", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("M,N,K", [(300, 264, 160), (64, 520, 1664), (2100, 72, 48), (256, 248, 4096)])
+def test_gemm_fp8(epi, M, N, K):
+    # C = q8(A) q8(B)^T with each operand's own per-tensor scale; both sides
+    # quantise the same bf16 inputs, so the codes agree and only the fp32
+    # accumulation order (and the bf16 output) differ
+    print(f"gemm fp8 epi={epi} M={M} N={N} K={K}", flush=True)
+    a = rounded(RNG.standard_normal((M, K)), "bf16")
+    b = rounded(RNG.standard_normal((N, K)) * 0.05, "bf16")
+    r = rounded(RNG.standard_normal((M, N)), "bf16")
+    amax_a, amax_b = empty((1,), torch.float32), empty((1,), torch.float32)
+    aq = torch.empty((M, K), dtype=torch.uint8, device=DEV)
+    bq = torch.empty((N, K), dtype=torch.uint8, device=DEV)
+    ops.fp8_quantize(dev(a, "bf16"), amax_a, aq)
+    ops.fp8_quantize(dev(b, "bf16"), amax_b, bq)
+    acc = O.fp8_quant_dequant(a.astype(np.float64)) @ O.fp8_quant_dequant(b.astype(np.float64)).T
+    rg = dev(r, "bf16")
+    if epi == ops.EPI_F32:
+        C = empty((M, N), torch.float32, fill=0.5)
+        ws = torch.empty(max(ops.gemm_fp8_ws_bytes(M, N, K, epi), 16), dtype=torch.uint8, device=DEV)
+        ops.gemm_fp8(M, N, K, aq, K, amax_a, bq, K, amax_b, epi, C, N, accumulate=True, ws=ws)
+        torch.cuda.synchronize()
+        assert_close(C, acc + 0.5, "f32", "C", tol=1e-3)
+        return
+    C = empty((M, N), "bf16")
+    C2 = empty((M, N), "bf16")
+    ops.gemm_fp8(M, N, K, aq, K, amax_a, bq, K, amax_b, epi, C, N, R=rg, ldr=N, C2=C2)
+    torch.cuda.synchronize()
+    if epi == ops.EPI_STORE:
+        assert_close(C, acc, "bf16", "C")
+    elif epi == ops.EPI_RESID:
+        assert_close(C, acc + r, "bf16", "C")
+    elif epi == ops.EPI_RELU2:
+        assert_close(C, acc, "bf16", "u")
+        assert_close(C2, np.maximum(acc, 0) ** 2, "bf16", "h")
+    else:
+        assert_close(C, acc * 2 * np.maximum(r, 0), "bf16", "du")
