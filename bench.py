@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "train tokens/s on 1 MI355X, d24 stack fwd+bwd; % of bf16 MFMA peak"
 PEAK_BF16 = 2.5e15       # dense bf16 MFMA, FLOP/s
+PEAK_FP8 = 5.0e15        # dense fp8 MFMA, FLOP/s
 PEAK_HBM = 8.0e12        # HBM3E, bytes/s
 
 
@@ -65,6 +66,11 @@ def counter_run(w):
     print(json.dumps({"counter_run": True, "gemm_shape": [N, F, C], "copy_bytes": src.numel() * 4}))
 
 
+def s_el(dt) -> int:
+    import torch
+    return 2 if dt == torch.bfloat16 else 4
+
+
 def ev_time(fn, reps, torch):
     """Average duration (s) of fn() over reps launches, HIP events on the current stream."""
     s = torch.cuda.current_stream()
@@ -99,6 +105,23 @@ def kernel_figures(w, st, reps, torch, ops):
     fl = 2.0 * N * F * C
     out["gemm_mlp_up_relu2"] = {"shape": [N, F, C], "ms": t * 1e3, "tflops": fl / t / 1e12,
                                 "frac_bf16_peak": fl / t / PEAK_BF16, "flops": fl}
+    if w.mlp_fp8:
+        # the same product on e4m3 codes (as the fp8 block runs it), and the
+        # quantiser of the activation (amax pass + codes row-major and transposed)
+        Np = (N + 15) // 16 * 16
+        am = torch.empty(2, dtype=torch.float32, device=dev)
+        Aq, AqT = torch.empty(N, C, dtype=torch.uint8, device=dev), torch.empty(C, Np, dtype=torch.uint8, device=dev)
+        Bq = torch.empty(F, C, dtype=torch.uint8, device=dev)
+        ops.fp8_quantize(B, am[1:], Bq)
+        tq = ev_time(lambda: ops.fp8_quantize(A, am[:1], Aq, AqT, Np), reps, torch)
+        by = N * C * (2.0 * s_el(dt) + 2.0)   # amax read + quantiser read, two code writes
+        out["fp8_quantize_act"] = {"shape": [N, C], "ms": tq * 1e3, "GBps": by / tq / 1e9,
+                                   "frac_hbm_peak": by / tq / PEAK_HBM}
+        t8 = ev_time(lambda: ops.gemm_fp8(N, F, C, Aq, C, am[:1], Bq, C, am[1:], ops.EPI_RELU2, U, F, C2=Hh),
+                     reps, torch)
+        out["gemm_fp8_mlp_up_relu2"] = {"shape": [N, F, C], "ms": t8 * 1e3, "tflops": fl / t8 / 1e12,
+                                        "frac_fp8_peak": fl / t8 / PEAK_FP8, "flops": fl}
+        del Aq, AqT, Bq
     # weight gradient of the MLP down projection (token contraction, fp32 out)
     dW = torch.empty(C, F, dtype=torch.float32, device=dev)
     wsz = ops.gemm_ws_bytes(dt, C, F, N, ops.EPI_F32)
@@ -186,7 +209,7 @@ def cpu_baseline(w, budget_s=40.0):
     """The fp64 oracle on the host cores: one block forward+backward per layer
     kind at B=1, T=w.T, plus the head at N=T tokens; scaled to the whole stack."""
     import oracle as O
-    from seeded_inputs import draw_globals, draw_layer, draw_upstream, to_dtype
+    from seeded_inputs import draw_globals, draw_ids, draw_layer, draw_upstream, to_dtype
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -196,16 +219,20 @@ def cpu_baseline(w, budget_s=40.0):
     cos, sin = O.rope_tables(T, w.head_dim, w.rope_base)
     times = {}
     t_start = time.perf_counter()
-    for l, win in enumerate(w.windows):
-        if win in times:
+    # layer kinds: window, and (with the extras) whether the block has a value embedding
+    kind = lambda l: (w.windows[l], bool(w.extras and l % 2 == 1))
+    ids = draw_ids(w.with_(B=1))[:, :T]
+    for l in range(w.n_layer):
+        if kind(l) in times:
             continue
-        p = {k: to_dtype(v, w.dtype).astype(np.float64) for k, v in draw_layer(w, l).items()}
+        p = {k: np.asarray(to_dtype(v, w.dtype), dtype=np.float64) for k, v in draw_layer(w, l).items()}
         x = draw_upstream(w, 100, (1, T, w.C), 1.0).astype(np.float64)
+        x0 = draw_upstream(w, 150, (1, T, w.C), 1.0).astype(np.float64) if w.extras else None
         dy = draw_upstream(w, 200, (1, T, w.C), 1.0).astype(np.float64)
         t0 = time.perf_counter()
-        out, c = O.block_forward(x, p, w, l, cos, sin)
-        O.block_backward(dy, c, p, w, l, cos, sin)
-        times[win] = time.perf_counter() - t0
+        out, c = O.block_forward(x, p, w, l, cos, sin, x0=x0, ids=ids)
+        O.block_backward(dy, c, p, w, l, cos, sin, ids=ids)
+        times[kind(l)] = time.perf_counter() - t0
     g = draw_globals(w)
     x = draw_upstream(w, 300, (T, w.C), 1.0).astype(np.float64)
     y = np.random.default_rng(0).integers(0, w.vocab, size=T)
@@ -213,7 +240,7 @@ def cpu_baseline(w, budget_s=40.0):
     O.lm_head_ce(x, to_dtype(g["w_lm"], w.dtype).astype(np.float64), y, w.eps)
     O.embed_backward(x, y, w.vocab)
     t_head = time.perf_counter() - t0
-    total = sum(times[win] for win in w.windows) + t_head
+    total = sum(times[kind(l)] for l in range(w.n_layer)) + t_head
     return {"value": T / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"one block fwd+bwd per layer kind ({len(times)} kinds) at B=1, T={T} and the "
                       f"head+embedding at {T} tokens, fp64 numpy; per-step time = sum over the {w.n_layer} "
@@ -236,24 +263,19 @@ def main():
     w = workload(args.workload)
     if args.batch:
         w = w.with_(B=args.batch)
-    if w.extras or w.mlp_fp8:
-        w = w.with_(extras=False, mlp_fp8=False)
     if args.counter_run:
         counter_run(w)
         return
     dev = "cuda:0"
     st = DecoderStack(n_layer=w.n_layer, B=w.B, T=w.T, C=w.C, n_head=w.n_head, n_kv_head=w.n_kv_head,
                       head_dim=w.head_dim, mlp_hidden=w.mlp_hidden, vocab=w.vocab, windows=w.windows,
-                      dtype=w.dtype, eps=w.eps, rope_base=w.rope_base, device=dev)
+                      dtype=w.dtype, eps=w.eps, rope_base=w.rope_base, device=dev, extras=w.extras,
+                      ve_gate_channels=w.ve_gate_channels, smear_channels=w.smear_channels, mlp_fp8=w.mlp_fp8)
     print(f"[bench] {w.name}: L={w.n_layer} B={w.B} T={w.T} C={w.C} H={w.n_head}/{w.n_kv_head} "
-          f"dtype={w.dtype}; drawing weights", file=sys.stderr, flush=True)
-    g = draw_globals(w)
-    st._put(st.wte, to_dtype(g["wte"], w.dtype))
-    st._put(st.w_lm, to_dtype(g["w_lm"], w.dtype))
-    for l in range(w.n_layer):
-        p = draw_layer(w, l)
-        for t, k in zip(st.layers[l], st.shapes):
-            st._put(t, to_dtype(p[k], w.dtype))
+          f"dtype={w.dtype} extras={w.extras} fp8={w.mlp_fp8}; drawing weights", file=sys.stderr, flush=True)
+    rd = lambda v: np.asarray(to_dtype(v, w.dtype)) if np.ndim(v) else np.float32(v)
+    st.load({k: rd(v) for k, v in draw_globals(w).items()},
+            [{k: rd(v) for k, v in draw_layer(w, l).items()} for l in range(w.n_layer)])
     st.set_ids(draw_ids(w))
     torch.cuda.synchronize()
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -284,18 +306,27 @@ def main():
                                       w.T, w.windows)
     tps = tokens / (ms / 1e3)
     tflops = fpt * tps / 1e12
-    dom = kern["gemm_mlp_up_relu2"]
-    roof = {"kernel": "gemm_bf16_k<K-major, K-major, ReLU2 epilogue> (MLP up-projection)",
-            "bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-            "frac": dom["tflops"] / (PEAK_BF16 / 1e12), "traffic": measured_traffic(),
+    if w.mlp_fp8:
+        dom, peak = kern["gemm_fp8_mlp_up_relu2"], PEAK_FP8
+        kname = "gemm_bf16_k<K-major, K-major, ReLU2 epilogue, fp8> (MLP up-projection on e4m3 codes)"
+        traffic = None
+    else:
+        dom, peak = kern["gemm_mlp_up_relu2"], PEAK_BF16
+        kname = "gemm_bf16_k<K-major, K-major, ReLU2 epilogue> (MLP up-projection)"
+        traffic = measured_traffic()
+    roof = {"kernel": kname, "bound": "mfma", "achieved": dom["tflops"], "peak": peak / 1e12, "unit": "TFLOP/s",
+            "frac": dom["tflops"] / (peak / 1e12), "traffic": traffic,
             "algorithmic_per_launch": f"2*M*N*K = {dom['flops']:.4g} FLOP (M={dom['shape'][0]} tokens, "
                                       f"N={dom['shape'][1]}, K={dom['shape'][2]})",
             "avg_launch_ms": dom["ms"]}
     res = {"metric": METRIC, "value": tps, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+           "vs_baseline": None, "dtype": w.dtype + ("; MLP products fp8 e4m3" if w.mlp_fp8 else ""),
+           "data": "synthetic",
            "config": {"workload": f"{w.name}: {w.n_layer} blocks, C={w.C}, heads {w.n_head}/{w.n_kv_head}x"
-                                  f"{w.head_dim}, MLP {w.mlp_hidden}, vocab {w.vocab}",
+                                  f"{w.head_dim}, MLP {w.mlp_hidden}, vocab {w.vocab}"
+                                  + (", residual mixing, value embeddings, smear, backout" if w.extras else "")
+                                  + (", fp8 MLP products" if w.mlp_fp8 else ""),
                       "global_batch": w.B, "seq_len": w.T, "windows": sorted(set(w.windows)),
                       "parallelism": "single GPU"},
            "tflops": tflops, "pct_bf16_peak": 100.0 * tflops * 1e12 / PEAK_BF16,
