@@ -14,8 +14,10 @@
 //     16-byte loads along m at eight consecutive k) and transposed in
 //     registers before the LDS store, so every global access is a coalesced
 //     16-byte load and the MFMA loop never sees the layout;
-//   * two LDS stages: the next K tile is fetched into registers while the MFMAs
-//     run on the current stage, one barrier per K step;
+//   * two LDS stages, one barrier per K step: while the MFMAs run on one stage
+//     the next K tile is copied into the other — straight from memory into LDS
+//     (buffer_load ... lds) when both operands are K-contiguous, through
+//     registers otherwise;
 //   * the MFMA is issued with the B fragment as its first operand, so each lane
 //     ends up holding 4 consecutive n of one output row m (8-byte bf16 or
 //     16-byte fp32 stores);
@@ -131,6 +133,43 @@ struct Loader {
   }
 };
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+#define WAIT_VM0() asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
+
+// K-contiguous operand copied straight from memory into the swizzled LDS
+// layout (no staging registers): in wave instruction q (rows 8q..8q+7) lane L
+// writes LDS bytes 16L of that 1 KiB block, i.e. physical chunk L%8 of row
+// 8q + L/8, so it fetches the logical chunk (L%8) ^ swz(row).
+struct DmaLoader {
+  __amdgpu_buffer_rsrc_t rs;
+  unsigned off[8];
+  int kc[8];
+  int kend_rel;
+  __device__ __forceinline__ void init(const void* P, int ld, int rows, int r0, int kbeg, int kend) {
+    const int t = threadIdx.x, w = t >> 6, L = t & 63;
+    const bf16* base = (const bf16*)P + (size_t)r0 * ld + kbeg;
+    const size_t bytes = rows > r0 ? ((size_t)(rows - r0) * ld - kbeg) * 2 : 0;
+    rs = make_rsrc(base, bytes);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 8 * (i * 4 + w) + (L >> 3);
+      const int c = (L & 7) ^ swz(row);
+      off[i] = (unsigned)((row * ld + c * 8) * 2);
+      kc[i] = c * 8;
+    }
+    kend_rel = kend - kbeg;
+  }
+  __device__ __forceinline__ void load(int kt, bf16* S) {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const unsigned bad = 0u - (unsigned)(kt * BK + kc[i] >= kend_rel);
+      const unsigned o = (off[i] + kt * BK * 2) | (bad & OOB);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(S + (i * 4 + w) * 8 * BK), 16, o, 0, 0, 0);
+    }
+  }
+};
+
 __device__ __forceinline__ void tile_coords(int bid, int nbm, int nbn, int& tm, int& tn) {
   const int total = nbm * nbn;
   const int full = (total / 8) * 8;
@@ -217,6 +256,46 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
+  if constexpr (!F8 && AK && BK_) {
+    // both operands K-contiguous: copies go straight into LDS
+    DmaLoader da, db;
+    da.init(p.A, p.lda, p.M, m0, kbeg, kend);
+    db.init(p.B, p.ldb, p.N, n0, kbeg, kend);
+    da.load(0, smem[0][0]);
+    db.load(0, smem[0][1]);
+    WAIT_VM0();
+    __syncthreads();
+    bf16x8 af[2][4], bfr[2][4];
+    load_frags(smem[0][0], smem[0][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st = kt & 1;
+      da.load(kt + 1, smem[st ^ 1][0]);
+      db.load(kt + 1, smem[st ^ 1][1]);
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16* As = smem[st][0];
+      const bf16* Bs = smem[st][1];
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int cb = kk & 1;
+        if (kk + 1 < BK / 16) load_frags(As, Bs, kk + 1, wm, wn, lr, lh, af[cb ^ 1], bfr[cb ^ 1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
+        if (kk + 1 < BK / 16) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        }
+      }
+      WAIT_VM0();
+      __syncthreads();
+      load_frags(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
+    }
+  } else {
   la.load(0);
   lb.load(0);
   la.store(smem[0][0]);
@@ -289,6 +368,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
     lb.store(smem[st ^ 1][1]);
     __syncthreads();
     load_frags(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
+  }
   }
   }
   // fp8: both per-tensor scales (amax / 448, the quantiser's float32 values)

@@ -443,7 +443,7 @@ def stack_forward_backward(cfg, ids: np.ndarray, glob: Dict[str, np.ndarray],
     e = embed_forward(glob["wte"], inp)
     x0 = None
     if cfg.extras:
-        x, sc = smear_forward(e, glob["smear_gate"], float(glob["smear_lambda"]))
+        x, sc = smear_forward(e, glob["smear_gate"], float(np.ravel(glob["smear_lambda"])[0]))
         x0 = x
     else:
         x = e
@@ -477,7 +477,7 @@ def stack_forward_backward(cfg, ids: np.ndarray, glob: Dict[str, np.ndarray],
         grads["layers"][l] = g
     if cfg.extras:
         dx = dx + dx0
-        de, dws, dlam = smear_backward(dx, e, glob["smear_gate"], float(glob["smear_lambda"]), sc)
+        de, dws, dlam = smear_backward(dx, e, glob["smear_gate"], float(np.ravel(glob["smear_lambda"])[0]), sc)
         grads["smear_gate"] = dws
         grads["smear_lambda"] = dlam
         sum_abs["smear_lambda"] = float(np.sum(np.abs(np.sum(dx * sc["prev"], axis=-1) * sc["sg"])))
