@@ -140,22 +140,25 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // layout (no staging registers): in wave instruction q (rows 8q..8q+7) lane L
 // writes LDS bytes 16L of that 1 KiB block, i.e. physical chunk L%8 of row
 // 8q + L/8, so it fetches the logical chunk (L%8) ^ swz(row).
+template <int ES = 2>
 struct DmaLoader {
+  static constexpr int VEC = 16 / ES;   // elements per 16-byte chunk
+  static constexpr int BKE = 128 / ES;  // elements per K step
   __amdgpu_buffer_rsrc_t rs;
   unsigned off[8];
   int kc[8];
   int kend_rel;
   __device__ __forceinline__ void init(const void* P, int ld, int rows, int r0, int kbeg, int kend) {
     const int t = threadIdx.x, w = t >> 6, L = t & 63;
-    const bf16* base = (const bf16*)P + (size_t)r0 * ld + kbeg;
-    const size_t bytes = rows > r0 ? ((size_t)(rows - r0) * ld - kbeg) * 2 : 0;
+    const char* base = (const char*)P + ((size_t)r0 * ld + kbeg) * ES;
+    const size_t bytes = rows > r0 ? ((size_t)(rows - r0) * ld - kbeg) * ES : 0;
     rs = make_rsrc(base, bytes);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = 8 * (i * 4 + w) + (L >> 3);
       const int c = (L & 7) ^ swz(row);
-      off[i] = (unsigned)((row * ld + c * 8) * 2);
-      kc[i] = c * 8;
+      off[i] = (unsigned)((row * ld + c * VEC) * ES);
+      kc[i] = c * VEC;
     }
     kend_rel = kend - kbeg;
   }
@@ -163,8 +166,8 @@ struct DmaLoader {
     const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const unsigned bad = 0u - (unsigned)(kt * BK + kc[i] >= kend_rel);
-      const unsigned o = (off[i] + kt * BK * 2) | (bad & OOB);
+      const unsigned bad = 0u - (unsigned)(kt * BKE + kc[i] >= kend_rel);
+      const unsigned o = (off[i] + kt * 128) | (bad & OOB);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(S + (i * 4 + w) * 8 * BK), 16, o, 0, 0, 0);
     }
   }
@@ -256,58 +259,21 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  if constexpr (!F8 && AK && BK_) {
-    // both operands K-contiguous: copies go straight into LDS
-    DmaLoader da, db;
+  if constexpr (F8) {
+    // fp8 operands are K-contiguous: both copied straight into LDS
+    DmaLoader<1> da, db;
     da.init(p.A, p.lda, p.M, m0, kbeg, kend);
     db.init(p.B, p.ldb, p.N, n0, kbeg, kend);
     da.load(0, smem[0][0]);
     db.load(0, smem[0][1]);
     WAIT_VM0();
     __syncthreads();
-    bf16x8 af[2][4], bfr[2][4];
-    load_frags(smem[0][0], smem[0][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
-    for (int kt = 0; kt < nk; ++kt) {
-      const int st = kt & 1;
-      da.load(kt + 1, smem[st ^ 1][0]);
-      db.load(kt + 1, smem[st ^ 1][1]);
-      __builtin_amdgcn_sched_barrier(0);
-      const bf16* As = smem[st][0];
-      const bf16* Bs = smem[st][1];
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int cb = kk & 1;
-        if (kk + 1 < BK / 16) load_frags(As, Bs, kk + 1, wm, wn, lr, lh, af[cb ^ 1], bfr[cb ^ 1]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
-        if (kk + 1 < BK / 16) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-        }
-      }
-      WAIT_VM0();
-      __syncthreads();
-      load_frags(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
-    }
-  } else {
-  la.load(0);
-  lb.load(0);
-  la.store(smem[0][0]);
-  lb.store(smem[0][1]);
-  __syncthreads();
-  if constexpr (F8) {
     i32x8 af[2][4], bfr[2][4];
     load_frags8(smem[0][0], smem[0][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
     for (int kt = 0; kt < nk; ++kt) {
       const int st = kt & 1;
-      la.load(kt + 1);
-      lb.load(kt + 1);
+      da.load(kt + 1, smem[st ^ 1][0]);
+      db.load(kt + 1, smem[st ^ 1][1]);
       __builtin_amdgcn_sched_barrier(0);
       const bf16* As = smem[st][0];
       const bf16* Bs = smem[st][1];
@@ -329,12 +295,64 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
           }
         }
       }
-      la.store(smem[st ^ 1][0]);
-      lb.store(smem[st ^ 1][1]);
+      WAIT_VM0();
       __syncthreads();
       load_frags8(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
     }
+  } else if constexpr (AK || BK_) {
+    // K-contiguous operands are copied straight into LDS; an M-contiguous one
+    // goes through registers (transposed on the way)
+    DmaLoader<2> da, db;
+    if constexpr (AK) da.init(p.A, p.lda, p.M, m0, kbeg, kend);
+    if constexpr (BK_) db.init(p.B, p.ldb, p.N, n0, kbeg, kend);
+    auto issue = [&](int kt, int stg) {
+      if constexpr (AK) da.load(kt, smem[stg][0]); else la.load(kt);
+      if constexpr (BK_) db.load(kt, smem[stg][1]); else lb.load(kt);
+    };
+    auto commit = [&](int stg) {
+      if constexpr (!AK) la.store(smem[stg][0]);
+      if constexpr (!BK_) lb.store(smem[stg][1]);
+    };
+    issue(0, 0);
+    commit(0);
+    WAIT_VM0();
+    __syncthreads();
+    bf16x8 af[2][4], bfr[2][4];
+    load_frags(smem[0][0], smem[0][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st = kt & 1;
+      issue(kt + 1, st ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16* As = smem[st][0];
+      const bf16* Bs = smem[st][1];
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int cb = kk & 1;
+        if (kk + 1 < BK / 16) load_frags(As, Bs, kk + 1, wm, wn, lr, lh, af[cb ^ 1], bfr[cb ^ 1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
+        if (kk + 1 < BK / 16) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        }
+      }
+      commit(st ^ 1);
+      WAIT_VM0();
+      __syncthreads();
+      load_frags(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
+    }
   } else {
+  la.load(0);
+  lb.load(0);
+  la.store(smem[0][0]);
+  lb.store(smem[0][1]);
+  __syncthreads();
   bf16x8 af[2][4], bfr[2][4];
   load_frags(smem[0][0], smem[0][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
 
@@ -368,7 +386,6 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
     lb.store(smem[st ^ 1][1]);
     __syncthreads();
     load_frags(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
-  }
   }
   }
   // fp8: both per-tensor scales (amax / 448, the quantiser's float32 values)
