@@ -14,6 +14,9 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgdb.so")
 
+# the GDB_ABI_VERSION this binding's structures and signatures follow
+ABI_VERSION = 2
+
 GDB_OK, GDB_EINVAL, GDB_EUNSUPPORTED, GDB_EHIP, GDB_EWORKSPACE = 0, -1, -2, -3, -4
 GDB_F32, GDB_BF16 = 0, 1
 
@@ -123,6 +126,9 @@ def lib() -> ctypes.CDLL:
             f = getattr(l, name)
             f.restype = res
             f.argtypes = args
+        if l.gdb_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {l.gdb_abi_version()}, the binding expects "
+                               f"{ABI_VERSION}: rebuild it")
         _lib = l
     return _lib
 

@@ -44,7 +44,10 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.lib().gdb_abi_version() == 2
+    # header, library and binding agree
+    hdr = open(HEADER).read()
+    m = re.search(r"#define GDB_ABI_VERSION (\d+)", hdr)
+    assert m and int(m.group(1)) == L.lib().gdb_abi_version() == L.ABI_VERSION
 
 
 def _cfg(L, **kw):
