@@ -134,7 +134,8 @@ void carve_saved(const BlockDims& d, Carver& c, Saved& s) {
   s.amax = c.take<float>(f8 * 4 * 4);
 }
 void carve_fwd(const BlockDims& d, Carver& c, WsFwd& w) {
-  w.qkv = c.take<char>((size_t)d.N * d.W3 * d.s);
+  // raw q, k, v: only the fp32 path (bf16 normalises them in the GEMM epilogue)
+  w.qkv = c.take<char>(d.dt == F32 ? (size_t)d.N * d.W3 * d.s : 0);
   w.x_mid = c.take<char>((size_t)d.N * d.C * d.s);
   w.x_mix = c.take<char>((size_t)d.N * d.C * d.s);
   const size_t f8 = d.fp8 ? 1 : 0, N = d.N;
@@ -327,11 +328,21 @@ gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
     x = wf.x_mix;
   }
   HIPCHK(rmsnorm_fwd(dt, x, sv.xn1, sv.r1, N, d.C, d.eps, s));
-  HIPCHK(gemm(dt, gemm_args(sv.xn1, true, d.C, w->w_qkv, true, d.C, N, d.W3, d.C, EPI_STORE, wf.qkv, d.W3), s));
-  if (xe.ve)
-    HIPCHK(ve_fwd(dt, wf.qkv, d.W3, d.Q + d.KV, sv.xn1, d.C, ex->ids, ex->ve, ex->ve_gate, ex->ve_gate_channels,
-                  d.Hkv, d.D, ex->ve_vocab, sv.ve_s, N, s));
-  HIPCHK(qk_norm_rope_fwd(dt, wf.qkv, sv.qkvh, sv.rqk, rope_tab, d.B, d.T, d.H, d.Hkv, d.D, d.eps, s));
+  if (dt == BF16) {
+    // QKV projection with the QK RMS-norm and RoPE fused into its epilogue
+    GemmArgs gq = gemm_args(sv.xn1, true, d.C, w->w_qkv, true, d.C, N, d.W3, d.C, EPI_QKNORM, sv.qkvh, d.W3);
+    gq.rope = rope_tab; gq.rinv = sv.rqk; gq.T = d.T; gq.qk_heads = d.H + d.Hkv; gq.eps = d.eps;
+    HIPCHK(gemm(dt, gq, s));
+    if (xe.ve)
+      HIPCHK(ve_fwd(dt, sv.qkvh, d.W3, d.Q + d.KV, sv.xn1, d.C, ex->ids, ex->ve, ex->ve_gate,
+                    ex->ve_gate_channels, d.Hkv, d.D, ex->ve_vocab, sv.ve_s, N, s));
+  } else {
+    HIPCHK(gemm(dt, gemm_args(sv.xn1, true, d.C, w->w_qkv, true, d.C, N, d.W3, d.C, EPI_STORE, wf.qkv, d.W3), s));
+    if (xe.ve)
+      HIPCHK(ve_fwd(dt, wf.qkv, d.W3, d.Q + d.KV, sv.xn1, d.C, ex->ids, ex->ve, ex->ve_gate, ex->ve_gate_channels,
+                    d.Hkv, d.D, ex->ve_vocab, sv.ve_s, N, s));
+    HIPCHK(qk_norm_rope_fwd(dt, wf.qkv, sv.qkvh, sv.rqk, rope_tab, d.B, d.T, d.H, d.Hkv, d.D, d.eps, s));
+  }
   AttnArgs at{};
   at.B = d.B; at.T = d.T; at.H = d.H; at.Hkv = d.Hkv; at.D = d.D; at.window = d.window;
   at.qk_normed = 1;  // q^, k^ come out of the QK RMS-norm

@@ -298,18 +298,30 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_k(AttnArgs a, float scal
 // ------------------------------------------------------- backward: delta
 template <typename T_>
 __global__ __launch_bounds__(256) void attn_delta_k(AttnArgs a) {
-  // one wave per (token, head); lanes stride over D
-  const int idx = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  // one wave per token: 16-byte vectors of O and dO, a head's D elements on
+  // G = D/VN consecutive lanes, summed by a butterfly over those lanes
+  constexpr int VN = V16<T_>::n;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
   const int N = a.B * a.T;
-  if (idx >= N * a.H) return;
-  const int n = idx / a.H, h = idx % a.H;
-  const T_* o = (const T_*)a.o + (size_t)n * a.ldo + h * a.D;
-  const T_* d = (const T_*)a.dout + (size_t)n * a.lddo + h * a.D;
-  float s = 0.f;
-  for (int e = l; e < a.D; e += 64) s += to_f(o[e]) * to_f(d[e]);
-  s = wave_sum(s);
+  if (n >= N) return;  // wave-uniform
+  const int G = a.D / VN, nchunk = a.H * G;
+  const T_* o = (const T_*)a.o + (size_t)n * a.ldo;
+  const T_* d = (const T_*)a.dout + (size_t)n * a.lddo;
   const int b = n / a.T, t = n % a.T;
-  if (l == 0) a.delta[((size_t)b * a.H + h) * a.T + t] = s;
+  for (int base = 0; base < nchunk; base += 64) {
+    const int ci = base + l;
+    float s = 0.f;
+    if (ci < nchunk) {
+      float x[VN], y[VN];
+      ld16(o + ci * VN, x);
+      ld16(d + ci * VN, y);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) s += x[e] * y[e];
+    }
+    for (int off = G / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    const int h = ci / G;
+    if (ci < nchunk && (l % G) == 0) a.delta[((size_t)b * a.H + h) * a.T + t] = s;
+  }
 }
 
 // ------------------------------------------------------ backward: dK, dV
@@ -657,7 +669,7 @@ hipError_t attn_fwd(int dt, const AttnArgs& a, hipStream_t s) {
 hipError_t attn_bwd(int dt, const AttnArgs& a, hipStream_t s) {
   if (a.B * a.T == 0) return hipSuccess;
   const float scale = 1.0f / sqrtf((float)a.D);
-  const int rows = a.B * a.T * a.H;
+  const int rows = a.B * a.T;  // one wave per token
   if (dt == BF16) hipLaunchKernelGGL(attn_delta_k<bf16>, dim3((rows + 3) / 4), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(attn_delta_k<float>, dim3((rows + 3) / 4), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();

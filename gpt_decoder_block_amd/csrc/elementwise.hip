@@ -266,40 +266,53 @@ __global__ __launch_bounds__(256) void qk_norm_rope_fwd_k(const T* __restrict__ 
     *(uint4*)(dst + voff + vi * VN) = *(const uint4*)(src + voff + vi * VN);
 }
 
+// Backward, one workgroup per token: thread (head, jq) owns the 4 rotary
+// pairs (j, j + D/2), j = 4jq .. 4jq+3, read as 4-element vectors.
 template <typename T>
 __global__ __launch_bounds__(256) void qk_norm_rope_bwd_k(T* d, const T* __restrict__ qkvh,
                                                            const float* __restrict__ rinv,
                                                            const float* __restrict__ rope, int T_, int H,
                                                            int Hkv, int D) {
+  typedef T T4 __attribute__((ext_vector_type(4)));
   const int row = blockIdx.x;
   const int t = row % T_;
-  const int HD = D / 2;
+  const int HD = D / 2, TPH = HD / 4;  // threads per head
   const int nqk = H + Hkv;
   const int ld = (H + 2 * Hkv) * D;
   T* g = d + (size_t)row * ld;
   const T* y = qkvh + (size_t)row * ld;
-  const int heads_per_pass = 256 / HD;
-  const int hh = threadIdx.x / HD, j = threadIdx.x % HD;
-  const float c = rope[((size_t)t * HD + j) * 2], sn = rope[((size_t)t * HD + j) * 2 + 1];
+  const int heads_per_pass = 256 / TPH;
+  const int hh = threadIdx.x / TPH, jq = threadIdx.x % TPH, j0 = 4 * jq;
+  const f32x4 cs0 = *(const f32x4*)(rope + ((size_t)t * HD + j0) * 2);      // (cos, sin) of j0, j0+1
+  const f32x4 cs1 = *(const f32x4*)(rope + ((size_t)t * HD + j0 + 2) * 2);  // (cos, sin) of j0+2, j0+3
+  const float c[4] = {cs0[0], cs0[2], cs1[0], cs1[2]}, sn[4] = {cs0[1], cs0[3], cs1[1], cs1[3]};
   for (int h0 = 0; h0 < nqk; h0 += heads_per_pass) {
     const int h = h0 + hh;
     const bool act = h < nqk;
-    float ga = 0.f, gb = 0.f, ya = 0.f, yb = 0.f;
+    T4 ga4{}, gb4{}, ya4{}, yb4{};
     if (act) {
-      ga = to_f(g[h * D + j]);
-      gb = to_f(g[h * D + j + HD]);
-      ya = to_f(y[h * D + j]);
-      yb = to_f(y[h * D + j + HD]);
+      ga4 = *(const T4*)(g + h * D + j0);
+      gb4 = *(const T4*)(g + h * D + HD + j0);
+      ya4 = *(const T4*)(y + h * D + j0);
+      yb4 = *(const T4*)(y + h * D + HD + j0);
     }
-    float dot = ga * ya + gb * yb;
-    for (int o = HD / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dot += to_f(ga4[e]) * to_f(ya4[e]) + to_f(gb4[e]) * to_f(yb4[e]);
+    for (int o = TPH / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
     const float m = dot / (float)D;
     if (act) {
       const float r = rinv[(size_t)row * nqk + h];
-      const float ua = ga - ya * m, ub = gb - yb * m;
-      // inverse rotation
-      g[h * D + j] = from_f<T>(r * (ua * c + ub * sn));
-      g[h * D + j + HD] = from_f<T>(r * (-ua * sn + ub * c));
+      T4 oa, ob;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ua = to_f(ga4[e]) - to_f(ya4[e]) * m, ub = to_f(gb4[e]) - to_f(yb4[e]) * m;
+        // inverse rotation
+        oa[e] = from_f<T>(r * (ua * c[e] + ub * sn[e]));
+        ob[e] = from_f<T>(r * (-ua * sn[e] + ub * c[e]));
+      }
+      *(T4*)(g + h * D + j0) = oa;
+      *(T4*)(g + h * D + HD + j0) = ob;
     }
   }
 }

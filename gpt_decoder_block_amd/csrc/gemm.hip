@@ -429,6 +429,68 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
         rv[k] = (cok && m < p.M) ? *(const OV*)((const OT*)p.R + (size_t)m * p.ldr + n) : OV{};
       }
     }
+    if constexpr (EPI == EPI_QKNORM) {
+      // Each half-wave takes one row per iteration; 16 lanes per head, lane
+      // hl owning columns 4hl..4hl+3 and their RoPE partners 64 + 4hl..: the
+      // rotation needs no exchange and the sum of squares is a butterfly
+      // over 16 lanes.  The RoPE table entries are fetched 4 rows ahead.
+      const int half = lane >> 5, hd = (lane >> 4) & 1, hl = lane & 15;
+      const int col = hd * 128 + 4 * hl;                 // tile column of the first value
+      const int head = (n0 >> 7) + hd;
+      const bool hok = hd * 128 < ncols;
+      constexpr int NIT = RPW / 2, RPF = 4;
+      f32x4 csr[RPF][2];
+#pragma unroll
+      for (int k = 0; k < RPF; ++k) {
+        const int m = min(m0 + q * 128 + w + (2 * k + half) * (NTHR / 64), p.M - 1);
+        const float* rp = p.rope + ((size_t)(m % p.T) * 64 + 4 * hl) * 2;
+        csr[k][0] = *(const f32x4*)rp;
+        csr[k][1] = *(const f32x4*)(rp + 4);
+      }
+#pragma unroll
+      for (int k = 0; k < NIT; ++k) {
+        const int r = w + (2 * k + half) * (NTHR / 64);
+        const int m = m0 + q * 128 + r;
+        const f32x4 cs0 = csr[k % RPF][0], cs1 = csr[k % RPF][1];
+        if (k + RPF < NIT) {
+          const int mn = min(m0 + q * 128 + w + (2 * (k + RPF) + half) * (NTHR / 64), p.M - 1);
+          const float* rp = p.rope + ((size_t)(mn % p.T) * 64 + 4 * hl) * 2;
+          csr[k % RPF][0] = *(const f32x4*)rp;
+          csr[k % RPF][1] = *(const f32x4*)(rp + 4);
+        }
+        const int ca = col >> 2, cb = (col + 64) >> 2;    // 16-byte chunks of the two halves
+        const f32x4 a4 = *(const f32x4*)(stage + r * 256 + ((ca ^ (r & 15)) << 2));
+        const f32x4 b4 = *(const f32x4*)(stage + r * 256 + ((cb ^ (r & 15)) << 2));
+        float va[4] = {a4[0], a4[1], a4[2], a4[3]}, vb[4] = {b4[0], b4[1], b4[2], b4[3]};
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += va[e] * va[e] + vb[e] * vb[e];
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+        if (m < p.M && hok) {
+          if (head < p.qk_heads) {
+            const float rr = rsqrtf(ss * (1.0f / 128.0f) + p.eps);
+            const float cc[4] = {cs0[0], cs0[2], cs1[0], cs1[2]}, sn[4] = {cs0[1], cs0[3], cs1[1], cs1[3]};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x = va[e], y = vb[e];
+              va[e] = rr * (x * cc[e] - y * sn[e]);
+              vb[e] = rr * (x * sn[e] + y * cc[e]);
+            }
+            if (hl == 0) p.rinv[(size_t)m * p.qk_heads + head] = rr;
+          }
+          bf16x4 oa, ob;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            oa[e] = (bf16)va[e];
+            ob[e] = (bf16)vb[e];
+          }
+          bf16* crow = (bf16*)p.C + (size_t)m * p.ldc + n0 + col;
+          *(bf16x4*)crow = oa;
+          *(bf16x4*)(crow + 64) = ob;
+        }
+      }
+    } else {
 #pragma unroll
     for (int k = 0; k < RPW; ++k) {
       const int r = w + k * (NTHR / 64);
@@ -477,6 +539,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
           }
         }
       }
+    }
     }
     if (q == 0) __syncthreads();
   }
@@ -557,6 +620,12 @@ hipError_t launch_bf16(const GemmArgs& a, dim3 g, hipStream_t s) {
     case EPI_RESID: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_RESID, F8, OT>), g, dim3(NTHR), 0, s, a); break;
     case EPI_RELU2: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_RELU2, F8, OT>), g, dim3(NTHR), 0, s, a); break;
     case EPI_DRELU2: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_DRELU2, F8, OT>), g, dim3(NTHR), 0, s, a); break;
+    case EPI_QKNORM:
+      if constexpr (AK && BKM && !F8 && std::is_same<OT, bf16>::value) {
+        hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_QKNORM, F8, OT>), g, dim3(NTHR), 0, s, a);
+        break;
+      }
+      return hipErrorInvalidValue;
     case EPI_F32:
       if constexpr (std::is_same<OT, bf16>::value) {
         hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_F32, F8, OT>), g, dim3(NTHR), 0, s, a);

@@ -46,7 +46,10 @@ enum Epi {
   EPI_RESID = 1,   // C = R + acc                   (dtype out, R may alias C)
   EPI_RELU2 = 2,   // C = acc (u), C2 = relu(acc)^2  (dtype out)
   EPI_DRELU2 = 3,  // C = acc * 2*max(R, 0)          (dtype out, R = saved u)
-  EPI_F32 = 4      // fp32 C (+)= acc (split-K through `partial`)
+  EPI_F32 = 4,     // fp32 C (+)= acc (split-K through `partial`)
+  EPI_QKNORM = 5   // bf16, both operands K-major, head_dim 128: the QKV projection
+                   // with the QK RMS-norm and RoPE applied to the q and k heads
+                   // (columns < qk_heads*128) on the way out; rinv [M, qk_heads]
 };
 struct GemmArgs {
   const void* A; const void* B;
@@ -61,6 +64,8 @@ struct GemmArgs {
   int splits;          // >= 1
   const float* amax_a; // fp8: per-tensor amax of A and B (scales amax/448)
   const float* amax_b;
+  // EPI_QKNORM: rope table [T][64][2], row m is position m % T
+  const float* rope; float* rinv; int T; int qk_heads; float eps;
 };
 hipError_t gemm(int dt, const GemmArgs& a, hipStream_t s);
 // fp8 e4m3 codes, both operands K-major (lda, ldb in codes, multiples of 16);
