@@ -37,31 +37,53 @@ namespace gdb {
 namespace {
 
 constexpr int HD = 128;  // head_dim of the MFMA path
+// forward: NW waves of IB 32-query blocks each; two waves per SIMD (NW = 8)
+// let one wave's softmax overlap the other's MFMAs
+#ifndef ATTN_NW
+#define ATTN_NW 8
+#define ATTN_IB 1
+#endif
+#ifndef ATTN_DQ_NW
+#define ATTN_DQ_NW 8
+#endif
+#ifndef ATTN_DKV_NW
+#define ATTN_DKV_NW 8
+#endif
+constexpr int ATTN_FQ = 32 * ATTN_IB * ATTN_NW;  // query rows per forward workgroup
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // Tiles are [64 rows][128] bf16 in LDS, row-major (256 B per row), with the
-// 16-byte chunk index XOR-swizzled by (row & 15).  They are filled by direct
-// global->LDS loads (no staging registers): in each wave instruction, lane L
-// writes the 16 bytes at LDS base + 16L, so lane L fetches the logical chunk
-// that belongs at physical chunk L%16 of row L/16.
-__device__ __forceinline__ int kswz(int row, int chunk) { return chunk ^ (row & 15); }
+// 16-byte chunk index XOR-swizzled by f(row) = 4(row & 3) + ((row >> 2) & 3).
+// f is a bijection on any 16 consecutive aligned rows, so a row-fragment read
+// (16 lanes, 16 rows, one logical chunk) touches 16 distinct chunks; and in a
+// transposed read (32 lanes: 4 rows x 2 adjacent chunk pairs) the row term
+// lands in chunk bits 2-3 while the column term stays in bits 0-1, so those
+// 32 lanes also hit 16 distinct chunks: both are free of bank conflicts.
+// Tiles are filled by direct global->LDS loads (no staging registers): in
+// each wave instruction, lane L writes the 16 bytes at LDS base + 16L, so
+// lane L fetches the logical chunk that belongs at physical chunk L%16 of
+// row L/16.
+__device__ __forceinline__ int kswz(int row, int chunk) { return chunk ^ (((row & 3) << 2) | ((row >> 2) & 3)); }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Issue the 4 direct loads (per wave) of a 64-row tile; rows past nrows are
-// clamped to the last row (finite values that every use masks out).
+// Issue the direct loads of a 64-row tile, 16/NW per wave of an NW-wave
+// workgroup (one load = 4 rows); rows past nrows are clamped to the last row
+// (finite values that every use masks out).
+template <int NW = 4>
 __device__ __forceinline__ void tile_async(const bf16* base, size_t ld, int row0, int nrows, bf16* S) {
+  constexpr int RW = 64 / NW;  // rows per wave
   const int t = threadIdx.x, w = t >> 6, L = t & 63;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = w * 16 + i * 4 + (L >> 4);
+  for (int i = 0; i < RW / 4; ++i) {
+    const int r = w * RW + i * 4 + (L >> 4);
     const int c = kswz(r, L & 15);
     int row = row0 + r;
     row = row < nrows ? row : nrows - 1;
-    __builtin_amdgcn_global_load_lds((const void*)(base + (size_t)row * ld + c * 8), (lds_ptr)(S + (w * 16 + i * 4) * HD),
+    __builtin_amdgcn_global_load_lds((const void*)(base + (size_t)row * ld + c * 8), (lds_ptr)(S + (w * RW + i * 4) * HD),
                                      16, 0, 0);
   }
 }
@@ -102,8 +124,10 @@ __device__ __forceinline__ bf16x8 tr_frag(const bf16* S, int db, int ks, int lan
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// written with non-short-circuit operators so that it compiles to compares
+// and a select, never to a branch per element
 __device__ __forceinline__ bool visible(int i, int j, int T, int W) {
-  return j < T && j <= i && (W < 0 || i - j <= W);
+  return (j < T) & (j <= i) & ((W < 0) | (i - j <= W));
 }
 
 // wait until at most N vector-memory operations of this wave are in flight
@@ -123,14 +147,31 @@ __device__ __forceinline__ bool visible(int i, int j, int T, int W) {
 // online max with rescaling.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Probabilities of one 32-query x 64-key tile for this lane's query, written
-// straight into the bf16 operand registers of the P V^T MFMA (pk[ks] = keys
-// 16ks..16ks+15 in contraction-slot order).  The row sum l accumulates the
-// bf16-rounded weights (v_dot2 with ones), so O is an exact convex
-// combination of V rows whatever the rounding of P.
-template <bool MASK, bool BOUNDED>
-__device__ __forceinline__ void softmax_pack(const f32x16 (&s)[2], bf16x8 (&pk)[4], int qi, int kv0, int lh, int T,
-                                             int W, float scale_log2, float& m, float& l, float& alpha) {
+// Scores the lane may not see become -inf in place, so the exponentials
+// that follow give exactly 0; called on tiles that cross the band's edge
+// only.  Register v of block jb holds the pair (fixed, var0 + 32jb +
+// 8(v>>2) + 4lh + (v&3)), the fixed index being the lane's own query (forward,
+// dQ: var = key) or key (dK/dV: var = query).
+template <bool VAR_IS_KEY, int NB>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[NB], int fixed, int var0, int lh, int T, int W) {
+#pragma unroll
+  for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int x = var0 + jb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+      const bool ok = VAR_IS_KEY ? visible(fixed, x, T, W) : (visible(x, fixed, T, W) & (x < T));
+      s[jb][v] = ok ? s[jb][v] : -INFINITY;
+    }
+}
+
+// Probabilities of one 32-query x 64-key tile for this lane's query (hidden
+// keys already at -inf), written straight into the bf16 operand registers of
+// the P V^T MFMA (pk[ks] = keys 16ks..16ks+15 in contraction-slot order).
+// The row sum l accumulates the bf16-rounded weights (v_dot2 with ones), so
+// O is an exact convex combination of V rows whatever the rounding of P.
+template <bool BOUNDED>
+__device__ __forceinline__ void softmax_pack(const f32x16 (&s)[2], bf16x8 (&pk)[4], float scale_log2, float& m,
+                                             float& l, float& alpha) {
   float msafe;
   if (BOUNDED) {
     msafe = m;
@@ -140,10 +181,7 @@ __device__ __forceinline__ void softmax_pack(const f32x16 (&s)[2], bf16x8 (&pk)[
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int j = kv0 + jb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-        mx = fmaxf(mx, (!MASK || visible(qi, j, T, W)) ? s[jb][v] : -INFINITY);
-      }
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[jb][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     // running max in the log2 domain (scores scaled by scale*log2(e))
     const float mnew = fmaxf(m, mx * scale_log2);
@@ -159,22 +197,19 @@ __device__ __forceinline__ void softmax_pack(const f32x16 (&s)[2], bf16x8 (&pk)[
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int jb = ks >> 1, v = 8 * (ks & 1) + e;
-      float p = __builtin_amdgcn_exp2f(fmaf(s[jb][v], scale_log2, -msafe));
-      if (MASK) {
-        const int j = kv0 + jb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-        if (!visible(qi, j, T, W)) p = 0.f;
-      }
-      out[e] = (bf16)p;
+      out[e] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[jb][v], scale_log2, -msafe));
     }
     pk[ks] = out;
+    typedef bf16x2 bf16x2x4[4];
+    const auto& pairs = *reinterpret_cast<const bf16x2x4*>(&pk[ks]);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{out[2 * q], out[2 * q + 1]}, ones, l, false);
+    for (int q = 0; q < 4; ++q) l = __builtin_amdgcn_fdot2_f32_bf16(pairs[q], ones, l, false);
   }
 }
 
-template <int IB, bool BOUNDED>
-__global__ __launch_bounds__(256, 1) void attn_fwd_bf16_k(AttnArgs a, float scale_log2) {
-  constexpr int FQ = 128 * IB;
+template <int IB, bool BOUNDED, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_k(AttnArgs a, float scale_log2) {
+  constexpr int FQ = 32 * IB * NW;
   __shared__ __attribute__((aligned(16))) bf16 Ks[3][64 * HD];
   __shared__ __attribute__((aligned(16))) bf16 Vs[3][64 * HD];
   const int T = a.T, H = a.H, Hkv = a.Hkv, W = a.window;
@@ -183,7 +218,8 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_k(AttnArgs a, float scal
   const int qb = nqb - 1 - (int)blockIdx.y;
   const int b = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / Hkv);
   const int q0 = qb * FQ;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 31, lh = lane >> 5;
+  const int t = threadIdx.x, lane = t & 63, lr = lane & 31, lh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: tile tests become scalar branches
   const int qw0 = q0 + w * 32 * IB;          // first query of this wave
   const bf16* base = (const bf16*)a.qkv + (size_t)b * T * a.ld;
   const bf16* kbase = base + (H + g) * HD;
@@ -197,11 +233,11 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_k(AttnArgs a, float scal
   const int wq_hi = min(qw0 + 32 * IB - 1, T - 1);
   const int wk_lo = W >= 0 ? max(0, qw0 - W) : 0;
 
-  tile_async(kbase, a.ld, kv_lo, T, Ks[0]);
-  tile_async(vbase, a.ld, kv_lo, T, Vs[0]);
+  tile_async<NW>(kbase, a.ld, kv_lo, T, Ks[0]);
+  tile_async<NW>(vbase, a.ld, kv_lo, T, Vs[0]);
   if (ntile > 1) {
-    tile_async(kbase, a.ld, kv_lo + 64, T, Ks[1]);
-    tile_async(vbase, a.ld, kv_lo + 64, T, Vs[1]);
+    tile_async<NW>(kbase, a.ld, kv_lo + 64, T, Ks[1]);
+    tile_async<NW>(vbase, a.ld, kv_lo + 64, T, Vs[1]);
   }
 
   bf16x8 qf[IB][8];
@@ -229,8 +265,8 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_k(AttnArgs a, float scal
     const bool ahead = it + 2 < ntile;
     if (ahead) {
       const int sn = (it + 2) % 3;
-      tile_async(kbase, a.ld, kv0 + 128, T, Ks[sn]);
-      tile_async(vbase, a.ld, kv0 + 128, T, Vs[sn]);
+      tile_async<NW>(kbase, a.ld, kv0 + 128, T, Ks[sn]);
+      tile_async<NW>(vbase, a.ld, kv0 + 128, T, Vs[sn]);
     }
     // wave-uniform: does the tile touch this wave's rows, and is it fully visible?
     const bool any = qw0 < T && kv0 <= wq_hi && kv0 + 63 >= wk_lo;
@@ -253,8 +289,8 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_k(AttnArgs a, float scal
       for (int ib = 0; ib < IB; ++ib) {
         const int qi = qw0 + ib * 32 + lr;
         float alpha;
-        if (full) softmax_pack<false, BOUNDED>(s[ib], pk[ib], qi, kv0, lh, T, W, scale_log2, m[ib], l[ib], alpha);
-        else softmax_pack<true, BOUNDED>(s[ib], pk[ib], qi, kv0, lh, T, W, scale_log2, m[ib], l[ib], alpha);
+        if (!full) mask_tile<true>(s[ib], qi, kv0, lh, T, W);
+        softmax_pack<BOUNDED>(s[ib], pk[ib], scale_log2, m[ib], l[ib], alpha);
         if (!BOUNDED && __any(alpha != 1.0f)) {
 #pragma unroll
           for (int db = 0; db < 4; ++db) o[ib][db] *= alpha;
@@ -270,8 +306,12 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_k(AttnArgs a, float scal
         }
       }
     }
-    if (ahead) WAIT_VM(8);  // tile it+1 landed; tile it+2 may still be in flight
-    else WAIT_VM(0);
+    if (ahead) {  // tile it+1 landed; tile it+2 may still be in flight
+      if constexpr (NW == 8) WAIT_VM(4);
+      else WAIT_VM(8);
+    } else {
+      WAIT_VM(0);
+    }
     __syncthreads();
   }
 
@@ -325,50 +365,57 @@ __global__ __launch_bounds__(256) void attn_delta_k(AttnArgs a) {
 }
 
 // ------------------------------------------------------ backward: dK, dV
-// Workgroup: 128 keys of one (b, kv head), 32 per wave (lane = key).  Loops
-// over the query heads of the group and the visible 64-row query tiles; Q,
-// dO (row-major) and the tile's log-sum-exp and delta stream through 3 LDS
-// stages.  dV^T += dO^T P and dK^T += Q^T dS accumulate in registers, with
-// the transposed operands read by the LDS transpose load.
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkv_bf16_k(AttnArgs a, float scale_log2, float scale) {
-  __shared__ __attribute__((aligned(16))) bf16 Qs[3][64 * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Ds[3][64 * HD];
-  __shared__ __attribute__((aligned(16))) float Ls[3][4][64];  // [stage][lse, delta, spare, spare][row]
+// Workgroup: 32*NW keys of one (b, kv head), 32 per wave (lane = key); with
+// NW = 8 two waves share each SIMD, so one wave's exp/convert work overlaps
+// the other's MFMAs.  The workgroup's V rows sit in LDS for the whole kernel
+// (the wave's K rows stay in registers).  Loops over the query heads of the
+// group and the visible 64-row query tiles; Q, dO (row-major) and the tile's
+// log-sum-exp and delta stream through 2 LDS stages, the next tile's loads
+// in flight during the current tile.  Each tile is taken as two 32-query
+// halves, so only one half's S and dP are live at a time: dV^T += dO^T P and
+// dK^T += Q^T dS accumulate in registers, with the transposed operands read
+// by the LDS transpose load.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_bf16_k(AttnArgs a, float scale_log2, float scale) {
+  constexpr int FK = 32 * NW;
+  __shared__ __attribute__((aligned(16))) bf16 Vs[FK * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Qs[2][64 * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Ds[2][64 * HD];
+  __shared__ __attribute__((aligned(16))) float Ls[2][NW][64];  // [stage][wave: lse (even), delta (odd)][row]
   const int T = a.T, H = a.H, Hkv = a.Hkv, W = a.window, G = H / Hkv;
-  const int b = blockIdx.x / Hkv, g = blockIdx.x % Hkv;   // grid (B*Hkv, key blocks), heaviest first
-  const int kv0 = blockIdx.y * 128;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 31, lh = lane >> 5;
+  const int b = blockIdx.x / Hkv, g = blockIdx.x % Hkv;   // grid (B*Hkv, key blocks)
+  const int kv0 = blockIdx.y * FK;
+  const int t = threadIdx.x, lane = t & 63, lr = lane & 31, lh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: tile tests become scalar branches
   const int kj = kv0 + w * 32 + lr;  // this lane's key
   const bf16* base = (const bf16*)a.qkv + (size_t)b * T * a.ld;
   const bf16* dbase = (const bf16*)a.dout + (size_t)b * T * a.lddo;
 
   const int q_lo = kv0;  // multiple of 64
-  const int q_hi = W >= 0 ? min(T, kv0 + 128 + W) : T;
+  const int q_hi = W >= 0 ? min(T, kv0 + FK + W) : T;
   const int nqt = q_hi > q_lo ? (q_hi - q_lo + 63) / 64 : 0;
   const int total = nqt * G;
   // wave's keys
   const int wk0 = kv0 + w * 32, wk_hi = min(wk0 + 31, T - 1);
 
+  // every wave issues the same number of loads per tile (2 x 16/NW + 1)
   auto issue = [&](int it, int stg) {
     const int hh = g * G + it / nqt;
     const int i0 = q_lo + (it % nqt) * 64;
-    tile_async(base + hh * HD, a.ld, i0, T, Qs[stg]);
-    tile_async(dbase + hh * HD, a.lddo, i0, T, Ds[stg]);
+    tile_async<NW>(base + hh * HD, a.ld, i0, T, Qs[stg]);
+    tile_async<NW>(dbase + hh * HD, a.lddo, i0, T, Ds[stg]);
     const size_t lo = ((size_t)b * H + hh) * T;
     vec64_async((w & 1) ? a.delta + lo : a.lse + lo, i0, T, Ls[stg][w]);
   };
+#pragma unroll
+  for (int r = 0; r < FK; r += 64) tile_async<NW>(base + (H + Hkv + g) * HD, a.ld, kv0 + r, T, Vs + r * HD);
   if (total > 0) issue(0, 0);
-  if (total > 1) issue(1, 1);
 
-  bf16x8 kf[8], vf[8];
+  bf16x8 kf[8];
   {
     const int kc = min(kj, T - 1);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const size_t roff = (size_t)kc * a.ld + kk * 16 + lh * 8;
-      kf[kk] = *(const bf16x8*)(base + roff + (H + g) * HD);
-      vf[kk] = *(const bf16x8*)(base + roff + (H + Hkv + g) * HD);
-    }
+    for (int kk = 0; kk < 8; ++kk) kf[kk] = *(const bf16x8*)(base + (size_t)kc * a.ld + (H + g) * HD + kk * 16 + lh * 8);
   }
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -377,57 +424,60 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_bf16_k(AttnArgs a, float 
   __syncthreads();
 
   for (int it = 0; it < total; ++it) {
-    const int st = it % 3;
+    const int st = it & 1;
     const int i0 = q_lo + (it % nqt) * 64;
-    const bool ahead = it + 2 < total;
-    if (ahead) issue(it + 2, (it + 2) % 3);
+    // the other stage was last read in iteration it-1, which every wave has left
+    if (it + 1 < total) issue(it + 1, st ^ 1);
     // wave-uniform visibility of this query tile for the wave's 32 keys
     const int iq_hi = min(i0 + 63, T - 1);
     const bool any = wk0 < T && i0 + 63 >= wk0 && (W < 0 || i0 - wk_hi <= W);
     if (any) {
       const bool full = i0 >= wk_hi && iq_hi < T && (W < 0 || iq_hi - wk0 <= W) && i0 + 63 < T;
-      // S[i][j] and dP[i][j]: lane = key j, registers = queries
-      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
+      for (int ib = 0; ib < 2; ++ib) {
+        // S[i][j] and dP[i][j] of query rows 32ib..32ib+31: lane = key j, registers = queries
+        f32x16 sv = f32x16{}, dpv = f32x16{};
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-          s[ib] = mfma32(row_frag(Qs[st], ib, kk, lr, lh), kf[kk], s[ib]);
-          dp[ib] = mfma32(row_frag(Ds[st], ib, kk, lr, lh), vf[kk], dp[ib]);
+        for (int kk = 0; kk < 8; ++kk) {
+          sv = mfma32(row_frag(Qs[st], ib, kk, lr, lh), kf[kk], sv);
+          dpv = mfma32(row_frag(Ds[st], ib, kk, lr, lh), row_frag(Vs, w, kk, lr, lh), dpv);
         }
-      }
-      // P and dS straight into bf16 operand registers (slot order of tr_frag)
-      bf16x8 pf[4], sf[4];
+        if (!full) {
+          f32x16 sm[1] = {sv};
+          mask_tile<false>(sm, kj, i0 + ib * 32, lh, T, W);
+          sv = sm[0];
+        }
+        // P and dS straight into bf16 operand registers (slot order of tr_frag)
+        bf16x8 pf[2], sf[2];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int ib = ks >> 1;
+        for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
-        for (int hq = 0; hq < 2; ++hq) {
-          const int gq = 2 * (ks & 1) + hq;
-          const int il = ib * 32 + 8 * gq + 4 * lh;
-          const f32x4 L4 = *(const f32x4*)(&Ls[st][0][il]);
-          const f32x4 D4 = *(const f32x4*)(&Ls[st][1][il]);
+          for (int hq = 0; hq < 2; ++hq) {
+            const int gq = 2 * k2 + hq;
+            const int il = ib * 32 + 8 * gq + 4 * lh;
+            const f32x4 L4 = *(const f32x4*)(&Ls[st][0][il]);
+            const f32x4 D4 = *(const f32x4*)(&Ls[st][1][il]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int v = 4 * gq + r;
-            float p = __builtin_amdgcn_exp2f(fmaf(s[ib][v], scale_log2, -L4[r] * 1.4426950408889634f));
-            if (!full && !(visible(i0 + il + r, kj, T, W) && i0 + il + r < T)) p = 0.f;
-            pf[ks][4 * hq + r] = (bf16)p;
-            sf[ks][4 * hq + r] = (bf16)(p * (dp[ib][v] - D4[r]));
+            for (int r = 0; r < 4; ++r) {
+              const int v = 4 * gq + r;
+              const float p = __builtin_amdgcn_exp2f(fmaf(sv[v], scale_log2, -L4[r] * 1.4426950408889634f));
+              pf[k2][4 * hq + r] = (bf16)p;
+              sf[k2][4 * hq + r] = (bf16)(p * (dpv[v] - D4[r]));
+            }
+          }
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int ks = 2 * ib + k2;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            dv[db] = mfma32(tr_frag(Ds[st], db, ks, lane), pf[k2], dv[db]);
+            dk[db] = mfma32(tr_frag(Qs[st], db, ks, lane), sf[k2], dk[db]);
           }
         }
       }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          dv[db] = mfma32(tr_frag(Ds[st], db, ks, lane), pf[ks], dv[db]);
-          dk[db] = mfma32(tr_frag(Qs[st], db, ks, lane), sf[ks], dk[db]);
-        }
-      }
     }
-    if (ahead) WAIT_VM(9);
-    else WAIT_VM(0);
+    WAIT_VM(0);  // tile it+1 has landed
     __syncthreads();
   }
 
@@ -451,15 +501,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_bf16_k(AttnArgs a, float 
 // Workgroup: 128 query rows of one (b, h), 32 per wave (lane = query).  K and
 // V tiles of 64 keys stream through 3 LDS stages; dQ^T += K^T dS^T with K^T
 // read by the LDS transpose load.
-__global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_k(AttnArgs a, float scale_log2, float scale) {
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_k(AttnArgs a, float scale_log2, float scale) {
+  constexpr int FQ = 32 * NW;
   __shared__ __attribute__((aligned(16))) bf16 Ks[3][64 * HD];
   __shared__ __attribute__((aligned(16))) bf16 Vs[3][64 * HD];
   const int T = a.T, H = a.H, Hkv = a.Hkv, W = a.window;
-  const int nqb = (T + 127) / 128;
+  const int nqb = (T + FQ - 1) / FQ;
   const int qb = nqb - 1 - (int)blockIdx.y;   // grid (B*H, query blocks), heaviest first
   const int b = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / Hkv);
-  const int q0 = qb * 128;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 31, lh = lane >> 5;
+  const int q0 = qb * FQ;
+  const int t = threadIdx.x, lane = t & 63, lr = lane & 31, lh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: tile tests become scalar branches
   const int qi = q0 + w * 32 + lr;
   const int qw0 = q0 + w * 32, wq_hi = min(qw0 + 31, T - 1);
   const int wk_lo = W >= 0 ? max(0, qw0 - W) : 0;
@@ -469,14 +522,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_k(AttnArgs a, float s
 
   int kv_lo = W >= 0 ? max(0, q0 - W) : 0;
   kv_lo &= ~63;
-  const int kv_hi = min(T, q0 + 128);
+  const int kv_hi = min(T, q0 + FQ);
   const int ntile = (kv_hi - kv_lo + 63) / 64;
 
-  tile_async(kbase, a.ld, kv_lo, T, Ks[0]);
-  tile_async(vbase, a.ld, kv_lo, T, Vs[0]);
+  tile_async<NW>(kbase, a.ld, kv_lo, T, Ks[0]);
+  tile_async<NW>(vbase, a.ld, kv_lo, T, Vs[0]);
   if (ntile > 1) {
-    tile_async(kbase, a.ld, kv_lo + 64, T, Ks[1]);
-    tile_async(vbase, a.ld, kv_lo + 64, T, Vs[1]);
+    tile_async<NW>(kbase, a.ld, kv_lo + 64, T, Ks[1]);
+    tile_async<NW>(vbase, a.ld, kv_lo + 64, T, Vs[1]);
   }
   bf16x8 qf[8], df[8];
   const int qc = min(qi, T - 1);
@@ -501,8 +554,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_k(AttnArgs a, float s
     const bool ahead = it + 2 < ntile;
     if (ahead) {
       const int sn = (it + 2) % 3;
-      tile_async(kbase, a.ld, kv0 + 128, T, Ks[sn]);
-      tile_async(vbase, a.ld, kv0 + 128, T, Vs[sn]);
+      tile_async<NW>(kbase, a.ld, kv0 + 128, T, Ks[sn]);
+      tile_async<NW>(vbase, a.ld, kv0 + 128, T, Vs[sn]);
     }
     const bool any = qw0 < T && kv0 <= wq_hi && kv0 + 63 >= wk_lo;
     if (any) {
@@ -516,6 +569,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_k(AttnArgs a, float s
           dp[jb] = mfma32(row_frag(Vs[st], jb, kk, lr, lh), df[kk], dp[jb]);
         }
       }
+      if (!full) mask_tile<true>(s, qi, kv0, lh, T, W);
       bf16x8 sf[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -523,11 +577,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_k(AttnArgs a, float s
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int v = 8 * (ks & 1) + e;
-          float p = __builtin_amdgcn_exp2f(fmaf(s[jb][v], scale_log2, -lse2));
-          if (!full) {
-            const int j = kv0 + jb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-            if (!visible(qi, j, T, W)) p = 0.f;
-          }
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[jb][v], scale_log2, -lse2));
           sf[ks][e] = (bf16)(p * (dp[jb][v] - dlt));
         }
       }
@@ -537,8 +587,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_k(AttnArgs a, float s
         for (int db = 0; db < 4; ++db) dq[db] = mfma32(tr_frag(Ks[st], db, ks, lane), sf[ks], dq[db]);
       }
     }
-    if (ahead) WAIT_VM(8);
-    else WAIT_VM(0);
+    if (ahead) {
+      if constexpr (NW == 8) WAIT_VM(4);
+      else WAIT_VM(8);
+    } else {
+      WAIT_VM(0);
+    }
     __syncthreads();
   }
   if (qi < T) {
@@ -652,11 +706,12 @@ hipError_t attn_fwd(int dt, const AttnArgs& a, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)a.D);
   if (dt == BF16) {
     if (a.qk_normed) {
-      dim3 g(a.B * a.H, (a.T + 255) / 256);
-      hipLaunchKernelGGL((attn_fwd_bf16_k<2, true>), g, dim3(256), 0, s, a, scale * 1.4426950408889634f);
+      dim3 g(a.B * a.H, (a.T + ATTN_FQ - 1) / ATTN_FQ);
+      hipLaunchKernelGGL((attn_fwd_bf16_k<ATTN_IB, true, ATTN_NW>), g, dim3(64 * ATTN_NW), 0, s, a,
+                         scale * 1.4426950408889634f);
     } else {
       dim3 g(a.B * a.H, (a.T + 127) / 128);
-      hipLaunchKernelGGL((attn_fwd_bf16_k<1, false>), g, dim3(256), 0, s, a, scale * 1.4426950408889634f);
+      hipLaunchKernelGGL((attn_fwd_bf16_k<1, false, 4>), g, dim3(256), 0, s, a, scale * 1.4426950408889634f);
     }
   } else {
     dim3 g((a.B * a.H * a.T + 63) / 64);
@@ -675,11 +730,12 @@ hipError_t attn_bwd(int dt, const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (dt == BF16) {
-    hipLaunchKernelGGL(attn_bwd_dkv_bf16_k, dim3(a.B * a.Hkv, (a.T + 127) / 128), dim3(256), 0, s, a,
-                       scale * 1.4426950408889634f, scale);
+    hipLaunchKernelGGL(attn_bwd_dkv_bf16_k<ATTN_DKV_NW>, dim3(a.B * a.Hkv, (a.T + 32 * ATTN_DKV_NW - 1) / (32 * ATTN_DKV_NW)),
+                       dim3(64 * ATTN_DKV_NW), 0, s, a, scale * 1.4426950408889634f, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_bwd_dq_bf16_k, dim3(a.B * a.H, (a.T + 127) / 128), dim3(256), 0, s, a,
+    hipLaunchKernelGGL(attn_bwd_dq_bf16_k<ATTN_DQ_NW>, dim3(a.B * a.H, (a.T + 32 * ATTN_DQ_NW - 1) / (32 * ATTN_DQ_NW)),
+                       dim3(64 * ATTN_DQ_NW), 0, s, a,
                        scale * 1.4426950408889634f, scale);
   } else {
     dim3 gq((a.B * a.H * a.T + 63) / 64), gk((a.B * a.Hkv * a.T + 63) / 64);

@@ -179,22 +179,19 @@ __global__ __launch_bounds__(256) void embed_fwd_k(const int32_t* __restrict__ i
   for (int vi = l; vi < C / VN; vi += 64) *(uint4*)(dst + vi * VN) = *(const uint4*)(src + vi * VN);
 }
 
+// One wave per token; lane l adds columns l, l+64, ... so each atomic
+// instruction covers 256 contiguous bytes of the dWte row.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_bwd_k(const int32_t* __restrict__ ids, const T* __restrict__ dx,
                                                     float* __restrict__ dwte, int N, int C, int V) {
-  constexpr int VN = V16<T>::n;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
   if (row >= N) return;
   int id = ids[row];
   id = id < 0 ? 0 : (id >= V ? V - 1 : id);
   float* dst = dwte + (size_t)id * C;
   const T* src = dx + (size_t)row * C;
-  for (int vi = l; vi < C / VN; vi += 64) {
-    float v[VN];
-    ld16(src + vi * VN, v);
-#pragma unroll
-    for (int e = 0; e < VN; ++e) unsafeAtomicAdd(dst + vi * VN + e, v[e]);
-  }
+#pragma unroll 4
+  for (int c = l; c < C; c += 64) unsafeAtomicAdd(dst + c, to_f(src[c]));
 }
 
 hipError_t embed_fwd(int dt, const int32_t* ids, const void* wte, void* x, int N, int C, int V, hipStream_t s) {

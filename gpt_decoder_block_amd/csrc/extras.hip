@@ -160,14 +160,14 @@ __global__ __launch_bounds__(256) void ve_fwd_k(T* qkv, int ldq, int voff, const
 // gradient to v unchanged):
 //   dgate_g = dv[n,g,:] . VE[id,g,:];  ds[n,g] = dgate_g * 3*sig(s)*(1 - sig(s));
 //   dVE[id,g,:] += gate_g * dv[n,g,:]  (fp32 atomics: ids repeat).
-// A head's D elements span G = D/VN consecutive lanes of one pass, so dgate_g
-// is a butterfly over those G lanes.
+// Lane l takes columns l, l+64, ... of each head, so one atomic instruction
+// covers 256 contiguous bytes (two cache lines) of the dVE row; dgate_g is a
+// butterfly over the wave.
 template <typename T>
 __global__ __launch_bounds__(256) void ve_bwd_k(const T* __restrict__ dqkv, int ldq, int voff,
                                                  const int32_t* __restrict__ ids, const T* __restrict__ ve,
                                                  const float* __restrict__ s_save, int Hkv, int D, int V,
                                                  float* __restrict__ ds, float* __restrict__ dve, int N) {
-  constexpr int VN = V16<T>::n;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int n = blockIdx.x * 4 + w;
   if (n >= N) return;  // wave-uniform
@@ -178,28 +178,19 @@ __global__ __launch_bounds__(256) void ve_bwd_k(const T* __restrict__ dqkv, int 
   const T* dv = dqkv + (size_t)n * ldq + voff;
   const T* erow = ve + (size_t)id * Hkv * D;
   float* drow = dve + (size_t)id * Hkv * D;
-  const int G = D / VN, hpp = 64 / G;  // lanes per head, heads per pass
-  const int nchunk = Hkv * G;
   float dg_mine = 0.f;
-  for (int base = 0; base < nchunk; base += 64) {
-    const int ci = base + l;
-    const float gate = __shfl(gate_mine, min(ci / G, Hkv - 1), 64);
+  for (int h = 0; h < Hkv; ++h) {
+    const float gate = __shfl(gate_mine, h, 64);
     float p = 0.f;
-    if (ci < nchunk) {
-      float g[VN], e[VN];
-      ld16(dv + ci * VN, g);
-      ld16(erow + ci * VN, e);
-#pragma unroll
-      for (int q = 0; q < VN; ++q) {
-        p += g[q] * e[q];
-        unsafeAtomicAdd(drow + ci * VN + q, gate * g[q]);
-      }
+#pragma unroll 2
+    for (int c = h * D + l; c < (h + 1) * D; c += 64) {
+      const float g = to_f(dv[c]);
+      p += g * to_f(erow[c]);
+      unsafeAtomicAdd(drow + c, gate * g);
     }
-    for (int o = G / 2; o > 0; o >>= 1) p += __shfl_xor(p, o, 64);
-    // every lane of head group j now holds the sum of head base/G + j; lane base/G + j keeps it
-    const int j = l - base / G;
-    const float v = __shfl(p, min(max(j, 0), hpp - 1) * G, 64);
-    if (j >= 0 && j < hpp) dg_mine += v;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) p += __shfl_xor(p, o, 64);
+    if (l == h) dg_mine = p;
   }
   if (l < Hkv) ds[(size_t)n * Hkv + l] = dg_mine * 3.0f * sg_mine * (1.0f - sg_mine);
 }
