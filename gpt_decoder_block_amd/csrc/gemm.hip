@@ -639,15 +639,49 @@ hipError_t launch_bf16(const GemmArgs& a, dim3 g, hipStream_t s) {
 
 }  // namespace
 
+namespace {
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cus[dev];
+}
+}  // namespace
+
 int gemm_splits(int dt, int M, int N, int K, int epi) {
   if (epi != EPI_F32) return 1;
   const int tile = dt == F32 ? FT : BM;
   const int tiles = ((M + tile - 1) / tile) * ((N + tile - 1) / tile);
   const int kstep = dt == F32 ? FK : (dt == FP8 ? BK8 : BK);
-  int s = 1;
-  // aim for >= 2 workgroups per CU on the 256-CU chip, keep >= 8 K steps per split
-  while (tiles * s < 512 && (K / (kstep * (s * 2))) >= 8 && s < 32) s *= 2;
-  return s;
+  if (dt == F32) {
+    int s = 1;
+    // aim for >= 2 workgroups per CU, keep >= 8 K steps per split
+    while (tiles * s < 512 && (K / (kstep * (s * 2))) >= 8 && s < 32) s *= 2;
+    return s;
+  }
+  // MFMA path (one workgroup per CU): pick the split count with the least
+  // modelled time, in units of one workgroup K step: the rounds of
+  // workgroups the CUs run times each one's K steps, plus the split partials'
+  // store and reduction (about 0.066 step per 256x256 fp32 tile).  Keeps at
+  // least 4 K steps per split.
+  const int cus = device_cus();
+  const int nsteps = (K + kstep - 1) / kstep;
+  int best = 1;
+  double bt = 1e300;
+  for (int sp = 1; sp <= 32; ++sp) {
+    if (sp > 1 && nsteps / sp < 4) break;
+    const double rounds = (double)((tiles * sp + cus - 1) / cus);
+    const double t = rounds * ((nsteps + sp - 1) / sp) + (sp > 1 ? 0.066 * tiles * sp : 0.0);
+    if (t < bt - 1e-9) {
+      bt = t;
+      best = sp;
+    }
+  }
+  return best;
 }
 
 hipError_t gemm_fp8(int out_dt, const GemmArgs& a, hipStream_t s) {
