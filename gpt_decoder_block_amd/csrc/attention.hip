@@ -32,6 +32,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace gdb {
 
 namespace {
@@ -154,13 +156,25 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // dQ: var = key) or key (dK/dV: var = query).
 template <bool VAR_IS_KEY, int NB>
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[NB], int fixed, int var0, int lh, int T, int W) {
+  // visible iff lo <= c <= hi for the register's compile-time offset
+  // c = 32jb + 8(v>>2) + (v&3) from this lane's first index var0 + 4lh
+  const int base = var0 + 4 * lh;
+  constexpr int FAR = 1 << 29;  // beyond any offset, no overflow
+  int lo, hi;
+  if (VAR_IS_KEY) {  // fixed = query i, var = key j: j <= i, j < T, i - j <= W
+    hi = min(fixed, T - 1) - base;
+    lo = W >= 0 ? fixed - W - base : -FAR;
+  } else {           // fixed = key j, var = query i: j <= i, i < T, i - j <= W, j < T
+    lo = fixed - base;
+    hi = (W >= 0 ? min(T - 1, fixed + W) : T - 1) - base;
+    if (fixed >= T) hi = -FAR;
+  }
 #pragma unroll
   for (int jb = 0; jb < NB; ++jb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int x = var0 + jb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-      const bool ok = VAR_IS_KEY ? visible(fixed, x, T, W) : (visible(x, fixed, T, W) & (x < T));
-      s[jb][v] = ok ? s[jb][v] : -INFINITY;
+      const int c = jb * 32 + 8 * (v >> 2) + (v & 3);
+      s[jb][v] = ((c >= lo) & (c <= hi)) ? s[jb][v] : -INFINITY;
     }
 }
 
@@ -259,60 +273,68 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_k(AttnArgs a, float sca
   WAIT_VM(0);
   __syncthreads();
 
-  for (int it = 0; it < ntile; ++it) {
-    const int st = it % 3;
-    const int kv0 = kv_lo + it * 64;
-    const bool ahead = it + 2 < ntile;
-    if (ahead) {
-      const int sn = (it + 2) % 3;
-      tile_async<NW>(kbase, a.ld, kv0 + 128, T, Ks[sn]);
-      tile_async<NW>(vbase, a.ld, kv0 + 128, T, Vs[sn]);
-    }
-    // wave-uniform: does the tile touch this wave's rows, and is it fully visible?
-    const bool any = qw0 < T && kv0 <= wq_hi && kv0 + 63 >= wk_lo;
-    if (any) {
-      const bool full = kv0 + 63 <= qw0 && kv0 + 63 < T && (W < 0 || wq_hi - kv0 <= W);
-      f32x16 s[IB][2];
-#pragma unroll
-      for (int ib = 0; ib < IB; ++ib) s[ib][0] = s[ib][1] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-          const bf16x8 kf = row_frag(Ks[st], jb, kk, lr, lh);
-#pragma unroll
-          for (int ib = 0; ib < IB; ++ib) s[ib][jb] = mfma32(kf, qf[ib][kk], s[ib][jb]);
+  // the stage index is a compile-time constant in each copy of the tile
+  // step, so every LDS address is a per-lane base plus an immediate offset
+  auto tile_step = [&](int it, auto stc) {
+    constexpr int ST = decltype(stc)::value;
+    constexpr int st = ST;
+      const int kv0 = kv_lo + it * 64;
+      const bool ahead = it + 2 < ntile;
+      if (ahead) {
+        constexpr int sn = (ST + 2) % 3;
+        tile_async<NW>(kbase, a.ld, kv0 + 128, T, Ks[sn]);
+        tile_async<NW>(vbase, a.ld, kv0 + 128, T, Vs[sn]);
+      }
+      // wave-uniform: does the tile touch this wave's rows, and is it fully visible?
+      const bool any = qw0 < T && kv0 <= wq_hi && kv0 + 63 >= wk_lo;
+      if (any) {
+        const bool full = kv0 + 63 <= qw0 && kv0 + 63 < T && (W < 0 || wq_hi - kv0 <= W);
+        f32x16 s[IB][2];
+  #pragma unroll
+        for (int ib = 0; ib < IB; ++ib) s[ib][0] = s[ib][1] = f32x16{};
+  #pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+  #pragma unroll
+          for (int jb = 0; jb < 2; ++jb) {
+            const bf16x8 kf = row_frag(Ks[st], jb, kk, lr, lh);
+  #pragma unroll
+            for (int ib = 0; ib < IB; ++ib) s[ib][jb] = mfma32(kf, qf[ib][kk], s[ib][jb]);
+          }
+        }
+        bf16x8 pk[IB][4];
+  #pragma unroll
+        for (int ib = 0; ib < IB; ++ib) {
+          const int qi = qw0 + ib * 32 + lr;
+          float alpha;
+          if (!full) mask_tile<true>(s[ib], qi, kv0, lh, T, W);
+          softmax_pack<BOUNDED>(s[ib], pk[ib], scale_log2, m[ib], l[ib], alpha);
+          if (!BOUNDED && __any(alpha != 1.0f)) {
+  #pragma unroll
+            for (int db = 0; db < 4; ++db) o[ib][db] *= alpha;
+          }
+        }
+  #pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+  #pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const bf16x8 vf = tr_frag(Vs[st], db, ks, lane);
+  #pragma unroll
+            for (int ib = 0; ib < IB; ++ib) o[ib][db] = mfma32(vf, pk[ib][ks], o[ib][db]);
+          }
         }
       }
-      bf16x8 pk[IB][4];
-#pragma unroll
-      for (int ib = 0; ib < IB; ++ib) {
-        const int qi = qw0 + ib * 32 + lr;
-        float alpha;
-        if (!full) mask_tile<true>(s[ib], qi, kv0, lh, T, W);
-        softmax_pack<BOUNDED>(s[ib], pk[ib], scale_log2, m[ib], l[ib], alpha);
-        if (!BOUNDED && __any(alpha != 1.0f)) {
-#pragma unroll
-          for (int db = 0; db < 4; ++db) o[ib][db] *= alpha;
-        }
+      if (ahead) {  // tile it+1 landed; tile it+2 may still be in flight
+        if constexpr (NW == 8) WAIT_VM(4);
+        else WAIT_VM(8);
+      } else {
+        WAIT_VM(0);
       }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const bf16x8 vf = tr_frag(Vs[st], db, ks, lane);
-#pragma unroll
-          for (int ib = 0; ib < IB; ++ib) o[ib][db] = mfma32(vf, pk[ib][ks], o[ib][db]);
-        }
-      }
-    }
-    if (ahead) {  // tile it+1 landed; tile it+2 may still be in flight
-      if constexpr (NW == 8) WAIT_VM(4);
-      else WAIT_VM(8);
-    } else {
-      WAIT_VM(0);
-    }
-    __syncthreads();
+      __syncthreads();
+  };
+  for (int it = 0; it < ntile; it += 3) {
+    tile_step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < ntile) tile_step(it + 1, std::integral_constant<int, 1>{});
+    if (it + 2 < ntile) tile_step(it + 2, std::integral_constant<int, 2>{});
   }
 
 #pragma unroll
@@ -548,52 +570,60 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_k(AttnArgs a, float 
   WAIT_VM(0);
   __syncthreads();
 
-  for (int it = 0; it < ntile; ++it) {
-    const int st = it % 3;
-    const int kv0 = kv_lo + it * 64;
-    const bool ahead = it + 2 < ntile;
-    if (ahead) {
-      const int sn = (it + 2) % 3;
-      tile_async<NW>(kbase, a.ld, kv0 + 128, T, Ks[sn]);
-      tile_async<NW>(vbase, a.ld, kv0 + 128, T, Vs[sn]);
-    }
-    const bool any = qw0 < T && kv0 <= wq_hi && kv0 + 63 >= wk_lo;
-    if (any) {
-      const bool full = kv0 + 63 <= qw0 && kv0 + 63 < T && (W < 0 || wq_hi - kv0 <= W);
-      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-          s[jb] = mfma32(row_frag(Ks[st], jb, kk, lr, lh), qf[kk], s[jb]);
-          dp[jb] = mfma32(row_frag(Vs[st], jb, kk, lr, lh), df[kk], dp[jb]);
+  // the stage index is a compile-time constant in each copy of the tile
+  // step, so every LDS address is a per-lane base plus an immediate offset
+  auto tile_step = [&](int it, auto stc) {
+    constexpr int ST = decltype(stc)::value;
+    constexpr int st = ST;
+      const int kv0 = kv_lo + it * 64;
+      const bool ahead = it + 2 < ntile;
+      if (ahead) {
+        constexpr int sn = (ST + 2) % 3;
+        tile_async<NW>(kbase, a.ld, kv0 + 128, T, Ks[sn]);
+        tile_async<NW>(vbase, a.ld, kv0 + 128, T, Vs[sn]);
+      }
+      const bool any = qw0 < T && kv0 <= wq_hi && kv0 + 63 >= wk_lo;
+      if (any) {
+        const bool full = kv0 + 63 <= qw0 && kv0 + 63 < T && (W < 0 || wq_hi - kv0 <= W);
+        f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+  #pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+  #pragma unroll
+          for (int jb = 0; jb < 2; ++jb) {
+            s[jb] = mfma32(row_frag(Ks[st], jb, kk, lr, lh), qf[kk], s[jb]);
+            dp[jb] = mfma32(row_frag(Vs[st], jb, kk, lr, lh), df[kk], dp[jb]);
+          }
+        }
+        if (!full) mask_tile<true>(s, qi, kv0, lh, T, W);
+        bf16x8 sf[4];
+  #pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int jb = ks >> 1;
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int v = 8 * (ks & 1) + e;
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[jb][v], scale_log2, -lse2));
+            sf[ks][e] = (bf16)(p * (dp[jb][v] - dlt));
+          }
+        }
+  #pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+  #pragma unroll
+          for (int db = 0; db < 4; ++db) dq[db] = mfma32(tr_frag(Ks[st], db, ks, lane), sf[ks], dq[db]);
         }
       }
-      if (!full) mask_tile<true>(s, qi, kv0, lh, T, W);
-      bf16x8 sf[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int jb = ks >> 1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int v = 8 * (ks & 1) + e;
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[jb][v], scale_log2, -lse2));
-          sf[ks][e] = (bf16)(p * (dp[jb][v] - dlt));
-        }
+      if (ahead) {
+        if constexpr (NW == 8) WAIT_VM(4);
+        else WAIT_VM(8);
+      } else {
+        WAIT_VM(0);
       }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) dq[db] = mfma32(tr_frag(Ks[st], db, ks, lane), sf[ks], dq[db]);
-      }
-    }
-    if (ahead) {
-      if constexpr (NW == 8) WAIT_VM(4);
-      else WAIT_VM(8);
-    } else {
-      WAIT_VM(0);
-    }
-    __syncthreads();
+      __syncthreads();
+  };
+  for (int it = 0; it < ntile; it += 3) {
+    tile_step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < ntile) tile_step(it + 1, std::integral_constant<int, 1>{});
+    if (it + 2 < ntile) tile_step(it + 2, std::integral_constant<int, 2>{});
   }
   if (qi < T) {
     bf16* row = (bf16*)a.dqkv + ((size_t)b * T + qi) * a.lddq + h * HD;
