@@ -39,14 +39,22 @@ namespace gdb {
 namespace {
 
 constexpr int HD = 128;  // head_dim of the MFMA path
-// forward: NW waves of IB 32-query blocks each; two waves per SIMD (NW = 8)
-// let one wave's softmax overlap the other's MFMAs
+// Two waves on every SIMD, so that one wave's softmax overlaps the other's
+// MFMAs: the forward runs two workgroups of 4 waves per CU (two K/V stages,
+// 64 KiB of LDS each; the workgroups synchronise independently), dQ and
+// dK/dV one workgroup of 8 waves (measured faster for them).
 #ifndef ATTN_NW
-#define ATTN_NW 8
+#define ATTN_NW 4
 #define ATTN_IB 1
+#endif
+#ifndef ATTN_NS
+#define ATTN_NS 2
 #endif
 #ifndef ATTN_DQ_NW
 #define ATTN_DQ_NW 8
+#endif
+#ifndef ATTN_DQ_NS
+#define ATTN_DQ_NS 3
 #endif
 #ifndef ATTN_DKV_NW
 #define ATTN_DKV_NW 8
@@ -136,10 +144,10 @@ __device__ __forceinline__ bool visible(int i, int j, int T, int W) {
 #define WAIT_VM(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
 
 // ----------------------------------------------------------------- forward
-// Workgroup: IB*128 query rows of one (b, h); wave w owns IB blocks of 32
+// Workgroup: 32*IB*NW query rows of one (b, h); wave w owns IB blocks of 32
 // rows (the K and V fragments read from LDS serve every block of the wave).
 // Lane (lr, lh) of block ib holds query q0 + 32*IB*w + 32ib + lr.  K and V
-// tiles of 64 keys stream through 3 LDS stages, two tiles ahead.
+// tiles of 64 keys stream through NS LDS stages, NS - 1 tiles ahead.
 //
 // BOUNDED: q^ and k^ come out of the QK RMS-norm (no affine), so each has
 // norm <= sqrt(D) and every score q^.k^/sqrt(D) lies in [-sqrt(D), sqrt(D)].
@@ -221,11 +229,12 @@ __device__ __forceinline__ void softmax_pack(const f32x16 (&s)[2], bf16x8 (&pk)[
   }
 }
 
-template <int IB, bool BOUNDED, int NW>
+template <int IB, bool BOUNDED, int NW, int NS>
 __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_k(AttnArgs a, float scale_log2) {
+  static_assert(NS == 2 || NS == 3, "two or three K/V stages");
   constexpr int FQ = 32 * IB * NW;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[3][64 * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[3][64 * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[NS][64 * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[NS][64 * HD];
   const int T = a.T, H = a.H, Hkv = a.Hkv, W = a.window;
   // grid (B*H, query blocks): every head's heaviest query block is dispatched first
   const int nqb = (T + FQ - 1) / FQ;
@@ -249,7 +258,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_k(AttnArgs a, float sca
 
   tile_async<NW>(kbase, a.ld, kv_lo, T, Ks[0]);
   tile_async<NW>(vbase, a.ld, kv_lo, T, Vs[0]);
-  if (ntile > 1) {
+  if (NS == 3 && ntile > 1) {
     tile_async<NW>(kbase, a.ld, kv_lo + 64, T, Ks[1]);
     tile_async<NW>(vbase, a.ld, kv_lo + 64, T, Vs[1]);
   }
@@ -278,63 +287,67 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_k(AttnArgs a, float sca
   auto tile_step = [&](int it, auto stc) {
     constexpr int ST = decltype(stc)::value;
     constexpr int st = ST;
-      const int kv0 = kv_lo + it * 64;
-      const bool ahead = it + 2 < ntile;
-      if (ahead) {
-        constexpr int sn = (ST + 2) % 3;
-        tile_async<NW>(kbase, a.ld, kv0 + 128, T, Ks[sn]);
-        tile_async<NW>(vbase, a.ld, kv0 + 128, T, Vs[sn]);
-      }
-      // wave-uniform: does the tile touch this wave's rows, and is it fully visible?
-      const bool any = qw0 < T && kv0 <= wq_hi && kv0 + 63 >= wk_lo;
-      if (any) {
-        const bool full = kv0 + 63 <= qw0 && kv0 + 63 < T && (W < 0 || wq_hi - kv0 <= W);
-        f32x16 s[IB][2];
-  #pragma unroll
-        for (int ib = 0; ib < IB; ++ib) s[ib][0] = s[ib][1] = f32x16{};
-  #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-  #pragma unroll
-          for (int jb = 0; jb < 2; ++jb) {
-            const bf16x8 kf = row_frag(Ks[st], jb, kk, lr, lh);
-  #pragma unroll
-            for (int ib = 0; ib < IB; ++ib) s[ib][jb] = mfma32(kf, qf[ib][kk], s[ib][jb]);
-          }
-        }
-        bf16x8 pk[IB][4];
-  #pragma unroll
-        for (int ib = 0; ib < IB; ++ib) {
-          const int qi = qw0 + ib * 32 + lr;
-          float alpha;
-          if (!full) mask_tile<true>(s[ib], qi, kv0, lh, T, W);
-          softmax_pack<BOUNDED>(s[ib], pk[ib], scale_log2, m[ib], l[ib], alpha);
-          if (!BOUNDED && __any(alpha != 1.0f)) {
-  #pragma unroll
-            for (int db = 0; db < 4; ++db) o[ib][db] *= alpha;
-          }
-        }
-  #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-  #pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const bf16x8 vf = tr_frag(Vs[st], db, ks, lane);
-  #pragma unroll
-            for (int ib = 0; ib < IB; ++ib) o[ib][db] = mfma32(vf, pk[ib][ks], o[ib][db]);
-          }
+    const int kv0 = kv_lo + it * 64;
+    // NS = 3: tile it+2 goes into the stage read two steps ago; NS = 2: tile
+    // it+1 into the stage read in the previous step (both freed by its barrier)
+    const bool ahead = it + NS - 1 < ntile;
+    if (ahead) {
+      constexpr int sn = (ST + NS - 1) % NS;
+      tile_async<NW>(kbase, a.ld, kv0 + 64 * (NS - 1), T, Ks[sn]);
+      tile_async<NW>(vbase, a.ld, kv0 + 64 * (NS - 1), T, Vs[sn]);
+    }
+    // wave-uniform: does the tile touch this wave's rows, and is it fully visible?
+    const bool any = qw0 < T && kv0 <= wq_hi && kv0 + 63 >= wk_lo;
+    if (any) {
+      const bool full = kv0 + 63 <= qw0 && kv0 + 63 < T && (W < 0 || wq_hi - kv0 <= W);
+      f32x16 s[IB][2];
+#pragma unroll
+      for (int ib = 0; ib < IB; ++ib) s[ib][0] = s[ib][1] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          const bf16x8 kf = row_frag(Ks[st], jb, kk, lr, lh);
+#pragma unroll
+          for (int ib = 0; ib < IB; ++ib) s[ib][jb] = mfma32(kf, qf[ib][kk], s[ib][jb]);
         }
       }
-      if (ahead) {  // tile it+1 landed; tile it+2 may still be in flight
-        if constexpr (NW == 8) WAIT_VM(4);
-        else WAIT_VM(8);
-      } else {
-        WAIT_VM(0);
+      bf16x8 pk[IB][4];
+#pragma unroll
+      for (int ib = 0; ib < IB; ++ib) {
+        const int qi = qw0 + ib * 32 + lr;
+        float alpha;
+        if (!full) mask_tile<true>(s[ib], qi, kv0, lh, T, W);
+        softmax_pack<BOUNDED>(s[ib], pk[ib], scale_log2, m[ib], l[ib], alpha);
+        if (!BOUNDED && __any(alpha != 1.0f)) {
+#pragma unroll
+          for (int db = 0; db < 4; ++db) o[ib][db] *= alpha;
+        }
       }
-      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16x8 vf = tr_frag(Vs[st], db, ks, lane);
+#pragma unroll
+          for (int ib = 0; ib < IB; ++ib) o[ib][db] = mfma32(vf, pk[ib][ks], o[ib][db]);
+        }
+      }
+    }
+    if (NS == 3 && ahead) {  // tile it+1 landed; tile it+2 may still be in flight
+      if constexpr (NW == 8) WAIT_VM(4);
+      else WAIT_VM(8);
+    } else {
+      WAIT_VM(0);
+    }
+    __syncthreads();
   };
-  for (int it = 0; it < ntile; it += 3) {
+  for (int it = 0; it < ntile; it += NS) {
     tile_step(it, std::integral_constant<int, 0>{});
     if (it + 1 < ntile) tile_step(it + 1, std::integral_constant<int, 1>{});
-    if (it + 2 < ntile) tile_step(it + 2, std::integral_constant<int, 2>{});
+    if constexpr (NS == 3) {
+      if (it + 2 < ntile) tile_step(it + 2, std::integral_constant<int, 2 % NS>{});
+    }
   }
 
 #pragma unroll
@@ -520,14 +533,15 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_bf16_k(AttnArgs a, float
 }
 
 // ------------------------------------------------------------ backward: dQ
-// Workgroup: 128 query rows of one (b, h), 32 per wave (lane = query).  K and
-// V tiles of 64 keys stream through 3 LDS stages; dQ^T += K^T dS^T with K^T
-// read by the LDS transpose load.
-template <int NW>
+// Workgroup: 32*NW query rows of one (b, h), 32 per wave (lane = query).  K
+// and V tiles of 64 keys stream through NS LDS stages, NS - 1 tiles ahead;
+// dQ^T += K^T dS^T with K^T read by the LDS transpose load.
+template <int NW, int NS>
 __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_k(AttnArgs a, float scale_log2, float scale) {
+  static_assert(NS == 2 || NS == 3, "two or three K/V stages");
   constexpr int FQ = 32 * NW;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[3][64 * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[3][64 * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[NS][64 * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[NS][64 * HD];
   const int T = a.T, H = a.H, Hkv = a.Hkv, W = a.window;
   const int nqb = (T + FQ - 1) / FQ;
   const int qb = nqb - 1 - (int)blockIdx.y;   // grid (B*H, query blocks), heaviest first
@@ -549,7 +563,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_k(AttnArgs a, float 
 
   tile_async<NW>(kbase, a.ld, kv_lo, T, Ks[0]);
   tile_async<NW>(vbase, a.ld, kv_lo, T, Vs[0]);
-  if (ntile > 1) {
+  if (NS == 3 && ntile > 1) {
     tile_async<NW>(kbase, a.ld, kv_lo + 64, T, Ks[1]);
     tile_async<NW>(vbase, a.ld, kv_lo + 64, T, Vs[1]);
   }
@@ -575,55 +589,58 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_k(AttnArgs a, float 
   auto tile_step = [&](int it, auto stc) {
     constexpr int ST = decltype(stc)::value;
     constexpr int st = ST;
-      const int kv0 = kv_lo + it * 64;
-      const bool ahead = it + 2 < ntile;
-      if (ahead) {
-        constexpr int sn = (ST + 2) % 3;
-        tile_async<NW>(kbase, a.ld, kv0 + 128, T, Ks[sn]);
-        tile_async<NW>(vbase, a.ld, kv0 + 128, T, Vs[sn]);
-      }
-      const bool any = qw0 < T && kv0 <= wq_hi && kv0 + 63 >= wk_lo;
-      if (any) {
-        const bool full = kv0 + 63 <= qw0 && kv0 + 63 < T && (W < 0 || wq_hi - kv0 <= W);
-        f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-  #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-  #pragma unroll
-          for (int jb = 0; jb < 2; ++jb) {
-            s[jb] = mfma32(row_frag(Ks[st], jb, kk, lr, lh), qf[kk], s[jb]);
-            dp[jb] = mfma32(row_frag(Vs[st], jb, kk, lr, lh), df[kk], dp[jb]);
-          }
-        }
-        if (!full) mask_tile<true>(s, qi, kv0, lh, T, W);
-        bf16x8 sf[4];
-  #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int jb = ks >> 1;
-  #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int v = 8 * (ks & 1) + e;
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[jb][v], scale_log2, -lse2));
-            sf[ks][e] = (bf16)(p * (dp[jb][v] - dlt));
-          }
-        }
-  #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-  #pragma unroll
-          for (int db = 0; db < 4; ++db) dq[db] = mfma32(tr_frag(Ks[st], db, ks, lane), sf[ks], dq[db]);
+    const int kv0 = kv_lo + it * 64;
+    // the next copy goes into the stage freed by the previous step's barrier
+    const bool ahead = it + NS - 1 < ntile;
+    if (ahead) {
+      constexpr int sn = (ST + NS - 1) % NS;
+      tile_async<NW>(kbase, a.ld, kv0 + 64 * (NS - 1), T, Ks[sn]);
+      tile_async<NW>(vbase, a.ld, kv0 + 64 * (NS - 1), T, Vs[sn]);
+    }
+    const bool any = qw0 < T && kv0 <= wq_hi && kv0 + 63 >= wk_lo;
+    if (any) {
+      const bool full = kv0 + 63 <= qw0 && kv0 + 63 < T && (W < 0 || wq_hi - kv0 <= W);
+      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          s[jb] = mfma32(row_frag(Ks[st], jb, kk, lr, lh), qf[kk], s[jb]);
+          dp[jb] = mfma32(row_frag(Vs[st], jb, kk, lr, lh), df[kk], dp[jb]);
         }
       }
-      if (ahead) {
-        if constexpr (NW == 8) WAIT_VM(4);
-        else WAIT_VM(8);
-      } else {
-        WAIT_VM(0);
+      if (!full) mask_tile<true>(s, qi, kv0, lh, T, W);
+      bf16x8 sf[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int jb = ks >> 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int v = 8 * (ks & 1) + e;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[jb][v], scale_log2, -lse2));
+          sf[ks][e] = (bf16)(p * (dp[jb][v] - dlt));
+        }
       }
-      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) dq[db] = mfma32(tr_frag(Ks[st], db, ks, lane), sf[ks], dq[db]);
+      }
+    }
+    if (NS == 3 && ahead) {
+      if constexpr (NW == 8) WAIT_VM(4);
+      else WAIT_VM(8);
+    } else {
+      WAIT_VM(0);
+    }
+    __syncthreads();
   };
-  for (int it = 0; it < ntile; it += 3) {
+  for (int it = 0; it < ntile; it += NS) {
     tile_step(it, std::integral_constant<int, 0>{});
     if (it + 1 < ntile) tile_step(it + 1, std::integral_constant<int, 1>{});
-    if (it + 2 < ntile) tile_step(it + 2, std::integral_constant<int, 2>{});
+    if constexpr (NS == 3) {
+      if (it + 2 < ntile) tile_step(it + 2, std::integral_constant<int, 2 % NS>{});
+    }
   }
   if (qi < T) {
     bf16* row = (bf16*)a.dqkv + ((size_t)b * T + qi) * a.lddq + h * HD;
@@ -737,11 +754,11 @@ hipError_t attn_fwd(int dt, const AttnArgs& a, hipStream_t s) {
   if (dt == BF16) {
     if (a.qk_normed) {
       dim3 g(a.B * a.H, (a.T + ATTN_FQ - 1) / ATTN_FQ);
-      hipLaunchKernelGGL((attn_fwd_bf16_k<ATTN_IB, true, ATTN_NW>), g, dim3(64 * ATTN_NW), 0, s, a,
+      hipLaunchKernelGGL((attn_fwd_bf16_k<ATTN_IB, true, ATTN_NW, ATTN_NS>), g, dim3(64 * ATTN_NW), 0, s, a,
                          scale * 1.4426950408889634f);
     } else {
       dim3 g(a.B * a.H, (a.T + 127) / 128);
-      hipLaunchKernelGGL((attn_fwd_bf16_k<1, false, 4>), g, dim3(256), 0, s, a, scale * 1.4426950408889634f);
+      hipLaunchKernelGGL((attn_fwd_bf16_k<1, false, 4, 3>), g, dim3(256), 0, s, a, scale * 1.4426950408889634f);
     }
   } else {
     dim3 g((a.B * a.H * a.T + 63) / 64);
@@ -764,7 +781,7 @@ hipError_t attn_bwd(int dt, const AttnArgs& a, hipStream_t s) {
                        dim3(64 * ATTN_DKV_NW), 0, s, a, scale * 1.4426950408889634f, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_bwd_dq_bf16_k<ATTN_DQ_NW>, dim3(a.B * a.H, (a.T + 32 * ATTN_DQ_NW - 1) / (32 * ATTN_DQ_NW)),
+    hipLaunchKernelGGL((attn_bwd_dq_bf16_k<ATTN_DQ_NW, ATTN_DQ_NS>), dim3(a.B * a.H, (a.T + 32 * ATTN_DQ_NW - 1) / (32 * ATTN_DQ_NW)),
                        dim3(64 * ATTN_DQ_NW), 0, s, a,
                        scale * 1.4426950408889634f, scale);
   } else {
