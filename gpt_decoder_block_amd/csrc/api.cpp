@@ -351,18 +351,20 @@ gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
   GemmArgs g = gemm_args(sv.o, true, d.Q, w->w_o, true, d.Q, N, d.C, d.Q, EPI_RESID, wf.x_mid, d.C);
   g.R = x; g.ldr = d.C;
   HIPCHK(gemm(dt, g, s));
-  HIPCHK(rmsnorm_fwd(dt, wf.x_mid, sv.xn2, sv.r2, N, d.C, d.eps, s));
   if (d.fp8) {
     // e4m3 codes of both operands of each MLP product (row-major for the
-    // forward, transposed copies kept for the backward), per-tensor scales
-    HIPCHK(fp8_amax(dt, sv.xn2, (size_t)N * d.C, sv.amax + 0, s));
+    // forward, transposed copies kept for the backward), per-tensor scales;
+    // the amax of xn2 and h comes from the kernels that write them
+    HIPCHK(fp8_amax_zero(sv.amax + 0, s));
+    HIPCHK(rmsnorm_fwd(dt, wf.x_mid, sv.xn2, sv.r2, N, d.C, d.eps, s, sv.amax + 0));
     HIPCHK(fp8_quant(dt, sv.xn2, N, d.C, sv.amax + 0, wf.xn2q, sv.xn2T, d.Np, s));
     HIPCHK(fp8_amax(dt, w->w_fc, (size_t)d.F * d.C, sv.amax + 1, s));
     HIPCHK(fp8_quant(dt, w->w_fc, d.F, d.C, sv.amax + 1, wf.wfcq, sv.wfcT, d.F, s));
     g = gemm_args(wf.xn2q, true, d.C, wf.wfcq, true, d.C, N, d.F, d.C, EPI_RELU2, sv.u, d.F);
     g.C2 = sv.h; g.amax_a = sv.amax + 0; g.amax_b = sv.amax + 1;
+    g.amax_out = sv.amax + 2;
+    HIPCHK(fp8_amax_zero(sv.amax + 2, s));
     HIPCHK(gemm_fp8(dt, g, s));
-    HIPCHK(fp8_amax(dt, sv.h, (size_t)N * d.F, sv.amax + 2, s));
     HIPCHK(fp8_quant(dt, sv.h, N, d.F, sv.amax + 2, wf.hq, sv.hT, d.Np, s));
     HIPCHK(fp8_amax(dt, w->w_proj, (size_t)d.C * d.F, sv.amax + 3, s));
     HIPCHK(fp8_quant(dt, w->w_proj, d.C, d.F, sv.amax + 3, wf.wprojq, sv.wprojT, d.C, s));
@@ -372,6 +374,7 @@ gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
     g_err.clear();
     return GDB_OK;
   }
+  HIPCHK(rmsnorm_fwd(dt, wf.x_mid, sv.xn2, sv.r2, N, d.C, d.eps, s));
   g = gemm_args(sv.xn2, true, d.C, w->w_fc, true, d.C, N, d.F, d.C, EPI_RELU2, sv.u, d.F);
   g.C2 = sv.h;
   HIPCHK(gemm(dt, g, s));
@@ -416,11 +419,13 @@ gdb_status gdb_block_bwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
     // weights and saved activations, fresh ones for dout and du
     HIPCHK(fp8_amax(dt, dx_out, (size_t)N * d.C, wb.amax8 + 0, s));
     HIPCHK(fp8_quant(dt, dx_out, N, d.C, wb.amax8 + 0, wb.doutq, wb.doutT, d.Np, s));
+    // du's amax comes from the GEMM that writes it
     GemmArgs g = gemm_args(wb.doutq, true, d.C, sv.wprojT, true, d.C, N, d.F, d.C, EPI_DRELU2, wb.du, d.F);
     g.R = sv.u; g.ldr = d.F; g.amax_a = wb.amax8 + 0; g.amax_b = sv.amax + 3;
+    g.amax_out = wb.amax8 + 1;
+    HIPCHK(fp8_amax_zero(wb.amax8 + 1, s));
     HIPCHK(gemm_fp8(dt, g, s));
     HIPCHK(wgrad_fp8(wb.doutT, wb.amax8 + 0, sv.hT, sv.amax + 2, d.C, d.F, d.Np, dw->dw_proj, acc, wb.partial, s));
-    HIPCHK(fp8_amax(dt, wb.du, (size_t)N * d.F, wb.amax8 + 1, s));
     HIPCHK(fp8_quant(dt, wb.du, N, d.F, wb.amax8 + 1, wb.duq, wb.duT, d.Np, s));
     g = gemm_args(wb.duq, true, d.F, sv.wfcT, true, d.F, N, d.C, d.F, EPI_STORE, wb.dxn, d.C);
     g.amax_a = wb.amax8 + 1; g.amax_b = sv.amax + 1;

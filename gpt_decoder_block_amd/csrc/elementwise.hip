@@ -36,11 +36,9 @@ hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s) {
 constexpr int RMS_MAXV = 4;
 
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_fwd_k(const T* __restrict__ x, T* __restrict__ xn,
-                                                      float* __restrict__ r, int N, int C, float eps) {
+__device__ __forceinline__ void rmsnorm_row(const T* __restrict__ x, T* __restrict__ xn, float* __restrict__ r,
+                                            int row, int l, int C, float eps, float& am) {
   constexpr int VN = V16<T>::n;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
-  if (row >= N) return;
   const T* xr = x + (size_t)row * C;
   T* yr = xn + (size_t)row * C;
   const int nv = C / VN;
@@ -62,7 +60,10 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const T* __restrict__ x, T*
       const int vi = l + 64 * i;
       if (vi < nv) {
 #pragma unroll
-        for (int e = 0; e < VN; ++e) v[i][e] *= ri;
+        for (int e = 0; e < VN; ++e) {
+          v[i][e] *= ri;
+          am = fmaxf(am, fabsf(v[i][e]));
+        }
         st16(yr + vi * VN, v[i]);
       }
     }
@@ -79,10 +80,29 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const T* __restrict__ x, T*
       float v[VN];
       ld16(xr + vi * VN, v);
 #pragma unroll
-      for (int e = 0; e < VN; ++e) v[e] *= ri;
+      for (int e = 0; e < VN; ++e) {
+        v[e] *= ri;
+        am = fmaxf(am, fabsf(v[e]));
+      }
       st16(yr + vi * VN, v);
     }
     if (l == 0) r[row] = ri;
+  }
+}
+
+// amax (optional): the largest |xn| stored, one atomic per workgroup
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_k(const T* __restrict__ x, T* __restrict__ xn,
+                                                      float* __restrict__ r, int N, int C, float eps,
+                                                      unsigned* __restrict__ amax) {
+  __shared__ float red[4];
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  float am = 0.f;
+  if (row < N) rmsnorm_row<T>(x, xn, r, row, l, C, eps, am);
+  if (amax) {
+    am = block_max<256>(am, red);
+    // rounding is monotone: the largest stored value is the rounded largest value
+    if (threadIdx.x == 0) atomicMax(amax, __float_as_uint((float)(T)am));
   }
 }
 
@@ -98,13 +118,22 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const T* __restrict__ dy, c
   const float ri = r[row];
   float dot = 0.f;
   if (nv <= 64 * RMS_MAXV) {
-    float g[RMS_MAXV][VN], h[RMS_MAXV][VN];
+    // the residual gradient is loaded with dy and y, before the reduction,
+    // so its latency is not exposed after it
+    float g[RMS_MAXV][VN], h[RMS_MAXV][VN], rs[RMS_MAXV][VN];
 #pragma unroll
     for (int i = 0; i < RMS_MAXV; ++i) {
       const int vi = l + 64 * i;
       if (vi < nv) {
         ld16(dy + off + vi * VN, g[i]);
         ld16(y + off + vi * VN, h[i]);
+        if (dres) ld16(dres + off + vi * VN, rs[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RMS_MAXV; ++i) {
+      const int vi = l + 64 * i;
+      if (vi < nv) {
 #pragma unroll
         for (int e = 0; e < VN; ++e) dot += g[i][e] * h[i][e];
       }
@@ -114,10 +143,9 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const T* __restrict__ dy, c
     for (int i = 0; i < RMS_MAXV; ++i) {
       const int vi = l + 64 * i;
       if (vi < nv) {
-        float o[VN], rs[VN];
-        if (dres) ld16(dres + off + vi * VN, rs);
+        float o[VN];
 #pragma unroll
-        for (int e = 0; e < VN; ++e) o[e] = ri * (g[i][e] - h[i][e] * m) + (dres ? rs[e] : 0.f);
+        for (int e = 0; e < VN; ++e) o[e] = ri * (g[i][e] - h[i][e] * m) + (dres ? rs[i][e] : 0.f);
         st16(dx + off + vi * VN, o);
       }
     }
@@ -142,13 +170,14 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const T* __restrict__ dy, c
   }
 }
 
-hipError_t rmsnorm_fwd(int dt, const void* x, void* xn, float* r, int N, int C, float eps, hipStream_t s) {
+hipError_t rmsnorm_fwd(int dt, const void* x, void* xn, float* r, int N, int C, float eps, hipStream_t s,
+                       float* amax) {
   if (N == 0) return hipSuccess;
   dim3 g((N + 3) / 4), b(256);
   if (dt == BF16)
-    hipLaunchKernelGGL(rmsnorm_fwd_k<bf16>, g, b, 0, s, (const bf16*)x, (bf16*)xn, r, N, C, eps);
+    hipLaunchKernelGGL(rmsnorm_fwd_k<bf16>, g, b, 0, s, (const bf16*)x, (bf16*)xn, r, N, C, eps, (unsigned*)amax);
   else
-    hipLaunchKernelGGL(rmsnorm_fwd_k<float>, g, b, 0, s, (const float*)x, (float*)xn, r, N, C, eps);
+    hipLaunchKernelGGL(rmsnorm_fwd_k<float>, g, b, 0, s, (const float*)x, (float*)xn, r, N, C, eps, (unsigned*)amax);
   return hipGetLastError();
 }
 
@@ -398,6 +427,79 @@ __global__ __launch_bounds__(256) void ce_k(T* z, const int32_t* __restrict__ tg
   if (threadIdx.x == 0) row_loss[n] = lse - zy;
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 logits: the row is kept in registers as its raw bf16 pairs (half the
+// registers of fp32 values, so twice the rows per CU hide the memory
+// latency) and widened on each of the three uses; the exponentials are taken
+// in base 2 on log2(e)-scaled logits.
+__global__ __launch_bounds__(256) void ce_bf16_k(bf16* z, const int32_t* __restrict__ tgt,
+                                                  float* __restrict__ row_loss, int N, int V) {
+  __shared__ float red[4];
+  constexpr float L2E = 1.4426950408889634f;
+  const int n = blockIdx.x;
+  bf16* zr = z + (size_t)n * V;
+  const int nv = V / 8;
+  int y = tgt[n];
+  y = y < 0 ? 0 : (y >= V ? V - 1 : y);
+  const float zy = (float)zr[y];
+  u32x4 raw[CE_MAXV];
+#pragma unroll
+  for (int i = 0; i < CE_MAXV; ++i) {
+    const int vi = threadIdx.x + 256 * i;
+    raw[i] = vi < nv ? *(const u32x4*)(zr + vi * 8) : u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+  }
+  // bf16 pair -> two floats: the low half shifted up, the high half masked
+  auto lo = [](unsigned w) { return __uint_as_float(w << 16); };
+  auto hi = [](unsigned w) { return __uint_as_float(w & 0xffff0000u); };
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < CE_MAXV; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mx = fmaxf(mx, fmaxf(lo(raw[i][q]), hi(raw[i][q])));
+  mx = block_max<256>(mx, red);
+  // an empty asm marks the raw words as changed, so the widened floats are
+  // recomputed in each pass rather than kept live (which would double the
+  // registers per row)
+#pragma unroll
+  for (int i = 0; i < CE_MAXV; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(raw[i][q]));
+  const float m2 = mx * L2E;
+  float se = 0.f;
+#pragma unroll
+  for (int i = 0; i < CE_MAXV; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      se += __builtin_amdgcn_exp2f(fmaf(lo(raw[i][q]), L2E, -m2)) + __builtin_amdgcn_exp2f(fmaf(hi(raw[i][q]), L2E, -m2));
+  se = block_sum<256>(se, red);
+#pragma unroll
+  for (int i = 0; i < CE_MAXV; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(raw[i][q]));
+  const float lse = mx + logf(se);
+  const float l2 = lse * L2E;
+  const float invN = 1.0f / (float)N;
+#pragma unroll
+  for (int i = 0; i < CE_MAXV; ++i) {
+    const int vi = threadIdx.x + 256 * i;
+    if (vi < nv) {
+      bf16x8 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(lo(raw[i][q]), L2E, -l2));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(hi(raw[i][q]), L2E, -l2));
+        o[2 * q] = (bf16)(p0 * invN);
+        o[2 * q + 1] = (bf16)(p1 * invN);
+      }
+      *(bf16x8*)(zr + vi * 8) = o;
+    }
+  }
+  // the target's entry, rewritten by the thread that stored its vector
+  if ((y >> 3) % 256 == (int)threadIdx.x) zr[y] = (bf16)((__builtin_amdgcn_exp2f(fmaf(zy, L2E, -l2)) - 1.0f) * invN);
+  if (threadIdx.x == 0) row_loss[n] = lse - zy;
+}
+
 // Rows longer than the register-resident capacity: three streamed passes.
 template <typename T>
 __global__ __launch_bounds__(256) void ce_long_k(T* z, const int32_t* __restrict__ tgt, float* __restrict__ row_loss,
@@ -444,7 +546,7 @@ hipError_t ce_fwd_bwd(int dt, void* z, const int32_t* tgt, float* row_loss, int 
   const int vn = dt == BF16 ? 8 : 4;
   const bool fits = V / vn <= 256 * CE_MAXV;
   if (dt == BF16) {
-    if (fits) hipLaunchKernelGGL(ce_k<bf16>, dim3(N), dim3(256), 0, s, (bf16*)z, tgt, row_loss, N, V);
+    if (fits) hipLaunchKernelGGL(ce_bf16_k, dim3(N), dim3(256), 0, s, (bf16*)z, tgt, row_loss, N, V);
     else hipLaunchKernelGGL(ce_long_k<bf16>, dim3(N), dim3(256), 0, s, (bf16*)z, tgt, row_loss, N, V);
   } else {
     if (fits) hipLaunchKernelGGL(ce_k<float>, dim3(N), dim3(256), 0, s, (float*)z, tgt, row_loss, N, V);

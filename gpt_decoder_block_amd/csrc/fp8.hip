@@ -109,6 +109,11 @@ __global__ __launch_bounds__(256) void quant_k(const T* __restrict__ x, int R, i
 
 }  // namespace
 
+hipError_t fp8_amax_zero(float* amax, hipStream_t s) {
+  hipLaunchKernelGGL(zero_u32_k, dim3(1), dim3(1), 0, s, (unsigned*)amax);
+  return hipGetLastError();
+}
+
 hipError_t fp8_amax(int dt, const void* x, size_t n, float* amax, hipStream_t s) {
   hipLaunchKernelGGL(zero_u32_k, dim3(1), dim3(1), 0, s, (unsigned*)amax);
   hipError_t e = hipGetLastError();

@@ -399,6 +399,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
   // 64 lanes x 4 columns = one 256-column row per instruction.
   float* stage = (float*)&smem[0][0][0];
   const int ncols = min(BN, p.N - n0);
+  float am = 0.f;  // largest |value| this thread stores into the quantiser's input (amax_out)
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     if (wm == q) {
@@ -522,7 +523,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
             for (int e = 0; e < 4; ++e) o[e] = (OT)(v[e] + (float)rv[k][e]);
           } else if (EPI == EPI_DRELU2) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = (OT)(v[e] * 2.0f * fmaxf((float)rv[k][e], 0.f));
+            for (int e = 0; e < 4; ++e) {
+              const float dv = v[e] * 2.0f * fmaxf((float)rv[k][e], 0.f);
+              o[e] = (OT)dv;
+              am = fmaxf(am, fabsf(dv));
+            }
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = (OT)v[e];
@@ -534,6 +539,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
             for (int e = 0; e < 4; ++e) {
               const float rl = fmaxf(v[e], 0.f);
               h[e] = (OT)(rl * rl);
+              am = fmaxf(am, rl * rl);
             }
             *(OV*)((OT*)p.C2 + off) = h;
           }
@@ -542,6 +548,14 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
     }
     }
     if (q == 0) __syncthreads();
+  }
+  if constexpr (EPI == EPI_RELU2 || EPI == EPI_DRELU2) {
+    if (p.amax_out) {
+      // rounding is monotone: the largest stored value is the rounded largest value
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+      if (lane == 0) atomicMax((unsigned*)p.amax_out, __float_as_uint((float)(OT)am));
+    }
   }
 }
 

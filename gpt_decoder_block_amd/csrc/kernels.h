@@ -16,7 +16,9 @@ inline int dt_size(int dt) { return dt == BF16 ? 2 : 4; }
 // ---------------------------------------------------------------- elementwise
 hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s);
 // xn = x * r, r = 1/sqrt(mean(x^2)+eps) per row of [N, C]
-hipError_t rmsnorm_fwd(int dt, const void* x, void* xn, float* r, int N, int C, float eps, hipStream_t s);
+// amax (optional): atomically raised to the largest |xn| stored; zeroed by the caller
+hipError_t rmsnorm_fwd(int dt, const void* x, void* xn, float* r, int N, int C, float eps, hipStream_t s,
+                       float* amax = nullptr);
 // dx = r*(dxn - xn*mean(dxn*xn)) (+ dres if non-null); dx may alias dres
 hipError_t rmsnorm_bwd(int dt, const void* dxn, const void* xn, const float* r, const void* dres,
                        void* dx, int N, int C, hipStream_t s);
@@ -64,6 +66,10 @@ struct GemmArgs {
   int splits;          // >= 1
   const float* amax_a; // fp8: per-tensor amax of A and B (scales amax/448)
   const float* amax_b;
+  // EPI_RELU2 / EPI_DRELU2: if set, atomically raised to the largest |value|
+  // stored in C2 (ReLU2) or C (DReLU2) -- the next quantiser's amax; the
+  // caller zeroes it first
+  float* amax_out;
   // EPI_QKNORM: rope table [T][64][2], row m is position m % T
   const float* rope; float* rinv; int T; int qk_heads; float eps;
 };
@@ -78,6 +84,8 @@ int gemm_splits(int dt, int M, int N, int K, int epi);
 // ------------------------------------------------------------ fp8 quantiser
 // amax[0] = max |x| over n elements (x dtype dt; n a multiple of 8); amax is
 // zeroed first (stream-ordered), so one call gives one tensor's amax.
+// zero an amax accumulator (before a producer that raises it)
+hipError_t fp8_amax_zero(float* amax, hipStream_t s);
 hipError_t fp8_amax(int dt, const void* x, size_t n, float* amax, hipStream_t s);
 // codes e4m3(x / s), s = amax / 448 (float32 division, round to nearest
 // even, saturating at 448): x [R, Cc] (dt), Cc a multiple of 16; xq [R, Cc]
