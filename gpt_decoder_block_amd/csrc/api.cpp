@@ -92,7 +92,7 @@ gdb_status check_cfg(const gdb_block_cfg* c, BlockDims* d) {
 }
 
 struct Saved {
-  void *xn1, *qkvh, *o, *xn2, *u, *h;
+  void *xn1, *qkvh, *o, *xn2, *h;
   float *r1, *rqk, *lse, *r2;
   float* ve_s;          // value-embedding gate logits [N, Hkv]
   // fp8 MLP: transposed codes for the backward and the four amax values
@@ -123,7 +123,6 @@ void carve_saved(const BlockDims& d, Carver& c, Saved& s) {
   s.lse = c.take<float>(N * d.H * 4);
   s.xn2 = c.take<char>(N * d.C * d.s);
   s.r2 = c.take<float>(N * 4);
-  s.u = c.take<char>(N * d.F * d.s);
   s.h = c.take<char>(N * d.F * d.s);
   s.ve_s = c.take<float>(N * d.Hkv * 4);
   const size_t f8 = d.fp8 ? 1 : 0, Np = d.Np;
@@ -360,8 +359,8 @@ gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
     HIPCHK(fp8_quant(dt, sv.xn2, N, d.C, sv.amax + 0, wf.xn2q, sv.xn2T, d.Np, s));
     HIPCHK(fp8_amax(dt, w->w_fc, (size_t)d.F * d.C, sv.amax + 1, s));
     HIPCHK(fp8_quant(dt, w->w_fc, d.F, d.C, sv.amax + 1, wf.wfcq, sv.wfcT, d.F, s));
-    g = gemm_args(wf.xn2q, true, d.C, wf.wfcq, true, d.C, N, d.F, d.C, EPI_RELU2, sv.u, d.F);
-    g.C2 = sv.h; g.amax_a = sv.amax + 0; g.amax_b = sv.amax + 1;
+    g = gemm_args(wf.xn2q, true, d.C, wf.wfcq, true, d.C, N, d.F, d.C, EPI_SQR, sv.h, d.F);
+    g.amax_a = sv.amax + 0; g.amax_b = sv.amax + 1;
     g.amax_out = sv.amax + 2;
     HIPCHK(fp8_amax_zero(sv.amax + 2, s));
     HIPCHK(gemm_fp8(dt, g, s));
@@ -375,8 +374,8 @@ gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
     return GDB_OK;
   }
   HIPCHK(rmsnorm_fwd(dt, wf.x_mid, sv.xn2, sv.r2, N, d.C, d.eps, s));
-  g = gemm_args(sv.xn2, true, d.C, w->w_fc, true, d.C, N, d.F, d.C, EPI_RELU2, sv.u, d.F);
-  g.C2 = sv.h;
+  // only h = relu(u)^2 is kept: the backward's ReLU^2 derivative 2*relu(u) is 2*sqrt(h)
+  g = gemm_args(sv.xn2, true, d.C, w->w_fc, true, d.C, N, d.F, d.C, EPI_SQR, sv.h, d.F);
   HIPCHK(gemm(dt, g, s));
   g = gemm_args(sv.h, true, d.F, w->w_proj, true, d.F, N, d.C, d.F, EPI_RESID, x_out, d.C);
   g.R = wf.x_mid; g.ldr = d.C;
@@ -420,8 +419,8 @@ gdb_status gdb_block_bwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
     HIPCHK(fp8_amax(dt, dx_out, (size_t)N * d.C, wb.amax8 + 0, s));
     HIPCHK(fp8_quant(dt, dx_out, N, d.C, wb.amax8 + 0, wb.doutq, wb.doutT, d.Np, s));
     // du's amax comes from the GEMM that writes it
-    GemmArgs g = gemm_args(wb.doutq, true, d.C, sv.wprojT, true, d.C, N, d.F, d.C, EPI_DRELU2, wb.du, d.F);
-    g.R = sv.u; g.ldr = d.F; g.amax_a = wb.amax8 + 0; g.amax_b = sv.amax + 3;
+    GemmArgs g = gemm_args(wb.doutq, true, d.C, sv.wprojT, true, d.C, N, d.F, d.C, EPI_DSQR, wb.du, d.F);
+    g.R = sv.h; g.ldr = d.F; g.amax_a = wb.amax8 + 0; g.amax_b = sv.amax + 3;
     g.amax_out = wb.amax8 + 1;
     HIPCHK(fp8_amax_zero(wb.amax8 + 1, s));
     HIPCHK(gemm_fp8(dt, g, s));
@@ -432,8 +431,8 @@ gdb_status gdb_block_bwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
     HIPCHK(gemm_fp8(dt, g, s));
     HIPCHK(wgrad_fp8(wb.duT, wb.amax8 + 1, sv.xn2T, sv.amax + 0, d.F, d.C, d.Np, dw->dw_fc, acc, wb.partial, s));
   } else {
-    GemmArgs g = gemm_args(dx_out, true, d.C, w->w_proj, false, d.F, N, d.F, d.C, EPI_DRELU2, wb.du, d.F);
-    g.R = sv.u; g.ldr = d.F;
+    GemmArgs g = gemm_args(dx_out, true, d.C, w->w_proj, false, d.F, N, d.F, d.C, EPI_DSQR, wb.du, d.F);
+    g.R = sv.h; g.ldr = d.F;
     HIPCHK(gemm(dt, g, s));
     HIPCHK(wgrad(dt, dx_out, d.C, sv.h, d.F, d.C, d.F, N, dw->dw_proj, acc, wb.partial, s));
     HIPCHK(gemm(dt, gemm_args(wb.du, true, d.F, w->w_fc, false, d.C, N, d.C, d.F, EPI_STORE, wb.dxn, d.C), s));
@@ -552,10 +551,13 @@ gdb_status gdb_rmsnorm_bwd(int32_t N, int32_t C, int32_t dtype, const void* dxn,
   return GDB_OK;
 }
 
+// epilogues of the GEMM entry points: 0-4, 6 (SQR) and 7 (DSQR); 5 is internal
+static bool public_epi(int epi) { return (epi >= EPI_STORE && epi <= EPI_F32) || epi == EPI_SQR || epi == EPI_DSQR; }
+
 gdb_status gdb_gemm_ws_bytes(int32_t dtype, int32_t M, int32_t N, int32_t K, int32_t epi, size_t* ws_bytes) {
   if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
   if (M < 0 || N < 0 || K < 0) return fail(GDB_EINVAL, "negative size");
-  if (epi < 0 || epi > EPI_F32) return fail(GDB_EINVAL, "unknown epilogue %d", epi);
+  if (!public_epi(epi)) return fail(GDB_EINVAL, "unknown epilogue %d", epi);
   const int sp = gemm_splits(dtype, M, N, K, epi);
   if (ws_bytes) *ws_bytes = sp > 1 ? (size_t)sp * M * N * 4 : 0;
   g_err.clear();
@@ -567,19 +569,23 @@ gdb_status gdb_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* 
                     int32_t ldr, void* C2, int32_t accumulate, void* ws, void* stream) {
   if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
   if (M < 0 || N < 0 || K < 0) return fail(GDB_EINVAL, "negative size");
-  if (epi < 0 || epi > EPI_F32) return fail(GDB_EINVAL, "unknown epilogue %d", epi);
+  if (!public_epi(epi)) return fail(GDB_EINVAL, "unknown epilogue %d", epi);
   if (N % 8 || ldc % 8 || lda % 8 || ldb % 8) return fail(GDB_EINVAL, "N, lda, ldb, ldc must be multiples of 8");
   if (a_kmajor ? (K % 8 != 0) : (M % 8 != 0)) return fail(GDB_EINVAL, "the contiguous dimension of A must be a multiple of 8");
   if (b_kmajor && K % 8) return fail(GDB_EINVAL, "K must be a multiple of 8 when B is K-major");
   if (lda < (a_kmajor ? K : M) || ldb < (b_kmajor ? K : N) || ldc < N) return fail(GDB_EINVAL, "leading dimension too small");
   if (M == 0 || N == 0) { g_err.clear(); return GDB_OK; }
   CHECK_PTR(A); CHECK_PTR(B); CHECK_PTR(C);
-  if (epi == EPI_RESID || epi == EPI_DRELU2) {
+  if (epi == EPI_RESID || epi == EPI_DRELU2 || epi == EPI_DSQR) {
     CHECK_PTR(R);
     if (ldr % 8 || ldr < N) return fail(GDB_EINVAL, "ldr must be a multiple of 8 and >= N");
   }
   if (epi == EPI_RELU2) CHECK_PTR(C2);
   if (epi == EPI_F32 && ldc != N) return fail(GDB_EINVAL, "fp32 output needs ldc == N");
+  if (dtype == GDB_BF16 && epi == EPI_SQR && !(a_kmajor && b_kmajor))
+    return fail(GDB_EUNSUPPORTED, "epilogue 6 needs both operands K-major in bf16");
+  if (dtype == GDB_BF16 && epi == EPI_DSQR && !a_kmajor)
+    return fail(GDB_EUNSUPPORTED, "epilogue 7 needs A K-major in bf16");
   GemmArgs g = gemm_args(A, a_kmajor != 0, lda, B, b_kmajor != 0, ldb, M, N, K, epi, C, ldc);
   g.R = R; g.ldr = ldr; g.C2 = C2; g.accumulate = accumulate ? 1 : 0;
   if (epi == EPI_F32) {
@@ -615,7 +621,7 @@ gdb_status gdb_fp8_quantize(int32_t R, int32_t Cc, int32_t dtype, const void* x,
 
 gdb_status gdb_gemm_fp8_ws_bytes(int32_t M, int32_t N, int32_t K, int32_t epi, size_t* ws_bytes) {
   if (M < 0 || N < 0 || K < 0) return fail(GDB_EINVAL, "negative size");
-  if (epi < 0 || epi > EPI_F32) return fail(GDB_EINVAL, "unknown epilogue %d", epi);
+  if (!public_epi(epi)) return fail(GDB_EINVAL, "unknown epilogue %d", epi);
   const int sp = gemm_splits(FP8, M, N, K, epi);
   if (ws_bytes) *ws_bytes = sp > 1 ? (size_t)sp * M * N * 4 : 0;
   g_err.clear();
@@ -628,7 +634,7 @@ gdb_status gdb_gemm_fp8(int32_t dtype, int32_t M, int32_t N, int32_t K, const ui
                         void* stream) {
   if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
   if (M < 0 || N < 0 || K < 0) return fail(GDB_EINVAL, "negative size");
-  if (epi < 0 || epi > EPI_F32) return fail(GDB_EINVAL, "unknown epilogue %d", epi);
+  if (!public_epi(epi)) return fail(GDB_EINVAL, "unknown epilogue %d", epi);
   if (K % 16 || lda % 16 || ldb % 16) return fail(GDB_EINVAL, "K, lda, ldb must be multiples of 16");
   if (N % 8 || ldc % 8) return fail(GDB_EINVAL, "N and ldc must be multiples of 8");
   if (lda < K || ldb < K || ldc < N) return fail(GDB_EINVAL, "leading dimension too small");
@@ -636,7 +642,7 @@ gdb_status gdb_gemm_fp8(int32_t dtype, int32_t M, int32_t N, int32_t K, const ui
   CHECK_PTR(A); CHECK_PTR(B); CHECK_PTR(C);
   if (!amax_a || !amax_b || (((uintptr_t)amax_a) & 3) || (((uintptr_t)amax_b) & 3))
     return fail(GDB_EINVAL, "amax_a or amax_b is NULL or not 4-byte aligned");
-  if (epi == EPI_RESID || epi == EPI_DRELU2) {
+  if (epi == EPI_RESID || epi == EPI_DRELU2 || epi == EPI_DSQR) {
     CHECK_PTR(R);
     if (ldr % 8 || ldr < N) return fail(GDB_EINVAL, "ldr must be a multiple of 8 and >= N");
   }

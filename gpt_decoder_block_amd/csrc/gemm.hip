@@ -423,7 +423,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
     constexpr int RPW = 128 / (NTHR / 64);  // rows per wave per pass
     // residual / saved-u operand for all of this wave's rows, loaded up front
     OV rv[RPW];
-    if (EPI == EPI_RESID || EPI == EPI_DRELU2) {
+    if (EPI == EPI_RESID || EPI == EPI_DRELU2 || EPI == EPI_DSQR) {
 #pragma unroll
       for (int k = 0; k < RPW; ++k) {
         const int m = m0 + q * 128 + w + k * (NTHR / 64);
@@ -521,12 +521,20 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
           if (EPI == EPI_RESID) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = (OT)(v[e] + (float)rv[k][e]);
-          } else if (EPI == EPI_DRELU2) {
+          } else if (EPI == EPI_DRELU2 || EPI == EPI_DSQR) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float dv = v[e] * 2.0f * fmaxf((float)rv[k][e], 0.f);
+              const float r = fmaxf((float)rv[k][e], 0.f);
+              const float dv = v[e] * 2.0f * (EPI == EPI_DSQR ? sqrtf(r) : r);
               o[e] = (OT)dv;
               am = fmaxf(am, fabsf(dv));
+            }
+          } else if (EPI == EPI_SQR) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float rl = fmaxf(v[e], 0.f);
+              o[e] = (OT)(rl * rl);
+              am = fmaxf(am, rl * rl);
             }
           } else {
 #pragma unroll
@@ -549,7 +557,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
     }
     if (q == 0) __syncthreads();
   }
-  if constexpr (EPI == EPI_RELU2 || EPI == EPI_DRELU2) {
+  if constexpr (EPI == EPI_RELU2 || EPI == EPI_DRELU2 || EPI == EPI_SQR || EPI == EPI_DSQR) {
     if (p.amax_out) {
       // rounding is monotone: the largest stored value is the rounded largest value
 #pragma unroll
@@ -617,6 +625,8 @@ __global__ __launch_bounds__(256) void gemm_f32_k(GemmArgs p) {
         float* C = (float*)p.C + (size_t)m * p.ldc + n;
         if (EPI == EPI_RESID) *C = ((const float*)p.R)[(size_t)m * p.ldr + n] + v;
         else if (EPI == EPI_DRELU2) *C = v * 2.0f * fmaxf(((const float*)p.R)[(size_t)m * p.ldr + n], 0.f);
+        else if (EPI == EPI_DSQR) *C = v * 2.0f * sqrtf(fmaxf(((const float*)p.R)[(size_t)m * p.ldr + n], 0.f));
+        else if (EPI == EPI_SQR) *C = fmaxf(v, 0.f) * fmaxf(v, 0.f);
         else *C = v;
         if (EPI == EPI_RELU2) {
           const float r = fmaxf(v, 0.f);
@@ -634,6 +644,18 @@ hipError_t launch_bf16(const GemmArgs& a, dim3 g, hipStream_t s) {
     case EPI_RESID: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_RESID, F8, OT>), g, dim3(NTHR), 0, s, a); break;
     case EPI_RELU2: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_RELU2, F8, OT>), g, dim3(NTHR), 0, s, a); break;
     case EPI_DRELU2: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_DRELU2, F8, OT>), g, dim3(NTHR), 0, s, a); break;
+    case EPI_SQR:  // the MLP up-projection: both operands K-major
+      if constexpr (AK && BKM) {
+        hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_SQR, F8, OT>), g, dim3(NTHR), 0, s, a);
+        break;
+      }
+      return hipErrorInvalidValue;
+    case EPI_DSQR:  // the hidden gradient: dout K-major, the weight either way
+      if constexpr (AK) {
+        hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_DSQR, F8, OT>), g, dim3(NTHR), 0, s, a);
+        break;
+      }
+      return hipErrorInvalidValue;
     case EPI_QKNORM:
       if constexpr (AK && BKM && !F8 && std::is_same<OT, bf16>::value) {
         hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_QKNORM, F8, OT>), g, dim3(NTHR), 0, s, a);
@@ -724,6 +746,8 @@ hipError_t gemm(int dt, const GemmArgs& a, hipStream_t s) {
     case EPI_RELU2: hipLaunchKernelGGL(gemm_f32_k<EPI_RELU2>, g, dim3(256), 0, s, a); break;
     case EPI_DRELU2: hipLaunchKernelGGL(gemm_f32_k<EPI_DRELU2>, g, dim3(256), 0, s, a); break;
     case EPI_F32: hipLaunchKernelGGL(gemm_f32_k<EPI_F32>, g, dim3(256), 0, s, a); break;
+    case EPI_SQR: hipLaunchKernelGGL(gemm_f32_k<EPI_SQR>, g, dim3(256), 0, s, a); break;
+    case EPI_DSQR: hipLaunchKernelGGL(gemm_f32_k<EPI_DSQR>, g, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

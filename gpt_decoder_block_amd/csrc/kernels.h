@@ -49,9 +49,12 @@ enum Epi {
   EPI_RELU2 = 2,   // C = acc (u), C2 = relu(acc)^2  (dtype out)
   EPI_DRELU2 = 3,  // C = acc * 2*max(R, 0)          (dtype out, R = saved u)
   EPI_F32 = 4,     // fp32 C (+)= acc (split-K through `partial`)
-  EPI_QKNORM = 5   // bf16, both operands K-major, head_dim 128: the QKV projection
+  EPI_QKNORM = 5,  // bf16, both operands K-major, head_dim 128: the QKV projection
                    // with the QK RMS-norm and RoPE applied to the q and k heads
                    // (columns < qk_heads*128) on the way out; rinv [M, qk_heads]
+  EPI_SQR = 6,     // C = relu(acc)^2 only (the block saves h, not u)
+  EPI_DSQR = 7     // C = acc * 2*sqrt(max(R, 0)), R = saved h = relu(u)^2, so
+                   // 2*sqrt(h) = 2*relu(u) is the ReLU^2 derivative
 };
 struct GemmArgs {
   const void* A; const void* B;
@@ -66,9 +69,9 @@ struct GemmArgs {
   int splits;          // >= 1
   const float* amax_a; // fp8: per-tensor amax of A and B (scales amax/448)
   const float* amax_b;
-  // EPI_RELU2 / EPI_DRELU2: if set, atomically raised to the largest |value|
-  // stored in C2 (ReLU2) or C (DReLU2) -- the next quantiser's amax; the
-  // caller zeroes it first
+  // EPI_RELU2 / EPI_SQR / EPI_DRELU2 / EPI_DSQR: if set, atomically raised to
+  // the largest |value| stored in C2 (ReLU2) or C (the others) -- the next
+  // quantiser's amax; the caller zeroes it first
   float* amax_out;
   // EPI_QKNORM: rope table [T][64][2], row m is position m % T
   const float* rope; float* rinv; int T; int qk_heads; float eps;

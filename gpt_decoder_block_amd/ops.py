@@ -178,7 +178,7 @@ def rmsnorm_bwd(dxn: torch.Tensor, xn: torch.Tensor, r: torch.Tensor, dres, dx: 
            _p(dx), _stream(dxn))
 
 
-EPI_STORE, EPI_RESID, EPI_RELU2, EPI_DRELU2, EPI_F32 = 0, 1, 2, 3, 4
+EPI_STORE, EPI_RESID, EPI_RELU2, EPI_DRELU2, EPI_F32, EPI_SQR, EPI_DSQR = 0, 1, 2, 3, 4, 6, 7
 
 
 def gemm_ws_bytes(dtype: torch.dtype, M: int, N: int, K: int, epi: int) -> int:

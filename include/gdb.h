@@ -260,7 +260,11 @@ gdb_status gdb_rmsnorm_bwd(int32_t N, int32_t C, int32_t dtype, const void* dxn,
 /* GEMM C[m, n] = sum_k A(m, k) B(n, k) with fp32 accumulation (bf16 dtype: MFMA).
  *   A(m, k) = a_kmajor ? A[m*lda + k] : A[k*lda + m];  B(n, k) likewise with ldb.
  *   epi 0: C = acc;  1: C = R + acc;  2: C = acc and C2 = relu(acc)^2;
- *   3: C = acc * 2*max(R, 0);  (C, C2, R in dtype, leading dims ldc, ldr)
+ *   3: C = acc * 2*max(R, 0);  6: C = relu(acc)^2;  7: C = acc * 2*sqrt(max(R, 0))
+ *   (R = relu(u)^2 saved by epi 6, so 2*sqrt(R) = 2*relu(u), the ReLU^2
+ *   derivative; the block keeps h only and uses 6 and 7);
+ *   (C, C2, R in dtype, leading dims ldc, ldr; bf16 epi 6 needs both operands
+ *   K-major and epi 7 A K-major, else GDB_EUNSUPPORTED; 5 is not accepted)
  *   4: C float32 [M, N] with ldc == N, C = acc or C += acc (accumulate); needs
  *      gdb_gemm_ws_bytes of workspace for the split-K partial sums.
  * The bias-free Linear y = x W^T of section "3. Gestion de la précision" is
@@ -288,7 +292,7 @@ gdb_status gdb_fp8_quantize(int32_t R, int32_t Cc, int32_t dtype, const void* x,
 /* GEMM on e4m3 codes, both operands K-contiguous:
  *   C[m, n] = s_a s_b sum_k A[m*lda + k] B[n*ldb + k],  s = amax / 448 of each operand,
  * with fp32 accumulation (v_mfma_f32_32x32x64_f8f6f4) and the epilogues of
- * gdb_gemm: epi 0-3 with C, C2 and R in `dtype`; epi 4 fp32 C (needs
+ * gdb_gemm: epi 0-3, 6 and 7 with C, C2 and R in `dtype`; epi 4 fp32 C (needs
  * gdb_gemm_fp8_ws_bytes of workspace).  K, lda, ldb multiples of 16. */
 gdb_status gdb_gemm_fp8_ws_bytes(int32_t M, int32_t N, int32_t K, int32_t epi, size_t* ws_bytes);
 gdb_status gdb_gemm_fp8(int32_t dtype, int32_t M, int32_t N, int32_t K, const uint8_t* A, int32_t lda,

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle as O
-from gpt_decoder_block_amd import ops
+from gpt_decoder_block_amd import _lib as L, ops
 from gpu_util import DEV, TDT, TOL, assert_close, dev, empty, host, rounded
 
 pytestmark = pytest.mark.gpu
@@ -77,6 +77,37 @@ def test_gemm(dt, ak, bk, epi):
         assert_close(C2, np.maximum(acc, 0) ** 2, dt, "relu2")
     elif epi == 3:
         assert_close(C, acc * 2.0 * np.maximum(R, 0), dt, "relu2 backward")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("ak,bk", [(True, True), (True, False)])
+def test_gemm_square_epilogues(dt, ak, bk):
+    # epi 6: h = relu(acc)^2 alone; epi 7: acc * 2*sqrt(h) with h saved by 6
+    M, N, K = 296, 264, 200
+    A = rounded(RNG.standard_normal((M, K)), dt)
+    B = rounded(RNG.standard_normal((N, K)), dt)
+    acc = A.astype(np.float64) @ B.astype(np.float64).T
+    Ag, Bg = dev(_store(A, ak), dt), dev(_store(B, bk), dt)
+    lda, ldb = (K if ak else M), (K if bk else N)
+    H = rounded(np.maximum(RNG.standard_normal((M, N)), 0) ** 2, dt)
+    C = empty((M, N), dt)
+    if ak and bk:
+        ops.gemm(M, N, K, Ag, ak, lda, Bg, bk, ldb, ops.EPI_SQR, C, N)
+        assert_close(C, np.maximum(acc, 0) ** 2, dt, "relu(acc)^2")
+    ops.gemm(M, N, K, Ag, ak, lda, Bg, bk, ldb, ops.EPI_DSQR, C, N, R=dev(H, dt), ldr=N)
+    assert_close(C, acc * 2.0 * np.sqrt(H), dt, "acc * 2 sqrt(h)")
+
+
+def test_gemm_square_epilogue_layout_rules():
+    # bf16 epi 6 needs both operands K-major, epi 7 a K-major A; 5 is refused
+    a = empty((64, 64), "bf16", fill=0.0)
+    c = empty((64, 64), "bf16")
+    with pytest.raises(L.GdbError, match="epilogue 6"):
+        ops.gemm(64, 64, 64, a, True, 64, a, False, 64, ops.EPI_SQR, c, 64)
+    with pytest.raises(L.GdbError, match="epilogue 7"):
+        ops.gemm(64, 64, 64, a, False, 64, a, True, 64, ops.EPI_DSQR, c, 64, R=c, ldr=64)
+    with pytest.raises(L.GdbError, match="unknown epilogue 5"):
+        ops.gemm(64, 64, 64, a, True, 64, a, True, 64, 5, c, 64)
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -270,7 +301,7 @@ def test_fp8_quantize_zero_tensor():
     assert host(amax)[0] == 0.0 and not torch.any(xq).item()
 
 
-@pytest.mark.parametrize("epi", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("epi", [0, 1, 2, 3, 4, 6, 7])
 @pytest.mark.parametrize("M,N,K", [(300, 264, 160), (64, 520, 1664), (2100, 72, 48), (256, 248, 4096)])
 def test_gemm_fp8(epi, M, N, K):
     # C = q8(A) q8(B)^T with each operand's own per-tensor scale; both sides
@@ -305,5 +336,9 @@ def test_gemm_fp8(epi, M, N, K):
     elif epi == ops.EPI_RELU2:
         assert_close(C, acc, "bf16", "u")
         assert_close(C2, np.maximum(acc, 0) ** 2, "bf16", "h")
+    elif epi == ops.EPI_SQR:
+        assert_close(C, np.maximum(acc, 0) ** 2, "bf16", "h")
+    elif epi == ops.EPI_DSQR:
+        assert_close(C, acc * 2 * np.sqrt(np.maximum(r, 0)), "bf16", "du")
     else:
         assert_close(C, acc * 2 * np.maximum(r, 0), "bf16", "du")
