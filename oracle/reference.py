@@ -329,6 +329,9 @@ def block_backward(dout: np.ndarray, c: dict, p: Dict[str, np.ndarray], cfg, l: 
         ds = dgate * 3.0 * sg * (1.0 - sg)
         nch = cfg.ve_gate_channels
         g["ve_gate"] = np.einsum("bth,btc->hc", ds, c["xn1"][..., :nch])
+        # per element, the sum over tokens of the summed terms' magnitudes (the
+        # scale of that sum's forward error bound)
+        ve_gate_sum_abs = np.einsum("bth,btc->hc", np.abs(ds), np.abs(c["xn1"][..., :nch]))
         dxe = np.zeros_like(c["xn1"])
         dxe[..., :nch] = ds @ p["ve_gate"]
         dxn1_extra = dxe
@@ -346,6 +349,8 @@ def block_backward(dout: np.ndarray, c: dict, p: Dict[str, np.ndarray], cfg, l: 
         # error bound of each of these two sums
         g["sum_abs"] = {"resid_lambda": np.sum(np.abs(dx * c["x_premix"])),
                         "x0_lambda": np.sum(np.abs(dx * c["x0"]))}
+        if "ve" in p:
+            g["sum_abs"]["ve_gate"] = ve_gate_sum_abs
         g["x0"] = p["x0_lambda"] * dx
         dx = p["resid_lambda"] * dx
     return dx, g

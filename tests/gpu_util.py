@@ -41,6 +41,21 @@ def assert_close(gpu, ref, dt: str, what: str = "", tol: float = None):
     return e
 
 
+def sum_close(gpu, ref, sum_abs, dt: str, what: str = "", tol: float = None):
+    """A gradient that is a sum over tokens with cancellation (the value
+    embedding gate's): the plain relative bar, or in bf16 the forward error
+    bound of each element's sum, |gpu - ref| <= TOL * sum|terms| with the
+    oracle's sum of the terms' magnitudes.  Returns the smaller normalised error."""
+    e = rel_err(gpu, ref)
+    bar = TOL[dt] if tol is None else tol
+    if e <= bar:
+        return e
+    g = host(gpu) if isinstance(gpu, torch.Tensor) else np.asarray(gpu, dtype=np.float64)
+    eb = float(np.max(np.abs(g - np.asarray(ref)) / np.maximum(np.asarray(sum_abs, dtype=np.float64), 1e-300)))
+    assert dt == "bf16" and eb <= TOL[dt], f"{what}: max rel err {e:.3e} > {bar:.1e} and err/sum|terms| {eb:.3e}"
+    return eb
+
+
 def empty(shape, dt, fill=None):
     t = torch.empty(shape, dtype=TDT[dt] if isinstance(dt, str) else dt, device=DEV)
     if fill is not None:

@@ -9,7 +9,7 @@ import torch
 import oracle as O
 from gpt_decoder_block_amd import ops
 from gpt_decoder_block_amd.stack import DecoderStack
-from gpu_util import (DEV, TDT, TOL, assert_close, dev, empty, fp8_alternative, fp8_alternatives, fp8_bars,
+from gpu_util import (DEV, TDT, TOL, assert_close, dev, empty, fp8_alternative, fp8_alternatives, fp8_bars, sum_close,
                       host, rounded)
 from seeded_inputs import draw_all, draw_ids, draw_layer, draw_upstream, workload
 
@@ -155,8 +155,8 @@ def _stack_case(w):
             gl = g["layers"][l]
             if st.ve_layers[l]:
                 errs[f"{l}.ve"] = assert_close(st.dve[l], gl["ve"], dt, f"layer {l} dve", bars.get(f"{l}.ve"))
-                errs[f"{l}.ve_gate"] = assert_close(st.dve_gate[l], gl["ve_gate"], dt, f"layer {l} dve_gate",
-                                                    bars.get(f"{l}.ve_gate"))
+                errs[f"{l}.ve_gate"] = sum_close(st.dve_gate[l], gl["ve_gate"], gl["sum_abs"]["ve_gate"], dt,
+                                                 f"layer {l} dve_gate", bars.get(f"{l}.ve_gate"))
     if w.extras:
         # The residual, smear and backout scalars' gradients are sums over all
         # B*T*C activations with heavy cancellation (the sum of the terms'
@@ -274,7 +274,7 @@ def _block_extras_case(w, l, B, T):
         errs[name] = assert_close(t, g[name], dt, "d" + name, bars.get(name))
     if has_ve:
         errs["ve"] = assert_close(dve, g["ve"], dt, "dve", bars.get("ve"))
-        errs["ve_gate"] = assert_close(dvg, g["ve_gate"], dt, "dve_gate", bars.get("ve_gate"))
+        errs["ve_gate"] = sum_close(dvg, g["ve_gate"], g["sum_abs"]["ve_gate"], dt, "dve_gate", bars.get("ve_gate"))
     print(f"block+extras {w.name} l={l} B={B} T={T} ve={has_ve} fp8={w.mlp_fp8} errs={errs}", flush=True)
 
 
