@@ -100,19 +100,23 @@ struct Loader {
       kend_rel = kend - kbeg;
     }
   }
-  __device__ __forceinline__ void load(int kt) {
-    // invalid vectors get an offset >= 0xFFFFFFF0 (past any resource size):
-    // an OR with an all-ones mask, so the compiler cannot turn it into a branch
+  // vector i (0..7) of K step kt.  Invalid vectors get an offset >=
+  // 0xFFFFFFF0 (past any resource size): an OR with an all-ones mask, so the
+  // compiler cannot turn it into a branch
+  __device__ __forceinline__ void load1(int kt, int i) {
     unsigned bad;
     if (KMAJ) bad = 0u - (unsigned)(kt * BKE + kcol >= kend_rel);
     else bad = 0u - (unsigned)(off0 == OOB);
     const unsigned o = (off0 + kt * step) | (bad & OOB);
+    r[i] = bload(rs, (o + i * rowstep) | (bad & OOB));
+  }
+  __device__ __forceinline__ void load(int kt) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = bload(rs, (o + i * rowstep) | (bad & OOB));
+    for (int i = 0; i < 8; ++i) load1(kt, i);
   }
   __device__ __forceinline__ void store(bf16* __restrict__ S) {
     const int t = threadIdx.x;
-    if (KMAJ) {
+    if constexpr (KMAJ) {
       const int c = t & 7, rr = t >> 3;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -120,16 +124,21 @@ struct Loader {
         *(bf16x8*)(S + row * BK + ((c ^ swz(row)) * 8)) = r[i];
       }
     } else {
-      const int mc = t & 31, kb = t >> 5;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        bf16x8 w;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = r[i][j];
-        const int row = mc * 8 + j;
-        *(bf16x8*)(S + row * BK + ((kb ^ swz(row)) * 8)) = w;
-      }
+      for (int j = 0; j < 8; ++j) store1(S, j);
     }
+  }
+  // M-major operand: the LDS row j of this thread's 8x8 block (column j of
+  // the eight loaded vectors)
+  __device__ __forceinline__ void store1(bf16* __restrict__ S, int j) {
+    static_assert(!KMAJ, "K-major operands are stored whole");
+    const int t = threadIdx.x;
+    const int mc = t & 31, kb = t >> 5;
+    bf16x8 w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = r[i][j];
+    const int row = mc * 8 + j;
+    *(bf16x8*)(S + row * BK + ((kb ^ swz(row)) * 8)) = w;
   }
 };
 
@@ -162,14 +171,17 @@ struct DmaLoader {
     }
     kend_rel = kend - kbeg;
   }
+  // copy i (0..7) of K step kt into stage S
+  __device__ __forceinline__ void load1(int kt, bf16* S, int i) {
+    // wave-uniform, so the LDS destination (M0) is computed on the scalar unit
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const unsigned bad = 0u - (unsigned)(kt * BKE + kc[i] >= kend_rel);
+    const unsigned o = (off[i] + kt * 128) | (bad & OOB);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(S + (i * 4 + w) * 8 * BK), 16, o, 0, 0, 0);
+  }
   __device__ __forceinline__ void load(int kt, bf16* S) {
-    const int w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const unsigned bad = 0u - (unsigned)(kt * BKE + kc[i] >= kend_rel);
-      const unsigned o = (off[i] + kt * 128) | (bad & OOB);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(S + (i * 4 + w) * 8 * BK), 16, o, 0, 0, 0);
-    }
+    for (int i = 0; i < 8; ++i) load1(kt, S, i);
   }
 };
 
@@ -299,94 +311,94 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
       __syncthreads();
       load_frags8(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
     }
-  } else if constexpr (AK || BK_) {
-    // K-contiguous operands are copied straight into LDS; an M-contiguous one
-    // goes through registers (transposed on the way)
+  } else {
+    // bf16: a K-contiguous operand is copied straight into LDS (DMA); an
+    // M/N-contiguous one is loaded into registers and stored transposed.
+    // Per K step: the first 16-wide sub-step's MFMAs are interleaved one to
+    // one with the 16 copies (or register loads) of the next step and two to
+    // one with the second sub-step's fragment reads; the last sub-step's
+    // MFMAs with the transposed LDS stores of the next step.  The order is
+    // pinned with scheduling barriers.
     DmaLoader<2> da, db;
     if constexpr (AK) da.init(p.A, p.lda, p.M, m0, kbeg, kend);
     if constexpr (BK_) db.init(p.B, p.ldb, p.N, n0, kbeg, kend);
-    auto issue = [&](int kt, int stg) {
-      if constexpr (AK) da.load(kt, smem[stg][0]); else la.load(kt);
-      if constexpr (BK_) db.load(kt, smem[stg][1]); else lb.load(kt);
+    auto issue1 = [&](int kt, int stg, int q) {
+      if (q < 8) {
+        if constexpr (AK) da.load1(kt, smem[stg][0], q);
+        else la.load1(kt, q);
+      } else {
+        if constexpr (BK_) db.load1(kt, smem[stg][1], q - 8);
+        else lb.load1(kt, q - 8);
+      }
     };
-    auto commit = [&](int stg) {
-      if constexpr (!AK) la.store(smem[stg][0]);
-      if constexpr (!BK_) lb.store(smem[stg][1]);
+    auto store1 = [&](int stg, int q) {
+      if (q < 8) {
+        if constexpr (!AK) la.store1(smem[stg][0], q);
+      } else {
+        if constexpr (!BK_) lb.store1(smem[stg][1], q - 8);
+      }
     };
-    issue(0, 0);
-    commit(0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) issue1(0, 0, q);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) store1(0, q);
     WAIT_VM0();
     __syncthreads();
     bf16x8 af[2][4], bfr[2][4];
     load_frags(smem[0][0], smem[0][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
     for (int kt = 0; kt < nk; ++kt) {
       const int st = kt & 1;
-      issue(kt + 1, st ^ 1);
-      __builtin_amdgcn_sched_barrier(0);
       const bf16* As = smem[st][0];
       const bf16* Bs = smem[st][1];
+      // sub-step 0 (fragments in set 0)
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
+      for (int q = 0; q < 16; ++q) {
+        const int i = q >> 2, j = q & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[0][j], af[0][i], acc[i][j], 0, 0, 0);
+        issue1(kt + 1, st ^ 1, q);
+        if (q & 1) {
+          const int r = q >> 1;  // fragment r of sub-step 1: A blocks 0-3, then B blocks 0-3
+          const int ch = 2 + lh;
+          if (r < 4) {
+            const int row = wm * 128 + r * 32 + lr;
+            af[1][r] = *(const bf16x8*)(As + row * BK + ((ch ^ swz(row)) * 8));
+          } else {
+            const int row = wn * 128 + (r - 4) * 32 + lr;
+            bfr[1][r - 4] = *(const bf16x8*)(Bs + row * BK + ((ch ^ swz(row)) * 8));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // sub-steps 1 and 2
+#pragma unroll
+      for (int kk = 1; kk < BK / 16 - 1; ++kk) {
         const int cb = kk & 1;
-        if (kk + 1 < BK / 16) load_frags(As, Bs, kk + 1, wm, wn, lr, lh, af[cb ^ 1], bfr[cb ^ 1]);
+        load_frags(As, Bs, kk + 1, wm, wn, lr, lh, af[cb ^ 1], bfr[cb ^ 1]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
-        if (kk + 1 < BK / 16) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-        }
-      }
-      commit(st ^ 1);
-      WAIT_VM0();
-      __syncthreads();
-      load_frags(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
-    }
-  } else {
-  la.load(0);
-  lb.load(0);
-  la.store(smem[0][0]);
-  lb.store(smem[0][1]);
-  __syncthreads();
-  bf16x8 af[2][4], bfr[2][4];
-  load_frags(smem[0][0], smem[0][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    // next tile (zeros past the end: harmless, the stage it lands in is not read)
-    la.load(kt + 1);
-    lb.load(kt + 1);
-    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch at the top of the step
-    const bf16* As = smem[st][0];
-    const bf16* Bs = smem[st][1];
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int cb = kk & 1;
-      if (kk + 1 < BK / 16) load_frags(As, Bs, kk + 1, wm, wn, lr, lh, af[cb ^ 1], bfr[cb ^ 1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
-      if (kk + 1 < BK / 16) {
-        // interleave the next sub-step's 8 LDS reads among the 16 MFMAs
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      // sub-step 3 (set 1), with the transposed stores of the next step's
+      // register-loaded operands (their stage was last read in step kt-1)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int i = q >> 2, j = q & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[1][j], af[1][i], acc[i][j], 0, 0, 0);
+        store1(st ^ 1, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      WAIT_VM0();
+      __syncthreads();
+      load_frags(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
     }
-    la.store(smem[st ^ 1][0]);
-    lb.store(smem[st ^ 1][1]);
-    __syncthreads();
-    load_frags(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
-  }
   }
   // fp8: both per-tensor scales (amax / 448, the quantiser's float32 values)
   float oscale = 1.0f;
@@ -525,7 +537,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float r = fmaxf((float)rv[k][e], 0.f);
-              const float dv = v[e] * 2.0f * (EPI == EPI_DSQR ? sqrtf(r) : r);
+              const float dv = v[e] * 2.0f * (EPI == EPI_DSQR ? __builtin_amdgcn_sqrtf(r) : r);  // v_sqrt_f32 (1 ulp)
               o[e] = (OT)dv;
               am = fmaxf(am, fabsf(dv));
             }
