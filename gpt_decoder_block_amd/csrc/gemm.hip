@@ -284,29 +284,31 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
     load_frags8(smem[0][0], smem[0][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
     for (int kt = 0; kt < nk; ++kt) {
       const int st = kt & 1;
-      da.load(kt + 1, smem[st ^ 1][0]);
-      db.load(kt + 1, smem[st ^ 1][1]);
-      __builtin_amdgcn_sched_barrier(0);
       const bf16* As = smem[st][0];
       const bf16* Bs = smem[st][1];
+      // first sub-step: each MFMA followed by one of the next step's 16
+      // copies and one of the second sub-step's 16 chunk reads (fixed order)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if (kk == 0) load_frags8(As, Bs, 1, wm, wn, lr, lh, af[1], bfr[1]);
+      for (int q = 0; q < 16; ++q) {
+        const int i = q >> 2, j = q & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[0][j], af[0][i], acc[i][j], 0, 0, 0, 0, 0, 0);
+        if (q < 8) da.load1(kt + 1, smem[st ^ 1][0], q);
+        else db.load1(kt + 1, smem[st ^ 1][1], q - 8);
+        // chunk h of fragment r (A blocks 0-3, then B blocks 0-3) of sub-step 1
+        const int r = q >> 1, h = q & 1, ch = 4 + lh * 2 + h;
+        const bool isa = r < 4;
+        const int row = isa ? wm * 128 + r * 32 + lr : wn * 128 + (r - 4) * 32 + lr;
+        const u32x4 v = *(const u32x4*)((isa ? As : Bs) + row * BK + ((ch ^ swz(row)) * 8));
+        i32x8& dst = isa ? af[1][r & 3] : bfr[1][r & 3];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[kk][j], af[kk][i], acc[i][j], 0, 0, 0, 0,
-                                                                       0, 0);
-        if (kk == 0) {
-          // interleave the second sub-step's 16 LDS reads among the 16 MFMAs
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-        }
+        for (int e = 0; e < 4; ++e) dst[4 * h + e] = (int)v[e];
+        __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[1][j], af[1][i], acc[i][j], 0, 0, 0, 0, 0, 0);
       WAIT_VM0();
       __syncthreads();
       load_frags8(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
