@@ -414,6 +414,47 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
   float* stage = (float*)&smem[0][0][0];
   const int ncols = min(BN, p.N - n0);
   float am = 0.f;  // largest |value| this thread stores into the quantiser's input (amax_out)
+  if constexpr ((EPI == EPI_STORE || EPI == EPI_SQR) && std::is_same<OT, bf16>::value) {
+    // bf16 output with nothing to add: the values are finished in registers
+    // and the whole 256x256 tile is staged once as bf16 (128 KiB).  A row is
+    // 64 slots of 8 bytes (4 columns); slot s of row r sits at s ^ (r & 31),
+    // so the 32 rows of a half-wave's write and the 64 slots of a row read
+    // each hit distinct bank pairs.
+    bf16* sb = &smem[0][0][0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + i * 32 + lr;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float v = acc[i][j][4 * g + e];
+            if constexpr (F8) v *= oscale;
+            if constexpr (EPI == EPI_SQR) {
+              const float rl = fmaxf(v, 0.f);
+              v = rl * rl;
+              am = fmaxf(am, v);
+            }
+            o[e] = (bf16)v;
+          }
+          const int slot = wn * 32 + j * 8 + 2 * g + lh;
+          *(bf16x4*)(sb + r * 256 + ((slot ^ (r & 31)) << 2)) = o;
+        }
+    }
+    __syncthreads();
+    const bool cok = 4 * lane < ncols;
+#pragma unroll 8
+    for (int k = 0; k < BM / (NTHR / 64); ++k) {
+      const int r = k * (NTHR / 64) + w;
+      const int m = m0 + r;
+      if (cok && m < p.M)
+        *(bf16x4*)((bf16*)p.C + (size_t)m * p.ldc + n0 + 4 * lane) =
+            *(const bf16x4*)(sb + r * 256 + ((lane ^ (r & 31)) << 2));
+    }
+  } else {
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     if (wm == q) {
@@ -570,6 +611,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_k(GemmArgs p) {
     }
     }
     if (q == 0) __syncthreads();
+  }
   }
   if constexpr (EPI == EPI_RELU2 || EPI == EPI_DRELU2 || EPI == EPI_SQR || EPI == EPI_DSQR) {
     if (p.amax_out) {
