@@ -447,8 +447,14 @@ gdb_status gdb_block_bwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
   at.B = d.B; at.T = d.T; at.H = d.H; at.Hkv = d.Hkv; at.D = d.D; at.window = d.window;
   at.qkv = sv.qkvh; at.ld = d.W3; at.o = sv.o; at.ldo = d.Q; at.lse = sv.lse;
   at.dout = wb.dout; at.lddo = d.Q; at.dqkv = wb.dqkv; at.lddq = d.W3; at.delta = wb.delta;
-  HIPCHK(attn_bwd(dt, at, s));
-  HIPCHK(qk_norm_rope_bwd(dt, wb.dqkv, sv.qkvh, sv.rqk, rope_tab, d.B, d.T, d.H, d.Hkv, d.D, s));
+  if (dt == BF16) {
+    // the QK RMS-norm and RoPE backward happen in the dQ and dK epilogues
+    at.rope = rope_tab; at.rinv = sv.rqk;
+    HIPCHK(attn_bwd(dt, at, s));
+  } else {
+    HIPCHK(attn_bwd(dt, at, s));
+    HIPCHK(qk_norm_rope_bwd(dt, wb.dqkv, sv.qkvh, sv.rqk, rope_tab, d.B, d.T, d.H, d.Hkv, d.D, s));
+  }
   // value embeddings: gate-logit gradients and the table's rows (dv passes through unchanged)
   if (xe.ve) {
     if (!acc) HIPCHK(fill_f32(dex->dve, (size_t)ex->ve_vocab * d.KV, 0.f, s));

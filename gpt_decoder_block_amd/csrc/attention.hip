@@ -399,6 +399,48 @@ __global__ __launch_bounds__(256) void attn_delta_k(AttnArgs a) {
   }
 }
 
+// Backward of y = rope(rms(x)) for one head row held by a lane pair (lh = 0,
+// 1), in the accumulator layout of the backward kernels: register 4gq + e of
+// block db is d = 32db + 8gq + 4lh + e.  g = gscale * acc is dL/dy; with
+// m = (g . y) / D, u = g - m y (the radial part removed), dL/dx is the inverse
+// rotation of u times rinv.  Rotary pair (j, j + 64) is (block db, block
+// db + 2) of the same lane.  y is the saved row, cs the (cos, sin) row of the
+// position; the result goes to out at the same d.
+__device__ __forceinline__ void qknorm_rope_bwd_row(const f32x16 (&acc)[4], float gscale, const bf16* __restrict__ y,
+                                                    float rinv, const float* __restrict__ cs, int lh,
+                                                    bf16* __restrict__ out) {
+  bf16x4 yv[4][4];
+  float dot = 0.f;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      yv[db][gq] = *(const bf16x4*)(y + db * 32 + 8 * gq + 4 * lh);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot += acc[db][4 * gq + e] * gscale * (float)yv[db][gq][e];
+    }
+  dot += __shfl_xor(dot, 32, 64);
+  const float m = dot * (1.0f / HD);
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int j0 = db * 32 + 8 * gq + 4 * lh;
+      const f32x4 c0 = *(const f32x4*)(cs + 2 * j0), c1 = *(const f32x4*)(cs + 2 * j0 + 4);
+      const float c[4] = {c0[0], c0[2], c1[0], c1[2]}, sn[4] = {c0[1], c0[3], c1[1], c1[3]};
+      bf16x4 oa, ob;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ua = acc[db][4 * gq + e] * gscale - (float)yv[db][gq][e] * m;
+        const float ub = acc[db + 2][4 * gq + e] * gscale - (float)yv[db + 2][gq][e] * m;
+        oa[e] = (bf16)(rinv * (ua * c[e] + ub * sn[e]));
+        ob[e] = (bf16)(rinv * (-ua * sn[e] + ub * c[e]));
+      }
+      *(bf16x4*)(out + j0) = oa;
+      *(bf16x4*)(out + j0 + 64) = ob;
+    }
+}
+
 // ------------------------------------------------------ backward: dK, dV
 // Workgroup: 32*NW keys of one (b, kv head), 32 per wave (lane = key); with
 // NW = 8 two waves share each SIMD, so one wave's exp/convert work overlaps
@@ -523,12 +565,17 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_bf16_k(AttnArgs a, float
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int d = db * 32 + 8 * gq + 4 * lh;
-        *(bf16x4*)(row + (H + g) * HD + d) =
-            bf16x4{(bf16)(dk[db][4 * gq] * scale), (bf16)(dk[db][4 * gq + 1] * scale),
-                   (bf16)(dk[db][4 * gq + 2] * scale), (bf16)(dk[db][4 * gq + 3] * scale)};
+        if (!a.rope)
+          *(bf16x4*)(row + (H + g) * HD + d) =
+              bf16x4{(bf16)(dk[db][4 * gq] * scale), (bf16)(dk[db][4 * gq + 1] * scale),
+                     (bf16)(dk[db][4 * gq + 2] * scale), (bf16)(dk[db][4 * gq + 3] * scale)};
         *(bf16x4*)(row + (H + Hkv + g) * HD + d) =
             bf16x4{(bf16)dv[db][4 * gq], (bf16)dv[db][4 * gq + 1], (bf16)dv[db][4 * gq + 2], (bf16)dv[db][4 * gq + 3]};
       }
+    if (a.rope)
+      qknorm_rope_bwd_row(dk, scale, base + (size_t)kj * a.ld + (H + g) * HD,
+                          a.rinv[((size_t)b * T + kj) * (H + Hkv) + H + g], a.rope + (size_t)kj * HD, lh,
+                          row + (H + g) * HD);
   }
 }
 
@@ -644,14 +691,19 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_k(AttnArgs a, float 
   }
   if (qi < T) {
     bf16* row = (bf16*)a.dqkv + ((size_t)b * T + qi) * a.lddq + h * HD;
+    if (a.rope) {
+      qknorm_rope_bwd_row(dq, scale, base + (size_t)qi * a.ld + h * HD,
+                          a.rinv[((size_t)b * T + qi) * (H + Hkv) + h], a.rope + (size_t)qi * HD, lh, row);
+    } else {
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d = db * 32 + 8 * gq + 4 * lh;
-        *(bf16x4*)(row + d) = bf16x4{(bf16)(dq[db][4 * gq] * scale), (bf16)(dq[db][4 * gq + 1] * scale),
-                                     (bf16)(dq[db][4 * gq + 2] * scale), (bf16)(dq[db][4 * gq + 3] * scale)};
-      }
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d = db * 32 + 8 * gq + 4 * lh;
+          *(bf16x4*)(row + d) = bf16x4{(bf16)(dq[db][4 * gq] * scale), (bf16)(dq[db][4 * gq + 1] * scale),
+                                       (bf16)(dq[db][4 * gq + 2] * scale), (bf16)(dq[db][4 * gq + 3] * scale)};
+        }
+    }
   }
 }
 

@@ -110,6 +110,10 @@ struct AttnArgs {
   void* dqkv; int lddq;           // dq^, dk^, dv written at the same offsets
   float* delta;                   // [B, H, T] scratch: rowsum(dO * O)
   float* dq_acc;                  // fp32 scratch [N, H*D] (fp32 path)
+  // bf16 backward: if rope is set, dq and dk are taken back through the QK
+  // RMS-norm and RoPE on the way out (gradients w.r.t. the raw q, k); rope
+  // [T][D/2][2] (cos, sin), rinv [B*T, H + Hkv] of the forward
+  const float* rope; const float* rinv;
 };
 hipError_t attn_fwd(int dt, const AttnArgs& a, hipStream_t s);
 hipError_t attn_bwd(int dt, const AttnArgs& a, hipStream_t s);
