@@ -142,6 +142,9 @@ __device__ __forceinline__ bool visible(int i, int j, int T, int W) {
 
 // wait until at most N vector-memory operations of this wave are in flight
 #define WAIT_VM(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
+// workgroup barrier that waits for this wave's LDS accesses but leaves its
+// copies into LDS in flight (__syncthreads waits for every one: vmcnt(0))
+#define LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
 // ----------------------------------------------------------------- forward
 // Workgroup: 32*IB*NW query rows of one (b, h); wave w owns IB blocks of 32
@@ -680,7 +683,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_k(AttnArgs a, float 
     } else {
       WAIT_VM(0);
     }
-    __syncthreads();
+    LDS_BARRIER();
   };
   for (int it = 0; it < ntile; it += NS) {
     tile_step(it, std::integral_constant<int, 0>{});
