@@ -1,6 +1,6 @@
 """Seeded synthetic workloads for the decoder-block training step.
 
-This module describes the five workload shapes and draws their random inputs
+This module describes the workload shapes and draws their random inputs
 (token ids, weight matrices, per-layer scalars).  It is the only code shared by
 the HIP path (via tests and bench) and the CPU oracle, and it holds none of the
 method's arithmetic: it only draws numbers and rounds them to the storage dtype.
@@ -9,7 +9,8 @@ Shapes follow the decoder described in "nanochat: обучи GPT-2 уровня 
 and "Comment Entraîner Votre Propre ChatGPT Pour 50€ ?" (section "1. Le modèle
 GPT": RoPE, QK norm, untied embedding/lm_head, ReLU² MLP, GQA, sliding window),
 at the depths the pages train (d12 trial runs, the d24 leaderboard run and the
-d26 fp8 run).  Every weight matrix is drawn N(0, 0.02^2); per-layer scalars of
+d26 fp8 run), plus the d24 record run's own model (the sliding-window pattern
+"SSSL" of section "1. Le modèle GPT" with every extra).  Every weight matrix is drawn N(0, 0.02^2); per-layer scalars of
 the d26 extras are drawn U(0.5, 1.5); token ids are uniform over the vocabulary.
 
 Each tensor has its own random stream keyed by (seed, tensor kind, layer), so a
@@ -25,7 +26,7 @@ from typing import Dict, Optional, Tuple
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "workload", "draw_ids", "draw_layer",
-           "draw_globals", "draw_all", "to_dtype", "draw_normal", "draw_ids_zipf"]
+           "draw_globals", "draw_all", "to_dtype", "draw_normal", "draw_ids_zipf", "sssl_windows"]
 
 # stream ids for SeedSequence keys
 _K_IDS, _K_WTE, _K_WLM, _K_QKV, _K_O, _K_FC, _K_PROJ = 1, 2, 3, 4, 5, 6, 7
@@ -74,6 +75,13 @@ def _alt_windows(n_layer: int, w: int) -> Tuple[int, ...]:
     return tuple(w if (l % 2 == 1) else -1 for l in range(n_layer))
 
 
+def sssl_windows(n_layer: int, short: int) -> Tuple[int, ...]:
+    """The repeating short-short-short-long layer pattern: layers l with
+    l % 4 < 3 get the short window, every fourth layer and the last one full
+    causal attention (the long context equals T here)."""
+    return tuple(-1 if (l % 4 == 3 or l == n_layer - 1) else short for l in range(n_layer))
+
+
 WORKLOADS: Dict[str, Workload] = {
     "tiny": Workload("tiny", 1, 1, 64, 128, 2, 1, 64, 512, 512, (-1,), "f32", 1001),
     "d12": Workload("d12", 12, 16, 2048, 768, 6, 6, 128, 3072, 32768,
@@ -84,6 +92,10 @@ WORKLOADS: Dict[str, Workload] = {
                     _alt_windows(24, 1024), "bf16", 1004),
     "d26": Workload("d26", 26, 16, 2048, 1664, 13, 13, 128, 6656, 32768,
                     (-1,) * 26, "bf16", 1005, extras=True, mlp_fp8=True),
+    # the d24 record run's model: SSSL windows (short 1024, long = T), value
+    # embeddings on alternating layers, residual mixing, smear and backout, bf16
+    "d24_record": Workload("d24_record", 24, 16, 2048, 1536, 12, 12, 128, 6144, 32768,
+                           sssl_windows(24, 1024), "bf16", 1006, extras=True),
 }
 
 

@@ -11,7 +11,7 @@ from gpt_decoder_block_amd import ops
 from gpt_decoder_block_amd.stack import DecoderStack
 from gpu_util import (DEV, TDT, TOL, assert_close, dev, empty, fp8_alternative, fp8_alternatives, fp8_bars, sum_close,
                       host, rounded)
-from seeded_inputs import draw_all, draw_ids, draw_layer, draw_upstream, workload
+from seeded_inputs import draw_all, draw_ids, draw_layer, draw_upstream, sssl_windows, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -294,6 +294,14 @@ def test_block_extras_tiny_fp32(l):
 
 def test_stack_extras_tiny_fp32():
     _stack_case(workload("tiny").with_(n_layer=4, windows=(-1,) * 4, extras=True))
+
+
+def test_stack_d24_record_pattern():
+    # the d24 record model at d24 widths: SSSL windows (short window 40 at
+    # T=130, so the window edge falls inside tiles), value embeddings on odd
+    # layers, residual mixing, smear and backout, bf16
+    w = workload("d24_record")
+    _stack_case(w.with_(n_layer=4, B=1, T=130, vocab=512, windows=sssl_windows(4, 40)))
 
 
 def test_stack_extras_d26_four_layers():

@@ -5,7 +5,7 @@ import pytest
 
 from gpt_decoder_block_amd.workmodel import (attn_pairs, flops_per_token, flops_per_token_pages,
                                              matrix_params, step_flops)
-from seeded_inputs import workload
+from seeded_inputs import sssl_windows, workload
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "d24_run_summary.txt")
 
@@ -51,3 +51,14 @@ def test_d24_algorithmic_flops():
     assert per_tok == 4775491584
     sf = step_flops(w)
     assert sf["total"] == pytest.approx(per_tok * w.B * w.T, rel=1e-15)
+
+
+def test_d24_record_workload_is_the_pinned_run():
+    # the d24 record workload carries the window pattern whose FLOP count
+    # reproduces the pages' printed total above, and the extras
+    w = workload("d24_record")
+    assert list(w.windows) == [1024 if (l % 4) != 3 else -1 for l in range(24)]
+    assert w.extras and not w.mlp_fp8 and w.dtype == "bf16"
+    assert (w.n_layer, w.C, w.n_head, w.n_kv_head, w.mlp_hidden, w.vocab) == (24, 1536, 12, 12, 6144, 32768)
+    # the pattern ends on a long layer whatever the depth
+    assert sssl_windows(6, 64) == (64, 64, 64, -1, 64, -1)
