@@ -18,6 +18,8 @@ Sources (page title, then section):
   [JA] the same article on dev.to (Japanese), section "1. GPTモデル".
   [ZH] "nanochat：仅需73美元，3小时训练GPT-2级别大语言模型", section "排行榜"
        (the d24 run: batch 16 per device, sequence 2048).
+  [FR] section "6. Moteur d'inférence": generation against a prefilled KV
+       cache (`attention_decode`).
 
 Readings taken where the pages are silent (each listed in the design doc):
   * pre-norm blocks x += Attn(rms(x)); x += MLP(rms(x)); final rms before the
@@ -44,7 +46,9 @@ GQA equals MHA on repeated K/V; causality under perturbation; the whole
 forward/backward against torch float64 autograd on library primitives
 (F.rms_norm, F.linear, F.scaled_dot_product_attention, F.cross_entropy);
 cross-entropy closed form at W_lm = 0; the e4m3 quantiser against torch's
-float8_e4m3fn cast.  Parity with nanochat's own numerics is unpinned: the
+float8_e4m3fn cast; decode attention against torch's scaled_dot_product_attention
+with an explicit mask, the last row of `attention`, and the uniform-weight and
+single-key closed forms.  Parity with nanochat's own numerics is unpinned: the
 pages print no forward or backward value.
 """
 from __future__ import annotations
@@ -56,7 +60,8 @@ import numpy as np
 
 __all__ = [
     "rms_norm", "rms_norm_backward", "rope_tables", "rope", "rope_backward",
-    "visible_mask", "attention", "attention_logsumexp", "attention_backward", "cross_entropy", "e4m3_round",
+    "visible_mask", "attention", "attention_logsumexp", "attention_backward", "attention_decode",
+    "cross_entropy", "e4m3_round",
     "bf16_round", "fp8_quantize", "fp8_quant_dequant", "block_forward", "block_backward", "lm_head_ce",
     "embed_forward", "embed_backward", "smear_forward", "smear_backward",
     "stack_forward_backward", "FP8_E4M3_MAX",
@@ -158,6 +163,37 @@ def attention_logsumexp(q: np.ndarray, k: np.ndarray, window: int) -> np.ndarray
             m = s.max(axis=1)
             out[b, h] = m + np.log(np.sum(np.exp(s - m[:, None]), axis=1))
     return out
+
+
+def attention_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, lens: np.ndarray, window: int
+                     ) -> Tuple[np.ndarray, np.ndarray]:
+    """One generation step against a key/value cache ([FR] section "6. Moteur
+    d'inférence": the prompt is prefilled into a KV cache, then each new token
+    attends to it).  q [B, H, D] is the query of position i = lens[b] - 1 of
+    sequence b; k, v [B, Tmax, Hkv, D] hold positions 0 .. lens[b] - 1 (the new
+    token's own key and value included).  Key j is visible iff j <= i and
+    (window < 0 or i - j <= window) -- the rule of `attention`, for its last
+    row.  Scale 1/sqrt(D); query head h reads K/V head h // (H / Hkv).
+    Returns o [B, H, D] and lse [B, H] (natural log of the softmax
+    denominator).  A length of 0 gives o = 0 and lse = -inf."""
+    B, H, D = q.shape
+    Hkv = k.shape[2]
+    o = np.zeros((B, H, D))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        L = int(lens[b])
+        if L <= 0:
+            continue
+        i = L - 1
+        lo = max(0, i - window) if window >= 0 else 0
+        for h in range(H):
+            g = _kv_head(h, H, Hkv)
+            s = (k[b, lo:L, g, :] @ q[b, h, :]) / math.sqrt(D)
+            m = s.max()
+            e = np.exp(s - m)
+            o[b, h] = (e / e.sum()) @ v[b, lo:L, g, :]
+            lse[b, h] = m + math.log(e.sum())
+    return o, lse
 
 
 def attention_backward(do: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray,

@@ -72,3 +72,33 @@ def test_pins_catch_mutant(monkeypatch, name, fn):
     monkeypatch.setattr(R, name, fn)
     with pytest.raises(AssertionError):
         _compare(cfg, ids, glob, layers)
+
+
+# decode attention: each mutant must fail the torch SDPA pin
+_orig_decode = R.attention_decode
+
+
+def _mut_decode_window(q, k, v, lens, window):   # window lower bound off by one
+    return _orig_decode(q, k, v, lens, window + 1 if window >= 0 else window)
+
+
+def _mut_decode_scale(q, k, v, lens, window):    # softmax scale 1/D instead of 1/sqrt(D)
+    return _orig_decode(q / np.sqrt(q.shape[-1]), k, v, lens, window)
+
+
+def _mut_decode_last_key(q, k, v, lens, window):  # the query's own key left out
+    o, lse = _orig_decode(q, k, v, np.asarray(lens) - 1, window - 1 if window > 0 else window)
+    return o, lse
+
+
+DECODE_MUTANTS = [_mut_decode_window, _mut_decode_scale, _mut_decode_last_key]
+
+
+@pytest.mark.parametrize("fn", DECODE_MUTANTS, ids=[f.__name__ for f in DECODE_MUTANTS])
+def test_decode_pins_catch_mutant(monkeypatch, fn):
+    import test_oracle_pins as P
+    P.test_decode_against_torch_sdpa(4)          # unmutated: passes
+    monkeypatch.setattr(R, "attention_decode", fn)
+    monkeypatch.setattr(P.O, "attention_decode", fn)
+    with pytest.raises(AssertionError):
+        P.test_decode_against_torch_sdpa(4)

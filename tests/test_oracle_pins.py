@@ -413,3 +413,65 @@ def test_cross_entropy_against_torch():
     assert abs(loss - float(lt)) < 1e-13
     np.testing.assert_allclose(dz, zt.grad.numpy(), atol=1e-15)
     np.testing.assert_allclose(lse, torch.logsumexp(torch.tensor(z), 1).numpy(), rtol=1e-14)
+
+
+# ----------------------------------------------------------- decode attention
+def _decode_inputs(B=3, Tmax=20, H=4, Hkv=2, D=8, seed=5):
+    g = np.random.default_rng(seed)
+    return (g.standard_normal((B, H, D)), g.standard_normal((B, Tmax, Hkv, D)),
+            g.standard_normal((B, Tmax, Hkv, D)))
+
+
+@pytest.mark.parametrize("window", [-1, 0, 3, 30])
+def test_decode_is_last_row_of_attention(window):
+    # decode of a sequence of length L equals row L-1 of the training attention
+    # on that sequence with the new query in its last row
+    q, k, v = _decode_inputs()
+    lens = np.array([1, 7, 20])
+    o, lse = O.attention_decode(q, k, v, lens, window)
+    for b, L in enumerate(lens):
+        qs = np.zeros((1, L, 4, 8))
+        qs[0, L - 1] = q[b]
+        oa, _ = O.attention(qs, k[b:b + 1, :L], v[b:b + 1, :L], window)
+        np.testing.assert_allclose(o[b], oa[0, L - 1], rtol=1e-12, atol=1e-14)
+        la = O.attention_logsumexp(qs, k[b:b + 1, :L], window)
+        np.testing.assert_allclose(lse[b], la[0, :, L - 1], rtol=1e-12)
+
+
+@pytest.mark.parametrize("window", [-1, 4])
+def test_decode_against_torch_sdpa(window):
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    q, k, v = _decode_inputs(B=2, Tmax=16, H=6, Hkv=2, D=16, seed=9)
+    lens = np.array([16, 9])
+    o, _ = O.attention_decode(q, k, v, lens, window)
+    for b, L in enumerate(lens):
+        i = L - 1
+        vis = np.array([(j <= i) and (window < 0 or i - j <= window) for j in range(16)])
+        kk = torch.from_numpy(np.repeat(k[b], 3, axis=1)).permute(1, 0, 2)   # [H, T, D]
+        vv = torch.from_numpy(np.repeat(v[b], 3, axis=1)).permute(1, 0, 2)
+        qq = torch.from_numpy(q[b])[:, None, :]                               # [H, 1, D]
+        ref = F.scaled_dot_product_attention(qq, kk, vv, attn_mask=torch.from_numpy(vis)[None, None, :])
+        np.testing.assert_allclose(o[b], ref[:, 0, :].numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_decode_closed_forms():
+    q, k, v = _decode_inputs()
+    lens = np.array([1, 7, 20])
+    # zero query: uniform weights, o = mean of the visible values, lse = log(count)
+    for window in (-1, 2):
+        o, lse = O.attention_decode(np.zeros_like(q), k, v, lens, window)
+        for b, L in enumerate(lens):
+            lo = max(0, L - 1 - window) if window >= 0 else 0
+            for h in range(4):
+                np.testing.assert_allclose(o[b, h], v[b, lo:L, h // 2].mean(axis=0), rtol=1e-13)
+                assert lse[b, h] == pytest.approx(math.log(L - lo), rel=1e-14)
+    # one visible key (length 1, or window 0): o is that value, lse its score
+    o, lse = O.attention_decode(q, k, v, lens, 0)
+    for b, L in enumerate(lens):
+        for h in range(4):
+            np.testing.assert_allclose(o[b, h], v[b, L - 1, h // 2], rtol=1e-14)
+            assert lse[b, h] == pytest.approx(float(q[b, h] @ k[b, L - 1, h // 2]) / math.sqrt(8), rel=1e-13)
+    # empty sequence
+    o, lse = O.attention_decode(q, k, v, np.array([0, 3, 3]), -1)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
