@@ -176,6 +176,24 @@ def kernel_figures(w, st, reps, torch, ops):
     by = N * V * 2.0 * s + 8 * N
     out["cross_entropy"] = {"ms": tce * 1e3, "GBps": by / tce / 1e9, "frac_hbm_peak": by / tce / PEAK_HBM}
     del z0, z
+    # decode attention (inference step, bandwidth): the workload's B sequences
+    # with T cached positions, one new query each; every visible K and V row
+    # read once (a window keeps only the last window+1 rows)
+    lens = torch.full((w.B,), w.T, dtype=torch.int32, device=dev)
+    kc, vc = rnd(w.B, w.T, Hkv, D), rnd(w.B, w.T, Hkv, D)
+    qd, od = rnd(w.B, H * D), torch.empty(w.B, H * D, dtype=dt, device=dev)
+    lsd = torch.empty(w.B, H, dtype=torch.float32, device=dev)
+    for win in sorted(set(w.windows)):
+        nb = ops.attention_decode_ws_bytes(w.B, H, Hkv, D, w.T, win)
+        wsd = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+        t = ev_time(lambda: ops.attention_decode(w.B, H, Hkv, D, win, qd, H * D, kc, vc, Hkv * D, w.T * Hkv * D,
+                                                 lens, w.T, od, H * D, lsd, wsd), reps, torch)
+        nvis = w.T if win < 0 else min(w.T, win + 1)
+        by = 2.0 * w.B * nvis * Hkv * D * s + 2.0 * w.B * H * D * s
+        key = "full" if win < 0 else f"window{win}"
+        out[f"attn_decode_{key}"] = {"shape": [w.B, w.T, H, Hkv, D], "ms": t * 1e3, "GBps": by / t / 1e9,
+                                     "frac_hbm_peak": by / t / PEAK_HBM}
+    del kc, vc
     torch.cuda.empty_cache()
     return out
 

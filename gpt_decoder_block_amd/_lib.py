@@ -15,12 +15,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgdb.so")
 
 # the GDB_ABI_VERSION this binding's structures and signatures follow
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 GDB_OK, GDB_EINVAL, GDB_EUNSUPPORTED, GDB_EHIP, GDB_EWORKSPACE = 0, -1, -2, -3, -4
 GDB_F32, GDB_BF16 = 0, 1
 
 c_void_p, c_int32, c_float, c_size_t = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+c_int64 = ctypes.c_int64
 
 
 class BlockCfg(ctypes.Structure):
@@ -112,6 +113,11 @@ SIGNATURES = {
                                     c_void_p, c_void_p]),
     "gdb_cross_entropy": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_void_p]),
+    "gdb_attention_decode_ws_bytes": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                                ctypes.POINTER(c_size_t)]),
+    "gdb_attention_decode": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32,
+                                       c_void_p, c_void_p, c_int32, c_int64, c_void_p, c_int32, c_void_p, c_int32,
+                                       c_void_p, c_void_p, c_size_t, c_void_p]),
 }
 
 

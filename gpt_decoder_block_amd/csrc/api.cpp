@@ -737,6 +737,60 @@ gdb_status gdb_attention_bwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32
   return GDB_OK;
 }
 
+namespace {
+gdb_status check_decode(int B, int H, int Hkv, int D, int max_len, int window) {
+  if (B <= 0 || H <= 0 || Hkv <= 0) return fail(GDB_EINVAL, "B, H, Hkv must be positive");
+  if (H % Hkv) return fail(GDB_EINVAL, "H (%d) must be a multiple of Hkv (%d)", H, Hkv);
+  if (!decode_group_supported(H / Hkv)) return fail(GDB_EUNSUPPORTED, "H / Hkv = %d not supported", H / Hkv);
+  if (D != 64 && D != 128) return fail(GDB_EUNSUPPORTED, "head_dim %d not supported", D);
+  if (max_len <= 0) return fail(GDB_EINVAL, "max_len must be positive");
+  if (window < -1) return fail(GDB_EINVAL, "window must be >= -1");
+  return GDB_OK;
+}
+size_t decode_ws(int B, int H, int Hkv, int D, int max_len, int window) {
+  int chunk = 0, nsplit = 1;
+  decode_plan(B, Hkv, max_len, window, &chunk, &nsplit);
+  return nsplit > 1 ? (size_t)B * H * nsplit * (D + 4) * sizeof(float) : 0;
+}
+}  // namespace
+
+gdb_status gdb_attention_decode_ws_bytes(int32_t B, int32_t H, int32_t Hkv, int32_t D, int32_t max_len,
+                                         int32_t window, size_t* ws_bytes) {
+  gdb_status st = check_decode(B, H, Hkv, D, max_len, window);
+  if (st != GDB_OK) return st;
+  if (!ws_bytes) return fail(GDB_EINVAL, "ws_bytes is NULL");
+  *ws_bytes = decode_ws(B, H, Hkv, D, max_len, window);
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_attention_decode(int32_t B, int32_t H, int32_t Hkv, int32_t D, int32_t window, int32_t dtype,
+                                const void* q, int32_t ldq, const void* k, const void* v, int32_t ldk,
+                                int64_t bstride, const int32_t* lens, int32_t max_len, void* o, int32_t ldo,
+                                float* lse, void* ws, size_t ws_bytes, void* stream) {
+  gdb_status st = check_decode(B, H, Hkv, D, max_len, window);
+  if (st != GDB_OK) return st;
+  if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
+  if (ldq < H * D || ldq % 8 || ldo < H * D || ldo % 8 || ldk < Hkv * D || ldk % 8)
+    return fail(GDB_EINVAL, "bad leading dimension");
+  if (B > 1 && (bstride < (int64_t)(max_len - 1) * ldk + Hkv * D || bstride % 8))
+    return fail(GDB_EINVAL, "bstride must be a multiple of 8 covering max_len rows");
+  CHECK_PTR(q); CHECK_PTR(k); CHECK_PTR(v); CHECK_PTR(lens); CHECK_PTR(o);
+  if (lse && (((uintptr_t)lse) & 15)) return fail(GDB_EINVAL, "lse is not 16-byte aligned");
+  const size_t need = decode_ws(B, H, Hkv, D, max_len, window);
+  if (need) {
+    CHECK_PTR(ws);
+    if (ws_bytes < need) return fail(GDB_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  }
+  DecodeArgs a{};
+  a.B = B; a.H = H; a.Hkv = Hkv; a.D = D; a.window = window; a.max_len = max_len;
+  a.q = q; a.ldq = ldq; a.k = k; a.v = v; a.ldk = ldk; a.bstride = bstride; a.lens = lens;
+  a.o = o; a.ldo = ldo; a.lse = lse; a.part = (float*)ws;
+  HIPCHK(attn_decode(dtype, a, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
 gdb_status gdb_cross_entropy(int32_t N, int32_t V, int32_t dtype, void* z, const int32_t* targets, float* row_loss,
                              float* loss, void* stream) {
   if (N <= 0 || V <= 0 || V % 8) return fail(GDB_EINVAL, "N must be positive, V a positive multiple of 8");

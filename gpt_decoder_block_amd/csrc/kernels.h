@@ -118,6 +118,24 @@ struct AttnArgs {
 hipError_t attn_fwd(int dt, const AttnArgs& a, hipStream_t s);
 hipError_t attn_bwd(int dt, const AttnArgs& a, hipStream_t s);
 
+// decode attention: query row b (q heads at columns h*D of row b, stride ldq)
+// against cache rows j of sequence b (k, v at b*bstride + j*ldk + g*D);
+// lens [B] device int32, clamped to [0, max_len]
+struct DecodeArgs {
+  int B, H, Hkv, D, window, max_len;
+  int chunk;                      // keys per split (set by attn_decode)
+  const void* q; int ldq;
+  const void* k; const void* v; int ldk; long long bstride;
+  const int32_t* lens;
+  void* o; int ldo;               // [B, ldo]
+  float* lse;                     // [B, H] or null
+  float* part;                    // [B, H, nsplit, D + 4] fp32 (nsplit > 1): o, m, l
+};
+bool decode_group_supported(int G);
+// split plan: keys per split and number of splits for the longest sequence
+void decode_plan(int B, int Hkv, int max_len, int window, int* chunk, int* nsplit);
+hipError_t attn_decode(int dt, const DecodeArgs& a, hipStream_t s);
+
 // --------------------------------------------------------------------- extras
 // Kernels that reduce scalar gradients write one fp32 partial row per
 // workgroup; *_partials(N) gives the number of rows (at most EXTRA_PBLK for the

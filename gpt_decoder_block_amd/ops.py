@@ -239,6 +239,21 @@ def attention_bwd(B: int, T: int, H: int, Hkv: int, D: int, window: int, qkv: to
            _p(dout), lddo, _p(dqkv), lddq, _p(delta), _stream(qkv))
 
 
+def attention_decode_ws_bytes(B: int, H: int, Hkv: int, D: int, max_len: int, window: int) -> int:
+    s = ctypes.c_size_t()
+    L.call("gdb_attention_decode_ws_bytes", B, H, Hkv, D, max_len, window, ctypes.byref(s))
+    return s.value
+
+
+def attention_decode(B: int, H: int, Hkv: int, D: int, window: int, q: torch.Tensor, ldq: int, k: torch.Tensor,
+                     v: torch.Tensor, ldk: int, bstride: int, lens: torch.Tensor, max_len: int, o: torch.Tensor,
+                     ldo: int, lse=None, ws=None) -> None:
+    """One new query per sequence against its K/V cache (lens: device int32 [B])."""
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    L.call("gdb_attention_decode", B, H, Hkv, D, window, dtype_code(q.dtype), _p(q), ldq, _p(k), _p(v), ldk,
+           bstride, _p(lens), max_len, _p(o), ldo, _opt(lse), _opt(ws), nbytes, _stream(q))
+
+
 def cross_entropy(z: torch.Tensor, targets: torch.Tensor, row_loss: torch.Tensor, loss: torch.Tensor) -> None:
     N, V = z.shape
     L.call("gdb_cross_entropy", N, V, dtype_code(z.dtype), _p(z), _p(targets), _p(row_loss), _p(loss),

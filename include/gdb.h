@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define GDB_ABI_VERSION 2
+#define GDB_ABI_VERSION 3
 
 /* Scratch bytes that gdb_smear_bwd and gdb_backout_bwd need in `ws`. */
 #define GDB_EXTRAS_WS_BYTES ((size_t)1 << 20)
@@ -332,6 +332,34 @@ gdb_status gdb_attention_bwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32
                              int32_t dtype, const void* qkv, int32_t ld, const void* o, int32_t ldo,
                              const float* lse, const void* dout, int32_t lddo, void* dqkv, int32_t lddq,
                              float* delta, void* stream);
+
+/* Decode attention against a key/value cache ("Comment Entraîner Votre
+ * Propre ChatGPT Pour 50€ ?", section "6. Moteur d'inférence": generation
+ * after the prompt is prefilled into a KV cache; the masking rule is the
+ * training attention's, section "5. Unification de Flash Attention").
+ * One new query per sequence b, at position i = lens[b] - 1:
+ *   o[b, h*D + d] = sum_j P_j v_j[d],  P = softmax over visible j of q.k_j / sqrt(D),
+ *   key j visible iff j <= i and (window < 0 or i - j <= window),
+ *   query head h reads K/V head g = h / (H / Hkv);
+ *   lse float32 [B, H] (optional, may be NULL) = log-sum-exp of the scores.
+ * q: row b at q + b*ldq holds the H query heads (column h*D); the query's own
+ *   key and value must already be in the cache at position i.
+ * k, v: key / value of position j of sequence b at (k|v) + b*bstride + j*ldk,
+ *   head g at column g*D (elements of `dtype`); a dedicated cache
+ *   [B][Tmax][Hkv][D] has ldk = Hkv*D, bstride = Tmax*Hkv*D, and the packed
+ *   QKV rows of a prefill serve as well (ldk = (H + 2*Hkv)*D, bstride = T*ldk,
+ *   k and v offset by H*D and (H + Hkv)*D).
+ * lens: DEVICE int32 [B], each in [1, max_len]; values outside are clamped
+ *   to [0, max_len] and a length of 0 gives o = 0, lse = -inf.
+ * max_len (host): bound on every length; it sizes the split-KV grid.
+ * ws: fp32 scratch of gdb_attention_decode_ws_bytes bytes (NULL if that is 0).
+ * D = 64 or 128 (bf16 and fp32); H / Hkv in {1, 2, 3, 4, 6, 8}. */
+gdb_status gdb_attention_decode_ws_bytes(int32_t B, int32_t H, int32_t Hkv, int32_t D, int32_t max_len,
+                                         int32_t window, size_t* ws_bytes);
+gdb_status gdb_attention_decode(int32_t B, int32_t H, int32_t Hkv, int32_t D, int32_t window, int32_t dtype,
+                                const void* q, int32_t ldq, const void* k, const void* v, int32_t ldk,
+                                int64_t bstride, const int32_t* lens, int32_t max_len, void* o, int32_t ldo,
+                                float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* Fused softmax cross-entropy on logits z [N, V] (overwritten by
  * dz = (softmax(z) - onehot(targets)) / N), row_loss float32 [N] =

@@ -236,3 +236,34 @@ def test_fp8_sizes_and_validation(L):
                             None) == L.GDB_EINVAL
     ws = ctypes.c_size_t()
     assert lib.gdb_gemm_fp8_ws_bytes(1536, 6144, 32768, 4, ctypes.byref(ws)) == L.GDB_OK
+
+
+def test_attention_decode_validation(L):
+    # every rejection happens before a launch (no GPU here)
+    lib = L.lib()
+    buf = ctypes.create_string_buffer(4096)
+    al = (ctypes.addressof(buf) + 255) & ~255
+    nb = ctypes.c_size_t()
+
+    def call(B=2, H=12, Hkv=12, D=128, window=-1, dtype=1, ldq=1536, ldk=1536, bstride=2048 * 1536, lens=al,
+             max_len=2048, ldo=1536, lse=None, ws=al, ws_bytes=1 << 30, q=al):
+        return lib.gdb_attention_decode(B, H, Hkv, D, window, dtype, q, ldq, al, al, ldk, bstride, lens, max_len,
+                                        al, ldo, lse, ws, ws_bytes, None)
+
+    assert lib.gdb_attention_decode_ws_bytes(2, 12, 12, 128, 2048, -1, ctypes.byref(nb)) == L.GDB_OK
+    assert nb.value > 0   # 2048 positions split over several workgroups
+    assert lib.gdb_attention_decode_ws_bytes(2, 12, 12, 128, 64, -1, ctypes.byref(nb)) == L.GDB_OK
+    assert nb.value == 0  # one chunk: no partials
+    assert call(H=12, Hkv=5) == L.GDB_EINVAL
+    assert call(H=10, Hkv=2) == L.GDB_EUNSUPPORTED and "H / Hkv = 5" in lib.gdb_last_error().decode()
+    assert call(D=96) == L.GDB_EUNSUPPORTED
+    assert call(max_len=0) == L.GDB_EINVAL
+    assert call(window=-2) == L.GDB_EINVAL
+    assert call(dtype=7) == L.GDB_EINVAL
+    assert call(ldk=1000) == L.GDB_EINVAL and "leading dimension" in lib.gdb_last_error().decode()
+    assert call(bstride=2047 * 1536) == L.GDB_EINVAL and "bstride" in lib.gdb_last_error().decode()
+    assert call(lens=None) == L.GDB_EINVAL and "lens is NULL" in lib.gdb_last_error().decode()
+    assert call(q=al + 8) == L.GDB_EINVAL and "aligned" in lib.gdb_last_error().decode()
+    assert call(lse=al + 4) == L.GDB_EINVAL
+    assert call(ws=None) == L.GDB_EINVAL
+    assert call(ws_bytes=16) == L.GDB_EWORKSPACE
