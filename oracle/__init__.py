@@ -11,3 +11,4 @@ passages each one follows and for the pins that tie it to something other than
 itself (the tests under `tests/test_oracle_*.py`).
 """
 from .reference import *  # noqa: F401,F403
+from .optim import *  # noqa: F401,F403

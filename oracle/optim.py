@@ -1,0 +1,79 @@
+"""Plain float64 CPU oracle of the optimizer step that follows the backward.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Sources (page title, then section):
+  [JA] the Japanese version of the French article on dev.to, section
+       "2. Muonオプティマイザー（nanochat/optim.py）": embeddings, lm_head and
+       scalar parameters take AdamW, 2-D matrices take Muon; the Polar Express
+       Newton-Schulz loop (A = X^T X; B = b A + c A^2; X = a X + X B) with the
+       first two of its coefficient triples.
+  [FR] "Comment Entraîner Votre Propre ChatGPT Pour 50€ ?", section "2.
+       L'optimiseur Muon (nanochat/optim.py)": the same loop, five iterations,
+       Muon read as momentum orthogonalised by that iteration.
+
+Readings taken where the pages are silent (each listed in the design doc):
+  * the iteration starts from X0 = G / (||G||_F * norm_scale + eps): the
+    polynomial steps only act as intended on singular values in (0, 1], and
+    the Frobenius norm bounds the largest one; norm_scale and eps are inputs;
+  * the coefficient table is an input (the pages print two of the five
+    triples); tests use the two printed ones and synthetic tables;
+  * Muon: buf <- momentum * buf + g; the orthogonalised matrix is that of
+    g + momentum * buf (Nesterov) or of buf; p <- p * (1 - lr * wd) -
+    lr * scale * NS(.), with the shape-dependent scale an input;
+  * AdamW is the decoupled-weight-decay Adam with bias correction (the
+    textbook method, as torch.optim.AdamW computes it);
+  * NorMuon's per-neuron variance normalisation is printed only in part and
+    is not modelled (out of scope).
+
+Pins (tests/test_oracle_pins.py): Newton-Schulz against the SVD closed form
+(singular vectors kept, each singular value through the composed
+polynomial), the transpose identity NS(G^T) = NS(G)^T, the classic cubic
+iteration converging to the polar factor U V^T; AdamW against
+torch.optim.AdamW over several steps; Muon with momentum 0 and no decay
+reduces to a Newton-Schulz step.
+"""
+from __future__ import annotations
+
+import math
+from typing import Sequence, Tuple
+
+import numpy as np
+
+__all__ = ["newton_schulz", "adamw_step", "muon_step"]
+
+
+def newton_schulz(G: np.ndarray, coeffs: Sequence[Tuple[float, float, float]], norm_scale: float = 1.0,
+                  eps: float = 1e-7) -> np.ndarray:
+    """The pages' orthogonalisation loop on G [m, n], one (a, b, c) triple per
+    iteration, starting from the Frobenius-normalised G."""
+    X = np.asarray(G, dtype=np.float64)
+    X = X / (np.linalg.norm(X) * norm_scale + eps)
+    for a, b, c in coeffs:
+        A = X.T @ X
+        B = b * A + c * (A @ A)
+        X = a * X + X @ B
+    return X
+
+
+def adamw_step(p, g, m, v, t: int, lr: float, beta1: float, beta2: float, eps: float, wd: float):
+    """One AdamW step (decoupled weight decay, bias-corrected moments); t >= 1
+    counts steps including this one.  Returns the new (p, m, v)."""
+    p = np.asarray(p, dtype=np.float64) * (1.0 - lr * wd)
+    m = beta1 * np.asarray(m, dtype=np.float64) + (1.0 - beta1) * g
+    v = beta2 * np.asarray(v, dtype=np.float64) + (1.0 - beta2) * np.square(g)
+    mhat = m / (1.0 - beta1 ** t)
+    vhat = v / (1.0 - beta2 ** t)
+    p = p - lr * mhat / (np.sqrt(vhat) + eps)
+    return p, m, v
+
+
+def muon_step(p, g, buf, lr: float, momentum: float, nesterov: bool, wd: float, scale: float,
+              coeffs: Sequence[Tuple[float, float, float]], norm_scale: float = 1.0, eps: float = 1e-7):
+    """One Muon step on a matrix parameter p [m, n] with gradient g and
+    momentum buffer buf.  Returns the new (p, buf)."""
+    buf = momentum * np.asarray(buf, dtype=np.float64) + g
+    u = g + momentum * buf if nesterov else buf
+    o = newton_schulz(u, coeffs, norm_scale, eps)
+    p = np.asarray(p, dtype=np.float64) * (1.0 - lr * wd) - lr * scale * o
+    return p, buf

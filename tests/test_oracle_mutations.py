@@ -102,3 +102,51 @@ def test_decode_pins_catch_mutant(monkeypatch, fn):
     monkeypatch.setattr(P.O, "attention_decode", fn)
     with pytest.raises(AssertionError):
         P.test_decode_against_torch_sdpa(4)
+
+
+# optimizer: each mutant must fail its closed-form or torch pin
+import oracle.optim as OPT
+
+_orig_ns = OPT.newton_schulz
+
+
+def _mut_ns_gram_side(G, coeffs, norm_scale=1.0, eps=1e-7):   # X B replaced by B X (square case)
+    X = np.asarray(G, dtype=np.float64)
+    X = X / (np.linalg.norm(X) * norm_scale + eps)
+    for a, b, c in coeffs:
+        A = X.T @ X
+        X = a * X + (b * A + c * (A @ A)) @ X
+    return X
+
+
+def _mut_ns_no_norm(G, coeffs, norm_scale=1.0, eps=1e-7):      # missing the Frobenius normalisation
+    return _orig_ns(np.asarray(G) * np.linalg.norm(G), coeffs, norm_scale, eps)
+
+
+_orig_adamw = OPT.adamw_step
+
+
+def _mut_adamw_no_bias_corr(p, g, m, v, t, lr, beta1, beta2, eps, wd):
+    return _orig_adamw(p, g, m, v, 10 ** 6, lr, beta1, beta2, eps, wd)
+
+
+def _mut_adamw_coupled_decay(p, g, m, v, t, lr, beta1, beta2, eps, wd):   # L2 penalty instead of decoupled decay
+    return _orig_adamw(p, g + wd * np.asarray(p), m, v, t, lr, beta1, beta2, eps, 0.0)
+
+
+@pytest.mark.parametrize("fn", [_mut_ns_gram_side, _mut_ns_no_norm], ids=["gram_side", "no_norm"])
+def test_newton_schulz_pin_catches_mutant(monkeypatch, fn):
+    import test_oracle_pins as P
+    P.test_newton_schulz_svd_closed_form((12, 12), P.PE_PRINTED)
+    monkeypatch.setattr(P.O, "newton_schulz", fn)
+    with pytest.raises(AssertionError):
+        P.test_newton_schulz_svd_closed_form((12, 12), P.PE_PRINTED)
+
+
+@pytest.mark.parametrize("fn", [_mut_adamw_no_bias_corr, _mut_adamw_coupled_decay], ids=["bias_corr", "decay"])
+def test_adamw_pin_catches_mutant(monkeypatch, fn):
+    import test_oracle_pins as P
+    P.test_adamw_against_torch()
+    monkeypatch.setattr(P.O, "adamw_step", fn)
+    with pytest.raises(AssertionError):
+        P.test_adamw_against_torch()

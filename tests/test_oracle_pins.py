@@ -475,3 +475,62 @@ def test_decode_closed_forms():
     # empty sequence
     o, lse = O.attention_decode(q, k, v, np.array([0, 3, 3]), -1)
     assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+
+
+# ----------------------------------------------------------------- optimizer
+PE_PRINTED = [(8.156, -22.483, 15.879), (4.043, -2.809, 0.500)]   # the two triples the pages print
+
+
+def _svd_closed_form(G, coeffs, norm_scale=1.0, eps=1e-7):
+    U, S, Vt = np.linalg.svd(G, full_matrices=False)
+    s = S / (np.linalg.norm(G) * norm_scale + eps)
+    for a, b, c in coeffs:
+        s = a * s + b * s ** 3 + c * s ** 5
+    return (U * s) @ Vt
+
+
+@pytest.mark.parametrize("shape", [(7, 5), (5, 7), (12, 12)])
+@pytest.mark.parametrize("coeffs", [PE_PRINTED, [(3.0, -3.2, 1.2)] * 3, [(1.5, -0.5, 0.0)]])
+def test_newton_schulz_svd_closed_form(shape, coeffs):
+    G = np.random.default_rng(3).standard_normal(shape)
+    X = O.newton_schulz(G, coeffs, norm_scale=1.02)
+    np.testing.assert_allclose(X, _svd_closed_form(G, coeffs, 1.02), rtol=1e-10, atol=1e-12)
+    # transpose identity of the exact map (the Gram can be taken on either side)
+    np.testing.assert_allclose(O.newton_schulz(G.T, coeffs, 1.02), X.T, rtol=1e-10, atol=1e-12)
+
+
+def test_newton_schulz_cubic_converges_to_polar_factor():
+    G = np.random.default_rng(4).standard_normal((9, 6))
+    U, S, Vt = np.linalg.svd(G, full_matrices=False)
+    X = O.newton_schulz(G, [(1.5, -0.5, 0.0)] * 60)
+    np.testing.assert_allclose(X, U @ Vt, atol=1e-9)
+
+
+def test_adamw_against_torch():
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(5)
+    p0 = g.standard_normal(37)
+    grads = [g.standard_normal(37) for _ in range(4)]
+    kw = dict(lr=3e-3, betas=(0.8, 0.95), eps=1e-8, weight_decay=0.1)
+    tp = torch.nn.Parameter(torch.from_numpy(p0.copy()))
+    opt = torch.optim.AdamW([tp], **kw)
+    p, m, v = p0.copy(), np.zeros(37), np.zeros(37)
+    for t, gr in enumerate(grads, 1):
+        tp.grad = torch.from_numpy(gr.copy())
+        opt.step()
+        p, m, v = O.adamw_step(p, gr, m, v, t, 3e-3, 0.8, 0.95, 1e-8, 0.1)
+        np.testing.assert_allclose(p, tp.detach().numpy(), rtol=1e-13, atol=1e-15)
+
+
+def test_muon_without_momentum_is_a_newton_schulz_step():
+    g = np.random.default_rng(6)
+    p, gr = g.standard_normal((8, 5)), g.standard_normal((8, 5))
+    p1, buf = O.muon_step(p, gr, np.zeros((8, 5)), 0.02, 0.0, True, 0.0, 1.5, PE_PRINTED)
+    np.testing.assert_allclose(p1, p - 0.02 * 1.5 * _svd_closed_form(gr, PE_PRINTED), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(buf, gr)
+    # Nesterov with momentum mu orthogonalises g + mu * (mu * buf + g)
+    b0 = g.standard_normal((8, 5))
+    p2, buf2 = O.muon_step(p, gr, b0, 0.02, 0.9, True, 0.1, 1.0, PE_PRINTED)
+    np.testing.assert_allclose(buf2, 0.9 * b0 + gr)
+    u = gr + 0.9 * buf2
+    np.testing.assert_allclose(p2, p * (1 - 0.002) - 0.02 * _svd_closed_form(u, PE_PRINTED), rtol=1e-10, atol=1e-12)
