@@ -36,23 +36,31 @@ reduces to a Newton-Schulz step.
 from __future__ import annotations
 
 import math
-from typing import Sequence, Tuple
+from typing import Optional, Sequence, Tuple
 
 import numpy as np
+
+from .reference import bf16_round
 
 __all__ = ["newton_schulz", "adamw_step", "muon_step"]
 
 
 def newton_schulz(G: np.ndarray, coeffs: Sequence[Tuple[float, float, float]], norm_scale: float = 1.0,
-                  eps: float = 1e-7) -> np.ndarray:
+                  eps: float = 1e-7, round_to: Optional[str] = None) -> np.ndarray:
     """The pages' orthogonalisation loop on G [m, n], one (a, b, c) triple per
-    iteration, starting from the Frobenius-normalised G."""
+    iteration, starting from the Frobenius-normalised G.
+
+    round_to="bf16" rounds the normalised input and the result of each of the
+    three lines to bfloat16 (an iteration run in bf16 storage with exact
+    arithmetic inside each line); used only to measure how far bf16 storage
+    alone moves the exact map, never as the reference."""
+    rnd = (lambda a: a) if round_to is None else bf16_round
     X = np.asarray(G, dtype=np.float64)
-    X = X / (np.linalg.norm(X) * norm_scale + eps)
+    X = rnd(X / (np.linalg.norm(X) * norm_scale + eps))
     for a, b, c in coeffs:
-        A = X.T @ X
-        B = b * A + c * (A @ A)
-        X = a * X + X @ B
+        A = rnd(X.T @ X)
+        B = rnd(b * A + c * (A @ A))
+        X = rnd(a * X + X @ B)
     return X
 
 

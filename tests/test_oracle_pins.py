@@ -534,3 +534,14 @@ def test_muon_without_momentum_is_a_newton_schulz_step():
     np.testing.assert_allclose(buf2, 0.9 * b0 + gr)
     u = gr + 0.9 * buf2
     np.testing.assert_allclose(p2, p * (1 - 0.002) - 0.02 * _svd_closed_form(u, PE_PRINTED), rtol=1e-10, atol=1e-12)
+
+
+def test_newton_schulz_bf16_storage_option():
+    # the bf16-storage variant only rounds: zero steps give the rounded
+    # normalised input, and its distance from the exact map shrinks with the
+    # number of bits (an fp32-like rounding would be ~2^16 times closer)
+    G = np.random.default_rng(8).standard_normal((40, 24))
+    x0 = O.newton_schulz(G, [], 1.0)
+    np.testing.assert_array_equal(O.newton_schulz(G, [], 1.0, round_to="bf16"), O.bf16_round(x0))
+    d = np.max(np.abs(O.newton_schulz(G, PE_PRINTED, round_to="bf16") - O.newton_schulz(G, PE_PRINTED)))
+    assert 1e-5 < d < 0.1 * np.max(np.abs(O.newton_schulz(G, PE_PRINTED)))
