@@ -194,6 +194,27 @@ def kernel_figures(w, st, reps, torch, ops):
         out[f"attn_decode_{key}"] = {"shape": [w.B, w.T, H, Hkv, D], "ms": t * 1e3, "GBps": by / t / 1e9,
                                      "frac_hbm_peak": by / t / PEAK_HBM}
     del kc, vc
+    # optimizer step (after the backward): Muon on the MLP up-projection
+    # matrix (momentum, 5 Newton-Schulz iterations on the MFMA GEMM, update),
+    # AdamW over the embedding and lm_head tables (bandwidth)
+    coeffs = [(8.156, -22.483, 15.879), (4.043, -2.809, 0.5)] + [(1.5, -0.5, 0.0)] * 3
+    pm = rnd(F, C).float()
+    gm, bm = rnd(F, C).float(), torch.zeros(F, C, dtype=torch.float32, device=dev)
+    wsm = torch.empty(ops.muon_ws_bytes(F, C, dt), dtype=torch.uint8, device=dev)
+    t = ev_time(lambda: ops.muon_step(pm, gm, bm, 0.02, 0.95, True, 0.0, 1.0, coeffs, dt, wsm), reps, torch)
+    s_, L_ = min(F, C), max(F, C)
+    fl = len(coeffs) * (4.0 * s_ * s_ * L_ + 2.0 * s_ ** 3)
+    out["muon_step_w_fc"] = {"shape": [F, C], "ns_steps": len(coeffs), "ms": t * 1e3, "tflops": fl / t / 1e12,
+                             "frac_bf16_peak": fl / t / PEAK_BF16}
+    del pm, gm, bm, wsm
+    na = 2 * V * C
+    pa, ga = torch.zeros(na, dtype=torch.float32, device=dev), rnd(na).float()
+    ma, va = torch.zeros(na, dtype=torch.float32, device=dev), torch.zeros(na, dtype=torch.float32, device=dev)
+    plo = torch.empty(na, dtype=torch.bfloat16, device=dev)
+    t = ev_time(lambda: ops.adamw_step(pa, ga, ma, va, 1, 1e-3, 0.8, 0.95, 1e-8, 0.0, p_bf16=plo), reps, torch)
+    by = na * (7 * 4.0 + 2)
+    out["adamw_wte_lm_head"] = {"params": na, "ms": t * 1e3, "GBps": by / t / 1e9, "frac_hbm_peak": by / t / PEAK_HBM}
+    del pa, ga, ma, va, plo
     torch.cuda.empty_cache()
     return out
 

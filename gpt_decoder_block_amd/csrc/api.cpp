@@ -791,6 +791,167 @@ gdb_status gdb_attention_decode(int32_t B, int32_t H, int32_t Hkv, int32_t D, in
   return GDB_OK;
 }
 
+// ----------------------------------------------------------------- optimizer
+namespace {
+size_t al256(size_t b) { return (b + 255) / 256 * 256; }
+
+// workspace of the Newton-Schulz iteration on an [m, n] matrix; with `muon`
+// also the fp32 momentum-blended matrix and the iteration's output
+struct NsWs {
+  size_t x, xa, a, bm, part, npart, inv, u, total;
+};
+// split count of the Gram product (the other two run unsplit)
+int ns_gram_splits(int m, int n, int dt) {
+  const int s_ = std::min(m, n), L = std::max(m, n);
+  return gemm_splits(dt, s_, s_, L, EPI_F32);
+}
+
+NsWs ns_layout(int m, int n, int dt, bool muon) {
+  const int s_ = std::min(m, n);
+  const size_t es = dt_size(dt);
+  const size_t part = (size_t)ns_gram_splits(m, n, dt) * s_ * s_ * 4;
+  NsWs w{};
+  size_t o = 0;
+  if (muon) { w.u = o; o += al256((size_t)m * n * 4); w.x = o; o += al256((size_t)m * n * es); }
+  w.xa = o; o += al256((size_t)m * n * es);
+  w.a = o; o += al256((size_t)s_ * s_ * es);
+  w.bm = o; o += al256((size_t)s_ * s_ * es);
+  w.part = o; o += al256(part);
+  w.npart = o; o += al256((size_t)OPT_PART * 4);
+  w.inv = o; o += 256;
+  w.total = o;
+  return w;
+}
+
+gdb_status check_ns(int m, int n, int dtype, const float* coeffs, int steps) {
+  if (m <= 0 || n <= 0 || m % 8 || n % 8) return fail(GDB_EINVAL, "m, n must be positive multiples of 8");
+  if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
+  if (steps < 0 || steps > 64) return fail(GDB_EINVAL, "steps must be in [0, 64]");
+  if (steps > 0 && !coeffs) return fail(GDB_EINVAL, "coeffs is NULL");
+  for (int i = 0; i < 3 * steps; ++i)
+    if (!std::isfinite(coeffs[i])) return fail(GDB_EINVAL, "coefficient %d is not finite", i);
+  return GDB_OK;
+}
+
+// the iteration from x0 (already in `start`), ending in `out`; `other` is the
+// ping-pong partner.  Tall matrices take the Gram X^T X, wide ones X X^T
+// (the same map: X p(X^T X) = p(X X^T) X).  The Gram runs split over K into
+// fp32 partials, added and cast in one pass; the other two lines apply their
+// axpy in the GEMM epilogue.
+hipError_t ns_iterate(int dt, int m, int n, const float* coeffs, int steps, void* out, void* other, void* A,
+                      void* Bm, float* part, hipStream_t s) {
+  const bool tall = m >= n;
+  const int s_ = tall ? n : m, L = tall ? m : n;
+  const int spg = ns_gram_splits(m, n, dt);
+  void* cur = steps % 2 == 0 ? out : other;
+  for (int it = 0; it < steps; ++it) {
+    const float a = coeffs[3 * it], b = coeffs[3 * it + 1], c = coeffs[3 * it + 2];
+    void* nxt = cur == out ? other : out;
+    // A = X^T X (tall: both operands M/N-contiguous) or X X^T (wide: both K-contiguous)
+    GemmArgs g = gemm_args(cur, !tall, n, cur, !tall, n, s_, s_, L, EPI_F32, part, s_);
+    g.splits = spg;
+    g.partial = part;
+    hipError_t e = gemm(dt, g, s);
+    if (e == hipSuccess) e = splitk_axpby(dt, part, spg, (size_t)s_ * s_, 1.0f, 0.0f, nullptr, A, s);
+    // B = b A + c A A (A symmetric: its rows serve as the second operand's K-contiguous rows)
+    GemmArgs g2 = gemm_args(A, true, s_, A, true, s_, s_, s_, s_, EPI_AXPBY, Bm, s_);
+    g2.R = A; g2.ldr = s_; g2.alpha = c; g2.beta = b;
+    if (e == hipSuccess) e = gemm(dt, g2, s);
+    // X' = a X + X B (tall) or a X + B X (wide); B symmetric
+    GemmArgs g3 = tall ? gemm_args(cur, true, n, Bm, true, s_, m, n, s_, EPI_AXPBY, nxt, n)
+                       : gemm_args(Bm, true, s_, cur, false, n, m, n, s_, EPI_AXPBY, nxt, n);
+    g3.R = cur; g3.ldr = n; g3.alpha = 1.0f; g3.beta = a;
+    if (e == hipSuccess) e = gemm(dt, g3, s);
+    if (e != hipSuccess) return e;
+    cur = nxt;
+  }
+  return hipSuccess;
+}
+}  // namespace
+
+gdb_status gdb_newton_schulz_ws_bytes(int32_t m, int32_t n, int32_t dtype, size_t* ws_bytes) {
+  gdb_status st = check_ns(m, n, dtype, nullptr, 0);
+  if (st != GDB_OK) return st;
+  if (!ws_bytes) return fail(GDB_EINVAL, "ws_bytes is NULL");
+  *ws_bytes = ns_layout(m, n, dtype, false).total;
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_newton_schulz(int32_t m, int32_t n, int32_t dtype, const float* G, void* X, const float* coeffs,
+                             int32_t steps, float norm_scale, float eps, void* ws, size_t ws_bytes, void* stream) {
+  gdb_status st = check_ns(m, n, dtype, coeffs, steps);
+  if (st != GDB_OK) return st;
+  if (!(norm_scale > 0.f) || !std::isfinite(norm_scale) || !(eps >= 0.f) || !std::isfinite(eps))
+    return fail(GDB_EINVAL, "norm_scale must be positive and eps non-negative");
+  CHECK_PTR(G); CHECK_PTR(X); CHECK_PTR(ws);
+  const NsWs w = ns_layout(m, n, dtype, false);
+  if (ws_bytes < w.total) return fail(GDB_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, w.total);
+  if ((const void*)G == X) return fail(GDB_EINVAL, "X must not alias G");
+  char* b = (char*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t mn = (size_t)m * n;
+  int np = 0;
+  void* start = steps % 2 == 0 ? X : (void*)(b + w.xa);
+  HIPCHK(sumsq_partials(G, mn, (float*)(b + w.npart), &np, s));
+  HIPCHK(norm_final((float*)(b + w.npart), np, norm_scale, eps, (float*)(b + w.inv), s));
+  HIPCHK(scale_cast(dtype, G, (float*)(b + w.inv), start, mn, s));
+  HIPCHK(ns_iterate(dtype, m, n, coeffs, steps, X, b + w.xa, b + w.a, b + w.bm, (float*)(b + w.part), s));
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_muon_ws_bytes(int32_t m, int32_t n, int32_t dtype, size_t* ws_bytes) {
+  gdb_status st = check_ns(m, n, dtype, nullptr, 0);
+  if (st != GDB_OK) return st;
+  if (!ws_bytes) return fail(GDB_EINVAL, "ws_bytes is NULL");
+  *ws_bytes = ns_layout(m, n, dtype, true).total;
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_muon_step(int32_t m, int32_t n, int32_t dtype, float* p, void* p_bf16, const float* g, float* buf,
+                         float lr, float momentum, int32_t nesterov, float wd, float scale, const float* coeffs,
+                         int32_t steps, float norm_scale, float eps, void* ws, size_t ws_bytes, void* stream) {
+  gdb_status st = check_ns(m, n, dtype, coeffs, steps);
+  if (st != GDB_OK) return st;
+  for (float f : {lr, momentum, wd, scale, norm_scale, eps})
+    if (!std::isfinite(f)) return fail(GDB_EINVAL, "non-finite hyperparameter");
+  if (!(norm_scale > 0.f) || eps < 0.f) return fail(GDB_EINVAL, "norm_scale must be positive and eps non-negative");
+  CHECK_PTR(p); CHECK_PTR(g); CHECK_PTR(buf); CHECK_PTR(ws);
+  if (p_bf16 && (((uintptr_t)p_bf16) & 15)) return fail(GDB_EINVAL, "p_bf16 is not 16-byte aligned");
+  const NsWs w = ns_layout(m, n, dtype, true);
+  if (ws_bytes < w.total) return fail(GDB_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, w.total);
+  char* b = (char*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t mn = (size_t)m * n;
+  int np = 0;
+  void* X = b + w.x;
+  void* start = steps % 2 == 0 ? X : (void*)(b + w.xa);
+  HIPCHK(muon_momentum(g, buf, (float*)(b + w.u), mn, momentum, nesterov ? 1 : 0, (float*)(b + w.npart), &np, s));
+  HIPCHK(norm_final((float*)(b + w.npart), np, norm_scale, eps, (float*)(b + w.inv), s));
+  HIPCHK(scale_cast(dtype, (float*)(b + w.u), (float*)(b + w.inv), start, mn, s));
+  HIPCHK(ns_iterate(dtype, m, n, coeffs, steps, X, b + w.xa, b + w.a, b + w.bm, (float*)(b + w.part), s));
+  HIPCHK(muon_apply(dtype, p, X, (bf16*)p_bf16, mn, 1.0f - lr * wd, lr * scale, s));
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_adamw_step(int64_t n, float* p, void* p_bf16, const float* g, float* m, float* v, int32_t t, float lr,
+                          float beta1, float beta2, float eps, float wd, void* stream) {
+  if (n <= 0 || n % 8) return fail(GDB_EINVAL, "n must be a positive multiple of 8");
+  if (t < 1) return fail(GDB_EINVAL, "t counts steps from 1");
+  for (float f : {lr, beta1, beta2, eps, wd})
+    if (!std::isfinite(f)) return fail(GDB_EINVAL, "non-finite hyperparameter");
+  if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f)) return fail(GDB_EINVAL, "betas must be in [0, 1)");
+  if (!(eps > 0.f)) return fail(GDB_EINVAL, "eps must be positive");
+  CHECK_PTR(p); CHECK_PTR(g); CHECK_PTR(m); CHECK_PTR(v);
+  if (p_bf16 && (((uintptr_t)p_bf16) & 15)) return fail(GDB_EINVAL, "p_bf16 is not 16-byte aligned");
+  HIPCHK(adamw(p, g, m, v, (bf16*)p_bf16, (size_t)n, lr, beta1, beta2, eps, wd, t, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
 gdb_status gdb_cross_entropy(int32_t N, int32_t V, int32_t dtype, void* z, const int32_t* targets, float* row_loss,
                              float* loss, void* stream) {
   if (N <= 0 || V <= 0 || V % 8) return fail(GDB_EINVAL, "N must be positive, V a positive multiple of 8");

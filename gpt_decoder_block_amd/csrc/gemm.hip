@@ -1,7 +1,7 @@
-// GEMMs of the block and the lm_head: C[m, n] = sum_k A(m, k) * B(n, k) with
-// either operand stored K-contiguous or M/N-contiguous, fused epilogues
-// (residual add, ReLU² with its saved pre-activation, ReLU² backward, fp32
-// weight-gradient output with split-K).
+// GEMMs of the block, the lm_head and the optimizer's Newton-Schulz steps:
+// C[m, n] = sum_k A(m, k) * B(n, k) with either operand stored K-contiguous or
+// M/N-contiguous, fused epilogues (residual add, ReLU² with its saved
+// pre-activation, ReLU² backward, fp32 output with split-K, alpha*acc + beta*R).
 //
 // bf16 path (gfx950 MFMA, v_mfma_f32_32x32x16_bf16):
 //   * 256x256 output tile per workgroup, K step 64, 256 threads = 4 waves in a
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_k(GemmArgs p) {
     constexpr int RPW = 128 / (NW);  // rows per wave per pass
     // residual / saved-u operand for all of this wave's rows, loaded up front
     OV rv[RPW];
-    if (EPI == EPI_RESID || EPI == EPI_DRELU2 || EPI == EPI_DSQR) {
+    if (EPI == EPI_RESID || EPI == EPI_DRELU2 || EPI == EPI_DSQR || EPI == EPI_AXPBY) {
 #pragma unroll
       for (int k = 0; k < RPW; ++k) {
         const int m = m0 + q * 128 + w + k * (NW);
@@ -607,6 +607,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_k(GemmArgs p) {
           if (EPI == EPI_RESID) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = (OT)(v[e] + (float)rv[k][e]);
+          } else if (EPI == EPI_AXPBY) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = (OT)(p.alpha * v[e] + p.beta * (float)rv[k][e]);
+
           } else if (EPI == EPI_DRELU2 || EPI == EPI_DSQR) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -713,6 +717,7 @@ __global__ __launch_bounds__(256) void gemm_f32_k(GemmArgs p) {
         if (EPI == EPI_RESID) *C = ((const float*)p.R)[(size_t)m * p.ldr + n] + v;
         else if (EPI == EPI_DRELU2) *C = v * 2.0f * fmaxf(((const float*)p.R)[(size_t)m * p.ldr + n], 0.f);
         else if (EPI == EPI_DSQR) *C = v * 2.0f * sqrtf(fmaxf(((const float*)p.R)[(size_t)m * p.ldr + n], 0.f));
+        else if (EPI == EPI_AXPBY) *C = p.alpha * v + p.beta * ((const float*)p.R)[(size_t)m * p.ldr + n];
         else if (EPI == EPI_SQR) *C = fmaxf(v, 0.f) * fmaxf(v, 0.f);
         else *C = v;
         if (EPI == EPI_RELU2) {
@@ -752,6 +757,12 @@ hipError_t launch_bf16(const GemmArgs& a, dim3 g, hipStream_t s) {
     case EPI_F32:
       if constexpr (std::is_same<OT, bf16>::value) {
         hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_F32, F8, OT, NW>), g, dim3(64 * NW), 0, s, a);
+        break;
+      }
+      return hipErrorInvalidValue;
+    case EPI_AXPBY:
+      if constexpr (!F8) {
+        hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_AXPBY, F8, OT, NW>), g, dim3(64 * NW), 0, s, a);
         break;
       }
       return hipErrorInvalidValue;
@@ -838,6 +849,7 @@ hipError_t gemm(int dt, const GemmArgs& a, hipStream_t s) {
     case EPI_F32: hipLaunchKernelGGL(gemm_f32_k<EPI_F32>, g, dim3(256), 0, s, a); break;
     case EPI_SQR: hipLaunchKernelGGL(gemm_f32_k<EPI_SQR>, g, dim3(256), 0, s, a); break;
     case EPI_DSQR: hipLaunchKernelGGL(gemm_f32_k<EPI_DSQR>, g, dim3(256), 0, s, a); break;
+    case EPI_AXPBY: hipLaunchKernelGGL(gemm_f32_k<EPI_AXPBY>, g, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

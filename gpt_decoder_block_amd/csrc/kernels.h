@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+typedef __bf16 bf16;
+
 namespace gdb {
 
 // storage dtype of activations/weights; FP8 (OCP e4m3 codes) only names the
@@ -53,8 +55,10 @@ enum Epi {
                    // with the QK RMS-norm and RoPE applied to the q and k heads
                    // (columns < qk_heads*128) on the way out; rinv [M, qk_heads]
   EPI_SQR = 6,     // C = relu(acc)^2 only (the block saves h, not u)
-  EPI_DSQR = 7     // C = acc * 2*sqrt(max(R, 0)), R = saved h = relu(u)^2, so
+  EPI_DSQR = 7,    // C = acc * 2*sqrt(max(R, 0)), R = saved h = relu(u)^2, so
                    // 2*sqrt(h) = 2*relu(u) is the ReLU^2 derivative
+  EPI_AXPBY = 8    // C = alpha*acc + beta*R (dtype out, R must not alias C): the
+                   // Newton-Schulz lines b*A + c*A@A and a*X + X@B
 };
 struct GemmArgs {
   const void* A; const void* B;
@@ -65,6 +69,7 @@ struct GemmArgs {
   const void* R; int ldr;
   void* C2;
   int accumulate;      // EPI_F32
+  float alpha, beta;   // EPI_AXPBY
   float* partial;      // EPI_F32 split-K scratch [splits, M, N] or null
   int splits;          // >= 1
   const float* amax_a; // fp8: per-tensor amax of A and B (scales amax/448)
@@ -171,5 +176,25 @@ hipError_t backout_fwd(int dt, const void* x, const void* xb, const float* lam, 
 // dxb += -lam*dy (in place); dlam (+)= -sum(dy*xb)
 hipError_t backout_bwd(int dt, const void* dy, const void* xb, const float* lam, void* dxb, float* part, float* dlam,
                        int accumulate, int N, int C, hipStream_t s);
+
+// ------------------------------------------------------------------ optimizer
+constexpr int OPT_PART = 1024;  // most workgroups (partials) of the reductions below
+// partial sums of x^2 (n a multiple of 4); *np partials written
+hipError_t sumsq_partials(const float* x, size_t n, float* part, int* np, hipStream_t s);
+// buf = mu*buf + g; u = nesterov ? g + mu*buf : buf; partial sums of u^2
+hipError_t muon_momentum(const float* g, float* buf, float* u, size_t n, float mu, int nesterov, float* part,
+                         int* np, hipStream_t s);
+// inv[0] = 1 / (sqrt(sum part) * norm_scale + eps)
+hipError_t norm_final(const float* part, int np, float norm_scale, float eps, float* inv, hipStream_t s);
+// x = g * inv[0] (dtype dt)
+hipError_t scale_cast(int dt, const float* g, const float* inv, void* x, size_t n, hipStream_t s);
+// out = alpha * (sum of `splits` fp32 partials [splits][n]) + beta * R (dtype dt; R may be null)
+hipError_t splitk_axpby(int dt, const float* part, int splits, size_t n, float alpha, float beta, const void* R,
+                        void* out, hipStream_t s);
+// p = p*decay - step*x (x dtype dt); plow (bf16 copy of p) if non-null
+hipError_t muon_apply(int dt, float* p, const void* x, bf16* plow, size_t n, float decay, float step, hipStream_t s);
+// one AdamW step (t counts steps, this one included)
+hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* plow, size_t n, float lr, float b1, float b2,
+                 float eps, float wd, int t, hipStream_t s);
 
 }  // namespace gdb

@@ -1,0 +1,194 @@
+// Optimizer step after the backward, as the Japanese and French articles
+// describe it (section "2. Muonオプティマイザー" / "2. L'optimiseur Muon"):
+// AdamW for embeddings, lm_head and scalars; for matrices Muon, momentum
+// orthogonalised by the Polar Express Newton-Schulz loop
+//   A = X^T X;  B = b A + c A^2;  X = a X + X B.
+// The loop's three products run on the MFMA GEMM: the Gram (a long
+// contraction onto a small output) split over K into fp32 partials that one
+// pass adds and casts, the other two with the axpy in the GEMM's epilogue.
+// This file holds that pass and the bandwidth kernels around the products:
+// the Frobenius norm that scales the loop's input, the momentum update, the
+// parameter update and AdamW.  Reductions are deterministic: fixed grids
+// write one partial per workgroup, one workgroup adds them in order.
+#include "common.h"
+#include "kernels.h"
+
+namespace gdb {
+
+namespace {
+
+constexpr int OPT_NT = 256;
+
+// per-workgroup sums of squares of x [n] (n a multiple of 4)
+__device__ __forceinline__ float sumsq4(f32x4 v) { return v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]; }
+
+__global__ __launch_bounds__(OPT_NT) void sumsq_part_k(const float* __restrict__ x, size_t n4, float* part) {
+  __shared__ float red[OPT_NT / 64];
+  float acc = 0.f;
+  for (size_t i = (size_t)blockIdx.x * OPT_NT + threadIdx.x; i < n4; i += (size_t)gridDim.x * OPT_NT)
+    acc += sumsq4(((const f32x4*)x)[i]);
+  acc = block_sum<OPT_NT>(acc, red);
+  if (threadIdx.x == 0) part[blockIdx.x] = acc;
+}
+
+// momentum: buf = mu*buf + g; u = nesterov ? g + mu*buf : buf; partial sums of u^2
+__global__ __launch_bounds__(OPT_NT) void muon_momentum_k(const float* __restrict__ g, float* __restrict__ buf,
+                                                         float* __restrict__ u, size_t n4, float mu, int nesterov,
+                                                         float* part) {
+  __shared__ float red[OPT_NT / 64];
+  float acc = 0.f;
+  for (size_t i = (size_t)blockIdx.x * OPT_NT + threadIdx.x; i < n4; i += (size_t)gridDim.x * OPT_NT) {
+    const f32x4 gv = ((const f32x4*)g)[i];
+    const f32x4 b = mu * ((const f32x4*)buf)[i] + gv;
+    ((f32x4*)buf)[i] = b;
+    const f32x4 uv = nesterov ? gv + mu * b : b;
+    ((f32x4*)u)[i] = uv;
+    acc += sumsq4(uv);
+  }
+  acc = block_sum<OPT_NT>(acc, red);
+  if (threadIdx.x == 0) part[blockIdx.x] = acc;
+}
+
+// inv[0] = 1 / (sqrt(sum of the partials) * norm_scale + eps); thread t adds
+// partials t, t + 256, ... then a fixed tree (deterministic)
+__global__ __launch_bounds__(OPT_NT) void norm_final_k(const float* part, int np, float norm_scale, float eps,
+                                                       float* inv) {
+  __shared__ float red[OPT_NT / 64];
+  float acc = 0.f;
+  for (int i = threadIdx.x; i < np; i += OPT_NT) acc += part[i];
+  acc = block_sum<OPT_NT>(acc, red);
+  if (threadIdx.x == 0) inv[0] = 1.0f / (sqrtf(acc) * norm_scale + eps);
+}
+
+// x0 = g * inv[0] in the iteration's dtype
+template <typename T>
+__global__ __launch_bounds__(OPT_NT) void scale_cast_k(const float* __restrict__ g, const float* inv,
+                                                      T* __restrict__ x, size_t n4) {
+  const float sc = inv[0];
+  for (size_t i = (size_t)blockIdx.x * OPT_NT + threadIdx.x; i < n4; i += (size_t)gridDim.x * OPT_NT) {
+    const f32x4 v = ((const f32x4*)g)[i] * sc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[4 * i + e] = from_f<T>(v[e]);
+  }
+}
+
+// out = alpha * (sum of split-K partials) + beta * R, in the iteration's dtype
+// (R of that dtype, or null): the three lines of the Newton-Schulz loop
+template <typename T>
+__global__ __launch_bounds__(OPT_NT) void splitk_axpby_k(const float* __restrict__ part, int splits, size_t n4,
+                                                        float alpha, float beta, const T* __restrict__ R,
+                                                        T* __restrict__ out) {
+  for (size_t i = (size_t)blockIdx.x * OPT_NT + threadIdx.x; i < n4; i += (size_t)gridDim.x * OPT_NT) {
+    f32x4 acc = ((const f32x4*)part)[i];
+    for (int z = 1; z < splits; ++z) acc += ((const f32x4*)(part + (size_t)z * n4 * 4))[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v = alpha * acc[e];
+      if (R) v = fmaf(beta, to_f(R[4 * i + e]), v);
+      out[4 * i + e] = from_f<T>(v);
+    }
+  }
+}
+
+// p = p*(1 - lr*wd) - lr*scale*x; optional low-precision copy of p
+template <typename T>
+__global__ __launch_bounds__(OPT_NT) void muon_apply_k(float* __restrict__ p, const T* __restrict__ x,
+                                                      bf16* __restrict__ plow, size_t n4, float decay, float step) {
+  for (size_t i = (size_t)blockIdx.x * OPT_NT + threadIdx.x; i < n4; i += (size_t)gridDim.x * OPT_NT) {
+    f32x4 pv = ((f32x4*)p)[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pv[e] = pv[e] * decay - step * to_f(x[4 * i + e]);
+    ((f32x4*)p)[i] = pv;
+    if (plow) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) plow[4 * i + e] = (bf16)pv[e];
+    }
+  }
+}
+
+// AdamW with bias correction: rc1 = 1/(1 - beta1^t), rc2 = 1/(1 - beta2^t)
+__global__ __launch_bounds__(OPT_NT) void adamw_k(float* __restrict__ p, const float* __restrict__ g,
+                                                 float* __restrict__ m, float* __restrict__ v,
+                                                 bf16* __restrict__ plow, size_t n4, float lr, float b1, float b2,
+                                                 float eps, float decay, float rc1, float rc2) {
+  for (size_t i = (size_t)blockIdx.x * OPT_NT + threadIdx.x; i < n4; i += (size_t)gridDim.x * OPT_NT) {
+    const f32x4 gv = ((const f32x4*)g)[i];
+    f32x4 pv = ((f32x4*)p)[i], mv = ((f32x4*)m)[i], vv = ((f32x4*)v)[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mv[e] = b1 * mv[e] + (1.0f - b1) * gv[e];
+      vv[e] = b2 * vv[e] + (1.0f - b2) * gv[e] * gv[e];
+      pv[e] = pv[e] * decay - lr * (mv[e] * rc1) / (sqrtf(vv[e] * rc2) + eps);
+    }
+    ((f32x4*)p)[i] = pv;
+    ((f32x4*)m)[i] = mv;
+    ((f32x4*)v)[i] = vv;
+    if (plow) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) plow[4 * i + e] = (bf16)pv[e];
+    }
+  }
+}
+
+unsigned grid_for(size_t n4) {
+  const size_t b = (n4 + OPT_NT - 1) / OPT_NT;
+  return (unsigned)(b < (size_t)OPT_PART ? (b ? b : 1) : (size_t)OPT_PART);
+}
+
+}  // namespace
+
+hipError_t sumsq_partials(const float* x, size_t n, float* part, int* np, hipStream_t s) {
+  *np = (int)grid_for(n / 4);
+  hipLaunchKernelGGL(sumsq_part_k, dim3(*np), dim3(OPT_NT), 0, s, x, n / 4, part);
+  return hipGetLastError();
+}
+
+hipError_t muon_momentum(const float* g, float* buf, float* u, size_t n, float mu, int nesterov, float* part,
+                         int* np, hipStream_t s) {
+  *np = (int)grid_for(n / 4);
+  hipLaunchKernelGGL(muon_momentum_k, dim3(*np), dim3(OPT_NT), 0, s, g, buf, u, n / 4, mu, nesterov, part);
+  return hipGetLastError();
+}
+
+hipError_t norm_final(const float* part, int np, float norm_scale, float eps, float* inv, hipStream_t s) {
+  hipLaunchKernelGGL(norm_final_k, dim3(1), dim3(OPT_NT), 0, s, part, np, norm_scale, eps, inv);
+  return hipGetLastError();
+}
+
+hipError_t scale_cast(int dt, const float* g, const float* inv, void* x, size_t n, hipStream_t s) {
+  if (dt == BF16) hipLaunchKernelGGL(scale_cast_k<bf16>, dim3(grid_for(n / 4)), dim3(OPT_NT), 0, s, g, inv, (bf16*)x, n / 4);
+  else hipLaunchKernelGGL(scale_cast_k<float>, dim3(grid_for(n / 4)), dim3(OPT_NT), 0, s, g, inv, (float*)x, n / 4);
+  return hipGetLastError();
+}
+
+hipError_t splitk_axpby(int dt, const float* part, int splits, size_t n, float alpha, float beta, const void* R,
+                        void* out, hipStream_t s) {
+  if (dt == BF16)
+    hipLaunchKernelGGL(splitk_axpby_k<bf16>, dim3(grid_for(n / 4)), dim3(OPT_NT), 0, s, part, splits, n / 4, alpha,
+                       beta, (const bf16*)R, (bf16*)out);
+  else
+    hipLaunchKernelGGL(splitk_axpby_k<float>, dim3(grid_for(n / 4)), dim3(OPT_NT), 0, s, part, splits, n / 4, alpha,
+                       beta, (const float*)R, (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t muon_apply(int dt, float* p, const void* x, bf16* plow, size_t n, float decay, float step, hipStream_t s) {
+  if (dt == BF16)
+    hipLaunchKernelGGL(muon_apply_k<bf16>, dim3(grid_for(n / 4)), dim3(OPT_NT), 0, s, p, (const bf16*)x, plow, n / 4,
+                       decay, step);
+  else
+    hipLaunchKernelGGL(muon_apply_k<float>, dim3(grid_for(n / 4)), dim3(OPT_NT), 0, s, p, (const float*)x, plow,
+                       n / 4, decay, step);
+  return hipGetLastError();
+}
+
+hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* plow, size_t n, float lr, float b1, float b2,
+                 float eps, float wd, int t, hipStream_t s) {
+  const float rc1 = (float)(1.0 / (1.0 - std::pow((double)b1, (double)t)));
+  const float rc2 = (float)(1.0 / (1.0 - std::pow((double)b2, (double)t)));
+  hipLaunchKernelGGL(adamw_k, dim3(grid_for(n / 4)), dim3(OPT_NT), 0, s, p, g, m, v, plow, n / 4, lr, b1, b2, eps,
+                     1.0f - lr * wd, rc1, rc2);
+  return hipGetLastError();
+}
+
+}  // namespace gdb

@@ -254,6 +254,48 @@ def attention_decode(B: int, H: int, Hkv: int, D: int, window: int, q: torch.Ten
            bstride, _p(lens), max_len, _p(o), ldo, _opt(lse), _opt(ws), nbytes, _stream(q))
 
 
+def _coeffs(coeffs):
+    flat = [float(x) for t in coeffs for x in t]
+    return (ctypes.c_float * max(len(flat), 1))(*flat), len(flat) // 3
+
+
+def newton_schulz_ws_bytes(m: int, n: int, dtype: torch.dtype) -> int:
+    s = ctypes.c_size_t()
+    L.call("gdb_newton_schulz_ws_bytes", m, n, dtype_code(dtype), ctypes.byref(s))
+    return s.value
+
+
+def newton_schulz(G: torch.Tensor, X: torch.Tensor, coeffs, norm_scale: float = 1.0, eps: float = 1e-7,
+                  ws=None) -> None:
+    """X (dtype of X) = the Newton-Schulz map of the float32 matrix G [m, n]."""
+    m, n = G.shape
+    arr, steps = _coeffs(coeffs)
+    L.call("gdb_newton_schulz", m, n, dtype_code(X.dtype), _p(G), _p(X), arr, steps, norm_scale, eps, _p(ws),
+           ws.numel() * ws.element_size(), _stream(G))
+
+
+def muon_ws_bytes(m: int, n: int, dtype: torch.dtype) -> int:
+    s = ctypes.c_size_t()
+    L.call("gdb_muon_ws_bytes", m, n, dtype_code(dtype), ctypes.byref(s))
+    return s.value
+
+
+def muon_step(p: torch.Tensor, g: torch.Tensor, buf: torch.Tensor, lr: float, momentum: float, nesterov: bool,
+              wd: float, scale: float, coeffs, dtype: torch.dtype, ws: torch.Tensor, p_bf16=None,
+              norm_scale: float = 1.0, eps: float = 1e-7) -> None:
+    m, n = p.shape
+    arr, steps = _coeffs(coeffs)
+    L.call("gdb_muon_step", m, n, dtype_code(dtype), _p(p), _opt(p_bf16), _p(g), _p(buf), lr, momentum,
+           int(nesterov), wd, scale, arr, steps, norm_scale, eps, _p(ws), ws.numel() * ws.element_size(),
+           _stream(p))
+
+
+def adamw_step(p: torch.Tensor, g: torch.Tensor, m: torch.Tensor, v: torch.Tensor, t: int, lr: float,
+               beta1: float, beta2: float, eps: float, wd: float, p_bf16=None) -> None:
+    L.call("gdb_adamw_step", p.numel(), _p(p), _opt(p_bf16), _p(g), _p(m), _p(v), t, lr, beta1, beta2, eps, wd,
+           _stream(p))
+
+
 def cross_entropy(z: torch.Tensor, targets: torch.Tensor, row_loss: torch.Tensor, loss: torch.Tensor) -> None:
     N, V = z.shape
     L.call("gdb_cross_entropy", N, V, dtype_code(z.dtype), _p(z), _p(targets), _p(row_loss), _p(loss),

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define GDB_ABI_VERSION 3
+#define GDB_ABI_VERSION 4
 
 /* Scratch bytes that gdb_smear_bwd and gdb_backout_bwd need in `ws`. */
 #define GDB_EXTRAS_WS_BYTES ((size_t)1 << 20)
@@ -360,6 +360,42 @@ gdb_status gdb_attention_decode(int32_t B, int32_t H, int32_t Hkv, int32_t D, in
                                 const void* q, int32_t ldq, const void* k, const void* v, int32_t ldk,
                                 int64_t bstride, const int32_t* lens, int32_t max_len, void* o, int32_t ldo,
                                 float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Optimizer step after the backward (the Japanese and French articles,
+ * section 2 on the Muon optimizer): AdamW for embeddings, lm_head and scalar
+ * parameters; Muon for matrices, i.e. momentum orthogonalised by the Polar
+ * Express Newton-Schulz loop, one (a, b, c) triple per iteration:
+ *   A = X^T X;  B = b*A + c*A@A;  X = a*X + X@B,
+ * starting from X0 = G / (||G||_F * norm_scale + eps).  The coefficient table
+ * is the caller's (the pages print two of its five triples).  The products
+ * run on the MFMA GEMM in `dtype` (bf16: bf16 operands and results, fp32
+ * accumulation; fp32: all fp32); a wide matrix (m < n) takes the Gram on the
+ * other side, X X^T (the same map).
+ *
+ * gdb_newton_schulz: G float32 [m, n] -> X [m, n] in `dtype` (X != G).
+ *   coeffs: HOST float [steps][3]; m, n multiples of 8; steps in [0, 64].
+ *   ws: gdb_newton_schulz_ws_bytes bytes of scratch. */
+gdb_status gdb_newton_schulz_ws_bytes(int32_t m, int32_t n, int32_t dtype, size_t* ws_bytes);
+gdb_status gdb_newton_schulz(int32_t m, int32_t n, int32_t dtype, const float* G, void* X, const float* coeffs,
+                             int32_t steps, float norm_scale, float eps, void* ws, size_t ws_bytes, void* stream);
+/* gdb_muon_step on a matrix parameter p float32 [m, n] with gradient g and
+ * momentum buffer buf (float32, updated in place):
+ *   buf = momentum*buf + g;  U = nesterov ? g + momentum*buf : buf;
+ *   p = p*(1 - lr*wd) - lr*scale*NS(U)
+ * (the momentum form, decay and the shape scale are inputs: the pages name
+ * Muon only as momentum orthogonalised by Newton-Schulz).  p_bf16 (optional,
+ * NULL to skip) receives the bf16 rounding of the new p.
+ * ws: gdb_muon_ws_bytes bytes. */
+gdb_status gdb_muon_ws_bytes(int32_t m, int32_t n, int32_t dtype, size_t* ws_bytes);
+gdb_status gdb_muon_step(int32_t m, int32_t n, int32_t dtype, float* p, void* p_bf16, const float* g, float* buf,
+                         float lr, float momentum, int32_t nesterov, float wd, float scale, const float* coeffs,
+                         int32_t steps, float norm_scale, float eps, void* ws, size_t ws_bytes, void* stream);
+/* gdb_adamw_step on n float32 parameters (n a multiple of 8), step t >= 1:
+ *   p *= 1 - lr*wd;  m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*g^2;
+ *   p -= lr * (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
+ * (decoupled weight decay with bias correction).  p_bf16 optional as above. */
+gdb_status gdb_adamw_step(int64_t n, float* p, void* p_bf16, const float* g, float* m, float* v, int32_t t, float lr,
+                          float beta1, float beta2, float eps, float wd, void* stream);
 
 /* Fused softmax cross-entropy on logits z [N, V] (overwritten by
  * dz = (softmax(z) - onehot(targets)) / N), row_loss float32 [N] =

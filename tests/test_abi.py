@@ -267,3 +267,45 @@ def test_attention_decode_validation(L):
     assert call(lse=al + 4) == L.GDB_EINVAL
     assert call(ws=None) == L.GDB_EINVAL
     assert call(ws_bytes=16) == L.GDB_EWORKSPACE
+
+
+def test_optimizer_validation(L):
+    lib = L.lib()
+    buf = ctypes.create_string_buffer(4096)
+    al = (ctypes.addressof(buf) + 255) & ~255
+    nb = ctypes.c_size_t()
+    co = (ctypes.c_float * 6)(8.156, -22.483, 15.879, 4.043, -2.809, 0.5)
+    assert lib.gdb_newton_schulz_ws_bytes(1536, 6144, 1, ctypes.byref(nb)) == L.GDB_OK and nb.value > 0
+    big = nb.value
+
+    def ns(m=64, n=32, dtype=1, G=al, X=al + 256, coeffs=co, steps=2, ns_=1.0, eps=1e-7, ws=al, wsb=big):
+        return lib.gdb_newton_schulz(m, n, dtype, G, X, coeffs, steps, ctypes.c_float(ns_), ctypes.c_float(eps), ws,
+                                     wsb, None)
+
+    assert ns(m=60) == L.GDB_EINVAL and "multiples of 8" in lib.gdb_last_error().decode()
+    assert ns(dtype=5) == L.GDB_EINVAL
+    assert ns(steps=65) == L.GDB_EINVAL
+    assert ns(coeffs=None) == L.GDB_EINVAL
+    assert ns(coeffs=(ctypes.c_float * 6)(1, float("nan"), 0, 1, 1, 1)) == L.GDB_EINVAL
+    assert ns(ns_=0.0) == L.GDB_EINVAL
+    assert ns(X=al) == L.GDB_EINVAL and "alias" in lib.gdb_last_error().decode()
+    assert ns(wsb=16) == L.GDB_EWORKSPACE
+    assert ns(G=al + 4) == L.GDB_EINVAL
+    # AdamW
+    f = ctypes.c_float
+    assert lib.gdb_adamw_step(12, al, None, al, al, al, 1, f(1e-3), f(0.9), f(0.95), f(1e-8), f(0.0), None) \
+        == L.GDB_EINVAL
+    assert lib.gdb_adamw_step(16, al, None, al, al, al, 0, f(1e-3), f(0.9), f(0.95), f(1e-8), f(0.0), None) \
+        == L.GDB_EINVAL
+    assert lib.gdb_adamw_step(16, al, None, al, al, al, 1, f(1e-3), f(1.0), f(0.95), f(1e-8), f(0.0), None) \
+        == L.GDB_EINVAL
+    assert lib.gdb_adamw_step(16, al, al + 2, al, al, al, 1, f(1e-3), f(0.9), f(0.95), f(1e-8), f(0.0), None) \
+        == L.GDB_EINVAL
+    # Muon
+    assert lib.gdb_muon_ws_bytes(64, 32, 1, ctypes.byref(nb)) == L.GDB_OK
+    st = lib.gdb_muon_step(64, 32, 1, al, None, al, None, f(0.02), f(0.95), 1, f(0.0), f(1.0), co, 2, f(1.0),
+                           f(1e-7), al, nb.value, None)
+    assert st == L.GDB_EINVAL and "buf is NULL" in lib.gdb_last_error().decode()
+    st = lib.gdb_muon_step(64, 32, 1, al, None, al, al, f(float("inf")), f(0.95), 1, f(0.0), f(1.0), co, 2, f(1.0),
+                           f(1e-7), al, nb.value, None)
+    assert st == L.GDB_EINVAL

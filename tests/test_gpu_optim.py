@@ -1,0 +1,110 @@
+"""Parity of the optimizer step (Newton-Schulz orthogonalisation on the MFMA
+GEMM, Muon, AdamW) with the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpt_decoder_block_amd import ops
+from gpu_util import DEV, TDT, TOL, assert_close, host, rounded
+
+pytestmark = pytest.mark.gpu
+
+PE_PRINTED = [(8.156, -22.483, 15.879), (4.043, -2.809, 0.500)]   # the two triples the pages print
+# five iterations: the printed two, then the textbook cubic Newton-Schulz step
+FIVE = PE_PRINTED + [(1.5, -0.5, 0.0)] * 3
+
+def ns_bar(dt, G, coeffs, norm_scale=1.02, eps=1e-7):
+    """Bar of a Newton-Schulz result against the exact map.  fp32: the suite's
+    1e-4.  bf16: every line of the loop is stored in bf16, and the printed
+    first step sums terms up to 30 times its result (8.156 - 22.483 + 15.879
+    = 1.552 at a unit singular value), so storage rounding alone moves the
+    result by percents.  The bar is twice that move, measured by the oracle
+    with its three lines' results rounded to bf16, and never below 2e-2 (the
+    same rule as the fp8 bars: twice the oracle's own spread)."""
+    if dt == "f32":
+        return TOL["f32"]
+    exact = O.newton_schulz(G, coeffs, norm_scale, eps)
+    stored = O.newton_schulz(G, coeffs, norm_scale, eps, round_to="bf16")
+    spread = float(np.max(np.abs(stored - exact)) / np.max(np.abs(exact)))
+    return max(TOL["bf16"], 2.0 * spread)
+
+
+def _ns_case(dt, m, n, coeffs, seed):
+    G = np.random.default_rng(seed).standard_normal((m, n)).astype(np.float32)
+    Gg = torch.from_numpy(G).to(DEV)
+    X = torch.full((m, n), float("nan"), dtype=TDT[dt], device=DEV)
+    ws = torch.empty(ops.newton_schulz_ws_bytes(m, n, TDT[dt]), dtype=torch.uint8, device=DEV)
+    print(f"newton_schulz dt={dt} m={m} n={n} steps={len(coeffs)}", flush=True)
+    ops.newton_schulz(Gg, X, coeffs, norm_scale=1.02, eps=1e-7, ws=ws)
+    torch.cuda.synchronize()
+    G = G.astype(np.float64)
+    return X, O.newton_schulz(G, coeffs, 1.02, 1e-7), G
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("m,n", [(256, 256), (768, 256), (256, 768), (136, 200), (1024, 512)])
+def test_newton_schulz(dt, m, n):
+    X, ref, G = _ns_case(dt, m, n, FIVE, m + n)
+    bar = ns_bar(dt, G, FIVE)
+    e = assert_close(X, ref, dt, "X", tol=bar)
+    print(f"newton_schulz err {e:.3e} bar {bar:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_newton_schulz_steps_zero_one_two(dt):
+    # zero steps: the normalised input; odd and even step counts end in X
+    for coeffs in ([], PE_PRINTED[:1], PE_PRINTED):
+        X, ref, G = _ns_case(dt, 200, 96, coeffs, 7)
+        assert_close(X, ref, dt, f"X ({len(coeffs)} steps)", tol=ns_bar(dt, G, coeffs))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("nesterov", [True, False])
+def test_muon_step(dt, nesterov):
+    m, n = 384, 128
+    g = np.random.default_rng(3)
+    p = g.standard_normal((m, n)).astype(np.float32) * 0.02
+    gr = g.standard_normal((m, n)).astype(np.float32)
+    buf = g.standard_normal((m, n)).astype(np.float32) * 0.5
+    pg, gg, bg = (torch.from_numpy(a.copy()).to(DEV) for a in (p, gr, buf))
+    plow = torch.empty(m, n, dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(ops.muon_ws_bytes(m, n, TDT[dt]), dtype=torch.uint8, device=DEV)
+    lr, mu, wd, sc = 0.02, 0.95, 0.1, 1.7
+    print(f"muon dt={dt} nesterov={nesterov}", flush=True)
+    ops.muon_step(pg, gg, bg, lr, mu, nesterov, wd, sc, FIVE, TDT[dt], ws, p_bf16=plow, norm_scale=1.02)
+    torch.cuda.synchronize()
+    p_ref, b_ref = O.muon_step(p.astype(np.float64), gr.astype(np.float64), buf.astype(np.float64), lr, mu,
+                               nesterov, wd, sc, FIVE, 1.02, 1e-7)
+    assert_close(bg, b_ref, "f32", "buf")
+    # the update is lr*scale*NS(.): compare it, so the bar is the iteration's
+    upd = (p.astype(np.float64) * (1 - lr * wd) - host(pg)) / (lr * sc)
+    upd_ref = (p.astype(np.float64) * (1 - lr * wd) - p_ref) / (lr * sc)
+    b64 = b_ref
+    u = gr.astype(np.float64) + mu * b64 if nesterov else b64
+    bar = ns_bar(dt, u, FIVE)
+    e = assert_close(upd, upd_ref, dt, "update", tol=bar)
+    print(f"muon update err {e:.3e} bar {bar:.3e}", flush=True)
+    assert_close(plow, rounded(host(pg), "bf16"), "f32", "p_bf16", tol=0.0)
+
+
+def test_adamw_step():
+    n = 4104
+    g = np.random.default_rng(4)
+    p = g.standard_normal(n).astype(np.float32)
+    pg = torch.from_numpy(p.copy()).to(DEV)
+    mg, vg = torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
+    plow = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    pr, mr, vr = p.astype(np.float64), np.zeros(n), np.zeros(n)
+    for t in range(1, 5):
+        gr = g.standard_normal(n).astype(np.float32)
+        print(f"adamw t={t}", flush=True)
+        ops.adamw_step(pg, torch.from_numpy(gr).to(DEV), mg, vg, t, 3e-3, 0.8, 0.95, 1e-8, 0.1, p_bf16=plow)
+        pr, mr, vr = O.adamw_step(pr, gr.astype(np.float64), mr, vr, t, 3e-3, 0.8, 0.95, 1e-8, 0.1)
+    torch.cuda.synchronize()
+    # fp32 arithmetic: the change of p (a few lr) to 1e-4 of its size, m and v to 1e-5
+    dp, dp_ref = host(pg) - p, pr - p
+    assert_close(dp, dp_ref, "f32", "p - p0", tol=1e-4)
+    assert_close(mg, mr, "f32", "m", tol=1e-5)
+    assert_close(vg, vr, "f32", "v", tol=1e-5)
+    assert_close(plow, rounded(host(pg), "bf16"), "f32", "p_bf16", tol=0.0)
