@@ -52,16 +52,27 @@ def newton_schulz(G: np.ndarray, coeffs: Sequence[Tuple[float, float, float]], n
 
     round_to="bf16" rounds the normalised input and the result of each of the
     three lines to bfloat16 (an iteration run in bf16 storage with exact
-    arithmetic inside each line); used only to measure how far bf16 storage
-    alone moves the exact map, never as the reference."""
-    rnd = (lambda a: a) if round_to is None else bf16_round
+    arithmetic inside each line), on the side whose Gram matrix is the
+    smaller one (a wide matrix iterates on its transpose; the exact map is
+    the same on either side, the rounding is not); used only to measure how
+    far bf16 storage alone moves the exact map, never as the reference."""
     X = np.asarray(G, dtype=np.float64)
-    X = rnd(X / (np.linalg.norm(X) * norm_scale + eps))
+    if round_to is None:
+        X = X / (np.linalg.norm(X) * norm_scale + eps)
+        for a, b, c in coeffs:
+            A = X.T @ X
+            B = b * A + c * (A @ A)
+            X = a * X + X @ B
+        return X
+    wide = X.shape[0] < X.shape[1]
+    if wide:
+        X = X.T
+    X = bf16_round(X / (np.linalg.norm(X) * norm_scale + eps))
     for a, b, c in coeffs:
-        A = rnd(X.T @ X)
-        B = rnd(b * A + c * (A @ A))
-        X = rnd(a * X + X @ B)
-    return X
+        A = bf16_round(X.T @ X)
+        B = bf16_round(b * A + c * (A @ A))
+        X = bf16_round(a * X + X @ B)
+    return X.T if wide else X
 
 
 def adamw_step(p, g, m, v, t: int, lr: float, beta1: float, beta2: float, eps: float, wd: float):

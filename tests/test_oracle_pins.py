@@ -545,3 +545,7 @@ def test_newton_schulz_bf16_storage_option():
     np.testing.assert_array_equal(O.newton_schulz(G, [], 1.0, round_to="bf16"), O.bf16_round(x0))
     d = np.max(np.abs(O.newton_schulz(G, PE_PRINTED, round_to="bf16") - O.newton_schulz(G, PE_PRINTED)))
     assert 1e-5 < d < 0.1 * np.max(np.abs(O.newton_schulz(G, PE_PRINTED)))
+    # a wide matrix is stored-and-iterated on its transpose: the transposed
+    # input gives exactly the transposed result
+    np.testing.assert_array_equal(O.newton_schulz(G.T, PE_PRINTED, round_to="bf16"),
+                                  O.newton_schulz(G, PE_PRINTED, round_to="bf16").T)
