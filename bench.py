@@ -194,18 +194,20 @@ def kernel_figures(w, st, reps, torch, ops):
         out[f"attn_decode_{key}"] = {"shape": [w.B, w.T, H, Hkv, D], "ms": t * 1e3, "GBps": by / t / 1e9,
                                      "frac_hbm_peak": by / t / PEAK_HBM}
     del kc, vc
-    # optimizer step (after the backward): Muon on the MLP up-projection
-    # matrix (momentum, 5 Newton-Schulz iterations on the MFMA GEMM, update),
-    # AdamW over the embedding and lm_head tables (bandwidth)
+    # optimizer step (after the backward): Muon on the stack of every layer's
+    # MLP up-projection matrix (momentum, 5 Newton-Schulz iterations as
+    # batched MFMA GEMMs, update), AdamW over the embedding and lm_head tables
     coeffs = [(8.156, -22.483, 15.879), (4.043, -2.809, 0.5)] + [(1.5, -0.5, 0.0)] * 3
-    pm = rnd(F, C).float()
-    gm, bm = rnd(F, C).float(), torch.zeros(F, C, dtype=torch.float32, device=dev)
-    wsm = torch.empty(ops.muon_ws_bytes(F, C, dt), dtype=torch.uint8, device=dev)
-    t = ev_time(lambda: ops.muon_step(pm, gm, bm, 0.02, 0.95, True, 0.0, 1.0, coeffs, dt, wsm), reps, torch)
+    nl = w.n_layer
+    pm = torch.zeros(nl, F, C, dtype=torch.float32, device=dev)
+    gm, bm = rnd(nl, F, C).float(), torch.zeros(nl, F, C, dtype=torch.float32, device=dev)
+    wsm = torch.empty(ops.muon_ws_bytes(F, C, dt, nl), dtype=torch.uint8, device=dev)
+    t = ev_time(lambda: ops.muon_step(pm, gm, bm, 0.02, 0.95, True, 0.0, 1.0, coeffs, dt, wsm), max(2, reps // 5),
+                torch)
     s_, L_ = min(F, C), max(F, C)
-    fl = len(coeffs) * (4.0 * s_ * s_ * L_ + 2.0 * s_ ** 3)
-    out["muon_step_w_fc"] = {"shape": [F, C], "ns_steps": len(coeffs), "ms": t * 1e3, "tflops": fl / t / 1e12,
-                             "frac_bf16_peak": fl / t / PEAK_BF16}
+    fl = nl * len(coeffs) * (4.0 * s_ * s_ * L_ + 2.0 * s_ ** 3)
+    out["muon_step_w_fc_stack"] = {"shape": [nl, F, C], "ns_steps": len(coeffs), "ms": t * 1e3,
+                                   "tflops": fl / t / 1e12, "frac_bf16_peak": fl / t / PEAK_BF16}
     del pm, gm, bm, wsm
     na = 2 * V * C
     pa, ga = torch.zeros(na, dtype=torch.float32, device=dev), rnd(na).float()

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgdb.so")
 
 # the GDB_ABI_VERSION this binding's structures and signatures follow
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 GDB_OK, GDB_EINVAL, GDB_EUNSUPPORTED, GDB_EHIP, GDB_EWORKSPACE = 0, -1, -2, -3, -4
 GDB_F32, GDB_BF16 = 0, 1
@@ -113,13 +113,13 @@ SIGNATURES = {
                                     c_void_p, c_void_p]),
     "gdb_cross_entropy": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_void_p]),
-    "gdb_newton_schulz_ws_bytes": (c_int32, [c_int32, c_int32, c_int32, ctypes.POINTER(c_size_t)]),
-    "gdb_newton_schulz": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_float,
-                                    c_float, c_void_p, c_size_t, c_void_p]),
-    "gdb_muon_ws_bytes": (c_int32, [c_int32, c_int32, c_int32, ctypes.POINTER(c_size_t)]),
-    "gdb_muon_step": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_float,
-                                c_int32, c_float, c_float, c_void_p, c_int32, c_float, c_float, c_void_p, c_size_t,
-                                c_void_p]),
+    "gdb_newton_schulz_ws_bytes": (c_int32, [c_int32, c_int32, c_int32, c_int32, ctypes.POINTER(c_size_t)]),
+    "gdb_newton_schulz": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int32,
+                                    c_float, c_float, c_void_p, c_size_t, c_void_p]),
+    "gdb_muon_ws_bytes": (c_int32, [c_int32, c_int32, c_int32, c_int32, ctypes.POINTER(c_size_t)]),
+    "gdb_muon_step": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_float,
+                                c_float, c_int32, c_float, c_float, c_void_p, c_int32, c_float, c_float, c_void_p,
+                                c_size_t, c_void_p]),
     "gdb_adamw_step": (c_int32, [c_int64, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_float,
                                  c_float, c_float, c_float, c_void_p]),
     "gdb_attention_decode_ws_bytes": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,

@@ -795,35 +795,37 @@ gdb_status gdb_attention_decode(int32_t B, int32_t H, int32_t Hkv, int32_t D, in
 namespace {
 size_t al256(size_t b) { return (b + 255) / 256 * 256; }
 
-// workspace of the Newton-Schulz iteration on an [m, n] matrix; with `muon`
-// also the fp32 momentum-blended matrix and the iteration's output
+// workspace of the Newton-Schulz iteration on a stack of `count` [m, n]
+// matrices; with `muon` also the fp32 momentum-blended stack and the
+// iteration's output
 struct NsWs {
   size_t x, xa, a, bm, part, npart, inv, u, total;
 };
-// split count of the Gram product (the other two run unsplit)
-int ns_gram_splits(int m, int n, int dt) {
+// split count of the Gram product of a single matrix (a stack runs its
+// products unsplit, batched over the items)
+int ns_gram_splits(int count, int m, int n, int dt) {
   const int s_ = std::min(m, n), L = std::max(m, n);
-  return gemm_splits(dt, s_, s_, L, EPI_F32);
+  return count > 1 ? 1 : gemm_splits(dt, s_, s_, L, EPI_F32);
 }
 
-NsWs ns_layout(int m, int n, int dt, bool muon) {
+NsWs ns_layout(int count, int m, int n, int dt, bool muon) {
   const int s_ = std::min(m, n);
-  const size_t es = dt_size(dt);
-  const size_t part = (size_t)ns_gram_splits(m, n, dt) * s_ * s_ * 4;
+  const size_t es = dt_size(dt), mn = (size_t)count * m * n, ss = (size_t)count * s_ * s_;
   NsWs w{};
   size_t o = 0;
-  if (muon) { w.u = o; o += al256((size_t)m * n * 4); w.x = o; o += al256((size_t)m * n * es); }
-  w.xa = o; o += al256((size_t)m * n * es);
-  w.a = o; o += al256((size_t)s_ * s_ * es);
-  w.bm = o; o += al256((size_t)s_ * s_ * es);
-  w.part = o; o += al256(part);
-  w.npart = o; o += al256((size_t)OPT_PART * 4);
-  w.inv = o; o += 256;
+  if (muon) { w.u = o; o += al256(mn * 4); w.x = o; o += al256(mn * es); }
+  w.xa = o; o += al256(mn * es);
+  w.a = o; o += al256(ss * es);
+  w.bm = o; o += al256(ss * es);
+  w.part = o; o += count > 1 ? 0 : al256((size_t)ns_gram_splits(count, m, n, dt) * s_ * s_ * 4);
+  w.npart = o; o += al256((size_t)count * OPT_PART * 4);
+  w.inv = o; o += al256((size_t)count * 4);
   w.total = o;
   return w;
 }
 
-gdb_status check_ns(int m, int n, int dtype, const float* coeffs, int steps) {
+gdb_status check_ns(int count, int m, int n, int dtype, const float* coeffs, int steps) {
+  if (count <= 0 || count > 65535) return fail(GDB_EINVAL, "count must be in [1, 65535]");
   if (m <= 0 || n <= 0 || m % 8 || n % 8) return fail(GDB_EINVAL, "m, n must be positive multiples of 8");
   if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
   if (steps < 0 || steps > 64) return fail(GDB_EINVAL, "steps must be in [0, 64]");
@@ -835,31 +837,43 @@ gdb_status check_ns(int m, int n, int dtype, const float* coeffs, int steps) {
 
 // the iteration from x0 (already in `start`), ending in `out`; `other` is the
 // ping-pong partner.  Tall matrices take the Gram X^T X, wide ones X X^T
-// (the same map: X p(X^T X) = p(X X^T) X).  The Gram runs split over K into
-// fp32 partials, added and cast in one pass; the other two lines apply their
-// axpy in the GEMM epilogue.
-hipError_t ns_iterate(int dt, int m, int n, const float* coeffs, int steps, void* out, void* other, void* A,
-                      void* Bm, float* part, hipStream_t s) {
+// (the same map: X p(X^T X) = p(X X^T) X).  A single matrix runs its Gram
+// split over K into fp32 partials, added and cast in one pass; a stack runs
+// every product as one batched launch over its items.  The two other lines
+// apply their axpy in the GEMM epilogue.
+hipError_t ns_iterate(int dt, int count, int m, int n, const float* coeffs, int steps, void* out, void* other,
+                      void* A, void* Bm, float* part, hipStream_t s) {
   const bool tall = m >= n;
   const int s_ = tall ? n : m, L = tall ? m : n;
-  const int spg = ns_gram_splits(m, n, dt);
+  const int spg = ns_gram_splits(count, m, n, dt);
+  const long long smn = (long long)m * n, sss = (long long)s_ * s_;
+  auto batched = [&](GemmArgs g, long long sa, long long sb, long long sc, long long sr) {
+    g.batch = count;
+    g.bsA = sa; g.bsB = sb; g.bsC = sc; g.bsR = sr;
+    return g;
+  };
   void* cur = steps % 2 == 0 ? out : other;
   for (int it = 0; it < steps; ++it) {
     const float a = coeffs[3 * it], b = coeffs[3 * it + 1], c = coeffs[3 * it + 2];
     void* nxt = cur == out ? other : out;
     // A = X^T X (tall: both operands M/N-contiguous) or X X^T (wide: both K-contiguous)
-    GemmArgs g = gemm_args(cur, !tall, n, cur, !tall, n, s_, s_, L, EPI_F32, part, s_);
-    g.splits = spg;
-    g.partial = part;
-    hipError_t e = gemm(dt, g, s);
-    if (e == hipSuccess) e = splitk_axpby(dt, part, spg, (size_t)s_ * s_, 1.0f, 0.0f, nullptr, A, s);
+    hipError_t e;
+    if (count == 1) {
+      GemmArgs g = gemm_args(cur, !tall, n, cur, !tall, n, s_, s_, L, EPI_F32, part, s_);
+      g.splits = spg;
+      g.partial = part;
+      e = gemm(dt, g, s);
+      if (e == hipSuccess) e = splitk_axpby(dt, part, spg, (size_t)sss, 1.0f, 0.0f, nullptr, A, s);
+    } else {
+      e = gemm(dt, batched(gemm_args(cur, !tall, n, cur, !tall, n, s_, s_, L, EPI_STORE, A, s_), smn, smn, sss, 0), s);
+    }
     // B = b A + c A A (A symmetric: its rows serve as the second operand's K-contiguous rows)
-    GemmArgs g2 = gemm_args(A, true, s_, A, true, s_, s_, s_, s_, EPI_AXPBY, Bm, s_);
+    GemmArgs g2 = batched(gemm_args(A, true, s_, A, true, s_, s_, s_, s_, EPI_AXPBY, Bm, s_), sss, sss, sss, sss);
     g2.R = A; g2.ldr = s_; g2.alpha = c; g2.beta = b;
     if (e == hipSuccess) e = gemm(dt, g2, s);
     // X' = a X + X B (tall) or a X + B X (wide); B symmetric
-    GemmArgs g3 = tall ? gemm_args(cur, true, n, Bm, true, s_, m, n, s_, EPI_AXPBY, nxt, n)
-                       : gemm_args(Bm, true, s_, cur, false, n, m, n, s_, EPI_AXPBY, nxt, n);
+    GemmArgs g3 = tall ? batched(gemm_args(cur, true, n, Bm, true, s_, m, n, s_, EPI_AXPBY, nxt, n), smn, sss, smn, smn)
+                       : batched(gemm_args(Bm, true, s_, cur, false, n, m, n, s_, EPI_AXPBY, nxt, n), sss, smn, smn, smn);
     g3.R = cur; g3.ldr = n; g3.alpha = 1.0f; g3.beta = a;
     if (e == hipSuccess) e = gemm(dt, g3, s);
     if (e != hipSuccess) return e;
@@ -869,23 +883,24 @@ hipError_t ns_iterate(int dt, int m, int n, const float* coeffs, int steps, void
 }
 }  // namespace
 
-gdb_status gdb_newton_schulz_ws_bytes(int32_t m, int32_t n, int32_t dtype, size_t* ws_bytes) {
-  gdb_status st = check_ns(m, n, dtype, nullptr, 0);
+gdb_status gdb_newton_schulz_ws_bytes(int32_t count, int32_t m, int32_t n, int32_t dtype, size_t* ws_bytes) {
+  gdb_status st = check_ns(count, m, n, dtype, nullptr, 0);
   if (st != GDB_OK) return st;
   if (!ws_bytes) return fail(GDB_EINVAL, "ws_bytes is NULL");
-  *ws_bytes = ns_layout(m, n, dtype, false).total;
+  *ws_bytes = ns_layout(count, m, n, dtype, false).total;
   g_err.clear();
   return GDB_OK;
 }
 
-gdb_status gdb_newton_schulz(int32_t m, int32_t n, int32_t dtype, const float* G, void* X, const float* coeffs,
-                             int32_t steps, float norm_scale, float eps, void* ws, size_t ws_bytes, void* stream) {
-  gdb_status st = check_ns(m, n, dtype, coeffs, steps);
+gdb_status gdb_newton_schulz(int32_t count, int32_t m, int32_t n, int32_t dtype, const float* G, void* X,
+                             const float* coeffs, int32_t steps, float norm_scale, float eps, void* ws,
+                             size_t ws_bytes, void* stream) {
+  gdb_status st = check_ns(count, m, n, dtype, coeffs, steps);
   if (st != GDB_OK) return st;
   if (!(norm_scale > 0.f) || !std::isfinite(norm_scale) || !(eps >= 0.f) || !std::isfinite(eps))
     return fail(GDB_EINVAL, "norm_scale must be positive and eps non-negative");
   CHECK_PTR(G); CHECK_PTR(X); CHECK_PTR(ws);
-  const NsWs w = ns_layout(m, n, dtype, false);
+  const NsWs w = ns_layout(count, m, n, dtype, false);
   if (ws_bytes < w.total) return fail(GDB_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, w.total);
   if ((const void*)G == X) return fail(GDB_EINVAL, "X must not alias G");
   char* b = (char*)ws;
@@ -893,34 +908,35 @@ gdb_status gdb_newton_schulz(int32_t m, int32_t n, int32_t dtype, const float* G
   const size_t mn = (size_t)m * n;
   int np = 0;
   void* start = steps % 2 == 0 ? X : (void*)(b + w.xa);
-  HIPCHK(sumsq_partials(G, mn, (float*)(b + w.npart), &np, s));
-  HIPCHK(norm_final((float*)(b + w.npart), np, norm_scale, eps, (float*)(b + w.inv), s));
-  HIPCHK(scale_cast(dtype, G, (float*)(b + w.inv), start, mn, s));
-  HIPCHK(ns_iterate(dtype, m, n, coeffs, steps, X, b + w.xa, b + w.a, b + w.bm, (float*)(b + w.part), s));
+  HIPCHK(sumsq_partials(G, mn, count, (float*)(b + w.npart), &np, s));
+  HIPCHK(norm_final((float*)(b + w.npart), np, count, norm_scale, eps, (float*)(b + w.inv), s));
+  HIPCHK(scale_cast(dtype, G, (float*)(b + w.inv), start, mn, count, s));
+  HIPCHK(ns_iterate(dtype, count, m, n, coeffs, steps, X, b + w.xa, b + w.a, b + w.bm, (float*)(b + w.part), s));
   g_err.clear();
   return GDB_OK;
 }
 
-gdb_status gdb_muon_ws_bytes(int32_t m, int32_t n, int32_t dtype, size_t* ws_bytes) {
-  gdb_status st = check_ns(m, n, dtype, nullptr, 0);
+gdb_status gdb_muon_ws_bytes(int32_t count, int32_t m, int32_t n, int32_t dtype, size_t* ws_bytes) {
+  gdb_status st = check_ns(count, m, n, dtype, nullptr, 0);
   if (st != GDB_OK) return st;
   if (!ws_bytes) return fail(GDB_EINVAL, "ws_bytes is NULL");
-  *ws_bytes = ns_layout(m, n, dtype, true).total;
+  *ws_bytes = ns_layout(count, m, n, dtype, true).total;
   g_err.clear();
   return GDB_OK;
 }
 
-gdb_status gdb_muon_step(int32_t m, int32_t n, int32_t dtype, float* p, void* p_bf16, const float* g, float* buf,
-                         float lr, float momentum, int32_t nesterov, float wd, float scale, const float* coeffs,
-                         int32_t steps, float norm_scale, float eps, void* ws, size_t ws_bytes, void* stream) {
-  gdb_status st = check_ns(m, n, dtype, coeffs, steps);
+gdb_status gdb_muon_step(int32_t count, int32_t m, int32_t n, int32_t dtype, float* p, void* p_bf16, const float* g,
+                         float* buf, float lr, float momentum, int32_t nesterov, float wd, float scale,
+                         const float* coeffs, int32_t steps, float norm_scale, float eps, void* ws, size_t ws_bytes,
+                         void* stream) {
+  gdb_status st = check_ns(count, m, n, dtype, coeffs, steps);
   if (st != GDB_OK) return st;
   for (float f : {lr, momentum, wd, scale, norm_scale, eps})
     if (!std::isfinite(f)) return fail(GDB_EINVAL, "non-finite hyperparameter");
   if (!(norm_scale > 0.f) || eps < 0.f) return fail(GDB_EINVAL, "norm_scale must be positive and eps non-negative");
   CHECK_PTR(p); CHECK_PTR(g); CHECK_PTR(buf); CHECK_PTR(ws);
   if (p_bf16 && (((uintptr_t)p_bf16) & 15)) return fail(GDB_EINVAL, "p_bf16 is not 16-byte aligned");
-  const NsWs w = ns_layout(m, n, dtype, true);
+  const NsWs w = ns_layout(count, m, n, dtype, true);
   if (ws_bytes < w.total) return fail(GDB_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, w.total);
   char* b = (char*)ws;
   hipStream_t s = (hipStream_t)stream;
@@ -928,11 +944,12 @@ gdb_status gdb_muon_step(int32_t m, int32_t n, int32_t dtype, float* p, void* p_
   int np = 0;
   void* X = b + w.x;
   void* start = steps % 2 == 0 ? X : (void*)(b + w.xa);
-  HIPCHK(muon_momentum(g, buf, (float*)(b + w.u), mn, momentum, nesterov ? 1 : 0, (float*)(b + w.npart), &np, s));
-  HIPCHK(norm_final((float*)(b + w.npart), np, norm_scale, eps, (float*)(b + w.inv), s));
-  HIPCHK(scale_cast(dtype, (float*)(b + w.u), (float*)(b + w.inv), start, mn, s));
-  HIPCHK(ns_iterate(dtype, m, n, coeffs, steps, X, b + w.xa, b + w.a, b + w.bm, (float*)(b + w.part), s));
-  HIPCHK(muon_apply(dtype, p, X, (bf16*)p_bf16, mn, 1.0f - lr * wd, lr * scale, s));
+  HIPCHK(muon_momentum(g, buf, (float*)(b + w.u), mn, count, momentum, nesterov ? 1 : 0, (float*)(b + w.npart), &np,
+                       s));
+  HIPCHK(norm_final((float*)(b + w.npart), np, count, norm_scale, eps, (float*)(b + w.inv), s));
+  HIPCHK(scale_cast(dtype, (float*)(b + w.u), (float*)(b + w.inv), start, mn, count, s));
+  HIPCHK(ns_iterate(dtype, count, m, n, coeffs, steps, X, b + w.xa, b + w.a, b + w.bm, (float*)(b + w.part), s));
+  HIPCHK(muon_apply(dtype, p, X, (bf16*)p_bf16, mn * count, 1.0f - lr * wd, lr * scale, s));
   g_err.clear();
   return GDB_OK;
 }

@@ -268,6 +268,13 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_k(GemmArgs p) {
   int tm, tn;
   tile_coords(blockIdx.x, nbm, nbn, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
+  if (blockIdx.z) {  // item of a batched launch
+    const size_t z = blockIdx.z;
+    p.A = (const char*)p.A + z * p.bsA * ES;
+    p.B = (const char*)p.B + z * p.bsB * ES;
+    p.C = (char*)p.C + z * p.bsC * (EPI == EPI_F32 ? sizeof(float) : sizeof(OT));
+    if (p.R) p.R = (const char*)p.R + z * p.bsR * sizeof(OT);
+  }
   // split-K range
   const int ksplit = ((p.K + p.splits * KSTEP - 1) / (p.splits * KSTEP)) * KSTEP;
   const int kbeg = min(p.K, (int)blockIdx.y * ksplit);
@@ -731,6 +738,7 @@ __global__ __launch_bounds__(256) void gemm_f32_k(GemmArgs p) {
 
 template <bool AK, bool BKM, bool F8 = false, typename OT = bf16, int NW = 4>
 hipError_t launch_bf16(const GemmArgs& a, dim3 g, hipStream_t s) {
+  g.z = a.batch > 1 ? a.batch : 1;
   switch (a.epi) {
     case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_STORE, F8, OT, NW>), g, dim3(64 * NW), 0, s, a); break;
     case EPI_RESID: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_RESID, F8, OT, NW>), g, dim3(64 * NW), 0, s, a); break;
@@ -829,6 +837,7 @@ hipError_t gemm_fp8(int out_dt, const GemmArgs& a, hipStream_t s) {
 
 hipError_t gemm(int dt, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
+  if (a.batch > 1 && a.splits > 1) return hipErrorInvalidValue;  // a batch runs unsplit
   if (dt == BF16) {
     const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
     dim3 g(nbm * nbn, a.splits);
@@ -839,6 +848,19 @@ hipError_t gemm(int dt, const GemmArgs& a, hipStream_t s) {
     if (a.a_kmajor && !a.b_kmajor) return launch_bf16<true, false, false, bf16, 4>(a, g, s);
     if (!a.a_kmajor && !a.b_kmajor) return launch_bf16<false, false, false, bf16, 4>(a, g, s);
     return launch_bf16<false, true, false, bf16, 4>(a, g, s);
+  }
+  if (a.batch > 1) {  // the fp32 path takes blockIdx.z for split-K: one launch per item
+    for (int z = 0; z < a.batch; ++z) {
+      GemmArgs b = a;
+      b.batch = 1;
+      b.A = (const float*)a.A + (size_t)z * a.bsA;
+      b.B = (const float*)a.B + (size_t)z * a.bsB;
+      b.C = (float*)a.C + (size_t)z * a.bsC;
+      if (a.R) b.R = (const float*)a.R + (size_t)z * a.bsR;
+      const hipError_t e = gemm(dt, b, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
   dim3 g((a.M + FT - 1) / FT, (a.N + FT - 1) / FT, a.splits);
   switch (a.epi) {

@@ -70,6 +70,10 @@ struct GemmArgs {
   void* C2;
   int accumulate;      // EPI_F32
   float alpha, beta;   // EPI_AXPBY
+  // batched launch (bf16/fp8 path, splits == 1): item z of `batch` reads and
+  // writes at these element offsets times z (0 or 1: one item)
+  int batch;
+  long long bsA, bsB, bsC, bsR;
   float* partial;      // EPI_F32 split-K scratch [splits, M, N] or null
   int splits;          // >= 1
   const float* amax_a; // fp8: per-tensor amax of A and B (scales amax/448)
@@ -179,15 +183,17 @@ hipError_t backout_bwd(int dt, const void* dy, const void* xb, const float* lam,
 
 // ------------------------------------------------------------------ optimizer
 constexpr int OPT_PART = 1024;  // most workgroups (partials) of the reductions below
-// partial sums of x^2 (n a multiple of 4); *np partials written
-hipError_t sumsq_partials(const float* x, size_t n, float* part, int* np, hipStream_t s);
+// Stacks of `count` matrices of n elements each (n a multiple of 4); the
+// partials of item i at part[i * OPT_PART ..], *np per item.
+// partial sums of x^2
+hipError_t sumsq_partials(const float* x, size_t n, int count, float* part, int* np, hipStream_t s);
 // buf = mu*buf + g; u = nesterov ? g + mu*buf : buf; partial sums of u^2
-hipError_t muon_momentum(const float* g, float* buf, float* u, size_t n, float mu, int nesterov, float* part,
-                         int* np, hipStream_t s);
-// inv[0] = 1 / (sqrt(sum part) * norm_scale + eps)
-hipError_t norm_final(const float* part, int np, float norm_scale, float eps, float* inv, hipStream_t s);
-// x = g * inv[0] (dtype dt)
-hipError_t scale_cast(int dt, const float* g, const float* inv, void* x, size_t n, hipStream_t s);
+hipError_t muon_momentum(const float* g, float* buf, float* u, size_t n, int count, float mu, int nesterov,
+                         float* part, int* np, hipStream_t s);
+// inv[i] = 1 / (sqrt(sum of item i's partials) * norm_scale + eps)
+hipError_t norm_final(const float* part, int np, int count, float norm_scale, float eps, float* inv, hipStream_t s);
+// x = g * inv[i] per item (dtype dt)
+hipError_t scale_cast(int dt, const float* g, const float* inv, void* x, size_t n, int count, hipStream_t s);
 // out = alpha * (sum of `splits` fp32 partials [splits][n]) + beta * R (dtype dt; R may be null)
 hipError_t splitk_axpby(int dt, const float* part, int splits, size_t n, float alpha, float beta, const void* R,
                         void* out, hipStream_t s);

@@ -22,8 +22,12 @@ constexpr int OPT_NT = 256;
 // per-workgroup sums of squares of x [n] (n a multiple of 4)
 __device__ __forceinline__ float sumsq4(f32x4 v) { return v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]; }
 
+// item blockIdx.y of a stack of matrices of n4*4 elements each; partials at
+// part[item * OPT_PART + block]
 __global__ __launch_bounds__(OPT_NT) void sumsq_part_k(const float* __restrict__ x, size_t n4, float* part) {
   __shared__ float red[OPT_NT / 64];
+  x += (size_t)blockIdx.y * n4 * 4;
+  part += (size_t)blockIdx.y * OPT_PART;
   float acc = 0.f;
   for (size_t i = (size_t)blockIdx.x * OPT_NT + threadIdx.x; i < n4; i += (size_t)gridDim.x * OPT_NT)
     acc += sumsq4(((const f32x4*)x)[i]);
@@ -36,6 +40,9 @@ __global__ __launch_bounds__(OPT_NT) void muon_momentum_k(const float* __restric
                                                          float* __restrict__ u, size_t n4, float mu, int nesterov,
                                                          float* part) {
   __shared__ float red[OPT_NT / 64];
+  const size_t off = (size_t)blockIdx.y * n4 * 4;
+  g += off; buf += off; u += off;
+  part += (size_t)blockIdx.y * OPT_PART;
   float acc = 0.f;
   for (size_t i = (size_t)blockIdx.x * OPT_NT + threadIdx.x; i < n4; i += (size_t)gridDim.x * OPT_NT) {
     const f32x4 gv = ((const f32x4*)g)[i];
@@ -49,22 +56,25 @@ __global__ __launch_bounds__(OPT_NT) void muon_momentum_k(const float* __restric
   if (threadIdx.x == 0) part[blockIdx.x] = acc;
 }
 
-// inv[0] = 1 / (sqrt(sum of the partials) * norm_scale + eps); thread t adds
-// partials t, t + 256, ... then a fixed tree (deterministic)
+// inv[item] = 1 / (sqrt(sum of the item's partials) * norm_scale + eps), item =
+// blockIdx.x; thread t adds partials t, t + 256, ... then a fixed tree
 __global__ __launch_bounds__(OPT_NT) void norm_final_k(const float* part, int np, float norm_scale, float eps,
                                                        float* inv) {
   __shared__ float red[OPT_NT / 64];
+  part += (size_t)blockIdx.x * OPT_PART;
   float acc = 0.f;
   for (int i = threadIdx.x; i < np; i += OPT_NT) acc += part[i];
   acc = block_sum<OPT_NT>(acc, red);
-  if (threadIdx.x == 0) inv[0] = 1.0f / (sqrtf(acc) * norm_scale + eps);
+  if (threadIdx.x == 0) inv[blockIdx.x] = 1.0f / (sqrtf(acc) * norm_scale + eps);
 }
 
-// x0 = g * inv[0] in the iteration's dtype
+// x0 = g * inv[item] in the iteration's dtype, item = blockIdx.y
 template <typename T>
 __global__ __launch_bounds__(OPT_NT) void scale_cast_k(const float* __restrict__ g, const float* inv,
                                                       T* __restrict__ x, size_t n4) {
-  const float sc = inv[0];
+  const float sc = inv[blockIdx.y];
+  g += (size_t)blockIdx.y * n4 * 4;
+  x += (size_t)blockIdx.y * n4 * 4;
   for (size_t i = (size_t)blockIdx.x * OPT_NT + threadIdx.x; i < n4; i += (size_t)gridDim.x * OPT_NT) {
     const f32x4 v = ((const f32x4*)g)[i] * sc;
 #pragma unroll
@@ -137,27 +147,28 @@ unsigned grid_for(size_t n4) {
 
 }  // namespace
 
-hipError_t sumsq_partials(const float* x, size_t n, float* part, int* np, hipStream_t s) {
+hipError_t sumsq_partials(const float* x, size_t n, int count, float* part, int* np, hipStream_t s) {
   *np = (int)grid_for(n / 4);
-  hipLaunchKernelGGL(sumsq_part_k, dim3(*np), dim3(OPT_NT), 0, s, x, n / 4, part);
+  hipLaunchKernelGGL(sumsq_part_k, dim3(*np, count), dim3(OPT_NT), 0, s, x, n / 4, part);
   return hipGetLastError();
 }
 
-hipError_t muon_momentum(const float* g, float* buf, float* u, size_t n, float mu, int nesterov, float* part,
-                         int* np, hipStream_t s) {
+hipError_t muon_momentum(const float* g, float* buf, float* u, size_t n, int count, float mu, int nesterov,
+                         float* part, int* np, hipStream_t s) {
   *np = (int)grid_for(n / 4);
-  hipLaunchKernelGGL(muon_momentum_k, dim3(*np), dim3(OPT_NT), 0, s, g, buf, u, n / 4, mu, nesterov, part);
+  hipLaunchKernelGGL(muon_momentum_k, dim3(*np, count), dim3(OPT_NT), 0, s, g, buf, u, n / 4, mu, nesterov, part);
   return hipGetLastError();
 }
 
-hipError_t norm_final(const float* part, int np, float norm_scale, float eps, float* inv, hipStream_t s) {
-  hipLaunchKernelGGL(norm_final_k, dim3(1), dim3(OPT_NT), 0, s, part, np, norm_scale, eps, inv);
+hipError_t norm_final(const float* part, int np, int count, float norm_scale, float eps, float* inv, hipStream_t s) {
+  hipLaunchKernelGGL(norm_final_k, dim3(count), dim3(OPT_NT), 0, s, part, np, norm_scale, eps, inv);
   return hipGetLastError();
 }
 
-hipError_t scale_cast(int dt, const float* g, const float* inv, void* x, size_t n, hipStream_t s) {
-  if (dt == BF16) hipLaunchKernelGGL(scale_cast_k<bf16>, dim3(grid_for(n / 4)), dim3(OPT_NT), 0, s, g, inv, (bf16*)x, n / 4);
-  else hipLaunchKernelGGL(scale_cast_k<float>, dim3(grid_for(n / 4)), dim3(OPT_NT), 0, s, g, inv, (float*)x, n / 4);
+hipError_t scale_cast(int dt, const float* g, const float* inv, void* x, size_t n, int count, hipStream_t s) {
+  const dim3 grid(grid_for(n / 4), count);
+  if (dt == BF16) hipLaunchKernelGGL(scale_cast_k<bf16>, grid, dim3(OPT_NT), 0, s, g, inv, (bf16*)x, n / 4);
+  else hipLaunchKernelGGL(scale_cast_k<float>, grid, dim3(OPT_NT), 0, s, g, inv, (float*)x, n / 4);
   return hipGetLastError();
 }
 

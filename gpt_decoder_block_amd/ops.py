@@ -259,33 +259,40 @@ def _coeffs(coeffs):
     return (ctypes.c_float * max(len(flat), 1))(*flat), len(flat) // 3
 
 
-def newton_schulz_ws_bytes(m: int, n: int, dtype: torch.dtype) -> int:
+def _stack(t: torch.Tensor):
+    """(count, m, n) of a [m, n] matrix or a [count, m, n] stack."""
+    return (1,) + tuple(t.shape) if t.dim() == 2 else tuple(t.shape)
+
+
+def newton_schulz_ws_bytes(m: int, n: int, dtype: torch.dtype, count: int = 1) -> int:
     s = ctypes.c_size_t()
-    L.call("gdb_newton_schulz_ws_bytes", m, n, dtype_code(dtype), ctypes.byref(s))
+    L.call("gdb_newton_schulz_ws_bytes", count, m, n, dtype_code(dtype), ctypes.byref(s))
     return s.value
 
 
 def newton_schulz(G: torch.Tensor, X: torch.Tensor, coeffs, norm_scale: float = 1.0, eps: float = 1e-7,
                   ws=None) -> None:
-    """X (dtype of X) = the Newton-Schulz map of the float32 matrix G [m, n]."""
-    m, n = G.shape
+    """X (dtype of X) = the Newton-Schulz map of each float32 matrix of G
+    ([m, n] or a stack [count, m, n])."""
+    count, m, n = _stack(G)
     arr, steps = _coeffs(coeffs)
-    L.call("gdb_newton_schulz", m, n, dtype_code(X.dtype), _p(G), _p(X), arr, steps, norm_scale, eps, _p(ws),
+    L.call("gdb_newton_schulz", count, m, n, dtype_code(X.dtype), _p(G), _p(X), arr, steps, norm_scale, eps, _p(ws),
            ws.numel() * ws.element_size(), _stream(G))
 
 
-def muon_ws_bytes(m: int, n: int, dtype: torch.dtype) -> int:
+def muon_ws_bytes(m: int, n: int, dtype: torch.dtype, count: int = 1) -> int:
     s = ctypes.c_size_t()
-    L.call("gdb_muon_ws_bytes", m, n, dtype_code(dtype), ctypes.byref(s))
+    L.call("gdb_muon_ws_bytes", count, m, n, dtype_code(dtype), ctypes.byref(s))
     return s.value
 
 
 def muon_step(p: torch.Tensor, g: torch.Tensor, buf: torch.Tensor, lr: float, momentum: float, nesterov: bool,
               wd: float, scale: float, coeffs, dtype: torch.dtype, ws: torch.Tensor, p_bf16=None,
               norm_scale: float = 1.0, eps: float = 1e-7) -> None:
-    m, n = p.shape
+    """One Muon step on a matrix [m, n] or a stack [count, m, n] (float32)."""
+    count, m, n = _stack(p)
     arr, steps = _coeffs(coeffs)
-    L.call("gdb_muon_step", m, n, dtype_code(dtype), _p(p), _opt(p_bf16), _p(g), _p(buf), lr, momentum,
+    L.call("gdb_muon_step", count, m, n, dtype_code(dtype), _p(p), _opt(p_bf16), _p(g), _p(buf), lr, momentum,
            int(nesterov), wd, scale, arr, steps, norm_scale, eps, _p(ws), ws.numel() * ws.element_size(),
            _stream(p))
 

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define GDB_ABI_VERSION 4
+#define GDB_ABI_VERSION 5
 
 /* Scratch bytes that gdb_smear_bwd and gdb_backout_bwd need in `ws`. */
 #define GDB_EXTRAS_WS_BYTES ((size_t)1 << 20)
@@ -372,24 +372,32 @@ gdb_status gdb_attention_decode(int32_t B, int32_t H, int32_t Hkv, int32_t D, in
  * accumulation; fp32: all fp32); a wide matrix (m < n) takes the Gram on the
  * other side, X X^T (the same map).
  *
- * gdb_newton_schulz: G float32 [m, n] -> X [m, n] in `dtype` (X != G).
- *   coeffs: HOST float [steps][3]; m, n multiples of 8; steps in [0, 64].
- *   ws: gdb_newton_schulz_ws_bytes bytes of scratch. */
-gdb_status gdb_newton_schulz_ws_bytes(int32_t m, int32_t n, int32_t dtype, size_t* ws_bytes);
-gdb_status gdb_newton_schulz(int32_t m, int32_t n, int32_t dtype, const float* G, void* X, const float* coeffs,
-                             int32_t steps, float norm_scale, float eps, void* ws, size_t ws_bytes, void* stream);
-/* gdb_muon_step on a matrix parameter p float32 [m, n] with gradient g and
- * momentum buffer buf (float32, updated in place):
+ * Both calls take a stack of `count` matrices of the same shape, stored one
+ * after the other ([count][m][n]); each item is normalised and iterated on
+ * its own, and the stack's products run as one batched launch (at d24 the
+ * 24 layers' matrices of one shape fill the GPU where one 1536 x 1536
+ * product does not).
+ *
+ * gdb_newton_schulz: G float32 [count][m][n] -> X [count][m][n] in `dtype`
+ *   (X != G).  coeffs: HOST float [steps][3]; m, n multiples of 8; steps in
+ *   [0, 64]; count in [1, 65535].  ws: gdb_newton_schulz_ws_bytes bytes. */
+gdb_status gdb_newton_schulz_ws_bytes(int32_t count, int32_t m, int32_t n, int32_t dtype, size_t* ws_bytes);
+gdb_status gdb_newton_schulz(int32_t count, int32_t m, int32_t n, int32_t dtype, const float* G, void* X,
+                             const float* coeffs, int32_t steps, float norm_scale, float eps, void* ws,
+                             size_t ws_bytes, void* stream);
+/* gdb_muon_step on matrix parameters p float32 [count][m][n] with gradients g
+ * and momentum buffers buf (float32, updated in place), per item:
  *   buf = momentum*buf + g;  U = nesterov ? g + momentum*buf : buf;
  *   p = p*(1 - lr*wd) - lr*scale*NS(U)
  * (the momentum form, decay and the shape scale are inputs: the pages name
  * Muon only as momentum orthogonalised by Newton-Schulz).  p_bf16 (optional,
  * NULL to skip) receives the bf16 rounding of the new p.
  * ws: gdb_muon_ws_bytes bytes. */
-gdb_status gdb_muon_ws_bytes(int32_t m, int32_t n, int32_t dtype, size_t* ws_bytes);
-gdb_status gdb_muon_step(int32_t m, int32_t n, int32_t dtype, float* p, void* p_bf16, const float* g, float* buf,
-                         float lr, float momentum, int32_t nesterov, float wd, float scale, const float* coeffs,
-                         int32_t steps, float norm_scale, float eps, void* ws, size_t ws_bytes, void* stream);
+gdb_status gdb_muon_ws_bytes(int32_t count, int32_t m, int32_t n, int32_t dtype, size_t* ws_bytes);
+gdb_status gdb_muon_step(int32_t count, int32_t m, int32_t n, int32_t dtype, float* p, void* p_bf16, const float* g,
+                         float* buf, float lr, float momentum, int32_t nesterov, float wd, float scale,
+                         const float* coeffs, int32_t steps, float norm_scale, float eps, void* ws, size_t ws_bytes,
+                         void* stream);
 /* gdb_adamw_step on n float32 parameters (n a multiple of 8), step t >= 1:
  *   p *= 1 - lr*wd;  m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*g^2;
  *   p -= lr * (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)

@@ -275,14 +275,16 @@ def test_optimizer_validation(L):
     al = (ctypes.addressof(buf) + 255) & ~255
     nb = ctypes.c_size_t()
     co = (ctypes.c_float * 6)(8.156, -22.483, 15.879, 4.043, -2.809, 0.5)
-    assert lib.gdb_newton_schulz_ws_bytes(1536, 6144, 1, ctypes.byref(nb)) == L.GDB_OK and nb.value > 0
+    assert lib.gdb_newton_schulz_ws_bytes(1, 1536, 6144, 1, ctypes.byref(nb)) == L.GDB_OK and nb.value > 0
     big = nb.value
+    assert lib.gdb_newton_schulz_ws_bytes(24, 1536, 6144, 1, ctypes.byref(nb)) == L.GDB_OK and nb.value > big
 
-    def ns(m=64, n=32, dtype=1, G=al, X=al + 256, coeffs=co, steps=2, ns_=1.0, eps=1e-7, ws=al, wsb=big):
-        return lib.gdb_newton_schulz(m, n, dtype, G, X, coeffs, steps, ctypes.c_float(ns_), ctypes.c_float(eps), ws,
-                                     wsb, None)
+    def ns(m=64, n=32, dtype=1, G=al, X=al + 256, coeffs=co, steps=2, ns_=1.0, eps=1e-7, ws=al, wsb=big, count=1):
+        return lib.gdb_newton_schulz(count, m, n, dtype, G, X, coeffs, steps, ctypes.c_float(ns_),
+                                     ctypes.c_float(eps), ws, wsb, None)
 
     assert ns(m=60) == L.GDB_EINVAL and "multiples of 8" in lib.gdb_last_error().decode()
+    assert ns(count=0) == L.GDB_EINVAL and "count" in lib.gdb_last_error().decode()
     assert ns(dtype=5) == L.GDB_EINVAL
     assert ns(steps=65) == L.GDB_EINVAL
     assert ns(coeffs=None) == L.GDB_EINVAL
@@ -302,10 +304,10 @@ def test_optimizer_validation(L):
     assert lib.gdb_adamw_step(16, al, al + 2, al, al, al, 1, f(1e-3), f(0.9), f(0.95), f(1e-8), f(0.0), None) \
         == L.GDB_EINVAL
     # Muon
-    assert lib.gdb_muon_ws_bytes(64, 32, 1, ctypes.byref(nb)) == L.GDB_OK
-    st = lib.gdb_muon_step(64, 32, 1, al, None, al, None, f(0.02), f(0.95), 1, f(0.0), f(1.0), co, 2, f(1.0),
+    assert lib.gdb_muon_ws_bytes(1, 64, 32, 1, ctypes.byref(nb)) == L.GDB_OK
+    st = lib.gdb_muon_step(1, 64, 32, 1, al, None, al, None, f(0.02), f(0.95), 1, f(0.0), f(1.0), co, 2, f(1.0),
                            f(1e-7), al, nb.value, None)
     assert st == L.GDB_EINVAL and "buf is NULL" in lib.gdb_last_error().decode()
-    st = lib.gdb_muon_step(64, 32, 1, al, None, al, al, f(float("inf")), f(0.95), 1, f(0.0), f(1.0), co, 2, f(1.0),
+    st = lib.gdb_muon_step(1, 64, 32, 1, al, None, al, al, f(float("inf")), f(0.95), 1, f(0.0), f(1.0), co, 2, f(1.0),
                            f(1e-7), al, nb.value, None)
     assert st == L.GDB_EINVAL

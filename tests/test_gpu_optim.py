@@ -108,3 +108,46 @@ def test_adamw_step():
     assert_close(mg, mr, "f32", "m", tol=1e-5)
     assert_close(vg, vr, "f32", "v", tol=1e-5)
     assert_close(plow, rounded(host(pg), "bf16"), "f32", "p_bf16", tol=0.0)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("m,n", [(200, 96), (96, 200), (256, 256)])
+def test_newton_schulz_stack(dt, m, n):
+    # a stack of matrices of one shape runs as batched launches; each item is
+    # normalised and iterated on its own (items of very different scales)
+    count = 3
+    G = np.random.default_rng(m * n).standard_normal((count, m, n)).astype(np.float32)
+    G *= np.array([1.0, 30.0, 0.01], dtype=np.float32)[:, None, None]
+    X = torch.full((count, m, n), float("nan"), dtype=TDT[dt], device=DEV)
+    ws = torch.empty(ops.newton_schulz_ws_bytes(m, n, TDT[dt], count), dtype=torch.uint8, device=DEV)
+    print(f"newton_schulz stack dt={dt} count={count} m={m} n={n}", flush=True)
+    ops.newton_schulz(torch.from_numpy(G).to(DEV), X, FIVE, norm_scale=1.02, eps=1e-7, ws=ws)
+    torch.cuda.synchronize()
+    for i in range(count):
+        Gi = G[i].astype(np.float64)
+        ref = O.newton_schulz(Gi, FIVE, 1.02, 1e-7)
+        e = assert_close(X[i], ref, dt, f"X[{i}]", tol=ns_bar(dt, Gi, FIVE))
+        print(f"  item {i} err {e:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_muon_step_stack(dt):
+    count, m, n = 4, 128, 384
+    g = np.random.default_rng(9)
+    p = g.standard_normal((count, m, n)).astype(np.float32) * 0.02
+    gr = g.standard_normal((count, m, n)).astype(np.float32)
+    buf = g.standard_normal((count, m, n)).astype(np.float32) * 0.5
+    pg, gg, bg = (torch.from_numpy(a.copy()).to(DEV) for a in (p, gr, buf))
+    ws = torch.empty(ops.muon_ws_bytes(m, n, TDT[dt], count), dtype=torch.uint8, device=DEV)
+    lr, mu, wd, sc = 0.02, 0.95, 0.1, 1.7
+    print(f"muon stack dt={dt} count={count}", flush=True)
+    ops.muon_step(pg, gg, bg, lr, mu, True, wd, sc, FIVE, TDT[dt], ws, norm_scale=1.02)
+    torch.cuda.synchronize()
+    for i in range(count):
+        p_ref, b_ref = O.muon_step(p[i].astype(np.float64), gr[i].astype(np.float64), buf[i].astype(np.float64), lr,
+                                   mu, True, wd, sc, FIVE, 1.02, 1e-7)
+        assert_close(bg[i], b_ref, "f32", f"buf[{i}]")
+        upd = (p[i].astype(np.float64) * (1 - lr * wd) - host(pg[i])) / (lr * sc)
+        upd_ref = (p[i].astype(np.float64) * (1 - lr * wd) - p_ref) / (lr * sc)
+        u = gr[i].astype(np.float64) + mu * b_ref
+        assert_close(upd, upd_ref, dt, f"update[{i}]", tol=ns_bar(dt, u, FIVE))
