@@ -85,6 +85,23 @@ def ev_time(fn, reps, torch):
     return a.elapsed_time(b) / 1e3 / reps
 
 
+def cold_time(fn, reps, torch, flush):
+    """Average duration (s) of fn() launched right after overwriting a flush
+    buffer larger than the 256 MB Infinity Cache, so its operands come from
+    HBM (only the launch is timed)."""
+    s = torch.cuda.current_stream()
+    tot = 0.0
+    for _ in range(reps):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        fn()
+        b.record(s)
+        torch.cuda.synchronize()
+        tot += a.elapsed_time(b) / 1e3
+    return tot / reps
+
+
 def kernel_figures(w, st, reps, torch, ops):
     """Each hot kernel class timed alone at the workload's shapes."""
     dev, dt = st.device, st.dt
@@ -158,12 +175,17 @@ def kernel_figures(w, st, reps, torch, ops):
     s = 2 if dt == torch.bfloat16 else 4
     t = ev_time(lambda: ops.rmsnorm_fwd(x, xn, r, w.eps), reps, torch)
     by = 2.0 * N * C * s + 4 * N
-    out["rmsnorm_fwd"] = {"ms": t * 1e3, "GBps": by / t / 1e9, "frac_hbm_peak": by / t / PEAK_HBM}
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+    tc = cold_time(lambda: ops.rmsnorm_fwd(x, xn, r, w.eps), 5, torch, flush)
+    out["rmsnorm_fwd"] = {"ms": t * 1e3, "GBps": by / t / 1e9, "frac_hbm_peak": by / t / PEAK_HBM,
+                          "cold_ms": tc * 1e3, "cold_frac_hbm_peak": by / tc / PEAK_HBM}
     dres = rnd(N, C)
     dx = torch.empty(N, C, dtype=dt, device=dev)
     t = ev_time(lambda: ops.rmsnorm_bwd(x, xn, r, dres, dx), reps, torch)
     by = 4.0 * N * C * s + 4 * N
-    out["rmsnorm_bwd"] = {"ms": t * 1e3, "GBps": by / t / 1e9, "frac_hbm_peak": by / t / PEAK_HBM}
+    tc = cold_time(lambda: ops.rmsnorm_bwd(x, xn, r, dres, dx), 5, torch, flush)
+    out["rmsnorm_bwd"] = {"ms": t * 1e3, "GBps": by / t / 1e9, "frac_hbm_peak": by / t / PEAK_HBM,
+                          "cold_ms": tc * 1e3, "cold_frac_hbm_peak": by / tc / PEAK_HBM}
     del x, xn, dres, dx
     # cross-entropy over the vocabulary (bandwidth): one read + one write of the logits
     z0 = rnd(N, V)
@@ -175,6 +197,7 @@ def kernel_figures(w, st, reps, torch, ops):
     tce = ev_time(lambda: (z.copy_(z0), ops.cross_entropy(z, tg, rl, ls)), reps, torch) - tc
     by = N * V * 2.0 * s + 8 * N
     out["cross_entropy"] = {"ms": tce * 1e3, "GBps": by / tce / 1e9, "frac_hbm_peak": by / tce / PEAK_HBM}
+    del flush
     del z0, z
     # decode attention (inference step, bandwidth): the workload's B sequences
     # with T cached positions, one new query each; every visible K and V row
@@ -290,6 +313,19 @@ def cpu_baseline(w, budget_s=40.0):
             "host_cpu_count": os.cpu_count()}
 
 
+def env_info(torch):
+    """Device and runtime the figures were taken on."""
+    pr = torch.cuda.get_device_properties(0)
+    cpu = ""
+    try:
+        cpu = next((l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"device": pr.name, "arch": getattr(pr, "gcnArchName", ""), "compute_units": pr.multi_processor_count,
+            "hbm_gib": round(pr.total_memory / 2 ** 30, 1), "hip": torch.version.hip, "torch": torch.__version__,
+            "host_cpu": cpu, "host_cpu_count": os.cpu_count()}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -333,13 +369,17 @@ def main():
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     e0.record(s)
-    for _ in range(args.steps):
+    evs[0].record(s)
+    for i in range(args.steps):
         st.step()
+        evs[i + 1].record(s)
     e1.record(s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     print(f"[bench] {args.steps} steps: {ms:.2f} ms/step (wall {wall / args.steps * 1e3:.2f}), loss {loss0:.4f}",
           file=sys.stderr, flush=True)
     tokens = w.B * w.T
@@ -375,6 +415,9 @@ def main():
            "flops_per_token": fpt, "flops_per_token_pages_convention": fpt_pages,
            "tflops_pages_convention": fpt_pages * tps / 1e12,
            "loss_after_warmup": loss0,
+           "ms_per_step_median": per_step[len(per_step) // 2], "ms_per_step_min": per_step[0],
+           "ms_per_step_max": per_step[-1],
+           "env": env_info(torch),
            "roofline": roof, "kernels": kern}
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
