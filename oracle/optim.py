@@ -12,7 +12,7 @@ Sources (page title, then section):
        L'optimiseur Muon (nanochat/optim.py)": the same loop, five iterations,
        Muon read as momentum orthogonalised by that iteration.
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
   * the iteration starts from X0 = G / (||G||_F * norm_scale + eps): the
     polynomial steps only act as intended on singular values in (0, 1], and
     the Frobenius norm bounds the largest one; norm_scale and eps are inputs;

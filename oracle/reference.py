@@ -21,7 +21,7 @@ Sources (page title, then section):
   [FR] section "6. Moteur d'inférence": generation against a prefilled KV
        cache (`attention_decode`).
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
   * pre-norm blocks x += Attn(rms(x)); x += MLP(rms(x)); final rms before the
     head; no biases; RMSNorm has no affine and eps = 1e-6 everywhere;
   * QK norm is an RMSNorm over head_dim per (token, head), applied before
