@@ -19,6 +19,10 @@
  *     the block whose output was subtracted) ... L x gdb_block_bwd(extras)
  *     -> gdb_smear_bwd -> gdb_embed_bwd
  *
+ * Beside the training step: the optimizer step that follows it
+ * (gdb_adamw_step, gdb_muon_step on gdb_newton_schulz) and the generation
+ * step of the inference engine (gdb_attention_decode against a KV cache).
+ *
  * Conventions shared by every entry point
  *   - Pointers named in a signature are DEVICE pointers unless the comment
  *     says "host".  The caller allocates every buffer (inputs, outputs, saved
