@@ -843,8 +843,11 @@ hipError_t gemm(int dt, const GemmArgs& a, hipStream_t s) {
     dim3 g(nbm * nbn, a.splits);
     // both operands copied straight into LDS: 8 waves (measured 2-10% faster
     // on the block's shapes); a register-loaded operand: 4 waves (with 8, the
-    // loading waves run out of registers)
+    // loading waves run out of registers: both operands loaded that way run at
+    // half speed, one at 4-7% below 4 waves), except the ReLU^2-backward
+    // product, whose epilogue reads a second [M, N] tensor (3.5% faster with 8)
     if (a.a_kmajor && a.b_kmajor) return launch_bf16<true, true, false, bf16, GEMM_NW>(a, g, s);
+    if (a.a_kmajor && !a.b_kmajor && a.epi == EPI_DSQR) return launch_bf16<true, false, false, bf16, 8>(a, g, s);
     if (a.a_kmajor && !a.b_kmajor) return launch_bf16<true, false, false, bf16, 4>(a, g, s);
     if (!a.a_kmajor && !a.b_kmajor) return launch_bf16<false, false, false, bf16, 4>(a, g, s);
     return launch_bf16<false, true, false, bf16, 4>(a, g, s);
