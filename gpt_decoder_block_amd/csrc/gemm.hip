@@ -483,14 +483,19 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_k(GemmArgs p) {
         }
     }
     __syncthreads();
-    const bool cok = 4 * lane < ncols;
+    // two rows per instruction, 16 bytes per lane: lane half h takes row
+    // 2(k*NW + w) + h, lane l = lane % 32 its slots 2l and 2l + 1, which sit
+    // in one aligned 16-byte pair at (2l) ^ x, x = row & 31 (swapped if x is odd)
+    const int l32 = lane & 31;
+    const bool cok = 8 * l32 < ncols;
 #pragma unroll 8
-    for (int k = 0; k < BM / NW; ++k) {
-      const int r = k * NW + w;
+    for (int k = 0; k < BM / NW / 2; ++k) {
+      const int r = 2 * (k * NW + w) + (lane >> 5);
       const int m = m0 + r;
-      if (cok && m < p.M)
-        *(bf16x4*)((bf16*)p.C + (size_t)m * p.ldc + n0 + 4 * lane) =
-            *(const bf16x4*)(sb + r * 256 + ((lane ^ (r & 31)) << 2));
+      const int x = r & 31;
+      bf16x8 v = *(const bf16x8*)(sb + r * 256 + ((((2 * l32) ^ x) & ~1) << 2));
+      if (x & 1) v = bf16x8{v[4], v[5], v[6], v[7], v[0], v[1], v[2], v[3]};
+      if (cok && m < p.M) *(bf16x8*)((bf16*)p.C + (size_t)m * p.ldc + n0 + 8 * l32) = v;
     }
   } else {
 #pragma unroll
