@@ -111,6 +111,7 @@ struct WsBwd {
   float* xpart;         // partial sums of the extras' parameter gradients
   uint8_t *doutq, *doutT, *duq, *duT;  // fp8 MLP backward codes: [N, C], [C, Np], [N, F], [F, Np]
   float* amax8;                        // dout, du
+  void* wt;             // bf16: K-major copy of the weight of the current data-gradient product
 };
 
 void carve_saved(const BlockDims& d, Carver& c, Saved& s) {
@@ -169,6 +170,7 @@ void carve_bwd(const BlockDims& d, Carver& c, WsBwd& w) {
   const size_t xp = std::max((size_t)mix_partials(d.N) * 2, (size_t)ve_gate_partials(d.N) * d.Hkv * MAX_VE_GATE);
   w.xpart = c.take<float>(xp * 4);
   const size_t f8 = d.fp8 ? 1 : 0, Np = d.Np;
+  w.wt = c.take<char>(d.dt == BF16 ? (size_t)std::max(std::max(d.W3, d.F), d.Q) * d.C * 2 : 0);
   w.doutq = c.take<uint8_t>(f8 * N * d.C);
   w.doutT = c.take<uint8_t>(f8 * d.C * Np);
   w.duq = c.take<uint8_t>(f8 * N * d.F);
@@ -384,6 +386,20 @@ gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
   return GDB_OK;
 }
 
+// Data gradient dX [N, Nn] = dY [N, K] . W [K, Nn] (W row-major, the layout of
+// the forward's K-major weight).  In bf16 W is first copied transposed into
+// wt, so the product runs with both operands K-major, the GEMM's fastest
+// layout (the copy costs a few percent of the product); fp32 reads W as is.
+static GemmArgs dgrad_args(int dt, const void* dY, int K, const void* W, int Nn, int N, int epi, void* dX, void* wt,
+                           hipStream_t s, hipError_t* err) {
+  *err = hipSuccess;
+  if (dt == BF16) {
+    *err = transpose_bf16(W, K, Nn, wt, s);
+    return gemm_args(dY, true, K, wt, true, K, N, Nn, K, epi, dX, Nn);
+  }
+  return gemm_args(dY, true, K, W, false, Nn, N, Nn, K, epi, dX, Nn);
+}
+
 gdb_status gdb_block_bwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, const gdb_block_extras* ex,
                          const float* rope_tab, const void* saved, const void* dx_out, void* dx_in,
                          const gdb_block_wgrads* dw, const gdb_block_extras_grads* dex, void* ws, void* stream) {
@@ -431,16 +447,25 @@ gdb_status gdb_block_bwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
     HIPCHK(gemm_fp8(dt, g, s));
     HIPCHK(wgrad_fp8(wb.duT, wb.amax8 + 1, sv.xn2T, sv.amax + 0, d.F, d.C, d.Np, dw->dw_fc, acc, wb.partial, s));
   } else {
-    GemmArgs g = gemm_args(dx_out, true, d.C, w->w_proj, false, d.F, N, d.F, d.C, EPI_DSQR, wb.du, d.F);
+    hipError_t te;
+    GemmArgs g = dgrad_args(dt, dx_out, d.C, w->w_proj, d.F, N, EPI_DSQR, wb.du, wb.wt, s, &te);
+    HIPCHK(te);
     g.R = sv.h; g.ldr = d.F;
     HIPCHK(gemm(dt, g, s));
     HIPCHK(wgrad(dt, dx_out, d.C, sv.h, d.F, d.C, d.F, N, dw->dw_proj, acc, wb.partial, s));
-    HIPCHK(gemm(dt, gemm_args(wb.du, true, d.F, w->w_fc, false, d.C, N, d.C, d.F, EPI_STORE, wb.dxn, d.C), s));
+    g = dgrad_args(dt, wb.du, d.F, w->w_fc, d.C, N, EPI_STORE, wb.dxn, wb.wt, s, &te);
+    HIPCHK(te);
+    HIPCHK(gemm(dt, g, s));
     HIPCHK(wgrad(dt, wb.du, d.F, sv.xn2, d.C, d.F, d.C, N, dw->dw_fc, acc, wb.partial, s));
   }
   HIPCHK(rmsnorm_bwd(dt, wb.dxn, sv.xn2, sv.r2, dx_out, wb.dx_mid, N, d.C, s));
   // attention output projection
-  HIPCHK(gemm(dt, gemm_args(wb.dx_mid, true, d.C, w->w_o, false, d.Q, N, d.Q, d.C, EPI_STORE, wb.dout, d.Q), s));
+  {
+    hipError_t te;
+    GemmArgs g = dgrad_args(dt, wb.dx_mid, d.C, w->w_o, d.Q, N, EPI_STORE, wb.dout, wb.wt, s, &te);
+    HIPCHK(te);
+    HIPCHK(gemm(dt, g, s));
+  }
   HIPCHK(wgrad(dt, wb.dx_mid, d.C, sv.o, d.Q, d.C, d.Q, N, dw->dw_o, acc, wb.partial, s));
   // attention
   AttnArgs at{};
@@ -462,7 +487,12 @@ gdb_status gdb_block_bwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
                   N, s));
   }
   // QKV projection
-  HIPCHK(gemm(dt, gemm_args(wb.dqkv, true, d.W3, w->w_qkv, false, d.C, N, d.C, d.W3, EPI_STORE, wb.dxn, d.C), s));
+  {
+    hipError_t te;
+    GemmArgs g = dgrad_args(dt, wb.dqkv, d.W3, w->w_qkv, d.C, N, EPI_STORE, wb.dxn, wb.wt, s, &te);
+    HIPCHK(te);
+    HIPCHK(gemm(dt, g, s));
+  }
   HIPCHK(wgrad(dt, wb.dqkv, d.W3, sv.xn1, d.C, d.W3, d.C, N, dw->dw_qkv, acc, wb.partial, s));
   if (xe.ve)
     HIPCHK(ve_gate_bwd(dt, wb.ds, sv.xn1, wb.dxn, d.C, ex->ve_gate, ex->ve_gate_channels, d.Hkv, wb.xpart,

@@ -30,6 +30,45 @@ hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s) {
   return hipGetLastError();
 }
 
+// -------------------------------------------------------------- transpose
+// out [Cc, R] = in [R, Cc]^T in bf16 (R, Cc multiples of 8), one 64x64 tile
+// per workgroup staged in LDS: rows are read and written as 16-byte chunks,
+// eight consecutive lanes cover one 128-byte line on both sides.  The
+// backward turns each weight into a K-major copy with it, so the data
+// gradients run on the GEMM's both-operands-K-major layout.
+__global__ __launch_bounds__(256) void transpose_bf16_k(const bf16* __restrict__ in, int R, int Cc,
+                                                       bf16* __restrict__ out) {
+  __shared__ bf16 t[64][66];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = threadIdx.x + 256 * k, r = i >> 3, cc = (i & 7) * 8;
+    if (r0 + r < R && c0 + cc < Cc) {
+      const bf16x8 v = *(const bf16x8*)(in + (size_t)(r0 + r) * Cc + c0 + cc);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[r][cc + e] = v[e];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = threadIdx.x + 256 * k, c = i >> 3, rr = (i & 7) * 8;
+    if (c0 + c < Cc && r0 + rr < R) {
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = t[rr + e][c];
+      *(bf16x8*)(out + (size_t)(c0 + c) * R + r0 + rr) = v;
+    }
+  }
+}
+
+hipError_t transpose_bf16(const void* in, int R, int Cc, void* out, hipStream_t s) {
+  if (R <= 0 || Cc <= 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_bf16_k, dim3((Cc + 63) / 64, (R + 63) / 64), dim3(256), 0, s, (const bf16*)in, R, Cc,
+                     (bf16*)out);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- RMSNorm
 // One wavefront per row; up to MAXV 16-byte vectors per lane stay in registers
 // (C <= 64*MAXV*VN), longer rows are streamed twice.

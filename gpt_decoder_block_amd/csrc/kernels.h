@@ -17,6 +17,8 @@ inline int dt_size(int dt) { return dt == BF16 ? 2 : 4; }
 
 // ---------------------------------------------------------------- elementwise
 hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s);
+// out [Cc, R] = in [R, Cc]^T, bf16, R and Cc multiples of 8, out not aliasing in
+hipError_t transpose_bf16(const void* in, int R, int Cc, void* out, hipStream_t s);
 // xn = x * r, r = 1/sqrt(mean(x^2)+eps) per row of [N, C]
 // amax (optional): atomically raised to the largest |xn| stored; zeroed by the caller
 hipError_t rmsnorm_fwd(int dt, const void* x, void* xn, float* r, int N, int C, float eps, hipStream_t s,
