@@ -135,6 +135,24 @@ def test_gemm_bf16_multi_tile_exact_shapes():
     assert_close(C, A.astype(np.float64) @ B.astype(np.float64).T, "bf16", "store")
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_gemm_token_major_strided(dt):
+    # both operands M/N-contiguous (the weight-gradient layout) with leading
+    # dimensions wider than the rows, several tiles and a ragged K tail
+    M, N, K, lda, ldb = 520, 776, 1000, 528, 800
+    A = rounded(RNG.standard_normal((K, lda)), dt)
+    B = rounded(RNG.standard_normal((K, ldb)), dt)
+    ref = A[:, :M].astype(np.float64).T @ B[:, :N].astype(np.float64)
+    print(f"gemm token-major dt={dt} M={M} N={N} K={K} lda={lda} ldb={ldb}", flush=True)
+    ws = empty((max(1, ops.gemm_ws_bytes(TDT[dt], M, N, K, 4) // 4),), torch.float32)
+    C = empty((M, N), torch.float32)
+    ops.gemm(M, N, K, dev(A, dt), False, lda, dev(B, dt), False, ldb, 4, C, N, ws=ws)
+    assert_close(C, ref, "f32", "fp32 out", tol=1e-5)
+    Cb = empty((M, N), dt)
+    ops.gemm(M, N, K, dev(A, dt), False, lda, dev(B, dt), False, ldb, 0, Cb, N)
+    assert_close(Cb, ref, dt, "store")
+
+
 # ---------------------------------------------------------------- attention
 def _attn_case(dt, B, T, H, Hkv, D, window, qk_normed=False):
     W3 = (H + 2 * Hkv) * D
