@@ -500,6 +500,20 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_k(GemmArgs p) {
   } else {
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
+    const int c = lane;            // this lane's 4-column chunk of the row
+    const int n = n0 + c * 4;
+    const bool cok = c * 4 < ncols;
+    constexpr int RPW = 128 / (NW);  // rows per wave per pass
+    // residual / saved-u operand for all of this wave's rows of the pass,
+    // loaded before the accumulators are staged so the loads overlap it
+    OV rv[RPW];
+    if (EPI == EPI_RESID || EPI == EPI_DRELU2 || EPI == EPI_DSQR || EPI == EPI_AXPBY) {
+#pragma unroll
+      for (int k = 0; k < RPW; ++k) {
+        const int m = m0 + q * 128 + w + k * (NW);
+        rv[k] = (cok && m < p.M) ? *(const OV*)((const OT*)p.R + (size_t)m * p.ldr + n) : OV{};
+      }
+    }
     if (wm == q) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -515,19 +529,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_k(GemmArgs p) {
       }
     }
     __syncthreads();
-    const int c = lane;            // this lane's 4-column chunk of the row
-    const int n = n0 + c * 4;
-    const bool cok = c * 4 < ncols;
-    constexpr int RPW = 128 / (NW);  // rows per wave per pass
-    // residual / saved-u operand for all of this wave's rows, loaded up front
-    OV rv[RPW];
-    if (EPI == EPI_RESID || EPI == EPI_DRELU2 || EPI == EPI_DSQR || EPI == EPI_AXPBY) {
-#pragma unroll
-      for (int k = 0; k < RPW; ++k) {
-        const int m = m0 + q * 128 + w + k * (NW);
-        rv[k] = (cok && m < p.M) ? *(const OV*)((const OT*)p.R + (size_t)m * p.ldr + n) : OV{};
-      }
-    }
     if constexpr (EPI == EPI_QKNORM) {
       // Each half-wave takes one row per iteration; 16 lanes per head, lane
       // hl owning columns 4hl..4hl+3 and their RoPE partners 64 + 4hl..: the
