@@ -454,14 +454,21 @@ __device__ __forceinline__ void qknorm_rope_bwd_row(const f32x16 (&acc)[4], floa
 // in flight during the current tile.  Each tile is taken as two 32-query
 // halves, so only one half's S and dP are live at a time: dV^T += dO^T P and
 // dK^T += Q^T dS accumulate in registers, with the transposed operands read
-// by the LDS transpose load.
-template <int NW>
+// by the LDS transpose load.  A wave has 256 registers (two per SIMD); the
+// accumulators take 128, so KX of its eight K fragments wait in LDS (KX = 3
+// fills the 160 KiB beside V and the two Q/dO stages) rather than in
+// scratch, whose reloads would also wait for the next tile's copies
+// (vector-memory counts retire in order).
+template <int NW, int KX = 3>
 __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_bf16_k(AttnArgs a, float scale_log2, float scale) {
   constexpr int FK = 32 * NW;
   __shared__ __attribute__((aligned(16))) bf16 Vs[FK * HD];
   __shared__ __attribute__((aligned(16))) bf16 Qs[2][64 * HD];
   __shared__ __attribute__((aligned(16))) bf16 Ds[2][64 * HD];
   __shared__ __attribute__((aligned(16))) float Ls[2][NW][64];  // [stage][wave: lse (even), delta (odd)][row]
+  // the last KX of the wave's eight K fragments, parked in LDS (private to
+  // the wave) to free registers
+  __shared__ __attribute__((aligned(16))) bf16x8 Kx[NW][KX > 0 ? KX : 1][64];
   const int T = a.T, H = a.H, Hkv = a.Hkv, W = a.window, G = H / Hkv;
   const int b = blockIdx.x / Hkv, g = blockIdx.x % Hkv;   // grid (B*Hkv, key blocks)
   const int kv0 = blockIdx.y * FK;
@@ -491,11 +498,15 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_bf16_k(AttnArgs a, float
   for (int r = 0; r < FK; r += 64) tile_async<NW>(base + (H + Hkv + g) * HD, a.ld, kv0 + r, T, Vs + r * HD);
   if (total > 0) issue(0, 0);
 
-  bf16x8 kf[8];
+  bf16x8 kf[8 - KX];
   {
     const int kc = min(kj, T - 1);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) kf[kk] = *(const bf16x8*)(base + (size_t)kc * a.ld + (H + g) * HD + kk * 16 + lh * 8);
+    for (int kk = 0; kk < 8; ++kk) {
+      const bf16x8 v = *(const bf16x8*)(base + (size_t)kc * a.ld + (H + g) * HD + kk * 16 + lh * 8);
+      if (kk < 8 - KX) kf[kk < 8 - KX ? kk : 0] = v;
+      else Kx[w][kk >= 8 - KX ? kk - (8 - KX) : 0][lane] = v;
+    }
   }
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -519,7 +530,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_bf16_k(AttnArgs a, float
         f32x16 sv = f32x16{}, dpv = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-          sv = mfma32(row_frag(Qs[st], ib, kk, lr, lh), kf[kk], sv);
+          sv = mfma32(row_frag(Qs[st], ib, kk, lr, lh), kk < 8 - KX ? kf[kk < 8 - KX ? kk : 0] : Kx[w][kk >= 8 - KX ? kk - (8 - KX) : 0][lane], sv);
           dpv = mfma32(row_frag(Ds[st], ib, kk, lr, lh), row_frag(Vs, w, kk, lr, lh), dpv);
         }
         if (!full) {
