@@ -80,6 +80,13 @@ def test_block_d26_widths_ragged_tiles():
     _block_case(w, 0, 1, 130)
 
 
+def test_block_mlp_width_not_tile_multiple():
+    # MLP width 1000 (a multiple of 8, not of 64): the backward's transposed
+    # weight copies end in partial 64x64 tiles on both sides
+    w = workload("d12_gqa_swa").with_(n_layer=1, windows=(-1,), mlp_hidden=1000)
+    _block_case(w, 0, 1, 96)
+
+
 @pytest.mark.parametrize("B,T", [(1, 64), (2, 37)])
 def test_block_tiny_fp32(B, T):
     w = workload("tiny")
