@@ -4,20 +4,22 @@
 // pre-activation, ReLU² backward, fp32 output with split-K, alpha*acc + beta*R).
 //
 // bf16 path (gfx950 MFMA, v_mfma_f32_32x32x16_bf16):
-//   * 256x256 output tile per workgroup, K step 64, 256 threads = 4 waves in a
-//     2x2 grid, each wave a 128x128 sub-tile = 4x4 MFMA blocks of 32x32;
+//   * 256x256 output tile per workgroup, K step 64, 512 threads = 8 waves in a
+//     2x4 grid, each wave a 128x64 sub-tile = 4x2 MFMA blocks of 32x32, two
+//     waves per SIMD (the fp8 path: 4 waves of 128x128);
 //   * both operands are staged in LDS K-contiguous ([row][64 k], 128 B rows)
 //     with the 16-byte chunk index XOR-swizzled by (row ^ row>>3) & 7, so the
 //     fragment reads (32 consecutive rows, one chunk) and the stores of both
 //     loaders are bank-conflict free;
-//   * an operand stored M- (or N-) contiguous is read as 8x8 blocks (eight
-//     16-byte loads along m at eight consecutive k) and transposed in
-//     registers before the LDS store, so every global access is a coalesced
-//     16-byte load and the MFMA loop never sees the layout;
+//   * an operand stored M- (or N-) contiguous is read as 8x8 blocks (16-byte
+//     loads along m at consecutive k; with 8 waves each thread loads four of
+//     them and stores half chunks) and transposed in registers before the LDS
+//     store, so every global access is a coalesced 16-byte load and the MFMA
+//     loop never sees the layout;
 //   * two LDS stages, one barrier per K step: while the MFMAs run on one stage
-//     the next K tile is copied into the other — straight from memory into LDS
-//     (buffer_load ... lds) when both operands are K-contiguous, through
-//     registers otherwise;
+//     the next K tile is copied into the other — a K-contiguous operand
+//     straight from memory into LDS (buffer_load ... lds), the other through
+//     registers;
 //   * the MFMA is issued with the B fragment as its first operand, so each lane
 //     ends up holding 4 consecutive n of one output row m (8-byte bf16 or
 //     16-byte fp32 stores);
@@ -41,7 +43,7 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
 // waves per workgroup of the bf16 GEMM with both operands K-contiguous
-// (the others and the fp8 one use 4)
+// (the other bf16 layouts use 8 too, the fp8 GEMM 4)
 #ifndef GEMM_NW
 #define GEMM_NW 8
 #endif
@@ -69,12 +71,17 @@ __device__ __forceinline__ bf16x8 bload(__amdgpu_buffer_rsrc_t r, unsigned off) 
 // the tile's first row (K-major) or at (kbeg, first row) (M-major), so offsets
 // stay far below 4 GiB; rows past the operand's end and k past the split's
 // end read as zero.
-template <bool KMAJ, int ES = 2>
+// HALF (M-contiguous only): 512 threads share the operand, each loads 4 of
+// the 8 k rows of its 8x8 block and stores 8-byte half chunks (the 8-wave
+// workgroup with both operands M-contiguous).
+template <bool KMAJ, int ES = 2, bool HALF = false>
 struct Loader {
   static_assert(ES == 2 || KMAJ, "fp8 operands are K-major");
+  static_assert(!HALF || !KMAJ, "HALF: M-contiguous operands");
   static constexpr int VEC = 16 / ES;   // elements per 16-byte vector
   static constexpr int BKE = 128 / ES;  // elements per K step
-  bf16x8 r[8];        // 16-byte containers
+  static constexpr int NV = HALF ? 4 : 8;  // vectors per thread and K step
+  bf16x8 r[NV];       // 16-byte containers
   __amdgpu_buffer_rsrc_t rs;
   int tid;            // this thread's index among the 256 that load the operand
   unsigned off0;      // byte offset of this thread's first vector at k step 0
@@ -101,7 +108,7 @@ struct Loader {
       const size_t bytes = (size_t)(kend - kbeg) * ld * 2;
       rs = make_rsrc(base, bytes);
       const bool mvalid = r0 + mc * 8 < rows;
-      off0 = mvalid ? (unsigned)(((kb * 8) * ld + mc * 8) * 2) : OOB;
+      off0 = mvalid ? (unsigned)(((kb * NV) * ld + mc * 8) * 2) : OOB;
       step = (unsigned)(BK * ld * 2);
       rowstep = (unsigned)(ld * 2);
       kcol = 0;
@@ -120,7 +127,7 @@ struct Loader {
   }
   __device__ __forceinline__ void load(int kt) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) load1(kt, i);
+    for (int i = 0; i < NV; ++i) load1(kt, i);
   }
   __device__ __forceinline__ void store(bf16* __restrict__ S) {
     const int t = tid;
@@ -142,11 +149,18 @@ struct Loader {
     static_assert(!KMAJ, "K-major operands are stored whole");
     const int t = tid;
     const int mc = t & 31, kb = t >> 5;
-    bf16x8 w;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = r[i][j];
     const int row = mc * 8 + j;
-    *(bf16x8*)(S + row * BK + ((kb ^ swz(row)) * 8)) = w;
+    if constexpr (HALF) {
+      bf16x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = r[i][j];
+      *(bf16x4*)(S + row * BK + (((kb >> 1) ^ swz(row)) * 8) + (kb & 1) * 4) = w;
+    } else {
+      bf16x8 w;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = r[i][j];
+      *(bf16x8*)(S + row * BK + ((kb ^ swz(row)) * 8)) = w;
+    }
   }
 };
 
@@ -281,14 +295,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_k(GemmArgs p) {
   const int kend = min(p.K, kbeg + ksplit);
   const int nk = (kend - kbeg + KSTEP - 1) / KSTEP;
 
-  // register loaders of M/N-contiguous operands: all threads load both with
-  // 4 waves; with 8, waves 0-3 load A and waves 4-7 load B
+  // register loaders of M/N-contiguous operands: every thread takes part in
+  // both; with 8 waves each thread loads half of its 8x8 block (HALF)
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  Loader<AK, ES> la;
-  Loader<BK_, ES> lb;
-  la.init(p.A, p.lda, p.M, m0, kbeg, kend, t & 255);
-  lb.init(p.B, p.ldb, p.N, n0, kbeg, kend, t & 255);
-  const bool ldA = NW == 4 || w < 4, ldB = NW == 4 || w >= 4;  // wave-uniform
+  constexpr bool HALF = NW == 8;
+  Loader<AK, ES, HALF && !AK> la;
+  Loader<BK_, ES, HALF && !BK_> lb;
+  la.init(p.A, p.lda, p.M, m0, kbeg, kend, HALF ? t : t & 255);
+  lb.init(p.B, p.ldb, p.N, n0, kbeg, kend, HALF ? t : t & 255);
 
   const int wm = w / WNN, wn = w % WNN;
   const int lr = lane & 31, lh = lane >> 5;
@@ -353,25 +367,26 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_k(GemmArgs p) {
     if constexpr (AK) da.init(p.A, p.lda, p.M, m0, kbeg, kend);
     if constexpr (BK_) db.init(p.B, p.ldb, p.N, n0, kbeg, kend);
     // the wave's loads of one K step, in a fixed order: DMA copies of A
-    // (32/NW), DMA copies of B (32/NW), register loads of A (8, if ldA),
-    // register loads of B (8, if ldB)
+    // (32/NW), DMA copies of B (32/NW), register loads of A (8, or 4 with
+    // 8 waves), register loads of B (likewise)
     constexpr int ND = 32 / NW;
-    constexpr int NQ = (AK ? ND : 8) + (BK_ ? ND : 8);  // at most per wave
+    constexpr int NRG = HALF ? 4 : 8;  // register loads per operand
+    constexpr int NQ = (AK ? ND : NRG) + (BK_ ? ND : NRG);  // at most per wave
     auto issue1 = [&](int kt, int stg, int q) {
-      if (q < (AK ? ND : 8)) {
+      if (q < (AK ? ND : NRG)) {
         if constexpr (AK) da.load1(kt, smem[stg][0], q);
-        else if (ldA) la.load1(kt, q);
+        else la.load1(kt, q);
       } else {
-        const int q2 = q - (AK ? ND : 8);
+        const int q2 = q - (AK ? ND : NRG);
         if constexpr (BK_) db.load1(kt, smem[stg][1], q2);
-        else if (ldB) lb.load1(kt, q2);
+        else lb.load1(kt, q2);
       }
     };
     auto store1 = [&](int stg, int q) {  // q < 16: A stores 0-7, B stores 8-15
       if (q < 8) {
-        if constexpr (!AK) { if (ldA) la.store1(smem[stg][0], q); }
+        if constexpr (!AK) la.store1(smem[stg][0], q);
       } else {
-        if constexpr (!BK_) { if (ldB) lb.store1(smem[stg][1], q - 8); }
+        if constexpr (!BK_) lb.store1(smem[stg][1], q - 8);
       }
     };
 #pragma unroll
@@ -847,16 +862,14 @@ hipError_t gemm(int dt, const GemmArgs& a, hipStream_t s) {
   if (dt == BF16) {
     const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
     dim3 g(nbm * nbn, a.splits);
-    // both operands copied straight into LDS: 8 waves (measured 2-10% faster
-    // on the block's shapes); a register-loaded operand: 4 waves (with 8, the
-    // loading waves run out of registers: both operands loaded that way run at
-    // half speed, one at 4-7% below 4 waves), except the ReLU^2-backward
-    // product, whose epilogue reads a second [M, N] tensor (3.5% faster with 8)
+    // 8 waves (two per SIMD, one wave's MFMAs running while the other waits
+    // on its copies or LDS reads): measured 2-10% faster than 4 with both
+    // operands copied straight into LDS, 4-6% with an M/N-contiguous operand
+    // loaded into registers (each thread loading half of its 8x8 block)
     if (a.a_kmajor && a.b_kmajor) return launch_bf16<true, true, false, bf16, GEMM_NW>(a, g, s);
-    if (a.a_kmajor && !a.b_kmajor && a.epi == EPI_DSQR) return launch_bf16<true, false, false, bf16, 8>(a, g, s);
-    if (a.a_kmajor && !a.b_kmajor) return launch_bf16<true, false, false, bf16, 4>(a, g, s);
-    if (!a.a_kmajor && !a.b_kmajor) return launch_bf16<false, false, false, bf16, 4>(a, g, s);
-    return launch_bf16<false, true, false, bf16, 4>(a, g, s);
+    if (a.a_kmajor) return launch_bf16<true, false, false, bf16, 8>(a, g, s);
+    if (!a.b_kmajor) return launch_bf16<false, false, false, bf16, 8>(a, g, s);
+    return launch_bf16<false, true, false, bf16, 8>(a, g, s);
   }
   if (a.batch > 1) {  // the fp32 path takes blockIdx.z for split-K: one launch per item
     for (int z = 0; z < a.batch; ++z) {
