@@ -57,53 +57,62 @@ __device__ __forceinline__ unsigned e4m3_code(float q) {
   return sign | code;
 }
 
-// Tile of 64 rows x 64 columns, 256 threads.  Thread t quantises 16
-// consecutive codes of row t/4; the transpose goes through LDS as 4x4 byte
-// blocks (thread t owns rows 4*(t%16).., columns 4*(t/16)..).
+// Tile of 128 rows x 64 columns, 256 threads.  Thread t quantises 16
+// consecutive codes of rows t/4 and 64 + t/4; the transpose goes through LDS
+// (one 32-bit word per 4 codes): output row c of the tile gathers its 128
+// codes as eight 16-byte pieces, so each transposed row segment is one whole
+// 128-byte line written by eight consecutive lanes.
 template <typename T>
 __global__ __launch_bounds__(256) void quant_k(const T* __restrict__ x, int R, int Cc, const float* __restrict__ amax,
                                                 uint8_t* __restrict__ xq, uint8_t* __restrict__ xqt, int Rp) {
-  __shared__ unsigned tile[64][17];
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  __shared__ unsigned tile[128][17];
+  const int r0 = blockIdx.y * 128, c0 = blockIdx.x * 64;
   const int t = threadIdx.x;
-  const int rr = t >> 2, cs = (t & 3) * 16;
-  const int r = r0 + rr, c = c0 + cs;
+  const int cs = (t & 3) * 16, c = c0 + cs;
   const float am = amax[0];
   const float s = am / 448.0f;
-  unsigned w[4] = {0u, 0u, 0u, 0u};
-  if (r < R && c < Cc && am > 0.f) {
-    float v[16];
-    if (sizeof(T) == 2) {
-      ld16(x + (size_t)r * Cc + c, v);
-      ld16(x + (size_t)r * Cc + c + 8, v + 8);
-    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ld16(x + (size_t)r * Cc + c + 4 * i, v + 4 * i);
+  for (int h = 0; h < 2; ++h) {
+    const int rr = (t >> 2) + 64 * h, r = r0 + rr;
+    unsigned w[4] = {0u, 0u, 0u, 0u};
+    if (r < R && c < Cc && am > 0.f) {
+      float v[16];
+      if (sizeof(T) == 2) {
+        ld16(x + (size_t)r * Cc + c, v);
+        ld16(x + (size_t)r * Cc + c + 8, v + 8);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ld16(x + (size_t)r * Cc + c + 4 * i, v + 4 * i);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) w[i] |= e4m3_code(v[4 * i + b] / s) << (8 * b);
+    }
+    if (xq && r < R && c < Cc) {
+      u32x4_t o = {w[0], w[1], w[2], w[3]};
+      *(u32x4_t*)(xq + (size_t)r * Cc + c) = o;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) w[i] |= e4m3_code(v[4 * i + b] / s) << (8 * b);
-  }
-  if (xq && r < R && c < Cc) {
-    u32x4_t o = {w[0], w[1], w[2], w[3]};
-    *(u32x4_t*)(xq + (size_t)r * Cc + c) = o;
+    for (int i = 0; i < 4; ++i) tile[rr][(t & 3) * 4 + i] = w[i];
   }
   if (!xqt) return;  // uniform over the workgroup
-#pragma unroll
-  for (int i = 0; i < 4; ++i) tile[rr][(t & 3) * 4 + i] = w[i];
   __syncthreads();
-  const int br = t & 15, bc = t >> 4;  // 4x4 block: rows 4br.., columns 4bc..
-  unsigned in[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) in[i] = tile[4 * br + i][bc];
+  for (int h = 0; h < 2; ++h) {
+    // piece (t & 7) of output row 32h + t/8: codes of tile rows 16(t&7) .. +15
+    const int oc = 32 * h + (t >> 3), rs = 16 * (t & 7);
+    const int word = oc >> 2, sh = 8 * (oc & 3);
+    unsigned o[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // column 4bc+j of rows 4br..4br+3 (byte j of each row word)
-    const unsigned o = ((in[0] >> (8 * j)) & 0xFFu) | (((in[1] >> (8 * j)) & 0xFFu) << 8) |
-                       (((in[2] >> (8 * j)) & 0xFFu) << 16) | (((in[3] >> (8 * j)) & 0xFFu) << 24);
-    const int cc = c0 + 4 * bc + j, rw = r0 + 4 * br;
-    if (cc < Cc && rw < Rp) *(unsigned*)(xqt + (size_t)cc * Rp + rw) = o;
+    for (int q = 0; q < 4; ++q) {
+      unsigned v = 0u;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) v |= ((tile[rs + 4 * q + b][word] >> sh) & 0xFFu) << (8 * b);
+      o[q] = v;
+    }
+    const int cc = c0 + oc, rw = r0 + rs;
+    if (cc < Cc && rw < Rp) *(u32x4_t*)(xqt + (size_t)cc * Rp + rw) = u32x4_t{o[0], o[1], o[2], o[3]};
   }
 }
 
@@ -129,7 +138,7 @@ hipError_t fp8_quant(int dt, const void* x, int R, int Cc, const float* amax, ui
                      hipStream_t s) {
   const int rows = xqt ? Rp : R;
   if (rows == 0 || Cc == 0) return hipSuccess;
-  const dim3 grid((Cc + 63) / 64, (rows + 63) / 64);
+  const dim3 grid((Cc + 63) / 64, (rows + 127) / 128);
   if (dt == BF16) hipLaunchKernelGGL(quant_k<bf16>, grid, dim3(256), 0, s, (const bf16*)x, R, Cc, amax, xq, xqt, Rp);
   else hipLaunchKernelGGL(quant_k<float>, grid, dim3(256), 0, s, (const float*)x, R, Cc, amax, xq, xqt, Rp);
   return hipGetLastError();
