@@ -6,7 +6,7 @@
 // bf16 path (gfx950 MFMA, v_mfma_f32_32x32x16_bf16):
 //   * 256x256 output tile per workgroup, K step 64, 512 threads = 8 waves in a
 //     2x4 grid, each wave a 128x64 sub-tile = 4x2 MFMA blocks of 32x32, two
-//     waves per SIMD (the fp8 path: 4 waves of 128x128);
+//     waves per SIMD;
 //   * both operands are staged in LDS K-contiguous ([row][64 k], 128 B rows)
 //     with the 16-byte chunk index XOR-swizzled by (row ^ row>>3) & 7, so the
 //     fragment reads (32 consecutive rows, one chunk) and the stores of both
@@ -43,7 +43,7 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
 // waves per workgroup of the bf16 GEMM with both operands K-contiguous
-// (the other bf16 layouts use 8 too, the fp8 GEMM 4)
+// (the other layouts and the fp8 GEMM use 8 too)
 #ifndef GEMM_NW
 #define GEMM_NW 8
 #endif
@@ -250,13 +250,14 @@ __device__ __forceinline__ i32x8 frag8(const bf16* S, int row, int ch) {
   const u32x4 hi = *(const u32x4*)(S + row * BK + (((ch + 1) ^ swz(row)) * 8));
   return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
+template <int JB = 4>
 __device__ __forceinline__ void load_frags8(const bf16* As, const bf16* Bs, int kk, int wm, int wn, int lr,
                                             int lh, i32x8* af, i32x8* bfr) {
   const int ch = kk * 4 + lh * 2;
 #pragma unroll
   for (int i = 0; i < 4; ++i) af[i] = frag8(As, wm * 128 + i * 32 + lr, ch);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) bfr[j] = frag8(Bs, wn * 128 + j * 32 + lr, ch);
+  for (int j = 0; j < JB; ++j) bfr[j] = frag8(Bs, wn * 32 * JB + j * 32 + lr, ch);
 }
 
 template <typename T> struct V4;
@@ -267,10 +268,10 @@ template <> struct V4<float> { typedef f32x4 t; };
 // float for the fp8 products of an fp32 model)
 // NW: waves per workgroup.  4: a 2x2 grid of 128x128 wave tiles (one wave
 // per SIMD); 8: a 2x4 grid of 128x64 wave tiles, two waves per SIMD, so one
-// wave's MFMAs run while the other waits on its copies or LDS reads (bf16 only).
+// wave's MFMAs run while the other waits on its copies or LDS reads.
 template <bool AK, bool BK_, int EPI, bool F8 = false, typename OT = bf16, int NW = 4>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_k(GemmArgs p) {
-  static_assert(NW == 4 || (NW == 8 && !F8), "8 waves: bf16 only");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int NTH = 64 * NW;
   constexpr int WNN = NW / 2;         // waves along N
   constexpr int JB = BN / WNN / 32;   // 32-column blocks per wave (4 or 2)
@@ -315,45 +316,54 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_k(GemmArgs p) {
 
   if constexpr (F8) {
     // fp8 operands are K-contiguous: both copied straight into LDS
-    DmaLoader<1> da, db;
+    constexpr int NDF = 32 / NW;        // copies per operand and wave
+    constexpr int NM = 4 * JB;          // MFMAs per sub-step
+    constexpr int CH = (4 + JB) * 2;    // 16-byte chunk reads of the next sub-step
+    DmaLoader<1, NW> da, db;
     da.init(p.A, p.lda, p.M, m0, kbeg, kend);
     db.init(p.B, p.ldb, p.N, n0, kbeg, kend);
     da.load(0, smem[0][0]);
     db.load(0, smem[0][1]);
     WAIT_VM0();
     __syncthreads();
-    i32x8 af[2][4], bfr[2][4];
-    load_frags8(smem[0][0], smem[0][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
+    i32x8 af[2][4], bfr[2][JB];
+    load_frags8<JB>(smem[0][0], smem[0][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
     for (int kt = 0; kt < nk; ++kt) {
       const int st = kt & 1;
       const bf16* As = smem[st][0];
       const bf16* Bs = smem[st][1];
-      // first sub-step: each MFMA followed by one of the next step's 16
-      // copies and one of the second sub-step's 16 chunk reads (fixed order)
+      // first sub-step: the MFMAs interleaved with the next step's copies
+      // and the second sub-step's chunk reads (fixed order)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int i = q >> 2, j = q & 3;
+      for (int q = 0; q < NM; ++q) {
+        const int i = q / JB, j = q % JB;
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[0][j], af[0][i], acc[i][j], 0, 0, 0, 0, 0, 0);
-        if (q < 8) da.load1(kt + 1, smem[st ^ 1][0], q);
-        else db.load1(kt + 1, smem[st ^ 1][1], q - 8);
-        // chunk h of fragment r (A blocks 0-3, then B blocks 0-3) of sub-step 1
-        const int r = q >> 1, h = q & 1, ch = 4 + lh * 2 + h;
-        const bool isa = r < 4;
-        const int row = isa ? wm * 128 + r * 32 + lr : wn * 128 + (r - 4) * 32 + lr;
-        const u32x4 v = *(const u32x4*)((isa ? As : Bs) + row * BK + ((ch ^ swz(row)) * 8));
-        i32x8& dst = isa ? af[1][r & 3] : bfr[1][r & 3];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[4 * h + e] = (int)v[e];
+        for (int u = q * 2 * NDF / NM; u < (q + 1) * 2 * NDF / NM; ++u) {
+          if (u < NDF) da.load1(kt + 1, smem[st ^ 1][0], u);
+          else db.load1(kt + 1, smem[st ^ 1][1], u - NDF);
+        }
+        // chunk h of fragment r (A blocks 0-3, then B blocks) of sub-step 1
+#pragma unroll
+        for (int v = q * CH / NM; v < (q + 1) * CH / NM; ++v) {
+          const int r = v >> 1, h = v & 1, ch = 4 + lh * 2 + h;
+          const bool isa = r < 4;
+          const int row = isa ? wm * 128 + r * 32 + lr : wn * 32 * JB + (r - 4) * 32 + lr;
+          const u32x4 x = *(const u32x4*)((isa ? As : Bs) + row * BK + ((ch ^ swz(row)) * 8));
+          i32x8& dst = isa ? af[1][r & 3] : bfr[1][(r - 4) & (JB - 1)];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dst[4 * h + e] = (int)x[e];
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[1][j], af[1][i], acc[i][j], 0, 0, 0, 0, 0, 0);
       WAIT_VM0();
       __syncthreads();
-      load_frags8(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
+      load_frags8<JB>(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
     }
   } else {
     // bf16: a K-contiguous operand is copied straight into LDS (DMA); an
@@ -852,8 +862,8 @@ hipError_t gemm_fp8(int out_dt, const GemmArgs& a, hipStream_t s) {
   if (!a.a_kmajor || !a.b_kmajor || !a.amax_a || !a.amax_b) return hipErrorInvalidValue;
   const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
   const dim3 g(nbm * nbn, a.splits);
-  if (out_dt == F32 && a.epi != EPI_F32) return launch_bf16<true, true, true, float>(a, g, s);
-  return launch_bf16<true, true, true>(a, g, s);
+  if (out_dt == F32 && a.epi != EPI_F32) return launch_bf16<true, true, true, float, 8>(a, g, s);
+  return launch_bf16<true, true, true, bf16, 8>(a, g, s);
 }
 
 hipError_t gemm(int dt, const GemmArgs& a, hipStream_t s) {
