@@ -64,6 +64,7 @@ __all__ = [
     "cross_entropy", "e4m3_round",
     "bf16_round", "fp8_quantize", "fp8_quant_dequant", "block_forward", "block_backward", "lm_head_ce",
     "embed_forward", "embed_backward", "smear_forward", "smear_backward",
+    "mix_forward", "mix_backward", "ve_forward", "ve_backward", "backout_forward", "backout_backward",
     "stack_forward_backward", "FP8_E4M3_MAX",
 ]
 
@@ -275,9 +276,70 @@ def _mm_nt(a, b, fp8, storage=None):
     return a @ b.T
 
 
-# ------------------------------------------------------------------- block
+# ------------------------------------------------------------------ extras
 def _sigmoid(x):
     return 1.0 / (1.0 + np.exp(-x))
+
+
+def mix_forward(x: np.ndarray, x0: np.ndarray, a: float, b: float) -> np.ndarray:
+    """Per-layer residual mixing ([FR] the per-layer residual scaling snippet):
+    the block runs on a*x + b*x0, x0 the stream after embedding and smear."""
+    return a * x + b * x0
+
+
+def mix_backward(dy: np.ndarray, x: np.ndarray, x0: np.ndarray, a: float, b: float) -> dict:
+    """Gradients of y = a*x + b*x0 given dy: dx = a*dy, dx0 = b*dy,
+    da = sum(dy*x), db = sum(dy*x0); sum_abs holds each scalar sum's terms'
+    magnitudes (the scale of its forward error bound)."""
+    return {"dx": a * dy, "dx0": b * dy, "da": float(np.sum(dy * x)), "db": float(np.sum(dy * x0)),
+            "sum_abs": {"da": float(np.sum(np.abs(dy * x))), "db": float(np.sum(np.abs(dy * x0)))}}
+
+
+def ve_forward(xn: np.ndarray, v: np.ndarray, ids: np.ndarray, ve: np.ndarray, wg: np.ndarray
+               ) -> Tuple[np.ndarray, dict]:
+    """Value embedding ([FR] the value-embedding snippet): per token and K/V
+    head g, s = xn[..., :nc] . wg[g], v[..., g, :] += 3*sigmoid(s) * VE[id, g, :].
+    xn [B, T, C], v [B, T, Hkv, D], ids [B, T], ve [V, Hkv*D], wg [Hkv, nc]."""
+    B, T, Hkv, D = v.shape
+    nc = wg.shape[1]
+    s = xn[..., :nc] @ wg.T                 # [B, T, Hkv]
+    gate = 3.0 * _sigmoid(s)
+    rows = ve[ids].reshape(B, T, Hkv, D)
+    return v + gate[..., None] * rows, {"ve_s": s, "ve_gate": gate, "ve_rows": rows}
+
+
+def ve_backward(dv: np.ndarray, xn: np.ndarray, ids: np.ndarray, wg: np.ndarray, V: int, c: dict) -> dict:
+    """Backward of `ve_forward` given dv (the gradient w.r.t. the updated v,
+    which also flows unchanged to the projection's v): the gate logits'
+    gradient ds, dwg = sum over tokens of ds (x) xn[..., :nc], the extra
+    gradient of xn, and the table's rows dve (repeated ids add up)."""
+    B, T, Hkv, D = dv.shape
+    nc = wg.shape[1]
+    dgate = np.sum(dv * c["ve_rows"], axis=-1)                   # [B, T, Hkv]
+    sg = _sigmoid(c["ve_s"])
+    ds = dgate * 3.0 * sg * (1.0 - sg)
+    dwg = np.einsum("bth,btc->hc", ds, xn[..., :nc])
+    dxn = np.zeros_like(xn)
+    dxn[..., :nc] = ds @ wg
+    dve = np.zeros((V, Hkv * D))
+    np.add.at(dve, ids.reshape(-1), (dv * c["ve_gate"][..., None]).reshape(B * T, Hkv * D))
+    # per element, the sum over tokens of the summed terms' magnitudes (the
+    # scale of that sum's forward error bound)
+    dwg_abs = np.einsum("bth,btc->hc", np.abs(ds), np.abs(xn[..., :nc]))
+    return {"ds": ds, "dwg": dwg, "dxn": dxn, "dve": dve, "dwg_sum_abs": dwg_abs}
+
+
+def backout_forward(x: np.ndarray, x_bo: np.ndarray, lam: float) -> np.ndarray:
+    """Backout ([FR] the backout snippet): x - lam * x_bo before the final norm."""
+    return x - lam * x_bo
+
+
+def backout_backward(dy: np.ndarray, x_bo: np.ndarray, lam: float) -> dict:
+    """Gradients of y = x - lam*x_bo: dx = dy, dx_bo = -lam*dy, dlam = -sum(dy*x_bo)."""
+    return {"dx_bo": -lam * dy, "dlam": -float(np.sum(dy * x_bo)), "sum_abs": float(np.sum(np.abs(dy * x_bo)))}
+
+
+# ------------------------------------------------------------------- block
 
 
 def block_forward(x: np.ndarray, p: Dict[str, np.ndarray], cfg, l: int,
@@ -300,7 +362,7 @@ def block_forward(x: np.ndarray, p: Dict[str, np.ndarray], cfg, l: int,
     c = {}
     if cfg.extras:
         c["x_premix"], c["x0"] = x, x0
-        x = p["resid_lambda"] * x + p["x0_lambda"] * x0
+        x = mix_forward(x, x0, p["resid_lambda"], p["x0_lambda"])
     c["x_in"] = x
     xn1, r1 = rms_norm(x, eps)
     qkv = xn1 @ p["w_qkv"].T
@@ -308,12 +370,8 @@ def block_forward(x: np.ndarray, p: Dict[str, np.ndarray], cfg, l: int,
     k = qkv[..., Q:Q + KV].reshape(B, T, Hkv, D)
     v = qkv[..., Q + KV:].reshape(B, T, Hkv, D)
     if cfg.extras and "ve" in p:
-        nch = cfg.ve_gate_channels
-        s = xn1[..., :nch] @ p["ve_gate"].T                 # [B, T, Hkv]
-        gate = 3.0 * _sigmoid(s)
-        ve = p["ve"][ids].reshape(B, T, Hkv, D)
-        c.update(ve_s=s, ve_gate=gate, ve_rows=ve)
-        v = v + gate[..., None] * ve
+        v, cv = ve_forward(xn1, v, ids, p["ve"], p["ve_gate"])
+        c.update(cv)
     qn, rq = rms_norm(q, eps)
     kn, rk = rms_norm(k, eps)
     qh, kh = rope(qn, cos, sin), rope(kn, cos, sin)
@@ -358,37 +416,21 @@ def block_backward(dout: np.ndarray, c: dict, p: Dict[str, np.ndarray], cfg, l: 
     dk = rms_norm_backward(rope_backward(dkh, cos, sin), c["kn"], c["rk"])
     dxn1_extra = 0.0
     if cfg.extras and "ve" in p:
-        # v' = v + gate * ve
-        dgate = np.sum(dv * c["ve_rows"], axis=-1)                   # [B,T,Hkv]
-        dve_rows = dv * c["ve_gate"][..., None]
-        sg = _sigmoid(c["ve_s"])
-        ds = dgate * 3.0 * sg * (1.0 - sg)
-        nch = cfg.ve_gate_channels
-        g["ve_gate"] = np.einsum("bth,btc->hc", ds, c["xn1"][..., :nch])
-        # per element, the sum over tokens of the summed terms' magnitudes (the
-        # scale of that sum's forward error bound)
-        ve_gate_sum_abs = np.einsum("bth,btc->hc", np.abs(ds), np.abs(c["xn1"][..., :nch]))
-        dxe = np.zeros_like(c["xn1"])
-        dxe[..., :nch] = ds @ p["ve_gate"]
-        dxn1_extra = dxe
-        dve = np.zeros_like(p["ve"])
-        np.add.at(dve, ids.reshape(-1), dve_rows.reshape(B * T, KV))
-        g["ve"] = dve
+        gv = ve_backward(dv, c["xn1"], ids, p["ve_gate"], p["ve"].shape[0], c)
+        g["ve_gate"], g["ve"], dxn1_extra = gv["dwg"], gv["dve"], gv["dxn"]
+        ve_gate_sum_abs = gv["dwg_sum_abs"]
     dqkv = np.concatenate([dq.reshape(B, T, Q), dk.reshape(B, T, KV), dv.reshape(B, T, KV)], -1)
     dxn1 = dqkv @ p["w_qkv"] + dxn1_extra
     g["w_qkv"] = np.einsum("btk,btc->kc", dqkv, c["xn1"])
     dx = dx_mid + rms_norm_backward(dxn1, c["xn1"], c["r1"])
     if cfg.extras:
-        g["resid_lambda"] = np.sum(dx * c["x_premix"])
-        g["x0_lambda"] = np.sum(dx * c["x0"])
-        # sum of the magnitudes of the summed terms: the scale of the forward
-        # error bound of each of these two sums
-        g["sum_abs"] = {"resid_lambda": np.sum(np.abs(dx * c["x_premix"])),
-                        "x0_lambda": np.sum(np.abs(dx * c["x0"]))}
+        gm = mix_backward(dx, c["x_premix"], c["x0"], p["resid_lambda"], p["x0_lambda"])
+        g["resid_lambda"], g["x0_lambda"] = gm["da"], gm["db"]
+        g["sum_abs"] = {"resid_lambda": gm["sum_abs"]["da"], "x0_lambda": gm["sum_abs"]["db"]}
         if "ve" in p:
             g["sum_abs"]["ve_gate"] = ve_gate_sum_abs
-        g["x0"] = p["x0_lambda"] * dx
-        dx = p["resid_lambda"] * dx
+        g["x0"] = gm["dx0"]
+        dx = gm["dx"]
     return dx, g
 
 
@@ -499,15 +541,16 @@ def stack_forward_backward(cfg, ids: np.ndarray, glob: Dict[str, np.ndarray],
             x_bo = x
     acts.append(x)
     if cfg.extras:
-        x_final = x - glob["backout_lambda"] * x_bo
+        x_final = backout_forward(x, x_bo, glob["backout_lambda"])
     else:
         x_final = x
     loss, dx, dw_lm, hc = lm_head_ce(x_final, glob["w_lm"], tgt, cfg.eps)
     grads = {"w_lm": dw_lm, "layers": [None] * L}
     if cfg.extras:
-        grads["backout_lambda"] = -float(np.sum(dx * x_bo))
-        sum_abs = {"backout_lambda": float(np.sum(np.abs(dx * x_bo)))}
-        dx_bo = -glob["backout_lambda"] * dx
+        gb = backout_backward(dx, x_bo, glob["backout_lambda"])
+        grads["backout_lambda"] = gb["dlam"]
+        sum_abs = {"backout_lambda": gb["sum_abs"]}
+        dx_bo = gb["dx_bo"]
         dx0 = np.zeros_like(dx)
     for l in reversed(range(L)):
         if cfg.extras and l == i_bo:

@@ -20,14 +20,20 @@ def ns_bar(dt, G, coeffs, norm_scale=1.02, eps=1e-7):
     first step sums terms up to 30 times its result (8.156 - 22.483 + 15.879
     = 1.552 at a unit singular value), so storage rounding alone moves the
     result by percents.  The bar is twice that move, measured by the oracle
-    with its three lines' results rounded to bf16, and never below 2e-2 (the
-    same rule as the fp8 bars: twice the oracle's own spread)."""
+    with its three lines' results rounded to bf16, taking the larger move of
+    the two orientations (G with Gram X^T X, and the transposed problem, whose
+    exact map is the same), never below 2e-2.  A bar above 2e-2 is a stated
+    exception to the bf16 bar, printed as such."""
     if dt == "f32":
         return TOL["f32"]
     exact = O.newton_schulz(G, coeffs, norm_scale, eps)
-    stored = O.newton_schulz(G, coeffs, norm_scale, eps, round_to="bf16")
-    spread = float(np.max(np.abs(stored - exact)) / np.max(np.abs(exact)))
-    return max(TOL["bf16"], 2.0 * spread)
+    den = float(np.max(np.abs(exact)))
+    spread = max(float(np.max(np.abs(O.newton_schulz(G, coeffs, norm_scale, eps, round_to="bf16") - exact))),
+                 float(np.max(np.abs(O.newton_schulz(G.T, coeffs, norm_scale, eps, round_to="bf16").T - exact))))
+    bar = max(TOL["bf16"], 2.0 * spread / den)
+    if bar > TOL["bf16"]:
+        print(f"newton_schulz bf16 exception: bar {bar:.3e} (storage-rounding move {spread / den:.3e})", flush=True)
+    return bar
 
 
 def _ns_case(dt, m, n, coeffs, seed):
