@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgdb.so")
 
 # the GDB_ABI_VERSION this binding's structures and signatures follow
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 GDB_OK, GDB_EINVAL, GDB_EUNSUPPORTED, GDB_EHIP, GDB_EWORKSPACE = 0, -1, -2, -3, -4
 GDB_F32, GDB_BF16 = 0, 1
@@ -28,7 +28,8 @@ class BlockCfg(ctypes.Structure):
     _fields_ = [("B", c_int32), ("T", c_int32), ("C", c_int32),
                 ("n_head", c_int32), ("n_kv_head", c_int32), ("head_dim", c_int32),
                 ("mlp_hidden", c_int32), ("window", c_int32), ("dtype", c_int32),
-                ("mlp_fp8", c_int32), ("accumulate_wgrad", c_int32), ("eps", c_float)]
+                ("mlp_fp8", c_int32), ("accumulate_wgrad", c_int32), ("deterministic", c_int32),
+                ("eps", c_float)]
 
 
 class BlockWeights(ctypes.Structure):
@@ -69,8 +70,9 @@ SIGNATURES = {
                                   ctypes.POINTER(c_size_t), ctypes.POINTER(c_size_t)]),
     "gdb_rope_table_host": (c_int32, [c_int32, c_int32, ctypes.c_double, c_void_p]),
     "gdb_embed_fwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "gdb_embed_bwd_ws_bytes": (c_int32, [c_int32, c_int32, ctypes.POINTER(c_size_t)]),
     "gdb_embed_bwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int32,
-                                c_void_p]),
+                                c_int32, c_void_p, c_void_p]),
     "gdb_block_fwd": (c_int32, [ctypes.POINTER(BlockCfg), ctypes.POINTER(BlockWeights),
                                 ctypes.POINTER(BlockExtras), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                 c_void_p]),
@@ -80,7 +82,8 @@ SIGNATURES = {
                                 c_void_p]),
     "gdb_lm_head_ce_sizes": (c_int32, [c_int32, c_int32, c_int32, c_int32, ctypes.POINTER(c_size_t)]),
     "gdb_lm_head_ce_fwd_bwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p,
-                                         c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
+                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                                         c_void_p]),
     "gdb_smear_fwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                 c_void_p, c_void_p, c_void_p]),
     "gdb_smear_bwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
@@ -89,6 +92,15 @@ SIGNATURES = {
     "gdb_backout_fwd": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "gdb_backout_bwd": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_int32, c_void_p, c_void_p]),
+    "gdb_mix_fwd": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "gdb_mix_bwd": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                              c_int32, c_void_p, c_int32, c_void_p, c_void_p]),
+    "gdb_ve_fwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_int32,
+                             c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p]),
+    "gdb_ve_bwd_ws_bytes": (c_int32, [c_int32, c_int32, c_int32, c_int32, ctypes.POINTER(c_size_t)]),
+    "gdb_ve_bwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                             c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p,
+                             c_int32, c_int32, c_void_p, c_void_p]),
     "gdb_rmsnorm_fwd": (c_int32, [c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p, c_void_p, c_void_p]),
     "gdb_rmsnorm_bwd": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p]),
@@ -120,6 +132,10 @@ SIGNATURES = {
     "gdb_muon_step": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_float,
                                 c_float, c_int32, c_float, c_float, c_void_p, c_int32, c_float, c_float, c_void_p,
                                 c_size_t, c_void_p]),
+    "gdb_normuon_ws_bytes": (c_int32, [c_int32, c_int32, c_int32, c_int32, ctypes.POINTER(c_size_t)]),
+    "gdb_normuon_step": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_void_p, c_float, c_float, c_int32, c_float, c_float, c_float, c_void_p, c_int32,
+                                   c_float, c_float, c_void_p, c_size_t, c_void_p]),
     "gdb_adamw_step": (c_int32, [c_int64, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_float,
                                  c_float, c_float, c_float, c_void_p]),
     "gdb_attention_decode_ws_bytes": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,

@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libgdb.so")
 BUILD = os.path.join(HERE, "_build")
 ARCH = "gfx950"
-SOURCES = ["elementwise.hip", "gemm.hip", "attention.hip", "decode.hip", "optim.hip", "extras.hip", "fp8.hip", "api.cpp"]
+SOURCES = ["elementwise.hip", "gemm.hip", "attention.hip", "decode.hip", "optim.hip", "extras.hip", "fp8.hip", "order.hip",
+           "api.cpp"]
 # per-file code-generation options: the attention kernels run their softmax on
 # the MFMA results, so those stay in VGPRs (no AGPR round trips)
 EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

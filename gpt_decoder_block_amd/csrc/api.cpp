@@ -61,6 +61,7 @@ struct BlockDims {
   int B, T, N, C, H, Hkv, D, Q, KV, W3, F, window, dt, s;
   float eps;
   bool fp8;   // MLP GEMMs on e4m3 codes
+  bool det;   // deterministic backward (fixed-order value-embedding table gradient)
   int Np;     // N rounded up to 16: K of the fp8 weight-gradient GEMMs
 };
 
@@ -80,6 +81,7 @@ gdb_status check_cfg(const gdb_block_cfg* c, BlockDims* d) {
   if (c->window < -1) return fail(GDB_EINVAL, "window must be >= -1 (got %d)", c->window);
   if (c->mlp_fp8 && (c->C % 16 || c->mlp_hidden % 16)) return fail(GDB_EINVAL, "mlp_fp8 needs C and mlp_hidden multiples of 16");
   if (!(c->eps > 0.f) || !std::isfinite(c->eps)) return fail(GDB_EINVAL, "eps must be positive and finite");
+  if (c->deterministic != 0 && c->deterministic != 1) return fail(GDB_EINVAL, "deterministic must be 0 or 1");
   if ((long long)c->B * c->T > (1LL << 30)) return fail(GDB_EINVAL, "B*T too large");
   d->B = c->B; d->T = c->T; d->N = c->B * c->T; d->C = c->C;
   d->H = c->n_head; d->Hkv = c->n_kv_head; d->D = c->head_dim;
@@ -87,6 +89,7 @@ gdb_status check_cfg(const gdb_block_cfg* c, BlockDims* d) {
   d->F = c->mlp_hidden; d->window = c->window >= c->T - 1 ? -1 : c->window;
   d->dt = c->dtype; d->s = dt_size(c->dtype); d->eps = c->eps;
   d->fp8 = c->mlp_fp8 != 0;
+  d->det = c->deterministic != 0;
   d->Np = (d->N + 15) / 16 * 16;
   return GDB_OK;
 }
@@ -112,6 +115,7 @@ struct WsBwd {
   uint8_t *doutq, *doutT, *duq, *duT;  // fp8 MLP backward codes: [N, C], [C, Np], [N, F], [F, Np]
   float* amax8;                        // dout, du
   void* wt;             // bf16: K-major copy of the weight of the current data-gradient product
+  void* order;          // deterministic: token sort scratch (token_order)
 };
 
 void carve_saved(const BlockDims& d, Carver& c, Saved& s) {
@@ -176,6 +180,7 @@ void carve_bwd(const BlockDims& d, Carver& c, WsBwd& w) {
   w.duq = c.take<uint8_t>(f8 * N * d.F);
   w.duT = c.take<uint8_t>(f8 * d.F * Np);
   w.amax8 = c.take<float>(f8 * 2 * 4);
+  w.order = c.take<char>(d.det ? token_order_ws_bytes(d.N) : 0);
 }
 
 // Which extras a call uses; validates their pointers and sizes.
@@ -293,13 +298,29 @@ gdb_status gdb_embed_fwd(int32_t N, int32_t C, int32_t V, int32_t dtype, const i
   return GDB_OK;
 }
 
+gdb_status gdb_embed_bwd_ws_bytes(int32_t N, int32_t deterministic, size_t* ws_bytes) {
+  if (N < 0) return fail(GDB_EINVAL, "N must be >= 0");
+  if (!ws_bytes) return fail(GDB_EINVAL, "ws_bytes is NULL");
+  *ws_bytes = deterministic ? token_order_ws_bytes(N) : 0;
+  g_err.clear();
+  return GDB_OK;
+}
+
 gdb_status gdb_embed_bwd(int32_t N, int32_t C, int32_t V, int32_t dtype, const int32_t* ids, const void* dx0,
-                         float* dwte, int32_t accumulate, void* stream) {
+                         float* dwte, int32_t accumulate, int32_t deterministic, void* ws, void* stream) {
   if (N < 0 || C <= 0 || V <= 0 || C % 8) return fail(GDB_EINVAL, "bad sizes N=%d C=%d V=%d (C multiple of 8)", N, C, V);
   if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
   CHECK_PTR(dwte);
   if (N > 0) { CHECK_PTR(ids); CHECK_PTR(dx0); }
-  HIPCHK(embed_bwd(dtype, ids, dx0, dwte, N, C, V, accumulate, (hipStream_t)stream));
+  hipStream_t s = (hipStream_t)stream;
+  if (deterministic && N > 0) {
+    CHECK_PTR(ws);
+    const int32_t *sk, *perm;
+    HIPCHK(token_order(ids, N, V, ws, &sk, &perm, s));
+    HIPCHK(rows_segsum(dtype, sk, perm, N, dx0, C, 0, C, nullptr, 1, C, dwte, V, accumulate ? 1 : 0, s));
+  } else {
+    HIPCHK(embed_bwd(dtype, ids, dx0, dwte, N, C, V, accumulate, s));
+  }
   g_err.clear();
   return GDB_OK;
 }
@@ -482,9 +503,19 @@ gdb_status gdb_block_bwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
   }
   // value embeddings: gate-logit gradients and the table's rows (dv passes through unchanged)
   if (xe.ve) {
-    if (!acc) HIPCHK(fill_f32(dex->dve, (size_t)ex->ve_vocab * d.KV, 0.f, s));
-    HIPCHK(ve_bwd(dt, wb.dqkv, d.W3, d.Q + d.KV, ex->ids, ex->ve, sv.ve_s, d.Hkv, d.D, ex->ve_vocab, wb.ds, dex->dve,
-                  N, s));
+    if (d.det) {
+      // the table's rows add their tokens in token order (stable sort by id)
+      const int32_t *sk, *perm;
+      HIPCHK(ve_bwd(dt, wb.dqkv, d.W3, d.Q + d.KV, ex->ids, ex->ve, sv.ve_s, d.Hkv, d.D, ex->ve_vocab, wb.ds,
+                    nullptr, N, s));
+      HIPCHK(token_order(ex->ids, N, ex->ve_vocab, wb.order, &sk, &perm, s));
+      HIPCHK(rows_segsum(dt, sk, perm, N, wb.dqkv, d.W3, d.Q + d.KV, d.KV, sv.ve_s, d.Hkv, d.D, dex->dve, ex->ve_vocab,
+                         acc, s));
+    } else {
+      if (!acc) HIPCHK(fill_f32(dex->dve, (size_t)ex->ve_vocab * d.KV, 0.f, s));
+      HIPCHK(ve_bwd(dt, wb.dqkv, d.W3, d.Q + d.KV, ex->ids, ex->ve, sv.ve_s, d.Hkv, d.D, ex->ve_vocab, wb.ds,
+                    dex->dve, N, s));
+    }
   }
   // QKV projection
   {
@@ -543,16 +574,18 @@ gdb_status gdb_lm_head_ce_sizes(int32_t N, int32_t C, int32_t V, int32_t dtype, 
 }
 
 gdb_status gdb_lm_head_ce_fwd_bwd(int32_t N, int32_t C, int32_t V, int32_t dtype, float eps, const void* x,
-                                  const void* w_lm, const int32_t* targets, float* loss, void* dx, float* dw_lm,
-                                  int32_t accumulate, void* ws, void* stream) {
+                                  const void* w_lm, const int32_t* targets, float* loss, float* row_loss, void* dx,
+                                  float* dw_lm, int32_t accumulate, void* ws, void* stream) {
   gdb_status st = check_head(N, C, V, dtype);
   if (st != GDB_OK) return st;
   if (!(eps > 0.f) || !std::isfinite(eps)) return fail(GDB_EINVAL, "eps must be positive and finite");
   CHECK_PTR(x); CHECK_PTR(w_lm); CHECK_PTR(targets); CHECK_PTR(loss); CHECK_PTR(dx); CHECK_PTR(dw_lm); CHECK_PTR(ws);
+  if (row_loss && (((uintptr_t)row_loss) & 3)) return fail(GDB_EINVAL, "row_loss is not 4-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   HeadWs h;
   Carver c(ws);
   carve_head(N, C, V, dtype, c, h);
+  if (row_loss) h.row_loss = row_loss;
   HIPCHK(rmsnorm_fwd(dtype, x, h.xf, h.rf, N, C, eps, s));
   HIPCHK(gemm(dtype, gemm_args(h.xf, true, C, w_lm, true, C, N, V, C, EPI_STORE, h.z, V), s));
   HIPCHK(ce_fwd_bwd(dtype, h.z, targets, h.row_loss, N, V, s));
@@ -1085,6 +1118,150 @@ gdb_status gdb_backout_bwd(int32_t N, int32_t C, int32_t dtype, const void* dy, 
   if ((st = check_scalar(dlam, "dlam")) != GDB_OK) return st;
   if (dx_bo == dy || dx_bo == x_bo) return fail(GDB_EINVAL, "dx_bo must not alias dy or x_bo");
   HIPCHK(backout_bwd(dtype, dy, x_bo, lam, dx_bo, (float*)ws, dlam, accumulate ? 1 : 0, N, C, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
+// ------------------------------------------------- mixing, value embedding
+gdb_status gdb_mix_fwd(int32_t N, int32_t C, int32_t dtype, const void* x, const void* x0, const float* lam, void* y,
+                       void* stream) {
+  gdb_status st;
+  if ((st = check_rows(N, C, dtype)) != GDB_OK) return st;
+  if (N == 0) { g_err.clear(); return GDB_OK; }
+  CHECK_PTR(x); CHECK_PTR(x0); CHECK_PTR(y);
+  if ((st = check_scalar(lam, "lam")) != GDB_OK) return st;
+  HIPCHK(mix_fwd(dtype, x, x0, lam, y, (size_t)N * C, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_mix_bwd(int32_t N, int32_t C, int32_t dtype, const void* dy, const void* x, const void* x0,
+                       const float* lam, void* dx, float* dx0, int32_t accumulate_dx0, float* dlam, int32_t accumulate,
+                       void* ws, void* stream) {
+  gdb_status st;
+  if ((st = check_rows(N, C, dtype)) != GDB_OK) return st;
+  if (N == 0) return fail(GDB_EINVAL, "N must be positive");
+  CHECK_PTR(dy); CHECK_PTR(x); CHECK_PTR(x0); CHECK_PTR(dx); CHECK_PTR(dx0); CHECK_PTR(ws);
+  if ((st = check_scalar(lam, "lam")) != GDB_OK) return st;
+  if ((st = check_scalar(dlam, "dlam")) != GDB_OK) return st;
+  if ((size_t)mix_partials(N) * 2 * 4 > GDB_EXTRAS_WS_BYTES) return fail(GDB_EWORKSPACE, "extras workspace too small");
+  HIPCHK(mix_bwd(dtype, dy, x, x0, lam, dx, dx0, accumulate_dx0 ? 1 : 0, (float*)ws, dlam, accumulate ? 1 : 0, N, C,
+                 (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
+namespace {
+gdb_status check_ve(int32_t N, int32_t Hkv, int32_t D, int32_t dtype, int32_t ldq, int32_t voff, int32_t ldx, int32_t V,
+                    int32_t nc) {
+  if (N < 0) return fail(GDB_EINVAL, "N must be >= 0");
+  if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
+  if (Hkv < 1 || Hkv > 64) return fail(GDB_EUNSUPPORTED, "Hkv must be in [1, 64] (got %d)", Hkv);
+  if (D != 64 && D != 128) return fail(GDB_EUNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+  if (V <= 0) return fail(GDB_EINVAL, "V must be positive");
+  if (ldx <= 0 || ldx % 8 || ldq % 8 || voff % 8 || voff < 0 || voff + Hkv * D > ldq)
+    return fail(GDB_EINVAL, "ldx, ldq, voff must be multiples of 8 with voff + Hkv*D <= ldq");
+  if (nc < 1 || nc > MAX_VE_GATE || nc > ldx) return fail(GDB_EINVAL, "nc must be in [1, min(%d, ldx)]", MAX_VE_GATE);
+  return GDB_OK;
+}
+size_t ve_bwd_ws(int N, int Hkv, int nc, int det) {
+  return al256((size_t)ve_gate_partials(N) * Hkv * nc * 4) + al256((size_t)std::max(N, 1) * Hkv * 4) +
+         (det ? token_order_ws_bytes(N) : 0);
+}
+}  // namespace
+
+gdb_status gdb_ve_fwd(int32_t N, int32_t Hkv, int32_t D, int32_t dtype, void* qkv, int32_t ldq, int32_t voff,
+                      const void* xn, int32_t ldx, const int32_t* ids, const void* ve, int32_t V, const void* wg,
+                      int32_t nc, float* s_save, void* stream) {
+  gdb_status st;
+  if ((st = check_ve(N, Hkv, D, dtype, ldq, voff, ldx, V, nc)) != GDB_OK) return st;
+  if (N == 0) { g_err.clear(); return GDB_OK; }
+  CHECK_PTR(qkv); CHECK_PTR(xn); CHECK_PTR(ve); CHECK_PTR(wg); CHECK_PTR(s_save);
+  if (!ids || (((uintptr_t)ids) & 3)) return fail(GDB_EINVAL, "ids is NULL or not 4-byte aligned");
+  HIPCHK(ve_fwd(dtype, qkv, ldq, voff, xn, ldx, ids, ve, wg, nc, Hkv, D, V, s_save, N, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_ve_bwd_ws_bytes(int32_t N, int32_t Hkv, int32_t nc, int32_t deterministic, size_t* ws_bytes) {
+  if (N < 0 || Hkv < 1 || Hkv > 64 || nc < 1 || nc > MAX_VE_GATE) return fail(GDB_EINVAL, "bad sizes");
+  if (!ws_bytes) return fail(GDB_EINVAL, "ws_bytes is NULL");
+  *ws_bytes = ve_bwd_ws(N, Hkv, nc, deterministic ? 1 : 0);
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_ve_bwd(int32_t N, int32_t Hkv, int32_t D, int32_t dtype, const void* dqkv, int32_t ldq, int32_t voff,
+                      const int32_t* ids, const void* ve, int32_t V, const float* s_save, const void* xn, void* dxn,
+                      int32_t ldx, const void* wg, int32_t nc, float* dve, float* dwg, int32_t accumulate,
+                      int32_t deterministic, void* ws, void* stream) {
+  gdb_status st;
+  if ((st = check_ve(N, Hkv, D, dtype, ldq, voff, ldx, V, nc)) != GDB_OK) return st;
+  if (N == 0) return fail(GDB_EINVAL, "N must be positive");
+  CHECK_PTR(dqkv); CHECK_PTR(ve); CHECK_PTR(s_save); CHECK_PTR(xn); CHECK_PTR(dxn); CHECK_PTR(wg); CHECK_PTR(dve);
+  CHECK_PTR(ws);
+  if (!ids || (((uintptr_t)ids) & 3)) return fail(GDB_EINVAL, "ids is NULL or not 4-byte aligned");
+  if ((st = check_scalar(dwg, "dwg")) != GDB_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* b = (char*)ws;
+  float* part = (float*)b;
+  float* ds = (float*)(b + al256((size_t)ve_gate_partials(N) * Hkv * nc * 4));
+  void* ord = b + al256((size_t)ve_gate_partials(N) * Hkv * nc * 4) + al256((size_t)N * Hkv * 4);
+  const int acc = accumulate ? 1 : 0;
+  if (deterministic) {
+    const int32_t *sk, *perm;
+    HIPCHK(ve_bwd(dtype, dqkv, ldq, voff, ids, ve, s_save, Hkv, D, V, ds, nullptr, N, s));
+    HIPCHK(token_order(ids, N, V, ord, &sk, &perm, s));
+    HIPCHK(rows_segsum(dtype, sk, perm, N, dqkv, ldq, voff, Hkv * D, s_save, Hkv, D, dve, V, acc, s));
+  } else {
+    if (!acc) HIPCHK(fill_f32(dve, (size_t)V * Hkv * D, 0.f, s));
+    HIPCHK(ve_bwd(dtype, dqkv, ldq, voff, ids, ve, s_save, Hkv, D, V, ds, dve, N, s));
+  }
+  HIPCHK(ve_gate_bwd(dtype, ds, xn, dxn, ldx, wg, nc, Hkv, part, dwg, acc, N, s));
+  g_err.clear();
+  return GDB_OK;
+}
+
+// ---------------------------------------------------------------- NorMuon
+gdb_status gdb_normuon_ws_bytes(int32_t count, int32_t m, int32_t n, int32_t dtype, size_t* ws_bytes) {
+  gdb_status st = check_ns(count, m, n, dtype, nullptr, 0);
+  if (st != GDB_OK) return st;
+  if (!ws_bytes) return fail(GDB_EINVAL, "ws_bytes is NULL");
+  *ws_bytes = ns_layout(count, m, n, dtype, true).total + al256((size_t)count * m * 3 * 4);
+  g_err.clear();
+  return GDB_OK;
+}
+
+gdb_status gdb_normuon_step(int32_t count, int32_t m, int32_t n, int32_t dtype, float* p, void* p_bf16,
+                            const float* g, float* buf, float* v, float lr, float momentum, int32_t nesterov,
+                            float wd, float scale, float beta2, const float* coeffs, int32_t steps, float norm_scale,
+                            float eps, void* ws, size_t ws_bytes, void* stream) {
+  gdb_status st = check_ns(count, m, n, dtype, coeffs, steps);
+  if (st != GDB_OK) return st;
+  for (float f : {lr, momentum, wd, scale, norm_scale, eps, beta2})
+    if (!std::isfinite(f)) return fail(GDB_EINVAL, "non-finite hyperparameter");
+  if (!(norm_scale > 0.f) || eps < 0.f) return fail(GDB_EINVAL, "norm_scale must be positive and eps non-negative");
+  if (!(beta2 >= 0.f && beta2 < 1.f)) return fail(GDB_EINVAL, "beta2 must be in [0, 1)");
+  CHECK_PTR(p); CHECK_PTR(g); CHECK_PTR(buf); CHECK_PTR(v); CHECK_PTR(ws);
+  if (p_bf16 && (((uintptr_t)p_bf16) & 15)) return fail(GDB_EINVAL, "p_bf16 is not 16-byte aligned");
+  const NsWs w = ns_layout(count, m, n, dtype, true);
+  const size_t need = w.total + al256((size_t)count * m * 3 * 4);
+  if (ws_bytes < need) return fail(GDB_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  char* b = (char*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t mn = (size_t)m * n;
+  int np = 0;
+  void* X = b + w.x;
+  void* start = steps % 2 == 0 ? X : (void*)(b + w.xa);
+  float* stat = (float*)(b + w.total);
+  float* fs = stat + 2 * (size_t)count * m;
+  HIPCHK(muon_momentum(g, buf, (float*)(b + w.u), mn, count, momentum, nesterov ? 1 : 0, (float*)(b + w.npart), &np,
+                       s));
+  HIPCHK(norm_final((float*)(b + w.npart), np, count, norm_scale, eps, (float*)(b + w.inv), s));
+  HIPCHK(scale_cast(dtype, (float*)(b + w.u), (float*)(b + w.inv), start, mn, count, s));
+  HIPCHK(ns_iterate(dtype, count, m, n, coeffs, steps, X, b + w.xa, b + w.a, b + w.bm, (float*)(b + w.part), s));
+  HIPCHK(normuon_scale(dtype, X, count, m, n, v, beta2, stat, fs, s));
+  HIPCHK(normuon_apply(dtype, p, X, fs, (bf16*)p_bf16, (size_t)count * m, n, 1.0f - lr * wd, lr * scale, s));
   g_err.clear();
   return GDB_OK;
 }

@@ -159,7 +159,8 @@ __global__ __launch_bounds__(256) void ve_fwd_k(T* qkv, int ldq, int voff, const
 // One wave per token n; dv = the v columns of dqkv (the addition passes the
 // gradient to v unchanged):
 //   dgate_g = dv[n,g,:] . VE[id,g,:];  ds[n,g] = dgate_g * 3*sig(s)*(1 - sig(s));
-//   dVE[id,g,:] += gate_g * dv[n,g,:]  (fp32 atomics: ids repeat).
+//   dVE[id,g,:] += gate_g * dv[n,g,:]  (fp32 atomics: ids repeat; skipped when
+//   dve is null, the deterministic path sums the rows in a fixed order instead).
 // Lane l takes columns l, l+64, ... of each head, so one atomic instruction
 // covers 256 contiguous bytes (two cache lines) of the dVE row; dgate_g is a
 // butterfly over the wave.
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(256) void ve_bwd_k(const T* __restrict__ dqkv, int 
   const float gate_mine = 3.0f * sg_mine;
   const T* dv = dqkv + (size_t)n * ldq + voff;
   const T* erow = ve + (size_t)id * Hkv * D;
-  float* drow = dve + (size_t)id * Hkv * D;
+  float* drow = dve ? dve + (size_t)id * Hkv * D : nullptr;
   float dg_mine = 0.f;
   for (int h = 0; h < Hkv; ++h) {
     const float gate = __shfl(gate_mine, h, 64);
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(256) void ve_bwd_k(const T* __restrict__ dqkv, int 
     for (int c = h * D + l; c < (h + 1) * D; c += 64) {
       const float g = to_f(dv[c]);
       p += g * to_f(erow[c]);
-      unsafeAtomicAdd(drow + c, gate * g);
+      if (drow) unsafeAtomicAdd(drow + c, gate * g);  // kernel-argument test: uniform
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) p += __shfl_xor(p, o, 64);

@@ -164,7 +164,8 @@ hipError_t mix_bwd(int dt, const void* dy, const void* x, const void* x0, const 
 // v columns (offset voff) of qkv [N, ldq] += 3*sigmoid(xn[:, :nc] Wg^T) * VE[ids]; s_save [N, Hkv]
 hipError_t ve_fwd(int dt, void* qkv, int ldq, int voff, const void* xn, int C, const int32_t* ids, const void* ve,
                   const void* wg, int nc, int Hkv, int D, int V, float* s_save, int N, hipStream_t s);
-// ds [N, Hkv] (gradient of the gate logits) and dve (fp32 atomics) from the v columns of dqkv
+// ds [N, Hkv] (gradient of the gate logits) and, if dve is non-null, dve (fp32 atomics) from the v
+// columns of dqkv
 hipError_t ve_bwd(int dt, const void* dqkv, int ldq, int voff, const int32_t* ids, const void* ve,
                   const float* s_save, int Hkv, int D, int V, float* ds, float* dve, int N, hipStream_t s);
 // dxn[:, :nc] += ds Wg; dwg (+)= ds^T xn[:, :nc]
@@ -182,6 +183,18 @@ hipError_t backout_fwd(int dt, const void* x, const void* xb, const float* lam, 
 // dxb += -lam*dy (in place); dlam (+)= -sum(dy*xb)
 hipError_t backout_bwd(int dt, const void* dy, const void* xb, const float* lam, void* dxb, float* part, float* dlam,
                        int accumulate, int N, int C, hipStream_t s);
+
+// ------------------------------------------------------- fixed-order scatter
+// bytes of scratch token_order needs for N tokens
+size_t token_order_ws_bytes(int N);
+// stable sort of the token indices 0..N-1 by id (ids clamped into [0, V)):
+// *sorted_ids and *perm point into ws on return (sorted_ids[j] = id of token perm[j])
+hipError_t token_order(const int32_t* ids, int N, int V, void* ws, const int32_t** sorted_ids, const int32_t** perm,
+                       hipStream_t s);
+// out[v, c] (+)= sum over tokens n of id v, in sorted order, of g(n, c) * x[n*ldx + xoff + c] (c < width),
+// g = 3*sigmoid(gate_s[n*G + c/D]) if gate_s is non-null, else 1; every row v < V is written
+hipError_t rows_segsum(int dt, const int32_t* sorted_ids, const int32_t* perm, int N, const void* x, int ldx, int xoff,
+                       int width, const float* gate_s, int G, int D, float* out, int V, int accumulate, hipStream_t s);
 
 // ------------------------------------------------------------------ optimizer
 constexpr int OPT_PART = 1024;  // most workgroups (partials) of the reductions below
@@ -201,6 +214,15 @@ hipError_t splitk_axpby(int dt, const float* part, int splits, size_t n, float a
                         void* out, hipStream_t s);
 // p = p*decay - step*x (x dtype dt); plow (bf16 copy of p) if non-null
 hipError_t muon_apply(int dt, float* p, const void* x, bf16* plow, size_t n, float decay, float step, hipStream_t s);
+// NorMuon statistics of the NS output x (count items of [m, n], dtype dt): per row r of item i,
+// vmean = mean_j x^2, v = beta2*v + (1-beta2)*vmean (state), step = 1/sqrt(max(v, 1e-10)); then per
+// item fs[r] = step[r]*sqrt(sum vmean)/max(sqrt(sum vmean*step^2), 1e-10) (fixed-order sums).
+// stat: fp32 scratch [2][count*m]; fs [count*m] receives the row factors.
+hipError_t normuon_scale(int dt, const void* x, int count, int m, int n, float* v, float beta2, float* stat,
+                         float* fs, hipStream_t s);
+// p = p*decay - step*fs[row]*x (x dtype dt, rows of n elements); plow (bf16 copy of p) if non-null
+hipError_t normuon_apply(int dt, float* p, const void* x, const float* fs, bf16* plow, size_t rows, int n,
+                         float decay, float step, hipStream_t s);
 // one AdamW step (t counts steps, this one included)
 hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* plow, size_t n, float lr, float b1, float b2,
                  float eps, float wd, int t, hipStream_t s);

@@ -116,6 +116,73 @@ __global__ __launch_bounds__(OPT_NT) void muon_apply_k(float* __restrict__ p, co
   }
 }
 
+// NorMuon row statistics: one wavefront per row r of the stacked NS output x
+// ([rows][n]): vmean = mean of x^2 over the row, then the per-neuron second
+// moment v = beta2*v + (1 - beta2)*vmean and step = 1/sqrt(max(v, 1e-10)).
+template <typename T>
+__global__ __launch_bounds__(256) void normuon_rows_k(const T* __restrict__ x, size_t rows, int n,
+                                                      float* __restrict__ v, float beta2, float* __restrict__ vmean,
+                                                      float* __restrict__ step) {
+  constexpr int VN = V16<T>::n;
+  const size_t r = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (r >= rows) return;  // wave-uniform
+  const T* xr = x + r * n;
+  float acc = 0.f;
+  for (int c = l * VN; c < n; c += 64 * VN) {
+    float a[VN];
+    ld16(xr + c, a);
+#pragma unroll
+    for (int e = 0; e < VN; ++e) acc += a[e] * a[e];
+  }
+  acc = wave_sum(acc);
+  if (l == 0) {
+    const float vm = acc / (float)n;
+    const float vv = beta2 * v[r] + (1.0f - beta2) * vm;
+    v[r] = vv;
+    vmean[r] = vm;
+    step[r] = 1.0f / sqrtf(fmaxf(vv, 1e-10f));
+  }
+}
+
+// One workgroup per item: v_norm = sqrt(sum vmean), v_norm_new =
+// sqrt(sum vmean*step^2) over the item's m rows (fixed order), then the row
+// factors fs = step * v_norm / max(v_norm_new, 1e-10).
+__global__ __launch_bounds__(OPT_NT) void normuon_final_k(const float* __restrict__ vmean,
+                                                          const float* __restrict__ step, int m,
+                                                          float* __restrict__ fs) {
+  __shared__ float red[OPT_NT / 64];
+  const size_t o = (size_t)blockIdx.x * m;
+  float a = 0.f, b = 0.f;
+  for (int r = threadIdx.x; r < m; r += OPT_NT) {
+    const float vm = vmean[o + r], st = step[o + r];
+    a += vm;
+    b += vm * st * st;
+  }
+  a = block_sum<OPT_NT>(a, red);
+  b = block_sum<OPT_NT>(b, red);
+  const float ratio = sqrtf(a) / fmaxf(sqrtf(b), 1e-10f);
+  for (int r = threadIdx.x; r < m; r += OPT_NT) fs[o + r] = step[o + r] * ratio;
+}
+
+// p = p*decay - step*fs[row]*x, rows of n elements; optional bf16 copy of p
+template <typename T>
+__global__ __launch_bounds__(OPT_NT) void normuon_apply_k(float* __restrict__ p, const T* __restrict__ x,
+                                                          const float* __restrict__ fs, bf16* __restrict__ plow,
+                                                          size_t n4, int n, float decay, float step) {
+  for (size_t i = (size_t)blockIdx.x * OPT_NT + threadIdx.x; i < n4; i += (size_t)gridDim.x * OPT_NT) {
+    const float f = step * fs[(4 * i) / n];  // n is a multiple of 4: the 4 elements share a row
+    f32x4 pv = ((f32x4*)p)[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pv[e] = pv[e] * decay - f * to_f(x[4 * i + e]);
+    ((f32x4*)p)[i] = pv;
+    if (plow) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) plow[4 * i + e] = (bf16)pv[e];
+    }
+  }
+}
+
 // AdamW with bias correction: rc1 = 1/(1 - beta1^t), rc2 = 1/(1 - beta2^t)
 __global__ __launch_bounds__(OPT_NT) void adamw_k(float* __restrict__ p, const float* __restrict__ g,
                                                  float* __restrict__ m, float* __restrict__ v,
@@ -190,6 +257,34 @@ hipError_t muon_apply(int dt, float* p, const void* x, bf16* plow, size_t n, flo
   else
     hipLaunchKernelGGL(muon_apply_k<float>, dim3(grid_for(n / 4)), dim3(OPT_NT), 0, s, p, (const float*)x, plow,
                        n / 4, decay, step);
+  return hipGetLastError();
+}
+
+hipError_t normuon_scale(int dt, const void* x, int count, int m, int n, float* v, float beta2, float* stat, float* fs,
+                         hipStream_t s) {
+  const size_t rows = (size_t)count * m;
+  float* vmean = stat;
+  float* step = stat + rows;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (dt == BF16)
+    hipLaunchKernelGGL(normuon_rows_k<bf16>, grid, dim3(256), 0, s, (const bf16*)x, rows, n, v, beta2, vmean, step);
+  else
+    hipLaunchKernelGGL(normuon_rows_k<float>, grid, dim3(256), 0, s, (const float*)x, rows, n, v, beta2, vmean, step);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(normuon_final_k, dim3(count), dim3(OPT_NT), 0, s, vmean, step, m, fs);
+  return hipGetLastError();
+}
+
+hipError_t normuon_apply(int dt, float* p, const void* x, const float* fs, bf16* plow, size_t rows, int n, float decay,
+                         float step, hipStream_t s) {
+  const size_t n4 = rows * n / 4;
+  if (dt == BF16)
+    hipLaunchKernelGGL(normuon_apply_k<bf16>, dim3(grid_for(n4)), dim3(OPT_NT), 0, s, p, (const bf16*)x, fs, plow, n4,
+                       n, decay, step);
+  else
+    hipLaunchKernelGGL(normuon_apply_k<float>, dim3(grid_for(n4)), dim3(OPT_NT), 0, s, p, (const float*)x, fs, plow,
+                       n4, n, decay, step);
   return hipGetLastError();
 }
 

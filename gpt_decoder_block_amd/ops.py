@@ -37,9 +37,9 @@ def _stream(t: torch.Tensor) -> ctypes.c_void_p:
 
 def make_cfg(B: int, T: int, C: int, n_head: int, n_kv_head: int, head_dim: int, mlp_hidden: int,
              window: int, dtype: torch.dtype, eps: float = 1e-6, accumulate_wgrad: bool = False,
-             mlp_fp8: bool = False) -> L.BlockCfg:
+             mlp_fp8: bool = False, deterministic: bool = False) -> L.BlockCfg:
     return L.BlockCfg(B, T, C, n_head, n_kv_head, head_dim, mlp_hidden, window, dtype_code(dtype), int(mlp_fp8),
-                      int(accumulate_wgrad), eps)
+                      int(accumulate_wgrad), int(deterministic), eps)
 
 
 def block_sizes(cfg: L.BlockCfg) -> Tuple[int, int, int]:
@@ -60,10 +60,18 @@ def embed_fwd(ids: torch.Tensor, wte: torch.Tensor, x0: torch.Tensor) -> None:
     L.call("gdb_embed_fwd", ids.numel(), C, V, dtype_code(wte.dtype), _p(ids), _p(wte), _p(x0), _stream(wte))
 
 
-def embed_bwd(ids: torch.Tensor, dx0: torch.Tensor, dwte: torch.Tensor, accumulate: bool = False) -> None:
+def embed_bwd_ws_bytes(N: int, deterministic: bool) -> int:
+    n = ctypes.c_size_t()
+    L.call("gdb_embed_bwd_ws_bytes", N, int(deterministic), ctypes.byref(n))
+    return n.value
+
+
+def embed_bwd(ids: torch.Tensor, dx0: torch.Tensor, dwte: torch.Tensor, accumulate: bool = False,
+              ws: torch.Tensor = None) -> None:
+    """ws given: the deterministic (fixed-order) path, ws of embed_bwd_ws_bytes(N, True) bytes."""
     V, C = dwte.shape
     L.call("gdb_embed_bwd", ids.numel(), C, V, dtype_code(dx0.dtype), _p(ids), _p(dx0), _p(dwte),
-           int(accumulate), _stream(dwte))
+           int(accumulate), int(ws is not None), None if ws is None else _p(ws), _stream(dwte))
 
 
 def _weights(w: Sequence[torch.Tensor]) -> L.BlockWeights:
@@ -155,11 +163,11 @@ def lm_head_ce_sizes(N: int, C: int, V: int, dtype: torch.dtype) -> int:
 
 def lm_head_ce_fwd_bwd(x: torch.Tensor, w_lm: torch.Tensor, targets: torch.Tensor, loss: torch.Tensor,
                        dx: torch.Tensor, dw_lm: torch.Tensor, ws: torch.Tensor, eps: float = 1e-6,
-                       accumulate: bool = False) -> None:
+                       accumulate: bool = False, row_loss: torch.Tensor = None) -> None:
     N, C = x.shape[-2] if x.dim() == 2 else x.numel() // x.shape[-1], x.shape[-1]
     V = w_lm.shape[0]
     L.call("gdb_lm_head_ce_fwd_bwd", N, C, V, dtype_code(x.dtype), eps, _p(x), _p(w_lm), _p(targets), _p(loss),
-           _p(dx), _p(dw_lm), int(accumulate), _p(ws), _stream(x))
+           _opt(row_loss), _p(dx), _p(dw_lm), int(accumulate), _p(ws), _stream(x))
 
 
 # ------------------------------------------------------------ building blocks
@@ -307,3 +315,55 @@ def cross_entropy(z: torch.Tensor, targets: torch.Tensor, row_loss: torch.Tensor
     N, V = z.shape
     L.call("gdb_cross_entropy", N, V, dtype_code(z.dtype), _p(z), _p(targets), _p(row_loss), _p(loss),
            _stream(z))
+
+
+def mix_fwd(x: torch.Tensor, x0: torch.Tensor, lam: torch.Tensor, y: torch.Tensor) -> None:
+    N, C = x.shape
+    L.call("gdb_mix_fwd", N, C, dtype_code(x.dtype), _p(x), _p(x0), _p(lam), _p(y), _stream(x))
+
+
+def mix_bwd(dy: torch.Tensor, x: torch.Tensor, x0: torch.Tensor, lam: torch.Tensor, dx: torch.Tensor,
+            dx0: torch.Tensor, dlam: torch.Tensor, ws: torch.Tensor, accumulate_dx0: bool = False,
+            accumulate: bool = False) -> None:
+    N, C = dy.shape
+    L.call("gdb_mix_bwd", N, C, dtype_code(dy.dtype), _p(dy), _p(x), _p(x0), _p(lam), _p(dx), _p(dx0),
+           int(accumulate_dx0), _p(dlam), int(accumulate), _p(ws), _stream(dy))
+
+
+def ve_fwd(Hkv: int, D: int, qkv: torch.Tensor, voff: int, xn: torch.Tensor, ids: torch.Tensor, ve: torch.Tensor,
+           wg: torch.Tensor, s_save: torch.Tensor) -> None:
+    N, ldq = qkv.shape
+    L.call("gdb_ve_fwd", N, Hkv, D, dtype_code(qkv.dtype), _p(qkv), ldq, voff, _p(xn), xn.shape[1], _p(ids),
+           _p(ve), ve.shape[0], _p(wg), wg.shape[1], _p(s_save), _stream(qkv))
+
+
+def ve_bwd_ws_bytes(N: int, Hkv: int, nc: int, deterministic: bool) -> int:
+    n = ctypes.c_size_t()
+    L.call("gdb_ve_bwd_ws_bytes", N, Hkv, nc, int(deterministic), ctypes.byref(n))
+    return n.value
+
+
+def ve_bwd(Hkv: int, D: int, dqkv: torch.Tensor, voff: int, ids: torch.Tensor, ve: torch.Tensor,
+           s_save: torch.Tensor, xn: torch.Tensor, dxn: torch.Tensor, wg: torch.Tensor, dve: torch.Tensor,
+           dwg: torch.Tensor, ws: torch.Tensor, accumulate: bool = False, deterministic: bool = False) -> None:
+    N, ldq = dqkv.shape
+    L.call("gdb_ve_bwd", N, Hkv, D, dtype_code(dqkv.dtype), _p(dqkv), ldq, voff, _p(ids), _p(ve), ve.shape[0],
+           _p(s_save), _p(xn), _p(dxn), xn.shape[1], _p(wg), wg.shape[1], _p(dve), _p(dwg), int(accumulate),
+           int(deterministic), _p(ws), _stream(dqkv))
+
+
+def normuon_ws_bytes(m: int, n: int, dtype: torch.dtype, count: int = 1) -> int:
+    b = ctypes.c_size_t()
+    L.call("gdb_normuon_ws_bytes", count, m, n, dtype_code(dtype), ctypes.byref(b))
+    return b.value
+
+
+def normuon_step(p: torch.Tensor, g: torch.Tensor, buf: torch.Tensor, v: torch.Tensor, lr: float, momentum: float,
+                 nesterov: bool, wd: float, scale: float, beta2: float, coeffs, dtype: torch.dtype,
+                 ws: torch.Tensor, p_bf16: torch.Tensor = None, norm_scale: float = 1.0, eps: float = 1e-7) -> None:
+    """p, g, buf float32 [count, m, n] (or [m, n]); v float32 [count, m] (or [m]): the per-neuron state."""
+    count, m, n = _stack(p)
+    c, steps = _coeffs(coeffs)
+    L.call("gdb_normuon_step", count, m, n, dtype_code(dtype), _p(p), None if p_bf16 is None else _p(p_bf16), _p(g),
+           _p(buf), _p(v), lr, momentum, int(nesterov), wd, scale, beta2, c, steps, norm_scale, eps, _p(ws),
+           ws.numel(), _stream(p))

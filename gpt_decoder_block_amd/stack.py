@@ -30,7 +30,8 @@ class DecoderStack:
     def __init__(self, *, n_layer: int, B: int, T: int, C: int, n_head: int, n_kv_head: int, head_dim: int,
                  mlp_hidden: int, vocab: int, windows: Sequence[int], dtype: str, eps: float = 1e-6,
                  rope_base: float = 10000.0, device: str = "cuda:0", extras: bool = False,
-                 ve_gate_channels: int = 32, smear_channels: int = 24, mlp_fp8: bool = False):
+                 ve_gate_channels: int = 32, smear_channels: int = 24, mlp_fp8: bool = False,
+                 deterministic: bool = False):
         if len(windows) != n_layer:
             raise ValueError("one window per layer")
         if extras and n_layer < 2:
@@ -41,8 +42,9 @@ class DecoderStack:
         self.eps = eps
         self.extras = extras
         self.device = torch.device(device)
+        self.deterministic = deterministic
         self.cfgs = [ops.make_cfg(B, T, C, n_head, n_kv_head, head_dim, mlp_hidden, w, self.dt, eps,
-                                  mlp_fp8=mlp_fp8) for w in windows]
+                                  mlp_fp8=mlp_fp8, deterministic=deterministic) for w in windows]
         Q, KV = n_head * head_dim, n_kv_head * head_dim
         self.shapes = {"w_qkv": (Q + 2 * KV, C), "w_o": (C, Q), "w_fc": (mlp_hidden, C), "w_proj": (C, mlp_hidden)}
         dev, dt = self.device, self.dt
@@ -65,6 +67,9 @@ class DecoderStack:
         self.dlayers = [[torch.empty(self.shapes[k], dtype=f32, device=dev) for k in self.shapes]
                         for _ in range(n_layer)]
         self.ids = torch.zeros((self.N,), dtype=torch.int32, device=dev)
+        # deterministic: the embedding gradient adds its tokens in a fixed order (sort scratch)
+        self.ws_e = (torch.empty(max(ops.embed_bwd_ws_bytes(self.N, True), 16), dtype=torch.uint8, device=dev)
+                     if deterministic else None)
         self.tgt = torch.zeros((self.N,), dtype=torch.int32, device=dev)
         if extras:
             self.i_bo = n_layer // 2 - 1
@@ -148,7 +153,7 @@ class DecoderStack:
             for l in reversed(range(self.L)):
                 ops.block_bwd(self.cfgs[l], self.layers[l], self.rope, self.saved[l], self.dx, self.dx,
                               self.dlayers[l], self.ws_b)
-            ops.embed_bwd(self.ids, self.dx, self.dwte)
+            ops.embed_bwd(self.ids, self.dx, self.dwte, ws=self.ws_e)
             return
         for l in reversed(range(self.L)):
             if l == self.i_bo:
@@ -160,7 +165,7 @@ class DecoderStack:
                           self.ws_b, self.ex[l], self.dex[l])
         ops.smear_bwd(self.B, self.T, self.e, self.smear_gate, self.smear_lambda, self.s_smear, self.dx, self.dx0,
                       self.de, self.d_smear_lambda, self.d_smear_gate, self.ws_x)
-        ops.embed_bwd(self.ids, self.de, self.dwte)
+        ops.embed_bwd(self.ids, self.de, self.dwte, ws=self.ws_e)
 
     def step(self) -> torch.Tensor:
         self.forward()

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDB_ABI_VERSION 5
+#define GDB_ABI_VERSION 6
 
 /* Scratch bytes that gdb_smear_bwd and gdb_backout_bwd need in `ws`. */
 #define GDB_EXTRAS_WS_BYTES ((size_t)1 << 20)
@@ -85,6 +85,10 @@ typedef struct {
   int32_t dtype;              /* gdb_dtype */
   int32_t mlp_fp8;            /* the MLP's six products on OCP e4m3 codes (gdb_fp8_quantize) */
   int32_t accumulate_wgrad;   /* 0: dW = ..., 1: dW += ... */
+  int32_t deterministic;      /* 1: gdb_block_bwd's results are the same bits on every run (the value
+                                 embedding table's gradient sums its tokens in a fixed order instead of
+                                 with float atomics); every other reduction of the block is always in a
+                                 fixed order */
   float eps;
 } gdb_block_cfg;
 
@@ -125,8 +129,9 @@ typedef struct {
 } gdb_block_extras;
 
 /* fp32 gradients of the extras.  dlambdas [2], dve and dve_gate are
- * overwritten, or added to when cfg->accumulate_wgrad != 0 (dve is zeroed
- * first otherwise; its rows are summed with atomics, in no fixed order).
+ * overwritten, or added to when cfg->accumulate_wgrad != 0 (dve's rows are
+ * summed with float atomics in no fixed order, or, with cfg->deterministic,
+ * in token order after a stable sort of the ids).
  * dx0 [N, C] receives lambdas[1]*dx (the x0 share of the mixed stream's
  * gradient): overwritten, or added to when accumulate_dx0 != 0, so the
  * blocks of one backward pass can sum their shares in place. */
@@ -166,11 +171,15 @@ gdb_status gdb_embed_fwd(int32_t N, int32_t C, int32_t V, int32_t dtype,
                          const int32_t* ids, const void* wte, void* x0, void* stream);
 
 /* Embedding gradient: dwte[v, :] (+)= sum of dx0[n, :] over n with ids[n] == v.
- * dx0 [N, C] in `dtype`; dwte [V, C] float32, zeroed first unless
- * `accumulate`. Summation order is not fixed (float32 atomics). */
+ * dx0 [N, C] in `dtype`; dwte [V, C] float32, overwritten unless `accumulate`.
+ * deterministic == 0: float32 atomics, summation order not fixed (ws may be
+ * NULL).  deterministic != 0: the tokens are sorted by id (stable), then each
+ * row adds its tokens in token order: the same bits on every run; ws must
+ * hold gdb_embed_bwd_ws_bytes bytes. */
+gdb_status gdb_embed_bwd_ws_bytes(int32_t N, int32_t deterministic, size_t* ws_bytes);
 gdb_status gdb_embed_bwd(int32_t N, int32_t C, int32_t V, int32_t dtype,
                          const int32_t* ids, const void* dx0, float* dwte,
-                         int32_t accumulate, void* stream);
+                         int32_t accumulate, int32_t deterministic, void* ws, void* stream);
 
 /* Forward of one pre-norm decoder block on x_in [N, C]:
  *   xn1 = rms(x_in); [q k v] = xn1 W_qkv^T;  q^ = rope(rms_D(q)), k^ = rope(rms_D(k));
@@ -207,10 +216,12 @@ gdb_status gdb_lm_head_ce_sizes(int32_t N, int32_t C, int32_t V, int32_t dtype,
  *   dz = (softmax(z) - onehot(targets)) / N;  dxf = dz W_lm;  dW_lm (+)= dz^T xf;
  *   dx = rms backward of dxf.
  * x [N, C], w_lm [V, C], dx [N, C] in `dtype`; targets int32 [N] in [0, V);
- * loss: device float32 scalar (written); dw_lm [V, C] float32. */
+ * loss: device float32 scalar (written); row_loss: NULL, or device float32
+ * [N] that receives each token's loss logsumexp(z_n) - z_n[targets[n]];
+ * dw_lm [V, C] float32. */
 gdb_status gdb_lm_head_ce_fwd_bwd(int32_t N, int32_t C, int32_t V, int32_t dtype, float eps,
                                   const void* x, const void* w_lm, const int32_t* targets,
-                                  float* loss, void* dx, float* dw_lm, int32_t accumulate,
+                                  float* loss, float* row_loss, void* dx, float* dw_lm, int32_t accumulate,
                                   void* ws, void* stream);
 
 /* Smear, once after the embedding (section "1. Le modèle GPT", the smear
@@ -245,6 +256,47 @@ gdb_status gdb_backout_fwd(int32_t N, int32_t C, int32_t dtype, const void* x, c
 gdb_status gdb_backout_bwd(int32_t N, int32_t C, int32_t dtype, const void* dy, const void* x_bo,
                            const float* lam, void* dx_bo, float* dlam, int32_t accumulate,
                            void* ws, void* stream);
+
+/* Residual mixing of one block of the largest model (section "1. Le modèle
+ * GPT", the per-layer residual scaling snippet), as gdb_block_fwd applies it
+ * when gdb_block_extras.lambdas is set: y = lam[0]*x + lam[1]*x0 over
+ * [N, C] rows (dtype); lam fp32 [2] device.  y may alias x. */
+gdb_status gdb_mix_fwd(int32_t N, int32_t C, int32_t dtype, const void* x, const void* x0, const float* lam,
+                       void* y, void* stream);
+/* Its backward, given dy = the gradient w.r.t. y: dx = lam[0]*dy (dtype, may
+ * alias dy); dx0 (fp32 [N, C]) = lam[1]*dy, or += when accumulate_dx0;
+ * dlam (fp32 [2]) = or += (sum dy*x, sum dy*x0), summed in a fixed order.
+ * ws: GDB_EXTRAS_WS_BYTES of scratch. */
+gdb_status gdb_mix_bwd(int32_t N, int32_t C, int32_t dtype, const void* dy, const void* x, const void* x0,
+                       const float* lam, void* dx, float* dx0, int32_t accumulate_dx0, float* dlam,
+                       int32_t accumulate, void* ws, void* stream);
+
+/* Value embedding of one block (section "1. Le modèle GPT", the
+ * value-embedding snippet), as gdb_block_fwd applies it when
+ * gdb_block_extras.ve is set.  For each token n and K/V head g:
+ *   s[n, g] = xn[n, :nc] . wg[g, :]   (fp32, saved in s_save [N, Hkv]),
+ *   v[n, g, :] += 3*sigmoid(s[n, g]) * ve[ids[n], g*D : (g+1)*D],
+ * where v[n] is the row qkv + n*ldq + voff (dtype, updated in place), xn
+ * [N, ldx] the block's normalised input, ve [V, Hkv*D], wg [Hkv, nc] (dtype);
+ * ids int32 [N] (clamped into [0, V)).  1 <= nc <= min(64, ldx), Hkv <= 64,
+ * D in {64, 128}; ldq, voff, ldx multiples of 8. */
+gdb_status gdb_ve_fwd(int32_t N, int32_t Hkv, int32_t D, int32_t dtype, void* qkv, int32_t ldq, int32_t voff,
+                      const void* xn, int32_t ldx, const int32_t* ids, const void* ve, int32_t V, const void* wg,
+                      int32_t nc, float* s_save, void* stream);
+/* Its backward, with dv the rows dqkv + n*ldq + voff (the gradient w.r.t.
+ * the v that came out of the addition, which passes to the projection's v
+ * unchanged):
+ *   ds[n, g] = (dv[n, g, :] . ve[ids[n], g, :]) * 3*sig(s)*(1 - sig(s));
+ *   dve[ids[n], g, :] (+)= 3*sigmoid(s[n, g]) * dv[n, g, :];
+ *   dwg[g, c] (+)= sum_n ds[n, g] * xn[n, c];   dxn[n, :nc] += ds[n, :] @ wg
+ * (dxn [N, ldx] dtype, in place; dve, dwg fp32, overwritten unless
+ * `accumulate`; deterministic as in gdb_embed_bwd).  ws:
+ * gdb_ve_bwd_ws_bytes of scratch. */
+gdb_status gdb_ve_bwd_ws_bytes(int32_t N, int32_t Hkv, int32_t nc, int32_t deterministic, size_t* ws_bytes);
+gdb_status gdb_ve_bwd(int32_t N, int32_t Hkv, int32_t D, int32_t dtype, const void* dqkv, int32_t ldq, int32_t voff,
+                      const int32_t* ids, const void* ve, int32_t V, const float* s_save, const void* xn, void* dxn,
+                      int32_t ldx, const void* wg, int32_t nc, float* dve, float* dwg, int32_t accumulate,
+                      int32_t deterministic, void* ws, void* stream);
 
 /* ------------------------------------------------------------------------
  * Building blocks.  The calls above are compositions of these; they are
@@ -402,6 +454,25 @@ gdb_status gdb_muon_step(int32_t count, int32_t m, int32_t n, int32_t dtype, flo
                          float* buf, float lr, float momentum, int32_t nesterov, float wd, float scale,
                          const float* coeffs, int32_t steps, float norm_scale, float eps, void* ws, size_t ws_bytes,
                          void* stream);
+/* gdb_normuon_step: Muon with the NorMuon variance normalisation the
+ * pages print in part (section "2. L'optimiseur Muon", "Réduction de la
+ * variance NorMuon": the orthogonalised update is normalised per neuron to
+ * avoid a collapse of its scale).  Per item, with O = NS(U) from Muon's
+ * momentum step above and r the rows of O (one output neuron each):
+ *   v_mean[r] = mean_j O[r, j]^2;          v_norm = sqrt(sum_r v_mean[r]);
+ *   v[r] = beta2*v[r] + (1 - beta2)*v_mean[r]   (v: fp32 state [count][m]);
+ *   step[r] = 1/sqrt(max(v[r], 1e-10));
+ *   v_norm_new = sqrt(sum_r v_mean[r]*step[r]^2);
+ *   final[r] = step[r] * v_norm / max(v_norm_new, 1e-10);
+ *   p = p*(1 - lr*wd) - lr*scale*final[r]*O[r, :]
+ * (the update keeps O's Frobenius norm and equalises its rows' RMS as far
+ * as v tracks them).  Sums over rows are in a fixed order.  ws:
+ * gdb_normuon_ws_bytes bytes. */
+gdb_status gdb_normuon_ws_bytes(int32_t count, int32_t m, int32_t n, int32_t dtype, size_t* ws_bytes);
+gdb_status gdb_normuon_step(int32_t count, int32_t m, int32_t n, int32_t dtype, float* p, void* p_bf16,
+                            const float* g, float* buf, float* v, float lr, float momentum, int32_t nesterov,
+                            float wd, float scale, float beta2, const float* coeffs, int32_t steps,
+                            float norm_scale, float eps, void* ws, size_t ws_bytes, void* stream);
 /* gdb_adamw_step on n float32 parameters (n a multiple of 8), step t >= 1:
  *   p *= 1 - lr*wd;  m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*g^2;
  *   p -= lr * (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)

@@ -62,7 +62,7 @@ __all__ = [
     "rms_norm", "rms_norm_backward", "rope_tables", "rope", "rope_backward",
     "visible_mask", "attention", "attention_logsumexp", "attention_backward", "attention_decode",
     "cross_entropy", "e4m3_round",
-    "bf16_round", "fp8_quantize", "fp8_quant_dequant", "block_forward", "block_backward", "lm_head_ce",
+    "bf16_round", "fp8_quantize", "fp8_quant_dequant", "mm_nt", "relu2", "relu2_grad", "block_forward", "block_backward", "lm_head_ce",
     "embed_forward", "embed_backward", "smear_forward", "smear_backward",
     "mix_forward", "mix_backward", "ve_forward", "ve_backward", "backout_forward", "backout_backward",
     "stack_forward_backward", "FP8_E4M3_MAX",
@@ -269,11 +269,23 @@ def fp8_quant_dequant(x: np.ndarray, storage: Optional[str] = None) -> np.ndarra
     return q * s
 
 
-def _mm_nt(a, b, fp8, storage=None):
-    """a @ b^T, operands optionally through the fp8 quantiser."""
+def mm_nt(a, b, fp8: bool = False, storage: Optional[str] = None) -> np.ndarray:
+    """The bias-free Linear's product a @ b^T ([FR] section "3. Gestion de la
+    précision": F.linear(x, W) with W [out, in]); with fp8, both operands go
+    through the per-tensor e4m3 quantiser first (each with its own scale)."""
     if fp8:
         a, b = fp8_quant_dequant(a, storage), fp8_quant_dequant(b, storage)
     return a @ b.T
+
+
+def relu2(u: np.ndarray) -> np.ndarray:
+    """The MLP activation ([FR] section "1. Le modèle GPT": ReLU²): max(u, 0)^2."""
+    return np.maximum(u, 0.0) ** 2
+
+
+def relu2_grad(u: np.ndarray) -> np.ndarray:
+    """d relu2 / du = 2 max(u, 0)."""
+    return 2.0 * np.maximum(u, 0.0)
 
 
 # ------------------------------------------------------------------ extras
@@ -380,9 +392,9 @@ def block_forward(x: np.ndarray, p: Dict[str, np.ndarray], cfg, l: int,
     x_mid = x + o2 @ p["w_o"].T
     xn2, r2 = rms_norm(x_mid, eps)
     st = getattr(cfg, "dtype", None)
-    u = _mm_nt(xn2, p["w_fc"], fp8, st)
-    h = np.maximum(u, 0.0) ** 2
-    out = x_mid + _mm_nt(h, p["w_proj"], fp8, st)
+    u = mm_nt(xn2, p["w_fc"], fp8, st)
+    h = relu2(u)
+    out = x_mid + mm_nt(h, p["w_proj"], fp8, st)
     c.update(xn1=xn1, r1=r1, qn=qn, rq=rq, kn=kn, rk=rk, qh=qh, kh=kh, v=v, o=o2,
              P=P, x_mid=x_mid, xn2=xn2, r2=r2, u=u, h=h)
     return out, c
@@ -404,7 +416,7 @@ def block_backward(dout: np.ndarray, c: dict, p: Dict[str, np.ndarray], cfg, l: 
     # MLP: out = x_mid + h W_proj^T, h = relu(u)^2, u = xn2 W_fc^T
     dh = q8(dout) @ q8(p["w_proj"])
     g["w_proj"] = np.einsum("btc,btf->cf", q8(dout), q8(c["h"]))
-    du = dh * 2.0 * np.maximum(c["u"], 0.0)
+    du = dh * relu2_grad(c["u"])
     dxn2 = q8(du) @ q8(p["w_fc"])
     g["w_fc"] = np.einsum("btf,btc->fc", q8(du), q8(c["xn2"]))
     dx_mid = dout + rms_norm_backward(dxn2, c["xn2"], c["r2"])

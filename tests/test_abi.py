@@ -52,7 +52,7 @@ def test_abi_version(L):
 
 def _cfg(L, **kw):
     base = dict(B=2, T=64, C=256, n_head=2, n_kv_head=1, head_dim=128, mlp_hidden=1024, window=-1, dtype=1,
-                mlp_fp8=0, accumulate_wgrad=0, eps=1e-6)
+                mlp_fp8=0, accumulate_wgrad=0, deterministic=0, eps=1e-6)
     base.update(kw)
     return L.BlockCfg(**base)
 
@@ -84,11 +84,47 @@ def test_block_sizes_valid_and_monotone(L):
     (dict(mlp_fp8=1, mlp_hidden=1032), -1, "multiples of 16"),
     (dict(mlp_hidden=1020), -1, "multiples of 8"),
     (dict(eps=0.0), -1, "eps"),
+    (dict(deterministic=2), -1, "deterministic"),
 ])
 def test_block_cfg_validation(L, kw, code, msg):
     st, *_ = _sizes(L, _cfg(L, **kw))
     assert st == code
     assert msg in L.lib().gdb_last_error().decode()
+
+
+def test_deterministic_backward_reserves_sort_scratch(L):
+    # the fixed-order path sorts the token ids in the backward workspace
+    st, s0, f0, b0 = _sizes(L, _cfg(L))
+    st1, s1, f1, b1 = _sizes(L, _cfg(L, deterministic=1))
+    assert st == st1 == L.GDB_OK and (s1, f1) == (s0, f0) and b1 > b0
+    n = ctypes.c_size_t()
+    assert L.lib().gdb_embed_bwd_ws_bytes(4096, 1, ctypes.byref(n)) == L.GDB_OK and n.value >= 4 * 4096 * 4
+    assert L.lib().gdb_embed_bwd_ws_bytes(4096, 0, ctypes.byref(n)) == L.GDB_OK and n.value == 0
+
+
+def test_stage_entry_points_validate(L):
+    lib = L.lib()
+    buf = ctypes.create_string_buffer(4096)
+    al = (ctypes.addressof(buf) + 255) & ~255
+    # mixing: lam misaligned, bad sizes
+    assert lib.gdb_mix_fwd(4, 12, 1, al, al, al + 2, al, None) == L.GDB_EINVAL
+    assert lib.gdb_mix_fwd(4, 12, 1, al, al, al, al, None) == L.GDB_EINVAL
+    assert "multiple of 8" in lib.gdb_last_error().decode()
+    # value embedding: unsupported head size, gate width, voff past the row
+    assert lib.gdb_ve_fwd(4, 2, 96, 1, al, 512, 256, al, 128, al, al, 10, al, 32, al, None) == L.GDB_EUNSUPPORTED
+    assert lib.gdb_ve_fwd(4, 2, 128, 1, al, 512, 256, al, 128, al, al, 10, al, 65, al, None) == L.GDB_EINVAL
+    assert lib.gdb_ve_fwd(4, 2, 128, 1, al, 512, 384, al, 128, al, al, 10, al, 32, al, None) == L.GDB_EINVAL
+    n = ctypes.c_size_t()
+    assert lib.gdb_ve_bwd_ws_bytes(100, 2, 32, 1, ctypes.byref(n)) == L.GDB_OK and n.value > 0
+    # NorMuon: beta2 out of range, workspace too small
+    coeffs = (ctypes.c_float * 3)(1.5, -0.5, 0.0)
+    assert lib.gdb_normuon_step(1, 16, 16, 1, al, None, al, al, al, 0.1, 0.9, 1, 0.0, 1.0, 1.0, coeffs, 1, 1.0,
+                                1e-7, al, 1 << 30, None) == L.GDB_EINVAL
+    assert "beta2" in lib.gdb_last_error().decode()
+    assert lib.gdb_normuon_ws_bytes(2, 16, 24, 1, ctypes.byref(n)) == L.GDB_OK
+    need = n.value
+    assert lib.gdb_normuon_step(2, 16, 24, 1, al, None, al, al, al, 0.1, 0.9, 1, 0.0, 1.0, 0.95, coeffs, 1, 1.0,
+                                1e-7, al, need - 1, None) == L.GDB_EWORKSPACE
 
 
 def test_block_fwd_rejects_null_and_misaligned_pointers(L):
@@ -181,7 +217,11 @@ def test_gemm_and_attention_validation(L):
     assert st == L.GDB_EINVAL and "multiple of Hkv" in lib.gdb_last_error().decode()
     st = lib.gdb_attention_fwd(1, 64, 2, 1, 64, -1, 0, 1, al, 256, al, 128, al, None)
     assert st == L.GDB_EUNSUPPORTED
-    st = lib.gdb_lm_head_ce_fwd_bwd(8, 128, 100, 1, 1e-6, al, al, al, al, al, al, 0, al, None)
+    st = lib.gdb_lm_head_ce_fwd_bwd(8, 128, 100, 1, 1e-6, al, al, al, al, None, al, al, 0, al, None)
+    assert st == L.GDB_EINVAL and "multiples of 8" in lib.gdb_last_error().decode()
+    st = lib.gdb_lm_head_ce_fwd_bwd(8, 128, 128, 1, 1e-6, al, al, al, al, al + 2, al, al, 0, al, None)
+    assert st == L.GDB_EINVAL and "row_loss" in lib.gdb_last_error().decode()
+    st = lib.gdb_lm_head_ce_fwd_bwd(8, 128, 100, 1, 1e-6, al, al, al, al, None, al, al, 0, al, None)
     assert st == L.GDB_EINVAL and "multiples of 8" in lib.gdb_last_error().decode()
     st = lib.gdb_embed_fwd(8, 12, 100, 1, al, al, al, None)
     assert st == L.GDB_EINVAL

@@ -7,9 +7,10 @@ oracle checks sampled outputs it can compute on its own.
   upstream gradient is non-zero only on the sampled sequences (so dW is the
   sum of those sequences' contributions, which the oracle computes).
 * Head: every token except a few sampled ones has x = 0, so its normalised
-  row is 0, its logits are 0 and its loss is exactly ln V; the mean loss, the
-  sampled rows of dx (the oracle's one-row gradient times 1/N) and dW_lm
-  (only sampled rows contribute) are then known from the sampled rows alone.
+  row is 0, its logits are 0 and its loss is exactly ln V; each sampled row's
+  loss, the mean loss, the sampled rows of dx (the oracle's one-row gradient
+  times 1/N) and dW_lm (only sampled rows contribute) are then known from the
+  sampled rows alone.
 """
 import math
 
@@ -86,17 +87,25 @@ def test_lm_head_ce_d24_full_size():
     y = draw_ids(w)[:, 1:].reshape(-1)
     ws = torch.empty(ops.lm_head_ce_sizes(N, C, V, TDT[dt]), dtype=torch.uint8, device=DEV)
     loss = empty((1,), torch.float32)
+    row_loss = empty((N,), torch.float32)
     dx = empty((N, C), dt)
     dw = empty((V, C), torch.float32)
     ops.lm_head_ce_fwd_bwd(dev(x, dt), dev(w_lm, dt), torch.from_numpy(y.astype(np.int32)).to(DEV), loss, dx, dw,
-                           ws, eps=w.eps)
+                           ws, eps=w.eps, row_loss=row_loss)
     torch.cuda.synchronize()
-    l_rows, dx_rows, dw_rows, _ = O.lm_head_ce(x[rows].astype(np.float64), w_lm.astype(np.float64), y[rows], w.eps)
-    # the one-row oracle means over len(rows); the full step means over N, and
-    # every other row contributes exactly ln V to the sum and nothing to dW
+    l_rows, dx_rows, dw_rows, hc = O.lm_head_ce(x[rows].astype(np.float64), w_lm.astype(np.float64), y[rows], w.eps)
+    # each sampled row's own loss (the oracle's per-row losses), every other
+    # row exactly ln V; then the mean over N, which those rows fix
+    z = hc["z"]
+    row_ref = hc["lse"] - z[np.arange(len(rows)), y[rows]]
+    rl = host(row_loss)
+    e_rows = assert_close(rl[rows], row_ref, dt, "row losses (sampled rows)")
+    others = np.setdiff1d(np.arange(N), rows)
+    assert np.max(np.abs(rl[others] - math.log(V))) <= 1e-5 * math.log(V)
     n = len(rows)
     loss_ref = (l_rows * n + (N - n) * math.log(V)) / N
     assert abs(loss.item() - loss_ref) <= 2e-2 * abs(loss_ref)
     e_dx = assert_close(host(dx)[rows], dx_rows * n / N, dt, "dx (sampled rows)")
     e_dw = assert_close(dw, dw_rows * n / N, dt, "dw_lm")
+    print(f"full-size head row losses {e_rows:.3e}", flush=True)
     print(f"full-size head loss {loss.item():.6f} ref {loss_ref:.6f} dx {e_dx:.3e} dw {e_dw:.3e}", flush=True)

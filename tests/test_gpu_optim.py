@@ -157,3 +157,38 @@ def test_muon_step_stack(dt):
         upd_ref = (p[i].astype(np.float64) * (1 - lr * wd) - p_ref) / (lr * sc)
         u = gr[i].astype(np.float64) + mu * b_ref
         assert_close(upd, upd_ref, dt, f"update[{i}]", tol=ns_bar(dt, u, FIVE))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("m,n", [(384, 128), (96, 320)])
+def test_normuon_step_stack(dt, m, n):
+    # Muon's momentum and Newton-Schulz, then the per-neuron normalisation with
+    # a state v that differs across rows (so it matters), on a stack of 3
+    count = 3
+    g = np.random.default_rng(m + 3 * n)
+    p = g.standard_normal((count, m, n)).astype(np.float32) * 0.02
+    gr = g.standard_normal((count, m, n)).astype(np.float32) * np.linspace(0.2, 3.0, m, dtype=np.float32)[:, None]
+    buf = g.standard_normal((count, m, n)).astype(np.float32) * 0.5
+    v = g.uniform(0.05, 2.0, size=(count, m)).astype(np.float32) / n
+    pg, gg, bg, vg = (torch.from_numpy(a.copy()).to(DEV) for a in (p, gr, buf, v))
+    plow = torch.empty(count, m, n, dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(ops.normuon_ws_bytes(m, n, TDT[dt], count), dtype=torch.uint8, device=DEV)
+    lr, mu, wd, sc, beta2 = 0.02, 0.95, 0.1, 1.7, 0.95
+    print(f"normuon dt={dt} count={count} m={m} n={n}", flush=True)
+    ops.normuon_step(pg, gg, bg, vg, lr, mu, True, wd, sc, beta2, FIVE, TDT[dt], ws, p_bf16=plow, norm_scale=1.02)
+    torch.cuda.synchronize()
+    for i in range(count):
+        p_ref, b_ref, v_ref = O.normuon_step(p[i].astype(np.float64), gr[i].astype(np.float64),
+                                             buf[i].astype(np.float64), v[i].astype(np.float64), lr, mu, True, wd,
+                                             sc, beta2, FIVE, 1.02, 1e-7)
+        assert_close(bg[i], b_ref, "f32", f"buf[{i}]")
+        u = gr[i].astype(np.float64) + mu * b_ref
+        bar = ns_bar(dt, u, FIVE)
+        # the normalisation rescales each row of the orthogonalised update
+        # smoothly, so its error passes through at the size of the iteration's
+        ev = assert_close(vg[i], v_ref, dt, f"v[{i}]", tol=bar)
+        upd = (p[i].astype(np.float64) * (1 - lr * wd) - host(pg[i])) / (lr * sc)
+        upd_ref = (p[i].astype(np.float64) * (1 - lr * wd) - p_ref) / (lr * sc)
+        e = assert_close(upd, upd_ref, dt, f"update[{i}]", tol=bar)
+        print(f"  item {i} update err {e:.3e} v err {ev:.3e} bar {bar:.3e}", flush=True)
+    assert_close(plow, rounded(host(pg), "bf16"), "f32", "p_bf16", tol=0.0)
