@@ -143,6 +143,9 @@ SIGNATURES = {
     "gdb_attention_decode": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32,
                                        c_void_p, c_void_p, c_int32, c_int64, c_void_p, c_int32, c_void_p, c_int32,
                                        c_void_p, c_void_p, c_size_t, c_void_p]),
+    "gdb_attention_decode_noalloc": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                               c_int32, c_void_p, c_void_p, c_int32, c_int64, c_void_p, c_int32,
+                                               c_void_p, c_int32, c_void_p, c_void_p]),
 }
 
 

@@ -854,6 +854,34 @@ gdb_status gdb_attention_decode(int32_t B, int32_t H, int32_t Hkv, int32_t D, in
   return GDB_OK;
 }
 
+gdb_status gdb_attention_decode_noalloc(int32_t B, int32_t H, int32_t Hkv, int32_t D, int32_t window, int32_t dtype,
+                                        const void* q, int32_t ldq, const void* k, const void* v, int32_t ldk,
+                                        int64_t bstride, const int32_t* lens, int32_t max_len, void* o, int32_t ldo,
+                                        float* lse, void* stream) {
+  gdb_status st = check_decode(B, H, Hkv, D, max_len, window);
+  if (st != GDB_OK) return st;
+  if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
+  if (ldq < H * D || ldq % 8 || ldo < H * D || ldo % 8 || ldk < Hkv * D || ldk % 8)
+    return fail(GDB_EINVAL, "bad leading dimension");
+  if (B > 1 && (bstride < (int64_t)(max_len - 1) * ldk + Hkv * D || bstride % 8))
+    return fail(GDB_EINVAL, "bstride must be a multiple of 8 covering max_len rows");
+  CHECK_PTR(q); CHECK_PTR(k); CHECK_PTR(v); CHECK_PTR(lens); CHECK_PTR(o);
+  if (lse && (((uintptr_t)lse) & 15)) return fail(GDB_EINVAL, "lse is not 16-byte aligned");
+  const size_t need = decode_ws(B, H, Hkv, D, max_len, window);
+  if (need > decode_scratch_bytes())
+    return fail(GDB_EWORKSPACE, "this decode needs %zu bytes of split scratch, above the fixed %zu", need,
+                decode_scratch_bytes());
+  void* part = nullptr;
+  if (need) HIPCHK(decode_scratch(&part));
+  DecodeArgs a{};
+  a.B = B; a.H = H; a.Hkv = Hkv; a.D = D; a.window = window; a.max_len = max_len;
+  a.q = q; a.ldq = ldq; a.k = k; a.v = v; a.ldk = ldk; a.bstride = bstride; a.lens = lens;
+  a.o = o; a.ldo = ldo; a.lse = lse; a.part = (float*)part;
+  HIPCHK(attn_decode(dtype, a, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
 // ----------------------------------------------------------------- optimizer
 namespace {
 size_t al256(size_t b) { return (b + 255) / 256 * 256; }

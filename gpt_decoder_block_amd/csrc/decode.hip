@@ -19,11 +19,20 @@
 // their partial states; with one split the workgroup writes the output, else
 // it writes (o, m, l) to the workspace and a second kernel merges the splits.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
 
 namespace gdb {
+
+// Split-KV partials of the allocation-free decode entry point: a fixed
+// device array instead of a caller workspace.  decode_plan keeps
+// B*H*nsplit below 2048*(H/Hkv) <= 16384 whenever it splits, i.e. at most
+// 16384 * (128 + 4) * 4 bytes = 8.65 MB, so 16 MiB holds every plan.  Each
+// GPU the library runs on holds its own copy until the process ends.
+constexpr size_t DECODE_SCRATCH_BYTES = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[DECODE_SCRATCH_BYTES];
 
 namespace {
 
@@ -213,6 +222,31 @@ hipError_t decode_g(const DecodeArgs& a, int nsplit, float scale_log2, hipStream
 }
 
 }  // namespace
+
+size_t decode_scratch_bytes() { return DECODE_SCRATCH_BYTES; }
+
+// Device address of the current device's copy of `scratch`, looked up with
+// hipGetSymbolAddress on the first call made with that device current and
+// kept per device (the array's name is a host-side stand-in, never a device
+// address).
+hipError_t decode_scratch(void** out) {
+  constexpr int MAXDEV = 64;
+  static std::mutex mu;
+  static void* ptrs[MAXDEV] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAXDEV) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
+}
 
 bool decode_group_supported(int G) { return G == 1 || G == 2 || G == 3 || G == 4 || G == 6 || G == 8; }
 

@@ -146,6 +146,10 @@ bool decode_group_supported(int G);
 // split plan: keys per split and number of splits for the longest sequence
 void decode_plan(int B, int Hkv, int max_len, int window, int* chunk, int* nsplit);
 hipError_t attn_decode(int dt, const DecodeArgs& a, hipStream_t s);
+// fixed per-device scratch of the allocation-free decode: its size, and its
+// device address on the current device (looked up once per device)
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** out);
 
 // --------------------------------------------------------------------- extras
 // Kernels that reduce scalar gradients write one fp32 partial row per

@@ -262,6 +262,14 @@ def attention_decode(B: int, H: int, Hkv: int, D: int, window: int, q: torch.Ten
            bstride, _p(lens), max_len, _p(o), ldo, _opt(lse), _opt(ws), nbytes, _stream(q))
 
 
+def attention_decode_noalloc(B: int, H: int, Hkv: int, D: int, window: int, q: torch.Tensor, ldq: int,
+                             k: torch.Tensor, v: torch.Tensor, ldk: int, bstride: int, lens: torch.Tensor,
+                             max_len: int, o: torch.Tensor, ldo: int, lse=None) -> None:
+    """attention_decode with the library's fixed split scratch (no workspace argument)."""
+    L.call("gdb_attention_decode_noalloc", B, H, Hkv, D, window, dtype_code(q.dtype), _p(q), ldq, _p(k), _p(v), ldk,
+           bstride, _p(lens), max_len, _p(o), ldo, _opt(lse), _stream(q))
+
+
 def _coeffs(coeffs):
     flat = [float(x) for t in coeffs for x in t]
     return (ctypes.c_float * max(len(flat), 1))(*flat), len(flat) // 3

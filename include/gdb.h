@@ -417,6 +417,20 @@ gdb_status gdb_attention_decode(int32_t B, int32_t H, int32_t Hkv, int32_t D, in
                                 int64_t bstride, const int32_t* lens, int32_t max_len, void* o, int32_t ldo,
                                 float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* gdb_attention_decode without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, result and validation as
+ * gdb_attention_decode; the split-KV partials go to a fixed device array
+ * inside the library (16 MiB per GPU, held until the process ends; every
+ * split plan fits in it, and a larger need returns GDB_EWORKSPACE).  The
+ * call allocates nothing.  All calls on one GPU share that array: calls that
+ * overlap on one GPU (concurrent streams or threads) race and must not be
+ * issued. */
+gdb_status gdb_attention_decode_noalloc(int32_t B, int32_t H, int32_t Hkv, int32_t D, int32_t window, int32_t dtype,
+                                        const void* q, int32_t ldq, const void* k, const void* v, int32_t ldk,
+                                        int64_t bstride, const int32_t* lens, int32_t max_len, void* o,
+                                        int32_t ldo, float* lse, void* stream);
+
 /* Optimizer step after the backward (the Japanese and French articles,
  * section 2 on the Muon optimizer): AdamW for embeddings, lm_head and scalar
  * parameters; Muon for matrices, i.e. momentum orthogonalised by the Polar
