@@ -39,31 +39,159 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--counter-run", action="store_true",
-                    help="only launch the roofline kernel (MLP up-projection GEMM at the workload's shape) 3 times "
-                         "and a 1 GiB device copy 3 times, for hardware-counter collection")
+                    help="only launch each hot kernel class 3 times at the workload's shapes, then a 1 GiB device "
+                         "copy 3 times, for hardware-counter collection (rocprofv3 --pmc)")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                    help="summarise the rocprofv3 counter CSV files under these directories (no GPU needed)")
     return ap.parse_args()
 
 
 def counter_run(w):
-    """Launch sequence for rocprofv3 --pmc passes: the roofline kernel, then a
-    plain copy of known size (its FETCH_SIZE / WRITE_SIZE readings calibrate
-    the counters to bytes)."""
+    """Launch sequence for rocprofv3 --pmc passes: each hot kernel class of
+    the step at the workload's shapes, 3 launches each, then a plain copy of
+    known size (its FETCH_SIZE / WRITE_SIZE readings calibrate the counters
+    to bytes).  Prints the launch list as JSON."""
     import torch
     from gpt_decoder_block_amd import ops
     dev, dt = "cuda:0", torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    N, C, F = w.B * w.T, w.C, w.mlp_hidden
+    N, C, F, V = w.B * w.T, w.C, w.mlp_hidden, w.vocab
+    H, Hkv, D = w.n_head, w.n_kv_head, w.head_dim
+    W3 = (H + 2 * Hkv) * D
     g = torch.Generator(device=dev).manual_seed(1)
-    A = torch.randn(N, C, generator=g, device=dev).to(dt)
-    B = (torch.randn(F, C, generator=g, device=dev) * 0.02).to(dt)
+    rnd = lambda *shape, sc=1.0: (torch.randn(*shape, generator=g, device=dev) * sc).to(dt)
+    launched = []
+    # GEMMs: MLP up-projection with relu^2 (stores h), and the MLP down-projection's weight gradient
+    A, B = rnd(N, C), rnd(F, C, sc=0.02)
     Hh = torch.empty(N, F, dtype=dt, device=dev)
     for _ in range(3):
         ops.gemm(N, F, C, A, True, C, B, True, C, ops.EPI_SQR, Hh, F)
+    launched.append({"kernel": "gemm mlp_up relu2", "shape": [N, F, C], "flops": 2.0 * N * F * C})
+    dW = torch.empty(C, F, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(ops.gemm_ws_bytes(dt, C, F, N, ops.EPI_F32), 16), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        ops.gemm(C, F, N, A, False, C, Hh, False, F, ops.EPI_F32, dW, F, ws=ws)
+    launched.append({"kernel": "gemm wgrad mlp_down", "shape": [C, F, N], "flops": 2.0 * N * F * C})
+    del Hh, dW, ws, B
+    # attention forward / backward at the workload's windows
+    from gpt_decoder_block_amd.workmodel import attn_pairs
+    qkv = rnd(N, W3)
+    qk = qkv[:, :(H + Hkv) * D].float().view(N, H + Hkv, D)
+    qkv[:, :(H + Hkv) * D] = (qk * torch.rsqrt(qk.pow(2).mean(-1, keepdim=True))).view(N, -1).to(dt)
+    del qk
+    o, do = torch.empty(N, H * D, dtype=dt, device=dev), rnd(N, H * D)
+    lse, delta = (torch.empty(w.B, H, w.T, dtype=torch.float32, device=dev) for _ in range(2))
+    dqkv = torch.empty(N, W3, dtype=dt, device=dev)
+    for win in sorted(set(w.windows)):
+        pairs = attn_pairs(w.T, win) * w.B * H
+        for _ in range(3):
+            ops.attention_fwd(w.B, w.T, H, Hkv, D, win, qkv, W3, o, H * D, lse, qk_normed=True)
+        for _ in range(3):
+            ops.attention_bwd(w.B, w.T, H, Hkv, D, win, qkv, W3, o, H * D, lse, do, H * D, dqkv, W3, delta)
+        launched.append({"kernel": f"attention window {win}", "pairs": pairs, "fwd_flops": 4.0 * D * pairs,
+                         "bwd_flops": 8.0 * D * pairs})
+    del qkv, o, do, dqkv
+    # bandwidth kernels: RMSNorm forward / backward, cross-entropy over the vocabulary
+    x, xn = rnd(N, C), torch.empty(N, C, dtype=dt, device=dev)
+    r = torch.empty(N, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        ops.rmsnorm_fwd(x, xn, r, w.eps)
+    dres, dx = rnd(N, C), torch.empty(N, C, dtype=dt, device=dev)
+    for _ in range(3):
+        ops.rmsnorm_bwd(x, xn, r, dres, dx)
+    launched.append({"kernel": "rmsnorm", "fwd_bytes": 2.0 * N * C * s_el(dt) + 4 * N,
+                     "bwd_bytes": 4.0 * N * C * s_el(dt) + 4 * N})
+    del x, xn, dres, dx
+    z = rnd(N, V)
+    tg = torch.randint(0, V, (N,), device=dev, dtype=torch.int32)
+    rl, ls = torch.empty(N, dtype=torch.float32, device=dev), torch.empty(1, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        ops.cross_entropy(z, tg, rl, ls)
+    launched.append({"kernel": "cross entropy", "bytes": N * V * 2.0 * s_el(dt) + 8 * N})
+    del z
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)   # 1 GiB
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"counter_run": True, "gemm_shape": [N, F, C], "copy_bytes": src.numel() * 4}))
+    launched.append({"kernel": "copy", "bytes_each_way": src.numel() * 4})
+    print(json.dumps({"counter_run": True, "workload": w.name, "launched": launched}))
+
+
+def _short(name: str) -> str:
+    """Readable kernel symbol: demangled (c++filt, when the tracer kept the
+    mangled name), without namespaces' anonymous parts and the argument list."""
+    if name.startswith("_Z"):
+        import subprocess
+        try:
+            # GNU c++filt does not know the DF16b code of __bf16; spell it as a vendor type
+            dm = name.replace("DF16b", "u6__bf16")
+            name = subprocess.run(["c++filt", dm], capture_output=True, text=True, timeout=10).stdout.strip() or name
+        except (OSError, subprocess.SubprocessError):
+            pass
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def counter_summary(dirs):
+    """Per-kernel averages of every counter found in the rocprofv3 CSV files
+    under `dirs` (one directory per --pmc pass), plus the derived figures:
+    MFMA busy (% of the SIMDs' cycles), VALU busy, the effective clock
+    (GUI-active cycles of the busiest XCD / duration), HBM bytes from
+    FETCH_SIZE / WRITE_SIZE calibrated on the 1 GiB copy.  Markdown on stdout."""
+    import csv
+    import glob
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(list))   # kernel -> counter -> per-dispatch values
+    durs = defaultdict(dict)                         # kernel -> dispatch -> ns
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            per = defaultdict(lambda: defaultdict(float))
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    k = _short(row["Kernel_Name"])
+                    key = (k, f, row["Dispatch_Id"])
+                    per[key][row["Counter_Name"]] += float(row["Counter_Value"])
+                    if row.get("End_Timestamp") and row.get("Start_Timestamp"):
+                        durs[k][(f, row["Dispatch_Id"])] = float(row["End_Timestamp"]) - float(row["Start_Timestamp"])
+            for (k, _, _), cs in per.items():
+                for c, v in cs.items():
+                    vals[k][c].append(v)
+    avg = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in vals.items()}
+    copy = next((k for k in avg if "copyBuffer" in k), None)
+    fmt = lambda v, p=1: "" if v is None else f"{v:.{p}f}"
+    gib = float(1 << 30)
+    rf = avg[copy]["FETCH_SIZE"] * 1024 / gib if copy and "FETCH_SIZE" in avg[copy] else None
+    wf = avg[copy]["WRITE_SIZE"] * 1024 / gib if copy and "WRITE_SIZE" in avg[copy] else None
+    cols = ["kernel", "dispatches", "avg us", "MfmaUtil %", "VALUBusy %", "clock MHz", "VALU/MFMA", "LDS/MFMA",
+            "LDS wait %", "LDS conflict %", "HBM read MB", "HBM write MB", "HBM GB/s"]
+    print("| " + " | ".join(cols) + " |")
+    print("|" + "---|" * len(cols))
+    for k in sorted(avg, key=lambda k: -sum(durs[k].values()) / max(1, len(durs[k]))):
+        a = avg[k]
+        n = max(len(v) for v in vals[k].values())
+        us = sum(durs[k].values()) / max(1, len(durs[k])) / 1e3
+        clk = a["GRBM_GUI_ACTIVE"] / 8 / (us * 1e-6) / 1e6 if "GRBM_GUI_ACTIVE" in a and us > 0 else None
+        ratio = lambda x, y: (a[x] / a[y]) if x in a and y in a and a[y] > 0 else None
+        rd = a["FETCH_SIZE"] * 1024 / rf / 1e6 if rf and "FETCH_SIZE" in a else None
+        wr = a["WRITE_SIZE"] * 1024 / wf / 1e6 if wf and "WRITE_SIZE" in a else None
+        bw = ((rd or 0) + (wr or 0)) * 1e6 / (us * 1e-6) / 1e9 if (rd or wr) and us > 0 else None
+        # share of the waves' cycles spent waiting on LDS; bank-conflict cycles per LDS-active cycle
+        lw = ratio("SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES")
+        lc = ratio("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE")
+        print(f"| `{k[:90]}` | {n} | {us:.1f} | {fmt(a.get('MfmaUtil'))} | {fmt(a.get('VALUBusy'))} | {fmt(clk, 0)} | "
+              f"{fmt(ratio('SQ_INSTS_VALU', 'SQ_INSTS_MFMA'), 2)} | {fmt(ratio('SQ_INSTS_LDS', 'SQ_INSTS_MFMA'), 2)} | "
+              f"{fmt(None if lw is None else 100 * lw)} | {fmt(None if lc is None else 100 * lc)} | "
+              f"{fmt(rd)} | {fmt(wr)} | {fmt(bw, 0)} |")
+    print(f"\ncalibration on the 1 GiB copy: read factor {fmt(rf, 4) if rf else 'n/a'}, write factor "
+          f"{fmt(wf, 4) if wf else 'n/a'} (counter KiB x 1024 / bytes moved)")
 
 
 def s_el(dt) -> int:
@@ -328,6 +456,9 @@ def env_info(torch):
 
 def main():
     args = parse()
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
                                    "(the multi-GPU data-parallel design is described, not built)"}))
