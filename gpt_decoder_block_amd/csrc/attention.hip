@@ -21,12 +21,12 @@
 //     row log-sum-exp (fp32).
 //   backward: delta_i = dO_i . O_i; then two deterministic kernels that each
 //     recompute P from the saved log-sum-exp:
-//       dK/dV: a workgroup owns 128 keys of one (b, kv head) and loops over
-//         the query heads of its group and the visible 64-row query tiles,
-//         accumulating dV^T += dO^T P and dK^T += Q^T dS in registers
-//         (the GQA head reduction happens in registers, no atomics);
-//       dQ: a workgroup owns 128 query rows and loops over the visible key
-//         tiles, dQ^T += K^T dS^T.
+//       dK/dV: a workgroup of 4 waves owns 128 keys of one (b, kv head) and
+//         loops over the query heads of its group and the visible 64-row
+//         query tiles, accumulating dV^T += dO^T P and dK^T += Q^T dS in
+//         registers (the GQA head reduction happens in registers, no atomics);
+//       dQ: a workgroup of 8 waves owns 256 query rows and loops over the
+//         visible key tiles, dQ^T += K^T dS^T.
 // fp32 path: one thread per query (or key) row; slow, exact reference-order
 // kernels for the fp32 mode.
 #include "common.h"
@@ -40,9 +40,10 @@ namespace {
 
 constexpr int HD = 128;  // head_dim of the MFMA path
 // Two waves on every SIMD, so that one wave's softmax overlaps the other's
-// MFMAs: the forward runs two workgroups of 4 waves per CU (two K/V stages,
-// 64 KiB of LDS each; the workgroups synchronise independently), dQ and
-// dK/dV one workgroup of 8 waves (measured faster for them).
+// MFMAs: the forward and dK/dV run two workgroups of 4 waves per CU (the
+// workgroups synchronise independently, so the two waves of a SIMD are not
+// held in step by a shared barrier), dQ one workgroup of 8 waves (measured
+// faster for it).
 #ifndef ATTN_NW
 #define ATTN_NW 4
 #define ATTN_IB 1
@@ -57,7 +58,10 @@ constexpr int HD = 128;  // head_dim of the MFMA path
 #define ATTN_DQ_NS 3
 #endif
 #ifndef ATTN_DKV_NW
-#define ATTN_DKV_NW 8
+#define ATTN_DKV_NW 4
+#endif
+#ifndef ATTN_DKV_NS
+#define ATTN_DKV_NS 1
 #endif
 constexpr int ATTN_FQ = 32 * ATTN_IB * ATTN_NW;  // query rows per forward workgroup
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -445,27 +449,32 @@ __device__ __forceinline__ void qknorm_rope_bwd_row(const f32x16 (&acc)[4], floa
 }
 
 // ------------------------------------------------------ backward: dK, dV
-// Workgroup: 32*NW keys of one (b, kv head), 32 per wave (lane = key); with
-// NW = 8 two waves share each SIMD, so one wave's exp/convert work overlaps
-// the other's MFMAs.  The workgroup's V rows sit in LDS for the whole kernel
-// (the wave's K rows stay in registers).  Loops over the query heads of the
-// group and the visible 64-row query tiles; Q, dO (row-major) and the tile's
-// log-sum-exp and delta stream through 2 LDS stages, the next tile's loads
-// in flight during the current tile.  Each tile is taken as two 32-query
-// halves, so only one half's S and dP are live at a time: dV^T += dO^T P and
-// dK^T += Q^T dS accumulate in registers, with the transposed operands read
-// by the LDS transpose load.  A wave has 256 registers (two per SIMD); the
-// accumulators take 128, so KX of its eight K fragments wait in LDS (KX = 3
-// fills the 160 KiB beside V and the two Q/dO stages) rather than in
-// scratch, whose reloads would also wait for the next tile's copies
-// (vector-memory counts retire in order).
-template <int NW, int KX = 3>
-__global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_bf16_k(AttnArgs a, float scale_log2, float scale) {
+// Workgroup: 32*NW keys of one (b, kv head), 32 per wave (lane = key).  Two
+// 4-wave workgroups share a CU (NW = 4, 78 KiB of LDS each), so the two
+// waves of a SIMD belong to different workgroups and one's exp/convert work
+// overlaps the other's MFMAs without a common barrier.  The workgroup's V
+// rows sit in LDS for the whole kernel (the wave's K rows stay in
+// registers).  Loops over the query heads of the group and the visible
+// 64-row query tiles; Q, dO (row-major) and the tile's log-sum-exp and delta
+// go through NS LDS stages (NS = 1: the next tile is copied once every wave
+// has read this one, the other workgroup computing meanwhile; NS = 2: it is
+// in flight during this tile).  Each tile is taken as two 32-query halves:
+// S, then P (kept in fp32 in place of S) into dV^T += dO^T P, then dP and
+// dS into dK^T += Q^T dS, so at most S and dP of one half are live; the
+// transposed operands come from the LDS transpose load.  A wave has 256
+// registers; the accumulators take 128, so KX of its eight K fragments wait
+// in LDS rather than in scratch, whose reloads would also wait for copies
+// in flight (vector-memory counts retire in order): at NW = 4, NS = 1,
+// KX = 3 the kernel needs 252 registers and no scratch.
+template <int NW, int KX = 3, int NS = 2>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void attn_bwd_dkv_bf16_k(AttnArgs a, float scale_log2,
+                                                                               float scale) {
+  static_assert(NS == 1 || NS == 2, "one or two Q/dO stages");
   constexpr int FK = 32 * NW;
   __shared__ __attribute__((aligned(16))) bf16 Vs[FK * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Qs[2][64 * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Ds[2][64 * HD];
-  __shared__ __attribute__((aligned(16))) float Ls[2][NW][64];  // [stage][wave: lse (even), delta (odd)][row]
+  __shared__ __attribute__((aligned(16))) bf16 Qs[NS][64 * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Ds[NS][64 * HD];
+  __shared__ __attribute__((aligned(16))) float Ls[NS][NW][64];  // [stage][wave: lse (even), delta (odd)][row]
   // the last KX of the wave's eight K fragments, parked in LDS (private to
   // the wave) to free registers
   __shared__ __attribute__((aligned(16))) bf16x8 Kx[NW][KX > 0 ? KX : 1][64];
@@ -515,10 +524,12 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_bf16_k(AttnArgs a, float
   __syncthreads();
 
   for (int it = 0; it < total; ++it) {
-    const int st = it & 1;
+    const int st = NS == 2 ? it & 1 : 0;
     const int i0 = q_lo + (it % nqt) * 64;
-    // the other stage was last read in iteration it-1, which every wave has left
-    if (it + 1 < total) issue(it + 1, st ^ 1);
+    // two stages: the other stage was last read in iteration it-1, which
+    // every wave has left; one stage: the next tile is copied after this one
+    // has been read (the other workgroup on the CU computes meanwhile)
+    if (NS == 2 && it + 1 < total) issue(it + 1, st ^ 1);
     // wave-uniform visibility of this query tile for the wave's 32 keys
     const int iq_hi = min(i0 + 63, T - 1);
     const bool any = wk0 < T && i0 + 63 >= wk0 && (W < 0 || i0 - wk_hi <= W);
@@ -526,47 +537,56 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_bf16_k(AttnArgs a, float
       const bool full = i0 >= wk_hi && iq_hi < T && (W < 0 || iq_hi - wk0 <= W) && i0 + 63 < T;
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
-        // S[i][j] and dP[i][j] of query rows 32ib..32ib+31: lane = key j, registers = queries
-        f32x16 sv = f32x16{}, dpv = f32x16{};
+        // query rows 32ib..32ib+31: lane = key j, registers = queries.  S
+        // first; P (kept in fp32 in place of S) feeds dV before dP is
+        // computed, so P's bf16 copy and dP are never live together
+        f32x16 sv = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
+        for (int kk = 0; kk < 8; ++kk)
           sv = mfma32(row_frag(Qs[st], ib, kk, lr, lh), kk < 8 - KX ? kf[kk < 8 - KX ? kk : 0] : Kx[w][kk >= 8 - KX ? kk - (8 - KX) : 0][lane], sv);
-          dpv = mfma32(row_frag(Ds[st], ib, kk, lr, lh), row_frag(Vs, w, kk, lr, lh), dpv);
-        }
         if (!full) {
           f32x16 sm[1] = {sv};
           mask_tile<false>(sm, kj, i0 + ib * 32, lh, T, W);
           sv = sm[0];
         }
-        // P and dS straight into bf16 operand registers (slot order of tr_frag)
-        bf16x8 pf[2], sf[2];
+        // P straight into bf16 operand registers (slot order of tr_frag)
+        bf16x8 pf[2];
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+        for (int gq = 0; gq < 4; ++gq) {
+          const f32x4 L4 = *(const f32x4*)(&Ls[st][0][ib * 32 + 8 * gq + 4 * lh]);
 #pragma unroll
-          for (int hq = 0; hq < 2; ++hq) {
-            const int gq = 2 * k2 + hq;
-            const int il = ib * 32 + 8 * gq + 4 * lh;
-            const f32x4 L4 = *(const f32x4*)(&Ls[st][0][il]);
-            const f32x4 D4 = *(const f32x4*)(&Ls[st][1][il]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int v = 4 * gq + r;
-              const float p = __builtin_amdgcn_exp2f(fmaf(sv[v], scale_log2, -L4[r] * 1.4426950408889634f));
-              pf[k2][4 * hq + r] = (bf16)p;
-              sf[k2][4 * hq + r] = (bf16)(p * (dpv[v] - D4[r]));
-            }
+          for (int r = 0; r < 4; ++r) {
+            const int v = 4 * gq + r;
+            sv[v] = __builtin_amdgcn_exp2f(fmaf(sv[v], scale_log2, -L4[r] * 1.4426950408889634f));
+            pf[gq >> 1][4 * (gq & 1) + r] = (bf16)sv[v];
           }
         }
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const int ks = 2 * ib + k2;
+        for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            dv[db] = mfma32(tr_frag(Ds[st], db, ks, lane), pf[k2], dv[db]);
-            dk[db] = mfma32(tr_frag(Qs[st], db, ks, lane), sf[k2], dk[db]);
+          for (int db = 0; db < 4; ++db) dv[db] = mfma32(tr_frag(Ds[st], db, 2 * ib + k2, lane), pf[k2], dv[db]);
+        f32x16 dpv = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) dpv = mfma32(row_frag(Ds[st], ib, kk, lr, lh), row_frag(Vs, w, kk, lr, lh), dpv);
+        bf16x8 sf[2];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const f32x4 D4 = *(const f32x4*)(&Ls[st][1][ib * 32 + 8 * gq + 4 * lh]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int v = 4 * gq + r;
+            sf[gq >> 1][4 * (gq & 1) + r] = (bf16)(sv[v] * (dpv[v] - D4[r]));
           }
         }
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int db = 0; db < 4; ++db) dk[db] = mfma32(tr_frag(Qs[st], db, 2 * ib + k2, lane), sf[k2], dk[db]);
       }
+    }
+    if (NS == 1) {
+      __syncthreads();  // every wave has read the stage
+      if (it + 1 < total) issue(it + 1, 0);
     }
     WAIT_VM(0);  // tile it+1 has landed
     __syncthreads();
@@ -598,7 +618,8 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_bf16_k(AttnArgs a, float
 // and V tiles of 64 keys stream through NS LDS stages, NS - 1 tiles ahead;
 // dQ^T += K^T dS^T with K^T read by the LDS transpose load.
 template <int NW, int NS>
-__global__ __launch_bounds__(64 * NW) void attn_bwd_dq_bf16_k(AttnArgs a, float scale_log2, float scale) {
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void attn_bwd_dq_bf16_k(AttnArgs a, float scale_log2,
+                                                                              float scale) {
   static_assert(NS == 2 || NS == 3, "two or three K/V stages");
   constexpr int FQ = 32 * NW;
   __shared__ __attribute__((aligned(16))) bf16 Ks[NS][64 * HD];
@@ -843,7 +864,7 @@ hipError_t attn_bwd(int dt, const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (dt == BF16) {
-    hipLaunchKernelGGL(attn_bwd_dkv_bf16_k<ATTN_DKV_NW>, dim3(a.B * a.Hkv, (a.T + 32 * ATTN_DKV_NW - 1) / (32 * ATTN_DKV_NW)),
+    hipLaunchKernelGGL((attn_bwd_dkv_bf16_k<ATTN_DKV_NW, 3, ATTN_DKV_NS>), dim3(a.B * a.Hkv, (a.T + 32 * ATTN_DKV_NW - 1) / (32 * ATTN_DKV_NW)),
                        dim3(64 * ATTN_DKV_NW), 0, s, a, scale * 1.4426950408889634f, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
