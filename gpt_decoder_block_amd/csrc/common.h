@@ -45,6 +45,31 @@ __device__ __forceinline__ void st16(bf16* p, const float* o) {
   *(bf16x8*)p = v;
 }
 
+// Non-temporal variants (streamed data read or written once: no reuse expected
+// from the caches, which lets the copy engines stream closer to the HBM limit)
+__device__ __forceinline__ void ld16_nt(const float* p, float* o) {
+  const f32x4 v = __builtin_nontemporal_load((const f32x4*)p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = v[i];
+}
+__device__ __forceinline__ void ld16_nt(const bf16* p, float* o) {
+  const bf16x8 v = __builtin_nontemporal_load((const bf16x8*)p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (float)v[i];
+}
+__device__ __forceinline__ void st16_nt(float* p, const float* o) {
+  f32x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = o[i];
+  __builtin_nontemporal_store(v, (f32x4*)p);
+}
+__device__ __forceinline__ void st16_nt(bf16* p, const float* o) {
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (bf16)o[i];
+  __builtin_nontemporal_store(v, (bf16x8*)p);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -73,6 +73,15 @@ hipError_t transpose_bf16(const void* in, int R, int Cc, void* out, hipStream_t 
 // One wavefront per row; up to MAXV 16-byte vectors per lane stay in registers
 // (C <= 64*MAXV*VN), longer rows are streamed twice.
 constexpr int RMS_MAXV = 4;
+// The norms stream their [N, C] operands once per call, so their register-
+// resident rows are read and written with non-temporal accesses: measured on
+// the d24 shapes, from a cold cache the forward runs 59 -> 38 us and the
+// backward 115 -> 67 us (a 16-byte-vector copy reaches 6.2 TB/s this way
+// against 4.7 TB/s without).
+template <typename T>
+__device__ __forceinline__ void rld16(const T* p, float* o) { ld16_nt(p, o); }
+template <typename T>
+__device__ __forceinline__ void rst16(T* p, const float* o) { st16_nt(p, o); }
 
 template <typename T>
 __device__ __forceinline__ void rmsnorm_row(const T* __restrict__ x, T* __restrict__ xn, float* __restrict__ r,
@@ -88,7 +97,7 @@ __device__ __forceinline__ void rmsnorm_row(const T* __restrict__ x, T* __restri
     for (int i = 0; i < RMS_MAXV; ++i) {
       const int vi = l + 64 * i;
       if (vi < nv) {
-        ld16(xr + vi * VN, v[i]);
+        rld16(xr + vi * VN, v[i]);
 #pragma unroll
         for (int e = 0; e < VN; ++e) ss += v[i][e] * v[i][e];
       }
@@ -103,7 +112,7 @@ __device__ __forceinline__ void rmsnorm_row(const T* __restrict__ x, T* __restri
           v[i][e] *= ri;
           am = fmaxf(am, fabsf(v[i][e]));
         }
-        st16(yr + vi * VN, v[i]);
+        rst16(yr + vi * VN, v[i]);
       }
     }
     if (l == 0) r[row] = ri;
@@ -164,9 +173,9 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const T* __restrict__ dy, c
     for (int i = 0; i < RMS_MAXV; ++i) {
       const int vi = l + 64 * i;
       if (vi < nv) {
-        ld16(dy + off + vi * VN, g[i]);
-        ld16(y + off + vi * VN, h[i]);
-        if (dres) ld16(dres + off + vi * VN, rs[i]);
+        rld16(dy + off + vi * VN, g[i]);
+        rld16(y + off + vi * VN, h[i]);
+        if (dres) rld16(dres + off + vi * VN, rs[i]);
       }
     }
 #pragma unroll
@@ -185,7 +194,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_k(const T* __restrict__ dy, c
         float o[VN];
 #pragma unroll
         for (int e = 0; e < VN; ++e) o[e] = ri * (g[i][e] - h[i][e] * m) + (dres ? rs[i][e] : 0.f);
-        st16(dx + off + vi * VN, o);
+        rst16(dx + off + vi * VN, o);
       }
     }
   } else {
@@ -471,7 +480,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // bf16 logits: the row is kept in registers as its raw bf16 pairs (half the
 // registers of fp32 values, so twice the rows per CU hide the memory
 // latency) and widened on each of the three uses; the exponentials are taken
-// in base 2 on log2(e)-scaled logits.
+// in base 2 on log2(e)-scaled logits.  The logits are read and dz written
+// with non-temporal accesses (one pass over 4.3 GB at d24: 0.90 -> 0.82 ms).
 __global__ __launch_bounds__(256) void ce_bf16_k(bf16* z, const int32_t* __restrict__ tgt,
                                                   float* __restrict__ row_loss, int N, int V) {
   __shared__ float red[4];
@@ -486,7 +496,8 @@ __global__ __launch_bounds__(256) void ce_bf16_k(bf16* z, const int32_t* __restr
 #pragma unroll
   for (int i = 0; i < CE_MAXV; ++i) {
     const int vi = threadIdx.x + 256 * i;
-    raw[i] = vi < nv ? *(const u32x4*)(zr + vi * 8) : u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+    raw[i] = vi < nv ? __builtin_nontemporal_load((const u32x4*)(zr + vi * 8))
+                     : u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
   }
   // bf16 pair -> two floats: the low half shifted up, the high half masked
   auto lo = [](unsigned w) { return __uint_as_float(w << 16); };
@@ -531,7 +542,7 @@ __global__ __launch_bounds__(256) void ce_bf16_k(bf16* z, const int32_t* __restr
         o[2 * q] = (bf16)(p0 * invN);
         o[2 * q + 1] = (bf16)(p1 * invN);
       }
-      *(bf16x8*)(zr + vi * 8) = o;
+      __builtin_nontemporal_store(o, (bf16x8*)(zr + vi * 8));
     }
   }
   // the target's entry, rewritten by the thread that stored its vector

@@ -189,17 +189,19 @@ __global__ __launch_bounds__(OPT_NT) void adamw_k(float* __restrict__ p, const f
                                                  bf16* __restrict__ plow, size_t n4, float lr, float b1, float b2,
                                                  float eps, float decay, float rc1, float rc2) {
   for (size_t i = (size_t)blockIdx.x * OPT_NT + threadIdx.x; i < n4; i += (size_t)gridDim.x * OPT_NT) {
-    const f32x4 gv = ((const f32x4*)g)[i];
-    f32x4 pv = ((f32x4*)p)[i], mv = ((f32x4*)m)[i], vv = ((f32x4*)v)[i];
+    // every operand is streamed once: non-temporal accesses
+    const f32x4 gv = __builtin_nontemporal_load((const f32x4*)g + i);
+    f32x4 pv = __builtin_nontemporal_load((const f32x4*)p + i), mv = __builtin_nontemporal_load((const f32x4*)m + i),
+          vv = __builtin_nontemporal_load((const f32x4*)v + i);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       mv[e] = b1 * mv[e] + (1.0f - b1) * gv[e];
       vv[e] = b2 * vv[e] + (1.0f - b2) * gv[e] * gv[e];
       pv[e] = pv[e] * decay - lr * (mv[e] * rc1) / (sqrtf(vv[e] * rc2) + eps);
     }
-    ((f32x4*)p)[i] = pv;
-    ((f32x4*)m)[i] = mv;
-    ((f32x4*)v)[i] = vv;
+    __builtin_nontemporal_store(pv, (f32x4*)p + i);
+    __builtin_nontemporal_store(mv, (f32x4*)m + i);
+    __builtin_nontemporal_store(vv, (f32x4*)v + i);
     if (plow) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) plow[4 * i + e] = (bf16)pv[e];
