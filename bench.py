@@ -268,14 +268,36 @@ def kernel_figures(w, st, reps, torch, ops):
         out["gemm_fp8_mlp_up_sqr"] = {"shape": [N, F, C], "ms": t8 * 1e3, "tflops": fl / t8 / 1e12,
                                         "frac_fp8_peak": fl / t8 / PEAK_FP8, "flops": fl}
         del Aq, AqT, Bq
-    # weight gradient of the MLP down projection (token contraction, fp32 out)
-    dW = torch.empty(C, F, dtype=torch.float32, device=dev)
-    wsz = ops.gemm_ws_bytes(dt, C, F, N, ops.EPI_F32)
-    ws = torch.empty(max(wsz, 16), dtype=torch.uint8, device=dev)
-    t = ev_time(lambda: ops.gemm(C, F, N, A, False, C, Hh, False, F, ops.EPI_F32, dW, F, ws=ws), reps, torch)
-    out["gemm_wgrad_mlp_down"] = {"shape": [C, F, N], "ms": t * 1e3, "tflops": fl / t / 1e12,
-                                  "frac_bf16_peak": fl / t / PEAK_BF16}
-    del Hh, dW, ws
+    # weight gradients (token contraction, fp32 out, split over K with a
+    # fixed-order reduction): every shape one step launches, with its count
+    # per step; both operands token-major as in the block
+    Q, KV = H * D, Hkv * D
+    W3 = Q + 2 * KV
+    wshapes = [("mlp_down", C, F, w.n_layer), ("mlp_up", F, C, w.n_layer), ("attn_out", C, Q, w.n_layer),
+               ("qkv", W3, C, w.n_layer), ("lm_head", V, C, 1)]
+    if not w.mlp_fp8:
+        src = torch.empty(N, max(F, V, W3), dtype=dt, device=dev).normal_()
+        tot_t = tot_f = 0.0
+        per = {}
+        for name, M_, N_, cnt in wshapes:
+            dW = torch.empty(M_, N_, dtype=torch.float32, device=dev)
+            ws = torch.empty(max(ops.gemm_ws_bytes(dt, M_, N_, N, ops.EPI_F32), 16), dtype=torch.uint8, device=dev)
+            a_op, b_op = src[:, :M_].contiguous(), src[:, :N_].contiguous()
+            t = ev_time(lambda: ops.gemm(M_, N_, N, a_op, False, M_, b_op, False, N_, ops.EPI_F32, dW, N_, ws=ws),
+                        reps, torch)
+            f_ = 2.0 * M_ * N_ * N
+            per[name] = {"shape": [M_, N_, N], "per_step": cnt, "ms": t * 1e3, "tflops": f_ / t / 1e12,
+                         "frac_bf16_peak": f_ / t / PEAK_BF16}
+            tot_t += cnt * t
+            tot_f += cnt * f_
+            del dW, ws, a_op, b_op
+        del src
+        out["gemm_wgrad"] = {"shapes": per, "step_ms": tot_t * 1e3, "tflops": tot_f / tot_t / 1e12,
+                             "frac_bf16_peak": tot_f / tot_t / PEAK_BF16,
+                             "launches_per_step": sum(c for *_, c in wshapes),
+                             "avg_launch_ms": tot_t / sum(c for *_, c in wshapes) * 1e3,
+                             "avg_flops_per_launch": tot_f / sum(c for *_, c in wshapes)}
+    del Hh
     # attention forward / backward, full causal and windowed
     from gpt_decoder_block_amd.workmodel import attn_pairs
     qkv = rnd(N, W3)
@@ -315,6 +337,15 @@ def kernel_figures(w, st, reps, torch, ops):
     out["rmsnorm_bwd"] = {"ms": t * 1e3, "GBps": by / t / 1e9, "frac_hbm_peak": by / t / PEAK_HBM,
                           "cold_ms": tc * 1e3, "cold_frac_hbm_peak": by / tc / PEAK_HBM}
     del x, xn, dres, dx
+    # the box's read+write reference: the library's streaming copy of 1 GiB,
+    # warm (back to back) and cold (after the flush buffer is written)
+    csrc, cdst = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0), torch.empty(1 << 28, device=dev)
+    t = ev_time(lambda: ops.stream_copy(csrc, cdst), reps, torch)
+    tc = cold_time(lambda: ops.stream_copy(csrc, cdst), 5, torch, flush)
+    out["stream_copy_1gib"] = {"GBps": 2.0 * (1 << 30) / t / 1e9, "frac_hbm_peak": 2.0 * (1 << 30) / t / PEAK_HBM,
+                               "cold_GBps": 2.0 * (1 << 30) / tc / 1e9,
+                               "cold_frac_hbm_peak": 2.0 * (1 << 30) / tc / PEAK_HBM}
+    del csrc, cdst
     # cross-entropy over the vocabulary (bandwidth): one read + one write of the logits
     z0 = rnd(N, V)
     z = torch.empty_like(z0)
@@ -398,7 +429,7 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(w, budget_s=40.0):
+def cpu_baseline(w):
     """The fp64 oracle on the host cores: one block forward+backward per layer
     kind at B=1, T=w.T, plus the head at N=T tokens; scaled to the whole stack."""
     import oracle as O
@@ -439,6 +470,45 @@ def cpu_baseline(w, budget_s=40.0):
                       f"head+embedding at {T} tokens, fp64 numpy; per-step time = sum over the {w.n_layer} "
                       f"layers of their kind's time + head; measured {time.perf_counter() - t_start:.1f} s",
             "host_cpu_count": os.cpu_count()}
+
+
+class ClockSampler:
+    """GPU core clock during the timed steps: `amd-smi metric -c` sampled in a
+    thread (the mean over the compute dies' current clocks per sample)."""
+
+    def __init__(self):
+        import threading
+        self.samples, self._stop = [], threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        import re
+        import subprocess
+        while not self._stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-c"], capture_output=True, text=True, timeout=5)
+                blk = r.stdout.split("CLOCK:", 1)[-1]
+                mhz = [int(m) for m in re.findall(r"GFX_\d+:\s*CLK:\s*(\d+)\s*MHz", blk)]
+                if mhz:
+                    self.samples.append(sum(mhz) / len(mhz))
+            except (OSError, subprocess.SubprocessError, ValueError):
+                return
+            self._stop.wait(0.2)
+
+    def __enter__(self):
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join(timeout=10)
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"samples": len(v), "median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1],
+                "source": "amd-smi metric -c, mean over the compute dies, sampled during the timed steps"}
 
 
 def env_info(torch):
@@ -501,13 +571,14 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    e0.record(s)
-    evs[0].record(s)
-    for i in range(args.steps):
-        st.step()
-        evs[i + 1].record(s)
-    e1.record(s)
-    torch.cuda.synchronize()
+    with ClockSampler() as clk:
+        e0.record(s)
+        evs[0].record(s)
+        for i in range(args.steps):
+            st.step()
+            evs[i + 1].record(s)
+        e1.record(s)
+        torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1) / args.steps
     per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
@@ -548,8 +619,24 @@ def main():
            "loss_after_warmup": loss0,
            "ms_per_step_median": per_step[len(per_step) // 2], "ms_per_step_min": per_step[0],
            "ms_per_step_max": per_step[-1],
-           "env": env_info(torch),
+           "env": env_info(torch), "gpu_clock_during_timed_steps": clk.summary(),
            "roofline": roof, "kernels": kern}
+    if "gemm_wgrad" in kern:
+        wg = kern["gemm_wgrad"]
+        res["roofline_weight_gradients"] = {
+            "kernel": "gemm_bf16_k<M-major, N-major, fp32 split-K epilogue> + splitk_reduce_k (every weight "
+                      "gradient of the step: the largest kernel by time)",
+            "bound": "mfma", "achieved": wg["tflops"], "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+            "frac": wg["frac_bf16_peak"], "avg_launch_ms": wg["avg_launch_ms"],
+            "algorithmic_per_launch": f"2*M*N*K averaged over the step's {wg['launches_per_step']} launches = "
+                                      f"{wg['avg_flops_per_launch']:.4g} FLOP (K = {w.B * w.T} tokens)"}
+    if w.mlp_fp8:
+        # mixed roofline: the MLP's six products per layer on the fp8 peak, the rest on bf16
+        f_fp8 = 6.0 * 2 * w.C * w.mlp_hidden * w.n_layer * tokens
+        f_all = fpt * tokens
+        t_ideal = (f_all - f_fp8) / PEAK_BF16 + f_fp8 / PEAK_FP8
+        res["mixed_roofline"] = {"fp8_flops_per_step": f_fp8, "bf16_flops_per_step": f_all - f_fp8,
+                                 "ideal_ms": t_ideal * 1e3, "frac": t_ideal / (ms / 1e3)}
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w)

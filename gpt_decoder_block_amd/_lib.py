@@ -101,6 +101,7 @@ SIGNATURES = {
     "gdb_ve_bwd": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                              c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p,
                              c_int32, c_int32, c_void_p, c_void_p]),
+    "gdb_stream_copy": (c_int32, [c_size_t, c_void_p, c_void_p, c_void_p]),
     "gdb_rmsnorm_fwd": (c_int32, [c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p, c_void_p, c_void_p]),
     "gdb_rmsnorm_bwd": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p]),

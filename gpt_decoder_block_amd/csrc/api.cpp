@@ -598,6 +598,17 @@ gdb_status gdb_lm_head_ce_fwd_bwd(int32_t N, int32_t C, int32_t V, int32_t dtype
 }
 
 // ----------------------------------------------------------- building blocks
+gdb_status gdb_stream_copy(size_t bytes, const void* src, void* dst, void* stream) {
+  if (bytes % 16) return fail(GDB_EINVAL, "bytes must be a multiple of 16");
+  if (bytes == 0) { g_err.clear(); return GDB_OK; }
+  CHECK_PTR(src); CHECK_PTR(dst);
+  if ((const char*)src < (const char*)dst + bytes && (const char*)dst < (const char*)src + bytes)
+    return fail(GDB_EINVAL, "src and dst overlap");
+  HIPCHK(stream_copy(src, dst, bytes, (hipStream_t)stream));
+  g_err.clear();
+  return GDB_OK;
+}
+
 gdb_status gdb_rmsnorm_fwd(int32_t N, int32_t C, int32_t dtype, float eps, const void* x, void* xn, float* r,
                            void* stream) {
   if (N < 0 || C <= 0 || C % 8) return fail(GDB_EINVAL, "bad sizes N=%d C=%d (C multiple of 8)", N, C);

@@ -242,6 +242,24 @@ hipError_t rmsnorm_bwd(int dt, const void* dxn, const void* xn, const float* r, 
   return hipGetLastError();
 }
 
+// ------------------------------------------------------ streaming copy
+// The bandwidth reference of the memory-bound kernels: a plain copy of
+// 16-byte vectors with non-temporal loads and stores, four vectors in
+// flight per thread, grid-stride over the buffer.
+__global__ __launch_bounds__(256) void stream_copy_k(const u32x4* __restrict__ src, u32x4* __restrict__ dst, size_t n) {
+  constexpr int U = 4;
+  const size_t stride = (size_t)gridDim.x * 256 * U;
+  for (size_t i = (size_t)blockIdx.x * 256 * U + threadIdx.x; i < n; i += stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + (size_t)u * 256 < n) v[u] = __builtin_nontemporal_load(src + i + (size_t)u * 256);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + (size_t)u * 256 < n) __builtin_nontemporal_store(v[u], dst + i + (size_t)u * 256);
+  }
+}
+
 // -------------------------------------------------------------- embedding
 template <typename T>
 __global__ __launch_bounds__(256) void embed_fwd_k(const int32_t* __restrict__ ids, const T* __restrict__ wte,
@@ -269,6 +287,15 @@ __global__ __launch_bounds__(256) void embed_bwd_k(const int32_t* __restrict__ i
   const T* src = dx + (size_t)row * C;
 #pragma unroll 4
   for (int c = l; c < C; c += 64) unsafeAtomicAdd(dst + c, to_f(src[c]));
+}
+
+hipError_t stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 16;
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 256 * 4 - 1) / (256 * 4);
+  hipLaunchKernelGGL(stream_copy_k, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, s,
+                     (const u32x4*)src, (u32x4*)dst, n);
+  return hipGetLastError();
 }
 
 hipError_t embed_fwd(int dt, const int32_t* ids, const void* wte, void* x, int N, int C, int V, hipStream_t s) {
@@ -475,7 +502,6 @@ __global__ __launch_bounds__(256) void ce_k(T* z, const int32_t* __restrict__ tg
   if (threadIdx.x == 0) row_loss[n] = lse - zy;
 }
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // bf16 logits: the row is kept in registers as its raw bf16 pairs (half the
 // registers of fp32 values, so twice the rows per CU hide the memory

@@ -84,6 +84,21 @@ struct Loader {
   bf16x8 r[NV];       // 16-byte containers
   __amdgpu_buffer_rsrc_t rs;
   int tid;            // this thread's index among the 256 that load the operand
+  // M-major: this thread's 8x8 block, m chunk mc (m = 8mc..8mc+7) and k group
+  // kb (k = NV*kb ..).  HALF: in wave w, lane 16g + u takes mc = 8g + u%8 and
+  // kb = 2w + u/8, so each 16 lanes of a transposed store write 16 different
+  // 8-byte bank slots (row, chunk and half); the plain t%32, t/32 split wrote
+  // only 8 and took twice the LDS cycles per store
+  __device__ __forceinline__ void block_of(int t, int& mc, int& kb) const {
+    if constexpr (HALF) {
+      const int w = t >> 6, l = t & 63, g = l >> 4, u = l & 15;
+      mc = (u & 7) + 8 * g;
+      kb = 2 * w + (u >> 3);
+    } else {
+      mc = t & 31;
+      kb = t >> 5;
+    }
+  }
   unsigned off0;      // byte offset of this thread's first vector at k step 0
   unsigned step;      // bytes to advance per K step
   unsigned rowstep;   // bytes between the thread's consecutive vectors
@@ -103,7 +118,8 @@ struct Loader {
       kcol = c * VEC;
       kend_rel = kend - kbeg;
     } else {
-      const int mc = t & 31, kb = t >> 5;
+      int mc, kb;
+      block_of(t, mc, kb);
       const bf16* base = (const bf16*)P + (size_t)kbeg * ld + r0;
       const size_t bytes = (size_t)(kend - kbeg) * ld * 2;
       rs = make_rsrc(base, bytes);
@@ -147,8 +163,8 @@ struct Loader {
   // the eight loaded vectors)
   __device__ __forceinline__ void store1(bf16* __restrict__ S, int j) {
     static_assert(!KMAJ, "K-major operands are stored whole");
-    const int t = tid;
-    const int mc = t & 31, kb = t >> 5;
+    int mc, kb;
+    block_of(tid, mc, kb);
     const int row = mc * 8 + j;
     if constexpr (HALF) {
       bf16x4 w;

@@ -175,6 +175,14 @@ def _opt(t):
     return None if t is None else _p(t)
 
 
+def stream_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
+    """dst = src (same byte size, a multiple of 16): the bandwidth reference copy."""
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("src and dst must have the same size in bytes")
+    L.call("gdb_stream_copy", nb, _p(src), _p(dst), _stream(src))
+
+
 def rmsnorm_fwd(x: torch.Tensor, xn: torch.Tensor, r: torch.Tensor, eps: float = 1e-6) -> None:
     C = x.shape[-1]
     L.call("gdb_rmsnorm_fwd", x.numel() // C, C, dtype_code(x.dtype), eps, _p(x), _p(xn), _p(r), _stream(x))

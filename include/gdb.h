@@ -304,6 +304,12 @@ gdb_status gdb_ve_bwd(int32_t N, int32_t Hkv, int32_t D, int32_t dtype, const vo
  * conventions (device pointers, caller-owned memory, async on `stream`).
  * ---------------------------------------------------------------------- */
 
+/* Bandwidth reference: dst = src over `bytes` (a multiple of 16; the
+ * buffers must not overlap), 16-byte non-temporal loads and stores.  The
+ * memory-bound kernels (norms, cross-entropy, embedding, optimizer) are
+ * compared against its rate as well as against the HBM's nominal peak. */
+gdb_status gdb_stream_copy(size_t bytes, const void* src, void* dst, void* stream);
+
 /* RMSNorm without affine over rows of x [N, C]: xn = x * r, r[n] = 1/sqrt(mean(x[n]^2) + eps)
  * (r float32 [N]).  RMSNorm with eps = 1e-6 is the norm before attention, before
  * the MLP, on q and k per head, and before the lm_head. */
