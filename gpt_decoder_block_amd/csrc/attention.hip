@@ -102,6 +102,36 @@ __device__ __forceinline__ void tile_async(const bf16* base, size_t ld, int row0
   }
 }
 
+// The same copy through a buffer resource over the operand (32-bit byte
+// offsets; the host checks that a sequence's rows fit), for the forward and
+// dQ loops that keep copies in flight while they read another stage.  The
+// compiler inserts a wait for pending LDS copies before any LDS read that may
+// alias them, and with global_load_lds into a stage array it could not tell
+// the stages apart: a vmcnt(0) before every other tile's reads drained the
+// prefetch.  Here the destination's origin is hidden, so no such wait is
+// inserted; the kernels wait for their own copies explicitly before the
+// barrier that publishes a stage.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16* base, size_t ld, int nrows) {
+  const size_t bytes = nrows > 0 ? ((size_t)(nrows - 1) * ld + HD) * 2 : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, (int)min(bytes, (size_t)0x7FFFFFF0),
+                                           0x00020000);
+}
+template <int NW = 4>
+__device__ __forceinline__ void tile_async(__amdgpu_buffer_rsrc_t rs, size_t ld, int row0, int nrows, bf16* S) {
+  constexpr int RW = 64 / NW;  // rows per wave
+  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), L = t & 63;
+#pragma unroll
+  for (int i = 0; i < RW / 4; ++i) {
+    const int r = w * RW + i * 4 + (L >> 4);
+    const int c = kswz(r, L & 15);
+    int row = row0 + r;
+    row = row < nrows ? row : nrows - 1;
+    lds_ptr d = (lds_ptr)(S + (w * RW + i * 4) * HD);
+    asm volatile("" : "+s"(d));  // hide the destination's origin from the alias analysis
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, (unsigned)((row * ld + c * 8) * 2), 0, 0, 0);
+  }
+}
+
 // 64 floats (one per lane) straight into LDS; index clamped to n - 1.
 __device__ __forceinline__ void vec64_async(const float* src, int i0, int n, float* S) {
   const int L = threadIdx.x & 63;
@@ -145,7 +175,9 @@ __device__ __forceinline__ bool visible(int i, int j, int T, int W) {
 }
 
 // wait until at most N vector-memory operations of this wave are in flight
-#define WAIT_VM(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
+// (the builtin, so that the compiler's own wait insertion knows which loads
+// are complete; gfx9 encoding: vmcnt in bits 3:0, expcnt 7, lgkmcnt 15)
+#define WAIT_VM(N) __builtin_amdgcn_s_waitcnt(0xF70 | (N))
 // workgroup barrier that waits for this wave's LDS accesses but leaves its
 // copies into LDS in flight (__syncthreads waits for every one: vmcnt(0))
 #define LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
@@ -162,7 +194,6 @@ __device__ __forceinline__ bool visible(int i, int j, int T, int W) {
 // margin for bf16 rounding of q^, k^) replaces the running row max: no max
 // reduction, no rescaling of O, and exp never overflows.  Otherwise the usual
 // online max with rescaling.
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Scores the lane may not see become -inf in place, so the exponentials
 // that follow give exactly 0; called on tiles that cross the band's edge
@@ -254,6 +285,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_k(AttnArgs a, float sca
   const bf16* base = (const bf16*)a.qkv + (size_t)b * T * a.ld;
   const bf16* kbase = base + (H + g) * HD;
   const bf16* vbase = base + (H + Hkv + g) * HD;
+  const auto krs = tile_rsrc(kbase, a.ld, T), vrs = tile_rsrc(vbase, a.ld, T);
 
   int kv_lo = W >= 0 ? max(0, q0 - W) : 0;
   kv_lo &= ~63;
@@ -263,11 +295,11 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_k(AttnArgs a, float sca
   const int wq_hi = min(qw0 + 32 * IB - 1, T - 1);
   const int wk_lo = W >= 0 ? max(0, qw0 - W) : 0;
 
-  tile_async<NW>(kbase, a.ld, kv_lo, T, Ks[0]);
-  tile_async<NW>(vbase, a.ld, kv_lo, T, Vs[0]);
+  tile_async<NW>(krs, a.ld, kv_lo, T, Ks[0]);
+  tile_async<NW>(vrs, a.ld, kv_lo, T, Vs[0]);
   if (NS == 3 && ntile > 1) {
-    tile_async<NW>(kbase, a.ld, kv_lo + 64, T, Ks[1]);
-    tile_async<NW>(vbase, a.ld, kv_lo + 64, T, Vs[1]);
+    tile_async<NW>(krs, a.ld, kv_lo + 64, T, Ks[1]);
+    tile_async<NW>(vrs, a.ld, kv_lo + 64, T, Vs[1]);
   }
 
   bf16x8 qf[IB][8];
@@ -300,8 +332,8 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_bf16_k(AttnArgs a, float sca
     const bool ahead = it + NS - 1 < ntile;
     if (ahead) {
       constexpr int sn = (ST + NS - 1) % NS;
-      tile_async<NW>(kbase, a.ld, kv0 + 64 * (NS - 1), T, Ks[sn]);
-      tile_async<NW>(vbase, a.ld, kv0 + 64 * (NS - 1), T, Vs[sn]);
+      tile_async<NW>(krs, a.ld, kv0 + 64 * (NS - 1), T, Ks[sn]);
+      tile_async<NW>(vrs, a.ld, kv0 + 64 * (NS - 1), T, Vs[sn]);
     }
     // wave-uniform: does the tile touch this wave's rows, and is it fully visible?
     const bool any = qw0 < T && kv0 <= wq_hi && kv0 + 63 >= wk_lo;
@@ -637,17 +669,18 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void attn_bwd_dq_bf16_k(A
   const bf16* base = (const bf16*)a.qkv + (size_t)b * T * a.ld;
   const bf16* kbase = base + (H + g) * HD;
   const bf16* vbase = base + (H + Hkv + g) * HD;
+  const auto krs = tile_rsrc(kbase, a.ld, T), vrs = tile_rsrc(vbase, a.ld, T);
 
   int kv_lo = W >= 0 ? max(0, q0 - W) : 0;
   kv_lo &= ~63;
   const int kv_hi = min(T, q0 + FQ);
   const int ntile = (kv_hi - kv_lo + 63) / 64;
 
-  tile_async<NW>(kbase, a.ld, kv_lo, T, Ks[0]);
-  tile_async<NW>(vbase, a.ld, kv_lo, T, Vs[0]);
+  tile_async<NW>(krs, a.ld, kv_lo, T, Ks[0]);
+  tile_async<NW>(vrs, a.ld, kv_lo, T, Vs[0]);
   if (NS == 3 && ntile > 1) {
-    tile_async<NW>(kbase, a.ld, kv_lo + 64, T, Ks[1]);
-    tile_async<NW>(vbase, a.ld, kv_lo + 64, T, Vs[1]);
+    tile_async<NW>(krs, a.ld, kv_lo + 64, T, Ks[1]);
+    tile_async<NW>(vrs, a.ld, kv_lo + 64, T, Vs[1]);
   }
   bf16x8 qf[8], df[8];
   const int qc = min(qi, T - 1);
@@ -676,8 +709,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void attn_bwd_dq_bf16_k(A
     const bool ahead = it + NS - 1 < ntile;
     if (ahead) {
       constexpr int sn = (ST + NS - 1) % NS;
-      tile_async<NW>(kbase, a.ld, kv0 + 64 * (NS - 1), T, Ks[sn]);
-      tile_async<NW>(vbase, a.ld, kv0 + 64 * (NS - 1), T, Vs[sn]);
+      tile_async<NW>(krs, a.ld, kv0 + 64 * (NS - 1), T, Ks[sn]);
+      tile_async<NW>(vrs, a.ld, kv0 + 64 * (NS - 1), T, Vs[sn]);
     }
     const bool any = qw0 < T && kv0 <= wq_hi && kv0 + 63 >= wk_lo;
     if (any) {
@@ -835,8 +868,12 @@ __global__ __launch_bounds__(64) void attn_bwd_dkv_f32_k(AttnArgs a, float scale
 
 }  // namespace
 
+// the bf16 kernels address a sequence's K and V rows by 32-bit byte offsets
+static bool offsets_fit(const AttnArgs& a) { return (size_t)a.T * a.ld * 2 <= 0x7FFFFF00ull; }
+
 hipError_t attn_fwd(int dt, const AttnArgs& a, hipStream_t s) {
   if (a.B * a.T == 0) return hipSuccess;
+  if (dt == BF16 && !offsets_fit(a)) return hipErrorInvalidValue;
   const float scale = 1.0f / sqrtf((float)a.D);
   if (dt == BF16) {
     if (a.qk_normed) {
@@ -857,6 +894,7 @@ hipError_t attn_fwd(int dt, const AttnArgs& a, hipStream_t s) {
 
 hipError_t attn_bwd(int dt, const AttnArgs& a, hipStream_t s) {
   if (a.B * a.T == 0) return hipSuccess;
+  if (dt == BF16 && !offsets_fit(a)) return hipErrorInvalidValue;
   const float scale = 1.0f / sqrtf((float)a.D);
   const int rows = a.B * a.T;  // one wave per token
   if (dt == BF16) hipLaunchKernelGGL(attn_delta_k<bf16>, dim3((rows + 3) / 4), dim3(256), 0, s, a);

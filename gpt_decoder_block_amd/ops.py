@@ -329,6 +329,9 @@ def adamw_step(p: torch.Tensor, g: torch.Tensor, m: torch.Tensor, v: torch.Tenso
 
 def cross_entropy(z: torch.Tensor, targets: torch.Tensor, row_loss: torch.Tensor, loss: torch.Tensor) -> None:
     N, V = z.shape
+    if targets.numel() != N or row_loss.numel() != N or loss.numel() < 1:
+        raise ValueError(f"cross_entropy: {N} rows of logits need {N} targets and {N} row losses "
+                         f"(got {targets.numel()} and {row_loss.numel()})")
     L.call("gdb_cross_entropy", N, V, dtype_code(z.dtype), _p(z), _p(targets), _p(row_loss), _p(loss),
            _stream(z))
 
