@@ -12,7 +12,9 @@ import os
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libgdb.so")
+# GDB_LIB selects another build of the same library (for example the
+# host-sanitizer build made by `python -m gpt_decoder_block_amd.build --sanitize`)
+LIB_PATH = os.environ.get("GDB_LIB") or os.path.join(HERE, "libgdb.so")
 
 # the GDB_ABI_VERSION this binding's structures and signatures follow
 ABI_VERSION = 6

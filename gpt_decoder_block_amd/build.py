@@ -46,6 +46,37 @@ def _compile(src: str) -> str:
     return obj
 
 
+def build_sanitized(verbose: bool = False) -> str:
+    """_build_san/libgdb_san.so: the host code (argument validation, workspace carving,
+    launch logic in api.cpp) built with AddressSanitizer and
+    UndefinedBehaviorSanitizer, the device code as in the normal build.  Load
+    it with GDB_LIB=<path> and the clang ASan runtime preloaded."""
+    san = os.path.join(HERE, "_build_san")
+    os.makedirs(san, exist_ok=True)
+    if any(not os.path.exists(os.path.join(BUILD, s + ".o")) for s in SOURCES if s != "api.cpp"):
+        build()  # the device objects of the normal build
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(san if src == "api.cpp" else BUILD, os.path.basename(src) + ".o")
+        if src == "api.cpp":
+            cmd = [hipcc()] + _flags() + ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+                                          "-fsanitize=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                                          "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stderr}")
+        objs.append(obj)
+    out = os.path.join(san, "libgdb_san.so")
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-fsanitize=address", "-fsanitize=undefined",
+           "-shared-libsan", "-o", out] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
+    if verbose:
+        print(f"built {out}")
+    return out
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
@@ -62,5 +93,8 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--sanitize" in sys.argv[1:]:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)
