@@ -47,6 +47,12 @@ constexpr int BM = 256, BN = 256, BK = 64;
 #ifndef GEMM_NW
 #define GEMM_NW 8
 #endif
+// both operands M/N-contiguous (the weight gradients): copied straight into
+// LDS as [k][m] and read with the LDS transpose load (1), or loaded into
+// registers and stored transposed (0)
+#ifndef GEMM_TRD
+#define GEMM_TRD 1
+#endif
 constexpr int TILE_ELEMS = BM * BK;  // bf16 elements of one operand tile (128-byte rows)
 constexpr int BK8 = 128;             // fp8 codes per K step (the same 128-byte rows)
 
@@ -224,6 +230,53 @@ struct DmaLoader {
   }
 };
 
+// M-contiguous operand copied straight from memory into LDS as [64 k][256 m]
+// (512-byte rows), the 16-byte chunk index XOR-swizzled by 4(k & 7): in wave
+// instruction q (k rows 2q, 2q + 1) lane L writes the 16 bytes at 16L, i.e.
+// physical chunk L%32 of row 2q + L/32, so it fetches logical chunk
+// (L%32) ^ 4(row & 7), m = 8 * chunk .. + 7.  The resource is rebased at
+// (kbeg, first m) and ends at the split's last k row, so k rows past the
+// split read as zero; chunks past the operand's m extent get an offset past
+// any resource size (zero too).
+template <int NW>
+struct TrDma {
+  static constexpr int NI = 32 / NW;  // copies per wave (32 per operand and K step)
+  __amdgpu_buffer_rsrc_t rs;
+  unsigned off[NI], bad[NI];
+  unsigned step;  // bytes per K step (64 k rows)
+  __device__ __forceinline__ void init(const void* P, int ld, int rows, int r0, int kbeg, int kend) {
+    const int t = threadIdx.x, w = t >> 6, L = t & 63;
+    const bf16* base = (const bf16*)P + (size_t)kbeg * ld + r0;
+    rs = make_rsrc(base, (size_t)(kend - kbeg) * ld * 2);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = 2 * (i * NW + w) + (L >> 5);
+      const int lc = (L & 31) ^ ((row & 7) << 2);
+      const bool ok = r0 + 8 * lc < rows;
+      off[i] = (unsigned)((row * ld + 8 * lc) * 2);
+      bad[i] = ok ? 0u : OOB;
+    }
+    step = (unsigned)(BK * ld * 2);
+  }
+  // Issued as an asm statement: the compiler then cannot see an LDS store
+  // that might alias the transposed fragment reads that follow (the
+  // intrinsic made it wait for every copy in flight before each of them);
+  // the kernel waits for its copies itself before the barrier that publishes
+  // a stage.  No register is written; M0 carries the LDS destination.
+  __device__ __forceinline__ void load1(int kt, bf16* S, int i) {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const unsigned d = (unsigned)(size_t)(lds_ptr_t)(S + (i * NW + w) * 512);
+    const unsigned o = (off[i] + kt * step) | bad[i];
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(d), "v"(o), "s"(rs)
+                 : "memory", "m0");
+  }
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 tr_read(const bf16* p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p));
+}
+
 __device__ __forceinline__ void tile_coords(int bid, int nbm, int nbn, int& tm, int& tn) {
   const int total = nbm * nbn;
   const int full = (total / 8) * 8;
@@ -380,6 +433,87 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_k(GemmArgs p) {
       WAIT_VM0();
       __syncthreads();
       load_frags8<JB>(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
+    }
+  } else if constexpr (!AK && !BK_ && GEMM_TRD) {
+    // both operands M/N-contiguous: copied straight into LDS as [k][m] rows
+    // and read as MFMA fragments with the LDS transpose load.  A lane's
+    // fragment then holds k = 16kk + 4lh + e%4 + 8(e/4) (e = 0..7) of its row,
+    // the same permutation of the contraction in both operands.  The
+    // schedule is the one below without the transposed stores.
+    TrDma<NW> da, db;
+    da.init(p.A, p.lda, p.M, m0, kbeg, kend);
+    db.init(p.B, p.ldb, p.N, n0, kbeg, kend);
+    constexpr int ND = 32 / NW;
+    constexpr int NQ = 2 * ND;
+    auto issue1 = [&](int kt, int stg, int q) {
+      if (q < ND) da.load1(kt, smem[stg][0], q);
+      else db.load1(kt, smem[stg][1], q - ND);
+    };
+    // transposed-read lane constants: rows 16kk + rl (and + 8), 32-column
+    // block c, its physical chunk group (c ^ (rl & 7)), chunk and half within
+    const int G = lane >> 4, sl = lane & 15;
+    const int rl = 4 * (G >> 1) + (sl >> 2);  // < 8, so rl & 7 = rl
+    const int lane_off = rl * 256 + 8 * (2 * (G & 1) + ((sl & 3) >> 1)) + 4 * (sl & 1);
+    auto frag = [&](const bf16* S, int c, int kk) {
+      const bf16* q0 = S + kk * 16 * 256 + lane_off + 32 * (c ^ rl);
+      const bf16x4 lo = tr_read(q0), hi = tr_read(q0 + 8 * 256);
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    auto load_tr = [&](const bf16* As, const bf16* Bs, int kk, bf16x8* af, bf16x8* bfr) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = frag(As, wm * 4 + i, kk);
+#pragma unroll
+      for (int j = 0; j < JB; ++j) bfr[j] = frag(Bs, wn * JB + j, kk);
+    };
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) issue1(0, 0, q);
+    WAIT_VM0();
+    __syncthreads();
+    bf16x8 af[2][4], bfr[2][JB];
+    load_tr(smem[0][0], smem[0][1], 0, af[0], bfr[0]);
+    constexpr int NM = 4 * JB;  // MFMAs per sub-step
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st = kt & 1;
+      const bf16* As = smem[st][0];
+      const bf16* Bs = smem[st][1];
+      // sub-step 0: its MFMAs interleaved with the next step's copies and
+      // the fragment reads of sub-step 1
+#pragma unroll
+      for (int q = 0; q < NM; ++q) {
+        const int i = q / JB, j = q % JB;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[0][j], af[0][i], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int u = q * NQ / NM; u < (q + 1) * NQ / NM; ++u) issue1(kt + 1, st ^ 1, u);
+        if (q < 4 + JB) {
+          if (q < 4) af[1][q] = frag(As, wm * 4 + q, 1);
+          else bfr[1][q - 4] = frag(Bs, wn * JB + q - 4, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int kk = 1; kk < BK / 16 - 1; ++kk) {
+        const int cb = kk & 1;
+        load_tr(As, Bs, kk + 1, af[cb ^ 1], bfr[cb ^ 1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < JB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cb][j], af[cb][i], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * (4 + JB) / NM, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < JB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[1][j], af[1][i], acc[i][j], 0, 0, 0);
+      WAIT_VM0();
+      __syncthreads();
+      load_tr(smem[st ^ 1][0], smem[st ^ 1][1], 0, af[0], bfr[0]);
     }
   } else {
     // bf16: a K-contiguous operand is copied straight into LDS (DMA); an
