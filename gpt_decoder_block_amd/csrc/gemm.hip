@@ -53,6 +53,17 @@ constexpr int BM = 256, BN = 256, BK = 64;
 #ifndef GEMM_TRD
 #define GEMM_TRD 1
 #endif
+// both operands K-contiguous, splits of a multiple of 128 k: fed by a ring of
+// four 32-k LDS stages with precomputed addresses (1), or by the two 64-k
+// stages of the main kernel (0).  The ring removes every VALU instruction from
+// the main loop but was 1-3% slower on the d24 shapes with 8 waves and 3-7%
+// with 4 (one barrier per 32 k, 64-byte copy segments), so it is off.
+#ifndef GEMM_RING
+#define GEMM_RING 0
+#endif
+#ifndef RING_NW
+#define RING_NW 8
+#endif
 constexpr int TILE_ELEMS = BM * BK;  // bf16 elements of one operand tile (128-byte rows)
 constexpr int BK8 = 128;             // fp8 codes per K step (the same 128-byte rows)
 
@@ -272,6 +283,48 @@ struct TrDma {
   }
 };
 
+// Both operands K-contiguous, 4 waves of 128x128: a ring of four LDS stages
+// of 32 k per operand (64-byte rows, 16 KiB per 256-row tile; A stages in the
+// first 64 KiB, B stages in the second), so copies run three steps ahead of
+// the MFMAs.  Copy q (0..15) of a step fills rows 16q..16q+15 of a stage:
+// lane L writes physical chunk L%4 of row 16q + L/4, so it fetches logical
+// chunk (L%4) ^ ring_swz(row).  ring_swz takes a different value on each row
+// of every aligned group of 4 rows with equal (row & 1) among 8, and of every
+// aligned group of 4 rows with equal (row & 3) among 16, so the 8 or 16 lanes
+// the LDS serves together in a 16-byte fragment read (32 consecutive rows,
+// one chunk) hit distinct banks.  The resource is rebased on the scalar unit
+// at every step (base + 64 bytes per step); steps past the end get an empty
+// resource (their copies write zeros into a stage nobody reads).
+__device__ __forceinline__ int ring_swz(int row) { return (((row >> 1) ^ (row >> 3)) & 1) | ((row >> 1) & 2); }
+
+template <int NW>
+struct RingDma {
+  static constexpr int NI = 16 / NW;  // copies per wave (16 per operand and step)
+  const char* base;
+  unsigned bytes;
+  unsigned off[NI];
+  __device__ __forceinline__ void init(const void* P, int ld, int rows, int r0, int kbeg, int w, int L) {
+    base = (const char*)P + ((size_t)r0 * ld + kbeg) * 2;
+    const size_t b = rows > r0 ? ((size_t)(rows - r0) * ld - kbeg) * 2 : 0;
+    bytes = b > 0xFFFFFF00ull ? 0xFFFFFF00u : (unsigned)b;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = 16 * (i * NW + w) + (L >> 2);
+      const int lc = (L & 3) ^ ring_swz(row);
+      off[i] = r0 + row < rows ? (unsigned)(row * ld * 2 + lc * 16) : OOB;
+    }
+  }
+  // copy i (0..NI-1) of this wave for K step kt into the LDS bytes at d (the
+  // wave's 1 KiB block of the stage); an asm statement, as for TrDma
+  __device__ __forceinline__ void load1(int kt, int nk, unsigned d, int i) const {
+    const unsigned adv = (unsigned)kt * 64u;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(base + adv), (short)0, kt < nk ? (int)(bytes - adv) : 0, 0x00020000);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(d), "v"(off[i]), "s"(rs)
+                 : "memory", "m0");
+  }
+};
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x4 tr_read(const bf16* p) {
   return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p));
@@ -341,7 +394,7 @@ template <> struct V4<float> { typedef f32x4 t; };
 // NW: waves per workgroup.  4: a 2x2 grid of 128x128 wave tiles (one wave
 // per SIMD); 8: a 2x4 grid of 128x64 wave tiles, two waves per SIMD, so one
 // wave's MFMAs run while the other waits on its copies or LDS reads.
-template <bool AK, bool BK_, int EPI, bool F8 = false, typename OT = bf16, int NW = 4>
+template <bool AK, bool BK_, int EPI, bool F8 = false, typename OT = bf16, int NW = 4, bool RING = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_k(GemmArgs p) {
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int NTH = 64 * NW;
@@ -437,6 +490,99 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_k(GemmArgs p) {
       __syncthreads();
       load_frags8<JB>(smem[st ^ 1][0], smem[st ^ 1][1], 0, wm, wn, lr, lh, af[0], bfr[0]);
     }
+  } else if constexpr (RING) {
+    // Ring of four 32-k stages (RingDma).  Step kt (stage kt % 4): sub-step
+    // 0's MFMAs run on fragments read during the previous step, interleaved
+    // with the reads of sub-step 1's fragments and half of this wave's copies
+    // of step kt + 3 (into the stage every wave finished reading before the
+    // last barrier); then each wave waits for its copies of step kt + 1 (those
+    // of steps kt + 2 and kt + 3 may stay in flight) and for its LDS reads,
+    // one barrier, and sub-step 1's MFMAs run with the reads of step kt + 1's
+    // first fragments and the other half of the copies.  The host sends only
+    // splits of a multiple of 128 k here, so the loop runs whole groups of 4
+    // steps.
+    static_assert(AK && BK_ && !F8, "the ring serves bf16 operands that are both K-contiguous");
+    constexpr int NM = 4 * JB;        // MFMAs per sub-step
+    constexpr int NR = 4 + JB;        // fragment reads per sub-step
+    constexpr int CPO = 16 / NW;      // copies per wave, operand and step
+    constexpr int CH = CPO;           // copies per sub-step (A in sub-step 0, B in 1)
+    const int nks = (kend - kbeg) / 32;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    RingDma<NW> ra, rb;
+    ra.init(p.A, p.lda, p.M, m0, kbeg, w, lane);
+    rb.init(p.B, p.ldb, p.N, n0, kbeg, w, lane);
+    const unsigned lds0 = (unsigned)(size_t)(lds_ptr_t)&smem[0][0][0];
+    const char* Lb = (const char*)&smem[0][0][0];
+    // fragment lane offsets (bytes): row wm*128 + lr of A / row wn*32*JB + lr
+    // of B (B stages start at 64 KiB), chunk (2kk + lh) ^ ring_swz(lr) = g ^ 2kk
+    const int g = lh ^ ring_swz(lr);
+    const int ao0 = (wm * 128 + lr) * 64 + 16 * g, ao1 = (wm * 128 + lr) * 64 + 16 * (g ^ 2);
+    const int bo0 = 65536 + (wn * 32 * JB + lr) * 64 + 16 * g;
+    const int bo1 = 65536 + (wn * 32 * JB + lr) * 64 + 16 * (g ^ 2);
+    auto copy = [&](int kt, int stg, int c) {  // c < CPO: A copy c, else B copy c - CPO
+      const int i = c % CPO;
+      const unsigned blk = (unsigned)(stg * 16384 + (i * NW + wu) * 1024);
+      if (c < CPO) ra.load1(kt, nks, lds0 + blk, i);
+      else rb.load1(kt, nks, lds0 + 65536u + blk, i);
+    };
+    auto fa = [&](int stg, int kk, int i) {
+      return *(const bf16x8*)(Lb + (kk ? ao1 : ao0) + stg * 16384 + i * 2048);
+    };
+    auto fb = [&](int stg, int kk, int j) {
+      return *(const bf16x8*)(Lb + (kk ? bo1 : bo0) + stg * 16384 + j * 2048);
+    };
+    // fragment read r of a sub-step, in the MFMAs' order of first use: A0, B0..B(JB-1), A1..A3
+    auto rd = [&](bf16x8* a, bf16x8* b, int stg, int kk, int r) {
+      if (r == 0) a[0] = fa(stg, kk, 0);
+      else if (r <= JB) b[r - 1] = fb(stg, kk, r - 1);
+      else a[r - JB] = fa(stg, kk, r - JB);
+    };
+#pragma unroll
+    for (int kt = 0; kt < 3; ++kt)
+#pragma unroll
+      for (int c = 0; c < 2 * CPO; ++c) copy(kt, kt, c);
+    if constexpr (NW == 4) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    bf16x8 a0[4], b0[JB], a1[4], b1[JB];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) rd(a0, b0, 0, 0, r);
+    for (int kt0 = 0; kt0 < nks; kt0 += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kt = kt0 + u;
+        const int sn = (u + 1) & 3, sc = (u + 3) & 3;
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+          const int i = q / JB, j = q % JB;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0[j], a0[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+          for (int h = 0; h < CH; ++h)
+            if (q == h * NM / CH) copy(kt + 3, sc, h);
+#pragma unroll
+          for (int r = 0; r < NR; ++r)
+            if (q == r * NM / NR) rd(a1, b1, u, 1, r);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (NW == 4) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+          const int i = q / JB, j = q % JB;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1[j], a1[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+          for (int h = 0; h < CH; ++h)
+            if (q == h * NM / CH) copy(kt + 3, sc, CH + h);
+#pragma unroll
+          for (int r = 0; r < NR; ++r)
+            if (q == r * NM / NR) rd(a0, b0, sn, 0, r);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    // the copies past the end still write zeros into the ring, which the
+    // epilogue reuses for staging
+    WAIT_VM0();
+    __syncthreads();
   } else if constexpr (!AK && !BK_ && GEMM_TRD) {
     // both operands M/N-contiguous: copied straight into LDS as [k][m] rows
     // and read as MFMA fragments with the LDS transpose load.  A lane's
@@ -923,41 +1069,41 @@ __global__ __launch_bounds__(256) void gemm_f32_k(GemmArgs p) {
   }
 }
 
-template <bool AK, bool BKM, bool F8 = false, typename OT = bf16, int NW = 4>
+template <bool AK, bool BKM, bool F8 = false, typename OT = bf16, int NW = 4, bool RING = false>
 hipError_t launch_bf16(const GemmArgs& a, dim3 g, hipStream_t s) {
   g.z = a.batch > 1 ? a.batch : 1;
   switch (a.epi) {
-    case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_STORE, F8, OT, NW>), g, dim3(64 * NW), 0, s, a); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_RESID, F8, OT, NW>), g, dim3(64 * NW), 0, s, a); break;
-    case EPI_RELU2: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_RELU2, F8, OT, NW>), g, dim3(64 * NW), 0, s, a); break;
-    case EPI_DRELU2: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_DRELU2, F8, OT, NW>), g, dim3(64 * NW), 0, s, a); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_STORE, F8, OT, NW, RING>), g, dim3(64 * NW), 0, s, a); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_RESID, F8, OT, NW, RING>), g, dim3(64 * NW), 0, s, a); break;
+    case EPI_RELU2: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_RELU2, F8, OT, NW, RING>), g, dim3(64 * NW), 0, s, a); break;
+    case EPI_DRELU2: hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_DRELU2, F8, OT, NW, RING>), g, dim3(64 * NW), 0, s, a); break;
     case EPI_SQR:  // the MLP up-projection: both operands K-major
       if constexpr (AK && BKM) {
-        hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_SQR, F8, OT, NW>), g, dim3(64 * NW), 0, s, a);
+        hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_SQR, F8, OT, NW, RING>), g, dim3(64 * NW), 0, s, a);
         break;
       }
       return hipErrorInvalidValue;
     case EPI_DSQR:  // the hidden gradient: dout K-major, the weight either way
       if constexpr (AK) {
-        hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_DSQR, F8, OT, NW>), g, dim3(64 * NW), 0, s, a);
+        hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_DSQR, F8, OT, NW, RING>), g, dim3(64 * NW), 0, s, a);
         break;
       }
       return hipErrorInvalidValue;
     case EPI_QKNORM:
       if constexpr (AK && BKM && !F8 && std::is_same<OT, bf16>::value) {
-        hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_QKNORM, F8, OT, NW>), g, dim3(64 * NW), 0, s, a);
+        hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_QKNORM, F8, OT, NW, RING>), g, dim3(64 * NW), 0, s, a);
         break;
       }
       return hipErrorInvalidValue;
     case EPI_F32:
       if constexpr (std::is_same<OT, bf16>::value) {
-        hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_F32, F8, OT, NW>), g, dim3(64 * NW), 0, s, a);
+        hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_F32, F8, OT, NW, RING>), g, dim3(64 * NW), 0, s, a);
         break;
       }
       return hipErrorInvalidValue;
     case EPI_AXPBY:
       if constexpr (!F8) {
-        hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_AXPBY, F8, OT, NW>), g, dim3(64 * NW), 0, s, a);
+        hipLaunchKernelGGL((gemm_bf16_k<AK, BKM, EPI_AXPBY, F8, OT, NW, RING>), g, dim3(64 * NW), 0, s, a);
         break;
       }
       return hipErrorInvalidValue;
@@ -1032,7 +1178,13 @@ hipError_t gemm(int dt, const GemmArgs& a, hipStream_t s) {
     // on its copies or LDS reads): measured 2-10% faster than 4 with both
     // operands copied straight into LDS, 4-6% with an M/N-contiguous operand
     // loaded into registers (each thread loading half of its 8x8 block)
-    if (a.a_kmajor && a.b_kmajor) return launch_bf16<true, true, false, bf16, GEMM_NW>(a, g, s);
+    if (a.a_kmajor && a.b_kmajor) {
+#if GEMM_RING
+      const int ksplit = ((a.K + a.splits * BK - 1) / (a.splits * BK)) * BK;
+      if (a.K % 128 == 0 && ksplit % 128 == 0) return launch_bf16<true, true, false, bf16, RING_NW, true>(a, g, s);
+#endif
+      return launch_bf16<true, true, false, bf16, GEMM_NW>(a, g, s);
+    }
     if (a.a_kmajor) return launch_bf16<true, false, false, bf16, 8>(a, g, s);
     if (!a.b_kmajor) return launch_bf16<false, false, false, bf16, 8>(a, g, s);
     return launch_bf16<false, true, false, bf16, 8>(a, g, s);

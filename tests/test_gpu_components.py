@@ -135,6 +135,37 @@ def test_gemm_bf16_multi_tile_exact_shapes():
     assert_close(C, A.astype(np.float64) @ B.astype(np.float64).T, "bf16", "store")
 
 
+@pytest.mark.parametrize("epi", [0, 1, 2, 3, 4, 6, 7])
+@pytest.mark.parametrize("M,N,K", [(296, 264, 384), (520, 776, 1024)])
+def test_gemm_bf16_kmajor_epilogues(epi, M, N, K):
+    # both operands K-contiguous with K a multiple of 128 (the shape class of
+    # every block product; also the one the ring-fed kernel variant accepts):
+    # ragged M and N over several tiles, 6 or 16 K steps, every epilogue
+    print(f"gemm kmajor epi={epi} M={M} N={N} K={K}", flush=True)
+    A = rounded(RNG.standard_normal((M, K)), "bf16")
+    B = rounded(RNG.standard_normal((N, K)), "bf16")
+    R = rounded(RNG.standard_normal((M, N)), "bf16")
+    acc = A.astype(np.float64) @ B.astype(np.float64).T
+    Ag, Bg = dev(A, "bf16"), dev(B, "bf16")
+    if epi == 4:
+        C0 = RNG.standard_normal((M, N)).astype(np.float32)
+        C = torch.from_numpy(C0).to(DEV)
+        ws = empty((max(1, ops.gemm_ws_bytes(TDT["bf16"], M, N, K, 4) // 4),), torch.float32)
+        ops.gemm(M, N, K, Ag, True, K, Bg, True, K, 4, C, N, accumulate=True, ws=ws)
+        assert_close(C, acc + C0, "f32", "fp32 out", tol=1e-5)
+        return
+    C, C2 = empty((M, N), "bf16"), empty((M, N), "bf16")
+    H = rounded(np.maximum(R, 0) ** 2, "bf16")
+    Rg = dev(H if epi == 7 else R, "bf16")
+    ops.gemm(M, N, K, Ag, True, K, Bg, True, K, epi, C, N, R=Rg if epi in (1, 3, 7) else None, ldr=N,
+             C2=C2 if epi == 2 else None)
+    want = {0: acc, 1: R + acc, 2: acc, 3: acc * 2.0 * np.maximum(R, 0), 6: np.maximum(acc, 0) ** 2,
+            7: acc * 2.0 * np.sqrt(H)}[epi]
+    assert_close(C, want, "bf16", f"epilogue {epi}")
+    if epi == 2:
+        assert_close(C2, np.maximum(acc, 0) ** 2, "bf16", "relu2")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_gemm_token_major_strided(dt):
     # both operands M/N-contiguous (the weight-gradient layout) with leading
