@@ -17,9 +17,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("GDB_LIB") or os.path.join(HERE, "libgdb.so")
 
 # the GDB_ABI_VERSION this binding's structures and signatures follow
-ABI_VERSION = 6
+ABI_VERSION = 7
 
-GDB_OK, GDB_EINVAL, GDB_EUNSUPPORTED, GDB_EHIP, GDB_EWORKSPACE = 0, -1, -2, -3, -4
+GDB_OK, GDB_EINVAL, GDB_EUNSUPPORTED, GDB_EHIP, GDB_EWORKSPACE, GDB_ENONFINITE = 0, -1, -2, -3, -4, -5
 GDB_F32, GDB_BF16 = 0, 1
 
 c_void_p, c_int32, c_float, c_size_t = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t

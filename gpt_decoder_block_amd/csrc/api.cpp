@@ -8,6 +8,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <initializer_list>
+#include <stdlib.h>
 #include <cmath>
 #include <string>
 
@@ -41,6 +43,31 @@ gdb_status fail(gdb_status st, const char* fmt, ...) {
     if ((p) == nullptr) return fail(GDB_EINVAL, "%s is NULL", #p);                         \
     if (((uintptr_t)(p)) & 15) return fail(GDB_EINVAL, "%s is not 16-byte aligned", #p);  \
   } while (0)
+
+// Debug check of the outputs (GDB_CHECK_FINITE in the environment, read on
+// every call): the first output holding a NaN or an infinity is named in the
+// error.  Off, it only clears the error text, as every successful call does.
+struct Output {
+  int dt;
+  const void* p;
+  size_t n;
+  const char* name;
+};
+bool check_finite_on() {
+  const char* e = getenv("GDB_CHECK_FINITE");
+  return e && *e && strcmp(e, "0") != 0;
+}
+gdb_status finished(std::initializer_list<Output> outs, hipStream_t s) {
+  if (check_finite_on()) {
+    for (const Output& o : outs) {
+      bool bad = false;
+      HIPCHK(any_nonfinite(o.dt, o.p, o.n, s, &bad));
+      if (bad) return fail(GDB_ENONFINITE, "%s holds NaN or Inf (GDB_CHECK_FINITE)", o.name);
+    }
+  }
+  g_err.clear();
+  return GDB_OK;
+}
 
 // Sequential carving of a caller buffer into 256-byte aligned pieces; with a
 // NULL base it only measures.
@@ -393,8 +420,7 @@ gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
     g = gemm_args(wf.hq, true, d.F, wf.wprojq, true, d.F, N, d.C, d.F, EPI_RESID, x_out, d.C);
     g.R = wf.x_mid; g.ldr = d.C; g.amax_a = sv.amax + 2; g.amax_b = sv.amax + 3;
     HIPCHK(gemm_fp8(dt, g, s));
-    g_err.clear();
-    return GDB_OK;
+    return finished({{dt, x_out, (size_t)N * d.C, "x_out"}}, s);
   }
   HIPCHK(rmsnorm_fwd(dt, wf.x_mid, sv.xn2, sv.r2, N, d.C, d.eps, s));
   // only h = relu(u)^2 is kept: the backward's ReLU^2 derivative 2*relu(u) is 2*sqrt(h)
@@ -403,8 +429,7 @@ gdb_status gdb_block_fwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
   g = gemm_args(sv.h, true, d.F, w->w_proj, true, d.F, N, d.C, d.F, EPI_RESID, x_out, d.C);
   g.R = wf.x_mid; g.ldr = d.C;
   HIPCHK(gemm(dt, g, s));
-  g_err.clear();
-  return GDB_OK;
+  return finished({{dt, x_out, (size_t)N * d.C, "x_out"}}, s);
 }
 
 // Data gradient dX [N, Nn] = dY [N, K] . W [K, Nn] (W row-major, the layout of
@@ -535,8 +560,12 @@ gdb_status gdb_block_bwd(const gdb_block_cfg* cfg, const gdb_block_weights* w, c
   } else {
     HIPCHK(rmsnorm_bwd(dt, wb.dxn, sv.xn1, sv.r1, wb.dx_mid, dx_in, N, d.C, s));
   }
-  g_err.clear();
-  return GDB_OK;
+  return finished({{dt, dx_in, (size_t)N * d.C, "dx_in"},
+                   {F32, dw->dw_qkv, (size_t)d.W3 * d.C, "dw_qkv"},
+                   {F32, dw->dw_o, (size_t)d.C * d.Q, "dw_o"},
+                   {F32, dw->dw_fc, (size_t)d.F * d.C, "dw_fc"},
+                   {F32, dw->dw_proj, (size_t)d.C * d.F, "dw_proj"}},
+                  s);
 }
 
 namespace {
@@ -593,8 +622,8 @@ gdb_status gdb_lm_head_ce_fwd_bwd(int32_t N, int32_t C, int32_t V, int32_t dtype
   HIPCHK(gemm(dtype, gemm_args(h.z, true, V, w_lm, false, C, N, C, V, EPI_STORE, h.dxf, C), s));
   HIPCHK(wgrad(dtype, h.z, V, h.xf, C, V, C, N, dw_lm, accumulate ? 1 : 0, h.partial, s));
   HIPCHK(rmsnorm_bwd(dtype, h.dxf, h.xf, h.rf, nullptr, dx, N, C, s));
-  g_err.clear();
-  return GDB_OK;
+  return finished({{F32, loss, 1, "loss"}, {dtype, dx, (size_t)N * C, "dx"}, {F32, dw_lm, (size_t)V * C, "dw_lm"}},
+                  s);
 }
 
 // ----------------------------------------------------------- building blocks

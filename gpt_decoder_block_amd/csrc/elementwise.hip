@@ -298,6 +298,52 @@ hipError_t stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s) 
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ debug scan
+// Flag word of the non-finite scan (one per device, as every __device__
+// variable).  The host takes its address with hipGetSymbolAddress.
+__device__ unsigned g_nonfinite_flag;
+
+__global__ void nonfinite_clear_k(unsigned* flag) { *flag = 0u; }
+
+// exponent field all ones (NaN or infinity), on the raw bits
+template <typename T>
+__global__ __launch_bounds__(256) void nonfinite_k(const T* __restrict__ x, size_t n, unsigned* flag) {
+  bool bad = false;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    if constexpr (sizeof(T) == 4) {
+      bad |= (__float_as_uint(x[i]) & 0x7F800000u) == 0x7F800000u;
+    } else {
+      bad |= (__builtin_bit_cast(unsigned short, x[i]) & 0x7F80u) == 0x7F80u;
+    }
+  }
+  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, 1u);
+}
+
+hipError_t any_nonfinite(int dt, const void* x, size_t n, hipStream_t s, bool* bad) {
+  *bad = false;
+  static unsigned* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!addr[dev]) {
+    e = hipGetSymbolAddress((void**)&addr[dev], HIP_SYMBOL(g_nonfinite_flag));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(nonfinite_clear_k, dim3(1), dim3(1), 0, s, addr[dev]);
+  if (n) {
+    const unsigned grid = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+    if (dt == F32) hipLaunchKernelGGL(nonfinite_k<float>, dim3(grid), dim3(256), 0, s, (const float*)x, n, addr[dev]);
+    else hipLaunchKernelGGL(nonfinite_k<bf16>, dim3(grid), dim3(256), 0, s, (const bf16*)x, n, addr[dev]);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  unsigned h = 0;
+  if ((e = hipMemcpyAsync(&h, addr[dev], sizeof(h), hipMemcpyDeviceToHost, s)) != hipSuccess) return e;
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+  *bad = h != 0u;
+  return hipSuccess;
+}
+
 hipError_t embed_fwd(int dt, const int32_t* ids, const void* wte, void* x, int N, int C, int V, hipStream_t s) {
   if (N == 0) return hipSuccess;
   dim3 g((N + 3) / 4), b(256);

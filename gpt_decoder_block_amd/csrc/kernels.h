@@ -19,6 +19,9 @@ inline int dt_size(int dt) { return dt == BF16 ? 2 : 4; }
 hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s);
 // dst = src over `bytes` (a multiple of 16): the bandwidth reference copy
 hipError_t stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+// Debug scan: *bad = whether any of the n elements (dt: F32 or BF16) is NaN or
+// infinite.  Synchronises s; the flag is a static device word.
+hipError_t any_nonfinite(int dt, const void* x, size_t n, hipStream_t s, bool* bad);
 // out [Cc, R] = in [R, Cc]^T, bf16, R and Cc multiples of 8, out not aliasing in
 hipError_t transpose_bf16(const void* in, int R, int Cc, void* out, hipStream_t s);
 // xn = x * r, r = 1/sqrt(mean(x^2)+eps) per row of [N, C]

@@ -44,6 +44,14 @@
  *     runtime (a failed launch) return GDB_EHIP.
  *   - Device pointers must be non-NULL and 16-byte aligned; feature sizes
  *     (C, head_dim, mlp_hidden, V) must be multiples of 8.
+ *   - Debug check: with the environment variable GDB_CHECK_FINITE set to a
+ *     value other than "0" (read on every call), gdb_block_fwd (x_out),
+ *     gdb_block_bwd (dx_in and the four weight gradients) and
+ *     gdb_lm_head_ce_fwd_bwd (loss, dx, dw_lm) scan their outputs after the
+ *     work and return GDB_ENONFINITE, naming the first tensor that holds a NaN
+ *     or an infinity.  The scan synchronises `stream` (the only entry points
+ *     that do, and only in this mode); its flag is a static device word, so
+ *     nothing is allocated.  Checked calls on one device must not overlap.
  */
 #ifndef GDB_H
 #define GDB_H
@@ -55,7 +63,7 @@
 extern "C" {
 #endif
 
-#define GDB_ABI_VERSION 6
+#define GDB_ABI_VERSION 7
 
 /* Scratch bytes that gdb_smear_bwd and gdb_backout_bwd need in `ws`. */
 #define GDB_EXTRAS_WS_BYTES ((size_t)1 << 20)
@@ -65,7 +73,8 @@ typedef enum {
   GDB_EINVAL = -1,        /* bad argument (shape, pointer, alignment, dtype) */
   GDB_EUNSUPPORTED = -2,  /* valid but not implemented (e.g. head_dim 96)     */
   GDB_EHIP = -3,          /* the HIP runtime reported an error                */
-  GDB_EWORKSPACE = -4     /* a size query's answer was not respected          */
+  GDB_EWORKSPACE = -4,    /* a size query's answer was not respected          */
+  GDB_ENONFINITE = -5     /* debug check (GDB_CHECK_FINITE): an output holds NaN or Inf */
 } gdb_status;
 
 typedef enum { GDB_F32 = 0, GDB_BF16 = 1 } gdb_dtype;

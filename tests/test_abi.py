@@ -50,6 +50,16 @@ def test_abi_version(L):
     assert m and int(m.group(1)) == L.lib().gdb_abi_version() == L.ABI_VERSION
 
 
+def test_status_codes(L):
+    # every gdb_status value the header declares has the same value in the binding
+    hdr = open(HEADER).read()
+    body = re.search(r"typedef enum \{(.*?)\} gdb_status;", hdr, re.S).group(1)
+    codes = dict((n, int(v)) for n, v in re.findall(r"(GDB_[A-Z]+) = (-?\d+)", body))
+    assert set(codes) == {"GDB_OK", "GDB_EINVAL", "GDB_EUNSUPPORTED", "GDB_EHIP", "GDB_EWORKSPACE", "GDB_ENONFINITE"}
+    for n, v in codes.items():
+        assert getattr(L, n) == v, n
+
+
 def _cfg(L, **kw):
     base = dict(B=2, T=64, C=256, n_head=2, n_kv_head=1, head_dim=128, mlp_hidden=1024, window=-1, dtype=1,
                 mlp_fp8=0, accumulate_wgrad=0, deterministic=0, eps=1e-6)
