@@ -109,3 +109,71 @@ def test_lm_head_ce_d24_full_size():
     e_dw = assert_close(dw, dw_rows * n / N, dt, "dw_lm")
     print(f"full-size head row losses {e_rows:.3e}", flush=True)
     print(f"full-size head loss {loss.item():.6f} ref {loss_ref:.6f} dx {e_dx:.3e} dw {e_dw:.3e}", flush=True)
+
+
+def test_block_d26_full_size_fp8_mixing():
+    """The d26 block (layer 0: residual mixing, fp8 MLP products; no value
+    embedding on even layers) at the full batch B=16, T=2048.  Only the
+    sampled sequences carry non-zero inputs (x, x0 and the upstream gradient),
+    so every other token's activations and gradients are exactly zero: the
+    per-tensor fp8 scales of the whole batch equal those of the sampled
+    sequences, which the oracle computes alone.  Bars: the fp8 bound 2q of the
+    block tests (q measured on the oracle with the quantiser off)."""
+    from gpu_util import fp8_bars
+    w = workload("d26")
+    l, rows = 0, [0, w.B - 1]
+    dt, B, T, C = w.dtype, w.B, w.T, w.C
+    N = B * T
+    print(f"full-size d26 block l={l} B={B} T={T} fp8={w.mlp_fp8} rows={rows}", flush=True)
+    p = {k: (rounded(v, dt) if np.ndim(v) else np.float32(v)) for k, v in draw_layer(w, l).items()}
+    assert "ve" not in p
+    def sampled(key, std):
+        a = np.zeros((B, T, C), dtype=np.float32)
+        a[rows] = rounded(draw_upstream(w, key, (len(rows), T, C), std), dt)
+        return a
+    x, x0, dy = sampled(100, 1.0), sampled(150, 1.0), sampled(200, 1.0)
+    ids = draw_ids(w)[:, :T]
+    cfg = ops.make_cfg(B, T, C, w.n_head, w.n_kv_head, w.head_dim, w.mlp_hidden, w.windows[l], TDT[dt], w.eps,
+                       mlp_fp8=w.mlp_fp8)
+    sv, wf, wb = ops.block_sizes(cfg)
+    saved = torch.empty(sv, dtype=torch.uint8, device=DEV)
+    wsf = torch.empty(wf, dtype=torch.uint8, device=DEV)
+    wsb = torch.empty(wb, dtype=torch.uint8, device=DEV)
+    W = [dev(p[k], dt) for k in ("w_qkv", "w_o", "w_fc", "w_proj")]
+    dW = [empty(t.shape, torch.float32) for t in W]
+    rope = ops.rope_table(T, w.head_dim, w.rope_base, DEV)
+    xg, x0g, out = dev(x.reshape(N, C), dt), dev(x0.reshape(N, C), dt), empty((N, C), dt)
+    lam = torch.tensor([p["resid_lambda"], p["x0_lambda"]], dtype=torch.float32, device=DEV)
+    idsg = torch.from_numpy(ids.reshape(-1).astype(np.int32)).to(DEV)
+    dlam = empty((2,), torch.float32)
+    dx0 = empty((N, C), torch.float32, fill=0.0)
+    ex = ops.block_extras(lam, x0g, xg, idsg, None, None)
+    dex = ops.block_extras_grads(dlam, dx0, None, None, accumulate_dx0=True)
+    ops.block_fwd(cfg, W, rope, xg, out, saved, wsf, ex)
+    dx = dev(dy.reshape(N, C), dt)
+    ops.block_bwd(cfg, W, rope, saved, dx, dx, dW, wsb, ex, dex)
+    torch.cuda.synchronize()
+    out_h, dx_h, dx0_h = host(out).reshape(B, T, C), host(dx).reshape(B, T, C), host(dx0).reshape(B, T, C)
+    others = np.setdiff1d(np.arange(B), rows)
+    assert not np.any(out_h[others]) and not np.any(dx_h[others]) and not np.any(dx0_h[others])
+    cos, sin = O.rope_tables(T, w.head_dim, w.rope_base)
+    pp = {k: np.asarray(v, dtype=np.float64) for k, v in p.items()}
+    s = np.array(rows)
+    x64, x064, dy64 = x[s].astype(np.float64), x0[s].astype(np.float64), dy[s].astype(np.float64)
+    o_out, c = O.block_forward(x64, pp, w, l, cos, sin, x0=x064, ids=ids[s])
+    o_dx, g = O.block_backward(dy64, c, pp, w, l, cos, sin, ids=ids[s])
+    we = w.with_(mlp_fp8=False)
+    oe, ce = O.block_forward(x64, pp, we, l, cos, sin, x0=x064, ids=ids[s])
+    dxe, ge = O.block_backward(dy64, ce, pp, we, l, cos, sin, ids=ids[s])
+    names = ("w_qkv", "w_o", "w_fc", "w_proj")
+    bars = fp8_bars({"x_out": (o_out, oe), "dx_in": (o_dx, dxe), "dx0": (g["x0"], ge["x0"]),
+                     "dlambdas": ([g["resid_lambda"], g["x0_lambda"]], [ge["resid_lambda"], ge["x0_lambda"]]),
+                     **{k: (g[k], ge[k]) for k in names}}, dt)
+    print("fp8 bars", {k: round(v, 4) for k, v in bars.items()}, flush=True)
+    errs = {"x_out": assert_close(out_h[s], o_out, dt, "x_out (sampled sequences)", bars["x_out"]),
+            "dx_in": assert_close(dx_h[s], o_dx, dt, "dx_in (sampled sequences)", bars["dx_in"]),
+            "dx0": assert_close(dx0_h[s], g["x0"], dt, "dx0 (sampled sequences)", bars["dx0"]),
+            "dlambdas": assert_close(dlam, [g["resid_lambda"], g["x0_lambda"]], dt, "dlambdas", bars["dlambdas"])}
+    for k, t in zip(names, dW):
+        errs[k] = assert_close(t, g[k], dt, "d" + k, bars[k])
+    print(f"full-size d26 block errs={errs}", flush=True)
