@@ -179,11 +179,11 @@ size_t wgrad_partial_floats(const BlockDims& d) {
   size_t m = 0;
   const int shapes[4][2] = {{d.C, d.F}, {d.F, d.C}, {d.C, d.Q}, {d.W3, d.C}};
   for (auto& sh : shapes) {
-    const int sp = gemm_splits(d.dt, sh[0], sh[1], d.N, EPI_F32);
-    if (sp > 1) m = std::max(m, (size_t)sp * sh[0] * sh[1]);
+    const SplitPlan pl = gemm_split_plan(d.dt, sh[0], sh[1], d.N);
+    if (pl.splits > 1 || pl.splits2 > 0) m = std::max(m, (size_t)plan_slices(pl) * sh[0] * sh[1]);
     if (d.fp8) {
-      const int s8 = gemm_splits(FP8, sh[0], sh[1], d.Np, EPI_F32);
-      if (s8 > 1) m = std::max(m, (size_t)s8 * sh[0] * sh[1]);
+      const SplitPlan p8 = gemm_split_plan(FP8, sh[0], sh[1], d.Np);
+      if (p8.splits > 1 || p8.splits2 > 0) m = std::max(m, (size_t)plan_slices(p8) * sh[0] * sh[1]);
     }
   }
   return m;
@@ -251,10 +251,14 @@ hipError_t wgrad(int dt, const void* A, int lda, const void* B, int ldb, int M, 
                  int accumulate, float* partial, hipStream_t s) {
   GemmArgs g = gemm_args(A, false, lda, B, false, ldb, M, N, K, EPI_F32, C, N);
   g.accumulate = accumulate;
-  g.splits = gemm_splits(dt, M, N, K, EPI_F32);
+  const SplitPlan pl = gemm_split_plan(dt, M, N, K);
+  g.splits = pl.splits;
+  g.split_cols = pl.split_cols; g.first1 = pl.first1; g.splits2 = pl.splits2;
   g.partial = partial;
   hipError_t e = gemm(dt, g, s);
-  if (e != hipSuccess || g.splits == 1) return e;
+  if (e != hipSuccess || (g.splits == 1 && g.splits2 == 0)) return e;
+  if (g.splits2 > 0)
+    return splitk_reduce2(partial, C, M, N, g.splits, g.split_cols, g.first1, g.splits2, accumulate, s);
   return splitk_reduce(partial, C, g.splits, (size_t)M * N, accumulate, s);
 }
 
@@ -264,11 +268,15 @@ hipError_t wgrad_fp8(const uint8_t* A, const float* amax_a, const uint8_t* B, co
                      int K, float* C, int accumulate, float* partial, hipStream_t s) {
   GemmArgs g = gemm_args(A, true, K, B, true, K, M, N, K, EPI_F32, C, N);
   g.accumulate = accumulate;
-  g.splits = gemm_splits(FP8, M, N, K, EPI_F32);
+  const SplitPlan pl = gemm_split_plan(FP8, M, N, K);
+  g.splits = pl.splits;
+  g.split_cols = pl.split_cols; g.first1 = pl.first1; g.splits2 = pl.splits2;
   g.partial = partial;
   g.amax_a = amax_a; g.amax_b = amax_b;
   hipError_t e = gemm_fp8(BF16, g, s);  // fp32 output: the element type of C is fixed
-  if (e != hipSuccess || g.splits == 1) return e;
+  if (e != hipSuccess || (g.splits == 1 && g.splits2 == 0)) return e;
+  if (g.splits2 > 0)
+    return splitk_reduce2(partial, C, M, N, g.splits, g.split_cols, g.first1, g.splits2, accumulate, s);
   return splitk_reduce(partial, C, g.splits, (size_t)M * N, accumulate, s);
 }
 
@@ -586,8 +594,8 @@ void carve_head(int N, int C, int V, int dt, Carver& c, HeadWs& h) {
   h.z = c.take<char>((size_t)N * V * s);
   h.row_loss = c.take<float>((size_t)N * 4);
   h.dxf = c.take<char>((size_t)N * C * s);
-  const int sp = gemm_splits(dt, V, C, N, EPI_F32);
-  h.partial = c.take<float>(sp > 1 ? (size_t)sp * V * C * 4 : 0);
+  const SplitPlan pl = gemm_split_plan(dt, V, C, N);
+  h.partial = c.take<float>(pl.splits > 1 || pl.splits2 > 0 ? (size_t)plan_slices(pl) * V * C * 4 : 0);
 }
 }  // namespace
 
@@ -667,8 +675,12 @@ gdb_status gdb_gemm_ws_bytes(int32_t dtype, int32_t M, int32_t N, int32_t K, int
   if (dtype != GDB_F32 && dtype != GDB_BF16) return fail(GDB_EINVAL, "unknown dtype %d", dtype);
   if (M < 0 || N < 0 || K < 0) return fail(GDB_EINVAL, "negative size");
   if (!public_epi(epi)) return fail(GDB_EINVAL, "unknown epilogue %d", epi);
-  const int sp = gemm_splits(dtype, M, N, K, epi);
-  if (ws_bytes) *ws_bytes = sp > 1 ? (size_t)sp * M * N * 4 : 0;
+  size_t b = 0;
+  if (epi == EPI_F32) {
+    const SplitPlan pl = gemm_split_plan(dtype, M, N, K);
+    if (pl.splits > 1 || pl.splits2 > 0) b = (size_t)plan_slices(pl) * M * N * 4;
+  }
+  if (ws_bytes) *ws_bytes = b;
   g_err.clear();
   return GDB_OK;
 }
@@ -698,11 +710,18 @@ gdb_status gdb_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* 
   GemmArgs g = gemm_args(A, a_kmajor != 0, lda, B, b_kmajor != 0, ldb, M, N, K, epi, C, ldc);
   g.R = R; g.ldr = ldr; g.C2 = C2; g.accumulate = accumulate ? 1 : 0;
   if (epi == EPI_F32) {
-    g.splits = gemm_splits(dtype, M, N, K, epi);
-    if (g.splits > 1) CHECK_PTR(ws);
+    const SplitPlan pl = gemm_split_plan(dtype, M, N, K);
+    g.splits = pl.splits;
+    g.split_cols = pl.split_cols; g.first1 = pl.first1; g.splits2 = pl.splits2;
+    const bool split = g.splits > 1 || g.splits2 > 0;
+    if (split) CHECK_PTR(ws);
     g.partial = (float*)ws;
     HIPCHK(gemm(dtype, g, (hipStream_t)stream));
-    if (g.splits > 1) HIPCHK(splitk_reduce(g.partial, (float*)C, g.splits, (size_t)M * N, g.accumulate, (hipStream_t)stream));
+    if (g.splits2 > 0)
+      HIPCHK(splitk_reduce2(g.partial, (float*)C, M, N, g.splits, g.split_cols, g.first1, g.splits2, g.accumulate,
+                            (hipStream_t)stream));
+    else if (split)
+      HIPCHK(splitk_reduce(g.partial, (float*)C, g.splits, (size_t)M * N, g.accumulate, (hipStream_t)stream));
   } else {
     HIPCHK(gemm(dtype, g, (hipStream_t)stream));
   }

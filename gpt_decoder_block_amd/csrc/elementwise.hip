@@ -701,6 +701,30 @@ __global__ __launch_bounds__(256) void splitk_reduce_k(const float* __restrict__
   *(f32x4*)(C + i) = acc;
 }
 
+// two-phase plan: the slice count depends on the element's tile row or column
+__global__ __launch_bounds__(256) void splitk_reduce2_k(const float* __restrict__ part, float* __restrict__ C, int N,
+                                                         size_t MN, int splits, int split_cols, int first1,
+                                                         int splits2, int accumulate) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= MN) return;  // N is a multiple of 4, so the 4 elements share a row and a 256-column tile
+  const size_t m = i / N, n = i - m * N;
+  const int t = split_cols ? (int)(n >> 8) : (int)(m >> 8);
+  const int ns = t < first1 ? splits : splits2;
+  f32x4 acc = accumulate ? *(const f32x4*)(C + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int z = 0; z < ns; ++z) acc += *(const f32x4*)(part + (size_t)z * MN + i);
+  *(f32x4*)(C + i) = acc;
+}
+
+hipError_t splitk_reduce2(const float* partial, float* C, int M, int N, int splits, int split_cols, int first1,
+                          int splits2, int accumulate, hipStream_t s) {
+  const size_t MN = (size_t)M * N;
+  if (MN == 0) return hipSuccess;
+  const size_t blocks = (MN / 4 + 255) / 256;
+  hipLaunchKernelGGL(splitk_reduce2_k, dim3((unsigned)blocks), dim3(256), 0, s, partial, C, N, MN, splits, split_cols,
+                     first1, splits2, accumulate);
+  return hipGetLastError();
+}
+
 hipError_t splitk_reduce(const float* partial, float* C, int splits, size_t MN, int accumulate, hipStream_t s) {
   if (MN == 0) return hipSuccess;
   size_t blocks = (MN / 4 + 255) / 256;

@@ -405,8 +405,29 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_k(GemmArgs p) {
   constexpr int KSTEP = F8 ? BK8 : BK;  // elements per K step
   __shared__ __attribute__((aligned(16))) bf16 smem[2][2][TILE_ELEMS];  // [stage][A|B]
   const int nbm = (p.M + BM - 1) / BM, nbn = (p.N + BN - 1) / BN;
-  int tm, tn;
-  tile_coords(blockIdx.x, nbm, nbn, tm, tn);
+  // tile and K range: one phase (blockIdx.x the tile, blockIdx.y the split)
+  // or two (blockIdx.x runs over the first phase's pieces, split-major, then
+  // the second's; each phase is a band of whole tile rows or columns)
+  int tm, tn, split = blockIdx.y, nsplit = p.splits;
+  if (p.splits2 > 0) {
+    const int bid = blockIdx.x;
+    const int r1 = p.split_cols ? nbm : p.first1, c1 = p.split_cols ? p.first1 : nbn;
+    const int t1 = r1 * c1, n1 = t1 * p.splits;
+    if (bid < n1) {
+      split = bid / t1;
+      tile_coords(bid - split * t1, r1, c1, tm, tn);
+    } else {
+      const int r2 = p.split_cols ? nbm : nbm - p.first1, c2 = p.split_cols ? nbn - p.first1 : nbn;
+      const int t2 = r2 * c2, b2 = bid - n1;
+      split = b2 / t2;
+      tile_coords(b2 - split * t2, r2, c2, tm, tn);
+      if (p.split_cols) tn += p.first1;
+      else tm += p.first1;
+      nsplit = p.splits2;
+    }
+  } else {
+    tile_coords(blockIdx.x, nbm, nbn, tm, tn);
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   if (blockIdx.z) {  // item of a batched launch
     const size_t z = blockIdx.z;
@@ -416,8 +437,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_k(GemmArgs p) {
     if (p.R) p.R = (const char*)p.R + z * p.bsR * sizeof(OT);
   }
   // split-K range
-  const int ksplit = ((p.K + p.splits * KSTEP - 1) / (p.splits * KSTEP)) * KSTEP;
-  const int kbeg = min(p.K, (int)blockIdx.y * ksplit);
+  const int ksplit = ((p.K + nsplit * KSTEP - 1) / (nsplit * KSTEP)) * KSTEP;
+  const int kbeg = min(p.K, split * ksplit);
   const int kend = min(p.K, kbeg + ksplit);
   const int nk = (kend - kbeg + KSTEP - 1) / KSTEP;
 
@@ -932,8 +953,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_k(GemmArgs p) {
         if (EPI == EPI_F32) {
           float* C = (float*)p.C;
           size_t off = (size_t)m * p.ldc + n;
-          if (p.splits > 1) {
-            C = p.partial + (size_t)blockIdx.y * p.M * p.N;
+          if (p.splits > 1 || p.splits2 > 0) {
+            C = p.partial + (size_t)split * p.M * p.N;
             off = (size_t)m * p.N + n;
           } else if (p.accumulate) {
             const f32x4 o = *(const f32x4*)(C + off);
@@ -1159,11 +1180,64 @@ int gemm_splits(int dt, int M, int N, int K, int epi) {
   return best;
 }
 
+// Two-phase split-K.  With one split count for every tile, the weight
+// gradients' tile counts leave the last round of workgroups part-full (144
+// tiles of a 6144 x 1536 product: 5 splits, 720 workgroups, 2.8 rounds).  Two
+// bands of whole tile rows or columns with two split counts can fill the
+// rounds (126 tiles x 2 splits, then 18 x 14 short pieces), at the price of
+// more partial slices.  The plan takes the cheapest band and split counts by
+// the same cost model (rounds x steps per piece + partial traffic), the longer
+// pieces first, and only when the model gains over 3%.
+#ifndef GEMM_TWO_PHASE
+#define GEMM_TWO_PHASE 1
+#endif
+SplitPlan gemm_split_plan(int dt, int M, int N, int K) {
+  SplitPlan pl{gemm_splits(dt, M, N, K, EPI_F32), 0, 0, 0};
+  if (!GEMM_TWO_PHASE || dt == F32 || M <= 0 || N <= 0 || K <= 0) return pl;
+  const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+  const int kstep = dt == FP8 ? BK8 : BK;
+  const int nsteps = (K + kstep - 1) / kstep;
+  const int cus = device_cus();
+  auto cost = [&](int tiles, int sp, bool part) {
+    if (tiles == 0) return 0.0;
+    return (double)((tiles * sp + cus - 1) / cus) * ((nsteps + sp - 1) / sp) + (part ? 0.066 * tiles * sp : 0.0);
+  };
+  const double one = cost(nbm * nbn, pl.splits, pl.splits > 1);
+  double best = 0.97 * one;
+  for (int cols = 0; cols < 2; ++cols) {
+    const int bands = cols ? nbn : nbm, other = cols ? nbm : nbn;
+    for (int f1 = 1; f1 < bands; ++f1)
+      for (int s1 = 1; s1 <= 32; ++s1) {
+        if (s1 > 1 && nsteps / s1 < 4) break;
+        for (int s2 = s1; s2 <= 32; ++s2) {
+          if (s2 > 1 && nsteps / s2 < 4) break;
+          const double c = cost(f1 * other, s1, true) + cost((bands - f1) * other, s2, true);
+          if (c < best - 1e-9) {
+            best = c;
+            pl = SplitPlan{s1, cols, f1, s2};
+          }
+        }
+      }
+  }
+  return pl;
+}
+
+// workgroups of a launch: one phase (tiles, splits) or two
+static dim3 gemm_grid(const GemmArgs& a) {
+  const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
+  if (a.splits2 > 0) {
+    const int r1 = a.split_cols ? nbm : a.first1, c1 = a.split_cols ? a.first1 : nbn;
+    const int t2 = nbm * nbn - r1 * c1;
+    return dim3(r1 * c1 * a.splits + t2 * a.splits2, 1);
+  }
+  return dim3(nbm * nbn, a.splits);
+}
+
 hipError_t gemm_fp8(int out_dt, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   if (!a.a_kmajor || !a.b_kmajor || !a.amax_a || !a.amax_b) return hipErrorInvalidValue;
-  const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
-  const dim3 g(nbm * nbn, a.splits);
+  if (a.splits2 > 0 && (a.epi != EPI_F32 || a.batch > 1)) return hipErrorInvalidValue;
+  const dim3 g = gemm_grid(a);
   if (out_dt == F32 && a.epi != EPI_F32) return launch_bf16<true, true, true, float, 8>(a, g, s);
   return launch_bf16<true, true, true, bf16, 8>(a, g, s);
 }
@@ -1171,9 +1245,9 @@ hipError_t gemm_fp8(int out_dt, const GemmArgs& a, hipStream_t s) {
 hipError_t gemm(int dt, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   if (a.batch > 1 && a.splits > 1) return hipErrorInvalidValue;  // a batch runs unsplit
+  if (a.splits2 > 0 && (dt != BF16 || a.epi != EPI_F32 || a.batch > 1)) return hipErrorInvalidValue;
   if (dt == BF16) {
-    const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
-    dim3 g(nbm * nbn, a.splits);
+    dim3 g = gemm_grid(a);
     // 8 waves (two per SIMD, one wave's MFMAs running while the other waits
     // on its copies or LDS reads): measured 2-10% faster than 4 with both
     // operands copied straight into LDS, 4-6% with an M/N-contiguous operand

@@ -47,6 +47,11 @@ hipError_t ce_fwd_bwd(int dt, void* z, const int32_t* tgt, float* row_loss, int 
 hipError_t loss_reduce(const float* row_loss, float* loss, int N, hipStream_t s);
 // C (+)= sum_z partial[z] over `splits` fp32 [M, N] slices
 hipError_t splitk_reduce(const float* partial, float* C, int splits, size_t MN, int accumulate, hipStream_t s);
+// the same for a two-phase plan: element (m, n) of C [M, N] sums the first
+// `splits` slices if its tile row (split_cols == 0: m / 256) or tile column
+// (n / 256) is below first1, else the first `splits2`
+hipError_t splitk_reduce2(const float* partial, float* C, int M, int N, int splits, int split_cols, int first1,
+                          int splits2, int accumulate, hipStream_t s);
 
 // ----------------------------------------------------------------------- GEMM
 // C[m, n] = sum_k A(m, k) * B(n, k)
@@ -81,8 +86,14 @@ struct GemmArgs {
   // writes at these element offsets times z (0 or 1: one item)
   int batch;
   long long bsA, bsB, bsC, bsR;
-  float* partial;      // EPI_F32 split-K scratch [splits, M, N] or null
+  float* partial;      // EPI_F32 split-K scratch [max(splits, splits2), M, N] or null
   int splits;          // >= 1
+  // two-phase split-K (EPI_F32, bf16 and fp8 paths): when splits2 > 0, the
+  // tiles of the first `first1` tile rows (split_cols == 0) or tile columns
+  // (split_cols == 1) take `splits` K ranges and the other tiles `splits2`,
+  // in one launch whose first-phase workgroups come first; every tile then
+  // writes partials, which splitk_reduce sums with the same phase rule
+  int split_cols, first1, splits2;
   const float* amax_a; // fp8: per-tensor amax of A and B (scales amax/448)
   const float* amax_b;
   // EPI_RELU2 / EPI_SQR / EPI_DRELU2 / EPI_DSQR: if set, atomically raised to
@@ -99,6 +110,14 @@ hipError_t gemm(int dt, const GemmArgs& a, hipStream_t s);
 hipError_t gemm_fp8(int out_dt, const GemmArgs& a, hipStream_t s);
 // split-K factor the GEMM will use for this shape (dt FP8 for gemm_fp8)
 int gemm_splits(int dt, int M, int N, int K, int epi);
+// split-K plan of an EPI_F32 product (dt BF16 or FP8): one phase (splits2 ==
+// 0, splits = gemm_splits) or two phases as GemmArgs describes them
+struct SplitPlan {
+  int splits, split_cols, first1, splits2;
+};
+SplitPlan gemm_split_plan(int dt, int M, int N, int K);
+// fp32 partial slices a plan writes ([slices, M, N])
+inline int plan_slices(const SplitPlan& p) { return p.splits2 > p.splits ? p.splits2 : p.splits; }
 
 // ------------------------------------------------------------ fp8 quantiser
 // amax[0] = max |x| over n elements (x dtype dt; n a multiple of 8); amax is

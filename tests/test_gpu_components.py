@@ -125,6 +125,27 @@ def test_gemm_splitk_large_k(dt):
     assert_close(C, A.astype(np.float64).T @ B.astype(np.float64), "f32", "split-K", tol=1e-5)
 
 
+@pytest.mark.parametrize("M,N,K,accumulate", [(1528, 6136, 32704, False), (6136, 1528, 32704, True),
+                                               (4600, 1528, 32704, False)])
+def test_gemm_bf16_two_phase_splitk(M, N, K, accumulate):
+    # weight-gradient shapes (token-major operands, long K) whose split-K plan
+    # has two phases: bands of tile columns, of tile rows and a third split
+    # pair; ragged M and N, the fp32 output accumulated onto a prior value in
+    # one case
+    print(f"gemm two-phase split-K M={M} N={N} K={K} accumulate={accumulate}", flush=True)
+    g = np.random.default_rng(2024)
+    A = rounded(g.standard_normal((K, M), dtype=np.float32), "bf16")
+    B = rounded(g.standard_normal((K, N), dtype=np.float32), "bf16")
+    ws = empty((max(1, ops.gemm_ws_bytes(TDT["bf16"], M, N, K, 4) // 4),), torch.float32)
+    C0 = g.standard_normal((M, N), dtype=np.float32)
+    C = torch.from_numpy(C0).to(DEV)
+    ops.gemm(M, N, K, dev(A, "bf16"), False, M, dev(B, "bf16"), False, N, 4, C, N, accumulate=accumulate, ws=ws)
+    ref = A.astype(np.float64).T @ B.astype(np.float64)
+    if accumulate:
+        ref += C0
+    assert_close(C, ref, "f32", "two-phase split-K", tol=1e-5)
+
+
 def test_gemm_bf16_multi_tile_exact_shapes():
     # full 256x256 tiles plus XCD remap over many tiles
     M, N, K = 1024, 2048, 768
