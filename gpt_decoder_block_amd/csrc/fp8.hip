@@ -22,13 +22,27 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 // max |x| over n elements: one atomic max per workgroup on the float's bit
 // pattern (non-negative floats order like their bits, so the result does not
 // depend on the order).
+// One workgroup per CU at most (256), each thread with four 16-byte loads in
+// flight per iteration: every workgroup ends in an atomic on the one result
+// word.  Against 2048 workgroups the amax + quantise of a d26 weight went
+// 36.7 -> 17.7 us, of a [32768, 1664] gradient 64.6 -> 46.0 us.
 template <typename T>
 __global__ __launch_bounds__(256) void amax_k(const T* __restrict__ x, size_t n, unsigned* __restrict__ out) {
   constexpr int VN = V16<T>::n;
   __shared__ float red[4];
   float m = 0.f;
-  const size_t nv = n / VN;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < nv; i += (size_t)gridDim.x * 256) {
+  const size_t nv = n / VN, stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < nv; i += 4 * stride) {
+    float v[4][VN];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ld16(x + (i + u * stride) * VN, v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < VN; ++e) m = fmaxf(m, fabsf(v[u][e]));
+  }
+  for (; i < nv; i += stride) {
     float v[VN];
     ld16(x + i * VN, v);
 #pragma unroll
@@ -139,7 +153,7 @@ hipError_t fp8_amax(int dt, const void* x, size_t n, float* amax, hipStream_t s)
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n == 0) return e;
   const size_t nv = n / (dt == BF16 ? 8 : 4);
-  const unsigned grid = (unsigned)std::min<size_t>((nv + 255) / 256, 2048);
+  const unsigned grid = (unsigned)std::min<size_t>((nv + 255) / 256, 256);
   if (dt == BF16) hipLaunchKernelGGL(amax_k<bf16>, dim3(grid), dim3(256), 0, s, (const bf16*)x, n, (unsigned*)amax);
   else hipLaunchKernelGGL(amax_k<float>, dim3(grid), dim3(256), 0, s, (const float*)x, n, (unsigned*)amax);
   return hipGetLastError();
