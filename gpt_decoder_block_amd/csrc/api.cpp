@@ -825,12 +825,18 @@ gdb_status gdb_qk_norm_rope_bwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, in
   return GDB_OK;
 }
 
+// The bf16 attention kernels address one sequence's rows by 32-bit byte
+// offsets from the sequence's first row.
+static bool seq_fits_32bit(int T, int ld) { return (size_t)T * (size_t)ld * 2 <= 0x7FFFFF00ull; }
+
 gdb_status gdb_attention_fwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t D, int32_t window,
                              int32_t qk_normed, int32_t dtype, const void* qkv, int32_t ld, void* o, int32_t ldo,
                              float* lse, void* stream) {
   gdb_status st = check_attn(B, T, H, Hkv, D, window, dtype);
   if (st != GDB_OK) return st;
   if (ld < (H + 2 * Hkv) * D || ld % 8 || ldo < H * D || ldo % 8) return fail(GDB_EINVAL, "bad leading dimension");
+  if (dtype == GDB_BF16 && !seq_fits_32bit(T, ld))
+    return fail(GDB_EUNSUPPORTED, "bf16 attention: a sequence's qkv rows (T * ld * 2 bytes) must span under 2 GiB");
   CHECK_PTR(qkv); CHECK_PTR(o); CHECK_PTR(lse);
   AttnArgs at{};
   at.B = B; at.T = T; at.H = H; at.Hkv = Hkv; at.D = D; at.window = window >= T - 1 ? -1 : window;
@@ -849,6 +855,9 @@ gdb_status gdb_attention_bwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32
   if (ld < (H + 2 * Hkv) * D || ld % 8 || ldo < H * D || ldo % 8 || lddo < H * D || lddo % 8 ||
       lddq < (H + 2 * Hkv) * D || lddq % 8)
     return fail(GDB_EINVAL, "bad leading dimension");
+  if (dtype == GDB_BF16 && (!seq_fits_32bit(T, ld) || !seq_fits_32bit(T, lddo)))
+    return fail(GDB_EUNSUPPORTED,
+                "bf16 attention: a sequence's qkv and dO rows (T * ld * 2, T * lddo * 2 bytes) must span under 2 GiB");
   CHECK_PTR(qkv); CHECK_PTR(o); CHECK_PTR(lse); CHECK_PTR(dout); CHECK_PTR(dqkv); CHECK_PTR(delta);
   AttnArgs at{};
   at.B = B; at.T = T; at.H = H; at.Hkv = Hkv; at.D = D; at.window = window >= T - 1 ? -1 : window;

@@ -392,13 +392,17 @@ gdb_status gdb_qk_norm_rope_bwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, in
  * qk_normed != 0 promises that every q and k head vector has RMS <= 1 (the
  * output of the QK RMS-norm, as in gdb_block_fwd); then |score| <= sqrt(D)
  * and the kernel uses that fixed softmax offset instead of a running max.
- * With larger vectors and qk_normed != 0 the result is undefined. */
+ * With larger vectors and qk_normed != 0 the result is undefined.
+ * bf16: one sequence's qkv rows must span under 2 GiB (T * ld * 2 bytes),
+ * else GDB_EUNSUPPORTED. */
 gdb_status gdb_attention_fwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t D, int32_t window,
                              int32_t qk_normed, int32_t dtype, const void* qkv, int32_t ld, void* o,
                              int32_t ldo, float* lse, void* stream);
 /* Attention backward: from dO [B*T, lddo] writes dq, dk, dv into dqkv [B*T, lddq]
  * at the same column offsets as qkv (dk, dv summed over the query heads that
- * share a K/V head). delta: float32 scratch [B, H, T]. */
+ * share a K/V head). delta: float32 scratch [B, H, T].  bf16: one sequence's
+ * qkv rows and dO rows must each span under 2 GiB (T * ld * 2 and
+ * T * lddo * 2 bytes), else GDB_EUNSUPPORTED. */
 gdb_status gdb_attention_bwd(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t D, int32_t window,
                              int32_t dtype, const void* qkv, int32_t ld, const void* o, int32_t ldo,
                              const float* lse, const void* dout, int32_t lddo, void* dqkv, int32_t lddq,

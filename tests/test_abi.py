@@ -227,6 +227,11 @@ def test_gemm_and_attention_validation(L):
     assert st == L.GDB_EINVAL and "multiple of Hkv" in lib.gdb_last_error().decode()
     st = lib.gdb_attention_fwd(1, 64, 2, 1, 64, -1, 0, 1, al, 256, al, 128, al, None)
     assert st == L.GDB_EUNSUPPORTED
+    # bf16 kernels address a sequence's rows with 32-bit byte offsets
+    st = lib.gdb_attention_fwd(1, 4096, 2, 1, 128, -1, 0, 1, al, 262144, al, 256, al, None)
+    assert st == L.GDB_EUNSUPPORTED and "2 GiB" in lib.gdb_last_error().decode()
+    st = lib.gdb_attention_bwd(1, 4096, 2, 1, 128, -1, 1, al, 512, al, 256, al, al, 262144, al, 512, al, None)
+    assert st == L.GDB_EUNSUPPORTED and "dO rows" in lib.gdb_last_error().decode()
     st = lib.gdb_lm_head_ce_fwd_bwd(8, 128, 100, 1, 1e-6, al, al, al, al, None, al, al, 0, al, None)
     assert st == L.GDB_EINVAL and "multiples of 8" in lib.gdb_last_error().decode()
     st = lib.gdb_lm_head_ce_fwd_bwd(8, 128, 128, 1, 1e-6, al, al, al, al, al + 2, al, al, 0, al, None)
