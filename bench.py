@@ -358,6 +358,43 @@ def kernel_figures(w, st, reps, torch, ops):
     out["cross_entropy"] = {"ms": tce * 1e3, "GBps": by / tce / 1e9, "frac_hbm_peak": by / tce / PEAK_HBM}
     del flush
     del z0, z
+    # embedding-gradient scatter (B0) and value-embedding table gradient (E2),
+    # with uniform ids and with Zipf(1.0) ids (many tokens on a few rows: a
+    # stand-in for natural text's contention), float32 atomics and the
+    # deterministic path (tokens sorted by id, each row summed in token order).
+    # B0's bytes: dx0 read once plus a float32 read-modify-write per token row;
+    # the overwrite's zero fill of the table is inside the timed call.
+    from seeded_inputs import draw_ids_zipf
+    ids_by = {"uniform": tg,
+              "zipf1": torch.from_numpy(draw_ids_zipf(w).reshape(-1)[:N].astype(np.int32)).to(dev)}
+    dx0 = rnd(N, C)
+    dwte = torch.empty(V, C, dtype=torch.float32, device=dev)
+    wse = torch.empty(max(ops.embed_bwd_ws_bytes(N, True), 16), dtype=torch.uint8, device=dev)
+    by = N * C * s + 8.0 * N * C
+    emb = {"shape": [N, C, V], "bytes": by}
+    for kind, ids in ids_by.items():
+        for det in (False, True):
+            t = ev_time(lambda: ops.embed_bwd(ids, dx0, dwte, ws=wse if det else None), reps, torch)
+            emb[f"{kind}_{'deterministic' if det else 'atomic'}"] = {
+                "ms": t * 1e3, "GBps": by / t / 1e9, "frac_hbm_peak": by / t / PEAK_HBM}
+    out["embed_bwd"] = emb
+    del dwte, wse
+    nc, voff = w.ve_gate_channels, (H + Hkv) * D
+    dq_ve, ve_t = rnd(N, W3), rnd(V, Hkv * D)
+    s_save = torch.randn(N, Hkv, generator=g, device=dev, dtype=torch.float32)
+    xn_ve, dxn_ve, wg = rnd(N, C), rnd(N, C), rnd(Hkv, nc)
+    dve = torch.empty(V, Hkv * D, dtype=torch.float32, device=dev)
+    dwg = torch.empty(Hkv, nc, dtype=torch.float32, device=dev)
+    vef = {"shape": [N, Hkv, D, V, nc]}
+    for det in (False, True):
+        wsv = torch.empty(max(ops.ve_bwd_ws_bytes(N, Hkv, nc, det), 16), dtype=torch.uint8, device=dev)
+        for kind, ids in ids_by.items():
+            t = ev_time(lambda: ops.ve_bwd(Hkv, D, dq_ve, voff, ids, ve_t, s_save, xn_ve, dxn_ve, wg, dve, dwg, wsv,
+                                           deterministic=det), reps, torch)
+            vef[f"{kind}_{'deterministic' if det else 'atomic'}"] = {"ms": t * 1e3}
+        del wsv
+    out["value_embed_bwd"] = vef
+    del dq_ve, ve_t, s_save, xn_ve, dxn_ve, wg, dve, dwg, dx0, ids_by
     # decode attention (inference step, bandwidth): the workload's B sequences
     # with T cached positions, one new query each; every visible K and V row
     # read once (a window keeps only the last window+1 rows)

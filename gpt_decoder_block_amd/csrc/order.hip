@@ -7,8 +7,8 @@
 // float atomics the order of those additions, and so the rounding, changes
 // from run to run.  Here the tokens are first sorted by id (a stable LSD radix
 // sort on 8-bit digits, so tokens of one id stay in token order), then one
-// wavefront per table row adds that row's tokens in sorted order: the result
-// is the same bits on every run.
+// wavefront per table row and block of columns adds that row's tokens in
+// sorted order: the result is the same bits on every run.
 //
 // Radix pass (digit = 8 bits of the clamped id):
 //   hist:    each workgroup counts the digits of its tile of ORD_TILE keys;
@@ -17,6 +17,7 @@
 //            ranks each key among equal digits (wave ballots on the 8 digit
 //            bits, then the waves in order), so equal digits keep their order.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -130,52 +131,127 @@ __global__ __launch_bounds__(ORD_THREADS) void ord_scatter_k(const int32_t* __re
   }
 }
 
-// first index j in [0, N) with key[j] >= v (keys sorted ascending)
-__device__ __forceinline__ int lower_bound(const int32_t* __restrict__ key, int N, int v) {
-  int lo = 0, hi = N;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (key[mid] < v) lo = mid + 1;
-    else hi = mid;
+// Lanes 0-31 find the first index j in [0, N) with key[j] >= t0, lanes 32-63
+// the first with key[j] >= t1 (keys sorted ascending), both at once: each
+// round, a half's 32 lanes probe 32 evenly spaced keys of its remaining range
+// and its first probe at or above the target narrows the range to one gap; a
+// range of at most 32 keys is settled in one round.  N = 32768 takes four
+// rounds of one load per lane (binary searches by one lane: two chains of
+// fifteen dependent loads).  Each half returns its own index.
+__device__ __forceinline__ int wave_bounds(const int32_t* __restrict__ key, int N, int t0, int t1, int l) {
+  const int h = l >> 5, ll = l & 31;
+  const int t = h ? t1 : t0;
+  int lo = 0, hi = N;  // the half's answer lies in [lo, hi]
+  while (__any(lo < hi)) {
+    const int len = hi - lo;
+    const int step = len > 32 ? (len + 31) >> 5 : 1;
+    const int p = lo + ll * step;
+    const unsigned long long m = __ballot(p >= hi || key[p] >= t);
+    const unsigned mh = (unsigned)(m >> (32 * h));
+    const int f = mh ? __ffs((int)mh) - 1 : 32;  // the half's first probe at or above t
+    if (len > 32) {
+      const int nlo = f == 0 ? lo : lo + (f - 1) * step + 1;
+      hi = f == 0 ? lo : (f < 32 ? min(hi, lo + f * step) : hi);
+      lo = nlo;
+    } else {
+      lo = hi = f < 32 ? lo + f : hi;
+    }
   }
   return lo;
 }
 
-// One wavefront per table row v: out[v, c] (+)= sum over the row's tokens n,
-// in sorted (token) order, of g(n, c) * x[n*ldx + xoff + c], c < width, with
-// g = 3*sigmoid(s[n*G + c/D]) when gate logits s are given, else 1.
-template <typename T>
+// One wavefront per (table row v, block of 64*VN columns): out[v, c] (+)= the
+// sum over the row's tokens n, in sorted (token) order, of
+// g(n, c) * x[n*ldx + xoff + c], c < width, with g = 3*sigmoid(s[n*G + c/D])
+// when gate logits s are given, else 1.  The rows of SEG_U tokens are loaded
+// together and then added one after another, so a row that many tokens share
+// (natural text's frequent ids) costs one memory latency per SEG_U tokens
+// rather than per token; the rest of a row goes in batches of 4.  The
+// additions keep the token order whatever the batching.
+constexpr int SEG_U = 16;
+template <typename T, bool GATE, int U>
+__device__ __forceinline__ void seg_batch(int myn, int cnt, const T* __restrict__ x, int ldx, int xoff, int cl,
+                                          const float* __restrict__ s, int G, int D, float* acc) {
+  constexpr int VN = V16<T>::n;
+  typedef typename std::conditional<sizeof(T) == 2, bf16x8, f32x4>::type Raw;
+  Raw raw[U];
+  float gs[U];
+  // every load issued before the first addition (tokens past cnt re-read the
+  // batch's first row and are not added)
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int n = __shfl(myn, u < cnt ? u : 0, 64);
+    raw[u] = *(const Raw*)(x + (size_t)n * ldx + xoff + cl);
+    if (GATE) gs[u] = s[(size_t)n * G + cl / D];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of every addition
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (u < cnt) {  // wave-uniform
+      const float g = GATE ? 3.0f / (1.0f + __expf(-gs[u])) : 1.0f;
+#pragma unroll
+      for (int e = 0; e < VN; ++e) acc[e] += g * (float)raw[u][e];
+    }
+  }
+}
+
+template <typename T, bool GATE>
 __global__ __launch_bounds__(256) void segsum_k(const int32_t* __restrict__ skey, const int32_t* __restrict__ perm,
                                                 int N, const T* __restrict__ x, int ldx, int xoff, int width,
                                                 const float* __restrict__ s, int G, int D, float* __restrict__ out,
-                                                int V, int accumulate) {
+                                                int V, int accumulate, int ncb) {
   constexpr int VN = V16<T>::n;
-  const int v = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  const int v = gw / ncb, cb = gw - v * ncb;
   if (v >= V) return;  // wave-uniform
-  const int lo = lower_bound(skey, N, v), hi = lower_bound(skey, N, v + 1);
-  float* orow = out + (size_t)v * width;
-  for (int c0 = l * VN; c0 < width; c0 += 64 * VN) {
-    float acc[VN];
+  const int c0 = (cb * 64 + l) * VN;
+  const bool on = c0 < width;
+  const int cl = on ? c0 : 0;  // lanes past the row's end load column 0 and store nothing
+  const int bnd = wave_bounds(skey, N, v, v + 1, l);
+  const int lo = __builtin_amdgcn_readlane(bnd, 0), hi = __builtin_amdgcn_readlane(bnd, 32);
+  float acc[VN];
 #pragma unroll
-    for (int e = 0; e < VN; ++e) acc[e] = 0.f;
-    for (int j = lo; j < hi; ++j) {
-      const int n = perm[j];
-      float a[VN];
-      ld16(x + (size_t)n * ldx + xoff + c0, a);
-      const float g = s ? 3.0f / (1.0f + __expf(-s[(size_t)n * G + c0 / D])) : 1.0f;
-#pragma unroll
-      for (int e = 0; e < VN; ++e) acc[e] += g * a[e];
+  for (int e = 0; e < VN; ++e) acc[e] = 0.f;
+  // the gated form holds a gate logit per token too: half the batch
+  constexpr int BU = GATE ? SEG_U / 2 : SEG_U;
+  int j0 = lo;
+  if (hi - j0 >= BU) {
+    // lane u < BU holds the batch's u-th token index; the next batch's
+    // indices are loaded while this batch's rows are in flight
+    int myn = perm[j0 + (l < BU ? l : 0)];
+    for (; hi - j0 >= BU; j0 += BU) {
+      const int j1 = j0 + BU;
+      const int nxt = perm[hi - j1 >= BU ? j1 + (l < BU ? l : 0) : j0];
+      seg_batch<T, GATE, BU>(myn, BU, x, ldx, xoff, cl, s, G, D, acc);
+      myn = nxt;
     }
-    if (accumulate) {
-#pragma unroll
-      for (int e = 0; e < VN; e += 4) {
-        const f32x4 o = *(const f32x4*)(orow + c0 + e);
-        acc[e] += o[0]; acc[e + 1] += o[1]; acc[e + 2] += o[2]; acc[e + 3] += o[3];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < VN; e += 4) *(f32x4*)(orow + c0 + e) = f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
   }
+  for (; j0 < hi; j0 += 4) {
+    const int cnt = min(4, hi - j0);
+    seg_batch<T, GATE, 4>(perm[j0 + (l < cnt ? l : 0)], cnt, x, ldx, xoff, cl, s, G, D, acc);
+  }
+  if (!on) return;
+  float* orow = out + (size_t)v * width + c0;
+  if (accumulate) {
+#pragma unroll
+    for (int e = 0; e < VN; e += 4) {
+      const f32x4 o = *(const f32x4*)(orow + e);
+      acc[e] += o[0]; acc[e + 1] += o[1]; acc[e + 2] += o[2]; acc[e + 3] += o[3];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < VN; e += 4) *(f32x4*)(orow + e) = f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+}
+
+template <typename T>
+void launch_segsum(dim3 grid, hipStream_t st, const int32_t* sk, const int32_t* perm, int N, const void* x, int ldx,
+                   int xoff, int width, const float* gs, int G, int D, float* out, int V, int accumulate, int ncb) {
+  if (gs)
+    hipLaunchKernelGGL((segsum_k<T, true>), grid, dim3(256), 0, st, sk, perm, N, (const T*)x, ldx, xoff, width, gs, G, D,
+                       out, V, accumulate, ncb);
+  else
+    hipLaunchKernelGGL((segsum_k<T, false>), grid, dim3(256), 0, st, sk, perm, N, (const T*)x, ldx, xoff, width, gs, G,
+                       D, out, V, accumulate, ncb);
 }
 
 int ord_blocks(int N) { return std::max(1, (N + ORD_TILE - 1) / ORD_TILE); }
@@ -220,13 +296,11 @@ hipError_t token_order(const int32_t* ids, int N, int V, void* ws, const int32_t
 
 hipError_t rows_segsum(int dt, const int32_t* sorted_ids, const int32_t* perm, int N, const void* x, int ldx, int xoff,
                        int width, const float* gate_s, int G, int D, float* out, int V, int accumulate, hipStream_t s) {
-  const dim3 grid((V + 3) / 4);
-  if (dt == BF16)
-    hipLaunchKernelGGL(segsum_k<bf16>, grid, dim3(256), 0, s, sorted_ids, perm, N, (const bf16*)x, ldx, xoff, width,
-                       gate_s, G, D, out, V, accumulate);
-  else
-    hipLaunchKernelGGL(segsum_k<float>, grid, dim3(256), 0, s, sorted_ids, perm, N, (const float*)x, ldx, xoff, width,
-                       gate_s, G, D, out, V, accumulate);
+  const int vn = dt == BF16 ? 8 : 4;
+  const int ncb = (width + 64 * vn - 1) / (64 * vn);  // column blocks per row
+  const dim3 grid((unsigned)(((size_t)V * ncb + 3) / 4));
+  if (dt == BF16) launch_segsum<bf16>(grid, s, sorted_ids, perm, N, x, ldx, xoff, width, gate_s, G, D, out, V, accumulate, ncb);
+  else launch_segsum<float>(grid, s, sorted_ids, perm, N, x, ldx, xoff, width, gate_s, G, D, out, V, accumulate, ncb);
   return hipGetLastError();
 }
 
