@@ -54,18 +54,23 @@ __global__ __launch_bounds__(256) void amax_k(const T* __restrict__ x, size_t n,
 
 __global__ void zero_u32_k(unsigned* p) { *p = 0u; }
 
-// Tile of 128 rows x 64 columns, 256 threads.  Thread t quantises 16
-// consecutive codes of rows t/4 and 64 + t/4; the transpose goes through LDS
-// (one 32-bit word per 4 codes): output row c of the tile gathers its 128
-// codes as eight 16-byte pieces, so each transposed row segment is one whole
-// 128-byte line written by eight consecutive lanes.
-template <typename T>
+// Tile of 128 rows x TC columns (TC = 64 or 128), 256 threads.  Thread t
+// quantises 16 consecutive codes of rows t/TPR + (256/TPR)h, TPR = TC/16
+// threads per row; the transpose goes through LDS (one 32-bit word per 4
+// codes): output row c of the tile gathers its 128 codes as eight 16-byte
+// pieces, so each transposed row segment is one whole 128-byte line written
+// by eight consecutive lanes.  With TC = 128 the row-major codes of a row are
+// one whole line too, and the row's 256 bytes (bf16) are read by 8 threads:
+// a [32768, 6656] activation 0.305 -> 0.261 ms (amax pass included); tensors
+// with fewer than 2048 such tiles keep TC = 64 for more workgroups.
+template <typename T, int TC>
 __global__ __launch_bounds__(256) void quant_k(const T* __restrict__ x, int R, int Cc, const float* __restrict__ amax,
                                                 uint8_t* __restrict__ xq, uint8_t* __restrict__ xqt, int Rp) {
-  __shared__ unsigned tile[128][17];
-  const int r0 = blockIdx.y * 128, c0 = blockIdx.x * 64;
+  constexpr int TPR = TC / 16, RPP = 256 / TPR;  // threads per row, rows per pass
+  __shared__ unsigned tile[128][TC / 4 + 1];
+  const int r0 = blockIdx.y * 128, c0 = blockIdx.x * TC;
   const int t = threadIdx.x;
-  const int cs = (t & 3) * 16, c = c0 + cs;
+  const int cs = (t % TPR) * 16, c = c0 + cs;
   const float am = amax[0];
   const float s = am / 448.0f;
   // The quotient x / s, correctly rounded, from the reciprocal: with
@@ -75,8 +80,8 @@ __global__ __launch_bounds__(256) void quant_k(const T* __restrict__ x, int R, i
   const float y = 1.0f / s;
   const bool recip = s >= 1.17549435e-38f;  // s normal
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int rr = (t >> 2) + 64 * h, r = r0 + rr;
+  for (int h = 0; h < 128 / RPP; ++h) {
+    const int rr = t / TPR + RPP * h, r = r0 + rr;
     unsigned w[4] = {0u, 0u, 0u, 0u};
     if (r < R && c < Cc && am > 0.f) {
       float v[16];
@@ -119,12 +124,12 @@ __global__ __launch_bounds__(256) void quant_k(const T* __restrict__ x, int R, i
       *(u32x4_t*)(xq + (size_t)r * Cc + c) = o;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tile[rr][(t & 3) * 4 + i] = w[i];
+    for (int i = 0; i < 4; ++i) tile[rr][(t % TPR) * 4 + i] = w[i];
   }
   if (!xqt) return;  // uniform over the workgroup
   __syncthreads();
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < TC / 32; ++h) {
     // piece (t & 7) of output row 32h + t/8: codes of tile rows 16(t&7) .. +15
     const int oc = 32 * h + (t >> 3), rs = 16 * (t & 7);
     const int word = oc >> 2, sh = 8 * (oc & 3);
@@ -163,9 +168,16 @@ hipError_t fp8_quant(int dt, const void* x, int R, int Cc, const float* amax, ui
                      hipStream_t s) {
   const int rows = xqt ? Rp : R;
   if (rows == 0 || Cc == 0) return hipSuccess;
-  const dim3 grid((Cc + 63) / 64, (rows + 127) / 128);
-  if (dt == BF16) hipLaunchKernelGGL(quant_k<bf16>, grid, dim3(256), 0, s, (const bf16*)x, R, Cc, amax, xq, xqt, Rp);
-  else hipLaunchKernelGGL(quant_k<float>, grid, dim3(256), 0, s, (const float*)x, R, Cc, amax, xq, xqt, Rp);
+  const size_t wide = (size_t)((Cc + 127) / 128) * ((rows + 127) / 128);
+  if (wide >= 2048) {
+    const dim3 grid((Cc + 127) / 128, (rows + 127) / 128);
+    if (dt == BF16) hipLaunchKernelGGL((quant_k<bf16, 128>), grid, dim3(256), 0, s, (const bf16*)x, R, Cc, amax, xq, xqt, Rp);
+    else hipLaunchKernelGGL((quant_k<float, 128>), grid, dim3(256), 0, s, (const float*)x, R, Cc, amax, xq, xqt, Rp);
+  } else {
+    const dim3 grid((Cc + 63) / 64, (rows + 127) / 128);
+    if (dt == BF16) hipLaunchKernelGGL((quant_k<bf16, 64>), grid, dim3(256), 0, s, (const bf16*)x, R, Cc, amax, xq, xqt, Rp);
+    else hipLaunchKernelGGL((quant_k<float, 64>), grid, dim3(256), 0, s, (const float*)x, R, Cc, amax, xq, xqt, Rp);
+  }
   return hipGetLastError();
 }
 

@@ -341,9 +341,11 @@ def _e4m3_values(codes: torch.Tensor) -> np.ndarray:
 
 
 @pytest.mark.parametrize("R,Cc,Rp,scale", [(130, 96, 144, 1.0), (64, 64, 64, 1e-3), (1, 16, 16, 300.0),
-                                            (300, 1664, 304, 1.0)])
+                                            (300, 1664, 304, 1.0), (30001, 1040, 30016, 1.0)])
 def test_fp8_quantize_codes_exact(R, Cc, Rp, scale):
-    # the codes are integer work: bit-exact against the oracle's float32 decisions
+    # the codes are integer work: bit-exact against the oracle's float32 decisions;
+    # the last shape takes the 128-column tiles (at least 2048 of them), with a
+    # partial last column tile and padded transposed rows
     print(f"fp8 quantize R={R} Cc={Cc} Rp={Rp}", flush=True)
     x = rounded(RNG.standard_normal((R, Cc)) * scale, "bf16")
     x[0, :3] = [0.0, -0.0, x[0, 3]]      # zeros and a repeated value
