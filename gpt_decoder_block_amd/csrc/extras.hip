@@ -48,8 +48,46 @@ __global__ __launch_bounds__(256) void reduce_cols_k(const float* __restrict__ p
   }
 }
 
+// The same sums for many columns (the value-embedding gate's Hkv*nc): a
+// workgroup of 16 waves per 64 columns, lane = column, so every partial row
+// is read as whole 256-byte segments; wave w adds rows w, w + 16, w + 32, ...
+// in that order (eight loads in flight), then the 16 wave sums are added in
+// wave order.  One workgroup walking the columns one at a time took ~260 us
+// for the d26 gate's 416 columns of 512 partials.
+__global__ __launch_bounds__(1024) void reduce_cols_wide_k(const float* __restrict__ part, int nblk, int K,
+                                                           float* out0, float* out1, int accumulate) {
+  __shared__ float red[16][64];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int k = blockIdx.x * 64 + l;
+  const int kc = k < K ? k : K - 1;  // lanes past the last column read a valid one and store nothing
+  float s = 0.f;
+  for (int i0 = w; i0 < nblk; i0 += 16 * 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + 16 * u;
+      v[u] = i < nblk ? part[(size_t)i * K + kc] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  red[w][l] = s;
+  __syncthreads();
+  if (w == 0 && k < K) {
+    float t = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) t += red[j][l];
+    float* o = k == 0 ? out0 : out1 + (k - 1);
+    *o = accumulate ? *o + t : t;
+  }
+}
+
 hipError_t reduce_cols(const float* part, int nblk, int K, float* out0, float* out1, int accumulate, hipStream_t s) {
-  hipLaunchKernelGGL(reduce_cols_k, dim3(1), dim3(256), 0, s, part, nblk, K, out0, out1, accumulate);
+  if (K > 8)
+    hipLaunchKernelGGL(reduce_cols_wide_k, dim3((K + 63) / 64), dim3(1024), 0, s, part, nblk, K, out0, out1,
+                       accumulate);
+  else
+    hipLaunchKernelGGL(reduce_cols_k, dim3(1), dim3(256), 0, s, part, nblk, K, out0, out1, accumulate);
   return hipGetLastError();
 }
 
