@@ -52,7 +52,9 @@ __global__ __launch_bounds__(256) void amax_k(const T* __restrict__ x, size_t n,
   if (threadIdx.x == 0) atomicMax(out, __float_as_uint(m));
 }
 
-__global__ void zero_u32_k(unsigned* p) { *p = 0u; }
+__global__ void zero_u32_k(unsigned* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+}
 
 // Tile of 128 rows x TC columns (TC = 64 or 128), 256 threads.  Thread t
 // quantises 16 consecutive codes of rows t/TPR + (256/TPR)h, TPR = TC/16
@@ -148,15 +150,17 @@ __global__ __launch_bounds__(256) void quant_k(const T* __restrict__ x, int R, i
 
 }  // namespace
 
-hipError_t fp8_amax_zero(float* amax, hipStream_t s) {
-  hipLaunchKernelGGL(zero_u32_k, dim3(1), dim3(1), 0, s, (unsigned*)amax);
+hipError_t fp8_amax_zero(float* amax, hipStream_t s, int count) {
+  hipLaunchKernelGGL(zero_u32_k, dim3(1), dim3(64), 0, s, (unsigned*)amax, count);
   return hipGetLastError();
 }
 
-hipError_t fp8_amax(int dt, const void* x, size_t n, float* amax, hipStream_t s) {
-  hipLaunchKernelGGL(zero_u32_k, dim3(1), dim3(1), 0, s, (unsigned*)amax);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || n == 0) return e;
+hipError_t fp8_amax(int dt, const void* x, size_t n, float* amax, hipStream_t s, bool zero) {
+  if (zero) {
+    const hipError_t e = fp8_amax_zero(amax, s);
+    if (e != hipSuccess) return e;
+  }
+  if (n == 0) return hipSuccess;
   const size_t nv = n / (dt == BF16 ? 8 : 4);
   const unsigned grid = (unsigned)std::min<size_t>((nv + 255) / 256, 256);
   if (dt == BF16) hipLaunchKernelGGL(amax_k<bf16>, dim3(grid), dim3(256), 0, s, (const bf16*)x, n, (unsigned*)amax);

@@ -121,10 +121,12 @@ inline int plan_slices(const SplitPlan& p) { return p.splits2 > p.splits ? p.spl
 
 // ------------------------------------------------------------ fp8 quantiser
 // amax[0] = max |x| over n elements (x dtype dt; n a multiple of 8); amax is
-// zeroed first (stream-ordered), so one call gives one tensor's amax.
-// zero an amax accumulator (before a producer that raises it)
-hipError_t fp8_amax_zero(float* amax, hipStream_t s);
-hipError_t fp8_amax(int dt, const void* x, size_t n, float* amax, hipStream_t s);
+// zeroed first (stream-ordered) unless zero = false (the word was zeroed
+// already, e.g. with its neighbours in one fp8_amax_zero launch).
+hipError_t fp8_amax(int dt, const void* x, size_t n, float* amax, hipStream_t s, bool zero = true);
+// zero the `count` amax accumulators at amax (count <= 64; before the
+// producers that raise them)
+hipError_t fp8_amax_zero(float* amax, hipStream_t s, int count = 1);
 // codes e4m3(x / s), s = amax / 448 (float32 division, round to nearest
 // even, saturating at 448): x [R, Cc] (dt), Cc a multiple of 16; xq [R, Cc]
 // row-major (or null); xqt [Cc, Rp] the transpose with rows R..Rp-1 zero (or
