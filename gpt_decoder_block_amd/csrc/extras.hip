@@ -168,11 +168,25 @@ __global__ __launch_bounds__(256) void ve_fwd_k(T* qkv, int ldq, int voff, const
   if (n >= N) return;  // wave-uniform
   int id = ids[n];
   id = id < 0 ? 0 : (id >= V ? V - 1 : id);
-  const float xv = l < nc ? to_f(xn[(size_t)n * C + l]) : 0.f;
+  // gate logits: lane l takes head g0 + l/LP and channels 8(l % LP) .. +7 of
+  // the nc, the LP lanes of a head are summed by a butterfly, and lane g ends
+  // with s_g (LP = 4 for nc = 32: all 16 heads of a pass at once, where one
+  // 64-lane sum per head took Hkv six-step butterflies)
+  const int LP = nc <= 8 ? 1 : nc <= 16 ? 2 : nc <= 32 ? 4 : 8, HPP = 64 / LP;
   float s_mine = 0.f;
-  for (int g = 0; g < Hkv; ++g) {
-    const float s = wave_sum(l < nc ? xv * to_f(wg[g * nc + l]) : 0.f);
-    if (l == g) s_mine = s;
+  for (int g0 = 0; g0 < Hkv; g0 += HPP) {
+    const int g = g0 + l / LP, c0 = 8 * (l % LP);
+    float acc = 0.f;
+    if (g < Hkv) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (c0 + i < nc) acc += to_f(xn[(size_t)n * C + c0 + i]) * to_f(wg[g * nc + c0 + i]);
+    }
+    for (int o = LP / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    const int j = l - g0;  // lane l takes head l's sum, held by lane (l - g0) * LP
+    const bool mine = j >= 0 && j < HPP;
+    const float sj = __shfl(acc, (mine ? j : 0) * LP, 64);
+    if (mine) s_mine = sj;
   }
   if (l < Hkv) s_save[(size_t)n * Hkv + l] = s_mine;
   const float gate_mine = 3.0f * sigm(s_mine);
@@ -240,19 +254,26 @@ template <typename T>
 __global__ __launch_bounds__(256) void ve_gate_bwd_k(const float* __restrict__ ds, const T* __restrict__ xn, T* dxn,
                                                       int C, const T* __restrict__ wg, int nc, int Hkv,
                                                       float* __restrict__ part, int N) {
-  const int n0 = blockIdx.x * 64, n1 = min(N, n0 + 64);
-  for (int e = threadIdx.x; e < 64 * nc; e += 256) {
-    const int n = n0 + e / nc, c = e % nc;
-    if (n >= N) continue;
+  // the block's 64 rows of ds and of xn's first nc channels, and wg, are
+  // staged in LDS with coalesced loads; the sums below then read LDS only
+  // (the same products added in the same order as from memory)
+  __shared__ float ds_s[64][65], xn_s[64][65], wg_s[64][65];
+  const int n0 = blockIdx.x * 64, n1 = min(N, n0 + 64), nn = n1 - n0;
+  for (int e = threadIdx.x; e < nn * Hkv; e += 256) ds_s[e / Hkv][e % Hkv] = ds[(size_t)n0 * Hkv + e];
+  for (int e = threadIdx.x; e < nn * nc; e += 256) xn_s[e / nc][e % nc] = to_f(xn[(size_t)(n0 + e / nc) * C + e % nc]);
+  for (int e = threadIdx.x; e < Hkv * nc; e += 256) wg_s[e / nc][e % nc] = to_f(wg[e]);
+  __syncthreads();
+  for (int e = threadIdx.x; e < nn * nc; e += 256) {
+    const int r = e / nc, c = e % nc;
     float acc = 0.f;
-    for (int g = 0; g < Hkv; ++g) acc += ds[(size_t)n * Hkv + g] * to_f(wg[g * nc + c]);
-    T* p = dxn + (size_t)n * C + c;
+    for (int g = 0; g < Hkv; ++g) acc += ds_s[r][g] * wg_s[g][c];
+    T* p = dxn + (size_t)(n0 + r) * C + c;
     *p = from_f<T>(to_f(*p) + acc);
   }
   for (int e = threadIdx.x; e < Hkv * nc; e += 256) {
     const int g = e / nc, c = e % nc;
     float acc = 0.f;
-    for (int n = n0; n < n1; ++n) acc += ds[(size_t)n * Hkv + g] * to_f(xn[(size_t)n * C + c]);
+    for (int r = 0; r < nn; ++r) acc += ds_s[r][g] * xn_s[r][c];
     part[(size_t)blockIdx.x * Hkv * nc + e] = acc;
   }
 }
