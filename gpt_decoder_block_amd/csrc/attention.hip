@@ -19,14 +19,16 @@
 //     second MFMA's operand registers directly, with a relabelling of the
 //     contraction index that both operands share.  Writes O (bf16) and the
 //     row log-sum-exp (fp32).
-//   backward: delta_i = dO_i . O_i; then two deterministic kernels that each
-//     recompute P from the saved log-sum-exp:
-//       dK/dV: a workgroup of 4 waves owns 128 keys of one (b, kv head) and
-//         loops over the query heads of its group and the visible 64-row
-//         query tiles, accumulating dV^T += dO^T P and dK^T += Q^T dS in
-//         registers (the GQA head reduction happens in registers, no atomics);
+//   backward: two deterministic kernels that each recompute P from the saved
+//     log-sum-exp:
 //       dQ: a workgroup of 8 waves owns 256 query rows and loops over the
-//         visible key tiles, dQ^T += K^T dS^T.
+//         visible key tiles, dQ^T += K^T dS^T; it also forms
+//         delta_i = dO_i . O_i from the dO rows it holds and writes it;
+//       dK/dV (after dQ): a workgroup of 4 waves owns 128 keys of one
+//         (b, kv head) and loops over the query heads of its group and the
+//         visible 64-row query tiles, accumulating dV^T += dO^T P and
+//         dK^T += Q^T dS in registers (the GQA head reduction happens in
+//         registers, no atomics).
 // fp32 path: one thread per query (or key) row; slow, exact reference-order
 // kernels for the fp32 mode.
 #include "common.h"
@@ -695,7 +697,21 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void attn_bwd_dq_bf16_k(A
   }
   const size_t li = ((size_t)b * H + h) * T + qc;
   const float lse2 = a.lse[li] * 1.4426950408889634f;
-  const float dlt = a.delta[li];
+  // delta_i = dO_i . O_i from the dO fragments held here (each lane of the
+  // pair has half of the row); written for the dK/dV kernel, which runs next
+  float dlt;
+  {
+    const bf16* orow = (const bf16*)a.o + ((size_t)b * T + qc) * a.ldo + h * HD;
+    float pd = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const bf16x8 ov = *(const bf16x8*)(orow + kk * 16 + lh * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pd = fmaf((float)ov[e], (float)df[kk][e], pd);
+    }
+    dlt = pd + __shfl_xor(pd, 32, 64);
+    if (lh == 0 && qi < T) a.delta[li] = dlt;
+  }
   f32x16 dq[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) dq[i] = f32x16{};
@@ -901,20 +917,20 @@ hipError_t attn_bwd(int dt, const AttnArgs& a, hipStream_t s) {
   if (a.B * a.T == 0) return hipSuccess;
   if (dt == BF16 && !bwd_offsets_fit(a)) return hipErrorInvalidValue;
   const float scale = 1.0f / sqrtf((float)a.D);
-  const int rows = a.B * a.T;  // one wave per token
-  if (dt == BF16) hipLaunchKernelGGL(attn_delta_k<bf16>, dim3((rows + 3) / 4), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(attn_delta_k<float>, dim3((rows + 3) / 4), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   if (dt == BF16) {
-    hipLaunchKernelGGL((attn_bwd_dkv_bf16_k<ATTN_DKV_NW, 3, ATTN_DKV_NS>), dim3(a.B * a.Hkv, (a.T + 32 * ATTN_DKV_NW - 1) / (32 * ATTN_DKV_NW)),
-                       dim3(64 * ATTN_DKV_NW), 0, s, a, scale * 1.4426950408889634f, scale);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // dQ first: it also writes delta, which dK/dV reads
     hipLaunchKernelGGL((attn_bwd_dq_bf16_k<ATTN_DQ_NW, ATTN_DQ_NS>), dim3(a.B * a.H, (a.T + 32 * ATTN_DQ_NW - 1) / (32 * ATTN_DQ_NW)),
                        dim3(64 * ATTN_DQ_NW), 0, s, a,
                        scale * 1.4426950408889634f, scale);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dkv_bf16_k<ATTN_DKV_NW, 3, ATTN_DKV_NS>), dim3(a.B * a.Hkv, (a.T + 32 * ATTN_DKV_NW - 1) / (32 * ATTN_DKV_NW)),
+                       dim3(64 * ATTN_DKV_NW), 0, s, a, scale * 1.4426950408889634f, scale);
   } else {
+    const int rows = a.B * a.T;  // one wave per token
+    hipLaunchKernelGGL(attn_delta_k<float>, dim3((rows + 3) / 4), dim3(256), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     dim3 gq((a.B * a.H * a.T + 63) / 64), gk((a.B * a.Hkv * a.T + 63) / 64);
     if (a.D == 64) {
       hipLaunchKernelGGL(attn_bwd_dq_f32_k<64>, gq, dim3(64), 0, s, a, scale);
