@@ -172,9 +172,12 @@ def test_mix_stage(dt, N, C):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("deterministic", [False, True])
-def test_value_embedding_stage(dt, deterministic):
-    # d26-like heads (13 K/V heads of 128), 32 gate channels, repeated ids
-    N, Hkv, D, nc, V = 300, 13, 128, 32, 97
+@pytest.mark.parametrize("Hkv,nc", [(13, 32), (40, 64), (3, 5), (20, 12)])
+def test_value_embedding_stage(dt, deterministic, Hkv, nc):
+    # d26-like heads (13 K/V heads of 128), 32 gate channels, repeated ids; the
+    # other head/channel counts take every lanes-per-head split of the gate
+    # logits (8, 1, 2 lanes per head) and several passes over the heads
+    N, D, V = 300, 128, 97
     C, KV = 1664, Hkv * 128
     ld = C + 2 * KV
     voff = C + KV
@@ -209,7 +212,8 @@ def test_value_embedding_stage(dt, deterministic):
     e1 = assert_close(dve, r["dve"], dt, "dve")
     e2 = assert_close(dwg, r["dwg"], dt, "dve_gate")
     e3 = assert_close(dxn, f(dxn0) + r["dxn"].reshape(N, C), dt, "dxn")
-    print(f"ve stage dt={dt} det={deterministic} errs dve {e1:.2e} dwg {e2:.2e} dxn {e3:.2e}", flush=True)
+    print(f"ve stage dt={dt} det={deterministic} Hkv={Hkv} nc={nc} errs dve {e1:.2e} dwg {e2:.2e} dxn {e3:.2e}",
+          flush=True)
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
