@@ -330,6 +330,37 @@ __device__ __forceinline__ bf16x4 tr_read(const bf16* p) {
   return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p));
 }
 
+#ifndef GEMM_XCD_SPLIT
+#define GEMM_XCD_SPLIT 1
+#endif
+// Split-K launches (the weight gradients): the dispatcher hands workgroups to
+// the 8 XCDs in turn, so with the tiles of one split numbered consecutively
+// an XCD's concurrent workgroups would hold two or more splits' K ranges of
+// scattered tiles.  xcd_rank gives workgroup i of a phase of n (the first at
+// linear index base) its rank in an order where each XCD takes one contiguous
+// run; the run is then read split-major and, within a split, in groups of 4
+// tile rows (tile_order), so an XCD's workgroups share one K range and
+// neighbouring operand panels in its L2.  Both are bijections.
+__device__ __forceinline__ int xcd_rank(int i, int n, int base) {
+  const int x = (base + i) & 7;
+  int start = 0;
+  for (int y = 0; y < x; ++y) {
+    const int off = (y - base) & 7;  // the phase's first workgroup on XCD y
+    start += off < n ? (n - off + 7) / 8 : 0;
+  }
+  return start + (i - ((x - base) & 7)) / 8;
+}
+__device__ __forceinline__ void tile_order(int idx, int nbm, int nbn, int& tm, int& tn) {
+  constexpr int GROUP = 4;
+  const int per_group = GROUP * nbn;
+  const int g = idx / per_group;
+  const int first_m = g * GROUP;
+  const int gsize = min(nbm - first_m, GROUP);
+  const int in = idx % per_group;
+  tm = first_m + in % gsize;
+  tn = in / gsize;
+}
+
 __device__ __forceinline__ void tile_coords(int bid, int nbm, int nbn, int& tm, int& tn) {
   const int total = nbm * nbn;
   const int full = (total / 8) * 8;
@@ -414,17 +445,34 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_k(GemmArgs p) {
     const int r1 = p.split_cols ? nbm : p.first1, c1 = p.split_cols ? p.first1 : nbn;
     const int t1 = r1 * c1, n1 = t1 * p.splits;
     if (bid < n1) {
-      split = bid / t1;
-      tile_coords(bid - split * t1, r1, c1, tm, tn);
+      if (GEMM_XCD_SPLIT) {
+        const int g = xcd_rank(bid, n1, 0);
+        split = g / t1;
+        tile_order(g - split * t1, r1, c1, tm, tn);
+      } else {
+        split = bid / t1;
+        tile_coords(bid - split * t1, r1, c1, tm, tn);
+      }
     } else {
       const int r2 = p.split_cols ? nbm : nbm - p.first1, c2 = p.split_cols ? nbn - p.first1 : nbn;
       const int t2 = r2 * c2, b2 = bid - n1;
-      split = b2 / t2;
-      tile_coords(b2 - split * t2, r2, c2, tm, tn);
+      if (GEMM_XCD_SPLIT) {
+        const int g = xcd_rank(b2, t2 * p.splits2, n1);
+        split = g / t2;
+        tile_order(g - split * t2, r2, c2, tm, tn);
+      } else {
+        split = b2 / t2;
+        tile_coords(b2 - split * t2, r2, c2, tm, tn);
+      }
       if (p.split_cols) tn += p.first1;
       else tm += p.first1;
       nsplit = p.splits2;
     }
+  } else if (GEMM_XCD_SPLIT && gridDim.y > 1) {
+    const int nt = gridDim.x, n = nt * gridDim.y;
+    const int g = xcd_rank(blockIdx.y * nt + blockIdx.x, n, (int)blockIdx.z * n);
+    split = g / nt;
+    tile_order(g - split * nt, nbm, nbn, tm, tn);
   } else {
     tile_coords(blockIdx.x, nbm, nbn, tm, tn);
   }
