@@ -26,7 +26,8 @@
 //         delta_i = dO_i . O_i from the dO rows it holds and writes it;
 //       dK/dV (after dQ): a workgroup of 4 waves owns 128 keys of one
 //         (b, kv head) and loops over the query heads of its group and the
-//         visible 64-row query tiles, accumulating dV^T += dO^T P and
+//         visible query rows, 32 at a time through two LDS stages,
+//         accumulating dV^T += dO^T P and
 //         dK^T += Q^T dS in registers (the GQA head reduction happens in
 //         registers, no atomics).
 // fp32 path: one thread per query (or key) row; slow, exact reference-order
@@ -63,7 +64,10 @@ constexpr int HD = 128;  // head_dim of the MFMA path
 #define ATTN_DKV_NW 4
 #endif
 #ifndef ATTN_DKV_NS
-#define ATTN_DKV_NS 1
+#define ATTN_DKV_NS 2
+#endif
+#ifndef ATTN_DKV_SR
+#define ATTN_DKV_SR 32
 #endif
 constexpr int ATTN_FQ = 32 * ATTN_IB * ATTN_NW;  // query rows per forward workgroup
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -121,9 +125,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16* base, si
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, (int)min(bytes, (size_t)0x7FFFFFF0),
                                            0x00020000);
 }
-template <int NW = 4>
+template <int NW = 4, int ROWS = 64>
 __device__ __forceinline__ void tile_async(__amdgpu_buffer_rsrc_t rs, size_t ld, int row0, int nrows, bf16* S) {
-  constexpr int RW = 64 / NW;  // rows per wave
+  static_assert(ROWS % (4 * NW) == 0, "whole 4-row loads per wave");
+  constexpr int RW = ROWS / NW;  // rows per wave
   const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), L = t & 63;
 #pragma unroll
   for (int i = 0; i < RW / 4; ++i) {
@@ -492,25 +497,29 @@ __device__ __forceinline__ void qknorm_rope_bwd_row(const f32x16 (&acc)[4], floa
 // overlaps the other's MFMAs without a common barrier.  The workgroup's V
 // rows sit in LDS for the whole kernel (the wave's K rows stay in
 // registers).  Loops over the query heads of the group and the visible
-// 64-row query tiles; Q, dO (row-major) and the tile's log-sum-exp and delta
-// go through NS LDS stages (NS = 1: the next tile is copied once every wave
-// has read this one, the other workgroup computing meanwhile; NS = 2: it is
-// in flight during this tile).  Each tile is taken as two 32-query halves:
-// S, then P (kept in fp32 in place of S) into dV^T += dO^T P, then dP and
-// dS into dK^T += Q^T dS, so at most S and dP of one half are live; the
-// transposed operands come from the LDS transpose load.  A wave has 256
-// registers; the accumulators take 128, so KX of its eight K fragments wait
-// in LDS rather than in scratch, whose reloads would also wait for copies
-// in flight (vector-memory counts retire in order): at NW = 4, NS = 1,
-// KX = 3 the kernel needs 252 registers and no scratch.
-template <int NW, int KX = 3, int NS = 2>
+// 64-row query tiles; Q, dO (row-major) and the rows' log-sum-exp and delta
+// go through NS LDS stages of SR rows (SR = 64, NS = 1: the next tile is
+// copied once every wave has read this one, the other workgroup computing
+// meanwhile; SR = 32, NS = 2, the default: each stage holds half a tile and
+// the next half is in flight while this one is used, in the same LDS).
+// Each tile is taken as two 32-query halves: S, then P (kept in fp32 in
+// place of S) into dV^T += dO^T P, then dP and dS into dK^T += Q^T dS, so
+// at most S and dP of one half are live; the transposed operands come from
+// the LDS transpose load.  A wave has 256 registers; the accumulators take
+// 128, so KX of its eight K fragments wait in LDS rather than in scratch,
+// whose reloads would also wait for copies in flight (vector-memory counts
+// retire in order): at NW = 4, KX = 3 the kernel needs 247 registers and
+// no scratch (SR = 64, NS = 1: 256 registers and an 8-byte spill).
+template <int NW, int KX = 3, int NS = 2, int SR = 64>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void attn_bwd_dkv_bf16_k(AttnArgs a, float scale_log2,
                                                                                float scale) {
   static_assert(NS == 1 || NS == 2, "one or two Q/dO stages");
+  static_assert(SR == 64 || (SR == 32 && NS == 2), "a stage holds a 64-row query tile or half of one");
   constexpr int FK = 32 * NW;
+  constexpr int HPT = 64 / SR;  // stages per 64-row query tile
   __shared__ __attribute__((aligned(16))) bf16 Vs[FK * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Qs[NS][64 * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Ds[NS][64 * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Qs[NS][SR * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Ds[NS][SR * HD];
   __shared__ __attribute__((aligned(16))) float Ls[NS][NW][64];  // [stage][wave: lse (even), delta (odd)][row]
   // the last KX of the wave's eight K fragments, parked in LDS (private to
   // the wave) to free registers
@@ -527,16 +536,18 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void attn_bwd_dkv_bf16_k(
   const int q_lo = kv0;  // multiple of 64
   const int q_hi = W >= 0 ? min(T, kv0 + FK + W) : T;
   const int nqt = q_hi > q_lo ? (q_hi - q_lo + 63) / 64 : 0;
-  const int total = nqt * G;
+  const int total = nqt * G * HPT;  // stage fills: (query head, query tile, part of the tile)
   // wave's keys
   const int wk0 = kv0 + w * 32, wk_hi = min(wk0 + 31, T - 1);
+  // first query row of stage fill `it`
+  auto row0 = [&](int it) { return q_lo + ((it / HPT) % nqt) * 64 + (it % HPT) * SR; };
 
-  // every wave issues the same number of loads per tile (2 x 16/NW + 1)
+  // every wave issues the same number of loads per fill (2 x SR/(4 NW) + 1)
   auto issue = [&](int it, int stg) {
-    const int hh = g * G + it / nqt;
-    const int i0 = q_lo + (it % nqt) * 64;
-    tile_async<NW>(tile_rsrc(base + hh * HD, a.ld, T), a.ld, i0, T, Qs[stg]);
-    tile_async<NW>(tile_rsrc(dbase + hh * HD, a.lddo, T), a.lddo, i0, T, Ds[stg]);
+    const int hh = g * G + it / (HPT * nqt);
+    const int i0 = row0(it);
+    tile_async<NW, SR>(tile_rsrc(base + hh * HD, a.ld, T), a.ld, i0, T, Qs[stg]);
+    tile_async<NW, SR>(tile_rsrc(dbase + hh * HD, a.lddo, T), a.lddo, i0, T, Ds[stg]);
     const size_t lo = ((size_t)b * H + hh) * T;
     vec64_async((w & 1) ? a.delta + lo : a.lse + lo, i0, T, Ls[stg][w]);
   };
@@ -562,18 +573,18 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void attn_bwd_dkv_bf16_k(
 
   for (int it = 0; it < total; ++it) {
     const int st = NS == 2 ? it & 1 : 0;
-    const int i0 = q_lo + (it % nqt) * 64;
+    const int i0 = row0(it);
     // two stages: the other stage was last read in iteration it-1, which
     // every wave has left; one stage: the next tile is copied after this one
     // has been read (the other workgroup on the CU computes meanwhile)
     if (NS == 2 && it + 1 < total) issue(it + 1, st ^ 1);
-    // wave-uniform visibility of this query tile for the wave's 32 keys
-    const int iq_hi = min(i0 + 63, T - 1);
-    const bool any = wk0 < T && i0 + 63 >= wk0 && (W < 0 || i0 - wk_hi <= W);
+    // wave-uniform visibility of this stage's query rows for the wave's 32 keys
+    const int iq_hi = min(i0 + SR - 1, T - 1);
+    const bool any = wk0 < T && i0 + SR - 1 >= wk0 && (W < 0 || i0 - wk_hi <= W);
     if (any) {
-      const bool full = i0 >= wk_hi && iq_hi < T && (W < 0 || iq_hi - wk0 <= W) && i0 + 63 < T;
+      const bool full = i0 >= wk_hi && iq_hi < T && (W < 0 || iq_hi - wk0 <= W) && i0 + SR - 1 < T;
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
+      for (int ib = 0; ib < SR / 32; ++ib) {
         // query rows 32ib..32ib+31: lane = key j, registers = queries.  S
         // first; P (kept in fp32 in place of S) feeds dV before dP is
         // computed, so P's bf16 copy and dP are never live together
@@ -924,7 +935,7 @@ hipError_t attn_bwd(int dt, const AttnArgs& a, hipStream_t s) {
                        scale * 1.4426950408889634f, scale);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dkv_bf16_k<ATTN_DKV_NW, 3, ATTN_DKV_NS>), dim3(a.B * a.Hkv, (a.T + 32 * ATTN_DKV_NW - 1) / (32 * ATTN_DKV_NW)),
+    hipLaunchKernelGGL((attn_bwd_dkv_bf16_k<ATTN_DKV_NW, 3, ATTN_DKV_NS, ATTN_DKV_SR>), dim3(a.B * a.Hkv, (a.T + 32 * ATTN_DKV_NW - 1) / (32 * ATTN_DKV_NW)),
                        dim3(64 * ATTN_DKV_NW), 0, s, a, scale * 1.4426950408889634f, scale);
   } else {
     const int rows = a.B * a.T;  // one wave per token
