@@ -574,11 +574,16 @@ __global__ __launch_bounds__(256) void ce_bf16_k(bf16* z, const int32_t* __restr
   // bf16 pair -> two floats: the low half shifted up, the high half masked
   auto lo = [](unsigned w) { return __uint_as_float(w << 16); };
   auto hi = [](unsigned w) { return __uint_as_float(w & 0xffff0000u); };
+  // the max of each word's two values with the running max in one v_max3:
+  // fmaxf on values made by bit operations would first quiet possible NaNs
+  // with an extra v_max per value (a finite row has none; a row holding a
+  // NaN gives a NaN loss either way)
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < CE_MAXV; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) mx = fmaxf(mx, fmaxf(lo(raw[i][q]), hi(raw[i][q])));
+    for (int q = 0; q < 4; ++q)
+      asm("v_max3_f32 %0, %1, %2, %3" : "=v"(mx) : "v"(mx), "v"(lo(raw[i][q])), "v"(hi(raw[i][q])));
   mx = block_max<256>(mx, red);
   // an empty asm marks the raw words as changed, so the widened floats are
   // recomputed in each pass rather than kept live (which would double the
@@ -602,6 +607,9 @@ __global__ __launch_bounds__(256) void ce_bf16_k(bf16* z, const int32_t* __restr
   const float lse = mx + logf(se);
   const float l2 = lse * L2E;
   const float invN = 1.0f / (float)N;
+  // p/N = 2^(z log2(e) - lse log2(e) - log2(N)): the division by N rides in
+  // the exponent (no multiply per element)
+  const float l2n = l2 + log2f((float)N);
 #pragma unroll
   for (int i = 0; i < CE_MAXV; ++i) {
     const int vi = threadIdx.x + 256 * i;
@@ -609,10 +617,8 @@ __global__ __launch_bounds__(256) void ce_bf16_k(bf16* z, const int32_t* __restr
       bf16x8 o;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(lo(raw[i][q]), L2E, -l2));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(hi(raw[i][q]), L2E, -l2));
-        o[2 * q] = (bf16)(p0 * invN);
-        o[2 * q + 1] = (bf16)(p1 * invN);
+        o[2 * q] = (bf16)__builtin_amdgcn_exp2f(fmaf(lo(raw[i][q]), L2E, -l2n));
+        o[2 * q + 1] = (bf16)__builtin_amdgcn_exp2f(fmaf(hi(raw[i][q]), L2E, -l2n));
       }
       __builtin_nontemporal_store(o, (bf16x8*)(zr + vi * 8));
     }
