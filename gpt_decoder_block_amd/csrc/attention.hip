@@ -142,12 +142,18 @@ __device__ __forceinline__ void tile_async(__amdgpu_buffer_rsrc_t rs, size_t ld,
   }
 }
 
-// 64 floats (one per lane) straight into LDS; index clamped to n - 1.
+// 64 floats (one per lane) straight into LDS; index clamped to n - 1.  The
+// destination's origin is hidden like the buffer copies' above: otherwise
+// the compiler waits for every copy in flight (vmcnt(0)) before the first
+// read of any LDS array these rows might alias, which in dK/dV drained the
+// next stage's Q/dO copies right after the S products.
 __device__ __forceinline__ void vec64_async(const float* src, int i0, int n, float* S) {
   const int L = threadIdx.x & 63;
   int i = i0 + L;
   i = i < n ? i : n - 1;
-  __builtin_amdgcn_global_load_lds((const void*)(src + i), (lds_ptr)S, 4, 0, 0);
+  lds_ptr d = (lds_ptr)S;
+  asm volatile("" : "+s"(d));  // hide the destination's origin from the alias analysis
+  __builtin_amdgcn_global_load_lds((const void*)(src + i), d, 4, 0, 0);
 }
 
 // MFMA operand with rows = tile rows (A of S = K Q^T etc.): lane (row lr of
