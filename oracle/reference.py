@@ -521,12 +521,24 @@ def smear_backward(dx: np.ndarray, e: np.ndarray, w_s: np.ndarray, lam: float, c
 
 # ------------------------------------------------------------------- stack
 def stack_forward_backward(cfg, ids: np.ndarray, glob: Dict[str, np.ndarray],
-                           layers: List[Dict[str, np.ndarray]], keep: bool = False):
+                           layers: List[Dict[str, np.ndarray]], keep: bool = False,
+                           stream_dtype: Optional[str] = None):
     """Full step on ids [B, T+1]: embedding [-> smear], L blocks [with residual
     mixing, value embeddings, backout], final rms, lm_head, mean next-token
     cross-entropy; then the backward of all of it.  Returns (loss, grads,
     acts) where grads has 'wte', 'w_lm', 'layers' (list of dicts) [and the
-    extras' scalars], and acts (if keep) holds each block's input stream."""
+    extras' scalars], and acts (if keep) holds each block's input stream.
+
+    stream_dtype="bf16" stores the residual streams between blocks as bf16
+    values, as a model with explicit bf16 activations does (section "3.
+    Gestion de la précision"): the stream entering the first block, every
+    block's output, the head's input gradient and every block's input
+    gradient are rounded to bf16; everything else stays exact.  Used only to
+    measure how far that storage alone moves each result over depth (the
+    bound of the full-depth parity tests); the default is the exact oracle."""
+    if stream_dtype not in (None, "bf16"):
+        raise ValueError(f"stream_dtype {stream_dtype!r}")
+    store = bf16_round if stream_dtype == "bf16" else (lambda a: a)
     B, T1 = ids.shape
     T = T1 - 1
     inp, tgt = ids[:, :T], ids[:, 1:]
@@ -539,15 +551,17 @@ def stack_forward_backward(cfg, ids: np.ndarray, glob: Dict[str, np.ndarray],
     x0 = None
     if cfg.extras:
         x, sc = smear_forward(e, glob["smear_gate"], float(np.ravel(glob["smear_lambda"])[0]))
+        x = store(x)
         x0 = x
     else:
-        x = e
+        x = store(e)
     caches, acts = [], []
     i_bo = L // 2 - 1
     x_bo = None
     for l in range(L):
         acts.append(x)
         x, c = block_forward(x, layers[l], cfg, l, cos, sin, x0=x0, ids=inp)
+        x = store(x)
         caches.append(c)
         if cfg.extras and l == i_bo:
             x_bo = x
@@ -557,6 +571,7 @@ def stack_forward_backward(cfg, ids: np.ndarray, glob: Dict[str, np.ndarray],
     else:
         x_final = x
     loss, dx, dw_lm, hc = lm_head_ce(x_final, glob["w_lm"], tgt, cfg.eps)
+    dx = store(dx)
     grads = {"w_lm": dw_lm, "layers": [None] * L}
     if cfg.extras:
         gb = backout_backward(dx, x_bo, glob["backout_lambda"])
@@ -568,6 +583,7 @@ def stack_forward_backward(cfg, ids: np.ndarray, glob: Dict[str, np.ndarray],
         if cfg.extras and l == i_bo:
             dx = dx + dx_bo
         dx, g = block_backward(dx, caches[l], layers[l], cfg, l, cos, sin, ids=inp)
+        dx = store(dx)
         if cfg.extras:
             dx0 += g.pop("x0")
         grads["layers"][l] = g

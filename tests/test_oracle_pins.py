@@ -614,3 +614,33 @@ def test_normuon_state_tracks_the_row_statistics():
     # one step from v = 0 weighs the new statistic by 1 - beta2
     _, v1 = O.normuon_scale(o, np.zeros(6), 0.75)
     np.testing.assert_allclose(v1, 0.25 * np.mean(o * o, axis=1), rtol=1e-15)
+
+
+# ------------------------------------------- bf16 storage of the streams
+@pytest.mark.parametrize("extras", [False, True])
+def test_stack_bf16_stream_storage_option(extras):
+    """The option that measures how bf16 storage of the residual streams moves
+    the result (the full-depth parity bound): off, the exact oracle bit for
+    bit; on, every stream entering a block is a bf16 value, and the loss and
+    every gradient move by more than nothing and by no more than a few bf16
+    unit roundoffs per stored stream."""
+    cfg = tiny_cfg(C=48, n_head=3, n_kv_head=1, head_dim=16, mlp_hidden=96, vocab=13, T=5, n_layer=4,
+                   windows=(-1, 2, -1, 1), extras=extras)
+    ids, glob, layers = _params(cfg, np.random.default_rng(31))
+    l0, g0, _ = O.stack_forward_backward(cfg, ids, glob, layers)
+    la, ga, _ = O.stack_forward_backward(cfg, ids, glob, layers, stream_dtype=None)
+    assert la == l0 and np.array_equal(ga["wte"], g0["wte"]) and np.array_equal(ga["w_lm"], g0["w_lm"])
+    l1, g1, o1 = O.stack_forward_backward(cfg, ids, glob, layers, keep=True, stream_dtype="bf16")
+    for a in o1["acts"]:
+        assert np.array_equal(O.bf16_round(a), a)
+    u = 2.0 ** -9  # bf16 unit roundoff
+    stores = 2 * (cfg.n_layer + 1)
+    rel = lambda a, b: float(np.max(np.abs(a - b))) / float(np.max(np.abs(b)))
+    assert 0 < abs(l1 - l0) / abs(l0) < stores * u
+    for k in ("wte", "w_lm"):
+        assert 0 < rel(g1[k], g0[k]) < 10 * stores * u
+    for l in range(cfg.n_layer):
+        for k in ("w_qkv", "w_o", "w_fc", "w_proj"):
+            assert 0 < rel(g1["layers"][l][k], g0["layers"][l][k]) < 10 * stores * u
+    with pytest.raises(ValueError):
+        O.stack_forward_backward(cfg, ids, glob, layers, stream_dtype="fp16")
