@@ -593,6 +593,15 @@ def stack_forward_backward(cfg, ids: np.ndarray, glob: Dict[str, np.ndarray],
         grads["smear_gate"] = dws
         grads["smear_lambda"] = dlam
         sum_abs["smear_lambda"] = float(np.sum(np.abs(np.sum(dx * sc["prev"], axis=-1) * sc["sg"])))
+        # the gate weight gradient nests two sums (over channels into each
+        # token's gate input, then over tokens): the magnitudes of both levels'
+        # terms, per gate channel
+        lam_s = float(np.ravel(glob["smear_lambda"])[0])
+        inner = np.sum(np.abs(dx * sc["prev"]), axis=-1)
+        inner[:, 0] = 0.0
+        n_s = glob["smear_gate"].shape[0]
+        sum_abs["smear_gate"] = np.einsum("bt,btc->c", inner * np.abs(lam_s * sc["sg"] * (1.0 - sc["sg"])),
+                                          np.abs(e[..., :n_s]))
     else:
         de = dx
     grads["wte"] = embed_backward(de, inp, glob["wte"].shape[0])

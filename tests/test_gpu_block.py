@@ -195,7 +195,9 @@ def _stack_case(w, depth_bars=None):
             check(f"{l}.ve", st.dve[l], gl["ve"])
             check(f"{l}.ve_gate", st.dve_gate[l], gl["ve_gate"], gl["sum_abs"]["ve_gate"])
     if w.extras:
-        check("smear_gate", st.d_smear_gate, g["smear_gate"])
+        # a token sum of per-token channel sums, both cancelling: the gate rule
+        # (the forward error bound of the sums) as for the value-embedding gate
+        check("smear_gate", st.d_smear_gate, g["smear_gate"], o_out["sum_abs"]["smear_gate"])
         # The residual, smear and backout scalars' gradients are sums over all
         # B*T*C activations with heavy cancellation (the sum of the terms'
         # magnitudes is 10^2..10^3 times the sum at these shapes).  fp32

@@ -644,3 +644,28 @@ def test_stack_bf16_stream_storage_option(extras):
             assert 0 < rel(g1["layers"][l][k], g0["layers"][l][k]) < 10 * stores * u
     with pytest.raises(ValueError):
         O.stack_forward_backward(cfg, ids, glob, layers, stream_dtype="fp16")
+
+
+def test_smear_gate_term_magnitudes_bound_the_gradient():
+    """sum_abs of the smear gate's gradient is the magnitude sum of its terms:
+    it bounds the gradient (triangle inequality) and equals it when every
+    term has one sign (dx = x_prev with the gate's derivative positive)."""
+    cfg = tiny_cfg(C=48, n_head=3, n_kv_head=1, head_dim=16, mlp_hidden=96, vocab=13, T=5, n_layer=2,
+                   windows=(-1, 2), extras=True)
+    ids, glob, layers = _params(cfg, np.random.default_rng(41))
+    _, g, o = O.stack_forward_backward(cfg, ids, glob, layers)
+    sa = o["sum_abs"]["smear_gate"]
+    assert sa.shape == g["smear_gate"].shape and np.all(sa >= np.abs(g["smear_gate"]) * (1 - 1e-12))
+    assert np.all(sa < 1e3 * (np.abs(g["smear_gate"]) + 1e-300))
+    # one sign: with the embedding rows positive and dx parallel to x_prev the
+    # two nested sums have no cancellation, so the bound is attained
+    e = np.abs(np.random.default_rng(3).standard_normal((1, 4, 8))) + 0.1
+    c = {"prev": np.concatenate([np.zeros((1, 1, 8)), e[:, :-1]], axis=1)}
+    c["sg"] = np.full((1, 4), 0.3)
+    c["gate"] = 0.5 * c["sg"]
+    dx = c["prev"].copy()
+    _, dws, _ = O.smear_backward(dx, e, np.ones(3), 0.5, c)
+    inner = np.sum(np.abs(dx * c["prev"]), axis=-1)
+    inner[:, 0] = 0.0
+    ref = np.einsum("bt,btc->c", inner * np.abs(0.5 * c["sg"] * (1 - c["sg"])), np.abs(e[..., :3]))
+    assert np.allclose(dws, ref, rtol=1e-14, atol=0)
