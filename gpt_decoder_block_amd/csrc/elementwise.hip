@@ -491,10 +491,14 @@ hipError_t qk_norm_rope_bwd(int dt, void* d, const void* qkvh, const float* rinv
 }
 
 // ------------------------------------------------------- cross-entropy
-// One workgroup of 256 threads per row of logits.  The row (up to
+// One workgroup per row of logits (256 threads; the bf16 kernel CE_NT).  The row (up to
 // 256*CE_MAXV vectors) is read once into registers: max, sum of exp,
 // log-sum-exp, then (softmax - onehot)/N is written over the logits.
 constexpr int CE_MAXV = 16;
+// threads per row of the bf16 kernel (each holds 256 * CE_MAXV / CE_NT vectors)
+#ifndef CE_NT
+#define CE_NT 512
+#endif
 
 template <typename T>
 __global__ __launch_bounds__(256) void ce_k(T* z, const int32_t* __restrict__ tgt, float* __restrict__ row_loss,
@@ -554,9 +558,11 @@ __global__ __launch_bounds__(256) void ce_k(T* z, const int32_t* __restrict__ tg
 // latency) and widened on each of the three uses; the exponentials are taken
 // in base 2 on log2(e)-scaled logits.  The logits are read and dz written
 // with non-temporal accesses (one pass over 4.3 GB at d24: 0.90 -> 0.82 ms).
-__global__ __launch_bounds__(256) void ce_bf16_k(bf16* z, const int32_t* __restrict__ tgt,
+template <int NT>
+__global__ __launch_bounds__(NT) void ce_bf16_k(bf16* z, const int32_t* __restrict__ tgt,
                                                   float* __restrict__ row_loss, int N, int V) {
-  __shared__ float red[4];
+  constexpr int MV = CE_MAXV * 256 / NT;  // 16-byte vectors per thread
+  __shared__ float red[NT / 64];
   constexpr float L2E = 1.4426950408889634f;
   const int n = blockIdx.x;
   bf16* zr = z + (size_t)n * V;
@@ -564,10 +570,10 @@ __global__ __launch_bounds__(256) void ce_bf16_k(bf16* z, const int32_t* __restr
   int y = tgt[n];
   y = y < 0 ? 0 : (y >= V ? V - 1 : y);
   const float zy = (float)zr[y];
-  u32x4 raw[CE_MAXV];
+  u32x4 raw[MV];
 #pragma unroll
-  for (int i = 0; i < CE_MAXV; ++i) {
-    const int vi = threadIdx.x + 256 * i;
+  for (int i = 0; i < MV; ++i) {
+    const int vi = threadIdx.x + NT * i;
     raw[i] = vi < nv ? __builtin_nontemporal_load((const u32x4*)(zr + vi * 8))
                      : u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
   }
@@ -580,28 +586,28 @@ __global__ __launch_bounds__(256) void ce_bf16_k(bf16* z, const int32_t* __restr
   // NaN gives a NaN loss either way)
   float mx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < CE_MAXV; ++i)
+  for (int i = 0; i < MV; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       asm("v_max3_f32 %0, %1, %2, %3" : "=v"(mx) : "v"(mx), "v"(lo(raw[i][q])), "v"(hi(raw[i][q])));
-  mx = block_max<256>(mx, red);
+  mx = block_max<NT>(mx, red);
   // an empty asm marks the raw words as changed, so the widened floats are
   // recomputed in each pass rather than kept live (which would double the
   // registers per row)
 #pragma unroll
-  for (int i = 0; i < CE_MAXV; ++i)
+  for (int i = 0; i < MV; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(raw[i][q]));
   const float m2 = mx * L2E;
   float se = 0.f;
 #pragma unroll
-  for (int i = 0; i < CE_MAXV; ++i)
+  for (int i = 0; i < MV; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       se += __builtin_amdgcn_exp2f(fmaf(lo(raw[i][q]), L2E, -m2)) + __builtin_amdgcn_exp2f(fmaf(hi(raw[i][q]), L2E, -m2));
-  se = block_sum<256>(se, red);
+  se = block_sum<NT>(se, red);
 #pragma unroll
-  for (int i = 0; i < CE_MAXV; ++i)
+  for (int i = 0; i < MV; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(raw[i][q]));
   const float lse = mx + logf(se);
@@ -611,8 +617,8 @@ __global__ __launch_bounds__(256) void ce_bf16_k(bf16* z, const int32_t* __restr
   // the exponent (no multiply per element)
   const float l2n = l2 + log2f((float)N);
 #pragma unroll
-  for (int i = 0; i < CE_MAXV; ++i) {
-    const int vi = threadIdx.x + 256 * i;
+  for (int i = 0; i < MV; ++i) {
+    const int vi = threadIdx.x + NT * i;
     if (vi < nv) {
       bf16x8 o;
 #pragma unroll
@@ -624,7 +630,7 @@ __global__ __launch_bounds__(256) void ce_bf16_k(bf16* z, const int32_t* __restr
     }
   }
   // the target's entry, rewritten by the thread that stored its vector
-  if ((y >> 3) % 256 == (int)threadIdx.x) zr[y] = (bf16)((__builtin_amdgcn_exp2f(fmaf(zy, L2E, -l2)) - 1.0f) * invN);
+  if ((y >> 3) % NT == (int)threadIdx.x) zr[y] = (bf16)((__builtin_amdgcn_exp2f(fmaf(zy, L2E, -l2)) - 1.0f) * invN);
   if (threadIdx.x == 0) row_loss[n] = lse - zy;
 }
 
@@ -674,7 +680,7 @@ hipError_t ce_fwd_bwd(int dt, void* z, const int32_t* tgt, float* row_loss, int 
   const int vn = dt == BF16 ? 8 : 4;
   const bool fits = V / vn <= 256 * CE_MAXV;
   if (dt == BF16) {
-    if (fits) hipLaunchKernelGGL(ce_bf16_k, dim3(N), dim3(256), 0, s, (bf16*)z, tgt, row_loss, N, V);
+    if (fits) hipLaunchKernelGGL(ce_bf16_k<CE_NT>, dim3(N), dim3(CE_NT), 0, s, (bf16*)z, tgt, row_loss, N, V);
     else hipLaunchKernelGGL(ce_long_k<bf16>, dim3(N), dim3(256), 0, s, (bf16*)z, tgt, row_loss, N, V);
   } else {
     if (fits) hipLaunchKernelGGL(ce_k<float>, dim3(N), dim3(256), 0, s, (float*)z, tgt, row_loss, N, V);
